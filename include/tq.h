@@ -1,0 +1,215 @@
+/*
+ * tq.h -- C ABI of the MI355X (gfx950) TurboQuant-style KV-cache library.
+ *
+ * The operations follow three summary pages, cited by tag:
+ *   [P1] "Resumen Técnico: Inferencia Estadística y Medidas de Calidad de
+ *        Cuantizaciones de Cache KV Inspiradas en TurboQuant"
+ *   [P2] "Resumo Técnico: Ablação, Inferência Estatística e Validação para
+ *        Compressão de KV-Cache"
+ *   [P3] "Resumo Técnico: HeadQ: Distorção Visível ao Modelo e Correção no
+ *        Espaço de Pontuação para Quantização de KV-Cache"
+ *
+ * Conventions for every entry point
+ *   - Pointers documented as "device" are HIP device memory owned by the
+ *     caller; "host" pointers are ordinary CPU memory.  The library owns only
+ *     its cached per-(device, seed, d) constants (freed by tq_release_cache).
+ *   - Every call returns tq_status.  All argument and descriptor checks run
+ *     on the host before any HIP call, so a rejected call touches no GPU
+ *     state.  tq_last_error() returns a thread-local message for the last
+ *     failure on the calling thread.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     tq_quantize and tq_decode_attention are stream-ordered and return
+ *     before the GPU work finishes; tq_metrics synchronises the stream.
+ *   - Head dimension d must be a power of two in [32, 1024].  Non-finite
+ *     inputs give unspecified (but memory-safe) output.
+ *
+ * Packed cache (one tq_packed per tensor, K or V)
+ *   Vector index v = (b*H + h)*T_cap + t.  Structure-of-arrays planes:
+ *     codes      uint8 [v][d*bits/8]   Lloyd-Max indices, LSB-first bitstream:
+ *                                      coordinate i in bits [bits*i, bits*i+bits)
+ *     norms      fp32  [v]             ||x||
+ *     qjl        uint8 [v][d/8]        PROD: bit i = [(S r)_i >= 0]
+ *     gamma      fp32  [v]             PROD: ||r||
+ *     side       uint8 [v][rank*side_bits/8]  HEADQ side code, LSB-first
+ *     side_scale fp32  [v]             HEADQ: s_z
+ *   Every plane base must be 16-byte aligned.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,       /* bad argument, NULL or misaligned pointer, bad size  */
+  TQ_EUNSUPPORTED = 2, /* valid but not supported (e.g. d = 2048)             */
+  TQ_EMISMATCH = 3,    /* descriptors disagree (K vs V, q vs cache, workspace)*/
+  TQ_ENOMEM = 4,       /* workspace too small or device allocation failed     */
+  TQ_EDEVICE = 5       /* a HIP call failed                                    */
+} tq_status;
+
+typedef enum tq_dtype { TQ_F32 = 0, TQ_F16 = 1 } tq_dtype;
+typedef enum tq_tensor { TQ_KEYS = 0, TQ_VALUES = 1 } tq_tensor;
+
+/* Per-tensor quantiser modes.
+ *   PLAIN: [P1] "Esquemas de Cuantización" 1 and [P2] "Contribuições
+ *          Principais" 1 (Plain-KV): norm split + scalar Lloyd-Max on the
+ *          unrotated unit vector.
+ *   MSE:   [P2] "Contribuições Principais" 1 (TQ-KV): norm split, seeded
+ *          sign flip + normalised Walsh-Hadamard rotation, Beta Lloyd-Max.
+ *   PROD:  [P1] "Esquemas de Cuantización" 2-3: MSE at n-1 bits plus a 1-bit
+ *          QJL sketch sign(S r) and ||r|| of the rotated residual.
+ *   HEADQ: [P3] section 3 "Metodologia: HeadQ": MSE base at 2 bits plus a
+ *          rank-r side code of the residual in a query-PCA basis (keys only). */
+typedef enum tq_mode { TQ_MODE_PLAIN = 0, TQ_MODE_MSE = 1, TQ_MODE_PROD = 2, TQ_MODE_HEADQ = 3 } tq_mode;
+
+/* Scheme presets at a budget of n bits per coordinate ([P1] "Esquemas de
+ * Cuantización", [P2] "Contribuições Principais" 1, [P3] section 3):
+ *   KV     K PLAIN(n)  V PLAIN(n)      TQ_KV  K MSE(n)   V MSE(n)
+ *   KQV    K MSE(n)    V PROD(n)       QKQV   K PROD(n)  V PROD(n)
+ *   TQ_QKV K PROD(n)   V MSE(n)        HEADQ  K HEADQ(2) V MSE(n)          */
+typedef enum tq_scheme {
+  TQ_SCHEME_KV = 0, TQ_SCHEME_TQ_KV = 1, TQ_SCHEME_KQV = 2,
+  TQ_SCHEME_QKQV = 3, TQ_SCHEME_TQ_QKV = 4, TQ_SCHEME_HEADQ = 5
+} tq_scheme;
+
+/* Dense device tensor [B][H][T][d]; the last dimension is contiguous and the
+ * other strides are in elements.  Queries use T = 1 and H = number of query
+ * heads. */
+typedef struct tq_tensor_desc {
+  const void* data;
+  int32_t dtype; /* tq_dtype */
+  int32_t B, H, T, d;
+  int64_t stride_b, stride_h, stride_t;
+} tq_tensor_desc;
+
+/* Bytes per vector of each plane. */
+typedef struct tq_layout {
+  int32_t code_bytes;
+  int32_t qjl_bytes;   /* 0 unless PROD  */
+  int32_t side_bytes;  /* 0 unless HEADQ */
+  int32_t has_gamma;
+  int32_t has_side_scale;
+} tq_layout;
+
+/* HeadQ side-code parameters ([P3] section 3).  basis: device fp32
+ * [H][d][rank], column j of head h is U_h[:, j]; caller-owned and read by
+ * both tq_quantize and the decode/metrics calls. */
+typedef struct tq_headq {
+  const float* basis;
+  int32_t rank;      /* r, multiple of 8, <= 64 */
+  int32_t side_bits; /* q_s in [2, 8]           */
+} tq_headq;
+
+/* One packed tensor.  The caller sets T_cap and the plane pointers; the
+ * header fields are written by tq_quantize. */
+typedef struct tq_packed {
+  int32_t B, H, T, T_cap, d;
+  int32_t mode;      /* tq_mode                                           */
+  int32_t bits;      /* width of the Lloyd-Max index (PROD: n-1, HEADQ: 2) */
+  int32_t side_rank, side_bits;
+  uint64_t seed;
+  uint8_t* codes;
+  float* norms;
+  uint8_t* qjl;
+  float* gamma;
+  uint8_t* side;
+  float* side_scale;
+  const float* basis; /* HEADQ: U, device [H][d][side_rank] */
+} tq_packed;
+
+/* Quality measures ([P1] "Métricas de Evaluación" and "Significado y
+ * Afirmaciones" 1; [P2] "Configuração Experimental").  KL is
+ * KL(p_ref || p_quant) in nats over each query's softmax, with its mean and
+ * worst case over queries; top-5 recall is |top5(s) ∩ top5(s_hat)| / 5 (ties
+ * to the lower index) averaged over queries; relMSE is pooled,
+ * sum ||x - x_hat||^2 / sum ||x||^2; dir_err is the mean of 1 - cos(x, x_hat)
+ * over vectors with non-zero norm on both sides.  Fields whose inputs were
+ * not given are NaN. */
+typedef struct tq_metrics_out {
+  double kl_mean, kl_max, top5_recall;
+  double relmse_k, relmse_v, dir_err_k, dir_err_v;
+  int64_t n_queries;
+} tq_metrics_out;
+
+int32_t tq_abi_version(void);
+const char* tq_status_str(tq_status s);
+const char* tq_last_error(void);
+
+/* Beta((d-1)/2,(d-1)/2) Lloyd-Max codebook for one coordinate of a unit
+ * vector in R^d ([P1] "Marco Teórico"; [P2] "Configuração Experimental").
+ * Host only.  centroids: host double[2^bits] ascending; boundaries: host
+ * double[2^bits - 1] (midpoints).  bits in [1, 8]; d power of two in
+ * [32, 1024]. */
+tq_status tq_codebook_build(int32_t d, int32_t bits, double* centroids, double* boundaries);
+
+/* Scheme preset -> (mode, index bits) of one tensor.  Host only. */
+tq_status tq_scheme_modes(int32_t scheme, int32_t n_bits, int32_t which, int32_t* mode, int32_t* bits);
+
+/* Bytes per vector of each plane for (d, mode, index bits, side code). */
+tq_status tq_packed_layout(int32_t d, int32_t mode, int32_t bits, int32_t side_rank,
+                           int32_t side_bits, tq_layout* out);
+
+/* The seeded random state of the rotation and the sketch ([P2]
+ * "Configuração Experimental": random Walsh-Hadamard transform and QJL
+ * sketch).  Host only.  signs: host float[d] (+1/-1); S: host float[d*d]
+ * row-major (m = d rows), either may be NULL.  Generated by SplitMix64 as
+ * specified in the design notes. */
+tq_status tq_rotation_state(uint64_t seed, int32_t d, float* signs, float* S);
+
+/* Write side: quantise x [B][H][T][d] (fp16 or fp32, device) into `out`.
+ * Mode and bits come from (scheme, n_bits, which).  n_bits in [1, 8]
+ * (PROD needs n_bits >= 2).  hq must be non-NULL exactly when the mode is
+ * HEADQ (keys of TQ_SCHEME_HEADQ).  out->T_cap >= x->T (0 means x->T); the
+ * planes the mode needs must be set, 16-byte aligned and sized per
+ * tq_packed_layout.  Writes tokens [0, x->T) and sets out->T = x->T.
+ * Stream-ordered. */
+tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, int32_t n_bits,
+                      uint64_t seed, const tq_headq* hq, tq_packed* out, void* stream);
+
+/* Workspace bytes tq_decode_attention needs for Hq query heads. */
+tq_status tq_decode_workspace_size(const tq_packed* k, const tq_packed* v, int32_t Hq, size_t* bytes);
+
+/* Read side ([P3] sections 2.1, 2.2 and 3; [P1] "Esquemas de Cuantización"):
+ * for every query q [B][Hq][1][d] (device, fp16/fp32) attend over the packed
+ * cache: s_j = (q^T k_hat_j + HeadQ correction q^T U z_hat_j) / sqrt(d),
+ * p = softmax(s), out = sum_j p_j v_hat_j.  Query head g reads KV head
+ * g / (Hq / H).  out: device fp32 [B][Hq][d]; lse: device fp32 [B][Hq]
+ * (log-sum-exp of s, may be NULL).  ws: device workspace of at least
+ * tq_decode_workspace_size bytes, 256-byte aligned.  Stream-ordered. */
+tq_status tq_decode_attention(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v,
+                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes tq_metrics needs. */
+tq_status tq_metrics_workspace_size(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v,
+                                    size_t* bytes);
+
+/* Quality measures of the packed cache against the raw tensors.  q may be
+ * NULL (no KL / top-5); k_ref or v_ref may be NULL (no relMSE/dir_err for
+ * that tensor; k_ref is required when q is given).  Synchronises `stream`
+ * and writes *out (host). */
+tq_status tq_metrics(const tq_tensor_desc* q, const tq_tensor_desc* k_ref, const tq_tensor_desc* v_ref,
+                     const tq_packed* k, const tq_packed* v, tq_metrics_out* out, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* HeadQ calibration ([P3] section 3, "Calibração"): rank-r PCA of the
+ * centred calibration queries calib [N][d] (host fp32).  U: host fp32
+ * [d][rank], columns = eigenvectors of the largest eigenvalues, each with
+ * its largest-magnitude entry positive.  Host only, synchronous. */
+tq_status tq_headq_fit(const float* calib, int32_t N, int32_t d, int32_t rank, float* U);
+
+/* Frees the cached device constants of every device. */
+tq_status tq_release_cache(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

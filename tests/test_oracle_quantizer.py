@@ -1,0 +1,142 @@
+"""Pins of the oracle's write side: packing, marginal law after rotation,
+end-to-end MSE against the codebook distortion, QJL estimator moments
+(CPU only)."""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import codebook as cb
+from oracle import quantizer as qz
+from oracle.rng import gaussian_sketch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _pack_cases():
+    for line in open(os.path.join(GOLDEN, "pack_examples.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        w, vals, hexes = [p.strip() for p in line.split("|")]
+        yield int(w), [int(v) for v in vals.split()], bytes.fromhex(hexes.replace(" ", ""))
+
+
+@pytest.mark.parametrize("case", list(_pack_cases()))
+def test_pack_golden(case):
+    w, vals, expect = case
+    got = qz.pack_bits(np.array([vals]), w)
+    assert bytes(got[0]) == expect
+    assert np.array_equal(qz.unpack_bits(got, w, len(vals))[0], vals)
+
+
+@pytest.mark.parametrize("w", [1, 2, 3, 4])
+def test_pack_roundtrip(w):
+    v = np.random.default_rng(w).integers(0, 1 << w, size=(7, 128))
+    assert np.array_equal(qz.unpack_bits(qz.pack_bits(v, w), w, 128), v)
+
+
+def test_rotated_coordinates_follow_beta_marginal():
+    # [P1] "Marco Teórico": Pi x / ||x|| of a Gaussian x is uniform on the
+    # sphere, so each coordinate follows the Beta marginal.
+    d = 128
+    st = qz.QState(d, qz.MSE, 2, seed=11)
+    x = np.random.default_rng(2).standard_normal((20000, d))
+    y = qz.quantize(x, st)["y"]
+    for j in (0, 77):
+        assert stats.kstest(y[:, j], lambda v: cb.cdf(v, d)).pvalue > 1e-3
+
+
+@pytest.mark.parametrize("mode", [qz.MSE, qz.PLAIN])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_mse_relmse_equals_codebook_distortion(mode, bits):
+    """For isotropic data E[relMSE] = d D(d, b) exactly (norm split + a
+    uniform direction), for the rotated and the plain quantiser alike."""
+    d = 128
+    st = qz.QState(d, mode, bits, seed=5)
+    x = np.random.default_rng(bits).standard_normal((3000, d))
+    q = qz.quantize(x, st)
+    xh = qz.dequantize(q, st)
+    per = np.sum((x - xh) ** 2, axis=1) / np.sum(x * x, axis=1)
+    D = d * cb.distortion(d, st.centroids, st.boundaries)
+    assert abs(per.mean() - D) < 4 * per.std() / math.sqrt(per.size) + 1e-6
+    # Direction: cos(x, x_hat) ~ sqrt(1 - D) for small D.
+    if bits >= 3:
+        cos = np.sum(x * xh, axis=1) / np.linalg.norm(x, axis=1) / np.linalg.norm(xh, axis=1)
+        assert abs(cos.mean() - math.sqrt(1 - D)) < 0.01
+
+
+def test_high_rate_roundtrip_is_close():
+    # A transposed rotation or a wrong index would give relMSE ~ 2, not ~ 0.009.
+    d = 64
+    st = qz.QState(d, qz.MSE, 4, seed=1)
+    x = np.random.default_rng(0).standard_normal((50, d)) * 3.0 + 1.0
+    xh = qz.dequantize(qz.quantize(x, st), st)
+    assert np.sum((x - xh) ** 2) / np.sum(x * x) < 0.02
+
+
+def test_zero_vector():
+    for mode in (qz.MSE, qz.PROD, qz.PLAIN):
+        st = qz.QState(32, mode, 3, seed=0)
+        x = np.zeros((2, 32))
+        x[1, 3] = 2.0
+        q = qz.quantize(x, st)
+        assert q["nu"][0] == 0 and np.all(q["idx"][0] == 0)
+        if mode == qz.PROD:
+            assert q["gamma"][0] == 0 and np.all(q["sign_bits"][0] == 0)
+        assert np.all(qz.dequantize(q, st)[0] == 0)
+
+
+def test_qjl_unbiased_with_pinned_variance():
+    """[P1] "Contribuciones Clave" 1: the 1-bit sketch estimate of <q, r> is
+    unbiased; its variance is ((pi/2)||q||^2||r||^2 - <q,r>^2)/m, whose
+    leading term for unit q and m = d is (pi/2)||r||^2/d."""
+    d = 64
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal(d)
+    q /= np.linalg.norm(q)
+    r = rng.standard_normal(d) * 0.1
+    est, sq = [], []
+    for seed in range(4000):
+        S = gaussian_sketch(seed, d)
+        sigma = np.where(S @ r >= 0, 1.0, -1.0)
+        rh = math.sqrt(math.pi / 2) / d * np.linalg.norm(r) * (S.T @ sigma)
+        est.append(q @ rh)
+        sq.append(np.sum((rh - r) ** 2))
+    est = np.array(est)
+    exact = q @ r
+    n = est.size
+    var = ((math.pi / 2) * (r @ r) - exact ** 2) / d
+    assert abs(est.mean() - exact) < 4 * math.sqrt(var / n)
+    # Sample variance of a near-Gaussian statistic: SE ~ var sqrt(2/n).
+    assert abs(est.var() - var) < 4 * var * math.sqrt(2 / n)
+    # E||r_hat - r||^2 = ||r||^2 (pi d / 2 - 1) / m.
+    sq = np.array(sq)
+    exp_sq = (r @ r) * (math.pi * d / 2 - 1) / d
+    assert abs(sq.mean() - exp_sq) < 4 * sq.std() / math.sqrt(n)
+
+
+def test_prod_relmse_matches_closed_form():
+    """relMSE of PROD(b+1) on isotropic data = d D(b) (pi/2 - 1/d) in
+    expectation (the sketch adds the variance of the previous test)."""
+    d = 128
+    st = qz.QState(d, qz.PROD, 4, seed=2)
+    x = np.random.default_rng(9).standard_normal((3000, d))
+    q = qz.quantize(x, st)
+    xh = qz.dequantize(q, st)
+    per = np.sum((x - xh) ** 2, axis=1) / np.sum(x * x, axis=1)
+    D3 = d * cb.distortion(d, st.centroids, st.boundaries)
+    assert abs(per.mean() - D3 * (math.pi / 2 - 1 / d)) < 4 * per.std() / math.sqrt(per.size)
+    # Unbiased: the mean error vector of x_hat - x is ~0 along any direction.
+    err = (xh - x).mean(axis=0)
+    assert np.max(np.abs(err)) < 5 * math.sqrt(per.mean() * 1.0 / 3000) * 1.5
+
+
+def test_jensen_amplification():
+    # [P2] "Contribuições Principais" 2: E[exp(s + eps)] = exp(s) exp(sigma^2/2)
+    # for zero-mean Gaussian eps.
+    rng = np.random.default_rng(0)
+    for sig in (0.1, 0.5, 1.0):
+        e = np.exp(rng.standard_normal(400000) * sig)
+        assert abs(e.mean() / math.exp(sig * sig / 2) - 1) < 4 * e.std() / math.sqrt(e.size)
