@@ -1,0 +1,169 @@
+"""Throughput of the packed-KV hot path on one MI355X.
+
+One step = quantise the full K and V caches (write side) + decode attention
+over the packed cache for every query (read side), on the isotropic decode
+workload: B=16, 32 heads, d=128, context 32768, fp16 K/V ~ N(0, 1/d), one
+fp16 query per head, scheme KQV at n=4 (KV and QKQV with --scheme).
+
+Prints one JSON line.  `value` = decode GB/s of packed cache read
+(algorithmic packed bytes / time of the decode entry point); quantize tok/s
+and the whole-step time ride along.  `roofline` covers the decode chain;
+`cpu_baseline` times the float64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PACKED_BYTES = {  # per token-head (K + V) at d=128, n=4, fp32 norms / gamma
+    "kv": 68 + 68, "kqv": 68 + 72, "qkqv": 72 + 72, "tq-kv": 68 + 68, "tq-qkv": 72 + 68,
+}
+
+
+def cpu_baseline(scheme, budget_s=12.0):
+    """Oracle (float64 numpy) on whole (b, h) slices of the same workload:
+    quantise K and V of one head (32768 tokens) and decode its query; repeat
+    slices until the budget is spent.  Scaled to decode GB/s of packed bytes."""
+    import numpy as np
+    from compressed_decode_attention_kv_amd import synth
+    from oracle import attention as oat
+    from oracle import quantizer as oqz
+    from oracle import schemes as osc
+
+    (km, kb), (vm, vb) = osc.modes(scheme, 4)
+    sk = oqz.QState(128, km, kb, 0)
+    sv = oqz.QState(128, vm, vb, 0)
+    T = 32768
+    done, t_quant, t_dec, slices = 0, 0.0, 0.0, 0
+    t_start = time.time()
+    while time.time() - t_start < budget_s and slices < 64:
+        K, V, Q = synth.isotropic(1, 1, 1, T, 128, seed=100 + slices, dtype=np.float16)
+        K, V, Q = K[0, 0].astype(np.float64), V[0, 0].astype(np.float64), Q[0].astype(np.float64)
+        t0 = time.time()
+        qk, qv = oqz.quantize(K, sk), oqz.quantize(V, sv)
+        t1 = time.time()
+        Kh, Vh = oqz.dequantize(qk, sk), oqz.dequantize(qv, sv)
+        oat.attend(Q, Kh, Vh)
+        t2 = time.time()
+        t_quant += t1 - t0
+        t_dec += t2 - t1
+        slices += 1
+        done += T
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    gbs = done * PACKED_BYTES[scheme] / t_dec / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": "%d whole (batch, head) slices x 32768 tokens, d=128, scheme %s n=4 "
+                      "(decode = dense dequantise + attention); quantize %.3g tok/s"
+                      % (slices, scheme, done / t_quant)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--scheme", default="kqv", choices=sorted(PACKED_BYTES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--B", type=int, default=16)
+    ap.add_argument("--H", type=int, default=32)
+    ap.add_argument("--T", type=int, default=32768)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from compressed_decode_attention_kv_amd import synth, tq
+
+    torch.cuda.set_device(0)
+    B, H, T, d, n = args.B, args.H, args.T, 128, 4
+    K, V, Q = synth.device_isotropic(B, H, 1, T, d, seed=1)
+    torch.cuda.synchronize()
+
+    kp = tq.quantize(K, tq.KEYS, args.scheme, n, 0)
+    vp = tq.quantize(V, tq.VALUES, args.scheme, n, 0)
+    ws = torch.empty(tq.decode_workspace_size(kp, vp, H), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    kdesc, _ = tq.tensor_desc(K)
+    vdesc, _ = tq.tensor_desc(V)
+    qdesc, _ = tq.tensor_desc(Q)
+    lib = tq.lib()
+    import ctypes
+    sid = tq.SCHEMES[args.scheme]
+
+    def stream():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def quant():
+        tq._check(lib.tq_quantize(ctypes.byref(kdesc), tq.KEYS, sid, n, 0, None, ctypes.byref(kp.c), stream()))
+        tq._check(lib.tq_quantize(ctypes.byref(vdesc), tq.VALUES, sid, n, 0, None, ctypes.byref(vp.c), stream()))
+
+    def decode():
+        tq._check(lib.tq_decode_attention(ctypes.byref(qdesc), ctypes.byref(kp.c), ctypes.byref(vp.c),
+                                          out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), stream()))
+
+    for _ in range(args.warmup):
+        quant()
+        decode()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.time()
+    for e in ev:
+        e[0].record()
+        quant()
+        e[1].record()
+        decode()
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    q_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    d_ms = [b.elapsed_time(c) for _, b, c in ev]
+    step_ms = wall * 1000.0 / args.steps
+    q_avg = sum(q_ms) / len(q_ms)
+    d_avg = sum(d_ms) / len(d_ms)
+    packed = B * H * T * PACKED_BYTES[args.scheme]
+    dec_gbs = packed / (d_avg * 1e-3) / 1e9
+    tok_s = B * T / (q_avg * 1e-3)
+    assert torch.isfinite(out).all().item()
+
+    res = {
+        "metric": "packed-KV decode attention GB/s (% HBM peak) + quantize tok/s, d=128 n=4",
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "isotropic decode: B=%d H=%d T=%d d=%d fp16 K/V~N(0,1/d), 1 query/head, %s n=%d"
+                               % (B, H, T, d, args.scheme, n),
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "scheme": args.scheme, "n_bits": n},
+        "decode_ms": round(d_avg, 4),
+        "decode_pct_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
+        "quantize_ms": round(q_avg, 4),
+        "quantize_tok_per_s": round(tok_s, 1),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode chain (query prep + split decode + combine)",
+                     "algorithmic_bytes_per_launch": packed},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.scheme)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

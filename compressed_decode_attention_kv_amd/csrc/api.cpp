@@ -1,0 +1,551 @@
+// C ABI of libtq (declared in include/tq.h): argument validation on the host
+// (before any HIP call), the per-device cache of the seeded sketch, and the
+// dispatch of the write-side, read-side and metric kernels.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "internal.h"
+
+namespace tq {
+int relerr_blocks(int T, int L, int BH);
+}
+
+using namespace tq;
+
+namespace {
+
+thread_local std::string g_err;
+
+tq_status fail(tq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+tq_status ok() { return TQ_OK; }
+
+bool pow2_in(int d, int lo, int hi) { return d >= lo && d <= hi && (d & (d - 1)) == 0; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int elem_size(int dtype) { return dtype == TQ_F16 ? 2 : 4; }
+
+tq_status check_d(int d) {
+  if (!pow2_in(d, 32, kMaxD)) return fail(TQ_EUNSUPPORTED, "head dim d=%d must be a power of two in [32, 1024]", d);
+  return TQ_OK;
+}
+
+tq_status modes_of(int scheme, int n_bits, int which, int* mode, int* bits) {
+  if (which != TQ_KEYS && which != TQ_VALUES) return fail(TQ_EINVAL, "which=%d is neither TQ_KEYS nor TQ_VALUES", which);
+  if (n_bits < 1 || n_bits > kMaxIndexBits) return fail(TQ_EINVAL, "n_bits=%d outside [1, %d]", n_bits, kMaxIndexBits);
+  int km, vm;
+  switch (scheme) {
+    case TQ_SCHEME_KV: km = TQ_MODE_PLAIN; vm = TQ_MODE_PLAIN; break;
+    case TQ_SCHEME_TQ_KV: km = TQ_MODE_MSE; vm = TQ_MODE_MSE; break;
+    case TQ_SCHEME_KQV: km = TQ_MODE_MSE; vm = TQ_MODE_PROD; break;
+    case TQ_SCHEME_QKQV: km = TQ_MODE_PROD; vm = TQ_MODE_PROD; break;
+    case TQ_SCHEME_TQ_QKV: km = TQ_MODE_PROD; vm = TQ_MODE_MSE; break;
+    case TQ_SCHEME_HEADQ: km = TQ_MODE_HEADQ; vm = TQ_MODE_MSE; break;
+    default: return fail(TQ_EINVAL, "unknown scheme %d", scheme);
+  }
+  const int m = which == TQ_KEYS ? km : vm;
+  int b = n_bits;
+  if (m == TQ_MODE_PROD) {
+    if (n_bits < 2) return fail(TQ_EINVAL, "a QJL tensor needs n_bits >= 2 (n-1 index bits + 1 sketch bit)");
+    b = n_bits - 1;
+  }
+  if (m == TQ_MODE_HEADQ) b = 2;
+  *mode = m;
+  *bits = b;
+  return TQ_OK;
+}
+
+tq_status layout_of(int d, int mode, int bits, int side_rank, int side_bits, tq_layout* out) {
+  if (tq_status s = check_d(d)) return s;
+  if (mode < TQ_MODE_PLAIN || mode > TQ_MODE_HEADQ) return fail(TQ_EINVAL, "unknown mode %d", mode);
+  if (bits < 1 || bits > kMaxIndexBits) return fail(TQ_EINVAL, "index bits %d outside [1, %d]", bits, kMaxIndexBits);
+  out->code_bytes = d * bits / 8;
+  out->qjl_bytes = mode == TQ_MODE_PROD ? d / 8 : 0;
+  out->has_gamma = mode == TQ_MODE_PROD;
+  out->side_bytes = 0;
+  out->has_side_scale = 0;
+  if (mode == TQ_MODE_HEADQ) {
+    if (side_rank < 8 || side_rank > 32 || side_rank % 8) return fail(TQ_EUNSUPPORTED, "HeadQ rank %d: must be 8, 16, 24 or 32", side_rank);
+    if (side_bits < 2 || side_bits > 8) return fail(TQ_EINVAL, "HeadQ side bits %d outside [2, 8]", side_bits);
+    if (d * side_rank > 16384) return fail(TQ_EUNSUPPORTED, "HeadQ d*rank=%d exceeds 16384", d * side_rank);
+    out->side_bytes = side_rank * side_bits / 8;
+    out->has_side_scale = 1;
+  }
+  return TQ_OK;
+}
+
+tq_status check_tensor(const tq_tensor_desc* x, const char* name) {
+  if (!x) return fail(TQ_EINVAL, "%s descriptor is NULL", name);
+  if (!x->data) return fail(TQ_EINVAL, "%s data pointer is NULL", name);
+  if (x->dtype != TQ_F16 && x->dtype != TQ_F32) return fail(TQ_EINVAL, "%s dtype %d is neither F16 nor F32", name, x->dtype);
+  if (x->B < 1 || x->H < 1 || x->T < 1) return fail(TQ_EINVAL, "%s has an empty dimension (B=%d H=%d T=%d)", name, x->B, x->H, x->T);
+  if (tq_status s = check_d(x->d)) return s;
+  const int es = elem_size(x->dtype);
+  if (!aligned(x->data, 16)) return fail(TQ_EINVAL, "%s data is not 16-byte aligned", name);
+  if (x->stride_t < x->d && x->T > 1) return fail(TQ_EINVAL, "%s stride_t < d", name);
+  if ((x->stride_t * es) % 16 || (x->stride_h * es) % 16 || (x->stride_b * es) % 16)
+    return fail(TQ_EINVAL, "%s strides must be multiples of 16 bytes", name);
+  return TQ_OK;
+}
+
+void fill_signbits(uint64_t seed, int d, uint32_t* words) {
+  std::vector<float> s(d);
+  sign_vector(seed, d, s.data());
+  for (int i = 0; i < kMaxD / 32; ++i) words[i] = 0;
+  for (int i = 0; i < d; ++i)
+    if (s[i] < 0) words[i >> 5] |= 1u << (i & 31);
+}
+
+// ---- per-device cache of the Gaussian sketch S ------------------------------------
+std::mutex g_cache_mu;
+std::map<std::tuple<int, uint64_t, int>, float*> g_sketch;
+
+tq_status sketch_on_device(uint64_t seed, int d, const float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_EDEVICE, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  auto key = std::make_tuple(dev, seed, d);
+  auto it = g_sketch.find(key);
+  if (it != g_sketch.end()) { *out = it->second; return TQ_OK; }
+  std::vector<float> S((size_t)d * d);
+  gaussian_sketch(seed, d, S.data());
+  float* p = nullptr;
+  if (hipMalloc(&p, S.size() * sizeof(float)) != hipSuccess) return fail(TQ_ENOMEM, "hipMalloc of the sketch failed");
+  if (hipMemcpy(p, S.data(), S.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(p);
+    return fail(TQ_EDEVICE, "hipMemcpy of the sketch failed");
+  }
+  g_sketch[key] = p;
+  *out = p;
+  return TQ_OK;
+}
+
+tq_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TQ_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return TQ_OK;
+}
+
+tq_status check_packed(const tq_packed* p, const char* name) {
+  if (!p) return fail(TQ_EINVAL, "%s packed descriptor is NULL", name);
+  if (p->B < 1 || p->H < 1 || p->T < 1 || p->T_cap < p->T)
+    return fail(TQ_EINVAL, "%s header is empty or T > T_cap (B=%d H=%d T=%d T_cap=%d)", name, p->B, p->H, p->T, p->T_cap);
+  tq_layout lay;
+  if (tq_status s = layout_of(p->d, p->mode, p->bits, p->side_rank, p->side_bits, &lay)) return s;
+  if (!p->codes || !p->norms) return fail(TQ_EINVAL, "%s codes/norms plane is NULL", name);
+  if (!aligned(p->codes, 16) || !aligned(p->norms, 16)) return fail(TQ_EINVAL, "%s planes must be 16-byte aligned", name);
+  if (p->mode == TQ_MODE_PROD && (!p->qjl || !p->gamma || !aligned(p->qjl, 16) || !aligned(p->gamma, 16)))
+    return fail(TQ_EINVAL, "%s QJL planes missing or misaligned", name);
+  if (p->mode == TQ_MODE_HEADQ && (!p->side || !p->side_scale || !p->basis || !aligned(p->side, 16) || !aligned(p->side_scale, 16)))
+    return fail(TQ_EINVAL, "%s HeadQ planes or basis missing or misaligned", name);
+  return TQ_OK;
+}
+
+// Kernel instantiations that exist (see launch_decode_split).
+bool key_supported(int kbits, bool kq, bool ksd) {
+  if (ksd) return !kq && kbits == 2;
+  if (kq) return kbits >= 1 && kbits <= 3;
+  return kbits >= 1 && kbits <= 4;
+}
+bool decode_supported(int kbits, bool kq, bool ksd, int vbits, bool vq) {
+  if (!key_supported(kbits, kq, ksd)) return false;
+  return vq ? (vbits >= 1 && vbits <= 3) : (vbits >= 1 && vbits <= 4);
+}
+
+struct DecodePlan {
+  int nsplit, chunk, part_stride, units, G;
+  size_t off_qrot, off_qsk, off_qw, off_part, off_qraw, bytes;
+};
+
+tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_qraw, DecodePlan* pl) {
+  if (tq_status s = check_packed(k, "K")) return s;
+  if (v) {
+    if (tq_status s = check_packed(v, "V")) return s;
+    if (k->B != v->B || k->H != v->H || k->T != v->T || k->d != v->d)
+      return fail(TQ_EMISMATCH, "K and V packed headers disagree (B, H, T or d)");
+    if (v->mode == TQ_MODE_HEADQ) return fail(TQ_EINVAL, "HeadQ is a key-side mode");
+  }
+  if (Hq < 1 || Hq % k->H) return fail(TQ_EMISMATCH, "Hq=%d is not a multiple of the KV heads H=%d", Hq, k->H);
+  const int d = k->d, L = d / 32, vpw = 64 / L;
+  const int G = Hq / k->H;
+  const int nq = k->B * Hq;
+  const int step = 4 * vpw;
+  const long groups = (long)k->B * k->H * G;
+  int nsplit = (int)std::max<long>(1, (2048 + groups - 1) / groups);
+  int chunk = (k->T + nsplit - 1) / nsplit;
+  chunk = std::max(step, (chunk + step - 1) / step * step);
+  nsplit = (k->T + chunk - 1) / chunk;
+  if (nsplit > 256) {
+    chunk = (k->T + 255) / 256;
+    chunk = (chunk + step - 1) / step * step;
+    nsplit = (k->T + chunk - 1) / chunk;
+  }
+  const bool vq = v && v->mode == TQ_MODE_PROD;
+  pl->nsplit = nsplit;
+  pl->chunk = chunk;
+  pl->G = G;
+  pl->part_stride = (int)round_up(2 + d + (vq ? d : 0), 4);
+  const long R = (long)k->B * k->H * nsplit;
+  pl->units = (int)(round_up(R, 8) * G);
+  size_t off = 0;
+  pl->off_qrot = off; off = round_up(off + (size_t)nq * d * 4, 256);
+  pl->off_qsk = off;  off = round_up(off + (k->mode == TQ_MODE_PROD ? (size_t)nq * d * 4 : 0), 256);
+  pl->off_qw = off;   off = round_up(off + (k->mode == TQ_MODE_HEADQ ? (size_t)nq * k->side_rank * 4 : 0), 256);
+  pl->off_qraw = off; off = round_up(off + (with_qraw ? (size_t)nq * d * 4 : 0), 256);
+  pl->off_part = off; off = round_up(off + (v ? (size_t)nq * nsplit * pl->part_stride * 4 : 0), 256);
+  pl->bytes = off;
+  return TQ_OK;
+}
+
+tq_status check_query(const tq_tensor_desc* q, const tq_packed* k) {
+  if (tq_status s = check_tensor(q, "q")) return s;
+  if (q->T != 1) return fail(TQ_EINVAL, "queries must have T = 1 (got %d)", q->T);
+  if (q->B != k->B || q->d != k->d) return fail(TQ_EMISMATCH, "query B/d (%d, %d) differ from the cache (%d, %d)", q->B, q->d, k->B, k->d);
+  if (q->H % k->H) return fail(TQ_EMISMATCH, "query heads %d not a multiple of KV heads %d", q->H, k->H);
+  return TQ_OK;
+}
+
+void fill_qprep(const tq_tensor_desc* q, const tq_packed* k, const float* S, char* ws, const DecodePlan& pl,
+                bool qraw, QPrepParams* qp) {
+  std::memset(qp, 0, sizeof(*qp));
+  qp->q = q->data; qp->dtype = q->dtype; qp->B = q->B; qp->Hq = q->H; qp->d = q->d; qp->Hkv = k->H;
+  qp->sb = q->stride_b; qp->sh = q->stride_h;
+  qp->rotate = k->mode != TQ_MODE_PLAIN;
+  qp->kqjl = k->mode == TQ_MODE_PROD;
+  qp->kside = k->mode == TQ_MODE_HEADQ;
+  qp->rank = k->side_rank;
+  fill_signbits(k->seed, k->d, qp->signbits);
+  qp->inv_sqrt_d = 1.0f / std::sqrt((float)k->d);
+  qp->S = S; qp->basis = k->basis;
+  qp->qrot = reinterpret_cast<float*>(ws + pl.off_qrot);
+  qp->qsk = reinterpret_cast<float*>(ws + pl.off_qsk);
+  qp->qw = reinterpret_cast<float*>(ws + pl.off_qw);
+  qp->qraw = qraw ? reinterpret_cast<float*>(ws + pl.off_qraw) : nullptr;
+}
+
+tq_status fill_codebook(int d, int bits, float* c16, float* b16) {
+  std::vector<double> c, t;
+  if (!codebook(d, bits, &c, &t)) return fail(TQ_EINVAL, "codebook(d=%d, bits=%d) failed", d, bits);
+  for (int i = 0; i < 16; ++i) {
+    c16[i] = i < (int)c.size() ? (float)c[i] : 0.f;
+    b16[i] = i < (int)t.size() ? (float)t[i] : INFINITY;
+  }
+  return TQ_OK;
+}
+
+void fill_scoring(const tq_tensor_desc* q, const tq_packed* k, const DecodePlan& pl, char* ws, DecodeParams* dp) {
+  std::memset(dp, 0, sizeof(*dp));
+  dp->B = k->B; dp->Hkv = k->H; dp->G = pl.G; dp->Hq = q->H; dp->T = k->T; dp->T_cap = k->T_cap;
+  dp->d = k->d; dp->L = k->d / 32; dp->nsplit = pl.nsplit; dp->chunk = pl.chunk;
+  dp->part_stride = pl.part_stride; dp->units = pl.units;
+  dp->k = {k->codes, k->norms, k->qjl, k->gamma, k->side, k->side_scale};
+  dp->rank = k->side_rank; dp->side_bits = k->side_bits;
+  float bnd[16];
+  fill_codebook(k->d, k->bits, dp->kc, bnd);
+  dp->k_qjl = (float)(std::sqrt(M_PI / 2.0) / k->d);
+  dp->scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)k->d));
+  dp->qrot = reinterpret_cast<const float*>(ws + pl.off_qrot);
+  dp->qsk = reinterpret_cast<const float*>(ws + pl.off_qsk);
+  dp->qw = reinterpret_cast<const float*>(ws + pl.off_qw);
+  dp->part = reinterpret_cast<float*>(ws + pl.off_part);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+const char* tq_status_str(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_EINVAL: return "TQ_EINVAL";
+    case TQ_EUNSUPPORTED: return "TQ_EUNSUPPORTED";
+    case TQ_EMISMATCH: return "TQ_EMISMATCH";
+    case TQ_ENOMEM: return "TQ_ENOMEM";
+    case TQ_EDEVICE: return "TQ_EDEVICE";
+  }
+  return "TQ_UNKNOWN";
+}
+
+const char* tq_last_error(void) { return g_err.c_str(); }
+
+tq_status tq_codebook_build(int32_t d, int32_t bits, double* centroids, double* boundaries) {
+  if (tq_status s = check_d(d)) return s;
+  if (bits < 1 || bits > 8) return fail(TQ_EINVAL, "bits=%d outside [1, 8]", bits);
+  if (!centroids || !boundaries) return fail(TQ_EINVAL, "output pointer is NULL");
+  std::vector<double> c, t;
+  if (!codebook(d, bits, &c, &t)) return fail(TQ_EINVAL, "codebook failed");
+  std::copy(c.begin(), c.end(), centroids);
+  std::copy(t.begin(), t.end(), boundaries);
+  return ok();
+}
+
+tq_status tq_scheme_modes(int32_t scheme, int32_t n_bits, int32_t which, int32_t* mode, int32_t* bits) {
+  if (!mode || !bits) return fail(TQ_EINVAL, "output pointer is NULL");
+  int m, b;
+  if (tq_status s = modes_of(scheme, n_bits, which, &m, &b)) return s;
+  *mode = m;
+  *bits = b;
+  return ok();
+}
+
+tq_status tq_packed_layout(int32_t d, int32_t mode, int32_t bits, int32_t side_rank, int32_t side_bits, tq_layout* out) {
+  if (!out) return fail(TQ_EINVAL, "output pointer is NULL");
+  return layout_of(d, mode, bits, side_rank, side_bits, out);
+}
+
+tq_status tq_rotation_state(uint64_t seed, int32_t d, float* signs, float* S) {
+  if (tq_status s = check_d(d)) return s;
+  if (signs) sign_vector(seed, d, signs);
+  if (S) gaussian_sketch(seed, d, S);
+  return ok();
+}
+
+tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, int32_t n_bits, uint64_t seed,
+                      const tq_headq* hq, tq_packed* out, void* stream) {
+  if (tq_status s = check_tensor(x, "x")) return s;
+  int mode, bits;
+  if (tq_status s = modes_of(scheme, n_bits, which, &mode, &bits)) return s;
+  if (!out) return fail(TQ_EINVAL, "output packed descriptor is NULL");
+  if ((mode == TQ_MODE_HEADQ) != (hq != nullptr))
+    return fail(TQ_EINVAL, mode == TQ_MODE_HEADQ ? "HeadQ keys need a tq_headq" : "tq_headq given for a non-HeadQ tensor");
+  tq_layout lay;
+  if (tq_status s = layout_of(x->d, mode, bits, hq ? hq->rank : 0, hq ? hq->side_bits : 0, &lay)) return s;
+  if (hq && (!hq->basis || !aligned(hq->basis, 4))) return fail(TQ_EINVAL, "HeadQ basis is NULL or misaligned");
+  const int T_cap = out->T_cap == 0 ? x->T : out->T_cap;
+  if (T_cap < x->T) return fail(TQ_EINVAL, "T_cap=%d < T=%d", T_cap, x->T);
+  if (!out->codes || !out->norms || !aligned(out->codes, 16) || !aligned(out->norms, 16))
+    return fail(TQ_EINVAL, "codes/norms planes missing or not 16-byte aligned");
+  if (mode == TQ_MODE_PROD && (!out->qjl || !out->gamma || !aligned(out->qjl, 16) || !aligned(out->gamma, 16)))
+    return fail(TQ_EINVAL, "QJL planes missing or not 16-byte aligned");
+  if (mode == TQ_MODE_HEADQ && (!out->side || !out->side_scale || !aligned(out->side, 16) || !aligned(out->side_scale, 16)))
+    return fail(TQ_EINVAL, "HeadQ side planes missing or not 16-byte aligned");
+  if ((long)x->B * x->H * (long)T_cap > (1L << 40)) return fail(TQ_EINVAL, "cache too large");
+
+  QuantParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = x->data; p.dtype = x->dtype; p.B = x->B; p.H = x->H; p.T = x->T; p.T_cap = T_cap; p.d = x->d; p.L = x->d / 32;
+  p.sb = x->stride_b; p.sh = x->stride_h; p.st = x->stride_t;
+  p.mode = mode; p.bits = bits; p.rotate = mode != TQ_MODE_PLAIN;
+  if (tq_status s = fill_codebook(x->d, bits, p.centroids, p.bounds)) return s;
+  fill_signbits(seed, x->d, p.signbits);
+  p.inv_sqrt_d = 1.0f / std::sqrt((float)x->d);
+  if (mode == TQ_MODE_PROD) {
+    if (tq_status s = sketch_on_device(seed, x->d, &p.S)) return s;
+  }
+  if (hq) { p.basis = hq->basis; p.rank = hq->rank; p.side_bits = hq->side_bits; }
+  p.codes = out->codes; p.norms = out->norms; p.qjl = out->qjl; p.gamma = out->gamma;
+  p.side = out->side; p.side_scale = out->side_scale;
+  if (tq_status s = hip_status(launch_quantize(p, (hipStream_t)stream), "quantize launch")) return s;
+  out->B = x->B; out->H = x->H; out->T = x->T; out->T_cap = T_cap; out->d = x->d;
+  out->mode = mode; out->bits = bits; out->seed = seed;
+  out->side_rank = hq ? hq->rank : 0; out->side_bits = hq ? hq->side_bits : 0;
+  out->basis = hq ? hq->basis : nullptr;
+  return ok();
+}
+
+tq_status tq_decode_workspace_size(const tq_packed* k, const tq_packed* v, int32_t Hq, size_t* bytes) {
+  if (!bytes) return fail(TQ_EINVAL, "output pointer is NULL");
+  if (!v) return fail(TQ_EINVAL, "V packed descriptor is NULL");
+  DecodePlan pl;
+  if (tq_status s = plan_decode(k, v, Hq, false, &pl)) return s;
+  *bytes = pl.bytes;
+  return ok();
+}
+
+tq_status tq_decode_attention(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v, float* out,
+                              float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!k || !v) return fail(TQ_EINVAL, "packed descriptor is NULL");
+  if (!q) return fail(TQ_EINVAL, "query descriptor is NULL");
+  DecodePlan pl;
+  if (tq_status s = plan_decode(k, v, q->H, false, &pl)) return s;
+  if (tq_status s = check_query(q, k)) return s;
+  if (!out || !aligned(out, 4) || (lse && !aligned(lse, 4))) return fail(TQ_EINVAL, "out/lse NULL or misaligned");
+  if (!ws || !aligned(ws, 256)) return fail(TQ_EINVAL, "workspace NULL or not 256-byte aligned");
+  if (ws_bytes < pl.bytes) return fail(TQ_ENOMEM, "workspace %zu bytes < required %zu", ws_bytes, pl.bytes);
+  const bool kq = k->mode == TQ_MODE_PROD, ksd = k->mode == TQ_MODE_HEADQ, vq = v->mode == TQ_MODE_PROD;
+  if (!decode_supported(k->bits, kq, ksd, v->bits, vq))
+    return fail(TQ_EUNSUPPORTED, "no decode kernel for K (mode %d, %d bits) with V (mode %d, %d bits)", k->mode, k->bits, v->mode, v->bits);
+  const float* Sk = nullptr;
+  const float* Sv = nullptr;
+  if (kq) { if (tq_status s = sketch_on_device(k->seed, k->d, &Sk)) return s; }
+  if (vq) { if (tq_status s = sketch_on_device(v->seed, v->d, &Sv)) return s; }
+  char* w = static_cast<char*>(ws);
+  hipStream_t st = (hipStream_t)stream;
+
+  DecodeParams dp;
+  fill_scoring(q, k, pl, w, &dp);
+  dp.v = {v->codes, v->norms, v->qjl, v->gamma, v->side, v->side_scale};
+  float vb[16];
+  if (tq_status s = fill_codebook(v->d, v->bits, dp.vc, vb)) return s;
+  dp.v_qjl = (float)(std::sqrt(M_PI / 2.0) / v->d);
+
+  QPrepParams qp;
+  fill_qprep(q, k, Sk, w, pl, false, &qp);
+  CombineParams cp;
+  std::memset(&cp, 0, sizeof(cp));
+  cp.nq = q->B * q->H; cp.d = k->d; cp.nsplit = pl.nsplit; cp.part_stride = pl.part_stride;
+  cp.vqjl = vq; cp.vrotate = v->mode != TQ_MODE_PLAIN; cp.v_qjl = dp.v_qjl;
+  fill_signbits(v->seed, v->d, cp.signbits);
+  cp.inv_sqrt_d = 1.0f / std::sqrt((float)k->d);
+  cp.S = Sv; cp.part = dp.part; cp.out = out; cp.lse = lse;
+
+  bool supported = true;
+  if (tq_status s = hip_status(launch_qprep(qp, st), "query prep launch")) return s;
+  if (tq_status s = hip_status(launch_decode_split(dp, k->bits, kq, ksd, v->bits, vq, st, &supported), "decode launch")) return s;
+  if (!supported) return fail(TQ_EUNSUPPORTED, "K/V mode combination has no decode kernel");
+  if (tq_status s = hip_status(launch_combine(cp, st), "combine launch")) return s;
+  return ok();
+}
+
+tq_status tq_metrics_workspace_size(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v, size_t* bytes) {
+  if (!bytes) return fail(TQ_EINVAL, "output pointer is NULL");
+  size_t need = 0;
+  if (q) {
+    if (!k) return fail(TQ_EINVAL, "KL/top-5 need the packed keys");
+    DecodePlan pl;
+    if (tq_status s = plan_decode(k, nullptr, q->H, true, &pl)) return s;
+    const size_t nq = (size_t)k->B * q->H;
+    need = pl.bytes + round_up(2 * nq * k->T * 4, 256) + round_up(nq * 2 * 8, 256);
+  }
+  for (const tq_packed* p : {k, v}) {
+    if (!p) continue;
+    if (tq_status s = check_packed(p, "packed")) return s;
+    need = std::max(need, round_up((size_t)relerr_blocks(p->T, p->d / 32, p->B * p->H) * 4 * 8, 256));
+  }
+  *bytes = need;
+  return ok();
+}
+
+static tq_status relerr(const tq_tensor_desc* x, const tq_packed* pk, char* ws, hipStream_t st, double* rel, double* dir) {
+  if (tq_status s = check_tensor(x, "reference")) return s;
+  if (x->B != pk->B || x->H != pk->H || x->T != pk->T || x->d != pk->d)
+    return fail(TQ_EMISMATCH, "reference tensor shape differs from the packed tensor");
+  RelErrParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = x->data; p.dtype = x->dtype; p.B = x->B; p.H = x->H; p.T = x->T; p.T_cap = pk->T_cap; p.d = x->d; p.L = x->d / 32;
+  p.sb = x->stride_b; p.sh = x->stride_h; p.st = x->stride_t;
+  p.mode = pk->mode; p.bits = pk->bits; p.rotate = pk->mode != TQ_MODE_PLAIN;
+  p.kqjl = pk->mode == TQ_MODE_PROD; p.kside = pk->mode == TQ_MODE_HEADQ;
+  p.rank = pk->side_rank; p.side_bits = pk->side_bits;
+  float bnd[16];
+  if (tq_status s = fill_codebook(pk->d, pk->bits, p.centroids, bnd)) return s;
+  fill_signbits(pk->seed, pk->d, p.signbits);
+  p.inv_sqrt_d = 1.0f / std::sqrt((float)pk->d);
+  p.qjl_c = (float)(std::sqrt(M_PI / 2.0) / pk->d);
+  if (p.kqjl) { if (tq_status s = sketch_on_device(pk->seed, pk->d, &p.S)) return s; }
+  p.basis = pk->basis;
+  p.planes = {pk->codes, pk->norms, pk->qjl, pk->gamma, pk->side, pk->side_scale};
+  const int nb = relerr_blocks(pk->T, pk->d / 32, pk->B * pk->H);
+  p.block_sums = reinterpret_cast<double*>(ws);
+  if (tq_status s = hip_status(launch_relerr(p, nb, st), "relerr launch")) return s;
+  std::vector<double> host((size_t)nb * 4);
+  if (tq_status s = hip_status(hipMemcpyAsync(host.data(), ws, host.size() * 8, hipMemcpyDeviceToHost, st), "copy")) return s;
+  if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
+  double e2 = 0, r2 = 0, ds = 0, cnt = 0;
+  for (int b = 0; b < nb; ++b) { e2 += host[b * 4]; r2 += host[b * 4 + 1]; ds += host[b * 4 + 2]; cnt += host[b * 4 + 3]; }
+  *rel = r2 > 0 ? e2 / r2 : NAN;
+  *dir = cnt > 0 ? ds / cnt : NAN;
+  return TQ_OK;
+}
+
+tq_status tq_metrics(const tq_tensor_desc* q, const tq_tensor_desc* k_ref, const tq_tensor_desc* v_ref,
+                     const tq_packed* k, const tq_packed* v, tq_metrics_out* out, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (!out) return fail(TQ_EINVAL, "output pointer is NULL");
+  size_t need = 0;
+  if (tq_status s = tq_metrics_workspace_size(q, k, v, &need)) return s;
+  if (!ws || !aligned(ws, 256)) return fail(TQ_EINVAL, "workspace NULL or not 256-byte aligned");
+  if (ws_bytes < need) return fail(TQ_ENOMEM, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if (q && !k_ref) return fail(TQ_EINVAL, "KL/top-5 need the raw keys");
+  if ((k_ref && !k) || (v_ref && !v)) return fail(TQ_EINVAL, "a reference tensor was given without its packed tensor");
+  if (q) {
+    if (tq_status s = check_query(q, k)) return s;
+    if (tq_status s = check_tensor(k_ref, "k_ref")) return s;
+    if (k_ref->B != k->B || k_ref->H != k->H || k_ref->T != k->T || k_ref->d != k->d)
+      return fail(TQ_EMISMATCH, "k_ref shape differs from the packed keys");
+  }
+  if (v_ref) { if (tq_status s = check_tensor(v_ref, "v_ref")) return s; }
+  out->kl_mean = out->kl_max = out->top5_recall = NAN;
+  out->relmse_k = out->relmse_v = out->dir_err_k = out->dir_err_v = NAN;
+  out->n_queries = 0;
+  char* w = static_cast<char*>(ws);
+  hipStream_t st = (hipStream_t)stream;
+  if (q) {
+    DecodePlan pl;
+    if (tq_status s = plan_decode(k, nullptr, q->H, true, &pl)) return s;
+    if (!key_supported(k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ))
+      return fail(TQ_EUNSUPPORTED, "no scoring kernel for key mode %d with %d bits", k->mode, k->bits);
+    const float* Sk = nullptr;
+    if (k->mode == TQ_MODE_PROD) { if (tq_status s = sketch_on_device(k->seed, k->d, &Sk)) return s; }
+    const size_t nq = (size_t)k->B * q->H;
+    float* s_ref = reinterpret_cast<float*>(w + pl.bytes);
+    float* s_hat = s_ref + nq * k->T;
+    double* perq = reinterpret_cast<double*>(w + pl.bytes + round_up(2 * nq * k->T * 4, 256));
+    QPrepParams qp;
+    fill_qprep(q, k, Sk, w, pl, true, &qp);
+    MetricScoreParams mp;
+    std::memset(&mp, 0, sizeof(mp));
+    fill_scoring(q, k, pl, w, &mp.dp);
+    mp.kref = k_ref->data; mp.kdtype = k_ref->dtype;
+    mp.ksb = k_ref->stride_b; mp.ksh = k_ref->stride_h; mp.kst = k_ref->stride_t;
+    mp.qraw = reinterpret_cast<const float*>(w + pl.off_qraw);
+    mp.s_ref = s_ref; mp.s_hat = s_hat;
+    MetricReduceParams rp{(int)nq, k->T, s_ref, s_hat, perq};
+    bool supported = true;
+    if (tq_status s = hip_status(launch_qprep(qp, st), "query prep launch")) return s;
+    if (tq_status s = hip_status(launch_metric_scores(mp, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, st, &supported), "score launch")) return s;
+    if (!supported) return fail(TQ_EUNSUPPORTED, "key mode has no scoring kernel");
+    if (tq_status s = hip_status(launch_metric_reduce(rp, st), "reduce launch")) return s;
+    std::vector<double> host(nq * 2);
+    if (tq_status s = hip_status(hipMemcpyAsync(host.data(), perq, host.size() * 8, hipMemcpyDeviceToHost, st), "copy")) return s;
+    if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
+    double klsum = 0, klmax = -INFINITY, rec = 0;
+    for (size_t i = 0; i < nq; ++i) { klsum += host[2 * i]; klmax = std::max(klmax, host[2 * i]); rec += host[2 * i + 1]; }
+    out->kl_mean = klsum / nq; out->kl_max = klmax; out->top5_recall = rec / nq;
+    out->n_queries = (int64_t)nq;
+  }
+  if (k_ref && k) { if (tq_status s = relerr(k_ref, k, w, st, &out->relmse_k, &out->dir_err_k)) return s; }
+  if (v_ref && v) { if (tq_status s = relerr(v_ref, v, w, st, &out->relmse_v, &out->dir_err_v)) return s; }
+  if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
+  return ok();
+}
+
+tq_status tq_headq_fit(const float* calib, int32_t N, int32_t d, int32_t rank, float* U) {
+  if (!calib || !U) return fail(TQ_EINVAL, "NULL pointer");
+  if (tq_status s = check_d(d)) return s;
+  if (N < 2 || rank < 1 || rank > d) return fail(TQ_EINVAL, "N=%d rank=%d invalid", N, rank);
+  if (!pca_basis(calib, N, d, rank, U)) return fail(TQ_EINVAL, "PCA failed");
+  return ok();
+}
+
+tq_status tq_release_cache(void) {
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (auto& kv : g_sketch) {
+    (void)hipSetDevice(std::get<0>(kv.first));
+    (void)hipFree(kv.second);
+  }
+  g_sketch.clear();
+  (void)hipSetDevice(cur);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// Internal declarations shared by the host dispatch and the HIP kernel
+// launchers of libtq.  Not part of the public ABI (include/tq.h is).
+#pragma once
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxIndexBits = 4;   // Lloyd-Max index width supported by the kernels
+constexpr int kMaxD = 1024;
+constexpr int kCoordsPerLane = 32; // every kernel gives a lane 32 consecutive coordinates
+constexpr int kMaxSideRank = 64;
+
+// ---- host math (host_math.cpp) -------------------------------------------
+// Beta((d-1)/2,(d-1)/2) Lloyd-Max codebook in double, cached per (d, bits).
+bool codebook(int d, int bits, std::vector<double>* centroids, std::vector<double>* boundaries);
+// SplitMix64 streams for the sign vector and the Gaussian sketch.
+void sign_vector(uint64_t seed, int d, float* signs);
+void gaussian_sketch(uint64_t seed, int d, float* S);  // m = d rows, row-major
+// Rank-r PCA of centred rows, Jacobi eigensolver.
+bool pca_basis(const float* X, int N, int d, int rank, float* U);
+
+// ---- kernel parameter blocks ----------------------------------------------
+struct QuantParams {
+  const void* x;
+  int dtype;            // tq_dtype
+  int B, H, T, T_cap, d, L;  // L = d / 32 lanes per vector
+  int64_t sb, sh, st;   // input strides (elements)
+  int mode, bits;
+  int rotate;           // 1 for MSE/PROD/HEADQ
+  float centroids[16];
+  float bounds[16];     // 2^bits - 1 used
+  uint32_t signbits[kMaxD / 32];  // bit i set <=> D_i = -1
+  float inv_sqrt_d;
+  const float* S;       // PROD: m x d row-major (device)
+  const float* basis;   // HEADQ: [H][d][rank] (device)
+  int rank, side_bits;
+  uint8_t* codes; float* norms; uint8_t* qjl; float* gamma; uint8_t* side; float* side_scale;
+};
+
+struct TensorPlanes {
+  const uint8_t* codes; const float* norms; const uint8_t* qjl; const float* gamma;
+  const uint8_t* side; const float* side_scale;
+};
+
+struct DecodeParams {
+  int B, Hkv, G, Hq, T, T_cap, d, L;
+  int nsplit, chunk;    // tokens per split (multiple of 64)
+  int part_stride;      // floats per partial record
+  int units;            // number of (query, split) work units, see the XCD mapping
+  TensorPlanes k, v;
+  int rank, side_bits;
+  float kc[16], vc[16];
+  float k_qjl, v_qjl;   // sqrt(pi/2)/m
+  float scale_log2;     // log2(e)/sqrt(d)
+  const float* qrot; const float* qsk; const float* qw;
+  float* part;
+};
+
+struct QPrepParams {
+  const void* q; int dtype; int B, Hq, d, Hkv;
+  int64_t sb, sh;
+  int rotate, kqjl, kside, rank;
+  uint32_t signbits[kMaxD / 32];
+  float inv_sqrt_d;
+  const float* S; const float* basis;
+  float* qrot; float* qsk; float* qw;
+  float* qraw;          // optional copy of the raw query (metrics)
+};
+
+struct CombineParams {
+  int nq, d, nsplit, part_stride, vqjl, vrotate;
+  float v_qjl;
+  uint32_t signbits[kMaxD / 32];
+  float inv_sqrt_d;
+  const float* S;
+  const float* part;
+  float* out; float* lse;
+};
+
+struct MetricScoreParams {
+  DecodeParams dp;      // scoring half of the decode parameters (k planes, q prep)
+  const void* kref; int kdtype; int64_t ksb, ksh, kst;
+  const float* qraw;    // [B*Hq][d] raw queries
+  float* s_ref; float* s_hat;  // [B*Hq][T]
+};
+
+struct MetricReduceParams {
+  int nq, T;
+  const float* s_ref; const float* s_hat;
+  double* per_query;  // [nq][2] = kl, recall
+};
+
+struct RelErrParams {
+  const void* x; int dtype; int B, H, T, T_cap, d, L;
+  int64_t sb, sh, st;
+  int mode, bits, rotate, kqjl, kside, rank, side_bits;
+  float centroids[16];
+  uint32_t signbits[kMaxD / 32];
+  float inv_sqrt_d, qjl_c;
+  const float* S; const float* basis;
+  TensorPlanes planes;
+  double* block_sums;  // [gridDim][4] = err2, ref2, (1-cos) sum, count
+};
+
+// ---- launchers (defined in the .hip files) --------------------------------
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+hipError_t launch_qprep(const QPrepParams& p, hipStream_t s);
+hipError_t launch_decode_split(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl,
+                               hipStream_t s, bool* supported);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_metric_scores(const MetricScoreParams& p, int kbits, int kqjl, int kside, hipStream_t s,
+                                bool* supported);
+hipError_t launch_metric_reduce(const MetricReduceParams& p, hipStream_t s);
+hipError_t launch_relerr(const RelErrParams& p, int nblocks, hipStream_t s);
+
+}  // namespace tq

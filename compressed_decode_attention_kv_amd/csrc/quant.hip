@@ -1,0 +1,376 @@
+// Write side of libtq: norm split, seeded sign flip + normalised
+// Walsh-Hadamard rotation, Beta Lloyd-Max index, bit packing, optional QJL
+// sketch or HeadQ side code.  Also the per-vector reconstruction error used
+// by tq_metrics (relMSE and direction error).
+//
+// [P1] = "Resumen Técnico: Inferencia Estadística y Medidas de Calidad de
+//        Cuantizaciones de Cache KV Inspiradas en TurboQuant"
+// [P2] = "Resumo Técnico: Ablação, Inferência Estatística e Validação para
+//        Compressão de KV-Cache"
+// [P3] = "Resumo Técnico: HeadQ: Distorção Visível ao Modelo e Correção no
+//        Espaço de Pontuação para Quantização de KV-Cache"
+#include "device_common.h"
+
+namespace tq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSteps = 4;            // wave steps per block
+constexpr int kMaxSideLds = 16384;   // floats of the rotated HeadQ basis in LDS
+
+// U'_h = Pi U_h = H D U_h / sqrt(d), column by column, into LDS as [d][rank].
+// The side code of [P3] section 3 projects the residual k - k_base on U_h;
+// with the residual held rotated, U'^T (Pi e) = U^T e gives the same value.
+__device__ void rotated_basis(const float* U, int d, int rank, const uint32_t* signbits,
+                              float inv_sqrt_d, float* lds) {
+  const int n = d * rank;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int k = i / rank;
+    const float s = ((signbits[k >> 5] >> (k & 31)) & 1u) ? -1.f : 1.f;
+    lds[i] = U[i] * s;
+  }
+  __syncthreads();
+  for (int h = 1; h < d; h <<= 1) {
+    for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
+      const int col = i % rank, pr = i / rank;           // pair index over k
+      const int lo = (pr / h) * 2 * h + (pr % h), hi = lo + h;
+      float a = lds[lo * rank + col], c = lds[hi * rank + col];
+      lds[lo * rank + col] = a + c;
+      lds[hi * rank + col] = a - c;
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < n; i += blockDim.x) lds[i] *= inv_sqrt_d;
+  __syncthreads();
+}
+
+template <int BITS, int MODE, typename TIN>
+__global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
+  // Residual staging of the QJL sketch: per wave, 64/L rows of d+1 floats
+  // (the +1 pad puts the rows of different vectors in different banks).
+  constexpr int kRowsFloats = 2048 + 64;
+  __shared__ float s_cent[16], s_bnd[16];
+  __shared__ float s_side[MODE == TQ_MODE_HEADQ ? kMaxSideLds : 1];
+  __shared__ float s_r[MODE == TQ_MODE_PROD ? 4 : 1][MODE == TQ_MODE_PROD ? kRowsFloats : 1];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int L = p.L, j = lane & (L - 1), slot = lane / L, vpw = 64 / L;
+  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int d = p.d;
+
+  if (threadIdx.x < 16) {
+    s_cent[threadIdx.x] = p.centroids[threadIdx.x];
+    s_bnd[threadIdx.x] = p.bounds[threadIdx.x];
+  }
+  if (MODE == TQ_MODE_HEADQ)
+    rotated_basis(p.basis + (size_t)h * d * p.rank, d, p.rank, p.signbits, p.inv_sqrt_d, s_side);
+  __syncthreads();
+
+  constexpr int NB = (1 << BITS) - 1;
+  const uint32_t myword = p.signbits[j];
+  const TIN* xbase = reinterpret_cast<const TIN*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const int64_t vbase = (int64_t)bh * p.T_cap;
+  const int tok_per_block = 4 * vpw * kSteps;
+
+  for (int step = 0; step < kSteps; ++step) {
+    const int t = blockIdx.x * tok_per_block + (step * 4 + wave) * vpw + slot;
+    const bool valid = t < p.T;
+    const int tc = valid ? t : p.T - 1;
+    float v[32];
+    load32<TIN>(xbase + (int64_t)tc * p.st + 32 * j, v);
+
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) ss = fmaf(v[e], v[e], ss);
+    ss = group_sum(ss, L);
+    const float nu = sqrtf(ss);
+    float inv;
+    if (MODE == TQ_MODE_PLAIN) {
+      inv = nu > 0.f ? 1.0f / nu : 0.f;
+    } else {
+      apply_signs(v, myword);
+      wht_group(v, j, L);
+      inv = nu > 0.f ? p.inv_sqrt_d / nu : 0.f;
+    }
+    uint32_t idx[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      v[e] *= inv;  // y: the rotated unit vector
+      uint32_t c = 0;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) c += (v[e] >= s_bnd[k]) ? 1u : 0u;
+      idx[e] = nu > 0.f ? c : 0u;
+    }
+    uint32_t w[BITS];
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) w[k] = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int bit = BITS * e, wi = bit >> 5, sh = bit & 31;
+      w[wi] |= idx[e] << sh;
+      if (sh + BITS > 32) w[wi + 1] |= idx[e] >> (32 - sh);
+    }
+    const int64_t vec = vbase + t;
+    if (valid) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vec * (d * BITS / 8)) + j * BITS;
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) dst[k] = w[k];
+      if (j == 0) p.norms[vec] = nu;
+    }
+
+    if (MODE == TQ_MODE_PROD) {
+      // Residual of the rotated unit vector and its 1-bit Gaussian sketch
+      // ([P1] "Esquemas de Cuantización" 2-3, "Contribuciones Clave" 1).
+      float g2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        v[e] = nu > 0.f ? v[e] - s_cent[idx[e]] : 0.f;
+        g2 = fmaf(v[e], v[e], g2);
+      }
+      g2 = group_sum(g2, L);
+      // Stage the residual of each vector of this wave in LDS: row = slot.
+      float* rrow = &s_r[wave][0];
+      const int rstride = d + 1;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 32; ++e) rrow[slot * rstride + 32 * j + e] = v[e];
+      __syncthreads();
+      uint32_t sw = 0;
+      for (int i = 0; i < 32; ++i) {
+        const float* srow = p.S + (size_t)(32 * j + i) * d;
+        float acc = 0.f;
+        for (int k = 0; k < d; ++k) acc = fmaf(srow[k], rrow[slot * rstride + k], acc);
+        sw |= (acc >= 0.f ? 1u : 0u) << i;
+      }
+      if (!(nu > 0.f)) sw = 0;
+      if (valid) {
+        reinterpret_cast<uint32_t*>(p.qjl + vec * (d / 8))[j] = sw;
+        if (j == 0) p.gamma[vec] = sqrtf(g2);
+      }
+    }
+
+    if (MODE == TQ_MODE_HEADQ) {
+      // e' = nu (y - c[idx]) = Pi (k - k_base); z = U'^T e' ([P3] section 3).
+      float z[32];
+      const int rank = p.rank;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) z[r] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float ep = nu > 0.f ? nu * (v[e] - s_cent[idx[e]]) : 0.f;
+        const float* urow = s_side + (32 * j + e) * rank;
+#pragma unroll
+        for (int r = 0; r < 32; ++r)
+          if (r < rank) z[r] = fmaf(urow[r], ep, z[r]);
+      }
+      float zmax = 0.f;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        if (r < rank) {
+          z[r] = group_sum(z[r], L);
+          zmax = fmaxf(zmax, fabsf(z[r]));
+        }
+      }
+      const int lev = (1 << (p.side_bits - 1)) - 1;
+      const float sz = zmax / (float)lev;
+      if (valid && j == 0) {
+        uint32_t sw[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sw[k] = 0;
+        const int sb = p.side_bits;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+          if (r < rank) {
+            int c = lev;
+            if (sz > 0.f) {
+              float q = rintf(z[r] / sz);
+              q = fminf(fmaxf(q, (float)-lev), (float)lev);
+              c = (int)q + lev;
+            }
+            const int bit = sb * r, wi = bit >> 5, sh = bit & 31;
+            sw[wi] |= (uint32_t)c << sh;
+            if (sh + sb > 32) sw[wi + 1] |= (uint32_t)c >> (32 - sh);
+          }
+        }
+        const int nbytes = rank * sb / 8;
+        uint8_t* dst = p.side + vec * nbytes;
+        for (int k = 0; k < nbytes; ++k) dst[k] = (uint8_t)(sw[k >> 2] >> (8 * (k & 3)));
+        p.side_scale[vec] = sz;
+      }
+    }
+  }
+}
+
+// Per-vector reconstruction error in the rotated domain, where
+// ||x - x_hat|| = ||Pi x - Pi x_hat|| and <x, x_hat> = <Pi x, Pi x_hat>
+// ([P2] "Configuração Experimental": relMSE and cosine direction error).
+template <int BITS, int MODE, typename TIN>
+__global__ __launch_bounds__(kThreads) void relerr_kernel(RelErrParams p) {
+  __shared__ float s_cent[16];
+  __shared__ float s_side[MODE == TQ_MODE_HEADQ ? kMaxSideLds : 1];
+  __shared__ double s_red[kThreads / 64][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int L = p.L, j = lane & (L - 1), slot = lane / L, vpw = 64 / L;
+  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int d = p.d;
+  if (threadIdx.x < 16) s_cent[threadIdx.x] = p.centroids[threadIdx.x];
+  if (MODE == TQ_MODE_HEADQ)
+    rotated_basis(p.basis + (size_t)h * d * p.rank, d, p.rank, p.signbits, p.inv_sqrt_d, s_side);
+  __syncthreads();
+
+  const TIN* xbase = reinterpret_cast<const TIN*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const int64_t vbase = (int64_t)bh * p.T_cap;
+  const int tok_per_block = 4 * vpw * kSteps;
+  double e2 = 0.0, r2 = 0.0, dsum = 0.0, cnt = 0.0;
+  for (int step = 0; step < kSteps; ++step) {
+    const int t = blockIdx.x * tok_per_block + (step * 4 + wave) * vpw + slot;
+    const bool valid = t < p.T;
+    const int tc = valid ? t : p.T - 1;
+    const int64_t vec = vbase + tc;
+    float a[32];
+    load32<TIN>(xbase + (int64_t)tc * p.st + 32 * j, a);
+    if (p.rotate) {
+      apply_signs(a, p.signbits[j]);
+      wht_group(a, j, L);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) a[e] *= p.inv_sqrt_d;
+    }
+    uint32_t w[BITS];
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(p.planes.codes + vec * (d * BITS / 8)) + j * BITS;
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) w[k] = cw[k];
+    const float nu = p.planes.norms[vec];
+    float ah[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) ah[e] = s_cent[code_at<BITS>(w, e)];
+    if (MODE == TQ_MODE_PROD) {
+      // y_hat += sqrt(pi/2)/m gamma S^T sigma
+      const float g = p.planes.gamma[vec] * p.qjl_c;
+      const uint32_t* sb = reinterpret_cast<const uint32_t*>(p.planes.qjl + vec * (d / 8));
+      for (int iw = 0; iw < d / 32; ++iw) {
+        const uint32_t bits = sb[iw];
+        for (int ib = 0; ib < 32; ++ib) {
+          const float sg = ((bits >> ib) & 1u) ? g : -g;
+          const float* srow = p.S + (size_t)(32 * iw + ib) * d + 32 * j;
+#pragma unroll
+          for (int e = 0; e < 32; ++e) ah[e] = fmaf(sg, srow[e], ah[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) ah[e] *= nu;
+    if (MODE == TQ_MODE_HEADQ) {
+      const int rank = p.rank, sbits = p.side_bits, lev = (1 << (sbits - 1)) - 1;
+      const float sz = p.planes.side_scale[vec];
+      const uint8_t* sc = p.planes.side + vec * (rank * sbits / 8);
+      for (int r = 0; r < rank; ++r) {
+        const int bit = sbits * r;
+        uint32_t raw = (uint32_t)sc[bit >> 3] | ((uint32_t)sc[(bit >> 3) + 1 < rank * sbits / 8 ? (bit >> 3) + 1 : (bit >> 3)] << 8);
+        const int code = (int)((raw >> (bit & 7)) & ((1u << sbits) - 1u));
+        const float zh = sz * (float)(code - lev);
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ah[e] = fmaf(s_side[(32 * j + e) * rank + r], zh, ah[e]);
+      }
+    }
+    float le2 = 0.f, lr2 = 0.f, ldot = 0.f, lh2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float df = a[e] - ah[e];
+      le2 = fmaf(df, df, le2);
+      lr2 = fmaf(a[e], a[e], lr2);
+      ldot = fmaf(a[e], ah[e], ldot);
+      lh2 = fmaf(ah[e], ah[e], lh2);
+    }
+    le2 = group_sum(le2, L); lr2 = group_sum(lr2, L);
+    ldot = group_sum(ldot, L); lh2 = group_sum(lh2, L);
+    if (valid && j == 0) {
+      e2 += le2; r2 += lr2;
+      if (lr2 > 0.f && lh2 > 0.f) {
+        dsum += 1.0 - (double)ldot / sqrt((double)lr2 * (double)lh2);
+        cnt += 1.0;
+      }
+    }
+  }
+  for (int m = 1; m < 64; m <<= 1) {
+    e2 += __shfl_xor(e2, m, 64); r2 += __shfl_xor(r2, m, 64);
+    dsum += __shfl_xor(dsum, m, 64); cnt += __shfl_xor(cnt, m, 64);
+  }
+  if (lane == 0) { s_red[wave][0] = e2; s_red[wave][1] = r2; s_red[wave][2] = dsum; s_red[wave][3] = cnt; }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    double s = 0.0;
+    for (int w = 0; w < kThreads / 64; ++w) s += s_red[w][threadIdx.x];
+    const size_t blk = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+    p.block_sums[blk * 4 + threadIdx.x] = s;
+  }
+}
+
+template <int BITS, int MODE>
+hipError_t launch_q(const QuantParams& p, hipStream_t s) {
+  const int vpw = 64 / p.L;
+  dim3 grid((p.T + 4 * vpw * kSteps - 1) / (4 * vpw * kSteps), p.B * p.H);
+  if (p.dtype == TQ_F16)
+    hipLaunchKernelGGL((quant_kernel<BITS, MODE, _Float16>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((quant_kernel<BITS, MODE, float>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int BITS, int MODE>
+hipError_t launch_r(const RelErrParams& p, hipStream_t s) {
+  const int vpw = 64 / p.L;
+  dim3 grid((p.T + 4 * vpw * kSteps - 1) / (4 * vpw * kSteps), p.B * p.H);
+  if (p.dtype == TQ_F16)
+    hipLaunchKernelGGL((relerr_kernel<BITS, MODE, _Float16>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((relerr_kernel<BITS, MODE, float>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int relerr_blocks(int T, int L, int BH) {
+  const int vpw = 64 / L;
+  return ((T + 4 * vpw * kSteps - 1) / (4 * vpw * kSteps)) * BH;
+}
+
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
+  switch (p.mode) {
+    case TQ_MODE_PLAIN:
+      switch (p.bits) { case 1: return launch_q<1, TQ_MODE_PLAIN>(p, s); case 2: return launch_q<2, TQ_MODE_PLAIN>(p, s);
+                        case 3: return launch_q<3, TQ_MODE_PLAIN>(p, s); case 4: return launch_q<4, TQ_MODE_PLAIN>(p, s); }
+      break;
+    case TQ_MODE_MSE:
+      switch (p.bits) { case 1: return launch_q<1, TQ_MODE_MSE>(p, s); case 2: return launch_q<2, TQ_MODE_MSE>(p, s);
+                        case 3: return launch_q<3, TQ_MODE_MSE>(p, s); case 4: return launch_q<4, TQ_MODE_MSE>(p, s); }
+      break;
+    case TQ_MODE_PROD:
+      switch (p.bits) { case 1: return launch_q<1, TQ_MODE_PROD>(p, s); case 2: return launch_q<2, TQ_MODE_PROD>(p, s);
+                        case 3: return launch_q<3, TQ_MODE_PROD>(p, s); }
+      break;
+    case TQ_MODE_HEADQ:
+      if (p.bits == 2) return launch_q<2, TQ_MODE_HEADQ>(p, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_relerr(const RelErrParams& p, int, hipStream_t s) {
+  switch (p.mode) {
+    case TQ_MODE_PLAIN:
+    case TQ_MODE_MSE:
+      switch (p.bits) { case 1: return launch_r<1, TQ_MODE_MSE>(p, s); case 2: return launch_r<2, TQ_MODE_MSE>(p, s);
+                        case 3: return launch_r<3, TQ_MODE_MSE>(p, s); case 4: return launch_r<4, TQ_MODE_MSE>(p, s); }
+      break;
+    case TQ_MODE_PROD:
+      switch (p.bits) { case 1: return launch_r<1, TQ_MODE_PROD>(p, s); case 2: return launch_r<2, TQ_MODE_PROD>(p, s);
+                        case 3: return launch_r<3, TQ_MODE_PROD>(p, s); }
+      break;
+    case TQ_MODE_HEADQ:
+      if (p.bits == 2) return launch_r<2, TQ_MODE_HEADQ>(p, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

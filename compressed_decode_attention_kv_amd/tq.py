@@ -1,0 +1,278 @@
+"""ctypes binding of libtq.so, the C-ABI library declared in include/tq.h.
+
+Argument marshalling only: every step of the quantiser and of the decode
+runs in the library's HIP kernels.  PyTorch supplies device memory and the
+current stream.  Importing this module loads libtq.so and raises if it is
+missing -- there is no CPU fallback.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libtq.so is not built (%s); run `python -m compressed_decode_attention_kv_amd.build`" % LIB_PATH)
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---- enums (include/tq.h) -------------------------------------------------------
+OK, EINVAL, EUNSUPPORTED, EMISMATCH, ENOMEM, EDEVICE = range(6)
+F32, F16 = 0, 1
+KEYS, VALUES = 0, 1
+MODE_PLAIN, MODE_MSE, MODE_PROD, MODE_HEADQ = range(4)
+SCHEMES = {"kv": 0, "tq-kv": 1, "kqv": 2, "qkqv": 3, "tq-qkv": 4, "headq": 5}
+
+EXPORTS = ["tq_abi_version", "tq_status_str", "tq_last_error", "tq_codebook_build", "tq_scheme_modes",
+           "tq_packed_layout", "tq_rotation_state", "tq_quantize", "tq_decode_workspace_size",
+           "tq_decode_attention", "tq_metrics_workspace_size", "tq_metrics", "tq_headq_fit",
+           "tq_release_cache"]
+
+
+class TensorDesc(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("B", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("code_bytes", ctypes.c_int32), ("qjl_bytes", ctypes.c_int32), ("side_bytes", ctypes.c_int32),
+                ("has_gamma", ctypes.c_int32), ("has_side_scale", ctypes.c_int32)]
+
+
+class HeadQ(ctypes.Structure):
+    _fields_ = [("basis", ctypes.c_void_p), ("rank", ctypes.c_int32), ("side_bits", ctypes.c_int32)]
+
+
+class Packed(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("T_cap", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("mode", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("side_rank", ctypes.c_int32), ("side_bits", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("qjl", ctypes.c_void_p),
+                ("gamma", ctypes.c_void_p), ("side", ctypes.c_void_p), ("side_scale", ctypes.c_void_p),
+                ("basis", ctypes.c_void_p)]
+
+
+class MetricsOut(ctypes.Structure):
+    _fields_ = [("kl_mean", ctypes.c_double), ("kl_max", ctypes.c_double), ("top5_recall", ctypes.c_double),
+                ("relmse_k", ctypes.c_double), ("relmse_v", ctypes.c_double), ("dir_err_k", ctypes.c_double),
+                ("dir_err_v", ctypes.c_double), ("n_queries", ctypes.c_int64)]
+
+
+_P = ctypes.POINTER
+_sigs = {
+    "tq_abi_version": ([], ctypes.c_int32),
+    "tq_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "tq_last_error": ([], ctypes.c_char_p),
+    "tq_codebook_build": ([ctypes.c_int32, ctypes.c_int32, _P(ctypes.c_double), _P(ctypes.c_double)], ctypes.c_int),
+    "tq_scheme_modes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P(ctypes.c_int32), _P(ctypes.c_int32)], ctypes.c_int),
+    "tq_packed_layout": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P(Layout)], ctypes.c_int),
+    "tq_rotation_state": ([ctypes.c_uint64, ctypes.c_int32, _P(ctypes.c_float), _P(ctypes.c_float)], ctypes.c_int),
+    "tq_quantize": ([_P(TensorDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64, _P(HeadQ),
+                     _P(Packed), ctypes.c_void_p], ctypes.c_int),
+    "tq_decode_workspace_size": ([_P(Packed), _P(Packed), ctypes.c_int32, _P(ctypes.c_size_t)], ctypes.c_int),
+    "tq_decode_attention": ([_P(TensorDesc), _P(Packed), _P(Packed), ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "tq_metrics_workspace_size": ([_P(TensorDesc), _P(Packed), _P(Packed), _P(ctypes.c_size_t)], ctypes.c_int),
+    "tq_metrics": ([_P(TensorDesc), _P(TensorDesc), _P(TensorDesc), _P(Packed), _P(Packed), _P(MetricsOut),
+                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "tq_headq_fit": ([_P(ctypes.c_float), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P(ctypes.c_float)], ctypes.c_int),
+    "tq_release_cache": ([], ctypes.c_int),
+}
+for _name, (_args, _res) in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+
+class TQError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (_lib.tq_status_str(status).decode(), msg))
+        self.status = status
+
+
+def _check(status):
+    if status != OK:
+        raise TQError(status, _lib.tq_last_error().decode())
+
+
+def lib():
+    return _lib
+
+
+# ---- host-only calls ---------------------------------------------------------------
+def codebook_build(d, bits):
+    c = np.zeros(1 << bits, dtype=np.float64)
+    t = np.zeros((1 << bits) - 1, dtype=np.float64)
+    _check(_lib.tq_codebook_build(d, bits, c.ctypes.data_as(_P(ctypes.c_double)), t.ctypes.data_as(_P(ctypes.c_double))))
+    return c, t
+
+
+def scheme_modes(scheme, n_bits, which):
+    m, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.tq_scheme_modes(SCHEMES.get(scheme, scheme), n_bits, which, ctypes.byref(m), ctypes.byref(b)))
+    return m.value, b.value
+
+
+def packed_layout(d, mode, bits, side_rank=0, side_bits=0):
+    lay = Layout()
+    _check(_lib.tq_packed_layout(d, mode, bits, side_rank, side_bits, ctypes.byref(lay)))
+    return lay
+
+
+def rotation_state(seed, d):
+    s = np.zeros(d, dtype=np.float32)
+    S = np.zeros((d, d), dtype=np.float32)
+    _check(_lib.tq_rotation_state(seed, d, s.ctypes.data_as(_P(ctypes.c_float)), S.ctypes.data_as(_P(ctypes.c_float))))
+    return s, S
+
+
+def headq_fit(calib, rank):
+    calib = np.ascontiguousarray(calib, dtype=np.float32)
+    N, d = calib.shape
+    U = np.zeros((d, rank), dtype=np.float32)
+    _check(_lib.tq_headq_fit(calib.ctypes.data_as(_P(ctypes.c_float)), N, d, rank, U.ctypes.data_as(_P(ctypes.c_float))))
+    return U
+
+
+# ---- device calls ------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def tensor_desc(t):
+    """Descriptor of a device tensor shaped [B, H, T, d] (or [B, Hq, d] for
+    queries) whose last dimension is contiguous."""
+    torch = _torch()
+    if t.dim() == 3:
+        t = t.unsqueeze(2)
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected [B, H, T, d] with a contiguous last dimension")
+    if t.dtype == torch.float16:
+        dt = F16
+    elif t.dtype == torch.float32:
+        dt = F32
+    else:
+        raise ValueError("dtype must be float16 or float32")
+    B, H, T, d = t.shape
+    return TensorDesc(t.data_ptr(), dt, B, H, T, d, t.stride(0), t.stride(1), t.stride(2)), t
+
+
+class PackedTensor:
+    """Device planes of one packed tensor (K or V) plus its C descriptor.
+    The planes are torch tensors owned by this object."""
+
+    def __init__(self, B, H, T_cap, d, mode, bits, side_rank=0, side_bits=0, device="cuda"):
+        torch = _torch()
+        lay = packed_layout(d, mode, bits, side_rank, side_bits)
+        n = B * H * T_cap
+        self.layout = lay
+
+        def plane(nbytes):
+            # 16-byte aligned (torch allocations are 256-byte aligned).
+            return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+        self.codes = plane(n * lay.code_bytes)
+        self.norms = plane(n * 4)
+        self.qjl = plane(n * lay.qjl_bytes) if lay.qjl_bytes else None
+        self.gamma = plane(n * 4) if lay.has_gamma else None
+        self.side = plane(n * lay.side_bytes) if lay.side_bytes else None
+        self.side_scale = plane(n * 4) if lay.has_side_scale else None
+        self.basis = None
+        self.c = Packed()
+        self.c.T_cap = T_cap
+        self.c.codes = self.codes.data_ptr()
+        self.c.norms = self.norms.data_ptr()
+        self.c.qjl = self.qjl.data_ptr() if self.qjl is not None else None
+        self.c.gamma = self.gamma.data_ptr() if self.gamma is not None else None
+        self.c.side = self.side.data_ptr() if self.side is not None else None
+        self.c.side_scale = self.side_scale.data_ptr() if self.side_scale is not None else None
+
+    @property
+    def n(self):
+        return self.c.B * self.c.H * self.c.T_cap
+
+    def planes(self):
+        """Host copies (numpy) of the planes, shaped per vector."""
+        n = self.n
+        out = {"codes": self.codes[: n * self.layout.code_bytes].cpu().numpy().reshape(n, -1),
+               "norms": self.norms[: n * 4].cpu().numpy().view(np.float32).copy()}
+        if self.qjl is not None:
+            out["qjl"] = self.qjl[: n * self.layout.qjl_bytes].cpu().numpy().reshape(n, -1)
+            out["gamma"] = self.gamma[: n * 4].cpu().numpy().view(np.float32).copy()
+        if self.side is not None:
+            out["side"] = self.side[: n * self.layout.side_bytes].cpu().numpy().reshape(n, -1)
+            out["side_scale"] = self.side_scale[: n * 4].cpu().numpy().view(np.float32).copy()
+        return out
+
+
+def quantize(x, which, scheme, n_bits, seed=0, basis=None, rank=16, side_bits=4, T_cap=None):
+    """Quantise x [B, H, T, d] (device, fp16/fp32) into a new PackedTensor."""
+    desc, x4 = tensor_desc(x)
+    mode, bits = scheme_modes(scheme, n_bits, which)
+    hq = None
+    if mode == MODE_HEADQ:
+        if basis is None:
+            raise ValueError("HeadQ keys need a basis [H, d, rank]")
+        rank = basis.shape[-1]
+        hq = HeadQ(basis.data_ptr(), rank, side_bits)
+    pt = PackedTensor(desc.B, desc.H, T_cap or desc.T, desc.d, mode, bits,
+                      rank if hq else 0, side_bits if hq else 0, device=x.device)
+    pt.basis = basis
+    _check(_lib.tq_quantize(ctypes.byref(desc), which, SCHEMES.get(scheme, scheme), n_bits, seed,
+                            ctypes.byref(hq) if hq else None, ctypes.byref(pt.c), _stream()))
+    pt._keep = x4
+    return pt
+
+
+def decode_workspace_size(kp, vp, Hq):
+    n = ctypes.c_size_t()
+    _check(_lib.tq_decode_workspace_size(ctypes.byref(kp.c), ctypes.byref(vp.c), Hq, ctypes.byref(n)))
+    return n.value
+
+
+def decode_attention(q, kp, vp, out=None, lse=None, ws=None):
+    """out [B, Hq, d] fp32 = softmax attention of q [B, Hq, d] over the packed
+    cache.  Returns (out, lse)."""
+    torch = _torch()
+    desc, q4 = tensor_desc(q)
+    B, Hq, d = desc.B, desc.H, desc.d
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_size(kp, vp, Hq)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(_lib.tq_decode_attention(ctypes.byref(desc), ctypes.byref(kp.c), ctypes.byref(vp.c), out.data_ptr(),
+                                    lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    return out, lse
+
+
+def metrics(q=None, k_ref=None, v_ref=None, kp=None, vp=None):
+    """Quality measures (synchronous).  Returns a dict."""
+    torch = _torch()
+    dq = tensor_desc(q)[0] if q is not None else None
+    dk = tensor_desc(k_ref)[0] if k_ref is not None else None
+    dv = tensor_desc(v_ref)[0] if v_ref is not None else None
+    n = ctypes.c_size_t()
+    _check(_lib.tq_metrics_workspace_size(ctypes.byref(dq) if dq else None, ctypes.byref(kp.c) if kp else None,
+                                          ctypes.byref(vp.c) if vp else None, ctypes.byref(n)))
+    dev = (q if q is not None else (k_ref if k_ref is not None else v_ref)).device
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    res = MetricsOut()
+    _check(_lib.tq_metrics(ctypes.byref(dq) if dq else None, ctypes.byref(dk) if dk else None,
+                           ctypes.byref(dv) if dv else None, ctypes.byref(kp.c) if kp else None,
+                           ctypes.byref(vp.c) if vp else None, ctypes.byref(res), ws.data_ptr(), ws.numel(),
+                           _stream()))
+    return {f: getattr(res, f) for f, _ in MetricsOut._fields_}
+
+
+def release_cache():
+    _check(_lib.tq_release_cache())

@@ -42,12 +42,14 @@ def side_levels(side_bits):
     return (1 << (side_bits - 1)) - 1
 
 
-def quantize(X, U, st_base, side_bits=4, side_quantizer=True):
+def quantize(X, U, st_base, side_bits=4, side_quantizer=True, flip_codes=None, flip_side=None, band=1e-6):
     """X [N, d]; U [d, r]; st_base: an MSE QState (bits = 2).
     Returns base fields, side codes, scale and the effective dense key
-    k_hat = k_base + U z_hat that enters every score."""
+    k_hat = k_base + U z_hat that enters every score.  flip_codes /
+    flip_side select decisions within `band` of their boundary that take the
+    other valid outcome (base index, or the rounding of z / s_z)."""
     X = np.asarray(X, dtype=np.float64)
-    base = qz.quantize(X, st_base)
+    base = qz.quantize(X, st_base, flip_codes=flip_codes, band=band)
     kbase = qz.dequantize(base, st_base)
     E = X - kbase
     Z = E @ U
@@ -58,10 +60,15 @@ def quantize(X, U, st_base, side_bits=4, side_quantizer=True):
         ratio = Z / safe[:, None]
         code = np.clip(np.rint(ratio), -L, L).astype(np.int64) + L
         code[s == 0] = L
+        frac = np.abs(ratio) - np.floor(np.abs(ratio))
+        hdist = np.abs(frac - 0.5)  # distance to the rounding boundary, in steps
+        if flip_side is not None and np.any(flip_side):
+            assert np.all(hdist[flip_side] <= band), "side flip requested outside the band"
+            lo = np.floor(ratio[flip_side]).astype(np.int64) + L
+            cur = code[flip_side]
+            code[flip_side] = np.where(cur == lo, lo + 1, lo)
         s32 = s.astype(np.float32).astype(np.float64)
         Zhat = s32[:, None] * (code - L)
-        frac = np.abs(ratio) - np.floor(np.abs(ratio))
-        hdist = np.abs(frac - 0.5) * s[:, None]
     else:
         s, code, Zhat, hdist = None, None, Z, None
     return {"base": base, "kbase": kbase, "z": Z, "side_scale": s,

@@ -54,10 +54,30 @@ def stored(v):
     return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
-def quantize(X, st):
+def other_side(Y, idx, boundaries, mask, band):
+    """For coordinates in `mask` (each within `band` of a decision boundary),
+    the index of the cell on the other side of that boundary.  A coordinate
+    this close to a boundary has two valid codes; this is the second one."""
+    idx = idx.copy()
+    if not np.any(mask):
+        return idx
+    y = Y[mask]
+    k = np.argmin(np.abs(y[:, None] - boundaries[None, :]), axis=1)
+    assert np.all(np.abs(y - boundaries[k]) <= band), "flip requested outside the decision band"
+    cur = idx[mask]
+    assert np.all((cur == k) | (cur == k + 1))
+    idx[mask] = np.where(cur == k, k + 1, k)
+    return idx
+
+
+def quantize(X, st, flip_codes=None, flip_signs=None, band=1e-6):
     """X: [N, d] float64.  Returns a dict of unpacked fields plus the
     parity-band diagnostics (distance of y to its nearest boundary, and
-    |(S r)_i| / ||r|| for the sign bits)."""
+    |(S r)_i| / ||r|| for the sign bits).
+
+    flip_codes / flip_signs ([N, d] / [N, m] boolean, optional) select
+    decisions taken within `band` of their boundary; those take the other
+    valid outcome, and everything downstream (residual, sketch) follows."""
     X = np.asarray(X, dtype=np.float64)
     N, d = X.shape
     nu = np.sqrt(np.sum(X * X, axis=1))
@@ -65,6 +85,8 @@ def quantize(X, st):
     U = X / safe[:, None]
     Y = U @ st.Pi.T
     idx = cb.quantize_index(Y, st.boundaries)
+    if flip_codes is not None:
+        idx = other_side(Y, idx, st.boundaries, flip_codes, band)
     zero = nu == 0
     idx[zero] = 0
     out = {"nu": nu, "idx": idx, "y": Y,
@@ -76,10 +98,14 @@ def quantize(X, st):
         bits = (P >= 0).astype(np.int64)
         gamma[zero] = 0.0
         bits[zero] = 0
+        g = np.where(gamma > 0, gamma, 1.0)
+        sdist = np.where(zero[:, None], np.inf, np.abs(P) / g[:, None])
+        if flip_signs is not None and np.any(flip_signs):
+            assert np.all(sdist[flip_signs] <= band), "sign flip requested outside the band"
+            bits[flip_signs] = 1 - bits[flip_signs]
         out["gamma"] = gamma
         out["sign_bits"] = bits
-        g = np.where(gamma > 0, gamma, 1.0)
-        out["sdist"] = np.where(zero[:, None], np.inf, np.abs(P) / g[:, None])
+        out["sdist"] = sdist
     return out
 
 

@@ -1,0 +1,154 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+symbol include/tq.h declares, its host-only functions agree with the oracle,
+and every validation error is returned before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import codebook as ocb
+from oracle import headq as ohq
+from oracle import rng as orng
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|tq_status|int32_t)\s+(tq_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(tqlib):
+    names = _declared()
+    assert len(names) >= 14
+    lib = ctypes.CDLL(tqlib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(tqlib.EXPORTS) == names
+    assert tqlib.lib().tq_abi_version() == 1
+
+
+@pytest.mark.parametrize("d,bits", [(32, 1), (128, 2), (128, 3), (128, 4), (1024, 2), (1024, 4)])
+def test_codebook_matches_oracle(tqlib, d, bits):
+    c, t = tqlib.codebook_build(d, bits)
+    oc, ot = ocb.lloyd_max(d, bits)
+    # Both are Lloyd fixed points computed independently (continued-fraction
+    # incomplete beta here, scipy's betainc in the oracle); they agree far
+    # inside the 1e-6 decision band.
+    assert np.max(np.abs(c - oc)) < 2e-12
+    assert np.max(np.abs(t - ot)) < 2e-12
+    # The fp32 boundaries the kernels compare against are identical.
+    assert np.array_equal(t.astype(np.float32), ot.astype(np.float32))
+
+
+@pytest.mark.parametrize("seed,d", [(0, 32), (0, 128), (12345, 128), (2**63 + 7, 256), (3, 1024)])
+def test_rotation_state_matches_oracle(tqlib, seed, d):
+    s, S = tqlib.rotation_state(seed, d)
+    assert np.array_equal(s.astype(np.float64), orng.sign_vector(seed, d))
+    assert np.array_equal(S.astype(np.float64), orng.gaussian_sketch(seed, d))
+
+
+def test_scheme_modes_table(tqlib):
+    K, V = tqlib.KEYS, tqlib.VALUES
+    P, M, Q, H = tqlib.MODE_PLAIN, tqlib.MODE_MSE, tqlib.MODE_PROD, tqlib.MODE_HEADQ
+    assert tqlib.scheme_modes("kv", 4, K) == (P, 4) and tqlib.scheme_modes("kv", 4, V) == (P, 4)
+    assert tqlib.scheme_modes("tq-kv", 3, K) == (M, 3)
+    assert tqlib.scheme_modes("kqv", 4, K) == (M, 4) and tqlib.scheme_modes("kqv", 4, V) == (Q, 3)
+    assert tqlib.scheme_modes("qkqv", 4, K) == (Q, 3) and tqlib.scheme_modes("qkqv", 2, V) == (Q, 1)
+    assert tqlib.scheme_modes("tq-qkv", 3, K) == (Q, 2) and tqlib.scheme_modes("tq-qkv", 3, V) == (M, 3)
+    assert tqlib.scheme_modes("headq", 4, K) == (H, 2) and tqlib.scheme_modes("headq", 4, V) == (M, 4)
+
+
+def test_layouts(tqlib):
+    lay = tqlib.packed_layout(128, tqlib.MODE_PROD, 3)
+    assert (lay.code_bytes, lay.qjl_bytes, lay.has_gamma) == (48, 16, 1)
+    lay = tqlib.packed_layout(128, tqlib.MODE_MSE, 4)
+    assert (lay.code_bytes, lay.qjl_bytes, lay.has_gamma, lay.side_bytes) == (64, 0, 0, 0)
+    lay = tqlib.packed_layout(128, tqlib.MODE_HEADQ, 2, 16, 4)
+    assert (lay.code_bytes, lay.side_bytes, lay.has_side_scale) == (32, 8, 1)
+    lay = tqlib.packed_layout(1024, tqlib.MODE_PROD, 3)
+    assert (lay.code_bytes, lay.qjl_bytes) == (384, 128)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(d=48), dict(d=2048), dict(d=16), dict(n_bits=0), dict(n_bits=5),
+    dict(scheme="kqv", which=1, n_bits=1), dict(scheme=99), dict(which=7),
+    dict(dtype=9), dict(T=0), dict(B=0), dict(align=8), dict(stride_t=10),
+    dict(no_codes=True), dict(scheme="kqv", which=1, no_qjl=True),
+    dict(scheme="headq", which=0, no_hq=True), dict(scheme="tq-kv", which=0, give_hq=True),
+    dict(scheme="headq", which=0, hq_rank=12), dict(scheme="headq", which=0, hq_bits=1),
+    dict(T_cap=3),
+])
+def test_quantize_rejects_before_any_gpu_call(tqlib, bad):
+    """Fake (never dereferenced) but aligned pointers: every case must be
+    rejected by host validation, so no HIP call is made."""
+    fake = 1 << 20
+    d = bad.get("d", 128)
+    desc = tqlib.TensorDesc(fake + bad.get("align", 0), bad.get("dtype", tqlib.F16), bad.get("B", 1), 2,
+                            bad.get("T", 8), d, 2 * 8 * d, 8 * d, bad.get("stride_t", d))
+    out = tqlib.Packed()
+    out.T_cap = bad.get("T_cap", 0)
+    out.codes = None if bad.get("no_codes") else fake
+    out.norms = fake
+    out.qjl = None if bad.get("no_qjl") else fake
+    out.gamma = fake
+    out.side = fake
+    out.side_scale = fake
+    hq = None
+    scheme = bad.get("scheme", "tq-kv")
+    if (scheme == "headq" and not bad.get("no_hq")) or bad.get("give_hq"):
+        hq = tqlib.HeadQ(fake, bad.get("hq_rank", 16), bad.get("hq_bits", 4))
+    sid = tqlib.SCHEMES.get(scheme, scheme)
+    st = tqlib.lib().tq_quantize(ctypes.byref(desc), bad.get("which", 0), sid, bad.get("n_bits", 4), 0,
+                                 ctypes.byref(hq) if hq else None, ctypes.byref(out), None)
+    assert st in (tqlib.EINVAL, tqlib.EUNSUPPORTED), st
+    assert tqlib.lib().tq_last_error().decode()
+
+
+def _packed(tqlib, mode, bits, B=1, H=2, T=8, d=128, fake=1 << 20):
+    p = tqlib.Packed(B, H, T, T, d, mode, bits, 0, 0, 0, fake, fake, fake, fake, fake, fake, fake)
+    return p
+
+
+def test_decode_rejects_mismatches(tqlib):
+    lib = tqlib.lib()
+    fake = 1 << 20
+    k = _packed(tqlib, tqlib.MODE_MSE, 4)
+    v = _packed(tqlib, tqlib.MODE_PROD, 3, T=9)
+    n = ctypes.c_size_t()
+    assert lib.tq_decode_workspace_size(ctypes.byref(k), ctypes.byref(v), 2, ctypes.byref(n)) == tqlib.EMISMATCH
+    v = _packed(tqlib, tqlib.MODE_PROD, 3)
+    assert lib.tq_decode_workspace_size(ctypes.byref(k), ctypes.byref(v), 3, ctypes.byref(n)) == tqlib.EMISMATCH
+    assert lib.tq_decode_workspace_size(ctypes.byref(k), ctypes.byref(v), 4, ctypes.byref(n)) == tqlib.OK
+    assert n.value > 0 and n.value % 256 == 0
+    q = tqlib.TensorDesc(fake, tqlib.F16, 1, 4, 1, 64, 4 * 64, 64, 64)   # wrong d
+    out = fake
+    assert lib.tq_decode_attention(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), out, None, fake,
+                                   n.value, None) == tqlib.EMISMATCH
+    q = tqlib.TensorDesc(fake, tqlib.F16, 1, 4, 1, 128, 4 * 128, 128, 128)
+    assert lib.tq_decode_attention(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), out, None, fake,
+                                   n.value - 256, None) == tqlib.ENOMEM
+    assert lib.tq_decode_attention(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), out, None, fake + 16,
+                                   n.value, None) == tqlib.EINVAL
+    hv = _packed(tqlib, tqlib.MODE_HEADQ, 2)
+    assert lib.tq_decode_workspace_size(ctypes.byref(k), ctypes.byref(hv), 4, ctypes.byref(n)) != tqlib.OK
+    # A hand-made PROD header with 4 index bits has no kernel: rejected before launch.
+    k4 = _packed(tqlib, tqlib.MODE_PROD, 4)
+    assert lib.tq_decode_workspace_size(ctypes.byref(k4), ctypes.byref(v), 4, ctypes.byref(n)) == tqlib.OK
+    assert lib.tq_decode_attention(ctypes.byref(q), ctypes.byref(k4), ctypes.byref(v), out, None, fake,
+                                   1 << 30, None) == tqlib.EUNSUPPORTED
+
+
+def test_headq_fit_matches_oracle_projector(tqlib):
+    rng = np.random.default_rng(0)
+    d, r = 128, 16
+    scales = 0.8 ** np.arange(d)
+    X = (rng.standard_normal((3000, d)) * scales + 0.5).astype(np.float32)
+    U = tqlib.headq_fit(X, r)
+    Uo, _ = ohq.fit_basis(X.astype(np.float64), r)
+    assert np.max(np.abs(U.T @ U - np.eye(r))) < 1e-5
+    assert np.max(np.abs(U @ U.T - Uo @ Uo.T)) < 1e-4
+    # Same sign convention, so the columns agree too (eigenvalues well separated).
+    assert np.max(np.abs(U - Uo)) < 1e-3

@@ -140,3 +140,32 @@ def test_jensen_amplification():
     for sig in (0.1, 0.5, 1.0):
         e = np.exp(rng.standard_normal(400000) * sig)
         assert abs(e.mean() / math.exp(sig * sig / 2) - 1) < 4 * e.std() / math.sqrt(e.size)
+
+
+def test_in_band_flip_takes_the_other_cell():
+    """A coordinate placed exactly on a boundary has two valid codes; the
+    flip selects the neighbour across that boundary and the sketch of the
+    residual follows; a flip far from any boundary is refused."""
+    d = 32
+    st = qz.QState(d, qz.PROD, 3, seed=4)
+    x = np.random.default_rng(1).standard_normal((1, d))
+    q0 = qz.quantize(x, st)
+    # Move coordinate 5 of y exactly onto boundary 1 and map back.
+    y = q0["y"][0].copy()
+    y[5] = st.boundaries[1]
+    xb = (y @ st.Pi)[None, :] * 3.0
+    q = qz.quantize(xb, st)
+    mask = np.zeros((1, d), bool)
+    mask[0, 5] = True
+    assert q["bdist"][0, 5] < 1e-12
+    qf = qz.quantize(xb, st, flip_codes=mask)
+    assert {int(q["idx"][0, 5]), int(qf["idx"][0, 5])} == {1, 2}
+    assert np.array_equal(np.delete(q["idx"], 5, axis=1), np.delete(qf["idx"], 5, axis=1))
+    # On the midpoint the residual coordinate only changes sign (same gamma),
+    # so the sketch of the residual changes.
+    assert abs(q["gamma"][0] - qf["gamma"][0]) < 1e-12
+    assert np.any(q["sign_bits"] != qf["sign_bits"])
+    far = np.zeros((1, d), bool)
+    far[0, np.argmax(q["bdist"][0])] = True
+    with pytest.raises(AssertionError):
+        qz.quantize(xb, st, flip_codes=far)

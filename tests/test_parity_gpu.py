@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle on
+the same seeded inputs.  Bar: codes and sign bits bit-exact outside the 1e-6
+decision band (in-band mismatches counted, < 1e-5 of all); attention outputs
+within 1e-3 relative L2 per query; KL within 1e-5 absolute."""
+import math
+
+import numpy as np
+import pytest
+
+from compressed_decode_attention_kv_amd import synth
+from oracle import quantizer as oqz
+from oracle import metrics as ome
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from compressed_decode_attention_kv_amd import tq as lib
+    return lib
+
+
+def _dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def _run_case(tq, K, V, Q, scheme, n, seed=0, U=None, dtype=torch.float32, label=""):
+    """K, V [B, H, T, d], Q [B, H*G, d] (numpy).  Quantise and decode on the
+    GPU, run the oracle per (b, h), compare everything."""
+    B, H, T, d = K.shape
+    Hq = Q.shape[1]
+    G = Hq // H
+    Kd, Vd, Qd = _dev(K, dtype), _dev(V, dtype), _dev(Q, dtype)
+    # The oracle sees exactly the values the GPU sees.
+    Kh_in = Kd.double().cpu().numpy()
+    Vh_in = Vd.double().cpu().numpy()
+    Qh_in = Qd.double().cpu().numpy()
+    basis = _dev(U.astype(np.float32)) if U is not None else None
+    kp = tq.quantize(Kd, tq.KEYS, scheme, n, seed, basis=basis)
+    vp = tq.quantize(Vd, tq.VALUES, scheme, n, seed)
+    out, lse = tq.decode_attention(Qd, kp, vp)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    kplanes, vplanes = kp.planes(), vp.planes()
+    kmode, vmode = pu.MODE_NAMES[kp.c.mode], pu.MODE_NAMES[vp.c.mode]
+    n_band, n_dec = 0, 0
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            sl = slice((b * H + h) * T, (b * H + h + 1) * T)
+            Uh = U[h] if U is not None else None
+            _, Khat, _, nb1, nd1 = pu.oracle_match(Kh_in[b, h], {k: v[sl] for k, v in kplanes.items()}, kmode,
+                                                   kp.c.bits, seed, U=Uh, label=label + " K")
+            _, Vhat, _, nb2, nd2 = pu.oracle_match(Vh_in[b, h], {k: v[sl] for k, v in vplanes.items()}, vmode,
+                                                   vp.c.bits, seed, label=label + " V")
+            n_band += nb1 + nb2
+            n_dec += nd1 + nd2
+            qs = Qh_in[b, h * G:(h + 1) * G]
+            o_ref, lse_ref, _ = pu.oracle_decode(qs, Khat, Vhat)
+            err = pu.rel_l2(out[b, h * G:(h + 1) * G], o_ref)
+            worst = max(worst, float(err.max()))
+            assert np.all(err <= pu.OUT_RTOL), "%s: output rel L2 %.3g at b=%d h=%d" % (label, err.max(), b, h)
+            assert np.allclose(lse[b, h * G:(h + 1) * G], lse_ref, atol=2e-4, rtol=1e-5), label + " lse"
+    assert n_band <= max(1, pu.MAX_BAND_FRACTION * n_dec), "%s: %d in-band mismatches of %d" % (label, n_band, n_dec)
+    return worst, n_band, kp, vp, (Kd, Vd, Qd)
+
+
+def test_config1_kqv_full(tq):
+    """Single head, d=128, T=4096, fp32 N(0,1), 16 queries, KQV at n=4."""
+    K, V, Q = synth.isotropic_small(seed=0)
+    worst, n_band, kp, vp, (Kd, Vd, Qd) = _run_case(tq, K, V, Q, "kqv", 4, seed=0, label="cfg1")
+    print("config1 worst rel L2 %.3g, in-band mismatches %d" % (worst, n_band))
+    # Metrics vs the oracle.
+    m = tq.metrics(Qd, Kd, Vd, kp, vp)
+    Kf, Vf, Qf = K[0, 0].astype(np.float64), V[0, 0].astype(np.float64), Q[0].astype(np.float64)
+    _, Khat, _, _, _ = pu.oracle_match(Kf, kp.planes(), oqz.MSE, 4, 0)
+    _, Vhat, _, _, _ = pu.oracle_match(Vf, vp.planes(), oqz.PROD, 3, 0)
+    kl, rec, s, sh = pu.kl_and_recall(Qf, Kf, Khat)
+    assert abs(m["kl_mean"] - kl.mean()) <= pu.KL_ATOL
+    assert abs(m["kl_max"] - kl.max()) <= pu.KL_ATOL
+    amb = pu.top5_ambiguous(sh).sum() + pu.top5_ambiguous(s).sum()
+    assert abs(m["top5_recall"] - rec.mean()) <= amb / (5.0 * len(rec)) + 1e-12
+    assert abs(m["relmse_k"] - ome.rel_mse(Kf, Khat)) <= 1e-5 * ome.rel_mse(Kf, Khat)
+    assert abs(m["relmse_v"] - ome.rel_mse(Vf, Vhat)) <= 1e-5 * ome.rel_mse(Vf, Vhat)
+    assert abs(m["dir_err_k"] - ome.direction_error(Kf, Khat)) <= 1e-5
+    assert abs(m["dir_err_v"] - ome.direction_error(Vf, Vhat)) <= 1e-5
+    assert m["n_queries"] == 16
+
+
+@pytest.mark.parametrize("scheme", ["kv", "tq-kv", "kqv", "qkqv", "tq-qkv"])
+@pytest.mark.parametrize("n", [2, 3, 4])
+def test_schemes_ragged_gqa(tq, scheme, n):
+    """Every preset and budget; T=1000 (ragged tail), B=2, H=2, 3 queries per
+    KV head, fp16 inputs."""
+    K, V, Q = synth.isotropic(2, 2, 3, 1000, 128, seed=10 + n, kv_std=1.0, dtype=np.float32)
+    worst, n_band, *_ = _run_case(tq, K, V, Q, scheme, n, seed=n, dtype=torch.float16, label=scheme)
+    print(scheme, n, "worst rel L2 %.3g band %d" % (worst, n_band))
+
+
+@pytest.mark.parametrize("d", [32, 64, 256, 1024])
+@pytest.mark.parametrize("scheme", ["kqv", "qkqv", "kv"])
+def test_head_dims(tq, d, scheme):
+    T = 700 if d < 1024 else 300
+    K, V, Q = synth.isotropic(1, 2, 2, T, d, seed=d, kv_std=1.0, dtype=np.float32)
+    _run_case(tq, K, V, Q, scheme, 4, seed=5, label="%s d=%d" % (scheme, d))
+
+
+def test_single_token_and_zero_vectors(tq):
+    K, V, Q = synth.isotropic(1, 1, 4, 1, 128, seed=1, kv_std=1.0, dtype=np.float32)
+    _run_case(tq, K, V, Q, "kqv", 4, label="T=1")
+    K, V, Q = synth.isotropic(1, 2, 2, 300, 128, seed=2, kv_std=1.0, dtype=np.float32)
+    K[0, 0, ::7] = 0.0
+    V[0, 1, ::5] = 0.0
+    _, _, kp, vp, _ = _run_case(tq, K, V, Q, "qkqv", 4, label="zeros")
+    pl = kp.planes()
+    z = np.arange(0, 300, 7)
+    assert np.all(pl["codes"][z] == 0) and np.all(pl["qjl"][z] == 0) and np.all(pl["gamma"][z] == 0)
+
+
+def test_strided_input_and_large_values(tq):
+    base = np.random.default_rng(3).standard_normal((1, 2, 400, 256)).astype(np.float32) * 300.0
+    Kd = torch.from_numpy(base).cuda()[..., :128]       # row stride 256
+    Vd = torch.from_numpy(base[..., 128:].copy()).cuda()
+    Q = np.random.default_rng(4).standard_normal((1, 2, 128)).astype(np.float32) * 0.01
+    kp = tq.quantize(Kd, tq.KEYS, "kqv", 4, 9)
+    vp = tq.quantize(Vd, tq.VALUES, "kqv", 4, 9)
+    out, _ = tq.decode_attention(torch.from_numpy(Q).cuda(), kp, vp)
+    out = out.cpu().numpy()
+    Kn = Kd.double().cpu().numpy()
+    Vn = Vd.double().cpu().numpy()
+    for h in range(2):
+        sl = slice(h * 400, (h + 1) * 400)
+        _, Khat, _, _, _ = pu.oracle_match(Kn[0, h], {k: v[sl] for k, v in kp.planes().items()}, oqz.MSE, 4, 9)
+        _, Vhat, _, _, _ = pu.oracle_match(Vn[0, h], {k: v[sl] for k, v in vp.planes().items()}, oqz.PROD, 3, 9)
+        o_ref, _, _ = pu.oracle_decode(Q[0, h:h + 1].astype(np.float64), Khat, Vhat)
+        assert pu.rel_l2(out[0, h:h + 1], o_ref).max() <= pu.OUT_RTOL
+
+
+def test_headq_gqa(tq):
+    """HeadQ keys (2-bit base + rank-16 4-bit side code) with TQ-4 values,
+    post-RoPE-like keys, 4 query heads per KV head."""
+    d, r = 128, 16
+    K, V, Q, C = synth.rope_gqa(1, 2, 4, 1500, d, seed=5, n_calib=4096, dtype=np.float32)
+    from oracle import headq as ohq
+    U = np.stack([ohq.fit_basis(C[h].astype(np.float64), r)[0] for h in range(2)])
+    worst, n_band, kp, vp, (Kd, Vd, Qd) = _run_case(tq, K, V, Q, "headq", 4, seed=3, U=U, label="headq")
+    m = tq.metrics(Qd, Kd, None, kp, None)
+    kls = []
+    for h in range(2):
+        Kf = Kd[0, h].double().cpu().numpy()
+        sl = slice(h * 1500, (h + 1) * 1500)
+        _, Khat, _, _, _ = pu.oracle_match(Kf, {k: v[sl] for k, v in kp.planes().items()}, oqz.HEADQ, 2, 3, U=U[h])
+        kl, _, _, _ = pu.kl_and_recall(Qd[0, 4 * h:4 * h + 4].double().cpu().numpy(), Kf, Khat)
+        kls.append(kl)
+    kls = np.concatenate(kls)
+    assert abs(m["kl_mean"] - kls.mean()) <= pu.KL_ATOL and abs(m["kl_max"] - kls.max()) <= pu.KL_ATOL
