@@ -136,6 +136,24 @@ tq_status sketch_on_device(uint64_t seed, int d, const float** out) {
   return TQ_OK;
 }
 
+// Compute units of the current device (cached per device).
+hipError_t cu_count(int* out) {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) { *out = it->second; return hipSuccess; }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  cache[dev] = n;
+  *out = n;
+  return hipSuccess;
+}
+
 tq_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(TQ_EDEVICE, "%s: %s", what, hipGetErrorString(e));
   return TQ_OK;
@@ -169,6 +187,7 @@ bool decode_supported(int kbits, bool kq, bool ksd, int vbits, bool vq) {
 
 struct DecodePlan {
   int nsplit, chunk, part_stride, units, G;
+  bool lut;
   size_t off_qrot, off_qsk, off_qw, off_part, off_qraw, bytes;
 };
 
@@ -184,9 +203,14 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   const int d = k->d, L = d / 32, vpw = 64 / L;
   const int G = Hq / k->H;
   const int nq = k->B * Hq;
-  const int step = 4 * vpw;
+  const bool lut = v && lut_supported(d, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, v->bits,
+                                      v->mode == TQ_MODE_PROD);
+  // The table-driven kernel walks 8 waves x (64/L) tokens per block step and
+  // runs one persistent block per CU; the generic one 4 waves per block.
+  const int step = (lut ? 8 : 4) * vpw;
   const long groups = (long)k->B * k->H * G;
-  int nsplit = (int)std::max<long>(1, (2048 + groups - 1) / groups);
+  const long target = lut ? 2048 : 2048;
+  int nsplit = (int)std::max<long>(1, (target + groups - 1) / groups);
   int chunk = (k->T + nsplit - 1) / nsplit;
   chunk = std::max(step, (chunk + step - 1) / step * step);
   nsplit = (k->T + chunk - 1) / chunk;
@@ -198,6 +222,7 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   const bool vq = v && v->mode == TQ_MODE_PROD;
   pl->nsplit = nsplit;
   pl->chunk = chunk;
+  pl->lut = lut;
   pl->G = G;
   pl->part_stride = (int)round_up(2 + d + (vq ? d : 0), 4);
   const long R = (long)k->B * k->H * nsplit;
@@ -408,7 +433,14 @@ tq_status tq_decode_attention(const tq_tensor_desc* q, const tq_packed* k, const
 
   bool supported = true;
   if (tq_status s = hip_status(launch_qprep(qp, st), "query prep launch")) return s;
-  if (tq_status s = hip_status(launch_decode_split(dp, k->bits, kq, ksd, v->bits, vq, st, &supported), "decode launch")) return s;
+  if (pl.lut) {
+    int cus = 0;
+    if (tq_status s = hip_status(cu_count(&cus), "device query")) return s;
+    const int nblocks = std::min(pl.units, std::max(1, cus));
+    if (tq_status s = hip_status(launch_decode_lut(dp, k->bits, kq, v->bits, vq, nblocks, st), "decode launch")) return s;
+  } else {
+    if (tq_status s = hip_status(launch_decode_split(dp, k->bits, kq, ksd, v->bits, vq, st, &supported), "decode launch")) return s;
+  }
   if (!supported) return fail(TQ_EUNSUPPORTED, "K/V mode combination has no decode kernel");
   if (tq_status s = hip_status(launch_combine(cp, st), "combine launch")) return s;
   return ok();

@@ -1,0 +1,377 @@
+// Table-driven split decode for 3- and 4-bit caches (any head dim), the
+// read side of [P1] "Esquemas de Cuantización" (KV, KQV, QKQV at n = 4) and
+// [P2] "Contribuições Principais" 1 (TQ-KV, TQ-QKV).
+//
+// [P1] = "Resumen Técnico: Inferencia Estadística y Medidas de Calidad de
+//        Cuantizaciones de Cache KV Inspiradas en TurboQuant"
+// [P2] = "Resumo Técnico: Ablação, Inferência Estatística e Validação para
+//        Compressão de KV-Cache"
+//
+// Same arithmetic as decode_split_kernel (scores and value sums in the
+// rotated domain), organised so that each byte of packed cache costs about
+// one VALU instruction:
+//   * a packed byte (two 4-bit codes) or a 6-bit field (two 3-bit codes) is
+//     turned into an LDS address by one v_perm / v_lshl_or, and one LDS read
+//     returns both centroids;
+//   * the LDS tables are replicated across lanes so that every read of a
+//     wave hits distinct banks:
+//       V region  [0, 64K):     entry e at e*256, fp16 pair, one copy per lane (b32)
+//       K region  [64K, 128K):  entry e at 64K + e*256, fp32 pair, a copy per lane%16 (b64)
+//       S region  (same entries, +128): 8 fp16 signs (+-1) of byte e, a copy per lane%8 (b128)
+//   * key centroids stay fp32 (scores are exact in fp32); value centroids and
+//     the +-1 sign patterns are fp16 and enter v_fma_mix_f32 with fp32
+//     weights and fp32 accumulators;
+//   * 4 lanes per 128-d token, lane j owns coordinates [32j, 32j+32); the
+//     per-token scalars (norms, residual norms) are loaded once per quad and
+//     broadcast with DPP;
+//   * all packed data is streamed with non-temporal loads, one token step
+//     ahead of the arithmetic;
+//   * one persistent block per CU loops over (query, context chunk) units.
+#include <cfloat>
+#include <cmath>
+
+#include "device_common.h"
+
+namespace tq {
+namespace {
+
+constexpr int kLutThreads = 512;
+constexpr int kLutWaves = kLutThreads / 64;
+constexpr uint32_t kRegionK = 0x10000;
+constexpr uint32_t kMergeBase = 0x20000;
+constexpr int kLdsBytes = 0x20000 + kLutWaves * (2 + 2 * 128) * 4 + 256;
+constexpr float kSlack = 8.0f;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS address of byte K of w: [lanereg.b0, w.bK, lanereg.b2, 0].
+template <int K>
+__device__ __forceinline__ uint32_t byte_addr(uint32_t w, uint32_t lanereg) {
+  return __builtin_amdgcn_perm(w, lanereg, 0x0C020000u | ((4u + K) << 8));
+}
+
+// 6-bit field at bit offset O of a 3-dword run.
+template <int O>
+__device__ __forceinline__ uint32_t field6(const uint32_t* w) {
+  constexpr int wi = O >> 5, sh = O & 31;
+  if (sh + 6 <= 32) return __builtin_amdgcn_ubfe(w[wi], sh, 6);
+  return __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh), 0, 6);
+}
+
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  return v;
+}
+
+template <int J>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), J * 0x55, 0xF, 0xF, true));
+}
+
+template <int KB, bool KQ, int VB, bool VQ>
+struct TokenData {
+  uint32_t k[KB];
+  uint32_t ks;   // key signs (KQ)
+  uint32_t v[VB];
+  uint32_t vs;   // value signs (VQ)
+  float sc;      // this lane's per-token scalar (lane j: nu_k, gamma_k, nu_v, gamma_v)
+};
+
+template <int KB, bool KQ, int VB, bool VQ>
+__device__ __forceinline__ void load_token(const DecodeParams& p, int64_t vec, int j, const float* sc_src,
+                                           TokenData<KB, KQ, VB, VQ>& t) {
+  const int d = p.d;
+  const uint32_t* kc = reinterpret_cast<const uint32_t*>(p.k.codes + vec * (d * KB / 8)) + j * KB;
+  if (KB == 4) {
+    u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc));
+    t.k[0] = x.x; t.k[1] = x.y; t.k[2] = x.z; t.k[3] = x.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) t.k[i] = __builtin_nontemporal_load(kc + i);
+  }
+  const uint32_t* vc = reinterpret_cast<const uint32_t*>(p.v.codes + vec * (d * VB / 8)) + j * VB;
+  if (VB == 4) {
+    u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc));
+    t.v[0] = x.x; t.v[1] = x.y; t.v[2] = x.z; t.v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < VB; ++i) t.v[i] = __builtin_nontemporal_load(vc + i);
+  }
+  if (KQ) t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.k.qjl + vec * (d / 8)) + j);
+  if (VQ) t.vs = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.v.qjl + vec * (d / 8)) + j);
+  t.sc = __builtin_nontemporal_load(sc_src + vec);
+}
+
+template <int KB, bool KQ, int VB, bool VQ>
+__global__ __launch_bounds__(kLutThreads) void decode_lut_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int L = p.L, j = lane & (L - 1), slot = lane / L, vpw = 64 / L;
+  const int d = p.d;
+
+  // ---- tables -------------------------------------------------------------------
+  {
+    constexpr int NV = VB == 4 ? 256 : 64;
+    for (int i = threadIdx.x; i < NV * 64; i += kLutThreads) {
+      const int e = i >> 6, l = i & 63;
+      const int lo = VB == 4 ? (e & 15) : (e & 7), hi = VB == 4 ? (e >> 4) : (e >> 3);
+      half2_t h;
+      h.x = (_Float16)p.vc[lo];
+      h.y = (_Float16)p.vc[hi];
+      *reinterpret_cast<half2_t*>(smem + e * 256 + l * 4) = h;
+    }
+    constexpr int NK = KB == 4 ? 256 : 64;
+    for (int i = threadIdx.x; i < NK * 16; i += kLutThreads) {
+      const int e = i >> 4, l = i & 15;
+      const int lo = KB == 4 ? (e & 15) : (e & 7), hi = KB == 4 ? (e >> 4) : (e >> 3);
+      float2_t c;
+      c.x = p.kc[lo];
+      c.y = p.kc[hi];
+      *reinterpret_cast<float2_t*>(smem + kRegionK + e * 256 + l * 8) = c;
+    }
+    if (KQ || VQ) {
+      for (int i = threadIdx.x; i < 256 * 8; i += kLutThreads) {
+        const int e = i >> 3, l = i & 7;
+        half8_t s;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) s[t] = ((e >> t) & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
+        *reinterpret_cast<half8_t*>(smem + kRegionK + e * 256 + 128 + l * 16) = s;
+      }
+    }
+  }
+  __syncthreads();
+
+  const uint32_t lr_v = (uint32_t)lane * 4u;
+  const uint32_t lr_k = kRegionK | ((uint32_t)(lane & 15) << 3);
+  const uint32_t lr_s = kRegionK | (128u + ((uint32_t)(lane & 7) << 4));
+  // Lane j of a quad streams one per-token scalar: 0 nu_k, 1 gamma_k, 2 nu_v, 3 gamma_v.
+  const float* sc_src = j == 0 ? p.k.norms : (j == 1 ? (KQ ? p.k.gamma : p.k.norms)
+                                                     : (j == 2 ? p.v.norms : (VQ ? p.v.gamma : p.v.norms)));
+  float* merge = reinterpret_cast<float*>(smem + kMergeBase);
+  const int R = p.B * p.Hkv * p.nsplit;
+
+  for (int unit = blockIdx.x; unit < p.units; unit += gridDim.x) {
+    const int x = unit & 7, kk = unit >> 3;
+    const int g = kk % p.G, r = (kk / p.G) * 8 + x;
+    if (r >= R) continue;  // uniform per block
+    const int split = r % p.nsplit, bkv = r / p.nsplit;
+    const int b = bkv / p.Hkv, kvh = bkv % p.Hkv;
+    const int qi = b * p.Hq + kvh * p.G + g;
+    const int t0 = split * p.chunk, t1 = min(p.T, t0 + p.chunk);
+    const int64_t vbase = (int64_t)bkv * p.T_cap;
+
+    float q[32], u[KQ ? 32 : 1];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) q[e] = p.qrot[(size_t)qi * d + 32 * j + e];
+    if (KQ) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) u[e] = p.qsk[(size_t)qi * d + 32 * j + e];
+    }
+    float acc[32], ask[VQ ? 32 : 1];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+    if (VQ) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) ask[e] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+
+    const int stride = kLutWaves * vpw;
+    int base = t0 + wave * vpw;
+    TokenData<KB, KQ, VB, VQ> nxt;
+    if (base < t1) load_token(p, vbase + min(base + slot, t1 - 1), j, sc_src, nxt);
+    for (; base < t1; base += stride) {
+      TokenData<KB, KQ, VB, VQ> cur = nxt;
+      const int t = base + slot;
+      const bool valid = t < t1;
+      if (base + stride < t1) load_token(p, vbase + min(base + stride + slot, t1 - 1), j, sc_src, nxt);
+
+      // ---- key score: this lane's 32 coordinates ---------------------------------
+      float sa = 0.f, sb = 0.f;
+      if (KB == 4) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#define TQ_KBYTE(BB)                                                                          \
+          {                                                                                   \
+            const float2_t c = *reinterpret_cast<const float2_t*>(smem + byte_addr<BB>(cur.k[w], lr_k)); \
+            sa = fmaf(q[8 * w + 2 * BB], c.x, sa);                                            \
+            sb = fmaf(q[8 * w + 2 * BB + 1], c.y, sb);                                        \
+          }
+          TQ_KBYTE(0) TQ_KBYTE(1) TQ_KBYTE(2) TQ_KBYTE(3)
+#undef TQ_KBYTE
+        }
+      } else {
+#define TQ_KPAIR(M)                                                                            \
+        {                                                                                      \
+          const uint32_t a = (field6<6 * (M)>(cur.k) << 8) | lr_k;                             \
+          const float2_t c = *reinterpret_cast<const float2_t*>(smem + a);                     \
+          sa = fmaf(q[2 * (M)], c.x, sa);                                                      \
+          sb = fmaf(q[2 * (M) + 1], c.y, sb);                                                  \
+        }
+        TQ_KPAIR(0) TQ_KPAIR(1) TQ_KPAIR(2) TQ_KPAIR(3) TQ_KPAIR(4) TQ_KPAIR(5) TQ_KPAIR(6) TQ_KPAIR(7)
+        TQ_KPAIR(8) TQ_KPAIR(9) TQ_KPAIR(10) TQ_KPAIR(11) TQ_KPAIR(12) TQ_KPAIR(13) TQ_KPAIR(14) TQ_KPAIR(15)
+#undef TQ_KPAIR
+      }
+      const float nu_k = quad_bcast<0>(cur.sc);
+      float part = nu_k * (sa + sb);
+      if (KQ) {
+        float pa = 0.f, pb = 0.f;
+#define TQ_KSIGN(BB)                                                                           \
+        {                                                                                      \
+          const half8_t s = *reinterpret_cast<const half8_t*>(smem + byte_addr<BB>(cur.ks, lr_s)); \
+          _Pragma("unroll") for (int t = 0; t < 8; t += 2) {                                   \
+            pa = fmaf(u[8 * BB + t], (float)s[t], pa);                                         \
+            pb = fmaf(u[8 * BB + t + 1], (float)s[t + 1], pb);                                 \
+          }                                                                                    \
+        }
+        TQ_KSIGN(0) TQ_KSIGN(1) TQ_KSIGN(2) TQ_KSIGN(3)
+#undef TQ_KSIGN
+        const float g_k = quad_bcast<1>(cur.sc);
+        part = fmaf(nu_k * p.k_qjl * g_k, pa + pb, part);
+      }
+      float s = quad_sum(part) * p.scale_log2;
+      if (!valid) s = -INFINITY;
+
+      // ---- online softmax (per token slot) ----------------------------------------
+      if (s > m + kSlack) {
+        const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - s);
+        l *= alpha;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) acc[e] *= alpha;
+        if (VQ) {
+#pragma unroll
+          for (int e = 0; e < 32; ++e) ask[e] *= alpha;
+        }
+        m = s;
+      }
+      const float pt = valid ? exp2f(s - m) : 0.f;
+      l += pt;
+      const float wv = pt * quad_bcast<2>(cur.sc);
+
+      // ---- value accumulation -----------------------------------------------------
+      if (VB == 4) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#define TQ_VBYTE(BB)                                                                           \
+          {                                                                                    \
+            const half2_t h = *reinterpret_cast<const half2_t*>(smem + byte_addr<BB>(cur.v[w], lr_v)); \
+            acc[8 * w + 2 * BB] = fmaf(wv, (float)h.x, acc[8 * w + 2 * BB]);                   \
+            acc[8 * w + 2 * BB + 1] = fmaf(wv, (float)h.y, acc[8 * w + 2 * BB + 1]);           \
+          }
+          TQ_VBYTE(0) TQ_VBYTE(1) TQ_VBYTE(2) TQ_VBYTE(3)
+#undef TQ_VBYTE
+        }
+      } else {
+#define TQ_VPAIR(M)                                                                            \
+        {                                                                                      \
+          const uint32_t a = (field6<6 * (M)>(cur.v) << 8) | lr_v;                             \
+          const half2_t h = *reinterpret_cast<const half2_t*>(smem + a);                       \
+          acc[2 * (M)] = fmaf(wv, (float)h.x, acc[2 * (M)]);                                   \
+          acc[2 * (M) + 1] = fmaf(wv, (float)h.y, acc[2 * (M) + 1]);                           \
+        }
+        TQ_VPAIR(0) TQ_VPAIR(1) TQ_VPAIR(2) TQ_VPAIR(3) TQ_VPAIR(4) TQ_VPAIR(5) TQ_VPAIR(6) TQ_VPAIR(7)
+        TQ_VPAIR(8) TQ_VPAIR(9) TQ_VPAIR(10) TQ_VPAIR(11) TQ_VPAIR(12) TQ_VPAIR(13) TQ_VPAIR(14) TQ_VPAIR(15)
+#undef TQ_VPAIR
+      }
+      if (VQ) {
+        const float wq = wv * quad_bcast<3>(cur.sc);
+#define TQ_VSIGN(BB)                                                                           \
+        {                                                                                      \
+          const half8_t sg = *reinterpret_cast<const half8_t*>(smem + byte_addr<BB>(cur.vs, lr_s)); \
+          _Pragma("unroll") for (int t = 0; t < 8; ++t)                                        \
+            ask[8 * BB + t] = fmaf(wq, (float)sg[t], ask[8 * BB + t]);                         \
+        }
+        TQ_VSIGN(0) TQ_VSIGN(1) TQ_VSIGN(2) TQ_VSIGN(3)
+#undef TQ_VSIGN
+      }
+    }
+
+    // ---- merge the token slots of the wave (lanes with equal j) -----------------------
+    for (int off = L; off < 64; off <<= 1) {
+      const float mo = __shfl_xor(m, off, 64), lo = __shfl_xor(l, off, 64);
+      const float M = fmaxf(m, mo);
+      const float a = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      const float c = (mo == -INFINITY) ? 0.f : exp2f(mo - M);
+      l = l * a + lo * c;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) acc[e] = acc[e] * a + __shfl_xor(acc[e], off, 64) * c;
+      if (VQ) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ask[e] = ask[e] * a + __shfl_xor(ask[e], off, 64) * c;
+      }
+      m = M;
+    }
+    const int rec = 2 + 2 * d;
+    if (slot == 0) {
+      float* wm = merge + wave * rec;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) wm[2 + 32 * j + e] = acc[e];
+      if (VQ) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) wm[2 + d + 32 * j + e] = ask[e];
+      }
+      if (j == 0) { wm[0] = m; wm[1] = l; }
+    }
+    __syncthreads();
+    {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kLutWaves; ++w) M = fmaxf(M, merge[w * rec]);
+      float sc[kLutWaves], lt = 0.f;
+#pragma unroll
+      for (int w = 0; w < kLutWaves; ++w) {
+        const float mw = merge[w * rec];
+        sc[w] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        lt += merge[w * rec + 1] * sc[w];
+      }
+      float* out = p.part + ((size_t)qi * p.nsplit + split) * p.part_stride;
+      const int nvals = VQ ? 2 * d : d;
+      for (int i = threadIdx.x; i < nvals; i += kLutThreads) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kLutWaves; ++w) v += merge[w * rec + 2 + i] * sc[w];
+        out[2 + i] = v;
+      }
+      if (threadIdx.x == 0) { out[0] = M; out[1] = lt; }
+    }
+    __syncthreads();
+  }
+}
+
+template <int KB, bool KQ, int VB, bool VQ>
+hipError_t launch_lut(const DecodeParams& p, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL((decode_lut_kernel<KB, KQ, VB, VQ>), dim3(nblocks), dim3(kLutThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool lut_supported(int d, int kbits, int kqjl, int kside, int vbits, int vqjl) {
+  if (kside || d != 128) return false;
+  return (kbits == 3 || kbits == 4) && (vbits == 3 || vbits == 4) && (!kqjl || kbits == 3) && (!vqjl || vbits == 3);
+}
+
+int lut_threads() { return kLutThreads; }
+
+hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int vbits, int vqjl, int nblocks,
+                             hipStream_t s) {
+  const int key = (kbits == 4 ? 0 : 2 + kqjl) * 4 + (vbits == 4 ? 0 : 2 + vqjl);
+  switch (key) {
+    case 0 * 4 + 0: return launch_lut<4, false, 4, false>(p, nblocks, s);
+    case 0 * 4 + 2: return launch_lut<4, false, 3, false>(p, nblocks, s);
+    case 0 * 4 + 3: return launch_lut<4, false, 3, true>(p, nblocks, s);
+    case 2 * 4 + 0: return launch_lut<3, false, 4, false>(p, nblocks, s);
+    case 2 * 4 + 2: return launch_lut<3, false, 3, false>(p, nblocks, s);
+    case 2 * 4 + 3: return launch_lut<3, false, 3, true>(p, nblocks, s);
+    case 3 * 4 + 0: return launch_lut<3, true, 4, false>(p, nblocks, s);
+    case 3 * 4 + 2: return launch_lut<3, true, 3, false>(p, nblocks, s);
+    case 3 * 4 + 3: return launch_lut<3, true, 3, true>(p, nblocks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

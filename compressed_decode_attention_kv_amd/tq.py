@@ -194,6 +194,31 @@ class PackedTensor:
         self.c.side = self.side.data_ptr() if self.side is not None else None
         self.c.side_scale = self.side_scale.data_ptr() if self.side_scale is not None else None
 
+    def head_view(self, b, h):
+        """A descriptor of the single (b, h) slice of this cache (B = H = 1),
+        pointing into the same planes."""
+        v = PackedTensor.__new__(PackedTensor)
+        v.layout = self.layout
+        v.basis = self.basis
+        v.c = Packed()
+        ctypes.pointer(v.c)[0] = self.c
+        v.c.B, v.c.H = 1, 1
+        off = (b * self.c.H + h) * self.c.T_cap
+        lay = self.layout
+        v.c.codes = self.c.codes + off * lay.code_bytes
+        v.c.norms = self.c.norms + off * 4
+        if self.c.qjl:
+            v.c.qjl = self.c.qjl + off * lay.qjl_bytes
+            v.c.gamma = self.c.gamma + off * 4
+        if self.c.side:
+            v.c.side = self.c.side + off * lay.side_bytes
+            v.c.side_scale = self.c.side_scale + off * 4
+        if self.c.basis:
+            d, r = self.c.d, self.c.side_rank
+            v.c.basis = self.c.basis + h * d * r * 4
+        v._parent = self
+        return v
+
     @property
     def n(self):
         return self.c.B * self.c.H * self.c.T_cap

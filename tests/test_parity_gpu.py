@@ -162,3 +162,37 @@ def test_headq_gqa(tq):
         kls.append(kl)
     kls = np.concatenate(kls)
     assert abs(m["kl_mean"] - kls.mean()) <= pu.KL_ATOL and abs(m["kl_max"] - kls.max()) <= pu.KL_ATOL
+
+
+@pytest.mark.parametrize("scheme", ["kqv", "kv", "qkqv"])
+def test_isotropic_decode_full_size_sampled(tq, scheme):
+    """The benchmark workload at full size (B=16, 32 heads, T=32768, d=128,
+    fp16, one query per head), in the launch configuration the benchmark
+    times; sampled (batch, head) slices are checked against the oracle
+    element by element, every output for finiteness, and the metrics call on
+    the same slices against the oracle's KL and top-5."""
+    B, H, T, d = 16, 32, 32768, 128
+    K, V, Q = synth.device_isotropic(B, H, 1, T, d, seed=1)
+    kp = tq.quantize(K, tq.KEYS, scheme, 4, 0)
+    vp = tq.quantize(V, tq.VALUES, scheme, 4, 0)
+    out, lse = tq.decode_attention(Q, kp, vp)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item()
+    kmode, vmode = pu.MODE_NAMES[kp.c.mode], pu.MODE_NAMES[vp.c.mode]
+    kpl, vpl = kp.planes(), vp.planes()
+    for (b, h) in [(0, 0), (7, 13), (15, 31)]:
+        sl = slice((b * H + h) * T, (b * H + h + 1) * T)
+        Kn = K[b, h].double().cpu().numpy()
+        Vn = V[b, h].double().cpu().numpy()
+        qn = Q[b, h:h + 1].double().cpu().numpy()
+        _, Khat, _, _, _ = pu.oracle_match(Kn, {k: v[sl] for k, v in kpl.items()}, kmode, kp.c.bits, 0, label="K")
+        _, Vhat, _, _, _ = pu.oracle_match(Vn, {k: v[sl] for k, v in vpl.items()}, vmode, vp.c.bits, 0, label="V")
+        o_ref, lse_ref, _ = pu.oracle_decode(qn, Khat, Vhat)
+        err = pu.rel_l2(out[b, h:h + 1].cpu().numpy(), o_ref)
+        assert err.max() <= pu.OUT_RTOL, (scheme, b, h, err)
+        assert abs(lse[b, h].item() - lse_ref[0]) <= 1e-4
+        m = tq.metrics(Q[b:b + 1, h:h + 1], K[b:b + 1, h:h + 1], None, kp.head_view(b, h), None)
+        kl, rec, s, sh = pu.kl_and_recall(qn, Kn, Khat)
+        assert abs(m["kl_mean"] - kl[0]) <= pu.KL_ATOL
+        amb = int(pu.top5_ambiguous(s).sum() + pu.top5_ambiguous(sh).sum())
+        assert abs(m["top5_recall"] - rec[0]) <= amb / 5.0 + 1e-12
