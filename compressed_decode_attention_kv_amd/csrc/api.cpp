@@ -136,6 +136,19 @@ tq_status sketch_on_device(uint64_t seed, int d, const float** out) {
   return TQ_OK;
 }
 
+// Grid for the index search: a cell width of a third of the smallest gap
+// between boundaries puts at most one boundary in any three adjacent cells.
+bool quant_grid(int d, int bits, QuantGrid* g) {
+  std::vector<double> c, t;
+  if (!codebook(d, bits, &c, &t)) return false;
+  double gap = 2.0;
+  for (size_t k = 1; k < t.size(); ++k) gap = std::min(gap, t[k] - t[k - 1]);
+  g->scale = (float)(3.2 / gap);
+  g->center = (int)std::ceil(g->scale) + 2;
+  g->cells = 2 * g->center + 1;
+  return g->cells <= quant_mfma_lut_max();
+}
+
 // Compute units of the current device (cached per device).
 hipError_t cu_count(int* out) {
   static std::mutex mu;
@@ -377,7 +390,16 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
   if (hq) { p.basis = hq->basis; p.rank = hq->rank; p.side_bits = hq->side_bits; }
   p.codes = out->codes; p.norms = out->norms; p.qjl = out->qjl; p.gamma = out->gamma;
   p.side = out->side; p.side_scale = out->side_scale;
-  if (tq_status s = hip_status(launch_quantize(p, (hipStream_t)stream), "quantize launch")) return s;
+  QuantGrid grid;
+  if (quant_mfma_supported(p) && quant_grid(x->d, bits, &grid)) {
+    int cus = 0;
+    if (tq_status s = hip_status(cu_count(&cus), "device query")) return s;
+    const long tiles = ((long)x->B * x->H * x->T + 15) / 16;
+    const int nblocks = (int)std::max<long>(1, std::min<long>((tiles + 3) / 4, (long)cus * 8));
+    if (tq_status s = hip_status(launch_quantize_mfma(p, grid, nblocks, (hipStream_t)stream), "quantize launch")) return s;
+  } else {
+    if (tq_status s = hip_status(launch_quantize(p, (hipStream_t)stream), "quantize launch")) return s;
+  }
   out->B = x->B; out->H = x->H; out->T = x->T; out->T_cap = T_cap; out->d = x->d;
   out->mode = mode; out->bits = bits; out->seed = seed;
   out->side_rank = hq ? hq->rank : 0; out->side_bits = hq ? hq->side_bits : 0;

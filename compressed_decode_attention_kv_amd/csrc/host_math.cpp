@@ -148,7 +148,9 @@ void sign_vector(uint64_t seed, int d, float* signs) {
 
 // Gaussian sketch S (m = d rows) of the QJL stage ([P1] "Contribuciones
 // Clave" 1): Box-Muller pairs in double from the stream at seed ^ kTagGauss,
-// rounded to float.
+// each rounded straight from double to the nearest fp16 value (so S is exact
+// in fp16, which the sketch projection on fp16 matrix cores relies on), and
+// returned as float.
 void gaussian_sketch(uint64_t seed, int d, float* S) {
   const uint64_t base = seed ^ kTagGauss;
   const size_t n = (size_t)d * d;
@@ -159,8 +161,8 @@ void gaussian_sketch(uint64_t seed, int d, float* S) {
     double u1 = ((double)o1 + 1.0) * 0x1.0p-53;
     double u2 = (double)o2 * 0x1.0p-53;
     double r = std::sqrt(-2.0 * std::log(u1));
-    S[2 * p] = (float)(r * std::cos(two_pi * u2));
-    if (2 * p + 1 < n) S[2 * p + 1] = (float)(r * std::sin(two_pi * u2));
+    S[2 * p] = (float)(_Float16)(r * std::cos(two_pi * u2));
+    if (2 * p + 1 < n) S[2 * p + 1] = (float)(_Float16)(r * std::sin(two_pi * u2));
   }
 }
 

@@ -43,6 +43,13 @@ struct QuantParams {
   uint8_t* codes; float* norms; uint8_t* qjl; float* gamma; uint8_t* side; float* side_scale;
 };
 
+// Uniform grid over the unit-sphere coordinate y in [-1, 1] used to find the
+// Lloyd-Max index: cell n = round(y * scale) + center, cells = 2 center + 1.
+struct QuantGrid {
+  float scale;
+  int center, cells;
+};
+
 struct TensorPlanes {
   const uint8_t* codes; const float* norms; const uint8_t* qjl; const float* gamma;
   const uint8_t* side; const float* side_scale;
@@ -110,6 +117,10 @@ struct RelErrParams {
 
 // ---- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+// Matrix-core write side (fp16 input, d = 128, PLAIN/MSE/PROD).
+bool quant_mfma_supported(const QuantParams& p);
+int quant_mfma_lut_max();
+hipError_t launch_quantize_mfma(const QuantParams& p, const QuantGrid& grid, int nblocks, hipStream_t s);
 hipError_t launch_qprep(const QPrepParams& p, hipStream_t s);
 hipError_t launch_decode_split(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl,
                                hipStream_t s, bool* supported);

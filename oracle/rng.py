@@ -23,7 +23,9 @@ Gaussian sketch: S (m x d, m = d, row-major) from Box-Muller pairs in
 double: pair p uses o1 = out_gauss(2p), o2 = out_gauss(2p+1),
 u1 = ((o1>>11)+1) 2^-53 in (0,1], u2 = (o2>>11) 2^-53 in [0,1),
 R = sqrt(-2 ln u1), S_flat[2p] = R cos(2 pi u2), S_flat[2p+1] = R sin(2 pi u2);
-S is defined as the float32 rounding of these doubles.
+S is defined as the float16 rounding (round to nearest even, straight from
+the double) of these values: an N(0,1) draw perturbed by at most 2^-11
+relative, exactly representable in fp16 and fp32 alike.
 """
 import numpy as np
 
@@ -59,7 +61,7 @@ def sign_vector(seed, d):
 
 
 def gaussian_sketch(seed, d, m=None):
-    """S in R^{m x d}: the float32 values, returned as float64."""
+    """S in R^{m x d}: the float16 values, returned as float64."""
     m = d if m is None else m
     n = m * d
     npairs = (n + 1) // 2
@@ -72,4 +74,4 @@ def gaussian_sketch(seed, d, m=None):
     z = np.empty(2 * npairs)
     z[0::2] = r * np.cos(TWO_PI * u2)
     z[1::2] = r * np.sin(TWO_PI * u2)
-    return z[:n].astype(np.float32).astype(np.float64).reshape(m, d)
+    return z[:n].astype(np.float16).astype(np.float64).reshape(m, d)

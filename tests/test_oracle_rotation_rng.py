@@ -54,7 +54,7 @@ def test_sign_vector_balanced_and_seeded():
 def test_gaussian_sketch_is_standard_normal():
     S = rng.gaussian_sketch(3, 128)
     assert S.shape == (128, 128)
-    assert np.all(S == S.astype(np.float32))
+    assert np.all(S == S.astype(np.float16))
     z = S.ravel()
     assert stats.kstest(z, "norm").pvalue > 1e-3
     assert abs(z.mean()) < 5 / 128 and abs(z.var() - 1) < 5 * np.sqrt(2 / z.size)

@@ -113,22 +113,24 @@ def test_head_dims(tq, d, scheme):
     _run_case(tq, K, V, Q, scheme, 4, seed=5, label="%s d=%d" % (scheme, d))
 
 
-def test_single_token_and_zero_vectors(tq):
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_single_token_and_zero_vectors(tq, dtype):
     K, V, Q = synth.isotropic(1, 1, 4, 1, 128, seed=1, kv_std=1.0, dtype=np.float32)
-    _run_case(tq, K, V, Q, "kqv", 4, label="T=1")
+    _run_case(tq, K, V, Q, "kqv", 4, label="T=1", dtype=dtype)
     K, V, Q = synth.isotropic(1, 2, 2, 300, 128, seed=2, kv_std=1.0, dtype=np.float32)
     K[0, 0, ::7] = 0.0
     V[0, 1, ::5] = 0.0
-    _, _, kp, vp, _ = _run_case(tq, K, V, Q, "qkqv", 4, label="zeros")
+    _, _, kp, vp, _ = _run_case(tq, K, V, Q, "qkqv", 4, label="zeros", dtype=dtype)
     pl = kp.planes()
     z = np.arange(0, 300, 7)
     assert np.all(pl["codes"][z] == 0) and np.all(pl["qjl"][z] == 0) and np.all(pl["gamma"][z] == 0)
 
 
-def test_strided_input_and_large_values(tq):
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_strided_input_and_large_values(tq, dtype):
     base = np.random.default_rng(3).standard_normal((1, 2, 400, 256)).astype(np.float32) * 300.0
-    Kd = torch.from_numpy(base).cuda()[..., :128]       # row stride 256
-    Vd = torch.from_numpy(base[..., 128:].copy()).cuda()
+    Kd = torch.from_numpy(base).to(dtype).cuda()[..., :128]       # row stride 256
+    Vd = torch.from_numpy(base[..., 128:].copy()).to(dtype).cuda()
     Q = np.random.default_rng(4).standard_normal((1, 2, 128)).astype(np.float32) * 0.01
     kp = tq.quantize(Kd, tq.KEYS, "kqv", 4, 9)
     vp = tq.quantize(Vd, tq.VALUES, "kqv", 4, 9)
