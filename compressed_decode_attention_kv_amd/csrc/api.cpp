@@ -218,8 +218,8 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   const int nq = k->B * Hq;
   const bool lut = v && lut_supported(d, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, v->bits,
                                       v->mode == TQ_MODE_PROD);
-  // The table-driven kernel walks 8 waves x (64/L) tokens per block step and
-  // runs one persistent block per CU; the generic one 4 waves per block.
+  // The table-driven kernel walks 8-12 waves x (64/L) tokens per block step
+  // and runs one persistent block per CU; the generic one 4 waves per block.
   const int step = (lut ? 8 : 4) * vpw;
   const long groups = (long)k->B * k->H * G;
   const long target = lut ? 2048 : 2048;
@@ -587,6 +587,13 @@ tq_status tq_headq_fit(const float* calib, int32_t N, int32_t d, int32_t rank, f
   if (N < 2 || rank < 1 || rank > d) return fail(TQ_EINVAL, "N=%d rank=%d invalid", N, rank);
   if (!pca_basis(calib, N, d, rank, U)) return fail(TQ_EINVAL, "PCA failed");
   return ok();
+}
+
+tq_status tq_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(TQ_EINVAL, "src must be 16-byte aligned, sink 4-byte aligned");
+  if (bytes == 0 || bytes % 16) return fail(TQ_EINVAL, "bytes must be a positive multiple of 16");
+  return hip_status(launch_stream_read(src, bytes, sink, (hipStream_t)stream), "stream read launch");
 }
 
 tq_status tq_release_cache(void) {

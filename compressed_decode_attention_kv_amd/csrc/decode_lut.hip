@@ -35,11 +35,13 @@
 namespace tq {
 namespace {
 
-constexpr int kLutThreads = 512;
-constexpr int kLutWaves = kLutThreads / 64;
+// Block size: 12 waves (3 per SIMD) where the variant fits in 168 VGPRs,
+// 8 waves for the variant with sketches on both K and V.
+constexpr int lut_threads(bool both_sketched) { return both_sketched ? 512 : 768; }
+constexpr int kMaxLutWaves = 12;
 constexpr uint32_t kRegionK = 0x10000;
 constexpr uint32_t kMergeBase = 0x20000;
-constexpr int kLdsBytes = 0x20000 + kLutWaves * (2 + 2 * 128) * 4 + 256;
+constexpr int kLdsBytes = 0x20000 + kMaxLutWaves * (2 + 2 * 128) * 4 + 256;
 constexpr float kSlack = 8.0f;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -86,7 +88,7 @@ __device__ __forceinline__ void load_token(const DecodeParams& p, int64_t vec, i
                                            TokenData<KB, KQ, VB, VQ>& t) {
   const int d = p.d;
   const uint32_t* kc = reinterpret_cast<const uint32_t*>(p.k.codes + vec * (d * KB / 8)) + j * KB;
-  if (KB == 4) {
+  if constexpr (KB == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc));
     t.k[0] = x.x; t.k[1] = x.y; t.k[2] = x.z; t.k[3] = x.w;
   } else {
@@ -94,7 +96,7 @@ __device__ __forceinline__ void load_token(const DecodeParams& p, int64_t vec, i
     for (int i = 0; i < KB; ++i) t.k[i] = __builtin_nontemporal_load(kc + i);
   }
   const uint32_t* vc = reinterpret_cast<const uint32_t*>(p.v.codes + vec * (d * VB / 8)) + j * VB;
-  if (VB == 4) {
+  if constexpr (VB == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc));
     t.v[0] = x.x; t.v[1] = x.y; t.v[2] = x.z; t.v[3] = x.w;
   } else {
@@ -107,7 +109,11 @@ __device__ __forceinline__ void load_token(const DecodeParams& p, int64_t vec, i
 }
 
 template <int KB, bool KQ, int VB, bool VQ>
-__global__ __launch_bounds__(kLutThreads) void decode_lut_kernel(DecodeParams p) {
+__global__ __launch_bounds__(lut_threads(KQ && VQ))
+__attribute__((amdgpu_waves_per_eu(lut_threads(KQ && VQ) / 256, lut_threads(KQ && VQ) / 256)))
+void decode_lut_kernel(DecodeParams p) {
+  constexpr int kLutThreads = lut_threads(KQ && VQ);
+  constexpr int kLutWaves = kLutThreads / 64;
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int L = p.L, j = lane & (L - 1), slot = lane / L, vpw = 64 / L;
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(kLutThreads) void decode_lut_kernel(DecodeParams p)
 
 template <int KB, bool KQ, int VB, bool VQ>
 hipError_t launch_lut(const DecodeParams& p, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((decode_lut_kernel<KB, KQ, VB, VQ>), dim3(nblocks), dim3(kLutThreads), 0, s, p);
+  hipLaunchKernelGGL((decode_lut_kernel<KB, KQ, VB, VQ>), dim3(nblocks), dim3(lut_threads(KQ && VQ)), 0, s, p);
   return hipGetLastError();
 }
 
@@ -355,7 +361,6 @@ bool lut_supported(int d, int kbits, int kqjl, int kside, int vbits, int vqjl) {
   return (kbits == 3 || kbits == 4) && (vbits == 3 || vbits == 4) && (!kqjl || kbits == 3) && (!vqjl || vbits == 3);
 }
 
-int lut_threads() { return kLutThreads; }
 
 hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int vbits, int vqjl, int nblocks,
                              hipStream_t s) {

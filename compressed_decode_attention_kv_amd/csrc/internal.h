@@ -133,5 +133,7 @@ hipError_t launch_metric_scores(const MetricScoreParams& p, int kbits, int kqjl,
                                 bool* supported);
 hipError_t launch_metric_reduce(const MetricReduceParams& p, hipStream_t s);
 hipError_t launch_relerr(const RelErrParams& p, int nblocks, hipStream_t s);
+int stream_read_blocks();
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 
 }  // namespace tq

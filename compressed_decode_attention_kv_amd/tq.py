@@ -27,7 +27,7 @@ SCHEMES = {"kv": 0, "tq-kv": 1, "kqv": 2, "qkqv": 3, "tq-qkv": 4, "headq": 5}
 EXPORTS = ["tq_abi_version", "tq_status_str", "tq_last_error", "tq_codebook_build", "tq_scheme_modes",
            "tq_packed_layout", "tq_rotation_state", "tq_quantize", "tq_decode_workspace_size",
            "tq_decode_attention", "tq_metrics_workspace_size", "tq_metrics", "tq_headq_fit",
-           "tq_release_cache"]
+           "tq_stream_read", "tq_release_cache"]
 
 
 class TensorDesc(ctypes.Structure):
@@ -78,6 +78,7 @@ _sigs = {
     "tq_metrics": ([_P(TensorDesc), _P(TensorDesc), _P(TensorDesc), _P(Packed), _P(Packed), _P(MetricsOut),
                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "tq_headq_fit": ([_P(ctypes.c_float), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P(ctypes.c_float)], ctypes.c_int),
+    "tq_stream_read": ([ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "tq_release_cache": ([], ctypes.c_int),
 }
 for _name, (_args, _res) in _sigs.items():
@@ -297,6 +298,11 @@ def metrics(q=None, k_ref=None, v_ref=None, kp=None, vp=None):
                            ctypes.byref(vp.c) if vp else None, ctypes.byref(res), ws.data_ptr(), ws.numel(),
                            _stream()))
     return {f: getattr(res, f) for f, _ in MetricsOut._fields_}
+
+
+def stream_read(buf, sink):
+    """Stream-read the device tensor `buf` (non-temporal 128-bit loads)."""
+    _check(_lib.tq_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), _stream()))
 
 
 def release_cache():

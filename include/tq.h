@@ -104,8 +104,8 @@ typedef struct tq_layout {
  * both tq_quantize and the decode/metrics calls. */
 typedef struct tq_headq {
   const float* basis;
-  int32_t rank;      /* r, multiple of 8, <= 64 */
-  int32_t side_bits; /* q_s in [2, 8]           */
+  int32_t rank;      /* r in {8, 16, 24, 32}, with d * r <= 16384 */
+  int32_t side_bits; /* q_s in [2, 8]                              */
 } tq_headq;
 
 /* One packed tensor.  The caller sets T_cap and the plane pointers; the
@@ -160,12 +160,15 @@ tq_status tq_packed_layout(int32_t d, int32_t mode, int32_t bits, int32_t side_r
 /* The seeded random state of the rotation and the sketch ([P2]
  * "Configuração Experimental": random Walsh-Hadamard transform and QJL
  * sketch).  Host only.  signs: host float[d] (+1/-1); S: host float[d*d]
- * row-major (m = d rows), either may be NULL.  Generated by SplitMix64 as
- * specified in the design notes. */
+ * row-major (m = d rows), either may be NULL.  Both come from SplitMix64
+ * streams started at seed ^ 0x243F6A8885A308D3 (signs: D_i = -1 iff bit 63 of
+ * output i is set) and seed ^ 0x13198A2E03707344 (S: Box-Muller pairs in
+ * double, u1 = ((o1 >> 11) + 1) 2^-53, u2 = (o2 >> 11) 2^-53, each value
+ * rounded to the nearest fp16). */
 tq_status tq_rotation_state(uint64_t seed, int32_t d, float* signs, float* S);
 
 /* Write side: quantise x [B][H][T][d] (fp16 or fp32, device) into `out`.
- * Mode and bits come from (scheme, n_bits, which).  n_bits in [1, 8]
+ * Mode and bits come from (scheme, n_bits, which).  n_bits in [1, 4]
  * (PROD needs n_bits >= 2).  hq must be non-NULL exactly when the mode is
  * HEADQ (keys of TQ_SCHEME_HEADQ).  out->T_cap >= x->T (0 means x->T); the
  * planes the mode needs must be set, 16-byte aligned and sized per
@@ -204,6 +207,14 @@ tq_status tq_metrics(const tq_tensor_desc* q, const tq_tensor_desc* k_ref, const
  * [d][rank], columns = eigenvectors of the largest eigenvalues, each with
  * its largest-magnitude entry positive.  Host only, synchronous. */
 tq_status tq_headq_fit(const float* calib, int32_t N, int32_t d, int32_t rank, float* U);
+
+/* Diagnostic: reads `bytes` (a positive multiple of 16) of device memory at
+ * `src` (16-byte aligned) with the non-temporal 128-bit loads the decode
+ * kernels stream the packed cache with, and writes one XOR checksum per block
+ * to `sink` (device, at least 2048 * 4 bytes).  Measures the achievable
+ * streaming-read bandwidth and serves as the known-size reference for the
+ * HBM byte counters.  Stream-ordered. */
+tq_status tq_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
 /* Frees the cached device constants of every device. */
 tq_status tq_release_cache(void);
