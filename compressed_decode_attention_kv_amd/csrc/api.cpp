@@ -222,7 +222,10 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   // and runs one persistent block per CU; the generic one 4 waves per block.
   const int step = (lut ? 8 : 4) * vpw;
   const long groups = (long)k->B * k->H * G;
-  const long target = lut ? 2048 : 2048;
+  // Work units (query, context chunk): the generic kernel wants ~2048 blocks
+  // in flight; the persistent table-driven kernel wants few, long units
+  // (about two per CU) because each unit ends with a merge of its token slots.
+  const long target = lut ? 512 : 2048;
   int nsplit = (int)std::max<long>(1, (target + groups - 1) / groups);
   int chunk = (k->T + nsplit - 1) / nsplit;
   chunk = std::max(step, (chunk + step - 1) / step * step);

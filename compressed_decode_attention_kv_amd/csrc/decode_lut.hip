@@ -39,9 +39,28 @@ namespace {
 // 8 waves for the variant with sketches on both K and V.
 constexpr int lut_threads(bool both_sketched) { return both_sketched ? 512 : 768; }
 constexpr int kMaxLutWaves = 12;
-constexpr uint32_t kRegionK = 0x10000;
-constexpr uint32_t kMergeBase = 0x20000;
-constexpr int kLdsBytes = 0x20000 + kMaxLutWaves * (2 + 2 * 128) * 4 + 256;
+// LDS map.  A table indexed by a whole packed byte needs a 64 KB window
+// (entry e at window + e*256, the byte lands in address bits 8..15 straight
+// from v_perm); at most two such tables are live (4-bit keys, 4-bit values,
+// sign patterns).  Tables indexed by a 6-bit field (3-bit codes) hold 64
+// entries (16 KB) and sit above 128 KB, followed by the wave-merge buffer.
+// Replication per table (chosen by measurement of read throughput):
+//   value pairs  fp16x2  b32   one copy per lane      (lane * 4)
+//   key pairs    fp32x2  b64   a copy per lane % 32   ((lane & 31) * 8)
+//   sign bytes   fp16x8  b128  a copy per lane % 16   ((lane & 15) * 16)
+template <int KB, bool KQ, int VB, bool VQ>
+struct LutMap {
+  static constexpr bool kSigns = KQ || VQ;
+  static constexpr uint32_t nbyte_tables = (KB == 4) + (VB == 4) + kSigns;
+  static constexpr uint32_t six_base = 0x10000u * nbyte_tables;
+  static constexpr uint32_t k_base = KB == 4 ? 0u : six_base;
+  static constexpr uint32_t v_base = VB == 4 ? (KB == 4 ? 0x10000u : 0u) : six_base + (KB == 3 ? 0x4000u : 0u);
+  static constexpr uint32_t s_base = 0x10000u * ((KB == 4) + (VB == 4));
+  static constexpr uint32_t merge = six_base + 0x4000u * ((KB == 3) + (VB == 3));
+  static constexpr uint32_t bytes = merge + kMaxLutWaves * (2 + 2 * 128) * 4 + 256;
+  static_assert(nbyte_tables <= 2, "at most two byte-indexed tables");
+  static_assert(bytes <= 163840, "LDS budget");
+};
 constexpr float kSlack = 8.0f;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -114,7 +133,8 @@ __attribute__((amdgpu_waves_per_eu(lut_threads(KQ && VQ) / 256, lut_threads(KQ &
 void decode_lut_kernel(DecodeParams p) {
   constexpr int kLutThreads = lut_threads(KQ && VQ);
   constexpr int kLutWaves = kLutThreads / 64;
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  using Map = LutMap<KB, KQ, VB, VQ>;
+  __shared__ __attribute__((aligned(16))) char smem[LutMap<KB, KQ, VB, VQ>::bytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int L = p.L, j = lane & (L - 1), slot = lane / L, vpw = 64 / L;
   const int d = p.d;
@@ -128,36 +148,36 @@ void decode_lut_kernel(DecodeParams p) {
       half2_t h;
       h.x = (_Float16)p.vc[lo];
       h.y = (_Float16)p.vc[hi];
-      *reinterpret_cast<half2_t*>(smem + e * 256 + l * 4) = h;
+      *reinterpret_cast<half2_t*>(smem + Map::v_base + e * 256 + l * 4) = h;
     }
     constexpr int NK = KB == 4 ? 256 : 64;
-    for (int i = threadIdx.x; i < NK * 16; i += kLutThreads) {
-      const int e = i >> 4, l = i & 15;
+    for (int i = threadIdx.x; i < NK * 32; i += kLutThreads) {
+      const int e = i >> 5, l = i & 31;
       const int lo = KB == 4 ? (e & 15) : (e & 7), hi = KB == 4 ? (e >> 4) : (e >> 3);
       float2_t c;
       c.x = p.kc[lo];
       c.y = p.kc[hi];
-      *reinterpret_cast<float2_t*>(smem + kRegionK + e * 256 + l * 8) = c;
+      *reinterpret_cast<float2_t*>(smem + Map::k_base + e * 256 + l * 8) = c;
     }
     if (KQ || VQ) {
-      for (int i = threadIdx.x; i < 256 * 8; i += kLutThreads) {
-        const int e = i >> 3, l = i & 7;
+      for (int i = threadIdx.x; i < 256 * 16; i += kLutThreads) {
+        const int e = i >> 4, l = i & 15;
         half8_t s;
 #pragma unroll
         for (int t = 0; t < 8; ++t) s[t] = ((e >> t) & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
-        *reinterpret_cast<half8_t*>(smem + kRegionK + e * 256 + 128 + l * 16) = s;
+        *reinterpret_cast<half8_t*>(smem + Map::s_base + e * 256 + l * 16) = s;
       }
     }
   }
   __syncthreads();
 
-  const uint32_t lr_v = (uint32_t)lane * 4u;
-  const uint32_t lr_k = kRegionK | ((uint32_t)(lane & 15) << 3);
-  const uint32_t lr_s = kRegionK | (128u + ((uint32_t)(lane & 7) << 4));
+  const uint32_t lr_v = Map::v_base | ((uint32_t)lane * 4u);
+  const uint32_t lr_k = Map::k_base | ((uint32_t)(lane & 31) << 3);
+  const uint32_t lr_s = Map::s_base | ((uint32_t)(lane & 15) << 4);
   // Lane j of a quad streams one per-token scalar: 0 nu_k, 1 gamma_k, 2 nu_v, 3 gamma_v.
   const float* sc_src = j == 0 ? p.k.norms : (j == 1 ? (KQ ? p.k.gamma : p.k.norms)
                                                      : (j == 2 ? p.v.norms : (VQ ? p.v.gamma : p.v.norms)));
-  float* merge = reinterpret_cast<float*>(smem + kMergeBase);
+  float* merge = reinterpret_cast<float*>(smem + Map::merge);
   const int R = p.B * p.Hkv * p.nsplit;
 
   for (int unit = blockIdx.x; unit < p.units; unit += gridDim.x) {
