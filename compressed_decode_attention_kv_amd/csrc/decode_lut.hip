@@ -1,4 +1,4 @@
-// Table-driven split decode for 3- and 4-bit caches (any head dim), the
+// Table-driven split decode for 3- and 4-bit caches at d = 128, the
 // read side of [P1] "Esquemas de Cuantización" (KV, KQV, QKQV at n = 4) and
 // [P2] "Contribuições Principais" 1 (TQ-KV, TQ-QKV).
 //
@@ -10,9 +10,9 @@
 // Same arithmetic as decode_split_kernel (scores and value sums in the
 // rotated domain), organised so that each byte of packed cache costs about
 // one VALU instruction:
-//   * a packed byte (two 4-bit codes) or a 6-bit field (two 3-bit codes) is
-//     turned into an LDS address by one v_perm / v_lshl_or, and one LDS read
-//     returns both centroids;
+//   * a packed byte (two 4-bit codes) is turned into an LDS address by one
+//     v_perm, a 6-bit field (two 3-bit codes) by a shift and one
+//     v_and_or_b32, and one LDS read returns both centroids;
 //   * the LDS tables are replicated across lanes so that every read of a
 //     wave hits distinct banks:
 //       V region  [0, 64K):     entry e at e*256, fp16 pair, one copy per lane (b32)
@@ -25,7 +25,8 @@
 //     per-token scalars (norms, residual norms) are loaded once per quad and
 //     broadcast with DPP;
 //   * all packed data is streamed with non-temporal loads, one token step
-//     ahead of the arithmetic;
+//     ahead of the arithmetic, addressed as a per-head base (scalar) plus a
+//     32-bit per-lane offset;
 //   * one persistent block per CU loops over (query, context chunk) units.
 #include <cfloat>
 #include <cmath>
@@ -35,9 +36,15 @@
 namespace tq {
 namespace {
 
-// Block size: 12 waves (3 per SIMD) where the variant fits in 168 VGPRs,
-// 8 waves for the variant with sketches on both K and V.
+// Block size and token loop, per variant (chosen by measurement):
+//   * sketches on both K and V: 8 waves (2 per SIMD, up to 256 VGPRs) and a
+//     two-buffer token loop;
+//   * a sketch on one side: 12 waves (3 per SIMD, 168 VGPRs) and a
+//     one-buffer loop (prefetch into a second set, then copy), since two
+//     buffers do not fit 168 VGPRs without serialising the table reads;
+//   * no sketch: 12 waves and the two-buffer loop.
 constexpr int lut_threads(bool both_sketched) { return both_sketched ? 512 : 768; }
+constexpr bool lut_two_buffers(bool kq, bool vq) { return kq == vq; }
 constexpr int kMaxLutWaves = 12;
 // LDS map.  A table indexed by a whole packed byte needs a 64 KB window
 // (entry e at window + e*256, the byte lands in address bits 8..15 straight
@@ -74,12 +81,23 @@ __device__ __forceinline__ uint32_t byte_addr(uint32_t w, uint32_t lanereg) {
   return __builtin_amdgcn_perm(w, lanereg, 0x0C020000u | ((4u + K) << 8));
 }
 
-// 6-bit field at bit offset O of a 3-dword run.
+// LDS address of the 6-bit field at bit offset O of a 3-dword run:
+// (field << 8) | lanereg, as one shift (or funnel shift) that puts the field
+// at bits 8..13 and one v_and_or_b32.  The and-or is written out because the
+// compiler otherwise splits it into an and plus an add.
 template <int O>
-__device__ __forceinline__ uint32_t field6(const uint32_t* w) {
+__device__ __forceinline__ uint32_t field6_addr(const uint32_t* w, uint32_t lanereg) {
   constexpr int wi = O >> 5, sh = O & 31;
-  if (sh + 6 <= 32) return __builtin_amdgcn_ubfe(w[wi], sh, 6);
-  return __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh), 0, 6);
+  uint32_t x;
+  if constexpr (sh + 6 <= 32) {
+    if constexpr (sh >= 8) x = w[wi] >> (sh - 8);
+    else x = w[wi] << (8 - sh);
+  } else {
+    x = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh - 8);  // sh >= 27 here
+  }
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(0x3f00u), "v"(lanereg));
+  return r;
 }
 
 __device__ __forceinline__ float quad_sum(float v) {
@@ -102,11 +120,34 @@ struct TokenData {
   float sc;      // this lane's per-token scalar (lane j: nu_k, gamma_k, nu_v, gamma_v)
 };
 
+// Planes of one (batch, kv head): scalar base pointers.
+struct HeadPlanes {
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const uint8_t* ks;
+  const uint8_t* vs;
+};
+
+// A 32-bit lane offset the compiler keeps as is, so that loads take the
+// scalar-base + vector-offset form instead of 64-bit address arithmetic.
+__device__ __forceinline__ uint32_t lane_off(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+template <uint32_t BYTES>
+__device__ __forceinline__ uint32_t token_bytes(uint32_t tr) {
+  if constexpr ((BYTES & (BYTES - 1)) == 0) return tr * BYTES;
+  else return __umul24(tr, BYTES);
+}
+
+// Token tr (index within the head) for lane j.  The host sends only
+// T_cap <= 2^24 here, so tr fits a 24-bit multiply (full rate, unlike a
+// 32-bit one) and every offset fits 32 bits.
 template <int KB, bool KQ, int VB, bool VQ>
-__device__ __forceinline__ void load_token(const DecodeParams& p, int64_t vec, int j, const float* sc_src,
+__device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int j, const float* sc_head,
                                            TokenData<KB, KQ, VB, VQ>& t) {
-  const int d = p.d;
-  const uint32_t* kc = reinterpret_cast<const uint32_t*>(p.k.codes + vec * (d * KB / 8)) + j * KB;
+  const uint32_t* kc = reinterpret_cast<const uint32_t*>(h.kc + lane_off(token_bytes<16u * KB>(tr) + (uint32_t)j * (4u * KB)));
   if constexpr (KB == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc));
     t.k[0] = x.x; t.k[1] = x.y; t.k[2] = x.z; t.k[3] = x.w;
@@ -114,7 +155,7 @@ __device__ __forceinline__ void load_token(const DecodeParams& p, int64_t vec, i
 #pragma unroll
     for (int i = 0; i < KB; ++i) t.k[i] = __builtin_nontemporal_load(kc + i);
   }
-  const uint32_t* vc = reinterpret_cast<const uint32_t*>(p.v.codes + vec * (d * VB / 8)) + j * VB;
+  const uint32_t* vc = reinterpret_cast<const uint32_t*>(h.vc + lane_off(token_bytes<16u * VB>(tr) + (uint32_t)j * (4u * VB)));
   if constexpr (VB == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc));
     t.v[0] = x.x; t.v[1] = x.y; t.v[2] = x.z; t.v[3] = x.w;
@@ -122,9 +163,9 @@ __device__ __forceinline__ void load_token(const DecodeParams& p, int64_t vec, i
 #pragma unroll
     for (int i = 0; i < VB; ++i) t.v[i] = __builtin_nontemporal_load(vc + i);
   }
-  if (KQ) t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.k.qjl + vec * (d / 8)) + j);
-  if (VQ) t.vs = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p.v.qjl + vec * (d / 8)) + j);
-  t.sc = __builtin_nontemporal_load(sc_src + vec);
+  if (KQ) t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.ks + lane_off(tr * 16u + (uint32_t)j * 4u)));
+  if (VQ) t.vs = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.vs + lane_off(tr * 16u + (uint32_t)j * 4u)));
+  t.sc = __builtin_nontemporal_load(sc_head + tr);
 }
 
 template <int KB, bool KQ, int VB, bool VQ>
@@ -136,8 +177,8 @@ void decode_lut_kernel(DecodeParams p) {
   using Map = LutMap<KB, KQ, VB, VQ>;
   __shared__ __attribute__((aligned(16))) char smem[LutMap<KB, KQ, VB, VQ>::bytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int L = p.L, j = lane & (L - 1), slot = lane / L, vpw = 64 / L;
-  const int d = p.d;
+  constexpr int d = 128, L = 4, vpw = 64 / L;  // 4 lanes per token, 16 tokens per wave step
+  const int j = lane & (L - 1), slot = lane / L;
 
   // ---- tables -------------------------------------------------------------------
   {
@@ -188,7 +229,13 @@ void decode_lut_kernel(DecodeParams p) {
     const int b = bkv / p.Hkv, kvh = bkv % p.Hkv;
     const int qi = b * p.Hq + kvh * p.G + g;
     const int t0 = split * p.chunk, t1 = min(p.T, t0 + p.chunk);
-    const int64_t vbase = (int64_t)bkv * p.T_cap;
+    const size_t vbase = (size_t)bkv * p.T_cap;
+    HeadPlanes hp;
+    hp.kc = p.k.codes + vbase * (16 * KB);
+    hp.vc = p.v.codes + vbase * (16 * VB);
+    hp.ks = KQ ? p.k.qjl + vbase * 16 : nullptr;
+    hp.vs = VQ ? p.v.qjl + vbase * 16 : nullptr;
+    const float* sc_head = sc_src + vbase;
 
     float q[32], u[KQ ? 32 : 1];
 #pragma unroll
@@ -208,13 +255,10 @@ void decode_lut_kernel(DecodeParams p) {
 
     const int stride = kLutWaves * vpw;
     int base = t0 + wave * vpw;
-    TokenData<KB, KQ, VB, VQ> nxt;
-    if (base < t1) load_token(p, vbase + min(base + slot, t1 - 1), j, sc_src, nxt);
-    for (; base < t1; base += stride) {
-      TokenData<KB, KQ, VB, VQ> cur = nxt;
-      const int t = base + slot;
+    // One token step of this lane (slot, j): score, online softmax, value sums.
+    auto step = [&](const TokenData<KB, KQ, VB, VQ>& cur, int sbase) {
+      const int t = sbase + slot;
       const bool valid = t < t1;
-      if (base + stride < t1) load_token(p, vbase + min(base + stride + slot, t1 - 1), j, sc_src, nxt);
 
       // ---- key score: this lane's 32 coordinates ---------------------------------
       float sa = 0.f, sb = 0.f;
@@ -233,7 +277,7 @@ void decode_lut_kernel(DecodeParams p) {
       } else {
 #define TQ_KPAIR(M)                                                                            \
         {                                                                                      \
-          const uint32_t a = (field6<6 * (M)>(cur.k) << 8) | lr_k;                             \
+          const uint32_t a = field6_addr<6 * (M)>(cur.k, lr_k);                                \
           const float2_t c = *reinterpret_cast<const float2_t*>(smem + a);                     \
           sa = fmaf(q[2 * (M)], c.x, sa);                                                      \
           sb = fmaf(q[2 * (M) + 1], c.y, sb);                                                  \
@@ -264,7 +308,9 @@ void decode_lut_kernel(DecodeParams p) {
 
       // ---- online softmax (per token slot) ----------------------------------------
       if (s > m + kSlack) {
-        const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - s);
+        // s - m > 8 here and m is finite or -inf: the raw exp2 is exact enough
+        // and gives 0 for m = -inf.
+        const float alpha = __builtin_amdgcn_exp2f(m - s);
         l *= alpha;
 #pragma unroll
         for (int e = 0; e < 32; ++e) acc[e] *= alpha;
@@ -274,7 +320,7 @@ void decode_lut_kernel(DecodeParams p) {
         }
         m = s;
       }
-      const float pt = valid ? exp2f(s - m) : 0.f;
+      const float pt = valid ? __builtin_amdgcn_exp2f(s - m) : 0.f;  // s - m <= 8
       l += pt;
       const float wv = pt * quad_bcast<2>(cur.sc);
 
@@ -294,7 +340,7 @@ void decode_lut_kernel(DecodeParams p) {
       } else {
 #define TQ_VPAIR(M)                                                                            \
         {                                                                                      \
-          const uint32_t a = (field6<6 * (M)>(cur.v) << 8) | lr_v;                             \
+          const uint32_t a = field6_addr<6 * (M)>(cur.v, lr_v);                                \
           const half2_t h = *reinterpret_cast<const half2_t*>(smem + a);                       \
           acc[2 * (M)] = fmaf(wv, (float)h.x, acc[2 * (M)]);                                   \
           acc[2 * (M) + 1] = fmaf(wv, (float)h.y, acc[2 * (M) + 1]);                           \
@@ -313,6 +359,34 @@ void decode_lut_kernel(DecodeParams p) {
         }
         TQ_VSIGN(0) TQ_VSIGN(1) TQ_VSIGN(2) TQ_VSIGN(3)
 #undef TQ_VSIGN
+      }
+    };
+
+    if constexpr (lut_two_buffers(KQ, VQ)) {
+      // Two buffers used in turn, so that the next step's loads never
+      // overwrite registers that the current step still reads (no copies).
+      // The next step is loaded unconditionally (the token index is clamped,
+      // so past the end it re-reads token t1 - 1): with a fixed number of
+      // loads in flight the wait before each step leaves the other buffer's
+      // loads outstanding.
+      TokenData<KB, KQ, VB, VQ> ta, tb;
+      if (base < t1) load_token(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, ta);
+      while (base < t1) {
+        load_token(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, tb);
+        step(ta, base);
+        base += stride;
+        if (base >= t1) break;
+        load_token(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, ta);
+        step(tb, base);
+        base += stride;
+      }
+    } else {
+      TokenData<KB, KQ, VB, VQ> nxt;
+      if (base < t1) load_token(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, nxt);
+      for (; base < t1; base += stride) {
+        const TokenData<KB, KQ, VB, VQ> cur = nxt;
+        if (base + stride < t1) load_token(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, nxt);
+        step(cur, base);
       }
     }
 
