@@ -114,6 +114,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   __shared__ __attribute__((aligned(16))) LutEntry s_lut[kLutMax];
   __shared__ float s_cent[16];
   __shared__ __attribute__((aligned(16))) half8 s_S[kProd ? 8 * 4 * 64 : 1];
+  __shared__ __attribute__((aligned(16))) half8 s_A[8 * 64];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tau = lane & 15, g = lane >> 4;
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
     s_lut[n].base = base;
   }
   if (threadIdx.x < 16) s_cent[threadIdx.x] = p.centroids[threadIdx.x];
-  if (kProd) {
+  if constexpr (kProd) {
     // S_perm[mb][pp][l] = S[16 mb + (l % 16)][16 (2 pp + j / 4) + 4 (l / 16) + j % 4], j < 8.
     for (int i = threadIdx.x; i < 8 * 4 * 64; i += kThreadsM) {
       const int l = i & 63, pp = (i >> 6) & 3, mb = i >> 8;
@@ -148,27 +149,31 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   __syncthreads();
 
   // ---- constant operands of the 16-point blocks: A_a[e][k] = H16[e][k'] D[coord] ----
-  half8 Aop[8];
-#pragma unroll
-  for (int a = 0; a < 8; ++a) {
+  // Kept in LDS (entry a * 64 + lane holds lane's 8 values of operand a) so
+  // that they do not occupy 32 registers for the whole kernel.
+  for (int i = threadIdx.x; i < 8 * 64; i += kThreadsM) {
+    const int a = i >> 6, ln = i & 63, ltau = ln & 15, lg = ln >> 4;
     const int pp = a >> 1, odd = a & 1;
+    half8 op;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int kappa = 8 * g + j;
+      const int kappa = 8 * lg + j;
       float v = 0.f;
       if ((kappa >> 4) == odd) {
         const int bcol = kappa & 15, coord = 32 * pp + kappa;
         if (MODE == TQ_MODE_PLAIN) {
-          v = (bcol == tau) ? 1.f : 0.f;
+          v = (bcol == ltau) ? 1.f : 0.f;
         } else {
-          const float h = parity((uint32_t)(tau & bcol)) ? -1.f : 1.f;
+          const float h = parity((uint32_t)(ltau & bcol)) ? -1.f : 1.f;
           const float dsg = ((p.signbits[coord >> 5] >> (coord & 31)) & 1u) ? -1.f : 1.f;
           v = h * dsg;
         }
       }
-      Aop[a][j] = (_Float16)v;
+      op[j] = (_Float16)v;
     }
+    s_A[i] = op;
   }
+  __syncthreads();
 
   const int64_t N = (int64_t)p.B * p.H * p.T;
   const int64_t ntiles = (N + 15) >> 4;
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
       float4v z = {0.f, 0.f, 0.f, 0.f};
-      Z[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aop[a], xin[a >> 1], z, 0, 0, 0);
+      Z[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_A[a * 64 + lane], xin[a >> 1], z, 0, 0, 0);
     }
     float y[8][4];  // y[c][i] <-> coordinate 16c + 4g + i
 #pragma unroll
@@ -285,19 +290,24 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         for (int i = 0; i < 4; ++i) g2 = fmaf(y[c][i], y[c][i], g2);
       g2 += __shfl_xor(g2, 16, 64);
       g2 += __shfl_xor(g2, 32, 64);
+      // Exact-enough fp16 split of the scaled residual: hi rounds toward
+      // zero, so r - hi is exact in fp32 and lo keeps its leading 11 bits.
       half8 Bhi[4], Blo[4];
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float r = y[2 * pp + j / 4][j & 3] * rs;
-          const _Float16 hi = (_Float16)r;
-          Bhi[pp][j] = hi;
-          Blo[pp][j] = (_Float16)(r - (float)hi);
+        for (int j = 0; j < 8; j += 2) {
+          const float r0 = y[2 * pp + j / 4][j & 3] * rs, r1 = y[2 * pp + (j + 1) / 4][(j + 1) & 3] * rs;
+          const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+          const half2v lo = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0 - (float)hi.x, r1 - (float)hi.y));
+          Bhi[pp][j] = hi.x; Bhi[pp][j + 1] = hi.y;
+          Blo[pp][j] = lo.x; Blo[pp][j + 1] = lo.y;
         }
       }
-      uint32_t schunk[8];
-#pragma unroll
+      // Two 16-row blocks of S in flight at a time keeps the S operands
+      // (LDS reads) from all being hoisted into registers.
+      uint32_t sbits = 0;  // 4 sign bits per row block mb
+#pragma unroll 2
       for (int mb = 0; mb < 8; ++mb) {
         float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -309,8 +319,11 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         uint32_t sc = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc |= (acc[i] >= 0.f ? 1u : 0u) << i;
-        schunk[mb] = sc;
+        sbits |= sc << (4 * mb);
       }
+      uint32_t schunk[8];
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) schunk[mb] = (sbits >> (4 * mb)) & 15u;
       uint32_t sw[1];
       merge_chunks<1>(schunk, g, sw);
       if (valid) {
