@@ -19,11 +19,14 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # Keep the compiler from emitting packed-FP32 VALU instructions.
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(PKG, "..", "include")]
+# Per-source extras.  The quantiser's matrix-core results are read by vector
+# code right away: keep them in ordinary VGPRs (no accumulator-register copies).
+EXTRA = {"quant_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src):
     obj = os.path.join(OUT, src + ".o")
-    cmd = ["hipcc"] + FLAGS + ["-c", os.path.join(SRC, src), "-o", obj]
+    cmd = ["hipcc"] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(SRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)

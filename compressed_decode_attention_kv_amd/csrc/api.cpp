@@ -400,7 +400,7 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
   if (quant_mfma_supported(p) && quant_grid(x->d, bits, &grid)) {
     int cus = 0;
     if (tq_status s = hip_status(cu_count(&cus), "device query")) return s;
-    const long tiles = ((long)x->B * x->H * x->T + 15) / 16;
+    const long tiles = (long)x->B * x->H * ((x->T + 15) / 16);  // 16-token tiles within a head
     const int nblocks = (int)std::max<long>(1, std::min<long>((tiles + 3) / 4, (long)cus * 8));
     if (tq_status s = hip_status(launch_quantize_mfma(p, grid, nblocks, (hipStream_t)stream), "quantize launch")) return s;
   } else {

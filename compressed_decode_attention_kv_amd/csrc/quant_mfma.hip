@@ -7,25 +7,29 @@
 //
 // Same result as quant_kernel (norm split, seeded sign flip + normalised
 // Walsh-Hadamard rotation, Beta Lloyd-Max index, LSB-first packing, QJL
-// sketch of the rotated residual), organised as:
-//   * rotation: H_128 = H_8 (x) H_16.  The 16-point blocks run on
-//     v_mfma_f32_16x16x32_f16 with the constant operand H_16 diag(D_block)
-//     (fp16 inputs times +-1 are exact, accumulation fp32); the 8-point
-//     stage across blocks is three in-register butterfly stages.  A wave
-//     handles 16 tokens; afterwards lane (g, tau) holds coordinates
-//     16c + 4g + i (c < 8, i < 4) of token tau.
-//   * index: one fma with a 1.5*2^23 bias yields the grid cell of y and,
-//     shifted, the LDS address of that cell's entry (boundary inside the
-//     cell and its two neighbours, count of boundaries below); one compare
-//     finishes the Lloyd-Max index.
-//   * packing: 4-index chunks are merged across the four lanes of a token
-//     in two exchange rounds, after which lane g holds the `bits` whole
-//     dwords [bits*g, bits*g + bits) of the token's code block.
+// sketch of the rotated residual), organised so that every lane ends up
+// owning 32 consecutive coordinates of one token and writes its own code
+// and sign words without any exchange:
+//   * rotation: a Sylvester Hadamard entry is a product over index bits, so
+//     H_128 = H_16 (x) H_8 with the 16-point factor acting on bits 3..6 and
+//     the 8-point factor on bits 0..2.  The 16-point part runs on
+//     v_mfma_f32_16x16x32_f16, one product per value a of the low bits, with
+//     the constant operand H_16 diag(D) (fp16 inputs times +-1 are exact,
+//     accumulation fp32); the 8-point part is three in-register butterfly
+//     stages over the 8 products.  A wave handles 16 tokens; the product's
+//     row index is the high output bits, so lane (g, tau) holds coordinates
+//     32 g + 8 i + a (i < 4, a < 8) of token tau.
+//   * index: one fma with a biased 1.5*2^23 constant yields the grid cell of
+//     y and, shifted, the LDS address of that cell's entry (boundary inside
+//     the cell and its two neighbours, count of boundaries below); one
+//     compare finishes the Lloyd-Max index, which goes straight into the
+//     lane's `bits` code dwords.
 //   * QJL ([P1] "Contribuciones Clave" 1): S r on the matrix cores.  S is
-//     exact in fp16; the residual, scaled by 2^12, is split exactly enough
-//     into fp16 hi + lo parts (two MFMAs per tile, fp32 accumulation).
-//     The 16x16 output tiles have the same lane layout as the codes, so the
-//     sign bits are packed by the same exchange.
+//     exact in fp16; the residual, scaled by 2^12, is split into fp16 hi
+//     (rounded toward zero) + lo parts, so r - hi is exact and two products
+//     per tile with fp32 accumulation keep about 22 bits.  The rows of S are
+//     ordered so that lane (g, tau) receives sketch rows 32 g .. 32 g + 31:
+//     its 32 sign bits are word g of the token's sign block.
 #include <cfloat>
 #include <cmath>
 
@@ -52,60 +56,13 @@ struct LutEntry {
 
 __device__ __forceinline__ int parity(uint32_t x) { return __builtin_popcount(x) & 1; }
 
-// Merge 4-index chunks (each 4*B bits, chunk c covers coordinates
-// 16c + 4g .. 16c + 4g + 3 of the lane group's token) across the four lanes
-// g = 0..3 of the token (lanes tau + 16 g).  Returns, in out[], the B dwords
-// of bits [32 B g, 32 B g + 32 B) of the token's bitstream.
-template <int B>
-__device__ __forceinline__ void merge_chunks(const uint32_t* chunk, int g, uint32_t* out) {
-  const int s = g & 1, t = g >> 1;
-  uint32_t kept[4], half[4];
-  uint32_t o01, o23;
-  {
-    uint32_t out4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lo_c = (q & 1) | ((q >> 1) << 2), hi_c = lo_c | 2;
-      kept[q] = s ? chunk[hi_c] : chunk[lo_c];
-      out4[q] = s ? chunk[lo_c] : chunk[hi_c];
-    }
-    o01 = out4[0] | (out4[1] << 16);
-    o23 = out4[2] | (out4[3] << 16);
-  }
-  const uint32_t i01 = shfl_xor_u(o01, 16), i23 = shfl_xor_u(o23, 16);
-  const uint32_t in4[4] = {i01 & 0xFFFFu, i01 >> 16, i23 & 0xFFFFu, i23 >> 16};
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    half[q] = s ? (in4[q] | (kept[q] << (4 * B))) : (kept[q] | (in4[q] << (4 * B)));
-  // Round 2: keep blocks 2g, 2g+1.
-  uint32_t keep2[2], send2[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    keep2[r] = t ? half[2 + r] : half[r];
-    send2[r] = t ? half[r] : half[2 + r];
-  }
-  uint64_t blk[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const uint64_t in = shfl_xor_u(send2[r], 32);
-    blk[r] = t ? (in | ((uint64_t)keep2[r] << (8 * B))) : ((uint64_t)keep2[r] | (in << (8 * B)));
-  }
-  // Concatenate the two 16B-bit blocks: 32B bits = B dwords.
-  if (B == 1) {
-    out[0] = (uint32_t)(blk[0] | (blk[1] << 16));
-  } else if (B == 2) {
-    out[0] = (uint32_t)blk[0];
-    out[1] = (uint32_t)blk[1];
-  } else if (B == 3) {
-    out[0] = (uint32_t)blk[0];
-    out[1] = (uint32_t)(blk[0] >> 32) | (uint32_t)(blk[1] << 16);
-    out[2] = (uint32_t)(blk[1] >> 16);
-  } else {
-    out[0] = (uint32_t)blk[0];
-    out[1] = (uint32_t)(blk[0] >> 32);
-    out[2] = (uint32_t)blk[1];
-    out[3] = (uint32_t)(blk[1] >> 32);
-  }
+// Put the BITS-bit index of coordinate O (of the lane's 32) into its place
+// in the lane's LSB-first bitstream words.
+template <int BITS, int O>
+__device__ __forceinline__ void put_index(uint32_t* words, uint32_t idx) {
+  constexpr int bit = BITS * O, w = bit >> 5, sh = bit & 31;
+  words[w] |= idx << sh;
+  if constexpr (sh + BITS > 32) words[w + 1] |= idx >> (32 - sh);
 }
 
 template <int BITS, int MODE>
@@ -116,7 +73,8 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   __shared__ __attribute__((aligned(16))) half8 s_S[kProd ? 8 * 4 * 64 : 1];
   __shared__ __attribute__((aligned(16))) half8 s_A[8 * 64];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tau = lane & 15, g = lane >> 4;
   constexpr int NB = (1 << BITS) - 1;
 
@@ -136,35 +94,33 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   }
   if (threadIdx.x < 16) s_cent[threadIdx.x] = p.centroids[threadIdx.x];
   if constexpr (kProd) {
-    // S_perm[mb][pp][l] = S[16 mb + (l % 16)][16 (2 pp + j / 4) + 4 (l / 16) + j % 4], j < 8.
+    // Operand (mb, pp), lane (gk, e): S[row][col + j], j < 8, with
+    // row = 32 (e / 4) + 4 mb + e % 4 and col = 32 gk + 8 pp.
     for (int i = threadIdx.x; i < 8 * 4 * 64; i += kThreadsM) {
       const int l = i & 63, pp = (i >> 6) & 3, mb = i >> 8;
-      const int row = 16 * mb + (l & 15), gg = l >> 4;
+      const int e = l & 15, gk = l >> 4;
+      const int row = 32 * (e >> 2) + 4 * mb + (e & 3), col = 32 * gk + 8 * pp;
       half8 v;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = (_Float16)p.S[row * 128 + 16 * (2 * pp + j / 4) + 4 * gg + (j & 3)];
+      for (int j = 0; j < 8; ++j) v[j] = (_Float16)p.S[row * 128 + col + j];
       s_S[i] = v;
     }
   }
-  __syncthreads();
-
-  // ---- constant operands of the 16-point blocks: A_a[e][k] = H16[e][k'] D[coord] ----
-  // Kept in LDS (entry a * 64 + lane holds lane's 8 values of operand a) so
-  // that they do not occupy 32 registers for the whole kernel.
+  // Rotation operand a (low input bits = a), lane (gA, e): slot j < 4 is the
+  // high input index jh = 4 j + gA, value H16[e][jh] D[8 jh + a] (identity
+  // for PLAIN); slots 4..7 are zero (the product uses half of its K = 32).
   for (int i = threadIdx.x; i < 8 * 64; i += kThreadsM) {
-    const int a = i >> 6, ln = i & 63, ltau = ln & 15, lg = ln >> 4;
-    const int pp = a >> 1, odd = a & 1;
+    const int a = i >> 6, ln = i & 63, e = ln & 15, gA = ln >> 4;
     half8 op;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int kappa = 8 * lg + j;
       float v = 0.f;
-      if ((kappa >> 4) == odd) {
-        const int bcol = kappa & 15, coord = 32 * pp + kappa;
+      if (j < 4) {
+        const int jh = 4 * j + gA, coord = 8 * jh + a;
         if (MODE == TQ_MODE_PLAIN) {
-          v = (bcol == ltau) ? 1.f : 0.f;
+          v = (e == jh) ? 1.f : 0.f;
         } else {
-          const float h = parity((uint32_t)(ltau & bcol)) ? -1.f : 1.f;
+          const float h = parity((uint32_t)(e & jh)) ? -1.f : 1.f;
           const float dsg = ((p.signbits[coord >> 5] >> (coord & 31)) & 1u) ? -1.f : 1.f;
           v = h * dsg;
         }
@@ -175,19 +131,25 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   }
   __syncthreads();
 
-  const int64_t N = (int64_t)p.B * p.H * p.T;
-  const int64_t ntiles = (N + 15) >> 4;
-  const float magic = 12582912.0f;  // 1.5 * 2^23: fma(y, s, magic) rounds y*s to an integer in the low bits
+  // Tiles are 16 consecutive tokens of one (b, h); the host guarantees that
+  // the tile count and every per-head byte offset fit 31 / 32 bits.
+  const int tph = (p.T + 15) >> 4;
+  const int ntiles = p.B * p.H * tph;
+  // 1.5 * 2^23 + center: fma(y, scale, bias) leaves round(y * scale) + center
+  // in the low mantissa bits, so (bits << 3) + const is the entry's LDS offset.
+  const float bias = 12582912.0f + (float)grid.center;
+  const char* lut_bytes = reinterpret_cast<const char*>(s_lut);
   const float inv_sqrt_d = p.inv_sqrt_d;
 
-  for (int64_t tile = (int64_t)blockIdx.x * kWavesM + wave; tile < ntiles; tile += (int64_t)gridDim.x * kWavesM) {
-    const int64_t v = tile * 16 + tau;
-    const bool valid = v < N;
-    const int64_t vc = valid ? v : N - 1;
-    const int bh = (int)(vc / p.T), t = (int)(vc % p.T);
-    const int b = bh / p.H, h = bh % p.H;
+  for (int tile = blockIdx.x * kWavesM + wave; tile < ntiles; tile += gridDim.x * kWavesM) {
+    const int bh = tile / tph;
+    const int t = (tile - bh * tph) * 16 + tau;
+    const bool valid = t < p.T;
+    const int tc = valid ? t : p.T - 1;
+    const int b = bh / p.H, h = bh - b * p.H;
     const _Float16* xrow = reinterpret_cast<const _Float16*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh +
-                           (int64_t)t * p.st;
+                           (int64_t)tc * p.st;
+    // xin[pp][j] = x[32 pp + 8 g + j]: high input index 4 pp + g, low index j.
     half8 xin[4];
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) xin[pp] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(xrow + 32 * pp + 8 * g));
@@ -209,13 +171,24 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
     const float nu = sqrtf(ss);
 
     // ---- rotation -------------------------------------------------------------------
+    u32x4 xw[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) xw[pp] = __builtin_bit_cast(u32x4, xin[pp]);
     float4v Z[8];
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
-      float4v z = {0.f, 0.f, 0.f, 0.f};
-      Z[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_A[a * 64 + lane], xin[a >> 1], z, 0, 0, 0);
+      // B slot j < 4 = x[8 (4 j + g) + a] = xin[j][a].
+      const uint32_t sel = (a & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 bw;
+      bw.x = __builtin_amdgcn_perm(xw[1][a >> 1], xw[0][a >> 1], sel);
+      bw.y = __builtin_amdgcn_perm(xw[3][a >> 1], xw[2][a >> 1], sel);
+      bw.z = 0u;
+      bw.w = 0u;
+      const float4v z = {0.f, 0.f, 0.f, 0.f};
+      Z[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_A[a * 64 + lane], __builtin_bit_cast(half8, bw), z, 0, 0, 0);
     }
-    float y[8][4];  // y[c][i] <-> coordinate 16c + 4g + i
+    // y[i][a] <-> coordinate 32 g + 8 i + a.
+    float y[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float w8[8];
@@ -235,32 +208,35 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         }
       }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) y[c][i] = w8[c];
+      for (int a = 0; a < 8; ++a) y[i][a] = w8[a];
     }
     const float inv = nu > 0.f ? (MODE == TQ_MODE_PLAIN ? 1.0f / nu : inv_sqrt_d / nu) : 0.f;
 
-    // ---- index ------------------------------------------------------------------------
-    uint32_t chunk[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t ch = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float yy = y[c][i] * inv;
-        y[c][i] = yy;
-        const float f = fmaf(yy, grid.scale, magic);
-        const LutEntry e = s_lut[(int)(__float_as_uint(f) - 0x4B400000u) + grid.center];
-        const uint32_t idx = e.base + (yy >= e.t ? 1u : 0u);
-        ch |= idx << (BITS * i);
-        if (kProd) y[c][i] = yy - s_cent[idx];   // residual
-      }
-      chunk[c] = ch;
-    }
+    // ---- index and packing ----------------------------------------------------------
     uint32_t words[BITS];
-    merge_chunks<BITS>(chunk, g, words);
-    const int64_t vec = (int64_t)bh * p.T_cap + t;
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) words[k] = 0;
+#define TQ_QIDX(I, A)                                                                          \
+    {                                                                                          \
+      const float yy = y[I][A] * inv;                                                          \
+      const float f = fmaf(yy, grid.scale, bias);                                              \
+      const LutEntry e = *reinterpret_cast<const LutEntry*>(                                   \
+          lut_bytes + ((__float_as_uint(f) << 3) - (0x4B400000u << 3)));                       \
+      const uint32_t idx = e.base + (yy >= e.t ? 1u : 0u);                                     \
+      put_index<BITS, 8 * (I) + (A)>(words, idx);                                              \
+      y[I][A] = kProd ? yy - s_cent[idx] : yy;                                                 \
+    }
+#define TQ_QROW(I) TQ_QIDX(I, 0) TQ_QIDX(I, 1) TQ_QIDX(I, 2) TQ_QIDX(I, 3) \
+                   TQ_QIDX(I, 4) TQ_QIDX(I, 5) TQ_QIDX(I, 6) TQ_QIDX(I, 7)
+    TQ_QROW(0) TQ_QROW(1) TQ_QROW(2) TQ_QROW(3)
+#undef TQ_QROW
+#undef TQ_QIDX
+
+    // Per-head planes: scalar base + 32-bit lane offset.
+    const size_t vbase = (size_t)bh * p.T_cap;
     if (valid) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vec * (16 * BITS)) + BITS * g;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vbase * (16 * BITS) +
+                                                  (uint32_t)(t * (16 * BITS) + g * (4 * BITS)));
       if (!(nu > 0.f)) {
 #pragma unroll
         for (int k = 0; k < BITS; ++k) words[k] = 0;
@@ -277,36 +253,36 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       } else {
         dst[0] = words[0];
       }
-      if (g == 0) p.norms[vec] = nu;
+      if (g == 0) p.norms[vbase + t] = nu;
     }
 
-    if (kProd) {
+    if constexpr (kProd) {
       // ---- QJL sketch of the residual ----------------------------------------------
       const float rs = nu > 0.f ? 4096.0f : 0.f;
       float g2 = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) g2 = fmaf(y[c][i], y[c][i], g2);
+        for (int a = 0; a < 8; ++a) g2 = fmaf(y[i][a], y[i][a], g2);
       g2 += __shfl_xor(g2, 16, 64);
       g2 += __shfl_xor(g2, 32, 64);
-      // Exact-enough fp16 split of the scaled residual: hi rounds toward
-      // zero, so r - hi is exact in fp32 and lo keeps its leading 11 bits.
+      // Operand pp, slot j = coordinate 32 g + 8 pp + j = y[pp][j].
       half8 Bhi[4], Blo[4];
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-          const float r0 = y[2 * pp + j / 4][j & 3] * rs, r1 = y[2 * pp + (j + 1) / 4][(j + 1) & 3] * rs;
+          const float r0 = y[pp][j] * rs, r1 = y[pp][j + 1] * rs;
           const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0, r1));
           const half2v lo = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0 - (float)hi.x, r1 - (float)hi.y));
           Bhi[pp][j] = hi.x; Bhi[pp][j + 1] = hi.y;
           Blo[pp][j] = lo.x; Blo[pp][j + 1] = lo.y;
         }
       }
-      // Two 16-row blocks of S in flight at a time keeps the S operands
-      // (LDS reads) from all being hoisted into registers.
-      uint32_t sbits = 0;  // 4 sign bits per row block mb
+      // Row block mb gives lane (g, tau) sketch rows 32 g + 4 mb + i, i < 4:
+      // bits 4 mb + i of the lane's sign word.  Two blocks in flight at a time
+      // keep the S operands (LDS reads) from all being hoisted into registers.
+      uint32_t sbits = 0;
 #pragma unroll 2
       for (int mb = 0; mb < 8; ++mb) {
         float4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -321,14 +297,9 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         for (int i = 0; i < 4; ++i) sc |= (acc[i] >= 0.f ? 1u : 0u) << i;
         sbits |= sc << (4 * mb);
       }
-      uint32_t schunk[8];
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) schunk[mb] = (sbits >> (4 * mb)) & 15u;
-      uint32_t sw[1];
-      merge_chunks<1>(schunk, g, sw);
       if (valid) {
-        reinterpret_cast<uint32_t*>(p.qjl + vec * 16)[g] = nu > 0.f ? sw[0] : 0u;
-        if (g == 0) p.gamma[vec] = nu > 0.f ? sqrtf(g2) : 0.f;
+        *reinterpret_cast<uint32_t*>(p.qjl + vbase * 16 + (uint32_t)(t * 16 + g * 4)) = nu > 0.f ? sbits : 0u;
+        if (g == 0) p.gamma[vbase + t] = nu > 0.f ? sqrtf(g2) : 0.f;
       }
     }
   }
@@ -343,7 +314,10 @@ hipError_t launch_m(const QuantParams& p, const QuantGrid& grid, int nblocks, hi
 }  // namespace
 
 bool quant_mfma_supported(const QuantParams& p) {
-  return p.d == 128 && p.dtype == TQ_F16 && p.mode != TQ_MODE_HEADQ && p.bits >= 1 && p.bits <= 4;
+  // 32-bit tile indices and per-head byte offsets (at most 64 bytes per token).
+  const long tiles = (long)p.B * p.H * ((p.T + 15) / 16);
+  return p.d == 128 && p.dtype == TQ_F16 && p.mode != TQ_MODE_HEADQ && p.bits >= 1 && p.bits <= 4 &&
+         tiles < (1L << 31) && p.T_cap <= (1 << 24);
 }
 
 int quant_mfma_lut_max() { return kLutMax; }
