@@ -37,14 +37,6 @@ def packed_bytes_total(kp, vp):
     return n // 16 * 16
 
 
-def _decode_sources_sha():
-    import hashlib
-    h = hashlib.sha1()
-    for f in ("decode_lut.hip", "decode.hip", "device_common.h", "internal.h"):
-        h.update(open(os.path.join(ROOT, "compressed_decode_attention_kv_amd", "csrc", f), "rb").read())
-    return h.hexdigest()
-
-
 def measured_traffic(scheme):
     """HBM bytes per decode-chain launch from the committed rocprofv3 counter
     summary, if it was taken on the current decode sources (else None)."""
@@ -56,7 +48,8 @@ def measured_traffic(scheme):
         if "=" in line and not line.startswith("#"):
             k, v = line.strip().split("=", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("decode_sources_sha1") != _decode_sources_sha():
+    from compressed_decode_attention_kv_amd.profiling import decode_sources_sha
+    if fields.get("decode_sources_sha1") != decode_sources_sha():
         return None
     return float(fields["decode_chain_bytes"])
 
@@ -204,6 +197,7 @@ def main():
         "decode_ms": round(d_avg, 4),
         "decode_pct_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
         "stream_read_GBps": round(stream_gbs, 1),
+        "stream_read_bytes": int(packed_bytes_total(kp, vp)),
         "decode_pct_of_stream_read": round(100.0 * dec_gbs / stream_gbs, 2),
         "quantize_ms": round(q_avg, 4),
         "quantize_tok_per_s": round(tok_s, 1),

@@ -3,8 +3,13 @@
   python -m compressed_decode_attention_kv_amd.profiling stats <kernel_stats.csv>
   python -m compressed_decode_attention_kv_amd.profiling traffic <fetch counter_collection.csv> \
         <write counter_collection.csv> --calib-bytes N
+  python -m compressed_decode_attention_kv_amd.profiling decode-traffic <fetch csv> <write csv> \
+        --calib-bytes N --algorithmic-bytes A --title "..." --command "..." [--command ...]
 
-`stats` prints the average duration per kernel.  `traffic` prints HBM bytes
+`stats` prints the average duration per kernel.  `decode-traffic` writes the
+committed per-scheme summary: the traffic table, the decode chain's bytes
+(query prep + split decode + combine) and the hash of the decode sources it
+was measured on (a summary taken on other sources is not used).  `traffic` prints HBM bytes
 per dispatch from the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch),
 the fetch side scaled by what the same counter reads for the library's
 streaming-read kernel over a buffer of N bytes (non-temporal loads count at
@@ -14,8 +19,22 @@ counter matches the known write volume of the quantize kernels).
 import argparse
 import collections
 import csv
+import hashlib
+import os
 import re
 import sys
+
+DECODE_SOURCES = ("decode_lut.hip", "decode.hip", "device_common.h", "internal.h")
+CHAIN = ("qprep_kernel", "decode_lut_kernel", "decode_split_kernel", "combine_kernel")
+
+
+def decode_sources_sha():
+    """sha1 over the sources of the decode chain's kernels."""
+    h = hashlib.sha1()
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(src, f), "rb").read())
+    return h.hexdigest()
 
 
 def short(name):
@@ -47,22 +66,54 @@ def _per_kernel(path, counter):
     return agg, grid
 
 
-def traffic(fetch_path, write_path, calib_bytes, write_factor=1.0):
+def _traffic_table(fetch_path, write_path, calib_bytes, write_factor):
     fetch, _ = _per_kernel(fetch_path, "FETCH_SIZE")
     write, _ = _per_kernel(write_path, "WRITE_SIZE")
     cal = [k for k in fetch if "stream_read" in k]
     if not cal:
         raise SystemExit("no streaming-read dispatch in %s" % fetch_path)
     fetch_factor = calib_bytes / (sum(fetch[cal[0]]) / len(fetch[cal[0]]) * 1024.0)
-    out = ["fetch factor (bytes per counted byte; streaming read of %d B): %.4f" % (calib_bytes, fetch_factor),
-           "write factor: %.4f" % write_factor,
-           "%-90s %16s %16s" % ("kernel", "fetch_bytes", "write_bytes")]
+    rows = []
     for k in sorted(fetch):
         if "tq" not in k and "stream_read" not in k:
             continue
         f = sum(fetch[k]) / len(fetch[k]) * 1024.0 * fetch_factor
         w = sum(write.get(k, [0])) / max(1, len(write.get(k, [0]))) * 1024.0 * write_factor
-        out.append("%-90s %16.6g %16.6g" % (short(k), f, w))
+        rows.append((short(k), f, w))
+    return fetch_factor, rows
+
+
+def traffic(fetch_path, write_path, calib_bytes, write_factor=1.0):
+    fetch_factor, rows = _traffic_table(fetch_path, write_path, calib_bytes, write_factor)
+    out = ["fetch factor (bytes per counted byte; streaming read of %d B): %.4f" % (calib_bytes, fetch_factor),
+           "write factor: %.4f" % write_factor,
+           "%-90s %16s %16s" % ("kernel", "fetch_bytes", "write_bytes")]
+    out += ["%-90s %16.6g %16.6g" % r for r in rows]
+    return "\n".join(out)
+
+
+def decode_traffic(fetch_path, write_path, calib_bytes, algorithmic, title, commands, write_factor=1.0):
+    fetch_factor, rows = _traffic_table(fetch_path, write_path, calib_bytes, write_factor)
+    chain = [r for r in rows if r[0].startswith(CHAIN)]
+    cf = sum(r[1] for r in chain)
+    cw = sum(r[2] for r in chain)
+    out = ["# " + title]
+    out += ["#   " + c for c in commands]
+    out += ["# The fetch counter is scaled by the streaming-read kernel over %d bytes" % calib_bytes,
+            "# (the packed planes' size; non-temporal loads count at half their size).",
+            "#",
+            "# fetch factor (bytes per counted byte): %.4f" % fetch_factor,
+            "# write factor: %.4f" % write_factor,
+            "# %-90s %16s %16s" % ("kernel", "fetch_bytes", "write_bytes")]
+    out += ["# %-90s %16.6g %16.6g" % r for r in rows]
+    out += ["#",
+            "# decode chain = %s; algorithmic packed bytes = %d" % (" + ".join(r[0].split("(")[0] for r in chain),
+                                                                   algorithmic),
+            "decode_sources_sha1 = %s" % decode_sources_sha(),
+            "decode_chain_fetch_bytes = %.6g" % cf,
+            "decode_chain_write_bytes = %.6g" % cw,
+            "decode_chain_bytes = %.6g" % (cf + cw),
+            "ratio_to_algorithmic = %.4f" % ((cf + cw) / algorithmic)]
     return "\n".join(out)
 
 
@@ -76,11 +127,22 @@ def main(argv=None):
     t.add_argument("write_csv")
     t.add_argument("--calib-bytes", type=int, required=True)
     t.add_argument("--write-factor", type=float, default=1.0)
+    dt = sub.add_parser("decode-traffic")
+    dt.add_argument("fetch_csv")
+    dt.add_argument("write_csv")
+    dt.add_argument("--calib-bytes", type=int, required=True)
+    dt.add_argument("--algorithmic-bytes", type=int, required=True)
+    dt.add_argument("--title", required=True)
+    dt.add_argument("--command", action="append", default=[])
+    dt.add_argument("--write-factor", type=float, default=1.0)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats(a.csv))
-    else:
+    elif a.cmd == "traffic":
         print(traffic(a.fetch_csv, a.write_csv, a.calib_bytes, a.write_factor))
+    else:
+        print(decode_traffic(a.fetch_csv, a.write_csv, a.calib_bytes, a.algorithmic_bytes, a.title, a.command,
+                             a.write_factor))
 
 
 if __name__ == "__main__":
