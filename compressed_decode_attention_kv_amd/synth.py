@@ -146,3 +146,70 @@ def device_isotropic(B, H, G, T, d, seed=1, device="cuda"):
     V = (torch.randn((B, H, T, d), generator=g, device=device, dtype=torch.float32) * s).half()
     Q = torch.randn((B, H * G, d), generator=g, device=device, dtype=torch.float32).half()
     return K, V, Q
+
+
+def device_heavy_tailed(B, H, T, d, seed=3, frac=0.01, mag=20.0, device="cuda"):
+    """Full-size heavy-tailed regime drawn on the device: K, V [B,H,T,d]
+    float32, Student-t(3)/sqrt(3) per coordinate (normal over the root of a
+    chi-square with 3 degrees of freedom / 3), with a `frac` fraction of token
+    vectors carrying one +-`mag` outlier coordinate; K and V independent."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = []
+    for _ in range(2):
+        X = torch.empty((B, H, T, d), device=device, dtype=torch.float32)
+        for b in range(B):  # one batch row at a time bounds the temporaries
+            z = torch.randn((H, T, d), generator=g, device=device)
+            chi2 = torch.zeros_like(z)
+            for _ in range(3):
+                e = torch.randn((H, T, d), generator=g, device=device)
+                chi2.addcmul_(e, e)
+            X[b] = z / torch.sqrt(chi2 / 3.0) / math.sqrt(3.0)
+        hit = torch.rand((B, H, T), generator=g, device=device) < frac
+        coord = torch.randint(0, d, (B, H, T), generator=g, device=device)
+        sign = torch.where(torch.rand((B, H, T), generator=g, device=device) < 0.5, -1.0, 1.0)
+        rows = torch.nonzero(hit.reshape(-1)).squeeze(1)
+        flat = X.view(-1, d)
+        flat[rows, coord.reshape(-1)[rows]] = sign.reshape(-1)[rows] * mag
+        out.append(X)
+    return out[0], out[1]
+
+
+def device_rope_gqa(B, Hkv, G, T, d, seed=5, n_calib=4096, decay=0.7, device="cuda"):
+    """Full-size post-RoPE GQA regime, the law of rope_gqa drawn on the device:
+    keys [B,Hkv,T,d] float16 = RoPE(N(0,1), position t), values N(0,1)
+    float16, queries [B,Hkv*G,d] float16 with pair variance ~ decay^i rotated
+    to position T; calibration queries [Hkv, n_calib, d] float32 drawn on the
+    host (numpy) from the same law at uniform positions in [0, T)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    i = torch.arange(d // 2, device=device, dtype=torch.float64)
+    theta = 10000.0 ** (-2.0 * i / d)
+    lam_np = decay ** np.arange(d // 2)
+    lam_np = lam_np * (d / (2.0 * lam_np.sum()))
+    pair_std = torch.from_numpy(np.repeat(np.sqrt(lam_np), 2)).float().to(device)
+
+    def rope(X, pos):
+        ang = pos.to(torch.float64)[..., None] * theta
+        c, s = torch.cos(ang).float(), torch.sin(ang).float()
+        x0, x1 = X[..., 0::2], X[..., 1::2]
+        r = torch.empty_like(X)
+        r[..., 0::2] = x0 * c - x1 * s
+        r[..., 1::2] = x0 * s + x1 * c
+        return r
+
+    pos = torch.arange(T, device=device)
+    K = torch.empty((B, Hkv, T, d), dtype=torch.float16, device=device)
+    for b in range(B):
+        K[b] = rope(torch.randn((Hkv, T, d), generator=g, device=device), pos).half()
+    V = torch.empty((B, Hkv, T, d), dtype=torch.float16, device=device)
+    for b in range(B):
+        V[b] = torch.randn((Hkv, T, d), generator=g, device=device).half()
+    Qr = torch.randn((B, Hkv * G, d), generator=g, device=device) * pair_std
+    Q = rope(Qr, torch.full((B, Hkv * G), T, device=device)).half()
+    crng = _np_rng(seed, 3)
+    cpos = crng.integers(0, T, size=(Hkv, n_calib))
+    C = _rope(crng.standard_normal((Hkv, n_calib, d)) * np.repeat(np.sqrt(lam_np), 2), cpos, d)
+    return K, V, Q, C.astype(np.float32)

@@ -238,14 +238,29 @@ class PackedTensor:
         return out
 
 
+def _check_basis(basis, x, H, d):
+    """The ABI reads the HeadQ basis as a dense float32 [H][d][rank] array at
+    basis.data_ptr(): refuse anything else (a strided view would be read in
+    the wrong order)."""
+    torch = _torch()
+    if basis is None:
+        raise ValueError("HeadQ keys need a basis [H, d, rank]")
+    if basis.dtype != torch.float32 or basis.dim() != 3 or tuple(basis.shape[:2]) != (H, d):
+        raise ValueError("HeadQ basis must be float32 [H=%d, d=%d, rank], got %s %s"
+                         % (H, d, basis.dtype, tuple(basis.shape)))
+    if not basis.is_contiguous():
+        raise ValueError("HeadQ basis must be contiguous (dense [H][d][rank]); pass basis.contiguous()")
+    if basis.device != x.device:
+        raise ValueError("HeadQ basis must be on the input's device (%s, got %s)" % (x.device, basis.device))
+
+
 def quantize(x, which, scheme, n_bits, seed=0, basis=None, rank=16, side_bits=4, T_cap=None):
     """Quantise x [B, H, T, d] (device, fp16/fp32) into a new PackedTensor."""
     desc, x4 = tensor_desc(x)
     mode, bits = scheme_modes(scheme, n_bits, which)
     hq = None
     if mode == MODE_HEADQ:
-        if basis is None:
-            raise ValueError("HeadQ keys need a basis [H, d, rank]")
+        _check_basis(basis, x, desc.H, desc.d)
         rank = basis.shape[-1]
         hq = HeadQ(basis.data_ptr(), rank, side_bits)
     pt = PackedTensor(desc.B, desc.H, T_cap or desc.T, desc.d, mode, bits,

@@ -152,3 +152,22 @@ def test_headq_fit_matches_oracle_projector(tqlib):
     assert np.max(np.abs(U @ U.T - Uo @ Uo.T)) < 1e-4
     # Same sign convention, so the columns agree too (eigenvalues well separated).
     assert np.max(np.abs(U - Uo)) < 1e-3
+
+
+@pytest.mark.parametrize("case", ["strided", "shape", "dtype", "missing"])
+def test_binding_refuses_bad_headq_basis(tqlib, case):
+    """The ABI reads the HeadQ basis as dense [H][d][rank] fp32 at its pointer:
+    the binding refuses a strided view (e.g. numpy eigenvectors, column-major)
+    or a wrong shape or dtype before calling the library."""
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 2, 8, 128), dtype=torch.float32)
+    bases = {
+        "strided": torch.zeros((2, 16, 128), dtype=torch.float32).transpose(1, 2),  # [2, 128, 16] view
+        "shape": torch.zeros((2, 64, 16), dtype=torch.float32),
+        "dtype": torch.zeros((2, 128, 16), dtype=torch.float64),
+        "missing": None,
+    }
+    if case == "strided":
+        assert not bases[case].is_contiguous()
+    with pytest.raises(ValueError):
+        tqlib.quantize(x, tqlib.KEYS, "headq", 4, 0, basis=bases[case])

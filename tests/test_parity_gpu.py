@@ -10,6 +10,7 @@ import pytest
 from compressed_decode_attention_kv_amd import synth
 from oracle import quantizer as oqz
 from oracle import metrics as ome
+from tests import gpu_util
 from tests import parity_util as pu
 
 pytestmark = pytest.mark.gpu
@@ -25,52 +26,11 @@ def tq():
     return lib
 
 
-def _dev(a, dtype=None):
-    t = torch.from_numpy(np.ascontiguousarray(a))
-    if dtype is not None:
-        t = t.to(dtype)
-    return t.cuda()
+_dev = gpu_util.dev
 
 
-def _run_case(tq, K, V, Q, scheme, n, seed=0, U=None, dtype=torch.float32, label=""):
-    """K, V [B, H, T, d], Q [B, H*G, d] (numpy).  Quantise and decode on the
-    GPU, run the oracle per (b, h), compare everything."""
-    B, H, T, d = K.shape
-    Hq = Q.shape[1]
-    G = Hq // H
-    Kd, Vd, Qd = _dev(K, dtype), _dev(V, dtype), _dev(Q, dtype)
-    # The oracle sees exactly the values the GPU sees.
-    Kh_in = Kd.double().cpu().numpy()
-    Vh_in = Vd.double().cpu().numpy()
-    Qh_in = Qd.double().cpu().numpy()
-    basis = _dev(U.astype(np.float32)) if U is not None else None
-    kp = tq.quantize(Kd, tq.KEYS, scheme, n, seed, basis=basis)
-    vp = tq.quantize(Vd, tq.VALUES, scheme, n, seed)
-    out, lse = tq.decode_attention(Qd, kp, vp)
-    torch.cuda.synchronize()
-    out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    kplanes, vplanes = kp.planes(), vp.planes()
-    kmode, vmode = pu.MODE_NAMES[kp.c.mode], pu.MODE_NAMES[vp.c.mode]
-    n_band, n_dec = 0, 0
-    worst = 0.0
-    for b in range(B):
-        for h in range(H):
-            sl = slice((b * H + h) * T, (b * H + h + 1) * T)
-            Uh = U[h] if U is not None else None
-            _, Khat, _, nb1, nd1 = pu.oracle_match(Kh_in[b, h], {k: v[sl] for k, v in kplanes.items()}, kmode,
-                                                   kp.c.bits, seed, U=Uh, label=label + " K")
-            _, Vhat, _, nb2, nd2 = pu.oracle_match(Vh_in[b, h], {k: v[sl] for k, v in vplanes.items()}, vmode,
-                                                   vp.c.bits, seed, label=label + " V")
-            n_band += nb1 + nb2
-            n_dec += nd1 + nd2
-            qs = Qh_in[b, h * G:(h + 1) * G]
-            o_ref, lse_ref, _ = pu.oracle_decode(qs, Khat, Vhat)
-            err = pu.rel_l2(out[b, h * G:(h + 1) * G], o_ref)
-            worst = max(worst, float(err.max()))
-            assert np.all(err <= pu.OUT_RTOL), "%s: output rel L2 %.3g at b=%d h=%d" % (label, err.max(), b, h)
-            assert np.allclose(lse[b, h * G:(h + 1) * G], lse_ref, atol=2e-4, rtol=1e-5), label + " lse"
-    assert n_band <= max(1, pu.MAX_BAND_FRACTION * n_dec), "%s: %d in-band mismatches of %d" % (label, n_band, n_dec)
-    return worst, n_band, kp, vp, (Kd, Vd, Qd)
+def _run_case(*args, **kw):
+    return gpu_util.run_case(*args, **kw)[:5]
 
 
 def test_config1_kqv_full(tq):
