@@ -11,14 +11,15 @@
 // owning 32 consecutive coordinates of one token and writes its own code
 // and sign words without any exchange:
 //   * rotation: a Sylvester Hadamard entry is a product over index bits, so
-//     H_128 = H_16 (x) H_8 with the 16-point factor acting on bits 3..6 and
-//     the 8-point factor on bits 0..2.  The 16-point part runs on
-//     v_mfma_f32_16x16x32_f16, one product per value a of the low bits, with
-//     the constant operand H_16 diag(D) (fp16 inputs times +-1 are exact,
-//     accumulation fp32); the 8-point part is three in-register butterfly
-//     stages over the 8 products.  A wave handles 16 tokens; the product's
-//     row index is the high output bits, so lane (g, tau) holds coordinates
-//     32 g + 8 i + a (i < 4, a < 8) of token tau.
+//     H_128 = H_64 (x) H_2 with the 64-point factor acting on bits 1..6 and
+//     the 2-point factor on bit 0.  The 64-point part runs on
+//     v_mfma_f32_16x16x32_f16 (4 row blocks x 2 K blocks per value a of the
+//     low input bit) with the constant operand H_64; D is applied to the fp16
+//     input by flipping sign bits (exact), and products of fp16 inputs with
+//     +-1 are exact in the fp32 accumulation; the 2-point part is one
+//     in-register butterfly stage.  A wave handles 16 tokens; the rows of the products
+//     are ordered so that lane (g, tau) holds coordinates 32 g + 8 rb + 2 i +
+//     b (rb, i < 4, b < 2) of token tau.
 //   * index: one fma with a biased 1.5*2^23 constant yields the grid cell of
 //     y and, shifted, the LDS address of that cell's entry (boundary inside
 //     the cell and its two neighbours, count of boundaries below); one
@@ -106,28 +107,36 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       s_S[i] = v;
     }
   }
-  // Rotation operand a (low input bits = a), lane (gA, e): slot j < 4 is the
-  // high input index jh = 4 j + gA, value H16[e][jh] D[8 jh + a] (identity
-  // for PLAIN); slots 4..7 are zero (the product uses half of its K = 32).
+  // Rotation operand (rb, kb) at s_A[(rb * 2 + kb) * 64 + lane]: lane (gA, e),
+  // slot jj holds H64[r][jh] (identity for PLAIN) with the output row
+  // r = 16 (e / 4) + 4 rb + e % 4 and the input index
+  // jh = 16 (2 kb + jj / 4) + 4 gA + jj % 4 (what lane gA's B slots carry).
   for (int i = threadIdx.x; i < 8 * 64; i += kThreadsM) {
-    const int a = i >> 6, ln = i & 63, e = ln & 15, gA = ln >> 4;
-    half8 op;
+    const int op = i >> 6, ln = i & 63, e = ln & 15, gA = ln >> 4;
+    const int rb = op >> 1, kb = op & 1;
+    const int r = 16 * (e >> 2) + 4 * rb + (e & 3);
+    half8 v8;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float v = 0.f;
-      if (j < 4) {
-        const int jh = 4 * j + gA, coord = 8 * jh + a;
-        if (MODE == TQ_MODE_PLAIN) {
-          v = (e == jh) ? 1.f : 0.f;
-        } else {
-          const float h = parity((uint32_t)(e & jh)) ? -1.f : 1.f;
-          const float dsg = ((p.signbits[coord >> 5] >> (coord & 31)) & 1u) ? -1.f : 1.f;
-          v = h * dsg;
-        }
-      }
-      op[j] = (_Float16)v;
+    for (int jj = 0; jj < 8; ++jj) {
+      const int jh = 16 * (2 * kb + (jj >> 2)) + 4 * gA + (jj & 3);
+      float v;
+      if (MODE == TQ_MODE_PLAIN) v = (r == jh) ? 1.f : 0.f;
+      else v = parity((uint32_t)(r & jh)) ? -1.f : 1.f;
+      v8[jj] = (_Float16)v;
     }
-    s_A[i] = op;
+    s_A[i] = v8;
+  }
+  // Sign flips D as XOR masks on the lane's fp16 input dwords: dword w of
+  // xin[pp] holds coordinates 32 pp + 8 g + 2 w and + 1.
+  uint32_t dmask[4][4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c0 = 32 * pp + 8 * g + 2 * w;
+      const uint32_t b0 = (p.signbits[c0 >> 5] >> (c0 & 31)) & 1u, b1 = (p.signbits[c0 >> 5] >> ((c0 + 1) & 31)) & 1u;
+      dmask[pp][w] = MODE == TQ_MODE_PLAIN ? 0u : (b0 << 15) | (b1 << 31);
+    }
   }
   __syncthreads();
 
@@ -141,18 +150,38 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   const char* lut_bytes = reinterpret_cast<const char*>(s_lut);
   const float inv_sqrt_d = p.inv_sqrt_d;
 
-  for (int tile = blockIdx.x * kWavesM + wave; tile < ntiles; tile += gridDim.x * kWavesM) {
+  // xin[pp][j] = x[32 pp + 8 g + j] of token tau of a tile (clamped to the
+  // head's last token past its end).
+  auto load_tile = [&](int tl, half8* xin) {
+    const int bh = tl / tph;
+    const int t = min((tl - bh * tph) * 16 + tau, p.T - 1);
+    const int b = bh / p.H, h = bh - b * p.H;
+    const _Float16* xrow = reinterpret_cast<const _Float16*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh +
+                           (int64_t)t * p.st;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) xin[pp] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(xrow + 32 * pp + 8 * g));
+  };
+  const int tstride = gridDim.x * kWavesM;
+  int tile = blockIdx.x * kWavesM + wave;
+  // MSE/PLAIN: the next tile's input is loaded while this one is processed
+  // (always issued, clamped to the last tile, so the wait before use is
+  // static).  PROD keeps one tile in flight: a second buffer would push it
+  // past 168 registers (3 waves per SIMD).
+  constexpr bool kPrefetch = !kProd;
+  half8 xnext[4];
+  if constexpr (kPrefetch) load_tile(min(tile, ntiles - 1), xnext);
+  for (; tile < ntiles; tile += tstride) {
+    half8 xin[4];
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) xin[pp] = xnext[pp];
+      load_tile(min(tile + tstride, ntiles - 1), xnext);
+    } else {
+      load_tile(tile, xin);
+    }
     const int bh = tile / tph;
     const int t = (tile - bh * tph) * 16 + tau;
     const bool valid = t < p.T;
-    const int tc = valid ? t : p.T - 1;
-    const int b = bh / p.H, h = bh - b * p.H;
-    const _Float16* xrow = reinterpret_cast<const _Float16*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh +
-                           (int64_t)tc * p.st;
-    // xin[pp][j] = x[32 pp + 8 g + j]: high input index 4 pp + g, low index j.
-    half8 xin[4];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) xin[pp] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(xrow + 32 * pp + 8 * g));
 
     // ||x||^2: fp16 products are exact in fp32.
     float ss = 0.f;
@@ -173,42 +202,53 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
     // ---- rotation -------------------------------------------------------------------
     u32x4 xw[4];
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) xw[pp] = __builtin_bit_cast(u32x4, xin[pp]);
-    float4v Z[8];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      // B slot j < 4 = x[8 (4 j + g) + a] = xin[j][a].
-      const uint32_t sel = (a & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 bw;
-      bw.x = __builtin_amdgcn_perm(xw[1][a >> 1], xw[0][a >> 1], sel);
-      bw.y = __builtin_amdgcn_perm(xw[3][a >> 1], xw[2][a >> 1], sel);
-      bw.z = 0u;
-      bw.w = 0u;
-      const float4v z = {0.f, 0.f, 0.f, 0.f};
-      Z[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_A[a * 64 + lane], __builtin_bit_cast(half8, bw), z, 0, 0, 0);
-    }
-    // y[i][a] <-> coordinate 32 g + 8 i + a.
-    float y[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float w8[8];
-#pragma unroll
-      for (int a = 0; a < 8; ++a) w8[a] = Z[a][i];
+    for (int pp = 0; pp < 4; ++pp) {
+      xw[pp] = __builtin_bit_cast(u32x4, xin[pp]);
       if (MODE != TQ_MODE_PLAIN) {
 #pragma unroll
-        for (int hs = 1; hs < 8; hs <<= 1) {
+        for (int w = 0; w < 4; ++w) xw[pp][w] ^= dmask[pp][w];
+      }
+    }
+    // Z[a][rb][i]: the 64-point product for input bit 0 = a at output index
+    // 16 g + 4 rb + i.  B slot jj of K block kb = x[2 jh + a], jh as above:
+    // halves a of dwords 2 m, 2 m + 1 of xin[2 kb + n / 2], m = n % 2.
+    float4v Z[2][4];
 #pragma unroll
-          for (int a = 0; a < 8; ++a) {
-            if (!(a & hs)) {
-              const float x0 = w8[a], x1 = w8[a | hs];
-              w8[a] = x0 + x1;
-              w8[a | hs] = x0 - x1;
-            }
-          }
+    for (int a = 0; a < 2; ++a) {
+      const uint32_t sel = a ? 0x07060302u : 0x05040100u;
+      u32x4 bw[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int pp = 2 * kb + (n >> 1), m = 2 * (n & 1);
+          bw[kb][n] = __builtin_amdgcn_perm(xw[pp][m + 1], xw[pp][m], sel);
         }
       }
 #pragma unroll
-      for (int a = 0; a < 8; ++a) y[i][a] = w8[a];
+      for (int rb = 0; rb < 4; ++rb) {
+        const float4v z = {0.f, 0.f, 0.f, 0.f};
+        float4v acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_A[(rb * 2 + 0) * 64 + lane],
+                                                              __builtin_bit_cast(half8, bw[0]), z, 0, 0, 0);
+        Z[a][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_A[(rb * 2 + 1) * 64 + lane],
+                                                           __builtin_bit_cast(half8, bw[1]), acc, 0, 0, 0);
+      }
+    }
+    // y[rb][2 i + b] <-> coordinate 32 g + 8 rb + 2 i + b: the 2-point stage.
+    float y[4][8];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float z0 = Z[0][rb][i], z1 = Z[1][rb][i];
+        if (MODE == TQ_MODE_PLAIN) {
+          y[rb][2 * i] = z0;
+          y[rb][2 * i + 1] = z1;
+        } else {
+          y[rb][2 * i] = z0 + z1;
+          y[rb][2 * i + 1] = z0 - z1;
+        }
+      }
     }
     const float inv = nu > 0.f ? (MODE == TQ_MODE_PLAIN ? 1.0f / nu : inv_sqrt_d / nu) : 0.f;
 
