@@ -219,8 +219,8 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   // The table-driven kernel addresses a head's planes with 24-bit token
   // indices and 32-bit byte offsets, hence the T_cap bound.
   const bool lut = v && k->T_cap <= (1 << 24) &&
-                   lut_supported(d, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, v->bits,
-                                 v->mode == TQ_MODE_PROD);
+                   lut_supported(d, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, k->side_rank,
+                                 k->side_bits, v->bits, v->mode == TQ_MODE_PROD);
   // The table-driven kernel walks 8-12 waves x (64/L) tokens per block step
   // and runs one persistent block per CU; the generic one 4 waves per block.
   const int step = (lut ? 8 : 4) * vpw;

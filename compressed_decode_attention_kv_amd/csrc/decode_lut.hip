@@ -1,6 +1,8 @@
 // Table-driven split decode for 3- and 4-bit caches at d = 128, the
 // read side of [P1] "Esquemas de Cuantización" (KV, KQV, QKQV at n = 4) and
-// [P2] "Contribuições Principais" 1 (TQ-KV, TQ-QKV).
+// [P2] "Contribuições Principais" 1 (TQ-KV, TQ-QKV), plus HeadQ keys (2-bit
+// base with a rank-16 4-bit side code, [P3] section 3 "Metodologia: HeadQ")
+// over 4-bit values.
 //
 // [P1] = "Resumen Técnico: Inferencia Estadística y Medidas de Calidad de
 //        Cuantizaciones de Cache KV Inspiradas en TurboQuant"
@@ -10,9 +12,9 @@
 // Same arithmetic as decode_split_kernel (scores and value sums in the
 // rotated domain), organised so that each byte of packed cache costs about
 // one VALU instruction:
-//   * a packed byte (two 4-bit codes) is turned into an LDS address by one
-//     v_perm, a 6-bit field (two 3-bit codes) by a shift and one
-//     v_and_or_b32, and one LDS read returns both centroids;
+//   * a packed byte (two 4-bit codes, or four 2-bit codes) is turned into an
+//     LDS address by one v_perm, a 6-bit field (two 3-bit codes) by a shift
+//     and one v_and_or_b32, and one LDS read returns the centroids;
 //   * the LDS tables are replicated across lanes so that every read of a
 //     wave hits distinct banks:
 //       V region  [0, 64K):     entry e at e*256, fp16 pair, one copy per lane (b32)
@@ -54,15 +56,18 @@ constexpr int kMaxLutWaves = 12;
 // Replication per table (chosen by measurement of read throughput):
 //   value pairs  fp16x2  b32   one copy per lane      (lane * 4)
 //   key pairs    fp32x2  b64   a copy per lane % 32   ((lane & 31) * 8)
+//   key quads    fp32x4  b128  a copy per lane % 16   ((lane & 15) * 16), 2-bit keys
 //   sign bytes   fp16x8  b128  a copy per lane % 16   ((lane & 15) * 16)
+// KB == 2 is the HeadQ base (with its side code).
 template <int KB, bool KQ, int VB, bool VQ>
 struct LutMap {
   static constexpr bool kSigns = KQ || VQ;
-  static constexpr uint32_t nbyte_tables = (KB == 4) + (VB == 4) + kSigns;
+  static constexpr bool kKeyByte = KB == 4 || KB == 2;
+  static constexpr uint32_t nbyte_tables = kKeyByte + (VB == 4) + kSigns;
   static constexpr uint32_t six_base = 0x10000u * nbyte_tables;
-  static constexpr uint32_t k_base = KB == 4 ? 0u : six_base;
-  static constexpr uint32_t v_base = VB == 4 ? (KB == 4 ? 0x10000u : 0u) : six_base + (KB == 3 ? 0x4000u : 0u);
-  static constexpr uint32_t s_base = 0x10000u * ((KB == 4) + (VB == 4));
+  static constexpr uint32_t k_base = kKeyByte ? 0u : six_base;
+  static constexpr uint32_t v_base = VB == 4 ? (kKeyByte ? 0x10000u : 0u) : six_base + (KB == 3 ? 0x4000u : 0u);
+  static constexpr uint32_t s_base = 0x10000u * (kKeyByte + (VB == 4));
   static constexpr uint32_t merge = six_base + 0x4000u * ((KB == 3) + (VB == 3));
   static constexpr uint32_t bytes = merge + kMaxLutWaves * (2 + 2 * 128) * 4 + 256;
   static_assert(nbyte_tables <= 2, "at most two byte-indexed tables");
@@ -74,6 +79,8 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // LDS address of byte K of w: [lanereg.b0, w.bK, lanereg.b2, 0].
 template <int K>
@@ -114,7 +121,7 @@ __device__ __forceinline__ float quad_bcast(float v) {
 template <int KB, bool KQ, int VB, bool VQ>
 struct TokenData {
   uint32_t k[KB];
-  uint32_t ks;   // key signs (KQ)
+  uint32_t ks;   // key signs (KQ) or the HeadQ side-code dword (KB == 2)
   uint32_t v[VB];
   uint32_t vs;   // value signs (VQ)
   float sc;      // this lane's per-token scalar (lane j: nu_k, gamma_k, nu_v, gamma_v)
@@ -124,7 +131,7 @@ struct TokenData {
 struct HeadPlanes {
   const uint8_t* kc;
   const uint8_t* vc;
-  const uint8_t* ks;
+  const uint8_t* ks;  // key signs, or the HeadQ side codes (KB == 2)
   const uint8_t* vs;
 };
 
@@ -151,6 +158,11 @@ __device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int
   if constexpr (KB == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc));
     t.k[0] = x.x; t.k[1] = x.y; t.k[2] = x.z; t.k[3] = x.w;
+  } else if constexpr (KB == 2) {
+    u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kc));
+    t.k[0] = x.x; t.k[1] = x.y;
+    // Side codes: 16 x 4 bits = 8 bytes per token; lane j uses codes 4j..4j+3.
+    t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.ks + lane_off(tr * 8u + (uint32_t)(j >> 1) * 4u)));
   } else {
 #pragma unroll
     for (int i = 0; i < KB; ++i) t.k[i] = __builtin_nontemporal_load(kc + i);
@@ -191,7 +203,18 @@ void decode_lut_kernel(DecodeParams p) {
       h.y = (_Float16)p.vc[hi];
       *reinterpret_cast<half2_t*>(smem + Map::v_base + e * 256 + l * 4) = h;
     }
-    constexpr int NK = KB == 4 ? 256 : 64;
+    if constexpr (KB == 2) {
+      for (int i = threadIdx.x; i < 256 * 16; i += kLutThreads) {
+        const int e = i >> 4, l = i & 15;
+        float4_t c;
+        c.x = p.kc[e & 3];
+        c.y = p.kc[(e >> 2) & 3];
+        c.z = p.kc[(e >> 4) & 3];
+        c.w = p.kc[e >> 6];
+        *reinterpret_cast<float4_t*>(smem + Map::k_base + e * 256 + l * 16) = c;
+      }
+    }
+    constexpr int NK = KB == 4 ? 256 : (KB == 3 ? 64 : 0);
     for (int i = threadIdx.x; i < NK * 32; i += kLutThreads) {
       const int e = i >> 5, l = i & 31;
       const int lo = KB == 4 ? (e & 15) : (e & 7), hi = KB == 4 ? (e >> 4) : (e >> 3);
@@ -213,10 +236,11 @@ void decode_lut_kernel(DecodeParams p) {
   __syncthreads();
 
   const uint32_t lr_v = Map::v_base | ((uint32_t)lane * 4u);
-  const uint32_t lr_k = Map::k_base | ((uint32_t)(lane & 31) << 3);
+  const uint32_t lr_k = KB == 2 ? (Map::k_base | ((uint32_t)(lane & 15) << 4)) : (Map::k_base | ((uint32_t)(lane & 31) << 3));
   const uint32_t lr_s = Map::s_base | ((uint32_t)(lane & 15) << 4);
-  // Lane j of a quad streams one per-token scalar: 0 nu_k, 1 gamma_k, 2 nu_v, 3 gamma_v.
-  const float* sc_src = j == 0 ? p.k.norms : (j == 1 ? (KQ ? p.k.gamma : p.k.norms)
+  // Lane j of a quad streams one per-token scalar: 0 nu_k, 1 gamma_k (or the
+  // HeadQ side scale), 2 nu_v, 3 gamma_v.
+  const float* sc_src = j == 0 ? p.k.norms : (j == 1 ? (KQ ? p.k.gamma : (KB == 2 ? p.k.side_scale : p.k.norms))
                                                      : (j == 2 ? p.v.norms : (VQ ? p.v.gamma : p.v.norms)));
   float* merge = reinterpret_cast<float*>(smem + Map::merge);
   const int R = p.B * p.Hkv * p.nsplit;
@@ -233,7 +257,7 @@ void decode_lut_kernel(DecodeParams p) {
     HeadPlanes hp;
     hp.kc = p.k.codes + vbase * (16 * KB);
     hp.vc = p.v.codes + vbase * (16 * VB);
-    hp.ks = KQ ? p.k.qjl + vbase * 16 : nullptr;
+    hp.ks = KQ ? p.k.qjl + vbase * 16 : (KB == 2 ? p.k.side + vbase * 8 : nullptr);
     hp.vs = VQ ? p.v.qjl + vbase * 16 : nullptr;
     const float* sc_head = sc_src + vbase;
 
@@ -243,6 +267,17 @@ void decode_lut_kernel(DecodeParams p) {
     if (KQ) {
 #pragma unroll
       for (int e = 0; e < 32; ++e) u[e] = p.qsk[(size_t)qi * d + 32 * j + e];
+    }
+    // HeadQ: this lane's 4 entries of w = U^T q (side codes 4j..4j+3) and the
+    // offset lev * sum(w) that turns a 4-bit code into code - lev.
+    float sw4[KB == 2 ? 4 : 1], swoff = 0.f;
+    if constexpr (KB == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sw4[i] = p.qw[(size_t)qi * 16 + 4 * j + i];
+        swoff += sw4[i];
+      }
+      swoff *= 7.0f;
     }
     float acc[32], ask[VQ ? 32 : 1];
 #pragma unroll
@@ -262,7 +297,21 @@ void decode_lut_kernel(DecodeParams p) {
 
       // ---- key score: this lane's 32 coordinates ---------------------------------
       float sa = 0.f, sb = 0.f;
-      if (KB == 4) {
+      if constexpr (KB == 2) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+#define TQ_K2BYTE(BB)                                                                          \
+          {                                                                                    \
+            const float4_t c = *reinterpret_cast<const float4_t*>(smem + byte_addr<BB>(cur.k[w], lr_k)); \
+            sa = fmaf(q[16 * w + 4 * BB], c.x, sa);                                            \
+            sb = fmaf(q[16 * w + 4 * BB + 1], c.y, sb);                                        \
+            sa = fmaf(q[16 * w + 4 * BB + 2], c.z, sa);                                        \
+            sb = fmaf(q[16 * w + 4 * BB + 3], c.w, sb);                                        \
+          }
+          TQ_K2BYTE(0) TQ_K2BYTE(1) TQ_K2BYTE(2) TQ_K2BYTE(3)
+#undef TQ_K2BYTE
+        }
+      } else if (KB == 4) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
 #define TQ_KBYTE(BB)                                                                          \
@@ -288,6 +337,14 @@ void decode_lut_kernel(DecodeParams p) {
       }
       const float nu_k = quad_bcast<0>(cur.sc);
       float part = nu_k * (sa + sb);
+      if constexpr (KB == 2) {
+        // Side-code correction s_z (w . (code - lev)) of this lane's 4 codes.
+        const uint32_t sd = cur.ks >> (16 * (j & 1));
+        float cs = -swoff;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs = fmaf(sw4[i], (float)((sd >> (4 * i)) & 15u), cs);
+        part = fmaf(quad_bcast<1>(cur.sc), cs, part);
+      }
       if (KQ) {
         float pa = 0.f, pb = 0.f;
 #define TQ_KSIGN(BB)                                                                           \
@@ -450,14 +507,16 @@ hipError_t launch_lut(const DecodeParams& p, int nblocks, hipStream_t s) {
 
 }  // namespace
 
-bool lut_supported(int d, int kbits, int kqjl, int kside, int vbits, int vqjl) {
-  if (kside || d != 128) return false;
+bool lut_supported(int d, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl) {
+  if (d != 128) return false;
+  if (kside) return kbits == 2 && side_rank == 16 && side_bits == 4 && vbits == 4 && !vqjl;
   return (kbits == 3 || kbits == 4) && (vbits == 3 || vbits == 4) && (!kqjl || kbits == 3) && (!vqjl || vbits == 3);
 }
 
 
 hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int vbits, int vqjl, int nblocks,
                              hipStream_t s) {
+  if (kbits == 2) return launch_lut<2, false, 4, false>(p, nblocks, s);  // HeadQ keys, 4-bit values
   const int key = (kbits == 4 ? 0 : 2 + kqjl) * 4 + (vbits == 4 ? 0 : 2 + vqjl);
   switch (key) {
     case 0 * 4 + 0: return launch_lut<4, false, 4, false>(p, nblocks, s);

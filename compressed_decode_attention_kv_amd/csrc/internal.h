@@ -126,7 +126,7 @@ hipError_t launch_decode_split(const DecodeParams& p, int kbits, int kqjl, int k
                                hipStream_t s, bool* supported);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 // Table-driven decode (3/4-bit codes at d = 128), persistent blocks.
-bool lut_supported(int d, int kbits, int kqjl, int kside, int vbits, int vqjl);
+bool lut_supported(int d, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl);
 hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int vbits, int vqjl, int nblocks,
                              hipStream_t s);
 hipError_t launch_metric_scores(const MetricScoreParams& p, int kbits, int kqjl, int kside, hipStream_t s,
