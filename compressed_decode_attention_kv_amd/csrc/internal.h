@@ -41,6 +41,13 @@ struct QuantParams {
   const float* basis;   // HEADQ: [H][d][rank] (device)
   int rank, side_bits;
   uint8_t* codes; float* norms; uint8_t* qjl; float* gamma; uint8_t* side; float* side_scale;
+  // Window of the launch: heads [bh0, bh0 + nbh), tokens [t0, t0 + tn).  With
+  // rcat set (PROD through a library GEMM), the kernel writes 2^12 r of each
+  // vector as fp16 hi | lo, row (bh - bh0) * tn + (t - t0) of [rows][2 d],
+  // instead of computing S r itself.
+  int bh0, nbh, t0, tn;
+  _Float16* rcat;
+  uint64_t seed_for_cat;  // host side only: the seed of S for the GEMM path
 };
 
 // Uniform grid over the unit-sphere coordinate y in [-1, 1] used to find the
@@ -117,6 +124,9 @@ struct RelErrParams {
 
 // ---- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+// Sign bits of the sketch P [rows][d] (row-major, rows as in QuantParams::rcat)
+// into the qjl plane; zero for zero vectors.
+hipError_t launch_sign_pack(const float* P, const QuantParams& p, hipStream_t s);
 // Matrix-core write side (fp16 input, d = 128, PLAIN/MSE/PROD).
 bool quant_mfma_supported(const QuantParams& p);
 int quant_mfma_lut_max();

@@ -55,8 +55,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int L = p.L, j = lane & (L - 1), slot = lane / L, vpw = 64 / L;
-  const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int bh = p.bh0 + blockIdx.y, b = bh / p.H, h = bh % p.H;
   const int d = p.d;
+  const int tend = min(p.T, p.t0 + p.tn);
 
   if (threadIdx.x < 16) {
     s_cent[threadIdx.x] = p.centroids[threadIdx.x];
@@ -73,9 +74,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   const int tok_per_block = 4 * vpw * kSteps;
 
   for (int step = 0; step < kSteps; ++step) {
-    const int t = blockIdx.x * tok_per_block + (step * 4 + wave) * vpw + slot;
-    const bool valid = t < p.T;
-    const int tc = valid ? t : p.T - 1;
+    const int t = p.t0 + blockIdx.x * tok_per_block + (step * 4 + wave) * vpw + slot;
+    const bool valid = t < tend;
+    const int tc = valid ? t : tend - 1;
     float v[32];
     load32<TIN>(xbase + (int64_t)tc * p.st + 32 * j, v);
 
@@ -128,24 +129,42 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
         g2 = fmaf(v[e], v[e], g2);
       }
       g2 = group_sum(g2, L);
-      // Stage the residual of each vector of this wave in LDS: row = slot.
-      float* rrow = &s_r[wave][0];
-      const int rstride = d + 1;
-      __syncthreads();
+      if (p.rcat) {
+        // Residual x 2^12 as fp16 hi (toward zero) + lo: r - hi is exact in
+        // fp32, so the GEMM's fp16 products reproduce S r to about 2^-22.
+        if (valid) {
+          _Float16* row = p.rcat + ((size_t)blockIdx.y * p.tn + (t - p.t0)) * (2 * d);
 #pragma unroll
-      for (int e = 0; e < 32; ++e) rrow[slot * rstride + 32 * j + e] = v[e];
-      __syncthreads();
-      uint32_t sw = 0;
-      for (int i = 0; i < 32; ++i) {
-        const float* srow = p.S + (size_t)(32 * j + i) * d;
-        float acc = 0.f;
-        for (int k = 0; k < d; ++k) acc = fmaf(srow[k], rrow[slot * rstride + k], acc);
-        sw |= (acc >= 0.f ? 1u : 0u) << i;
-      }
-      if (!(nu > 0.f)) sw = 0;
-      if (valid) {
-        reinterpret_cast<uint32_t*>(p.qjl + vec * (d / 8))[j] = sw;
-        if (j == 0) p.gamma[vec] = sqrtf(g2);
+          for (int e = 0; e < 32; e += 2) {
+            const float r0 = v[e] * 4096.0f, r1 = v[e + 1] * 4096.0f;
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+            const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(r0 - (float)hi[0], r1 - (float)hi[1]));
+            *reinterpret_cast<h2*>(row + 32 * j + e) = hi;
+            *reinterpret_cast<h2*>(row + d + 32 * j + e) = lo;
+          }
+          if (j == 0) p.gamma[vec] = sqrtf(g2);
+        }
+      } else {
+        // Stage the residual of each vector of this wave in LDS: row = slot.
+        float* rrow = &s_r[wave][0];
+        const int rstride = d + 1;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 32; ++e) rrow[slot * rstride + 32 * j + e] = v[e];
+        __syncthreads();
+        uint32_t sw = 0;
+        for (int i = 0; i < 32; ++i) {
+          const float* srow = p.S + (size_t)(32 * j + i) * d;
+          float acc = 0.f;
+          for (int k = 0; k < d; ++k) acc = fmaf(srow[k], rrow[slot * rstride + k], acc);
+          sw |= (acc >= 0.f ? 1u : 0u) << i;
+        }
+        if (!(nu > 0.f)) sw = 0;
+        if (valid) {
+          reinterpret_cast<uint32_t*>(p.qjl + vec * (d / 8))[j] = sw;
+          if (j == 0) p.gamma[vec] = sqrtf(g2);
+        }
       }
     }
 
@@ -305,10 +324,28 @@ __global__ __launch_bounds__(kThreads) void relerr_kernel(RelErrParams p) {
   }
 }
 
+// Sign bits of P rows: one thread per (row, 32-bit word).
+__global__ __launch_bounds__(256) void sign_pack_kernel(const float* __restrict__ P, QuantParams p) {
+  const int d = p.d, words = d / 32;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long)p.nbh * p.tn * words) return;
+  const long row = idx / words;
+  const int w = (int)(idx % words);
+  const int hh = (int)(row / p.tn), t = p.t0 + (int)(row % p.tn);
+  if (t >= p.T) return;
+  const int64_t vec = (int64_t)(p.bh0 + hh) * p.T_cap + t;
+  const float* pr = P + row * d + 32 * w;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) bits |= (pr[k] >= 0.f ? 1u : 0u) << k;
+  if (!(p.norms[vec] > 0.f)) bits = 0;
+  reinterpret_cast<uint32_t*>(p.qjl + vec * (d / 8))[w] = bits;
+}
+
 template <int BITS, int MODE>
 hipError_t launch_q(const QuantParams& p, hipStream_t s) {
   const int vpw = 64 / p.L;
-  dim3 grid((p.T + 4 * vpw * kSteps - 1) / (4 * vpw * kSteps), p.B * p.H);
+  dim3 grid((p.tn + 4 * vpw * kSteps - 1) / (4 * vpw * kSteps), p.nbh);
   if (p.dtype == TQ_F16)
     hipLaunchKernelGGL((quant_kernel<BITS, MODE, _Float16>), grid, dim3(kThreads), 0, s, p);
   else
@@ -353,6 +390,12 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
       break;
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_sign_pack(const float* P, const QuantParams& p, hipStream_t s) {
+  const long n = (long)p.nbh * p.tn * (p.d / 32);
+  hipLaunchKernelGGL(sign_pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, P, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_relerr(const RelErrParams& p, int, hipStream_t s) {

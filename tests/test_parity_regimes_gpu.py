@@ -148,3 +148,15 @@ def test_headq_gqa_full_size_sampled(tq):
     m = tq.metrics(Q[b:b + 1, G * h:G * h + G], K[b:b + 1, h:h + 1], None, kp.head_view(b, h), None)
     kl, _, _, _ = pu.kl_and_recall(qn, Kn, Khat)
     assert abs(m["kl_mean"] - kl.mean()) <= pu.KL_ATOL and abs(m["kl_max"] - kl.max()) <= pu.KL_ATOL
+
+
+@pytest.mark.parametrize("scheme", ["kqv", "qkqv"])
+def test_sketch_gemm_chunks(tq, scheme):
+    """d=256, T=20000 (two 16384-row chunks per head, the second ragged),
+    B=1, H=2, fp32, n=4: the QJL sketch at d >= 256 runs as a library GEMM
+    over fp16 hi/lo residual rows; codes, signs, norms, gamma and outputs
+    against the oracle."""
+    from tests import gpu_util
+    K, V, Q = synth.isotropic(1, 2, 2, 20000, 256, seed=77, kv_std=1.0, dtype=np.float32)
+    worst, n_band, *_ = gpu_util.run_case(tq, K, V, Q, scheme, 4, seed=19, label="gemm %s" % scheme)
+    print("sketch gemm", scheme, "worst rel L2 %.3g band %d" % (worst, n_band))
