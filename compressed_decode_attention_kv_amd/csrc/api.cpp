@@ -512,6 +512,19 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
     if (mode == TQ_MODE_PROD && x->d >= 256) {
       p.seed_for_cat = seed;
       if (tq_status s = quantize_prod_gemm(p, (hipStream_t)stream)) return s;
+    } else if (mode == TQ_MODE_HEADQ) {
+      // Pi U_h once per head (stream-ordered scratch) instead of once per block.
+      hipStream_t st = (hipStream_t)stream;
+      void* rb = nullptr;
+      if (hipMallocAsync(&rb, (size_t)x->H * x->d * hq->rank * sizeof(float), st) != hipSuccess)
+        return fail(TQ_ENOMEM, "rotated-basis scratch allocation failed");
+      tq_status s = hip_status(launch_rotate_basis(p, reinterpret_cast<float*>(rb), st), "basis rotation launch");
+      if (s == TQ_OK) {
+        p.rbasis = reinterpret_cast<const float*>(rb);
+        s = hip_status(launch_quantize(p, st), "quantize launch");
+      }
+      (void)hipFreeAsync(rb, st);
+      if (s) return s;
     } else {
       if (tq_status s = hip_status(launch_quantize(p, (hipStream_t)stream), "quantize launch")) return s;
     }

@@ -48,6 +48,7 @@ struct QuantParams {
   int bh0, nbh, t0, tn;
   _Float16* rcat;
   uint64_t seed_for_cat;  // host side only: the seed of S for the GEMM path
+  const float* rbasis;    // HEADQ: (Pi U_h)^T per head, [H][rank][d]
 };
 
 // Uniform grid over the unit-sphere coordinate y in [-1, 1] used to find the
@@ -127,6 +128,8 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 // Sign bits of the sketch P [rows][d] (row-major, rows as in QuantParams::rcat)
 // into the qjl plane; zero for zero vectors.
 hipError_t launch_sign_pack(const float* P, const QuantParams& p, hipStream_t s);
+// (Pi U_h)^T of every head into out [H][rank][d] (device).
+hipError_t launch_rotate_basis(const QuantParams& p, float* out, hipStream_t s);
 // Matrix-core write side (fp16 input, d = 128, PLAIN/MSE/PROD).
 bool quant_mfma_supported(const QuantParams& p);
 int quant_mfma_lut_max();

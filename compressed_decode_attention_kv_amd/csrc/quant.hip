@@ -44,13 +44,78 @@ __device__ void rotated_basis(const float* U, int d, int rank, const uint32_t* s
   __syncthreads();
 }
 
+// HeadQ side code of one vector ([P3] section 3): e' = nu (y - c[idx]) =
+// Pi (k - k_base) held rotated, z = U'^T e' with U'^T = (Pi U)^T in LDS as
+// [rank][d] (each z_r a dot product over the lane's 32 contiguous entries),
+// s_z = max |z| / lev, code = clamp(rne(z / s_z), -lev, lev) + lev.
+__device__ __forceinline__ void headq_side(const QuantParams& p, const float* v, const uint32_t* idx, float nu,
+                                           const float* s_cent, const float* s_side, int j, int L, bool valid,
+                                           int64_t vec) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const int rank = p.rank;
+  float ep[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) ep[e] = nu > 0.f ? nu * (v[e] - s_cent[idx[e]]) : 0.f;
+  float z[32];
+  float zmax = 0.f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    z[r] = 0.f;
+    if (r < rank) {  // uniform
+      const f4* ur = reinterpret_cast<const f4*>(s_side + r * p.d + 32 * j);
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const f4 u = ur[i];
+        a0 = fmaf(u.x, ep[4 * i], a0);
+        a1 = fmaf(u.y, ep[4 * i + 1], a1);
+        a0 = fmaf(u.z, ep[4 * i + 2], a0);
+        a1 = fmaf(u.w, ep[4 * i + 3], a1);
+      }
+      z[r] = group_sum(a0 + a1, L);
+      zmax = fmaxf(zmax, fabsf(z[r]));
+    }
+  }
+  const int lev = (1 << (p.side_bits - 1)) - 1;
+  const float sz = zmax / (float)lev;
+  if (valid && j == 0) {
+    uint32_t sw[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sw[k] = 0;
+    const int sb = p.side_bits;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      if (r < rank) {
+        int c = lev;
+        if (sz > 0.f) {
+          float q = rintf(z[r] / sz);
+          q = fminf(fmaxf(q, (float)-lev), (float)lev);
+          c = (int)q + lev;
+        }
+        const int bit = sb * r, wi = bit >> 5, sh = bit & 31;
+        sw[wi] |= (uint32_t)c << sh;
+        if (sh + sb > 32) sw[wi + 1] |= (uint32_t)c >> (32 - sh);
+      }
+    }
+    const int nbytes = rank * sb / 8;
+    uint8_t* dst = p.side + vec * nbytes;
+    if ((nbytes & 3) == 0) {
+      for (int k = 0; k < nbytes / 4; ++k) reinterpret_cast<uint32_t*>(dst)[k] = sw[k];
+    } else {
+      for (int k = 0; k < nbytes; ++k) dst[k] = (uint8_t)(sw[k >> 2] >> (8 * (k & 3)));
+    }
+    p.side_scale[vec] = sz;
+  }
+}
+
 template <int BITS, int MODE, typename TIN>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   // Residual staging of the QJL sketch: per wave, 64/L rows of d+1 floats
   // (the +1 pad puts the rows of different vectors in different banks).
   constexpr int kRowsFloats = 2048 + 64;
   __shared__ float s_cent[16], s_bnd[16];
-  __shared__ float s_side[MODE == TQ_MODE_HEADQ ? kMaxSideLds : 1];
+  // HEADQ: (Pi U_h)^T, d * rank floats, in dynamic LDS (sized at launch).
+  extern __shared__ float s_side[];
   __shared__ float s_r[MODE == TQ_MODE_PROD ? 4 : 1][MODE == TQ_MODE_PROD ? kRowsFloats : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -63,8 +128,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
     s_cent[threadIdx.x] = p.centroids[threadIdx.x];
     s_bnd[threadIdx.x] = p.bounds[threadIdx.x];
   }
-  if (MODE == TQ_MODE_HEADQ)
-    rotated_basis(p.basis + (size_t)h * d * p.rank, d, p.rank, p.signbits, p.inv_sqrt_d, s_side);
+  if (MODE == TQ_MODE_HEADQ) {
+    // (Pi U_h)^T, [rank][d], computed once per head by rotate_basis_kernel.
+    const float* src = p.rbasis + (size_t)h * d * p.rank;
+    for (int i = threadIdx.x; i < d * p.rank; i += blockDim.x) s_side[i] = src[i];
+  }
   __syncthreads();
 
   constexpr int NB = (1 << BITS) - 1;
@@ -169,53 +237,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
     }
 
     if (MODE == TQ_MODE_HEADQ) {
-      // e' = nu (y - c[idx]) = Pi (k - k_base); z = U'^T e' ([P3] section 3).
-      float z[32];
-      const int rank = p.rank;
-#pragma unroll
-      for (int r = 0; r < 32; ++r) z[r] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const float ep = nu > 0.f ? nu * (v[e] - s_cent[idx[e]]) : 0.f;
-        const float* urow = s_side + (32 * j + e) * rank;
-#pragma unroll
-        for (int r = 0; r < 32; ++r)
-          if (r < rank) z[r] = fmaf(urow[r], ep, z[r]);
-      }
-      float zmax = 0.f;
-#pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        if (r < rank) {
-          z[r] = group_sum(z[r], L);
-          zmax = fmaxf(zmax, fabsf(z[r]));
-        }
-      }
-      const int lev = (1 << (p.side_bits - 1)) - 1;
-      const float sz = zmax / (float)lev;
-      if (valid && j == 0) {
-        uint32_t sw[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) sw[k] = 0;
-        const int sb = p.side_bits;
-#pragma unroll
-        for (int r = 0; r < 32; ++r) {
-          if (r < rank) {
-            int c = lev;
-            if (sz > 0.f) {
-              float q = rintf(z[r] / sz);
-              q = fminf(fmaxf(q, (float)-lev), (float)lev);
-              c = (int)q + lev;
-            }
-            const int bit = sb * r, wi = bit >> 5, sh = bit & 31;
-            sw[wi] |= (uint32_t)c << sh;
-            if (sh + sb > 32) sw[wi + 1] |= (uint32_t)c >> (32 - sh);
-          }
-        }
-        const int nbytes = rank * sb / 8;
-        uint8_t* dst = p.side + vec * nbytes;
-        for (int k = 0; k < nbytes; ++k) dst[k] = (uint8_t)(sw[k >> 2] >> (8 * (k & 3)));
-        p.side_scale[vec] = sz;
-      }
+      headq_side(p, v, idx, nu, s_cent, s_side, j, L, valid, vec);
     }
   }
 }
@@ -324,6 +346,17 @@ __global__ __launch_bounds__(kThreads) void relerr_kernel(RelErrParams p) {
   }
 }
 
+// (Pi U_h)^T for every head h (one block per head) into out [H][rank][d].
+__global__ __launch_bounds__(kThreads) void rotate_basis_kernel(QuantParams p, float* out) {
+  __shared__ float s_side[kMaxSideLds];
+  const int h = blockIdx.x, n = p.d * p.rank;
+  rotated_basis(p.basis + (size_t)h * n, p.d, p.rank, p.signbits, p.inv_sqrt_d, s_side);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int r = i / p.d, k = i % p.d;
+    out[(size_t)h * n + i] = s_side[k * p.rank + r];
+  }
+}
+
 // Sign bits of P rows: one thread per (row, 32-bit word).
 __global__ __launch_bounds__(256) void sign_pack_kernel(const float* __restrict__ P, QuantParams p) {
   const int d = p.d, words = d / 32;
@@ -346,10 +379,11 @@ template <int BITS, int MODE>
 hipError_t launch_q(const QuantParams& p, hipStream_t s) {
   const int vpw = 64 / p.L;
   dim3 grid((p.tn + 4 * vpw * kSteps - 1) / (4 * vpw * kSteps), p.nbh);
+  const size_t dyn = MODE == TQ_MODE_HEADQ ? (size_t)p.d * p.rank * sizeof(float) : 0;
   if (p.dtype == TQ_F16)
-    hipLaunchKernelGGL((quant_kernel<BITS, MODE, _Float16>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((quant_kernel<BITS, MODE, _Float16>), grid, dim3(kThreads), dyn, s, p);
   else
-    hipLaunchKernelGGL((quant_kernel<BITS, MODE, float>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((quant_kernel<BITS, MODE, float>), grid, dim3(kThreads), dyn, s, p);
   return hipGetLastError();
 }
 
@@ -390,6 +424,11 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
       break;
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_rotate_basis(const QuantParams& p, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(rotate_basis_kernel, dim3(p.H), dim3(kThreads), 0, s, p, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_sign_pack(const float* P, const QuantParams& p, hipStream_t s) {

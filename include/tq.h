@@ -15,8 +15,10 @@
  *     its cached per-(device, seed, d) constants and one rocBLAS handle per
  *     device (all freed by tq_release_cache).  A tq_quantize of a PROD
  *     tensor at d >= 256 also takes a stream-ordered scratch buffer (8 d
- *     bytes per row, at most 16384 rows) from the stream's memory pool and
- *     returns it before the call's work completes on that stream.
+ *     bytes per row, at most 16384 rows), and one of a HEADQ tensor a
+ *     buffer for the rotated basis (4 H d rank bytes), from the stream's
+ *     memory pool and returns it before the call's work completes on that
+ *     stream.
  *   - Every call returns tq_status.  All argument and descriptor checks run
  *     on the host before any HIP call, so a rejected call touches no GPU
  *     state.  tq_last_error() returns a thread-local message for the last

@@ -158,3 +158,37 @@ def test_isotropic_decode_full_size_sampled(tq, scheme):
         assert abs(m["kl_mean"] - kl[0]) <= pu.KL_ATOL
         amb = int(pu.top5_ambiguous(s).sum() + pu.top5_ambiguous(sh).sum())
         assert abs(m["top5_recall"] - rec[0]) <= amb / 5.0 + 1e-12
+
+
+@pytest.mark.parametrize("scheme", ["kqv", "qkqv", "headq"])
+def test_capacity_larger_than_length(tq, scheme):
+    """T_cap > T: the planes of each head are padded to the capacity; the
+    decode must read only the first T tokens of each head."""
+    B, H, G, T, d, cap = 2, 2, 2, 777, 128, 1000
+    if scheme == "headq":
+        K, V, Q, C = synth.rope_gqa(B, H, G, T, d, seed=8, n_calib=2048, dtype=np.float32)
+        from oracle import headq as ohq
+        U = np.stack([ohq.fit_basis(C[h].astype(np.float64), 16)[0] for h in range(H)])
+        basis = gpu_util.dev(U.astype(np.float32))
+    else:
+        K, V, Q = synth.isotropic(B, H, G, T, d, seed=9, kv_std=1.0, dtype=np.float32)
+        U, basis = None, None
+    Kd, Vd, Qd = gpu_util.dev(K, torch.float16), gpu_util.dev(V, torch.float16), gpu_util.dev(Q, torch.float16)
+    kp = tq.quantize(Kd, tq.KEYS, scheme, 4, 6, basis=basis, T_cap=cap)
+    vp = tq.quantize(Vd, tq.VALUES, scheme, 4, 6, T_cap=cap)
+    out, lse = tq.decode_attention(Qd, kp, vp)
+    torch.cuda.synchronize()
+    kpl, vpl = kp.planes(), vp.planes()
+    kmode, vmode = pu.MODE_NAMES[kp.c.mode], pu.MODE_NAMES[vp.c.mode]
+    for b in range(B):
+        for h in range(H):
+            sl = slice((b * H + h) * cap, (b * H + h) * cap + T)
+            Kn, Vn = Kd[b, h].double().cpu().numpy(), Vd[b, h].double().cpu().numpy()
+            _, Khat, _, _, _ = pu.oracle_match(Kn, {k: v[sl] for k, v in kpl.items()}, kmode, kp.c.bits, 6,
+                                               U=U[h] if U is not None else None, label="cap K")
+            _, Vhat, _, _, _ = pu.oracle_match(Vn, {k: v[sl] for k, v in vpl.items()}, vmode, vp.c.bits, 6,
+                                               label="cap V")
+            qn = Qd[b, G * h:G * h + G].double().cpu().numpy()
+            o_ref, lse_ref, _ = pu.oracle_decode(qn, Khat, Vhat)
+            assert pu.rel_l2(out[b, G * h:G * h + G].cpu().numpy(), o_ref).max() <= pu.OUT_RTOL
+            assert np.allclose(lse[b, G * h:G * h + G].cpu().numpy(), lse_ref, atol=2e-4, rtol=1e-5)
