@@ -304,6 +304,7 @@ bool decode_supported(int kbits, bool kq, bool ksd, int vbits, bool vq) {
 
 struct DecodePlan {
   int nsplit, chunk, part_stride, units, G;
+  int nparts;  // partials per query: nsplit, times the waves per block at d > 128 (table-driven)
   bool lut;
   size_t off_qrot, off_qsk, off_qw, off_part, off_qraw, bytes;
 };
@@ -321,8 +322,9 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   const int G = Hq / k->H;
   const int nq = k->B * Hq;
   // The table-driven kernel addresses a head's planes with 24-bit token
-  // indices and 32-bit byte offsets, hence the T_cap bound.
-  const bool lut = v && k->T_cap <= (1 << 24) &&
+  // indices and 32-bit byte offsets (at most d/2 code bytes per token),
+  // hence the T_cap bounds.
+  const bool lut = v && k->T_cap <= (1 << 24) && (long)k->T_cap * (d / 2) < (1L << 32) &&
                    lut_supported(d, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, k->side_rank,
                                  k->side_bits, v->bits, v->mode == TQ_MODE_PROD);
   // The table-driven kernel walks 8-12 waves x (64/L) tokens per block step
@@ -337,13 +339,18 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   int chunk = (k->T + nsplit - 1) / nsplit;
   chunk = std::max(step, (chunk + step - 1) / step * step);
   nsplit = (k->T + chunk - 1) / chunk;
-  if (nsplit > 256) {
-    chunk = (k->T + 255) / 256;
+  // The combine step merges at most 256 partials per query; the table-driven
+  // kernel at d > 128 writes one per wave.
+  const bool vq = v && v->mode == TQ_MODE_PROD;
+  const int per_split = (lut && d > 128) ? lut_waves(k->mode == TQ_MODE_PROD, vq) : 1;
+  const int max_split = 256 / per_split;
+  if (nsplit > max_split) {
+    chunk = (k->T + max_split - 1) / max_split;
     chunk = (chunk + step - 1) / step * step;
     nsplit = (k->T + chunk - 1) / chunk;
   }
-  const bool vq = v && v->mode == TQ_MODE_PROD;
   pl->nsplit = nsplit;
+  pl->nparts = nsplit * per_split;
   pl->chunk = chunk;
   pl->lut = lut;
   pl->G = G;
@@ -355,7 +362,7 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   pl->off_qsk = off;  off = round_up(off + (k->mode == TQ_MODE_PROD ? (size_t)nq * d * 4 : 0), 256);
   pl->off_qw = off;   off = round_up(off + (k->mode == TQ_MODE_HEADQ ? (size_t)nq * k->side_rank * 4 : 0), 256);
   pl->off_qraw = off; off = round_up(off + (with_qraw ? (size_t)nq * d * 4 : 0), 256);
-  pl->off_part = off; off = round_up(off + (v ? (size_t)nq * nsplit * pl->part_stride * 4 : 0), 256);
+  pl->off_part = off; off = round_up(off + (v ? (size_t)nq * pl->nparts * pl->part_stride * 4 : 0), 256);
   pl->bytes = off;
   return TQ_OK;
 }
@@ -576,7 +583,7 @@ tq_status tq_decode_attention(const tq_tensor_desc* q, const tq_packed* k, const
   fill_qprep(q, k, Sk, w, pl, false, &qp);
   CombineParams cp;
   std::memset(&cp, 0, sizeof(cp));
-  cp.nq = q->B * q->H; cp.d = k->d; cp.nsplit = pl.nsplit; cp.part_stride = pl.part_stride;
+  cp.nq = q->B * q->H; cp.d = k->d; cp.nsplit = pl.nparts; cp.part_stride = pl.part_stride;
   cp.vqjl = vq; cp.vrotate = v->mode != TQ_MODE_PLAIN; cp.v_qjl = dp.v_qjl;
   fill_signbits(v->seed, v->d, cp.signbits);
   cp.inv_sqrt_d = 1.0f / std::sqrt((float)k->d);

@@ -1,4 +1,4 @@
-// Table-driven split decode for 3- and 4-bit caches at d = 128, the
+// Table-driven split decode for 3- and 4-bit caches at d = 128..1024, the
 // read side of [P1] "Esquemas de Cuantización" (KV, KQV, QKQV at n = 4) and
 // [P2] "Contribuições Principais" 1 (TQ-KV, TQ-QKV), plus HeadQ keys (2-bit
 // base with a rank-16 4-bit side code, [P3] section 3 "Metodologia: HeadQ")
@@ -23,9 +23,9 @@
 //   * key centroids stay fp32 (scores are exact in fp32); value centroids and
 //     the +-1 sign patterns are fp16 and enter v_fma_mix_f32 with fp32
 //     weights and fp32 accumulators;
-//   * 4 lanes per 128-d token, lane j owns coordinates [32j, 32j+32); the
-//     per-token scalars (norms, residual norms) are loaded once per quad and
-//     broadcast with DPP;
+//   * d/32 lanes per token, lane j owns coordinates [32j, 32j+32); the
+//     per-token scalars (norms, residual norms) are loaded by lanes 0..3 of
+//     the token's group and broadcast (DPP within a quad at d = 128);
 //   * all packed data is streamed with non-temporal loads, one token step
 //     ahead of the arithmetic, addressed as a per-head base (scalar) plus a
 //     32-bit per-lane offset;
@@ -59,7 +59,7 @@ constexpr int kMaxLutWaves = 12;
 //   key quads    fp32x4  b128  a copy per lane % 16   ((lane & 15) * 16), 2-bit keys
 //   sign bytes   fp16x8  b128  a copy per lane % 16   ((lane & 15) * 16)
 // KB == 2 is the HeadQ base (with its side code).
-template <int KB, bool KQ, int VB, bool VQ>
+template <int D, int KB, bool KQ, int VB, bool VQ>
 struct LutMap {
   static constexpr bool kSigns = KQ || VQ;
   static constexpr bool kKeyByte = KB == 4 || KB == 2;
@@ -69,7 +69,9 @@ struct LutMap {
   static constexpr uint32_t v_base = VB == 4 ? (kKeyByte ? 0x10000u : 0u) : six_base + (KB == 3 ? 0x4000u : 0u);
   static constexpr uint32_t s_base = 0x10000u * (kKeyByte + (VB == 4));
   static constexpr uint32_t merge = six_base + 0x4000u * ((KB == 3) + (VB == 3));
-  static constexpr uint32_t bytes = merge + kMaxLutWaves * (2 + 2 * 128) * 4 + 256;
+  // The wave-merge buffer exists at d = 128 only; wider heads write one
+  // partial per wave and leave the merge to the combine step.
+  static constexpr uint32_t bytes = merge + (D == 128 ? kMaxLutWaves * (2 + 2 * 128) * 4 + 256 : 0);
   static_assert(nbyte_tables <= 2, "at most two byte-indexed tables");
   static_assert(bytes <= 163840, "LDS budget");
 };
@@ -118,6 +120,22 @@ __device__ __forceinline__ float quad_bcast(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), J * 0x55, 0xF, 0xF, true));
 }
 
+// Value of lane J of this lane's token group (L lanes per token).
+template <int L, int J>
+__device__ __forceinline__ float tok_bcast(float v, int lane) {
+  if constexpr (L == 4) return quad_bcast<J>(v);
+  else return __shfl(v, (lane & ~(L - 1)) | J, 64);
+}
+
+// Sum over the L lanes of this lane's token group.
+template <int L>
+__device__ __forceinline__ float tok_sum(float v) {
+  v = quad_sum(v);
+#pragma unroll
+  for (int off = 4; off < L; off <<= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
 template <int KB, bool KQ, int VB, bool VQ>
 struct TokenData {
   uint32_t k[KB];
@@ -149,12 +167,12 @@ __device__ __forceinline__ uint32_t token_bytes(uint32_t tr) {
 }
 
 // Token tr (index within the head) for lane j.  The host sends only
-// T_cap <= 2^24 here, so tr fits a 24-bit multiply (full rate, unlike a
-// 32-bit one) and every offset fits 32 bits.
-template <int KB, bool KQ, int VB, bool VQ>
+// T_cap <= 2^24 with T_cap * d / 2 < 2^32 here, so tr fits a 24-bit multiply
+// (full rate, unlike a 32-bit one) and every byte offset fits 32 bits.
+template <int D, int KB, bool KQ, int VB, bool VQ>
 __device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int j, const float* sc_head,
                                            TokenData<KB, KQ, VB, VQ>& t) {
-  const uint32_t* kc = reinterpret_cast<const uint32_t*>(h.kc + lane_off(token_bytes<16u * KB>(tr) + (uint32_t)j * (4u * KB)));
+  const uint32_t* kc = reinterpret_cast<const uint32_t*>(h.kc + lane_off(token_bytes<(uint32_t)D * KB / 8>(tr) + (uint32_t)j * (4u * KB)));
   if constexpr (KB == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc));
     t.k[0] = x.x; t.k[1] = x.y; t.k[2] = x.z; t.k[3] = x.w;
@@ -167,7 +185,7 @@ __device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int
 #pragma unroll
     for (int i = 0; i < KB; ++i) t.k[i] = __builtin_nontemporal_load(kc + i);
   }
-  const uint32_t* vc = reinterpret_cast<const uint32_t*>(h.vc + lane_off(token_bytes<16u * VB>(tr) + (uint32_t)j * (4u * VB)));
+  const uint32_t* vc = reinterpret_cast<const uint32_t*>(h.vc + lane_off(token_bytes<(uint32_t)D * VB / 8>(tr) + (uint32_t)j * (4u * VB)));
   if constexpr (VB == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc));
     t.v[0] = x.x; t.v[1] = x.y; t.v[2] = x.z; t.v[3] = x.w;
@@ -175,21 +193,21 @@ __device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int
 #pragma unroll
     for (int i = 0; i < VB; ++i) t.v[i] = __builtin_nontemporal_load(vc + i);
   }
-  if (KQ) t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.ks + lane_off(tr * 16u + (uint32_t)j * 4u)));
-  if (VQ) t.vs = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.vs + lane_off(tr * 16u + (uint32_t)j * 4u)));
+  if (KQ) t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.ks + lane_off(token_bytes<(uint32_t)D / 8>(tr) + (uint32_t)j * 4u)));
+  if (VQ) t.vs = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.vs + lane_off(token_bytes<(uint32_t)D / 8>(tr) + (uint32_t)j * 4u)));
   t.sc = __builtin_nontemporal_load(sc_head + tr);
 }
 
-template <int KB, bool KQ, int VB, bool VQ>
+template <int D, int KB, bool KQ, int VB, bool VQ>
 __global__ __launch_bounds__(lut_threads(KQ && VQ))
 __attribute__((amdgpu_waves_per_eu(lut_threads(KQ && VQ) / 256, lut_threads(KQ && VQ) / 256)))
 void decode_lut_kernel(DecodeParams p) {
   constexpr int kLutThreads = lut_threads(KQ && VQ);
   constexpr int kLutWaves = kLutThreads / 64;
-  using Map = LutMap<KB, KQ, VB, VQ>;
-  __shared__ __attribute__((aligned(16))) char smem[LutMap<KB, KQ, VB, VQ>::bytes];
+  using Map = LutMap<D, KB, KQ, VB, VQ>;
+  __shared__ __attribute__((aligned(16))) char smem[LutMap<D, KB, KQ, VB, VQ>::bytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int d = 128, L = 4, vpw = 64 / L;  // 4 lanes per token, 16 tokens per wave step
+  constexpr int d = D, L = D / 32, vpw = 64 / L;  // L lanes per token, 64/L tokens per wave step
   const int j = lane & (L - 1), slot = lane / L;
 
   // ---- tables -------------------------------------------------------------------
@@ -240,8 +258,9 @@ void decode_lut_kernel(DecodeParams p) {
   const uint32_t lr_s = Map::s_base | ((uint32_t)(lane & 15) << 4);
   // Lane j of a quad streams one per-token scalar: 0 nu_k, 1 gamma_k (or the
   // HeadQ side scale), 2 nu_v, 3 gamma_v.
+  // (Lanes j >= 4 of wider groups load a norm they do not use.)
   const float* sc_src = j == 0 ? p.k.norms : (j == 1 ? (KQ ? p.k.gamma : (KB == 2 ? p.k.side_scale : p.k.norms))
-                                                     : (j == 2 ? p.v.norms : (VQ ? p.v.gamma : p.v.norms)));
+                                          : (j == 2 ? p.v.norms : (j == 3 ? (VQ ? p.v.gamma : p.v.norms) : p.k.norms)));
   float* merge = reinterpret_cast<float*>(smem + Map::merge);
   const int R = p.B * p.Hkv * p.nsplit;
 
@@ -255,10 +274,10 @@ void decode_lut_kernel(DecodeParams p) {
     const int t0 = split * p.chunk, t1 = min(p.T, t0 + p.chunk);
     const size_t vbase = (size_t)bkv * p.T_cap;
     HeadPlanes hp;
-    hp.kc = p.k.codes + vbase * (16 * KB);
-    hp.vc = p.v.codes + vbase * (16 * VB);
-    hp.ks = KQ ? p.k.qjl + vbase * 16 : (KB == 2 ? p.k.side + vbase * 8 : nullptr);
-    hp.vs = VQ ? p.v.qjl + vbase * 16 : nullptr;
+    hp.kc = p.k.codes + vbase * (D * KB / 8);
+    hp.vc = p.v.codes + vbase * (D * VB / 8);
+    hp.ks = KQ ? p.k.qjl + vbase * (D / 8) : (KB == 2 ? p.k.side + vbase * 8 : nullptr);
+    hp.vs = VQ ? p.v.qjl + vbase * (D / 8) : nullptr;
     const float* sc_head = sc_src + vbase;
 
     float q[32], u[KQ ? 32 : 1];
@@ -335,7 +354,7 @@ void decode_lut_kernel(DecodeParams p) {
         TQ_KPAIR(8) TQ_KPAIR(9) TQ_KPAIR(10) TQ_KPAIR(11) TQ_KPAIR(12) TQ_KPAIR(13) TQ_KPAIR(14) TQ_KPAIR(15)
 #undef TQ_KPAIR
       }
-      const float nu_k = quad_bcast<0>(cur.sc);
+      const float nu_k = tok_bcast<L, 0>(cur.sc, lane);
       float part = nu_k * (sa + sb);
       if constexpr (KB == 2) {
         // Side-code correction s_z (w . (code - lev)) of this lane's 4 codes.
@@ -343,7 +362,7 @@ void decode_lut_kernel(DecodeParams p) {
         float cs = -swoff;
 #pragma unroll
         for (int i = 0; i < 4; ++i) cs = fmaf(sw4[i], (float)((sd >> (4 * i)) & 15u), cs);
-        part = fmaf(quad_bcast<1>(cur.sc), cs, part);
+        part = fmaf(tok_bcast<L, 1>(cur.sc, lane), cs, part);
       }
       if (KQ) {
         float pa = 0.f, pb = 0.f;
@@ -357,10 +376,10 @@ void decode_lut_kernel(DecodeParams p) {
         }
         TQ_KSIGN(0) TQ_KSIGN(1) TQ_KSIGN(2) TQ_KSIGN(3)
 #undef TQ_KSIGN
-        const float g_k = quad_bcast<1>(cur.sc);
+        const float g_k = tok_bcast<L, 1>(cur.sc, lane);
         part = fmaf(nu_k * p.k_qjl * g_k, pa + pb, part);
       }
-      float s = quad_sum(part) * p.scale_log2;
+      float s = tok_sum<L>(part) * p.scale_log2;
       if (!valid) s = -INFINITY;
 
       // ---- online softmax (per token slot) ----------------------------------------
@@ -379,7 +398,7 @@ void decode_lut_kernel(DecodeParams p) {
       }
       const float pt = valid ? __builtin_amdgcn_exp2f(s - m) : 0.f;  // s - m <= 8
       l += pt;
-      const float wv = pt * quad_bcast<2>(cur.sc);
+      const float wv = pt * tok_bcast<L, 2>(cur.sc, lane);
 
       // ---- value accumulation -----------------------------------------------------
       if (VB == 4) {
@@ -407,7 +426,7 @@ void decode_lut_kernel(DecodeParams p) {
 #undef TQ_VPAIR
       }
       if (VQ) {
-        const float wq = wv * quad_bcast<3>(cur.sc);
+        const float wq = wv * tok_bcast<L, 3>(cur.sc, lane);
 #define TQ_VSIGN(BB)                                                                           \
         {                                                                                      \
           const half8_t sg = *reinterpret_cast<const half8_t*>(smem + byte_addr<BB>(cur.vs, lr_s)); \
@@ -427,22 +446,22 @@ void decode_lut_kernel(DecodeParams p) {
       // loads in flight the wait before each step leaves the other buffer's
       // loads outstanding.
       TokenData<KB, KQ, VB, VQ> ta, tb;
-      if (base < t1) load_token(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, ta);
+      if (base < t1) load_token<D>(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, ta);
       while (base < t1) {
-        load_token(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, tb);
+        load_token<D>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, tb);
         step(ta, base);
         base += stride;
         if (base >= t1) break;
-        load_token(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, ta);
+        load_token<D>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, ta);
         step(tb, base);
         base += stride;
       }
     } else {
       TokenData<KB, KQ, VB, VQ> nxt;
-      if (base < t1) load_token(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, nxt);
+      if (base < t1) load_token<D>(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, nxt);
       for (; base < t1; base += stride) {
         const TokenData<KB, KQ, VB, VQ> cur = nxt;
-        if (base + stride < t1) load_token(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, nxt);
+        if (base + stride < t1) load_token<D>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, nxt);
         step(cur, base);
       }
     }
@@ -461,6 +480,21 @@ void decode_lut_kernel(DecodeParams p) {
         for (int e = 0; e < 32; ++e) ask[e] = ask[e] * a + __shfl_xor(ask[e], off, 64) * c;
       }
       m = M;
+    }
+    if constexpr (D > 128) {
+      // One partial per wave, [m, l, acc[d], ask[d]], merged by the combine
+      // step with the other waves and splits of this query.
+      if (slot == 0) {
+        float* out = p.part + (((size_t)qi * p.nsplit + split) * kLutWaves + wave) * p.part_stride;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) out[2 + 32 * j + e] = acc[e];
+        if (VQ) {
+#pragma unroll
+          for (int e = 0; e < 32; ++e) out[2 + d + 32 * j + e] = ask[e];
+        }
+        if (j == 0) { out[0] = m; out[1] = l; }
+      }
+      continue;
     }
     const int rec = 2 + 2 * d;
     if (slot == 0) {
@@ -499,24 +533,37 @@ void decode_lut_kernel(DecodeParams p) {
   }
 }
 
+template <int D, int KB, bool KQ, int VB, bool VQ>
+hipError_t launch_lut_d(const DecodeParams& p, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL((decode_lut_kernel<D, KB, KQ, VB, VQ>), dim3(nblocks), dim3(lut_threads(KQ && VQ)), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int KB, bool KQ, int VB, bool VQ>
 hipError_t launch_lut(const DecodeParams& p, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((decode_lut_kernel<KB, KQ, VB, VQ>), dim3(nblocks), dim3(lut_threads(KQ && VQ)), 0, s, p);
-  return hipGetLastError();
+  switch (p.d) {
+    case 128: return launch_lut_d<128, KB, KQ, VB, VQ>(p, nblocks, s);
+    case 256: return launch_lut_d<256, KB, KQ, VB, VQ>(p, nblocks, s);
+    case 512: return launch_lut_d<512, KB, KQ, VB, VQ>(p, nblocks, s);
+    case 1024: return launch_lut_d<1024, KB, KQ, VB, VQ>(p, nblocks, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+int lut_waves(int kqjl, int vqjl) { return lut_threads(kqjl && vqjl) / 64; }
+
 bool lut_supported(int d, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl) {
-  if (d != 128) return false;
-  if (kside) return kbits == 2 && side_rank == 16 && side_bits == 4 && vbits == 4 && !vqjl;
+  if (d != 128 && d != 256 && d != 512 && d != 1024) return false;
+  if (kside) return d == 128 && kbits == 2 && side_rank == 16 && side_bits == 4 && vbits == 4 && !vqjl;
   return (kbits == 3 || kbits == 4) && (vbits == 3 || vbits == 4) && (!kqjl || kbits == 3) && (!vqjl || vbits == 3);
 }
 
 
 hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int vbits, int vqjl, int nblocks,
                              hipStream_t s) {
-  if (kbits == 2) return launch_lut<2, false, 4, false>(p, nblocks, s);  // HeadQ keys, 4-bit values
+  if (kbits == 2) return launch_lut_d<128, 2, false, 4, false>(p, nblocks, s);  // HeadQ keys, 4-bit values
   const int key = (kbits == 4 ? 0 : 2 + kqjl) * 4 + (vbits == 4 ? 0 : 2 + vqjl);
   switch (key) {
     case 0 * 4 + 0: return launch_lut<4, false, 4, false>(p, nblocks, s);

@@ -65,7 +65,7 @@ def test_schemes_ragged_gqa(tq, scheme, n):
     print(scheme, n, "worst rel L2 %.3g band %d" % (worst, n_band))
 
 
-@pytest.mark.parametrize("d", [32, 64, 256, 1024])
+@pytest.mark.parametrize("d", [32, 64, 256, 512, 1024])
 @pytest.mark.parametrize("scheme", ["kqv", "qkqv", "kv"])
 def test_head_dims(tq, d, scheme):
     T = 700 if d < 1024 else 300
