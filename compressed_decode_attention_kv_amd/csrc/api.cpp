@@ -167,25 +167,28 @@ tq_status sketch_cat_on_device(uint64_t seed, int d, const _Float16** out) {
   return TQ_OK;
 }
 
-// PROD on the generic path at d >= 256: S r is a [rows x d] x [d x d] GEMM,
-// run by rocBLAS in chunks of vectors.  The quantiser writes 2^12 r as fp16
+// PROD on the generic path (fp32 inputs, or d != 128): S r is a
+// [rows x d] x [d x d] GEMM, run by rocBLAS in chunks of vectors.  The quantiser writes 2^12 r as fp16
 // hi | lo rows; P = [r_hi | r_lo] [S | S]^T with fp16 products (exact) and
 // fp32 accumulation; a small kernel packs the signs.  Scratch for one chunk
 // (8 d bytes per row) is taken from and returned to the stream's pool.
-constexpr long kSketchChunkRows = 16384;
+// Scratch per chunk: 8 d bytes per row (fp16 hi|lo residual + fp32 product),
+// 128 MiB in all, i.e. 16384 rows at d = 1024 and 131072 at d = 128.
+constexpr long kSketchChunkBytes = 128l << 20;
 
 tq_status hip_status(hipError_t e, const char* what);
 
 tq_status quantize_prod_gemm(const QuantParams& p0, hipStream_t st) {
   const int d = p0.d;
   const long BH = (long)p0.B * p0.H;
+  const long chunk_rows = kSketchChunkBytes / (8l * d);
   int tn, nbh_per;
-  if (p0.T >= kSketchChunkRows) {
-    tn = (int)kSketchChunkRows;
+  if (p0.T >= chunk_rows) {
+    tn = (int)chunk_rows;
     nbh_per = 1;
   } else {
     tn = p0.T;
-    nbh_per = (int)std::max<long>(1, std::min<long>(BH, kSketchChunkRows / p0.T));
+    nbh_per = (int)std::max<long>(1, std::min<long>(BH, chunk_rows / p0.T));
   }
   const size_t rows = (size_t)tn * nbh_per;
   const size_t rc_bytes = rows * 2 * d * sizeof(_Float16), p_bytes = rows * d * sizeof(float);
@@ -516,7 +519,7 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
     if (tq_status s = hip_status(launch_quantize_mfma(p, grid, nblocks, (hipStream_t)stream), "quantize launch")) return s;
   } else {
     p.bh0 = 0; p.nbh = x->B * x->H; p.t0 = 0; p.tn = x->T; p.rcat = nullptr;
-    if (mode == TQ_MODE_PROD && x->d >= 256) {
+    if (mode == TQ_MODE_PROD) {
       p.seed_for_cat = seed;
       if (tq_status s = quantize_prod_gemm(p, (hipStream_t)stream)) return s;
     } else if (mode == TQ_MODE_HEADQ) {

@@ -110,13 +110,9 @@ __device__ __forceinline__ void headq_side(const QuantParams& p, const float* v,
 
 template <int BITS, int MODE, typename TIN>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
-  // Residual staging of the QJL sketch: per wave, 64/L rows of d+1 floats
-  // (the +1 pad puts the rows of different vectors in different banks).
-  constexpr int kRowsFloats = 2048 + 64;
   __shared__ float s_cent[16], s_bnd[16];
   // HEADQ: (Pi U_h)^T, d * rank floats, in dynamic LDS (sized at launch).
   extern __shared__ float s_side[];
-  __shared__ float s_r[MODE == TQ_MODE_PROD ? 4 : 1][MODE == TQ_MODE_PROD ? kRowsFloats : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int L = p.L, j = lane & (L - 1), slot = lane / L, vpw = 64 / L;
@@ -197,42 +193,20 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
         g2 = fmaf(v[e], v[e], g2);
       }
       g2 = group_sum(g2, L);
-      if (p.rcat) {
-        // Residual x 2^12 as fp16 hi (toward zero) + lo: r - hi is exact in
-        // fp32, so the GEMM's fp16 products reproduce S r to about 2^-22.
-        if (valid) {
-          _Float16* row = p.rcat + ((size_t)blockIdx.y * p.tn + (t - p.t0)) * (2 * d);
+      // Residual x 2^12 as fp16 hi (toward zero) + lo: r - hi is exact in
+      // fp32, so the sketch GEMM's fp16 products reproduce S r to ~2^-22.
+      if (valid) {
+        _Float16* row = p.rcat + ((size_t)blockIdx.y * p.tn + (t - p.t0)) * (2 * d);
 #pragma unroll
-          for (int e = 0; e < 32; e += 2) {
-            const float r0 = v[e] * 4096.0f, r1 = v[e + 1] * 4096.0f;
-            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-            const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-            const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(r0 - (float)hi[0], r1 - (float)hi[1]));
-            *reinterpret_cast<h2*>(row + 32 * j + e) = hi;
-            *reinterpret_cast<h2*>(row + d + 32 * j + e) = lo;
-          }
-          if (j == 0) p.gamma[vec] = sqrtf(g2);
+        for (int e = 0; e < 32; e += 2) {
+          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+          const float r0 = v[e] * 4096.0f, r1 = v[e + 1] * 4096.0f;
+          const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+          const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(r0 - (float)hi[0], r1 - (float)hi[1]));
+          *reinterpret_cast<h2*>(row + 32 * j + e) = hi;
+          *reinterpret_cast<h2*>(row + d + 32 * j + e) = lo;
         }
-      } else {
-        // Stage the residual of each vector of this wave in LDS: row = slot.
-        float* rrow = &s_r[wave][0];
-        const int rstride = d + 1;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 32; ++e) rrow[slot * rstride + 32 * j + e] = v[e];
-        __syncthreads();
-        uint32_t sw = 0;
-        for (int i = 0; i < 32; ++i) {
-          const float* srow = p.S + (size_t)(32 * j + i) * d;
-          float acc = 0.f;
-          for (int k = 0; k < d; ++k) acc = fmaf(srow[k], rrow[slot * rstride + k], acc);
-          sw |= (acc >= 0.f ? 1u : 0u) << i;
-        }
-        if (!(nu > 0.f)) sw = 0;
-        if (valid) {
-          reinterpret_cast<uint32_t*>(p.qjl + vec * (d / 8))[j] = sw;
-          if (j == 0) p.gamma[vec] = sqrtf(g2);
-        }
+        if (j == 0) p.gamma[vec] = sqrtf(g2);
       }
     }
 

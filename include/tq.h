@@ -14,8 +14,8 @@
  *     caller; "host" pointers are ordinary CPU memory.  The library owns only
  *     its cached per-(device, seed, d) constants and one rocBLAS handle per
  *     device (all freed by tq_release_cache).  A tq_quantize of a PROD
- *     tensor at d >= 256 also takes a stream-ordered scratch buffer (8 d
- *     bytes per row, at most 16384 rows), and one of a HEADQ tensor a
+ *     tensor that is not fp16 at d = 128 also takes a stream-ordered scratch
+ *     buffer (8 d bytes per row, at most 128 MiB), and one of a HEADQ tensor a
  *     buffer for the rotated basis (4 H d rank bytes), from the stream's
  *     memory pool and returns it before the call's work completes on that
  *     stream.
