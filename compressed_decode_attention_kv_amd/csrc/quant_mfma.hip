@@ -283,17 +283,17 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       }
       if (BITS == 4) {
         u32x4 w4 = {words[0], words[1], words[2], words[3]};
-        *reinterpret_cast<u32x4*>(dst) = w4;
+        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(dst));
       } else if (BITS == 3) {
         u32x3 w3 = {words[0], words[1], words[2]};
-        *reinterpret_cast<u32x3*>(dst) = w3;
+        __builtin_nontemporal_store(w3, reinterpret_cast<u32x3*>(dst));
       } else if (BITS == 2) {
         u32x2 w2 = {words[0], words[1]};
-        *reinterpret_cast<u32x2*>(dst) = w2;
+        __builtin_nontemporal_store(w2, reinterpret_cast<u32x2*>(dst));
       } else {
-        dst[0] = words[0];
+        __builtin_nontemporal_store(words[0], dst);
       }
-      if (g == 0) p.norms[vbase + t] = nu;
+      if (g == 0) __builtin_nontemporal_store(nu, p.norms + vbase + t);
     }
 
     if constexpr (kProd) {
@@ -338,8 +338,9 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         sbits |= sc << (4 * mb);
       }
       if (valid) {
-        *reinterpret_cast<uint32_t*>(p.qjl + vbase * 16 + (uint32_t)(t * 16 + g * 4)) = nu > 0.f ? sbits : 0u;
-        if (g == 0) p.gamma[vbase + t] = nu > 0.f ? sqrtf(g2) : 0.f;
+        __builtin_nontemporal_store(nu > 0.f ? sbits : 0u,
+                                    reinterpret_cast<uint32_t*>(p.qjl + vbase * 16 + (uint32_t)(t * 16 + g * 4)));
+        if (g == 0) __builtin_nontemporal_store(nu > 0.f ? sqrtf(g2) : 0.f, p.gamma + vbase + t);
       }
     }
   }
