@@ -39,14 +39,15 @@ namespace tq {
 namespace {
 
 // Block size and token loop, per variant (chosen by measurement):
-//   * sketches on both K and V: 8 waves (2 per SIMD, up to 256 VGPRs) and a
-//     two-buffer token loop;
-//   * a sketch on one side: 12 waves (3 per SIMD, 168 VGPRs) and a
-//     one-buffer loop (prefetch into a second set, then copy), since two
-//     buffers do not fit 168 VGPRs without serialising the table reads;
-//   * no sketch: 12 waves and the two-buffer loop.
+//   * sketches on both K and V: 8 waves (2 per SIMD, up to 256 VGPRs);
+//     every other variant 12 waves (3 per SIMD, 168 VGPRs);
+//   * one token step is prefetched.  Two register buffers used in turn save
+//     the copies of a prefetch-then-copy loop, and win at d <= 256; with a
+//     sketch on one side only at d >= 512 they spill and serialise the table
+//     reads, and the copy loop is kept there.  Deeper prefetch (three or four
+//     buffers) measured no faster.
 constexpr int lut_threads(bool both_sketched) { return both_sketched ? 512 : 768; }
-constexpr bool lut_two_buffers(bool kq, bool vq) { return kq == vq; }
+constexpr bool lut_two_buffers(int d, bool kq, bool vq) { return kq == vq || d <= 256; }
 constexpr int kMaxLutWaves = 12;
 // LDS map.  A table indexed by a whole packed byte needs a 64 KB window
 // (entry e at window + e*256, the byte lands in address bits 8..15 straight
@@ -438,7 +439,7 @@ void decode_lut_kernel(DecodeParams p) {
       }
     };
 
-    if constexpr (lut_two_buffers(KQ, VQ)) {
+    if constexpr (lut_two_buffers(D, KQ, VQ)) {
       // Two buffers used in turn, so that the next step's loads never
       // overwrite registers that the current step still reads (no copies).
       // The next step is loaded unconditionally (the token index is clamped,

@@ -31,6 +31,8 @@
 //     per tile with fp32 accumulation keep about 22 bits.  The rows of S are
 //     ordered so that lane (g, tau) receives sketch rows 32 g .. 32 g + 31:
 //     its 32 sign bits are word g of the token's sign block.
+//   * stores: non-temporal, so that a decode streaming the cache soon after
+//     does not meet its lines still dirty in the caches (~20% slower).
 #include <cfloat>
 #include <cmath>
 
