@@ -5,6 +5,7 @@
         <write counter_collection.csv> --calib-bytes N
   python -m compressed_decode_attention_kv_amd.profiling decode-traffic <fetch csv> <write csv> \
         --calib-bytes N --algorithmic-bytes A --title "..." --command "..." [--command ...]
+  python -m compressed_decode_attention_kv_amd.profiling counters <counter_collection.csv> [...]
 
 `stats` prints the average duration per kernel.  `decode-traffic` writes the
 committed per-scheme summary: the traffic table, the decode chain's bytes
@@ -15,6 +16,15 @@ the fetch side scaled by what the same counter reads for the library's
 streaming-read kernel over a buffer of N bytes (non-temporal loads count at
 half their size on this device), the write side by --write-factor (1.0: the
 counter matches the known write volume of the quantize kernels).
+`counters` prints, per kernel, the median over dispatches of rocprof's own
+derived utilisations from SQ counters of one or more --pmc passes, each
+computed within a dispatch against that dispatch's GRBM_GUI_ACTIVE:
+  VALUBusy        = SQ_ACTIVE_INST_VALU / CUs / busy cycles
+  LdsUtil         = SQ_LDS_IDX_ACTIVE / CUs / busy cycles
+  LDSBankConflict = SQ_LDS_BANK_CONFLICT / CUs / busy cycles
+  MfmaUtil        = SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / busy cycles
+The CSV sums GRBM_GUI_ACTIVE over the XCDs, so busy cycles are that sum over
+the XCD count; CU, SIMD and XCD counts come from run_agent_info.csv beside it.
 """
 import argparse
 import collections
@@ -29,11 +39,13 @@ CHAIN = ("qprep_kernel", "decode_lut_kernel", "decode_split_kernel", "combine_ke
 
 
 def decode_sources_sha():
-    """sha1 over the sources of the decode chain's kernels."""
+    """sha1 over the sources of the decode chain's kernels and the build
+    script (its per-source compiler flags shape the kernels too)."""
     h = hashlib.sha1()
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    pkg = os.path.dirname(os.path.abspath(__file__))
     for f in DECODE_SOURCES:
-        h.update(open(os.path.join(src, f), "rb").read())
+        h.update(open(os.path.join(pkg, "csrc", f), "rb").read())
+    h.update(open(os.path.join(pkg, "build.py"), "rb").read())
     return h.hexdigest()
 
 
@@ -117,6 +129,61 @@ def decode_traffic(fetch_path, write_path, calib_bytes, algorithmic, title, comm
     return "\n".join(out)
 
 
+def _agent(path):
+    info = os.path.join(os.path.dirname(path), "run_agent_info.csv")
+    cu, simd, xcc = 256, 1024, 8
+    if os.path.exists(info):
+        for r in csv.DictReader(open(info)):
+            if r.get("Agent_Type") == "GPU":
+                cu, simd, xcc = int(r["Cu_Count"]), int(r["Simd_Count"]), int(r["Num_Xcc"])
+    return cu, simd, xcc
+
+
+_DERIVED = (  # name, numerator counter, divisor ("cu" or "simd")
+    ("VALUBusy%", "SQ_ACTIVE_INST_VALU", "cu"),
+    ("LdsUtil%", "SQ_LDS_IDX_ACTIVE", "cu"),
+    ("LDSBankConflict%", "SQ_LDS_BANK_CONFLICT", "cu"),
+    ("MfmaUtil%", "SQ_VALU_MFMA_BUSY_CYCLES", "simd"),
+)
+
+
+def counters(paths):
+    """Per-kernel medians over dispatches of the VALU instruction count and of
+    rocprof's derived utilisations (each computed within one dispatch)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))   # kernel -> column -> values
+    for path in paths:
+        cu, simd, xcc = _agent(path)
+        disp = collections.defaultdict(dict)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            if "tq" not in r["Kernel_Name"]:
+                continue
+            disp[r["Dispatch_Id"]][r["Counter_Name"]] = float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        for did, c in disp.items():
+            k = names[did]
+            if "SQ_INSTS_VALU" in c:
+                per[k]["VALU insts"].append(c["SQ_INSTS_VALU"])
+            busy = c.get("GRBM_GUI_ACTIVE", 0.0) / xcc
+            if busy <= 0:
+                continue
+            for name, num, unit in _DERIVED:
+                if num in c:
+                    per[k][name].append(100.0 * c[num] / (cu if unit == "cu" else simd) / busy)
+
+    def median(v):
+        v = sorted(v)
+        return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+    cols = ["VALU insts"] + [d[0] for d in _DERIVED]
+    out = ["%-90s %5s " % ("kernel", "disp") + " ".join("%16s" % c for c in cols)]
+    for k in sorted(per):
+        n = max(len(v) for v in per[k].values())
+        out.append("%-90s %5d " % (short(k), n) +
+                   " ".join(("%16.4g" % median(per[k][c])) if per[k].get(c) else "%16s" % "-" for c in cols))
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -135,9 +202,13 @@ def main(argv=None):
     dt.add_argument("--title", required=True)
     dt.add_argument("--command", action="append", default=[])
     dt.add_argument("--write-factor", type=float, default=1.0)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats(a.csv))
+    elif a.cmd == "counters":
+        print(counters(a.csv))
     elif a.cmd == "traffic":
         print(traffic(a.fetch_csv, a.write_csv, a.calib_bytes, a.write_factor))
     else:
