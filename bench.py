@@ -183,6 +183,37 @@ def main():
     stream_gbs = sbuf.numel() / (s_ms * 1e-3) / 1e9
     del sbuf
 
+    # One generation step on the same cache: append one new token per
+    # (batch, head) to K and V, then decode over per-sequence lengths.  The
+    # token goes to the last slot (T - 1) and is that slot's own token, so the
+    # cache is unchanged and the step can be repeated.
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    kn, vn = K[:, :, T - 1:T].contiguous(), V[:, :, T - 1:T].contiguous()
+    kndesc, _ = tq.tensor_desc(kn)
+    vndesc, _ = tq.tensor_desc(vn)
+
+    def gen_step():
+        tq._check(lib.tq_quantize_append(ctypes.byref(kndesc), tq.KEYS, sid, n, 0, None, pos.data_ptr(),
+                                         ctypes.byref(kp.c), stream()))
+        tq._check(lib.tq_quantize_append(ctypes.byref(vndesc), tq.VALUES, sid, n, 0, None, pos.data_ptr(),
+                                         ctypes.byref(vp.c), stream()))
+        tq._check(lib.tq_decode_attention_lens(ctypes.byref(qdesc), ctypes.byref(kp.c), ctypes.byref(vp.c),
+                                               lens.data_ptr(), out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                                               ws.numel(), stream()))
+
+    for _ in range(3):
+        gen_step()
+    torch.cuda.synchronize()
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in gev:
+        a.record()
+        gen_step()
+        b.record()
+    torch.cuda.synchronize()
+    gen_ms = sorted(a.elapsed_time(b) for a, b in gev)[len(gev) // 2]
+    assert torch.isfinite(out).all().item()
+
     res = {
         "metric": "packed-KV decode attention GB/s (% HBM peak) + quantize tok/s, d=128 n=4",
         "value": round(dec_gbs, 1),
@@ -201,6 +232,7 @@ def main():
         "decode_pct_of_stream_read": round(100.0 * dec_gbs / stream_gbs, 2),
         "quantize_ms": round(q_avg, 4),
         "quantize_tok_per_s": round(tok_s, 1),
+        "append_decode_step_ms": round(gen_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.scheme),
                      "kernel": "decode chain (query prep + split decode + combine)",

@@ -406,6 +406,11 @@ tq_status fill_codebook(int d, int bits, float* c16, float* b16) {
   return TQ_OK;
 }
 
+tq_status quantize_core(const tq_tensor_desc* x, int mode, int bits, uint64_t seed, const tq_headq* hq,
+                        const tq_packed* out, int T_cap, const int32_t* pos, void* stream);
+tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v, const int32_t* lens,
+                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
 void fill_scoring(const tq_tensor_desc* q, const tq_packed* k, const DecodePlan& pl, char* ws, DecodeParams* dp) {
   std::memset(dp, 0, sizeof(*dp));
   dp->B = k->B; dp->Hkv = k->H; dp->G = pl.G; dp->Hq = q->H; dp->T = k->T; dp->T_cap = k->T_cap;
@@ -495,7 +500,42 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
   if (mode == TQ_MODE_HEADQ && (!out->side || !out->side_scale || !aligned(out->side, 16) || !aligned(out->side_scale, 16)))
     return fail(TQ_EINVAL, "HeadQ side planes missing or not 16-byte aligned");
   if ((long)x->B * x->H * (long)T_cap > (1L << 40)) return fail(TQ_EINVAL, "cache too large");
+  if (tq_status s = quantize_core(x, mode, bits, seed, hq, out, T_cap, nullptr, stream)) return s;
+  out->B = x->B; out->H = x->H; out->T = x->T; out->T_cap = T_cap; out->d = x->d;
+  out->mode = mode; out->bits = bits; out->seed = seed;
+  out->side_rank = hq ? hq->rank : 0; out->side_bits = hq ? hq->side_bits : 0;
+  out->basis = hq ? hq->basis : nullptr;
+  return ok();
+}
 
+tq_status tq_quantize_append(const tq_tensor_desc* x, int32_t which, int32_t scheme, int32_t n_bits, uint64_t seed,
+                             const tq_headq* hq, const int32_t* pos, tq_packed* cache, void* stream) {
+  if (tq_status s = check_tensor(x, "x")) return s;
+  int mode, bits;
+  if (tq_status s = modes_of(scheme, n_bits, which, &mode, &bits)) return s;
+  if (tq_status s = check_packed(cache, "cache")) return s;
+  if (!pos || !aligned(pos, 4)) return fail(TQ_EINVAL, "positions NULL or not 4-byte aligned");
+  if (cache->B != x->B || cache->H != x->H || cache->d != x->d)
+    return fail(TQ_EMISMATCH, "new tokens (B=%d H=%d d=%d) do not match the cache (B=%d H=%d d=%d)", x->B, x->H, x->d,
+                cache->B, cache->H, cache->d);
+  if (cache->mode != mode || cache->bits != bits || cache->seed != seed)
+    return fail(TQ_EMISMATCH, "scheme/bits/seed give mode %d with %d bits, seed %llu; the cache holds mode %d, %d bits, seed %llu",
+                mode, bits, (unsigned long long)seed, cache->mode, cache->bits, (unsigned long long)cache->seed);
+  if ((mode == TQ_MODE_HEADQ) != (hq != nullptr))
+    return fail(TQ_EINVAL, mode == TQ_MODE_HEADQ ? "HeadQ keys need a tq_headq" : "tq_headq given for a non-HeadQ tensor");
+  if (hq && (hq->basis != cache->basis || hq->rank != cache->side_rank || hq->side_bits != cache->side_bits))
+    return fail(TQ_EMISMATCH, "HeadQ basis, rank or side bits differ from the cache's");
+  if (x->T > cache->T_cap) return fail(TQ_EINVAL, "%d new tokens exceed T_cap=%d", x->T, cache->T_cap);
+  tq_packed planes = *cache;
+  return quantize_core(x, mode, bits, seed, hq, &planes, cache->T_cap, pos, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+tq_status quantize_core(const tq_tensor_desc* x, int mode, int bits, uint64_t seed, const tq_headq* hq,
+                        const tq_packed* out, int T_cap, const int32_t* pos, void* stream) {
   QuantParams p;
   std::memset(&p, 0, sizeof(p));
   p.x = x->data; p.dtype = x->dtype; p.B = x->B; p.H = x->H; p.T = x->T; p.T_cap = T_cap; p.d = x->d; p.L = x->d / 32;
@@ -510,6 +550,7 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
   if (hq) { p.basis = hq->basis; p.rank = hq->rank; p.side_bits = hq->side_bits; }
   p.codes = out->codes; p.norms = out->norms; p.qjl = out->qjl; p.gamma = out->gamma;
   p.side = out->side; p.side_scale = out->side_scale;
+  p.pos = pos;
   QuantGrid grid;
   if (quant_mfma_supported(p) && quant_grid(x->d, bits, &grid)) {
     int cus = 0;
@@ -539,12 +580,12 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
       if (tq_status s = hip_status(launch_quantize(p, (hipStream_t)stream), "quantize launch")) return s;
     }
   }
-  out->B = x->B; out->H = x->H; out->T = x->T; out->T_cap = T_cap; out->d = x->d;
-  out->mode = mode; out->bits = bits; out->seed = seed;
-  out->side_rank = hq ? hq->rank : 0; out->side_bits = hq ? hq->side_bits : 0;
-  out->basis = hq ? hq->basis : nullptr;
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 tq_status tq_decode_workspace_size(const tq_packed* k, const tq_packed* v, int32_t Hq, size_t* bytes) {
   if (!bytes) return fail(TQ_EINVAL, "output pointer is NULL");
@@ -557,6 +598,22 @@ tq_status tq_decode_workspace_size(const tq_packed* k, const tq_packed* v, int32
 
 tq_status tq_decode_attention(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v, float* out,
                               float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return decode_core(q, k, v, nullptr, out, lse, ws, ws_bytes, stream);
+}
+
+tq_status tq_decode_attention_lens(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v,
+                                   const int32_t* lens, float* out, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (!lens || !aligned(lens, 4)) return fail(TQ_EINVAL, "lengths NULL or not 4-byte aligned");
+  return decode_core(q, k, v, lens, out, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v, const int32_t* lens,
+                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (!k || !v) return fail(TQ_EINVAL, "packed descriptor is NULL");
   if (!q) return fail(TQ_EINVAL, "query descriptor is NULL");
   DecodePlan pl;
@@ -578,6 +635,7 @@ tq_status tq_decode_attention(const tq_tensor_desc* q, const tq_packed* k, const
   DecodeParams dp;
   fill_scoring(q, k, pl, w, &dp);
   dp.v = {v->codes, v->norms, v->qjl, v->gamma, v->side, v->side_scale};
+  dp.lens = lens;
   float vb[16];
   if (tq_status s = fill_codebook(v->d, v->bits, dp.vc, vb)) return s;
   dp.v_qjl = (float)(std::sqrt(M_PI / 2.0) / v->d);
@@ -606,6 +664,10 @@ tq_status tq_decode_attention(const tq_tensor_desc* q, const tq_packed* k, const
   if (tq_status s = hip_status(launch_combine(cp, st), "combine launch")) return s;
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 tq_status tq_metrics_workspace_size(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v, size_t* bytes) {
   if (!bytes) return fail(TQ_EINVAL, "output pointer is NULL");

@@ -177,7 +177,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int split = r % p.nsplit, bkv = r / p.nsplit;
   const int b = bkv / p.Hkv, kvh = bkv % p.Hkv;
   const int qi = b * p.Hq + kvh * p.G + g;
-  const int t0 = split * p.chunk, t1 = min(p.T, t0 + p.chunk);
+  // Per-sequence length (clamped to [0, T]); a split past it has no tokens.
+  const int Tb = p.lens ? min(max(p.lens[b], 0), p.T) : p.T;
+  const int t0 = split * p.chunk, t1 = min(Tb, t0 + p.chunk);
   const int64_t vbase = (int64_t)bkv * p.T_cap;
 
   KScorer<KB, KQ, KS> ks;
@@ -286,7 +288,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     s_M = M; s_L = Lsum;
   }
   __syncthreads();
-  const float invl = 1.0f / s_L;
+  // A sequence with no tokens (length 0) has l = 0: its output is 0 and its
+  // log-sum-exp -inf.
+  const float invl = s_L > 0.f ? 1.0f / s_L : 0.f;
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
     float a = 0.f, k = 0.f;
     for (int s = 0; s < p.nsplit; ++s) {
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     __syncthreads();
   }
   for (int i = threadIdx.x; i < d; i += blockDim.x) p.out[(size_t)qi * d + i] = s_o[i];
-  if (threadIdx.x == 0 && p.lse) p.lse[qi] = (s_M + log2f(s_L)) * 0.69314718055994530942f;
+  if (threadIdx.x == 0 && p.lse) p.lse[qi] = s_L > 0.f ? (s_M + log2f(s_L)) * 0.69314718055994530942f : -INFINITY;
 }
 
 // ---- metric scores ---------------------------------------------------------------

@@ -272,7 +272,9 @@ void decode_lut_kernel(DecodeParams p) {
     const int split = r % p.nsplit, bkv = r / p.nsplit;
     const int b = bkv / p.Hkv, kvh = bkv % p.Hkv;
     const int qi = b * p.Hq + kvh * p.G + g;
-    const int t0 = split * p.chunk, t1 = min(p.T, t0 + p.chunk);
+    // Per-sequence length (clamped to [0, T]); a split past it has no tokens.
+    const int Tb = p.lens ? min(max(p.lens[b], 0), p.T) : p.T;
+    const int t0 = split * p.chunk, t1 = min(Tb, t0 + p.chunk);
     const size_t vbase = (size_t)bkv * p.T_cap;
     HeadPlanes hp;
     hp.kc = p.k.codes + vbase * (D * KB / 8);

@@ -49,6 +49,9 @@ struct QuantParams {
   _Float16* rcat;
   uint64_t seed_for_cat;  // host side only: the seed of S for the GEMM path
   const float* rbasis;    // HEADQ: (Pi U_h)^T per head, [H][rank][d]
+  // Append: token t of sequence b is written to slot pos[b] + t (device
+  // int32 [B]); slots outside [0, T_cap) are skipped.  NULL: slot t.
+  const int* pos;
 };
 
 // Uniform grid over the unit-sphere coordinate y in [-1, 1] used to find the
@@ -75,6 +78,9 @@ struct DecodeParams {
   float scale_log2;     // log2(e)/sqrt(d)
   const float* qrot; const float* qsk; const float* qw;
   float* part;
+  // Per-sequence lengths (device int32 [B]), each clamped to [0, T); NULL:
+  // every sequence has T tokens.
+  const int* lens;
 };
 
 struct QPrepParams {

@@ -140,6 +140,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   const TIN* xbase = reinterpret_cast<const TIN*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh;
   const int64_t vbase = (int64_t)bh * p.T_cap;
   const int tok_per_block = 4 * vpw * kSteps;
+  const int64_t slot0 = p.pos ? p.pos[b] : 0;  // destination slot of token 0
 
   for (int step = 0; step < kSteps; ++step) {
     const int t = p.t0 + blockIdx.x * tok_per_block + (step * 4 + wave) * vpw + slot;
@@ -179,8 +180,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
       w[wi] |= idx[e] << sh;
       if (sh + BITS > 32) w[wi + 1] |= idx[e] >> (32 - sh);
     }
-    const int64_t vec = vbase + t;
-    if (valid) {
+    // Destination slot: t, or pos[b] + t when appending; never outside [0, T_cap).
+    const int64_t tw = slot0 + t;
+    const bool wr = valid && tw >= 0 && tw < p.T_cap;
+    const int64_t vec = vbase + tw;
+    if (wr) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vec * (d * BITS / 8)) + j * BITS;
 #pragma unroll
       for (int k = 0; k < BITS; ++k) __builtin_nontemporal_store(w[k], dst + k);
@@ -210,12 +214,12 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
           *reinterpret_cast<h2*>(row + 32 * j + e) = hi;
           *reinterpret_cast<h2*>(row + d + 32 * j + e) = lo;
         }
-        if (j == 0) __builtin_nontemporal_store(sqrtf(g2), p.gamma + vec);
+        if (j == 0 && wr) __builtin_nontemporal_store(sqrtf(g2), p.gamma + vec);
       }
     }
 
     if (MODE == TQ_MODE_HEADQ) {
-      headq_side(p, v, idx, nu, s_cent, s_side, j, L, valid, vec);
+      headq_side(p, v, idx, nu, s_cent, s_side, j, L, wr, vec);
     }
   }
 }
@@ -344,7 +348,10 @@ __global__ __launch_bounds__(256) void sign_pack_kernel(const float* __restrict_
   const int w = (int)(idx % words);
   const int hh = (int)(row / p.tn), t = p.t0 + (int)(row % p.tn);
   if (t >= p.T) return;
-  const int64_t vec = (int64_t)(p.bh0 + hh) * p.T_cap + t;
+  const int bh = p.bh0 + hh;
+  const int64_t tw = (int64_t)t + (p.pos ? p.pos[bh / p.H] : 0);
+  if (tw < 0 || tw >= p.T_cap) return;
+  const int64_t vec = (int64_t)bh * p.T_cap + tw;
   const float* pr = P + row * d + 32 * w;
   uint32_t bits = 0;
 #pragma unroll

@@ -184,6 +184,10 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
     const int bh = tile / tph;
     const int t = (tile - bh * tph) * 16 + tau;
     const bool valid = t < p.T;
+    // Destination slot: t, or pos[b] + t when appending; never outside [0, T_cap).
+    const int64_t tw64 = (int64_t)t + (p.pos ? p.pos[bh / p.H] : 0);
+    const bool wr = valid && tw64 >= 0 && tw64 < p.T_cap;
+    const uint32_t tw = (uint32_t)tw64;
 
     // ||x||^2: fp16 products are exact in fp32.
     float ss = 0.f;
@@ -276,9 +280,9 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
 
     // Per-head planes: scalar base + 32-bit lane offset.
     const size_t vbase = (size_t)bh * p.T_cap;
-    if (valid) {
+    if (wr) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vbase * (16 * BITS) +
-                                                  (uint32_t)(t * (16 * BITS) + g * (4 * BITS)));
+                                                  (uint32_t)(tw * (16 * BITS) + g * (4 * BITS)));
       if (!(nu > 0.f)) {
 #pragma unroll
         for (int k = 0; k < BITS; ++k) words[k] = 0;
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       } else {
         __builtin_nontemporal_store(words[0], dst);
       }
-      if (g == 0) __builtin_nontemporal_store(nu, p.norms + vbase + t);
+      if (g == 0) __builtin_nontemporal_store(nu, p.norms + vbase + tw);
     }
 
     if constexpr (kProd) {
@@ -339,10 +343,10 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         for (int i = 0; i < 4; ++i) sc |= (acc[i] >= 0.f ? 1u : 0u) << i;
         sbits |= sc << (4 * mb);
       }
-      if (valid) {
+      if (wr) {
         __builtin_nontemporal_store(nu > 0.f ? sbits : 0u,
-                                    reinterpret_cast<uint32_t*>(p.qjl + vbase * 16 + (uint32_t)(t * 16 + g * 4)));
-        if (g == 0) __builtin_nontemporal_store(nu > 0.f ? sqrtf(g2) : 0.f, p.gamma + vbase + t);
+                                    reinterpret_cast<uint32_t*>(p.qjl + vbase * 16 + (uint32_t)(tw * 16 + g * 4)));
+        if (g == 0) __builtin_nontemporal_store(nu > 0.f ? sqrtf(g2) : 0.f, p.gamma + vbase + tw);
       }
     }
   }

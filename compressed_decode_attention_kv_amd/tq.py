@@ -25,8 +25,9 @@ MODE_PLAIN, MODE_MSE, MODE_PROD, MODE_HEADQ = range(4)
 SCHEMES = {"kv": 0, "tq-kv": 1, "kqv": 2, "qkqv": 3, "tq-qkv": 4, "headq": 5}
 
 EXPORTS = ["tq_abi_version", "tq_status_str", "tq_last_error", "tq_codebook_build", "tq_scheme_modes",
-           "tq_packed_layout", "tq_rotation_state", "tq_quantize", "tq_decode_workspace_size",
-           "tq_decode_attention", "tq_metrics_workspace_size", "tq_metrics", "tq_headq_fit",
+           "tq_packed_layout", "tq_rotation_state", "tq_quantize", "tq_quantize_append",
+           "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_attention_lens",
+           "tq_metrics_workspace_size", "tq_metrics", "tq_headq_fit",
            "tq_stream_read", "tq_release_cache"]
 
 
@@ -71,9 +72,13 @@ _sigs = {
     "tq_rotation_state": ([ctypes.c_uint64, ctypes.c_int32, _P(ctypes.c_float), _P(ctypes.c_float)], ctypes.c_int),
     "tq_quantize": ([_P(TensorDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64, _P(HeadQ),
                      _P(Packed), ctypes.c_void_p], ctypes.c_int),
+    "tq_quantize_append": ([_P(TensorDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64,
+                            _P(HeadQ), ctypes.c_void_p, _P(Packed), ctypes.c_void_p], ctypes.c_int),
     "tq_decode_workspace_size": ([_P(Packed), _P(Packed), ctypes.c_int32, _P(ctypes.c_size_t)], ctypes.c_int),
     "tq_decode_attention": ([_P(TensorDesc), _P(Packed), _P(Packed), ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "tq_decode_attention_lens": ([_P(TensorDesc), _P(Packed), _P(Packed), ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "tq_metrics_workspace_size": ([_P(TensorDesc), _P(Packed), _P(Packed), _P(ctypes.c_size_t)], ctypes.c_int),
     "tq_metrics": ([_P(TensorDesc), _P(TensorDesc), _P(TensorDesc), _P(Packed), _P(Packed), _P(MetricsOut),
                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
@@ -272,15 +277,41 @@ def quantize(x, which, scheme, n_bits, seed=0, basis=None, rank=16, side_bits=4,
     return pt
 
 
+def _check_index_vector(v, B, like, what):
+    """Positions and lengths are read by the kernels as dense int32 [B] on the
+    device: refuse anything else."""
+    torch = _torch()
+    if v is None or v.dtype != torch.int32 or v.dim() != 1 or v.shape[0] != B or not v.is_contiguous():
+        raise ValueError("%s must be a contiguous int32 tensor of shape [%d]" % (what, B))
+    if v.device != like.device:
+        raise ValueError("%s must be on %s (got %s)" % (what, like.device, v.device))
+
+
+def quantize_append(x, which, scheme, n_bits, pos, cache, seed=0):
+    """Quantise the new tokens x [B, H, Tn, d] and write token t of sequence b
+    at slot pos[b] + t of the PackedTensor `cache` (same scheme, bits and seed
+    as it was written with).  cache.c.T is left as is."""
+    desc, x4 = tensor_desc(x)
+    _check_index_vector(pos, desc.B, x, "pos")
+    hq = None
+    if cache.c.mode == MODE_HEADQ:
+        hq = HeadQ(cache.c.basis, cache.c.side_rank, cache.c.side_bits)
+    _check(_lib.tq_quantize_append(ctypes.byref(desc), which, SCHEMES.get(scheme, scheme), n_bits, seed,
+                                   ctypes.byref(hq) if hq else None, pos.data_ptr(), ctypes.byref(cache.c),
+                                   _stream()))
+    cache._keep_append = (x4, pos)
+
+
 def decode_workspace_size(kp, vp, Hq):
     n = ctypes.c_size_t()
     _check(_lib.tq_decode_workspace_size(ctypes.byref(kp.c), ctypes.byref(vp.c), Hq, ctypes.byref(n)))
     return n.value
 
 
-def decode_attention(q, kp, vp, out=None, lse=None, ws=None):
+def decode_attention(q, kp, vp, out=None, lse=None, ws=None, lens=None):
     """out [B, Hq, d] fp32 = softmax attention of q [B, Hq, d] over the packed
-    cache.  Returns (out, lse)."""
+    cache; with lens (device int32 [B]) sequence b attends over its first
+    lens[b] tokens.  Returns (out, lse)."""
     torch = _torch()
     desc, q4 = tensor_desc(q)
     B, Hq, d = desc.B, desc.H, desc.d
@@ -291,8 +322,14 @@ def decode_attention(q, kp, vp, out=None, lse=None, ws=None):
     need = decode_workspace_size(kp, vp, Hq)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(_lib.tq_decode_attention(ctypes.byref(desc), ctypes.byref(kp.c), ctypes.byref(vp.c), out.data_ptr(),
-                                    lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    if lens is None:
+        _check(_lib.tq_decode_attention(ctypes.byref(desc), ctypes.byref(kp.c), ctypes.byref(vp.c), out.data_ptr(),
+                                        lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    else:
+        _check_index_vector(lens, B, q, "lens")
+        _check(_lib.tq_decode_attention_lens(ctypes.byref(desc), ctypes.byref(kp.c), ctypes.byref(vp.c),
+                                             lens.data_ptr(), out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                                             ws.numel(), _stream()))
     return out, lse
 
 

@@ -183,6 +183,21 @@ tq_status tq_rotation_state(uint64_t seed, int32_t d, float* signs, float* S);
 tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, int32_t n_bits,
                       uint64_t seed, const tq_headq* hq, tq_packed* out, void* stream);
 
+/* Append to a packed cache (the generation loop around the read side:
+ * [P2] "Resumo" and "Contribuições Principais" place the cost in long-context
+ * generation, where the cache grows by one token per step).  Quantises
+ * x [B][H][Tn][d] exactly as tq_quantize does and writes token t of
+ * sequence b to slot pos[b] + t of `cache`.  pos: device int32 [B], read by
+ * the kernels (no host synchronisation); a token whose slot falls outside
+ * [0, cache->T_cap) is not written.  `cache` must carry a header written by
+ * tq_quantize with the same mode, bits and seed as (scheme, n_bits, which,
+ * seed), the same B, H and d as x, and for HEADQ the same basis, rank and
+ * side bits as hq; otherwise TQ_EMISMATCH.  cache->T is not changed: the
+ * caller tracks lengths (tq_decode_attention_lens).  Stream-ordered. */
+tq_status tq_quantize_append(const tq_tensor_desc* x, int32_t which, int32_t scheme, int32_t n_bits,
+                             uint64_t seed, const tq_headq* hq, const int32_t* pos, tq_packed* cache,
+                             void* stream);
+
 /* Workspace bytes tq_decode_attention needs for Hq query heads. */
 tq_status tq_decode_workspace_size(const tq_packed* k, const tq_packed* v, int32_t Hq, size_t* bytes);
 
@@ -195,6 +210,16 @@ tq_status tq_decode_workspace_size(const tq_packed* k, const tq_packed* v, int32
  * tq_decode_workspace_size bytes, 256-byte aligned.  Stream-ordered. */
 tq_status tq_decode_attention(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v,
                               float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* tq_decode_attention over per-sequence lengths: the queries of sequence b
+ * attend over tokens [0, len[b]) of the cache, len[b] clamped to
+ * [0, k->T] (so k->T should be the longest length; the splits are planned
+ * on it).  lens: device int32 [B], 4-byte aligned, read by the kernels.  A
+ * sequence of length 0 gets out = 0 and lse = -inf.  Same workspace as
+ * tq_decode_attention.  Stream-ordered. */
+tq_status tq_decode_attention_lens(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v,
+                                   const int32_t* lens, float* out, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /* Workspace bytes tq_metrics needs. */
 tq_status tq_metrics_workspace_size(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v,

@@ -171,3 +171,39 @@ def test_binding_refuses_bad_headq_basis(tqlib, case):
         assert not bases[case].is_contiguous()
     with pytest.raises(ValueError):
         tqlib.quantize(x, tqlib.KEYS, "headq", 4, 0, basis=bases[case])
+
+
+def test_append_and_lengths_reject_before_any_gpu_call(tqlib):
+    """tq_quantize_append checks the new tokens against the cache header
+    (mode, bits, seed, B, H, d, capacity) and tq_decode_attention_lens its
+    length vector, on the host; fake pointers, invalid cases only."""
+    lib = tqlib.lib()
+    fake = 1 << 20
+    cache = _packed(tqlib, tqlib.MODE_MSE, 4, B=1, H=2, T=8)
+    cache.seed = 5
+
+    def desc(H=2, T=1):
+        return tqlib.TensorDesc(fake, tqlib.F16, 1, H, T, 128, H * T * 128, T * 128, 128)
+
+    kqv, qkqv = tqlib.SCHEMES["kqv"], tqlib.SCHEMES["qkqv"]
+    cases = [
+        (desc(), kqv, 4, 6, fake, tqlib.EMISMATCH),       # seed differs
+        (desc(), kqv, 3, 5, fake, tqlib.EMISMATCH),       # index bits differ
+        (desc(), qkqv, 4, 5, fake, tqlib.EMISMATCH),      # mode differs (PROD keys)
+        (desc(H=3), kqv, 4, 5, fake, tqlib.EMISMATCH),    # heads differ
+        (desc(), kqv, 4, 5, None, tqlib.EINVAL),          # no positions
+        (desc(), kqv, 4, 5, fake + 2, tqlib.EINVAL),      # misaligned positions
+        (desc(T=9), kqv, 4, 5, fake, tqlib.EINVAL),       # more new tokens than the capacity
+    ]
+    for d, scheme, n, seed, pos, want in cases:
+        st = lib.tq_quantize_append(ctypes.byref(d), tqlib.KEYS, scheme, n, seed, None, pos, ctypes.byref(cache), None)
+        assert st == want, (scheme, n, seed, pos, st)
+        assert lib.tq_last_error().decode()
+    hq = tqlib.HeadQ(fake, 16, 4)
+    assert lib.tq_quantize_append(ctypes.byref(desc()), tqlib.KEYS, kqv, 4, 5, ctypes.byref(hq), fake,
+                                  ctypes.byref(cache), None) == tqlib.EINVAL
+    v = _packed(tqlib, tqlib.MODE_PROD, 3, B=1, H=2, T=8)
+    q = tqlib.TensorDesc(fake, tqlib.F16, 1, 2, 1, 128, 2 * 128, 128, 128)
+    for lens in (None, fake + 2):
+        assert lib.tq_decode_attention_lens(ctypes.byref(q), ctypes.byref(cache), ctypes.byref(v), lens, fake, None,
+                                            fake, 1 << 30, None) == tqlib.EINVAL
