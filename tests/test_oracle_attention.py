@@ -90,8 +90,7 @@ def test_kl_nonnegative_and_fisher_limit():
         ds = rng.standard_normal(s.shape) * eps
         kl = me.kl_from_scores(s, s + ds)
         assert np.all(kl >= 0)
-        p = np.exp(s - at.logsumexp(s)[:, None])
-        fisher = 0.5 * (np.sum(p * ds ** 2, axis=1) - np.sum(p * ds, axis=1) ** 2)
+        fisher = me.fisher_score_error(s, s + ds)
         ratio = kl / fisher
         assert np.all(np.abs(ratio - 1) < 3 * eps + 1e-6)
     # A constant shift is softmax-null.
@@ -157,3 +156,76 @@ def test_pca_basis_matches_dominant_subspace():
     assert np.all(np.diff(lam) <= 0)
     for j in range(r):
         assert U[np.argmax(np.abs(U[:, j])), j] > 0
+
+
+def test_fisher_score_error_closed_forms():
+    """Two tokens with p = (a, 1-a) and errors (x, y): Var_p = a (1-a) (x-y)^2.
+    A common shift of all score errors changes nothing; a constant error
+    gives zero.  The KL limit is pinned in test_kl_nonnegative_and_fisher_limit."""
+    a, x, y = 0.3, 0.7, -0.2
+    s = np.log(np.array([[a, 1 - a]]))
+    f = me.fisher_score_error(s, s + np.array([[x, y]]))
+    assert abs(f[0] - 0.5 * a * (1 - a) * (x - y) ** 2) < 1e-15
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal((4, 50))
+    ds = rng.standard_normal((4, 50)) * 0.1
+    assert np.allclose(me.fisher_score_error(s, s + ds), me.fisher_score_error(s, s + ds + 2.5), atol=1e-15)
+    assert np.allclose(me.fisher_score_error(s, s + 4.0), 0.0, atol=1e-15)
+    # Adding one vector to every key is softmax-null ([P3] section 2.1): zero Fisher error.
+    K, V, Q = _data()
+    mu = rng.standard_normal(K.shape[1])
+    _, _, s1, _ = at.attend(Q, K, V)
+    _, _, s2, _ = at.attend(Q, K + mu, V)
+    assert np.allclose(me.fisher_score_error(s1, s2), 0.0, atol=1e-12)
+
+
+def test_spearman_textbook_values():
+    """Ranks (1..5) against (2, 1, 4, 3, 5): rho = 1 - 6 sum d^2 / (n (n^2 - 1))
+    = 1 - 24/120 = 0.8.  Ties: a = (1, 2, 2, 3), b = (1, 2, 3, 4) has average
+    ranks (1, 2.5, 2.5, 4) and rho = 3 / sqrt(10).  Monotone maps give +-1."""
+    assert abs(me.spearman([1, 2, 3, 4, 5], [2, 1, 4, 3, 5]) - 0.8) < 1e-15
+    assert abs(me.spearman([1, 2, 2, 3], [1, 2, 3, 4]) - 3 / np.sqrt(10)) < 1e-15
+    x = np.random.default_rng(4).standard_normal(40)
+    assert abs(me.spearman(x, np.exp(3 * x)) - 1) < 1e-15
+    assert abs(me.spearman(x, -x ** 3) + 1) < 1e-15
+    assert list(me.average_ranks([3.0, 1.0, 3.0, 2.0])) == [3.5, 1.0, 3.5, 2.0]
+    assert np.isnan(me.spearman([1, 1, 1], [1, 2, 3]))
+
+
+def test_snr_and_angle_closed_forms():
+    """x = 1 in R^4 (10 vectors), noise of norm 0.1 per vector: sum ||x||^2 = 40,
+    sum ||e||^2 = 0.1, SNR = 10 log10(400).  SNR = -10 log10(relMSE).  A vector
+    turned by theta in a plane and rescaled has angle theta."""
+    X = np.ones((10, 4))
+    E = np.zeros((10, 4))
+    E[:, 1] = 0.1
+    assert abs(me.snr_db(X, X + E) - 10 * np.log10(400)) < 1e-12
+    rng = np.random.default_rng(6)
+    Y, Yh = rng.standard_normal((30, 8)), rng.standard_normal((30, 8))
+    assert abs(me.snr_db(Y, Yh) + 10 * np.log10(me.rel_mse(Y, Yh))) < 1e-12
+    th = np.array([0.1, 0.5, 1.0, 2.0, np.pi])
+    U = np.stack([np.cos(th), np.sin(th), np.zeros_like(th)], axis=1) * np.array([[3.0], [1.0], [0.5], [2.0], [1.0]])
+    Xr = np.tile([1.0, 0.0, 0.0], (5, 1))
+    assert abs(me.direction_angle(Xr, U) - th.mean()) < 1e-12
+    # Zero vectors are left out.
+    assert abs(me.direction_angle(np.vstack([Xr, np.zeros(3)]), np.vstack([U, np.ones(3)])) - th.mean()) < 1e-12
+
+
+def test_a2_value_distortion_is_the_output_error_of_independent_value_errors():
+    """[P3] section 2.2: with independent zero-mean value errors,
+    E ||sum_j p_j dv_j||^2 = sum_j p_j^2 E ||dv_j||^2 (Monte Carlo, 40000
+    draws, 1 % tolerance); a one-hot p reads exactly ||dv||^2 of its token."""
+    rng = np.random.default_rng(7)
+    T, d = 12, 5
+    p = rng.dirichlet(np.ones(T))[None, :]
+    sig = rng.uniform(0.2, 1.5, T)
+    V = rng.standard_normal((T, d))
+    expected = me.a2_value_distortion(p, V, V + sig[:, None] / np.sqrt(d) * np.ones((T, d)))[0]
+    # E ||dv_j||^2 = sig_j^2 for dv_j ~ N(0, sig_j^2 / d I_d); the fixed draw above has the same norm.
+    dv = rng.standard_normal((40000, T, d)) * (sig[None, :, None] / np.sqrt(d))
+    mc = np.mean(np.sum(np.einsum("t,ntd->nd", p[0], dv) ** 2, axis=1))
+    assert abs(mc - expected) < 0.01 * expected
+    oh = np.zeros((1, T))
+    oh[0, 4] = 1.0
+    Vh = V + rng.standard_normal((T, d))
+    assert abs(me.a2_value_distortion(oh, V, Vh)[0] - np.sum((Vh[4] - V[4]) ** 2)) < 1e-12
