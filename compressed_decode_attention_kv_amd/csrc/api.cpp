@@ -428,6 +428,130 @@ void fill_scoring(const tq_tensor_desc* q, const tq_packed* k, const DecodePlan&
   dp->part = reinterpret_cast<float*>(ws + pl.off_part);
 }
 
+// Workspace of tq_metrics: the scoring plan (query prep), the score rows,
+// the per-query measures; with packed values also the per-vector value
+// errors, a decode workspace and the two output sets of the output site; the
+// per-block sums of the reconstruction-error pass.
+struct MetricsLayout {
+  bool site = false;
+  DecodePlan pl{}, dpl{};
+  size_t nq = 0, off_s = 0, off_perq = 0, off_verr = 0, off_dec = 0, off_o = 0, off_blk = 0, bytes = 0;
+};
+
+tq_status metrics_layout(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v, MetricsLayout* m) {
+  size_t off = 0;
+  if (q) {
+    if (!k) return fail(TQ_EINVAL, "KL/top-5 need the packed keys");
+    if (tq_status s = plan_decode(k, nullptr, q->H, true, &m->pl)) return s;
+    m->nq = (size_t)k->B * q->H;
+    off = m->pl.bytes;
+    m->off_s = off;    off = round_up(off + 2 * m->nq * k->T * 4, 256);
+    m->off_perq = off; off = round_up(off + m->nq * kPerQuery * 8, 256);
+    if (v) {
+      if (tq_status s = plan_decode(k, v, q->H, false, &m->dpl)) return s;
+      m->site = true;
+      m->off_verr = off; off = round_up(off + (size_t)v->B * v->H * v->T_cap * 4, 256);
+      m->off_dec = off;  off = round_up(off + m->dpl.bytes, 256);
+      m->off_o = off;    off = round_up(off + 2 * m->nq * k->d * 4, 256);
+    }
+  }
+  size_t nb = 0;
+  for (const tq_packed* p : {k, v}) {
+    if (!p) continue;
+    if (tq_status s = check_packed(p, "packed")) return s;
+    nb = std::max(nb, (size_t)relerr_blocks(p->T, p->d / 32, p->B * p->H));
+  }
+  m->off_blk = off;
+  off = round_up(off + nb * 5 * 8, 256);
+  m->bytes = off;
+  return TQ_OK;
+}
+
+double snr_db(double signal2, double noise2) {
+  if (!(signal2 > 0)) return NAN;
+  return noise2 > 0 ? 10.0 * std::log10(signal2 / noise2) : INFINITY;
+}
+
+// Spearman rank correlation: Pearson correlation of the ranks, ties at the
+// mean of their ranks; NaN when a sample is constant.
+double spearman(const std::vector<double>& a, const std::vector<double>& b) {
+  auto ranks = [](const std::vector<double>& x) {
+    const size_t n = x.size();
+    std::vector<size_t> order(n);
+    for (size_t i = 0; i < n; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](size_t i, size_t j) { return x[i] < x[j]; });
+    std::vector<double> r(n);
+    for (size_t i = 0; i < n;) {
+      size_t j = i;
+      while (j + 1 < n && x[order[j + 1]] == x[order[i]]) ++j;
+      for (size_t t = i; t <= j; ++t) r[order[t]] = 0.5 * (double)(i + j) + 1.0;
+      i = j + 1;
+    }
+    return r;
+  };
+  if (a.size() != b.size() || a.size() < 2) return NAN;
+  for (double x : a) if (!std::isfinite(x)) return NAN;
+  for (double x : b) if (!std::isfinite(x)) return NAN;
+  std::vector<double> ra = ranks(a), rb = ranks(b);
+  const double n = (double)a.size(), mean = 0.5 * (n + 1.0);
+  double sab = 0, saa = 0, sbb = 0;
+  for (size_t i = 0; i < a.size(); ++i) {
+    const double x = ra[i] - mean, y = rb[i] - mean;
+    sab += x * y; saa += x * x; sbb += y * y;
+  }
+  return (saa > 0 && sbb > 0) ? sab / std::sqrt(saa * sbb) : NAN;
+}
+
+// Reconstruction error of a packed tensor against its raw input: pooled
+// relMSE, mean 1 - cos, SNR (dB), mean angle, and the squared error summed
+// per (b, h); per_vec (optional) receives ||x_hat - x||^2 of every vector.
+struct RelErrOut {
+  double rel = NAN, dir = NAN, snr = NAN, phi = NAN;
+  std::vector<double> head_e2;
+};
+
+tq_status relerr(const tq_tensor_desc* x, const tq_packed* pk, double* blk, float* per_vec, hipStream_t st,
+                 RelErrOut* o) {
+  if (tq_status s = check_tensor(x, "reference")) return s;
+  if (x->B != pk->B || x->H != pk->H || x->T != pk->T || x->d != pk->d)
+    return fail(TQ_EMISMATCH, "reference tensor shape differs from the packed tensor");
+  RelErrParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = x->data; p.dtype = x->dtype; p.B = x->B; p.H = x->H; p.T = x->T; p.T_cap = pk->T_cap; p.d = x->d; p.L = x->d / 32;
+  p.sb = x->stride_b; p.sh = x->stride_h; p.st = x->stride_t;
+  p.mode = pk->mode; p.bits = pk->bits; p.rotate = pk->mode != TQ_MODE_PLAIN;
+  p.kqjl = pk->mode == TQ_MODE_PROD; p.kside = pk->mode == TQ_MODE_HEADQ;
+  p.rank = pk->side_rank; p.side_bits = pk->side_bits;
+  float bnd[16];
+  if (tq_status s = fill_codebook(pk->d, pk->bits, p.centroids, bnd)) return s;
+  fill_signbits(pk->seed, pk->d, p.signbits);
+  p.inv_sqrt_d = 1.0f / std::sqrt((float)pk->d);
+  p.qjl_c = (float)(std::sqrt(M_PI / 2.0) / pk->d);
+  if (p.kqjl) { if (tq_status s = sketch_on_device(pk->seed, pk->d, &p.S)) return s; }
+  p.basis = pk->basis;
+  p.planes = {pk->codes, pk->norms, pk->qjl, pk->gamma, pk->side, pk->side_scale};
+  p.block_sums = blk;
+  p.per_vec = per_vec;
+  const int BH = pk->B * pk->H;
+  const int nb = relerr_blocks(pk->T, pk->d / 32, BH);
+  if (tq_status s = hip_status(launch_relerr(p, nb, st), "relerr launch")) return s;
+  std::vector<double> host((size_t)nb * 5);
+  if (tq_status s = hip_status(hipMemcpyAsync(host.data(), blk, host.size() * 8, hipMemcpyDeviceToHost, st), "copy")) return s;
+  if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
+  double e2 = 0, r2 = 0, ds = 0, cnt = 0, as = 0;
+  o->head_e2.assign(BH, 0.0);
+  const int gx = nb / BH;  // blocks per (b, h): block index = bh * gx + x
+  for (int b = 0; b < nb; ++b) {
+    e2 += host[b * 5]; r2 += host[b * 5 + 1]; ds += host[b * 5 + 2]; cnt += host[b * 5 + 3]; as += host[b * 5 + 4];
+    o->head_e2[b / gx] += host[b * 5];
+  }
+  o->rel = r2 > 0 ? e2 / r2 : NAN;
+  o->dir = cnt > 0 ? ds / cnt : NAN;
+  o->phi = cnt > 0 ? as / cnt : NAN;
+  o->snr = snr_db(r2, e2);
+  return TQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -671,63 +795,20 @@ extern "C" {
 
 tq_status tq_metrics_workspace_size(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v, size_t* bytes) {
   if (!bytes) return fail(TQ_EINVAL, "output pointer is NULL");
-  size_t need = 0;
-  if (q) {
-    if (!k) return fail(TQ_EINVAL, "KL/top-5 need the packed keys");
-    DecodePlan pl;
-    if (tq_status s = plan_decode(k, nullptr, q->H, true, &pl)) return s;
-    const size_t nq = (size_t)k->B * q->H;
-    need = pl.bytes + round_up(2 * nq * k->T * 4, 256) + round_up(nq * 2 * 8, 256);
-  }
-  for (const tq_packed* p : {k, v}) {
-    if (!p) continue;
-    if (tq_status s = check_packed(p, "packed")) return s;
-    need = std::max(need, round_up((size_t)relerr_blocks(p->T, p->d / 32, p->B * p->H) * 4 * 8, 256));
-  }
-  *bytes = need;
+  MetricsLayout m;
+  if (tq_status s = metrics_layout(q, k, v, &m)) return s;
+  *bytes = m.bytes;
   return ok();
-}
-
-static tq_status relerr(const tq_tensor_desc* x, const tq_packed* pk, char* ws, hipStream_t st, double* rel, double* dir) {
-  if (tq_status s = check_tensor(x, "reference")) return s;
-  if (x->B != pk->B || x->H != pk->H || x->T != pk->T || x->d != pk->d)
-    return fail(TQ_EMISMATCH, "reference tensor shape differs from the packed tensor");
-  RelErrParams p;
-  std::memset(&p, 0, sizeof(p));
-  p.x = x->data; p.dtype = x->dtype; p.B = x->B; p.H = x->H; p.T = x->T; p.T_cap = pk->T_cap; p.d = x->d; p.L = x->d / 32;
-  p.sb = x->stride_b; p.sh = x->stride_h; p.st = x->stride_t;
-  p.mode = pk->mode; p.bits = pk->bits; p.rotate = pk->mode != TQ_MODE_PLAIN;
-  p.kqjl = pk->mode == TQ_MODE_PROD; p.kside = pk->mode == TQ_MODE_HEADQ;
-  p.rank = pk->side_rank; p.side_bits = pk->side_bits;
-  float bnd[16];
-  if (tq_status s = fill_codebook(pk->d, pk->bits, p.centroids, bnd)) return s;
-  fill_signbits(pk->seed, pk->d, p.signbits);
-  p.inv_sqrt_d = 1.0f / std::sqrt((float)pk->d);
-  p.qjl_c = (float)(std::sqrt(M_PI / 2.0) / pk->d);
-  if (p.kqjl) { if (tq_status s = sketch_on_device(pk->seed, pk->d, &p.S)) return s; }
-  p.basis = pk->basis;
-  p.planes = {pk->codes, pk->norms, pk->qjl, pk->gamma, pk->side, pk->side_scale};
-  const int nb = relerr_blocks(pk->T, pk->d / 32, pk->B * pk->H);
-  p.block_sums = reinterpret_cast<double*>(ws);
-  if (tq_status s = hip_status(launch_relerr(p, nb, st), "relerr launch")) return s;
-  std::vector<double> host((size_t)nb * 4);
-  if (tq_status s = hip_status(hipMemcpyAsync(host.data(), ws, host.size() * 8, hipMemcpyDeviceToHost, st), "copy")) return s;
-  if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
-  double e2 = 0, r2 = 0, ds = 0, cnt = 0;
-  for (int b = 0; b < nb; ++b) { e2 += host[b * 4]; r2 += host[b * 4 + 1]; ds += host[b * 4 + 2]; cnt += host[b * 4 + 3]; }
-  *rel = r2 > 0 ? e2 / r2 : NAN;
-  *dir = cnt > 0 ? ds / cnt : NAN;
-  return TQ_OK;
 }
 
 tq_status tq_metrics(const tq_tensor_desc* q, const tq_tensor_desc* k_ref, const tq_tensor_desc* v_ref,
                      const tq_packed* k, const tq_packed* v, tq_metrics_out* out, void* ws, size_t ws_bytes,
                      void* stream) {
   if (!out) return fail(TQ_EINVAL, "output pointer is NULL");
-  size_t need = 0;
-  if (tq_status s = tq_metrics_workspace_size(q, k, v, &need)) return s;
+  MetricsLayout m;
+  if (tq_status s = metrics_layout(q, k, v, &m)) return s;
   if (!ws || !aligned(ws, 256)) return fail(TQ_EINVAL, "workspace NULL or not 256-byte aligned");
-  if (ws_bytes < need) return fail(TQ_ENOMEM, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if (ws_bytes < m.bytes) return fail(TQ_ENOMEM, "workspace %zu bytes < required %zu", ws_bytes, m.bytes);
   if (q && !k_ref) return fail(TQ_EINVAL, "KL/top-5 need the raw keys");
   if ((k_ref && !k) || (v_ref && !v)) return fail(TQ_EINVAL, "a reference tensor was given without its packed tensor");
   if (q) {
@@ -737,22 +818,39 @@ tq_status tq_metrics(const tq_tensor_desc* q, const tq_tensor_desc* k_ref, const
       return fail(TQ_EMISMATCH, "k_ref shape differs from the packed keys");
   }
   if (v_ref) { if (tq_status s = check_tensor(v_ref, "v_ref")) return s; }
-  out->kl_mean = out->kl_max = out->top5_recall = NAN;
-  out->relmse_k = out->relmse_v = out->dir_err_k = out->dir_err_v = NAN;
+  const double nan = NAN;
+  out->kl_mean = out->kl_max = out->top5_recall = nan;
+  out->relmse_k = out->relmse_v = out->dir_err_k = out->dir_err_v = nan;
+  out->fisher_mean = out->fisher_max = out->spearman_fisher_kl = out->spearman_keymse_kl = nan;
+  out->snr_k_db = out->snr_v_db = out->snr_out_db = nan;
+  out->phi_k = out->phi_v = out->phi_out = nan;
+  out->a2_value_mean = nan;
   out->n_queries = 0;
   char* w = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
+  double* blk = reinterpret_cast<double*>(w + m.off_blk);
+  // Output site and A^2 measure: queries, both raw tensors and the packed values.
+  const bool site = q && m.site && v_ref;
+  float* verr = site ? reinterpret_cast<float*>(w + m.off_verr) : nullptr;
+
+  // 1. Values first: their per-vector errors feed the A^2 measure.
+  RelErrOut ev, ek;
+  if (v_ref && v) { if (tq_status s = relerr(v_ref, v, blk, verr, st, &ev)) return s; }
+
+  // 2. Score rows and the per-query measures.
+  double* perq = nullptr;
+  float* o_hat = nullptr;
+  float* o_ref = nullptr;
+  const size_t nq = m.nq;
   if (q) {
-    DecodePlan pl;
-    if (tq_status s = plan_decode(k, nullptr, q->H, true, &pl)) return s;
+    const DecodePlan& pl = m.pl;
     if (!key_supported(k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ))
       return fail(TQ_EUNSUPPORTED, "no scoring kernel for key mode %d with %d bits", k->mode, k->bits);
     const float* Sk = nullptr;
     if (k->mode == TQ_MODE_PROD) { if (tq_status s = sketch_on_device(k->seed, k->d, &Sk)) return s; }
-    const size_t nq = (size_t)k->B * q->H;
-    float* s_ref = reinterpret_cast<float*>(w + pl.bytes);
+    float* s_ref = reinterpret_cast<float*>(w + m.off_s);
     float* s_hat = s_ref + nq * k->T;
-    double* perq = reinterpret_cast<double*>(w + pl.bytes + round_up(2 * nq * k->T * 4, 256));
+    perq = reinterpret_cast<double*>(w + m.off_perq);
     QPrepParams qp;
     fill_qprep(q, k, Sk, w, pl, true, &qp);
     MetricScoreParams mp;
@@ -762,22 +860,86 @@ tq_status tq_metrics(const tq_tensor_desc* q, const tq_tensor_desc* k_ref, const
     mp.ksb = k_ref->stride_b; mp.ksh = k_ref->stride_h; mp.kst = k_ref->stride_t;
     mp.qraw = reinterpret_cast<const float*>(w + pl.off_qraw);
     mp.s_ref = s_ref; mp.s_hat = s_hat;
-    MetricReduceParams rp{(int)nq, k->T, s_ref, s_hat, perq};
+    MetricReduceParams rp;
+    std::memset(&rp, 0, sizeof(rp));
+    rp.nq = (int)nq; rp.T = k->T; rp.s_ref = s_ref; rp.s_hat = s_hat; rp.per_query = perq;
+    rp.verr = verr; rp.Hq = q->H; rp.G = pl.G; rp.Hkv = k->H; rp.T_cap = v ? v->T_cap : 0;
     bool supported = true;
     if (tq_status s = hip_status(launch_qprep(qp, st), "query prep launch")) return s;
     if (tq_status s = hip_status(launch_metric_scores(mp, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, st, &supported), "score launch")) return s;
     if (!supported) return fail(TQ_EUNSUPPORTED, "key mode has no scoring kernel");
     if (tq_status s = hip_status(launch_metric_reduce(rp, st), "reduce launch")) return s;
-    std::vector<double> host(nq * 2);
+
+    // 3. Output site: exact attention over the raw values against the decode.
+    if (site) {
+      if (v_ref->B != v->B || v_ref->H != v->H || v_ref->T != v->T || v_ref->d != v->d)
+        return fail(TQ_EMISMATCH, "v_ref shape differs from the packed values");
+      o_hat = reinterpret_cast<float*>(w + m.off_o);
+      o_ref = o_hat + nq * k->d;
+      if (tq_status s = decode_core(q, k, v, nullptr, o_hat, nullptr, w + m.off_dec, m.dpl.bytes, stream)) return s;
+      AttnRefParams ap;
+      std::memset(&ap, 0, sizeof(ap));
+      ap.nq = (int)nq; ap.T = k->T; ap.d = k->d; ap.Hq = q->H; ap.G = pl.G; ap.Hkv = k->H;
+      ap.s_ref = s_ref; ap.per_query = perq;
+      ap.v = v_ref->data; ap.vdtype = v_ref->dtype;
+      ap.vsb = v_ref->stride_b; ap.vsh = v_ref->stride_h; ap.vst = v_ref->stride_t;
+      ap.o_ref = o_ref;
+      if (tq_status s = hip_status(launch_attn_ref(ap, st), "reference attention launch")) return s;
+    }
+  }
+
+  // 4. Keys.
+  if (k_ref && k) { if (tq_status s = relerr(k_ref, k, blk, nullptr, st, &ek)) return s; }
+
+  // 5. Host side: per-query statistics, rank correlations and the output site.
+  out->relmse_k = ek.rel; out->dir_err_k = ek.dir; out->snr_k_db = ek.snr; out->phi_k = ek.phi;
+  out->relmse_v = ev.rel; out->dir_err_v = ev.dir; out->snr_v_db = ev.snr; out->phi_v = ev.phi;
+  if (q) {
+    std::vector<double> host(nq * kPerQuery);
     if (tq_status s = hip_status(hipMemcpyAsync(host.data(), perq, host.size() * 8, hipMemcpyDeviceToHost, st), "copy")) return s;
+    std::vector<float> oh, orf;
+    if (site) {
+      oh.resize(nq * k->d);
+      orf.resize(nq * k->d);
+      if (tq_status s = hip_status(hipMemcpyAsync(oh.data(), o_hat, oh.size() * 4, hipMemcpyDeviceToHost, st), "copy")) return s;
+      if (tq_status s = hip_status(hipMemcpyAsync(orf.data(), o_ref, orf.size() * 4, hipMemcpyDeviceToHost, st), "copy")) return s;
+    }
     if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
-    double klsum = 0, klmax = -INFINITY, rec = 0;
-    for (size_t i = 0; i < nq; ++i) { klsum += host[2 * i]; klmax = std::max(klmax, host[2 * i]); rec += host[2 * i + 1]; }
+    std::vector<double> kl(nq), fisher(nq), kmse(nq);
+    double klsum = 0, klmax = -INFINITY, rec = 0, fsum = 0, fmax = -INFINITY, a2sum = 0;
+    for (size_t i = 0; i < nq; ++i) {
+      const double* r = &host[i * kPerQuery];
+      kl[i] = r[0]; fisher[i] = r[2];
+      klsum += r[0]; klmax = std::max(klmax, r[0]); rec += r[1];
+      fsum += r[2]; fmax = std::max(fmax, r[2]); a2sum += r[3];
+      const int b = (int)(i / q->H), kvh = (int)(i % q->H) / m.pl.G;
+      kmse[i] = ek.head_e2.empty() ? nan : ek.head_e2[(size_t)b * k->H + kvh] / k->T;
+    }
     out->kl_mean = klsum / nq; out->kl_max = klmax; out->top5_recall = rec / nq;
+    out->fisher_mean = fsum / nq; out->fisher_max = fmax;
+    out->spearman_fisher_kl = spearman(fisher, kl);
+    out->spearman_keymse_kl = ek.head_e2.empty() ? nan : spearman(kmse, kl);
+    if (site) {
+      out->a2_value_mean = a2sum / nq;
+      double s2 = 0, e2 = 0, asum = 0, cnt = 0;
+      const int d = k->d;
+      for (size_t i = 0; i < nq; ++i) {
+        double r2 = 0, h2 = 0, dot = 0, de = 0;
+        for (int c = 0; c < d; ++c) {
+          const double a = orf[i * d + c], h = oh[i * d + c];
+          r2 += a * a; h2 += h * h; dot += a * h; de += (a - h) * (a - h);
+        }
+        s2 += r2; e2 += de;
+        if (r2 > 0 && h2 > 0) {
+          asum += std::acos(std::min(1.0, std::max(-1.0, dot / std::sqrt(r2 * h2))));
+          cnt += 1;
+        }
+      }
+      out->snr_out_db = snr_db(s2, e2);
+      out->phi_out = cnt > 0 ? asum / cnt : nan;
+    }
     out->n_queries = (int64_t)nq;
   }
-  if (k_ref && k) { if (tq_status s = relerr(k_ref, k, w, st, &out->relmse_k, &out->dir_err_k)) return s; }
-  if (v_ref && v) { if (tq_status s = relerr(v_ref, v, w, st, &out->relmse_v, &out->dir_err_v)) return s; }
   if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
   return ok();
 }

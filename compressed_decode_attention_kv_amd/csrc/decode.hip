@@ -434,6 +434,25 @@ __global__ __launch_bounds__(kThreads) void metric_reduce_kernel(MetricReducePar
   zh = block_reduce(zh, false);
   cross = block_reduce(cross, false);
   const double kl = cross / zr - (mr + log(zr)) + (mh + log(zh));
+  // Fisher score error 1/2 Var_p(s_hat - s_ref), two passes (mean, then
+  // spread), and the A^2 value distortion sum_j p_j^2 ||v_hat_j - v_j||^2.
+  const int b = qi / p.Hq, kvh = (qi % p.Hq) / p.G;
+  const float* verr = p.verr ? p.verr + ((size_t)b * p.Hkv + kvh) * p.T_cap : nullptr;
+  double m1 = 0.0, a2 = 0.0;
+  for (int t = tid; t < T; t += kThreads) {
+    const double pt = exp((double)sr[t] - mr) / zr;
+    m1 += pt * ((double)sh[t] - (double)sr[t]);
+    if (verr) a2 += pt * pt * (double)verr[t];
+  }
+  m1 = block_reduce(m1, false);
+  a2 = block_reduce(a2, false);
+  double var = 0.0;
+  for (int t = tid; t < T; t += kThreads) {
+    const double pt = exp((double)sr[t] - mr) / zr;
+    const double dv = (double)sh[t] - (double)sr[t] - m1;
+    var += pt * dv * dv;
+  }
+  var = block_reduce(var, false);
   // top-5 of each score row
   int hits = 0;
   for (int pass = 0; pass < 2; ++pass) {
@@ -463,8 +482,44 @@ __global__ __launch_bounds__(kThreads) void metric_reduce_kernel(MetricReducePar
     __syncthreads();
   }
   if (tid == 0) {
-    p.per_query[(size_t)qi * 2] = kl;
-    p.per_query[(size_t)qi * 2 + 1] = (double)hits / 5.0;
+    double* o = p.per_query + (size_t)qi * kPerQuery;
+    o[0] = kl;
+    o[1] = (double)hits / 5.0;
+    o[2] = 0.5 * var;
+    o[3] = verr ? a2 : NAN;
+    o[4] = mr + log(zr);
+  }
+}
+
+// o_ref = sum_t p_t v_t over the raw values, p_t = exp(s_ref_t - lse_ref):
+// one block per query, wave w takes tokens t = w mod 4, lane i coordinates
+// i, i + 64, ...; the four waves' sums meet in LDS.
+template <typename TIN>
+__global__ __launch_bounds__(kThreads) void attn_ref_kernel(AttnRefParams p) {
+  __shared__ float s_acc[kThreads / 64][kMaxD];
+  const int qi = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = qi / p.Hq, kvh = (qi % p.Hq) / p.G, d = p.d;
+  const float* sr = p.s_ref + (size_t)qi * p.T;
+  const double lse = p.per_query[(size_t)qi * kPerQuery + 4];
+  const TIN* v = reinterpret_cast<const TIN*>(p.v) + (int64_t)b * p.vsb + (int64_t)kvh * p.vsh;
+  float acc[kMaxD / 64];
+#pragma unroll
+  for (int c = 0; c < kMaxD / 64; ++c) acc[c] = 0.f;
+  for (int t = wave; t < p.T; t += kThreads / 64) {
+    const float pt = (float)exp((double)sr[t] - lse);
+    const TIN* row = v + (int64_t)t * p.vst;
+#pragma unroll
+    for (int c = 0; c < kMaxD / 64; ++c)
+      if (64 * c + lane < d) acc[c] = fmaf(pt, (float)row[64 * c + lane], acc[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < kMaxD / 64; ++c)
+    if (64 * c + lane < d) s_acc[wave][64 * c + lane] = acc[c];
+  __syncthreads();
+  for (int i = threadIdx.x; i < d; i += kThreads) {
+    float o = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) o += s_acc[w][i];
+    p.o_ref[(size_t)qi * d + i] = o;
   }
 }
 
@@ -497,6 +552,14 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
 
 hipError_t launch_metric_reduce(const MetricReduceParams& p, hipStream_t s) {
   hipLaunchKernelGGL(metric_reduce_kernel, dim3(p.nq), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_ref(const AttnRefParams& p, hipStream_t s) {
+  if (p.vdtype == TQ_F16)
+    hipLaunchKernelGGL(attn_ref_kernel<_Float16>, dim3(p.nq), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(attn_ref_kernel<float>, dim3(p.nq), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -111,10 +111,26 @@ struct MetricScoreParams {
   float* s_ref; float* s_hat;  // [B*Hq][T]
 };
 
+// Per-query measures from the score rows: KL, top-5 recall, the Fisher
+// score error 1/2 Var_p(s_hat - s_ref), the A^2 value distortion
+// sum_j p_j^2 verr[j] (when verr, per value vector, is given) and the
+// reference log-sum-exp.
+constexpr int kPerQuery = 5;
 struct MetricReduceParams {
   int nq, T;
   const float* s_ref; const float* s_hat;
-  double* per_query;  // [nq][2] = kl, recall
+  double* per_query;  // [nq][kPerQuery] = kl, recall, fisher, a2, lse_ref
+  const float* verr;  // [B*Hkv][T_cap] ||v_hat - v||^2, or NULL
+  int Hq, G, Hkv, T_cap;
+};
+
+// Exact attention output over the raw values: o_ref = sum_j p_j v_j with p
+// from the reference score rows and their log-sum-exp.
+struct AttnRefParams {
+  int nq, T, d, Hq, G, Hkv;
+  const float* s_ref; const double* per_query;
+  const void* v; int vdtype; int64_t vsb, vsh, vst;
+  float* o_ref;       // [nq][d]
 };
 
 struct RelErrParams {
@@ -126,7 +142,8 @@ struct RelErrParams {
   float inv_sqrt_d, qjl_c;
   const float* S; const float* basis;
   TensorPlanes planes;
-  double* block_sums;  // [gridDim][4] = err2, ref2, (1-cos) sum, count
+  double* block_sums;  // [gridDim][5] = err2, ref2, (1-cos) sum, count, angle sum
+  float* per_vec;      // [B*H][T_cap] ||x_hat - x||^2 per vector, or NULL
 };
 
 // ---- launchers (defined in the .hip files) --------------------------------
@@ -154,6 +171,7 @@ hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int vbi
 hipError_t launch_metric_scores(const MetricScoreParams& p, int kbits, int kqjl, int kside, hipStream_t s,
                                 bool* supported);
 hipError_t launch_metric_reduce(const MetricReduceParams& p, hipStream_t s);
+hipError_t launch_attn_ref(const AttnRefParams& p, hipStream_t s);
 hipError_t launch_relerr(const RelErrParams& p, int nblocks, hipStream_t s);
 int stream_read_blocks();
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);

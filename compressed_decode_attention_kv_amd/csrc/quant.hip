@@ -231,7 +231,7 @@ template <int BITS, int MODE, typename TIN>
 __global__ __launch_bounds__(kThreads) void relerr_kernel(RelErrParams p) {
   __shared__ float s_cent[16];
   __shared__ float s_side[MODE == TQ_MODE_HEADQ ? kMaxSideLds : 1];
-  __shared__ double s_red[kThreads / 64][4];
+  __shared__ double s_red[kThreads / 64][5];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int L = p.L, j = lane & (L - 1), slot = lane / L, vpw = 64 / L;
   const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void relerr_kernel(RelErrParams p) {
   const TIN* xbase = reinterpret_cast<const TIN*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh;
   const int64_t vbase = (int64_t)bh * p.T_cap;
   const int tok_per_block = 4 * vpw * kSteps;
-  double e2 = 0.0, r2 = 0.0, dsum = 0.0, cnt = 0.0;
+  double e2 = 0.0, r2 = 0.0, dsum = 0.0, cnt = 0.0, asum = 0.0;
   for (int step = 0; step < kSteps; ++step) {
     const int t = blockIdx.x * tok_per_block + (step * 4 + wave) * vpw + slot;
     const bool valid = t < p.T;
@@ -309,22 +309,28 @@ __global__ __launch_bounds__(kThreads) void relerr_kernel(RelErrParams p) {
     if (valid && j == 0) {
       e2 += le2; r2 += lr2;
       if (lr2 > 0.f && lh2 > 0.f) {
-        dsum += 1.0 - (double)ldot / sqrt((double)lr2 * (double)lh2);
+        const double c = (double)ldot / sqrt((double)lr2 * (double)lh2);
+        dsum += 1.0 - c;
+        asum += acos(fmin(1.0, fmax(-1.0, c)));
         cnt += 1.0;
       }
+      if (p.per_vec) p.per_vec[vec] = le2;
     }
   }
   for (int m = 1; m < 64; m <<= 1) {
     e2 += __shfl_xor(e2, m, 64); r2 += __shfl_xor(r2, m, 64);
     dsum += __shfl_xor(dsum, m, 64); cnt += __shfl_xor(cnt, m, 64);
+    asum += __shfl_xor(asum, m, 64);
   }
-  if (lane == 0) { s_red[wave][0] = e2; s_red[wave][1] = r2; s_red[wave][2] = dsum; s_red[wave][3] = cnt; }
+  if (lane == 0) {
+    s_red[wave][0] = e2; s_red[wave][1] = r2; s_red[wave][2] = dsum; s_red[wave][3] = cnt; s_red[wave][4] = asum;
+  }
   __syncthreads();
-  if (threadIdx.x < 4) {
+  if (threadIdx.x < 5) {
     double s = 0.0;
     for (int w = 0; w < kThreads / 64; ++w) s += s_red[w][threadIdx.x];
     const size_t blk = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
-    p.block_sums[blk * 4 + threadIdx.x] = s;
+    p.block_sums[blk * 5 + threadIdx.x] = s;
   }
 }
 

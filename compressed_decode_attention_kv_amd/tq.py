@@ -58,7 +58,12 @@ class Packed(ctypes.Structure):
 class MetricsOut(ctypes.Structure):
     _fields_ = [("kl_mean", ctypes.c_double), ("kl_max", ctypes.c_double), ("top5_recall", ctypes.c_double),
                 ("relmse_k", ctypes.c_double), ("relmse_v", ctypes.c_double), ("dir_err_k", ctypes.c_double),
-                ("dir_err_v", ctypes.c_double), ("n_queries", ctypes.c_int64)]
+                ("dir_err_v", ctypes.c_double), ("n_queries", ctypes.c_int64),
+                ("fisher_mean", ctypes.c_double), ("fisher_max", ctypes.c_double),
+                ("spearman_fisher_kl", ctypes.c_double), ("spearman_keymse_kl", ctypes.c_double),
+                ("snr_k_db", ctypes.c_double), ("snr_v_db", ctypes.c_double), ("snr_out_db", ctypes.c_double),
+                ("phi_k", ctypes.c_double), ("phi_v", ctypes.c_double), ("phi_out", ctypes.c_double),
+                ("a2_value_mean", ctypes.c_double)]
 
 
 _P = ctypes.POINTER

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -143,6 +143,29 @@ typedef struct tq_metrics_out {
   double kl_mean, kl_max, top5_recall;
   double relmse_k, relmse_v, dir_err_k, dir_err_v;
   int64_t n_queries;
+  /* Score space ([P3] section 2.1, Eq. 6: KL is locally a Fisher-weighted
+   * variance of the score errors): per query 1/2 Var_p(s_hat - s), p the
+   * reference softmax, s in natural units (q^T k / sqrt(d)); mean and max
+   * over queries.  Needs q. */
+  double fisher_mean, fisher_max;
+  /* Spearman rank correlation (ties at their average rank) across the
+   * queries of this call between KL and the Fisher score error, and between
+   * KL and the raw key MSE of the query's KV head (mean ||k_hat - k||^2 over
+   * its tokens) ([P3] section 4: score-space error predicts KL better than
+   * raw key MSE).  Need q; NaN when a sample is constant. */
+  double spearman_fisher_kl, spearman_keymse_kl;
+  /* 6D error framework ([P1] "Métricas de Evaluación"): scale and direction
+   * at the key cache, the value cache and the attention output.  SNR in dB,
+   * pooled: 10 log10(sum ||x||^2 / sum ||x - x_hat||^2); phi: mean angle in
+   * radians between x and x_hat over vectors with non-zero norms.  Output
+   * site: the exact attention over the raw K, V against tq_decode_attention
+   * over the packed cache; needs q, k_ref, v_ref and v. */
+  double snr_k_db, snr_v_db, snr_out_db;
+  double phi_k, phi_v, phi_out;
+  /* A^2-weighted value distortion ([P3] section 2.2): per query
+   * sum_j p_j^2 ||v_hat_j - v_j||^2, mean over queries; needs q, k_ref, v_ref
+   * and v. */
+  double a2_value_mean;
 } tq_metrics_out;
 
 int32_t tq_abi_version(void);

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(tqlib):
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(tqlib.EXPORTS) == names
-    assert tqlib.lib().tq_abi_version() == 1
+    assert tqlib.lib().tq_abi_version() == 2
 
 
 @pytest.mark.parametrize("d,bits", [(32, 1), (128, 2), (128, 3), (128, 4), (1024, 2), (1024, 4)])
