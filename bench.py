@@ -95,6 +95,88 @@ def cpu_baseline(scheme, budget_s=12.0):
                       % (slices, scheme, done / t_quant)}
 
 
+def _median_ms(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return ms[len(ms) // 2]
+
+
+def other_workload(args):
+    """The pages' other regimes at full size (not the headline): one JSON
+    line with the median quantize / decode time per scheme."""
+    import numpy as np
+    import torch
+    from compressed_decode_attention_kv_amd import synth, tq
+
+    torch.cuda.set_device(0)
+    rows = []
+
+    def packed_bytes(p):
+        return sum(t.numel() for t in (p.codes, p.norms, p.qjl, p.gamma, p.side, p.side_scale) if t is not None)
+
+    if args.workload == "heavy-tailed":
+        B, H, T, d = 4, 8, 131072, 128
+        K, V = synth.device_heavy_tailed(B, H, T, d, seed=33)
+        in_bytes = 2 * K.numel() * 4
+        for scheme in ("kv", "tq-kv", "tq-qkv"):
+            for n in (2, 3):
+                ps = []
+
+                def quant():
+                    ps[:] = [tq.quantize(K, tq.KEYS, scheme, n, 0), tq.quantize(V, tq.VALUES, scheme, n, 0)]
+                q_ms = _median_ms(torch, quant, args.steps, args.warmup)
+                moved = in_bytes + sum(packed_bytes(p) for p in ps)
+                rows.append({"scheme": scheme, "n_bits": n, "quantize_ms": round(q_ms, 4),
+                             "quantize_tok_per_s": round(B * T / (q_ms * 1e-3), 1),
+                             "quantize_hbm_GBps": round(moved / (q_ms * 1e-3) / 1e9, 1)})
+        cfg = "heavy-tailed: B=4 H=8 T=131072 d=128 fp32 Student-t(3) + 1% outlier tokens; quantize only"
+    elif args.workload == "low-rank":
+        K, V, Q = synth.low_rank(4, 65536, 1024, 16, seed=40)
+        K, V, Q = (torch.from_numpy(x).cuda() for x in (K, V, Q))
+        for scheme in ("kqv", "qkqv"):
+            kp = tq.quantize(K, tq.KEYS, scheme, 4, 3)
+            vp = tq.quantize(V, tq.VALUES, scheme, 4, 3)
+            q_ms = _median_ms(torch, lambda: (tq.quantize(K, tq.KEYS, scheme, 4, 3),
+                                              tq.quantize(V, tq.VALUES, scheme, 4, 3)), args.steps, args.warmup)
+            out, lse = tq.decode_attention(Q, kp, vp)
+            ws = torch.empty(tq.decode_workspace_size(kp, vp, Q.shape[1]), dtype=torch.uint8, device="cuda")
+            d_ms = _median_ms(torch, lambda: tq.decode_attention(Q, kp, vp, out, lse, ws), args.steps, args.warmup)
+            nb = packed_bytes(kp) + packed_bytes(vp)
+            rows.append({"scheme": scheme, "n_bits": 4, "quantize_ms": round(q_ms, 4), "decode_ms": round(d_ms, 4),
+                         "decode_GBps": round(nb / (d_ms * 1e-3) / 1e9, 1), "queries": int(Q.shape[1])})
+        cfg = "low-rank: H=4 T=65536 d=1024 fp32, K rank 16 (0.7^i) + 0.01 noise, 16 queries per head"
+    else:  # headq-gqa
+        B, Hkv, G, T, d, r = 8, 8, 4, 131072, 128, 16
+        K, V, Q, C = synth.device_rope_gqa(B, Hkv, G, T, d, seed=55)
+        U = np.stack([tq.headq_fit(C[h], r) for h in range(Hkv)])
+        basis = torch.from_numpy(np.ascontiguousarray(U)).cuda()
+        for scheme in ("headq", "tq-kv"):
+            bas = basis if scheme == "headq" else None
+            kp = tq.quantize(K, tq.KEYS, scheme, 4, 13, basis=bas)
+            vp = tq.quantize(V, tq.VALUES, scheme, 4, 13)
+            q_ms = _median_ms(torch, lambda: (tq.quantize(K, tq.KEYS, scheme, 4, 13, basis=bas),
+                                              tq.quantize(V, tq.VALUES, scheme, 4, 13)), args.steps, args.warmup)
+            out, lse = tq.decode_attention(Q, kp, vp)
+            ws = torch.empty(tq.decode_workspace_size(kp, vp, Q.shape[1]), dtype=torch.uint8, device="cuda")
+            d_ms = _median_ms(torch, lambda: tq.decode_attention(Q, kp, vp, out, lse, ws), args.steps, args.warmup)
+            nb = packed_bytes(kp) + packed_bytes(vp)
+            rows.append({"scheme": scheme, "n_bits": 4, "quantize_ms": round(q_ms, 4), "decode_ms": round(d_ms, 4),
+                         "decode_GBps": round(nb / (d_ms * 1e-3) / 1e9, 1),
+                         "decode_pct_hbm_peak": round(100.0 * nb / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+        cfg = "headq-gqa: B=8, 8 KV heads x 4 query heads, T=131072, d=128, fp16 post-RoPE keys; rank-16 basis " \
+              "fitted from 4096 calibration queries per KV head"
+    print(json.dumps({"workload": args.workload, "config": cfg, "data": "synthetic", "n_gpus": 1,
+                      "steps": args.steps, "warmup": args.warmup, "results": rows}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,14 +184,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--scheme", default="kqv", choices=sorted(PACKED_BYTES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--beside", default=None,
+                    help="comma-separated schemes timed the same way and reported beside the headline "
+                         "(default: the other two of kv, kqv, qkqv; '' for none)")
     ap.add_argument("--B", type=int, default=16)
     ap.add_argument("--H", type=int, default=32)
     ap.add_argument("--T", type=int, default=32768)
+    ap.add_argument("--workload", default="isotropic", choices=["isotropic", "heavy-tailed", "low-rank", "headq-gqa"],
+                    help="isotropic: the headline line; the others print their own timing line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.workload != "isotropic":
+        other_workload(args)
+        return
 
     import torch
     from compressed_decode_attention_kv_amd import synth, tq
@@ -119,53 +209,57 @@ def main():
     K, V, Q = synth.device_isotropic(B, H, 1, T, d, seed=1)
     torch.cuda.synchronize()
 
-    kp = tq.quantize(K, tq.KEYS, args.scheme, n, 0)
-    vp = tq.quantize(V, tq.VALUES, args.scheme, n, 0)
-    ws = torch.empty(tq.decode_workspace_size(kp, vp, H), dtype=torch.uint8, device="cuda")
-    out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
-    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     kdesc, _ = tq.tensor_desc(K)
     vdesc, _ = tq.tensor_desc(V)
     qdesc, _ = tq.tensor_desc(Q)
+    out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     lib = tq.lib()
     import ctypes
-    sid = tq.SCHEMES[args.scheme]
 
     def stream():
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
-    def quant():
-        tq._check(lib.tq_quantize(ctypes.byref(kdesc), tq.KEYS, sid, n, 0, None, ctypes.byref(kp.c), stream()))
-        tq._check(lib.tq_quantize(ctypes.byref(vdesc), tq.VALUES, sid, n, 0, None, ctypes.byref(vp.c), stream()))
+    def run_steps(scheme):
+        """Quantize K and V, then decode, `warmup` untimed and `steps` timed
+        times; returns the packed tensors, workspace and the timings."""
+        kp = tq.quantize(K, tq.KEYS, scheme, n, 0)
+        vp = tq.quantize(V, tq.VALUES, scheme, n, 0)
+        ws = torch.empty(tq.decode_workspace_size(kp, vp, H), dtype=torch.uint8, device="cuda")
+        sid = tq.SCHEMES[scheme]
 
-    def decode():
-        tq._check(lib.tq_decode_attention(ctypes.byref(qdesc), ctypes.byref(kp.c), ctypes.byref(vp.c),
-                                          out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), stream()))
+        def quant():
+            tq._check(lib.tq_quantize(ctypes.byref(kdesc), tq.KEYS, sid, n, 0, None, ctypes.byref(kp.c), stream()))
+            tq._check(lib.tq_quantize(ctypes.byref(vdesc), tq.VALUES, sid, n, 0, None, ctypes.byref(vp.c), stream()))
 
-    for _ in range(args.warmup):
-        quant()
-        decode()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.time()
-    for e in ev:
-        e[0].record()
-        quant()
-        e[1].record()
-        decode()
-        e[2].record()
-    torch.cuda.synchronize()
-    wall = time.time() - t0
-    q_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    d_ms = [b.elapsed_time(c) for _, b, c in ev]
-    step_ms = wall * 1000.0 / args.steps
-    q_avg = sum(q_ms) / len(q_ms)
-    d_avg = sum(d_ms) / len(d_ms)
+        def decode():
+            tq._check(lib.tq_decode_attention(ctypes.byref(qdesc), ctypes.byref(kp.c), ctypes.byref(vp.c),
+                                              out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), stream()))
+
+        for _ in range(args.warmup):
+            quant()
+            decode()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t0 = time.time()
+        for e in ev:
+            e[0].record()
+            quant()
+            e[1].record()
+            decode()
+            e[2].record()
+        torch.cuda.synchronize()
+        wall = time.time() - t0
+        q_ms = [a.elapsed_time(b) for a, b, _ in ev]
+        d_ms = [b.elapsed_time(c) for _, b, c in ev]
+        assert torch.isfinite(out).all().item()
+        return kp, vp, ws, sid, wall * 1000.0 / args.steps, sum(q_ms) / len(q_ms), sum(d_ms) / len(d_ms)
+
+    kp, vp, ws, sid, step_ms, q_avg, d_avg = run_steps(args.scheme)
     packed = B * H * T * PACKED_BYTES[args.scheme]
     dec_gbs = packed / (d_avg * 1e-3) / 1e9
     tok_s = B * T / (q_avg * 1e-3)
-    assert torch.isfinite(out).all().item()
 
     # Streaming-read reference: the same non-temporal 128-bit loads over a
     # plain buffer of the packed cache's size.
@@ -238,6 +332,20 @@ def main():
                      "kernel": "decode chain (query prep + split decode + combine)",
                      "algorithmic_bytes_per_launch": packed},
     }
+    # The other schemes of the workload, timed the same way (not the headline).
+    beside = [x for x in ("kv", "kqv", "qkqv") if x != args.scheme] if args.beside is None else \
+        [x for x in args.beside.split(",") if x]
+    del kp, vp, ws
+    torch.cuda.empty_cache()
+    res["beside"] = {}
+    for scheme in beside:
+        bkp, bvp, bws, _, _, bq, bd = run_steps(scheme)
+        nbytes = B * H * T * PACKED_BYTES[scheme]
+        res["beside"][scheme] = {"decode_ms": round(bd, 4), "decode_GBps": round(nbytes / (bd * 1e-3) / 1e9, 1),
+                                 "decode_pct_hbm_peak": round(100.0 * nbytes / (bd * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                                 "quantize_ms": round(bq, 4)}
+        del bkp, bvp, bws
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.scheme)
     print(json.dumps(res))

@@ -50,6 +50,11 @@ def decode_sources_sha():
 
 
 def short(name):
+    # Names the profiler could not demangle (an fp16 template argument):
+    # <len>quant_kernelILi<a>ELi<b>EDF16_EEvNS_11QuantParamsE.
+    m = re.match(r"^(?:_ZN2tq12_GLOBAL__N_1)?\d*(\w+?)ILi(\d+)ELi(\d+)EDF16_EEvNS_\d+(\w+)E$", name)
+    if m:
+        name = "%s<%s, %s, _Float16>(tq::%s)" % m.groups()
     name = re.sub(r"^void ", "", name)
     name = name.replace("tq::(anonymous namespace)::", "")
     name = name.replace("_ZN2tq12_GLOBAL__N_1", "")
