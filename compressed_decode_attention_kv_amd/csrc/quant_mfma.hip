@@ -1,4 +1,4 @@
-// Write side for fp16 inputs at d = 128 on the matrix cores.
+// Write side for fp16 and fp32 inputs at d = 128 on the matrix cores.
 //
 // [P1] = "Resumen Técnico: Inferencia Estadística y Medidas de Calidad de
 //        Cuantizaciones de Cache KV Inspiradas en TurboQuant"
@@ -44,6 +44,7 @@ namespace {
 constexpr int kThreadsM = 256;
 constexpr int kWavesM = kThreadsM / 64;
 constexpr int kLutMax = 1024;
+constexpr float kSplitScale = 16384.0f;  // fp32 input: 2^14 / ||x|| before the fp16 hi/lo split
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -68,9 +69,16 @@ __device__ __forceinline__ void put_index(uint32_t* words, uint32_t idx) {
   if constexpr (sh + BITS > 32) words[w + 1] |= idx >> (32 - sh);
 }
 
-template <int BITS, int MODE>
+// One tile's input for this lane: x[32 pp + 8 g + j] of token tau.  fp16:
+// four half8; fp32: eight float4 (c = 2 pp + k holds j = 4 k .. 4 k + 3).
+template <typename TIN> struct RawTile;
+template <> struct RawTile<_Float16> { half8 x[4]; };
+template <> struct RawTile<float> { float4v x[8]; };
+
+template <int BITS, int MODE, typename TIN>
 __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, QuantGrid grid) {
   constexpr bool kProd = MODE == TQ_MODE_PROD;
+  constexpr bool kF32 = sizeof(TIN) == 4;
   __shared__ __attribute__((aligned(16))) LutEntry s_lut[kLutMax];
   __shared__ float s_cent[16];
   __shared__ __attribute__((aligned(16))) half8 s_S[kProd ? 8 * 4 * 64 : 1];
@@ -152,16 +160,21 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   const char* lut_bytes = reinterpret_cast<const char*>(s_lut);
   const float inv_sqrt_d = p.inv_sqrt_d;
 
-  // xin[pp][j] = x[32 pp + 8 g + j] of token tau of a tile (clamped to the
-  // head's last token past its end).
-  auto load_tile = [&](int tl, half8* xin) {
+  // The lane's input of token tau of a tile (clamped to the head's last
+  // token past its end).
+  auto load_tile = [&](int tl, RawTile<TIN>& raw) {
     const int bh = tl / tph;
     const int t = min((tl - bh * tph) * 16 + tau, p.T - 1);
     const int b = bh / p.H, h = bh - b * p.H;
-    const _Float16* xrow = reinterpret_cast<const _Float16*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh +
-                           (int64_t)t * p.st;
+    const TIN* xrow = reinterpret_cast<const TIN*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh + (int64_t)t * p.st;
+    if constexpr (kF32) {
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) xin[pp] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(xrow + 32 * pp + 8 * g));
+      for (int c = 0; c < 8; ++c)
+        raw.x[c] = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(xrow + 32 * (c >> 1) + 8 * g + 4 * (c & 1)));
+    } else {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) raw.x[pp] = __builtin_nontemporal_load(reinterpret_cast<const half8*>(xrow + 32 * pp + 8 * g));
+    }
   };
   const int tstride = gridDim.x * kWavesM;
   int tile = blockIdx.x * kWavesM + wave;
@@ -170,16 +183,15 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   // static).  PROD keeps one tile in flight: a second buffer would push it
   // past 168 registers (3 waves per SIMD).
   constexpr bool kPrefetch = !kProd;
-  half8 xnext[4];
+  RawTile<TIN> xnext;
   if constexpr (kPrefetch) load_tile(min(tile, ntiles - 1), xnext);
   for (; tile < ntiles; tile += tstride) {
-    half8 xin[4];
+    RawTile<TIN> raw;
     if constexpr (kPrefetch) {
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) xin[pp] = xnext[pp];
+      raw = xnext;
       load_tile(min(tile + tstride, ntiles - 1), xnext);
     } else {
-      load_tile(tile, xin);
+      load_tile(tile, raw);
     }
     const int bh = tile / tph;
     const int t = (tile - bh * tph) * 16 + tau;
@@ -189,55 +201,91 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
     const bool wr = valid && tw64 >= 0 && tw64 < p.T_cap;
     const uint32_t tw = (uint32_t)tw64;
 
-    // ||x||^2: fp16 products are exact in fp32.
+    // ||x||^2: fp16 products are exact in fp32.  fp32 input: the vector is
+    // scaled by 2^14 / nu (entries at most 2^14, inside fp16's range; typical
+    // entries large enough that the lo part stays a normal fp16) and split
+    // into fp16 hi + lo parts, about 22 significant bits together; both parts
+    // go through the same exact +-1 products into one fp32 accumulator.
+    half8 xin[kF32 ? 2 : 1][4];
     float ss = 0.f;
+    if constexpr (kF32) {
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
+      for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        half2v a2;
-        a2.x = xin[pp][j];
-        a2.y = xin[pp][j + 1];
-        ss = __builtin_amdgcn_fdot2(a2, a2, ss, false);
+        for (int i = 0; i < 4; ++i) ss = fmaf(raw.x[c][i], raw.x[c][i], ss);
+    } else {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        xin[0][pp] = raw.x[pp];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          half2v a2;
+          a2.x = xin[0][pp][j];
+          a2.y = xin[0][pp][j + 1];
+          ss = __builtin_amdgcn_fdot2(a2, a2, ss, false);
+        }
       }
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
     const float nu = sqrtf(ss);
+    if constexpr (kF32) {
+      const float rn = nu > 0.f ? kSplitScale / nu : 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // v is kept as the rounded fp32 product: left to itself the compiler
+          // rounds the exact product straight to fp16 for hi but subtracts a
+          // hi re-derived from the fp32 value for lo, which disagree next to
+          // an fp16 rounding tie (lo then lands on the wrong side).
+          float v = raw.x[c][i] * rn;
+          asm volatile("" : "+v"(v));
+          const _Float16 hi = (_Float16)v;
+          xin[0][c >> 1][4 * (c & 1) + i] = hi;
+          xin[1][c >> 1][4 * (c & 1) + i] = (_Float16)(v - (float)hi);
+        }
+    }
 
     // ---- rotation -------------------------------------------------------------------
-    u32x4 xw[4];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      xw[pp] = __builtin_bit_cast(u32x4, xin[pp]);
-      if (MODE != TQ_MODE_PLAIN) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) xw[pp][w] ^= dmask[pp][w];
-      }
-    }
     // Z[a][rb][i]: the 64-point product for input bit 0 = a at output index
     // 16 g + 4 rb + i.  B slot jj of K block kb = x[2 jh + a], jh as above:
     // halves a of dwords 2 m, 2 m + 1 of xin[2 kb + n / 2], m = n % 2.
     float4v Z[2][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const uint32_t sel = a ? 0x07060302u : 0x05040100u;
-      u32x4 bw[2];
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int rb = 0; rb < 4; ++rb) Z[a][rb] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const int pp = 2 * kb + (n >> 1), m = 2 * (n & 1);
-          bw[kb][n] = __builtin_amdgcn_perm(xw[pp][m + 1], xw[pp][m], sel);
+    for (int part = 0; part < (kF32 ? 2 : 1); ++part) {
+      u32x4 xw[4];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        xw[pp] = __builtin_bit_cast(u32x4, xin[part][pp]);
+        if (MODE != TQ_MODE_PLAIN) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) xw[pp][w] ^= dmask[pp][w];
         }
       }
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const float4v z = {0.f, 0.f, 0.f, 0.f};
-        float4v acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_A[(rb * 2 + 0) * 64 + lane],
-                                                              __builtin_bit_cast(half8, bw[0]), z, 0, 0, 0);
-        Z[a][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_A[(rb * 2 + 1) * 64 + lane],
-                                                           __builtin_bit_cast(half8, bw[1]), acc, 0, 0, 0);
+      for (int a = 0; a < 2; ++a) {
+        const uint32_t sel = a ? 0x07060302u : 0x05040100u;
+        u32x4 bw[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            const int pp = 2 * kb + (n >> 1), m = 2 * (n & 1);
+            bw[kb][n] = __builtin_amdgcn_perm(xw[pp][m + 1], xw[pp][m], sel);
+          }
+        }
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const float4v acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_A[(rb * 2 + 0) * 64 + lane],
+                                                                    __builtin_bit_cast(half8, bw[0]), Z[a][rb], 0, 0, 0);
+          Z[a][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(s_A[(rb * 2 + 1) * 64 + lane],
+                                                             __builtin_bit_cast(half8, bw[1]), acc, 0, 0, 0);
+        }
       }
     }
     // y[rb][2 i + b] <-> coordinate 32 g + 8 rb + 2 i + b: the 2-point stage.
@@ -256,7 +304,10 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         }
       }
     }
-    const float inv = nu > 0.f ? (MODE == TQ_MODE_PLAIN ? 1.0f / nu : inv_sqrt_d / nu) : 0.f;
+    // fp32 input was already scaled by 2^14 / nu.
+    const float inv = nu > 0.f ? (kF32 ? (MODE == TQ_MODE_PLAIN ? 1.0f / kSplitScale : inv_sqrt_d / kSplitScale)
+                                       : (MODE == TQ_MODE_PLAIN ? 1.0f / nu : inv_sqrt_d / nu))
+                               : 0.f;
 
     // ---- index and packing ----------------------------------------------------------
     uint32_t words[BITS];
@@ -354,7 +405,10 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
 
 template <int BITS, int MODE>
 hipError_t launch_m(const QuantParams& p, const QuantGrid& grid, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((quant_mfma_kernel<BITS, MODE>), dim3(nblocks), dim3(kThreadsM), 0, s, p, grid);
+  if (p.dtype == TQ_F32)
+    hipLaunchKernelGGL((quant_mfma_kernel<BITS, MODE, float>), dim3(nblocks), dim3(kThreadsM), 0, s, p, grid);
+  else
+    hipLaunchKernelGGL((quant_mfma_kernel<BITS, MODE, _Float16>), dim3(nblocks), dim3(kThreadsM), 0, s, p, grid);
   return hipGetLastError();
 }
 
@@ -363,7 +417,8 @@ hipError_t launch_m(const QuantParams& p, const QuantGrid& grid, int nblocks, hi
 bool quant_mfma_supported(const QuantParams& p) {
   // 32-bit tile indices and per-head byte offsets (at most 64 bytes per token).
   const long tiles = (long)p.B * p.H * ((p.T + 15) / 16);
-  return p.d == 128 && p.dtype == TQ_F16 && p.mode != TQ_MODE_HEADQ && p.bits >= 1 && p.bits <= 4 &&
+  return p.d == 128 && (p.dtype == TQ_F16 || p.dtype == TQ_F32) && p.mode != TQ_MODE_HEADQ && p.bits >= 1 &&
+         p.bits <= 4 &&
          tiles < (1L << 31) && p.T_cap <= (1 << 24);
 }
 
