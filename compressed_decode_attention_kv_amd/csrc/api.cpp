@@ -675,35 +675,39 @@ tq_status quantize_core(const tq_tensor_desc* x, int mode, int bits, uint64_t se
   p.codes = out->codes; p.norms = out->norms; p.qjl = out->qjl; p.gamma = out->gamma;
   p.side = out->side; p.side_scale = out->side_scale;
   p.pos = pos;
+  hipStream_t st = (hipStream_t)stream;
+  // HeadQ: Pi U_h once per head, [H][rank][d], in stream-ordered scratch.
+  void* rb = nullptr;
+  if (mode == TQ_MODE_HEADQ) {
+    if (hipMallocAsync(&rb, (size_t)x->H * x->d * hq->rank * sizeof(float), st) != hipSuccess)
+      return fail(TQ_ENOMEM, "rotated-basis scratch allocation failed");
+    if (tq_status s = hip_status(launch_rotate_basis(p, reinterpret_cast<float*>(rb), st), "basis rotation launch")) {
+      (void)hipFreeAsync(rb, st);
+      return s;
+    }
+    p.rbasis = reinterpret_cast<const float*>(rb);
+  }
+  tq_status status = TQ_OK;
   QuantGrid grid;
   if (quant_mfma_supported(p) && quant_grid(x->d, bits, &grid)) {
     int cus = 0;
-    if (tq_status s = hip_status(cu_count(&cus), "device query")) return s;
-    const long tiles = (long)x->B * x->H * ((x->T + 15) / 16);  // 16-token tiles within a head
-    const int nblocks = (int)std::max<long>(1, std::min<long>((tiles + 3) / 4, (long)cus * 8));
-    if (tq_status s = hip_status(launch_quantize_mfma(p, grid, nblocks, (hipStream_t)stream), "quantize launch")) return s;
+    status = hip_status(cu_count(&cus), "device query");
+    if (status == TQ_OK) {
+      const long tiles = (long)x->B * x->H * ((x->T + 15) / 16);  // 16-token tiles within a head
+      const int nblocks = (int)std::max<long>(1, std::min<long>((tiles + 3) / 4, (long)cus * 8));
+      status = hip_status(launch_quantize_mfma(p, grid, nblocks, st), "quantize launch");
+    }
   } else {
     p.bh0 = 0; p.nbh = x->B * x->H; p.t0 = 0; p.tn = x->T; p.rcat = nullptr;
     if (mode == TQ_MODE_PROD) {
       p.seed_for_cat = seed;
-      if (tq_status s = quantize_prod_gemm(p, (hipStream_t)stream)) return s;
-    } else if (mode == TQ_MODE_HEADQ) {
-      // Pi U_h once per head (stream-ordered scratch) instead of once per block.
-      hipStream_t st = (hipStream_t)stream;
-      void* rb = nullptr;
-      if (hipMallocAsync(&rb, (size_t)x->H * x->d * hq->rank * sizeof(float), st) != hipSuccess)
-        return fail(TQ_ENOMEM, "rotated-basis scratch allocation failed");
-      tq_status s = hip_status(launch_rotate_basis(p, reinterpret_cast<float*>(rb), st), "basis rotation launch");
-      if (s == TQ_OK) {
-        p.rbasis = reinterpret_cast<const float*>(rb);
-        s = hip_status(launch_quantize(p, st), "quantize launch");
-      }
-      (void)hipFreeAsync(rb, st);
-      if (s) return s;
+      status = quantize_prod_gemm(p, st);
     } else {
-      if (tq_status s = hip_status(launch_quantize(p, (hipStream_t)stream), "quantize launch")) return s;
+      status = hip_status(launch_quantize(p, st), "quantize launch");
     }
   }
+  if (rb) (void)hipFreeAsync(rb, st);
+  if (status != TQ_OK) return status;
   return ok();
 }
 

@@ -78,6 +78,7 @@ template <> struct RawTile<float> { float4v x[8]; };
 template <int BITS, int MODE, typename TIN>
 __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, QuantGrid grid) {
   constexpr bool kProd = MODE == TQ_MODE_PROD;
+  constexpr bool kHeadq = MODE == TQ_MODE_HEADQ;  // 2-bit base + rank-16 4-bit side code
   constexpr bool kF32 = sizeof(TIN) == 4;
   __shared__ __attribute__((aligned(16))) LutEntry s_lut[kLutMax];
   __shared__ float s_cent[16];
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
           lut_bytes + ((__float_as_uint(f) << 3) - (0x4B400000u << 3)));                       \
       const uint32_t idx = e.base + (yy >= e.t ? 1u : 0u);                                     \
       put_index<BITS, 8 * (I) + (A)>(words, idx);                                              \
-      y[I][A] = kProd ? yy - s_cent[idx] : yy;                                                 \
+      y[I][A] = (kProd || kHeadq) ? yy - s_cent[idx] : yy;                                     \
     }
 #define TQ_QROW(I) TQ_QIDX(I, 0) TQ_QIDX(I, 1) TQ_QIDX(I, 2) TQ_QIDX(I, 3) \
                    TQ_QIDX(I, 4) TQ_QIDX(I, 5) TQ_QIDX(I, 6) TQ_QIDX(I, 7)
@@ -351,6 +352,71 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         __builtin_nontemporal_store(words[0], dst);
       }
       if (g == 0) __builtin_nontemporal_store(nu, p.norms + vbase + tw);
+    }
+
+    if constexpr (kHeadq) {
+      // ---- HeadQ side code ([P3] section 3) ----------------------------------------
+      // z = U'^T e' with e' = nu (y - c[idx]) (the residual k - k_base, rotated)
+      // and U' = Pi U_h: a [16 ranks x 128] x [128 x 16 tokens] product on the
+      // matrix cores.  K block kb takes row 8 g + j from lane (g, tau)'s own
+      // coordinate 32 g + 8 kb + j (its y[kb][j]), so the A operand holds
+      // U'[32 g + 8 kb + j][tau] at lane (g, tau) and the result gives lane
+      // (g, tau) ranks 4 g .. 4 g + 3 of token tau.  Both factors are split
+      // into fp16 hi + lo (residual x 2^12, basis x 2^10; each value pinned as
+      // its rounded fp32 before the split) and hi hi + hi lo + lo hi summed.
+      const float* ub = p.rbasis + (size_t)(bh % p.H) * (16 * 128) + tau * 128 + 32 * g;
+      const float rs = nu > 0.f ? 4096.0f : 0.f;
+      float4v zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        half8 eh, el, uh, ul;
+        const float4v u0 = *reinterpret_cast<const float4v*>(ub + 8 * kb);
+        const float4v u1 = *reinterpret_cast<const float4v*>(ub + 8 * kb + 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float ev = y[kb][j] * rs;
+          asm volatile("" : "+v"(ev));
+          const _Float16 ehj = (_Float16)ev;
+          eh[j] = ehj;
+          el[j] = (_Float16)(ev - (float)ehj);
+          float uv = (j < 4 ? u0[j] : u1[j - 4]) * 1024.0f;
+          asm volatile("" : "+v"(uv));
+          const _Float16 uhj = (_Float16)uv;
+          uh[j] = uhj;
+          ul[j] = (_Float16)(uv - (float)uhj);
+        }
+        zacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(uh, eh, zacc, 0, 0, 0);
+        zacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(uh, el, zacc, 0, 0, 0);
+        zacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ul, eh, zacc, 0, 0, 0);
+      }
+      // z_r = nu * zacc / 2^22; s_z = max_r |z_r| / 7; code = clamp(rne(z / s_z), -7, 7) + 7.
+      const float zs = nu * (1.0f / 4194304.0f);
+      float z[4], zmax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i] = zacc[i] * zs;
+        zmax = fmaxf(zmax, fabsf(z[i]));
+      }
+      zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
+      zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
+      const float sz = zmax / 7.0f;
+      uint32_t half = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int c = 7;
+        if (sz > 0.f) {
+          float qz = rintf(z[i] / sz);
+          qz = fminf(fmaxf(qz, -7.0f), 7.0f);
+          c = (int)qz + 7;
+        }
+        half |= (uint32_t)c << (4 * i);
+      }
+      if (wr) {
+        // Ranks 4 g .. 4 g + 3 are bits 16 g .. 16 g + 15 of the token's 8-byte code.
+        __builtin_nontemporal_store((uint16_t)half,
+                                    reinterpret_cast<uint16_t*>(p.side + vbase * 8 + (uint32_t)(tw * 8 + 2 * g)));
+        if (g == 0) __builtin_nontemporal_store(sz, p.side_scale + vbase + tw);
+      }
     }
 
     if constexpr (kProd) {
@@ -417,8 +483,11 @@ hipError_t launch_m(const QuantParams& p, const QuantGrid& grid, int nblocks, hi
 bool quant_mfma_supported(const QuantParams& p) {
   // 32-bit tile indices and per-head byte offsets (at most 64 bytes per token).
   const long tiles = (long)p.B * p.H * ((p.T + 15) / 16);
-  return p.d == 128 && (p.dtype == TQ_F16 || p.dtype == TQ_F32) && p.mode != TQ_MODE_HEADQ && p.bits >= 1 &&
-         p.bits <= 4 &&
+  // HeadQ: the 2-bit base with a rank-16, 4-bit side code, once the rotated
+  // basis (Pi U_h)^T [H][16][128] is in p.rbasis.
+  const bool headq_ok = p.mode == TQ_MODE_HEADQ && p.bits == 2 && p.rank == 16 && p.side_bits == 4 && p.rbasis;
+  return p.d == 128 && (p.dtype == TQ_F16 || p.dtype == TQ_F32) && (p.mode != TQ_MODE_HEADQ || headq_ok) &&
+         p.bits >= 1 && p.bits <= 4 &&
          tiles < (1L << 31) && p.T_cap <= (1 << 24);
 }
 
@@ -437,6 +506,7 @@ hipError_t launch_quantize_mfma(const QuantParams& p, const QuantGrid& grid, int
     case TQ_MODE_PROD * 8 + 1: return launch_m<1, TQ_MODE_PROD>(p, grid, nblocks, s);
     case TQ_MODE_PROD * 8 + 2: return launch_m<2, TQ_MODE_PROD>(p, grid, nblocks, s);
     case TQ_MODE_PROD * 8 + 3: return launch_m<3, TQ_MODE_PROD>(p, grid, nblocks, s);
+    case TQ_MODE_HEADQ * 8 + 2: return launch_m<2, TQ_MODE_HEADQ>(p, grid, nblocks, s);
   }
   return hipErrorInvalidValue;
 }
