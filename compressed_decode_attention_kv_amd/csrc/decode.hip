@@ -306,7 +306,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     for (int c = 0; c < d / (int)blockDim.x + 1; ++c) {
       const int kk = threadIdx.x + c * blockDim.x;
       if (kk < d && c < kMaxD / kThreads) {
+        // S^T acc_sk: coalesced across kk; unrolled so that several L2
+        // loads are in flight per thread.
         float acc = 0.f;
+#pragma unroll 16
         for (int i = 0; i < d; ++i) acc = fmaf(p.S[(size_t)i * d + kk], s_k[i], acc);
         add[c] = acc;
       }
