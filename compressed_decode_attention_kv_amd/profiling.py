@@ -7,7 +7,12 @@
         --calib-bytes N --algorithmic-bytes A --title "..." --command "..." [--command ...]
   python -m compressed_decode_attention_kv_amd.profiling counters <counter_collection.csv> [...]
 
-`stats` prints the average duration per kernel.  `decode-traffic` writes the
+Every summary keeps, per kernel, only the dispatches at its largest grid
+size: the workload's full-size launch (a benchmark run also makes small
+launches of the same kernels, e.g. one-token appends, which would otherwise
+dominate the per-kernel averages and medians).  `stats` prints the average
+duration per kernel over those dispatches, from the kernel trace beside the
+stats file.  `decode-traffic` writes the
 committed per-scheme summary: the traffic table, the decode chain's bytes
 (query prep + split decode + combine) and the hash of the decode sources it
 was measured on (a summary taken on other sources is not used).  `traffic` prints HBM bytes
@@ -61,31 +66,46 @@ def short(name):
     return name[:90]
 
 
-def stats(path):
-    rows = list(csv.DictReader(open(path)))
-    out = ["%-90s %6s %14s" % ("kernel", "calls", "avg_us")]
+def _largest_grid(rows, grid_of):
+    """The rows of each kernel's dispatches at that kernel's largest grid size."""
+    top = {}
     for r in rows:
-        if "tq" not in r["Name"] and "stream_read" not in r["Name"]:
-            continue
-        out.append("%-90s %6s %14.2f" % (short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1000.0))
+        k = r["Kernel_Name"]
+        top[k] = max(top.get(k, 0), grid_of(r))
+    return [r for r in rows if grid_of(r) == top[r["Kernel_Name"]]]
+
+
+def _trace_grid(r):
+    return int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+
+
+def stats(path):
+    """Calls and average duration per library kernel, over the dispatches at
+    its largest grid size, from run_kernel_trace.csv beside `path`."""
+    trace = os.path.join(os.path.dirname(path), "run_kernel_trace.csv")
+    rows = [r for r in csv.DictReader(open(trace)) if "tq" in r["Kernel_Name"] or "stream_read" in r["Kernel_Name"]]
+    calls = collections.Counter(r["Kernel_Name"] for r in rows)
+    dur = collections.defaultdict(list)
+    for r in _largest_grid(rows, _trace_grid):
+        dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    out = ["%-90s %6s %10s %14s" % ("kernel", "calls", "full-size", "avg_us")]
+    for k in sorted(dur, key=lambda k: -sum(dur[k])):
+        out.append("%-90s %6d %10d %14.2f" % (short(k), calls[k], len(dur[k]), sum(dur[k]) / len(dur[k])))
     return "\n".join(out)
 
 
 def _per_kernel(path, counter):
-    rows = list(csv.DictReader(open(path)))
+    rows = _largest_grid([r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter],
+                         lambda r: int(r["Grid_Size"]))
     agg = collections.defaultdict(list)
-    grid = {}
     for r in rows:
-        if r["Counter_Name"] != counter:
-            continue
         agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-        grid.setdefault(r["Kernel_Name"], set()).add(int(r["Grid_Size"]))
-    return agg, grid
+    return agg
 
 
 def _traffic_table(fetch_path, write_path, calib_bytes, write_factor):
-    fetch, _ = _per_kernel(fetch_path, "FETCH_SIZE")
-    write, _ = _per_kernel(write_path, "WRITE_SIZE")
+    fetch = _per_kernel(fetch_path, "FETCH_SIZE")
+    write = _per_kernel(write_path, "WRITE_SIZE")
     cal = [k for k in fetch if "stream_read" in k]
     if not cal:
         raise SystemExit("no streaming-read dispatch in %s" % fetch_path)
@@ -153,16 +173,16 @@ _DERIVED = (  # name, numerator counter, divisor ("cu" or "simd")
 
 
 def counters(paths):
-    """Per-kernel medians over dispatches of the VALU instruction count and of
-    rocprof's derived utilisations (each computed within one dispatch)."""
+    """Per-kernel medians, over the dispatches at the kernel's largest grid
+    size, of the VALU instruction count and of rocprof's derived utilisations
+    (each computed within one dispatch)."""
     per = collections.defaultdict(lambda: collections.defaultdict(list))   # kernel -> column -> values
     for path in paths:
         cu, simd, xcc = _agent(path)
         disp = collections.defaultdict(dict)
         names = {}
-        for r in csv.DictReader(open(path)):
-            if "tq" not in r["Kernel_Name"]:
-                continue
+        rows = [r for r in csv.DictReader(open(path)) if "tq" in r["Kernel_Name"]]
+        for r in _largest_grid(rows, lambda r: int(r["Grid_Size"])):
             disp[r["Dispatch_Id"]][r["Counter_Name"]] = float(r["Counter_Value"])
             names[r["Dispatch_Id"]] = r["Kernel_Name"]
         for did, c in disp.items():
