@@ -30,7 +30,12 @@
 //     (rounded toward zero) + lo parts, so r - hi is exact and two products
 //     per tile with fp32 accumulation keep about 22 bits.  The rows of S are
 //     ordered so that lane (g, tau) receives sketch rows 32 g .. 32 g + 31:
-//     its 32 sign bits are word g of the token's sign block.
+//     its 32 sign bits are word g of the token's sign block, shifted in one
+//     per row with a funnel shift of the product's sign bit.
+//   * sketched and HeadQ modes run the index search on y 2^12 (boundaries,
+//     centroids and grid scale scaled to match, all by a power of two, so
+//     every decision and the residual are those of y itself, scaled), which
+//     leaves the residual already at the scale its fp16 split needs.
 //   * stores: non-temporal, so that a decode streaming the cache soon after
 //     does not meet its lines still dirty in the caches (~20% slower).
 #include <cfloat>
@@ -80,6 +85,8 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   constexpr bool kProd = MODE == TQ_MODE_PROD;
   constexpr bool kHeadq = MODE == TQ_MODE_HEADQ;  // 2-bit base + rank-16 4-bit side code
   constexpr bool kF32 = sizeof(TIN) == 4;
+  // Index search on y * kRes: the residual comes out at the 2^12 scale of its fp16 split.
+  constexpr float kRes = (kProd || kHeadq) ? 4096.0f : 1.0f;
   __shared__ __attribute__((aligned(16))) LutEntry s_lut[kLutMax];
   __shared__ float s_cent[16];
   __shared__ __attribute__((aligned(16))) half8 s_S[kProd ? 8 * 4 * 64 : 1];
@@ -101,10 +108,10 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       if (b < lo) base++;
       else if (b < hi && t == INFINITY) t = b;
     }
-    s_lut[n].t = t;
+    s_lut[n].t = t * kRes;
     s_lut[n].base = base;
   }
-  if (threadIdx.x < 16) s_cent[threadIdx.x] = p.centroids[threadIdx.x];
+  if (threadIdx.x < 16) s_cent[threadIdx.x] = p.centroids[threadIdx.x] * kRes;
   if constexpr (kProd) {
     // Operand (mb, pp), lane (gk, e): S[row][col + j], j < 8, with
     // row = 32 (e / 4) + 4 mb + e % 4 and col = 32 gk + 8 pp.
@@ -158,6 +165,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   // 1.5 * 2^23 + center: fma(y, scale, bias) leaves round(y * scale) + center
   // in the low mantissa bits, so (bits << 3) + const is the entry's LDS offset.
   const float bias = 12582912.0f + (float)grid.center;
+  const float gscale = grid.scale / kRes;
   const char* lut_bytes = reinterpret_cast<const char*>(s_lut);
   const float inv_sqrt_d = p.inv_sqrt_d;
 
@@ -179,21 +187,15 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
   };
   const int tstride = gridDim.x * kWavesM;
   int tile = blockIdx.x * kWavesM + wave;
-  // MSE/PLAIN: the next tile's input is loaded while this one is processed
-  // (always issued, clamped to the last tile, so the wait before use is
-  // static).  PROD keeps one tile in flight: a second buffer would push it
-  // past 168 registers (3 waves per SIMD).
-  constexpr bool kPrefetch = !kProd;
+  // The next tile's input is loaded while this one is processed (always
+  // issued, clamped to the last tile, so the wait before use is static).
+  // PROD's occupancy is set by its 48 KB of LDS (3 blocks per CU), so the
+  // second buffer's registers cost it no waves.
   RawTile<TIN> xnext;
-  if constexpr (kPrefetch) load_tile(min(tile, ntiles - 1), xnext);
+  load_tile(min(tile, ntiles - 1), xnext);
   for (; tile < ntiles; tile += tstride) {
-    RawTile<TIN> raw;
-    if constexpr (kPrefetch) {
-      raw = xnext;
-      load_tile(min(tile + tstride, ntiles - 1), xnext);
-    } else {
-      load_tile(tile, raw);
-    }
+    const RawTile<TIN> raw = xnext;
+    load_tile(min(tile + tstride, ntiles - 1), xnext);
     const int bh = tile / tph;
     const int t = (tile - bh * tph) * 16 + tau;
     const bool valid = t < p.T;
@@ -305,9 +307,10 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         }
       }
     }
-    // fp32 input was already scaled by 2^14 / nu.
-    const float inv = nu > 0.f ? (kF32 ? (MODE == TQ_MODE_PLAIN ? 1.0f / kSplitScale : inv_sqrt_d / kSplitScale)
-                                       : (MODE == TQ_MODE_PLAIN ? 1.0f / nu : inv_sqrt_d / nu))
+    // fp32 input was already scaled by 2^14 / nu.  Times kRes: exact, and
+    // (a 2^12) / nu rounds to exactly 2^12 (a / nu).
+    const float inv = nu > 0.f ? (kF32 ? (MODE == TQ_MODE_PLAIN ? 1.0f / kSplitScale : inv_sqrt_d * (kRes / kSplitScale))
+                                       : (MODE == TQ_MODE_PLAIN ? 1.0f / nu : (inv_sqrt_d * kRes) / nu))
                                : 0.f;
 
     // ---- index and packing ----------------------------------------------------------
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
 #define TQ_QIDX(I, A)                                                                          \
     {                                                                                          \
       const float yy = y[I][A] * inv;                                                          \
-      const float f = fmaf(yy, grid.scale, bias);                                              \
+      const float f = fmaf(yy, gscale, bias);                                                  \
       const LutEntry e = *reinterpret_cast<const LutEntry*>(                                   \
           lut_bytes + ((__float_as_uint(f) << 3) - (0x4B400000u << 3)));                       \
       const uint32_t idx = e.base + (yy >= e.t ? 1u : 0u);                                     \
@@ -364,8 +367,8 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       // (g, tau) ranks 4 g .. 4 g + 3 of token tau.  Both factors are split
       // into fp16 hi + lo (residual x 2^12, basis x 2^10; each value pinned as
       // its rounded fp32 before the split) and hi hi + hi lo + lo hi summed.
+      // y holds the residual times 2^12 already; for nu = 0 the scale zs below is 0.
       const float* ub = p.rbasis + (size_t)(bh % p.H) * (16 * 128) + tau * 128 + 32 * g;
-      const float rs = nu > 0.f ? 4096.0f : 0.f;
       float4v zacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         const float4v u1 = *reinterpret_cast<const float4v*>(ub + 8 * kb + 4);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          float ev = y[kb][j] * rs;
+          float ev = y[kb][j];
           asm volatile("" : "+v"(ev));
           const _Float16 ehj = (_Float16)ev;
           eh[j] = ehj;
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
 
     if constexpr (kProd) {
       // ---- QJL sketch of the residual ----------------------------------------------
-      const float rs = nu > 0.f ? 4096.0f : 0.f;
+      // y holds r 2^12: g2 = 2^24 ||r||^2 exactly, and sqrt of it 2^12 ||r||.
       float g2 = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -430,14 +433,20 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       g2 += __shfl_xor(g2, 16, 64);
       g2 += __shfl_xor(g2, 32, 64);
       // Operand pp, slot j = coordinate 32 g + 8 pp + j = y[pp][j].
+      // r - hi (exact) as one mixed-precision fma per element, hi * m1 + r: m1
+      // is -1 kept opaque so that it is not folded into a subtraction, which
+      // would first convert hi to fp32.
+      float m1 = -1.0f;
+      asm volatile("" : "+s"(m1));
       half8 Bhi[4], Blo[4];
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-          const float r0 = y[pp][j] * rs, r1 = y[pp][j + 1] * rs;
+          const float r0 = y[pp][j], r1 = y[pp][j + 1];
           const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-          const half2v lo = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0 - (float)hi.x, r1 - (float)hi.y));
+          const half2v lo = __builtin_bit_cast(
+              half2v, __builtin_amdgcn_cvt_pkrtz(fmaf((float)hi.x, m1, r0), fmaf((float)hi.y, m1, r1)));
           Bhi[pp][j] = hi.x; Bhi[pp][j + 1] = hi.y;
           Blo[pp][j] = lo.x; Blo[pp][j + 1] = lo.y;
         }
@@ -445,9 +454,12 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       // Row block mb gives lane (g, tau) sketch rows 32 g + 4 mb + i, i < 4:
       // bits 4 mb + i of the lane's sign word.  Two blocks in flight at a time
       // keep the S operands (LDS reads) from all being hoisted into registers.
-      uint32_t sbits = 0;
+      // Rows are visited from 31 down, each shifting its product's sign bit in
+      // at the bottom; the bit is [p >= 0], the complement of the sign bit
+      // (they differ only at p = -0, where p is exactly zero).
+      uint32_t sneg = 0;
 #pragma unroll 2
-      for (int mb = 0; mb < 8; ++mb) {
+      for (int mb = 7; mb >= 0; --mb) {
         float4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
@@ -455,15 +467,13 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bhi[pp], acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Blo[pp], acc, 0, 0, 0);
         }
-        uint32_t sc = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc |= (acc[i] >= 0.f ? 1u : 0u) << i;
-        sbits |= sc << (4 * mb);
+        for (int i = 3; i >= 0; --i) sneg = __builtin_amdgcn_alignbit(sneg, __float_as_uint(acc[i]), 31);
       }
       if (wr) {
-        __builtin_nontemporal_store(nu > 0.f ? sbits : 0u,
+        __builtin_nontemporal_store(nu > 0.f ? ~sneg : 0u,
                                     reinterpret_cast<uint32_t*>(p.qjl + vbase * 16 + (uint32_t)(tw * 16 + g * 4)));
-        if (g == 0) __builtin_nontemporal_store(nu > 0.f ? sqrtf(g2) : 0.f, p.gamma + vbase + tw);
+        if (g == 0) __builtin_nontemporal_store(nu > 0.f ? sqrtf(g2) * (1.0f / 4096.0f) : 0.f, p.gamma + vbase + tw);
       }
     }
   }
