@@ -22,7 +22,10 @@
 //       S region  (same entries, +128): 8 fp16 signs (+-1) of byte e, a copy per lane%8 (b128)
 //   * key centroids stay fp32 (scores are exact in fp32); value centroids and
 //     the +-1 sign patterns are fp16 and enter v_fma_mix_f32 with fp32
-//     weights and fp32 accumulators;
+//     weights and fp32 accumulators; with sketches on both sides (8 waves,
+//     registers to spare) the key sketch term <S q, sigma> runs on
+//     v_dot2_f32_f16 with S q in fp16 pairs (scaled by a power of two, its
+//     largest entry in [1/2, 1)) against the exact +-1 pairs;
 //   * d/32 lanes per token, lane j owns coordinates [32j, 32j+32); the
 //     per-token scalars (norms, residual norms) are loaded by lanes 0..3 of
 //     the token's group and broadcast (DPP within a quad at d = 128);
@@ -126,6 +129,14 @@ template <int L, int J>
 __device__ __forceinline__ float tok_bcast(float v, int lane) {
   if constexpr (L == 4) return quad_bcast<J>(v);
   else return __shfl(v, (lane & ~(L - 1)) | J, 64);
+}
+
+// Maximum over the L lanes of this lane's token group.
+template <int L>
+__device__ __forceinline__ float tok_max(float v) {
+#pragma unroll
+  for (int off = 1; off < L; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
 }
 
 // Sum over the L lanes of this lane's token group.
@@ -283,12 +294,35 @@ void decode_lut_kernel(DecodeParams p) {
     hp.vs = VQ ? p.v.qjl + vbase * (D / 8) : nullptr;
     const float* sc_head = sc_src + vbase;
 
-    float q[32], u[KQ ? 32 : 1];
+    constexpr bool kUDot = KQ && VQ;
+    float q[32], u[KQ && !kUDot ? 32 : 1];
 #pragma unroll
     for (int e = 0; e < 32; ++e) q[e] = p.qrot[(size_t)qi * d + 32 * j + e];
-    if (KQ) {
+    if constexpr (KQ && !kUDot) {
 #pragma unroll
       for (int e = 0; e < 32; ++e) u[e] = p.qsk[(size_t)qi * d + 32 * j + e];
+    }
+    // kUDot: S q as fp16 pairs times 2^-e (largest |entry| of the whole
+    // vector in [1/2, 1): an exact scaling, taken back in uscale).
+    half2_t uh[kUDot ? 16 : 1];
+    float uscale = p.k_qjl;
+    if constexpr (kUDot) {
+      float uf[32], mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        uf[e] = p.qsk[(size_t)qi * d + 32 * j + e];
+        mx = fmaxf(mx, fabsf(uf[e]));
+      }
+      mx = tok_max<L>(mx);
+      int ex = 0;
+      (void)frexpf(mx, &ex);
+      const float down = ldexpf(1.0f, -ex);
+      uscale = ldexpf(p.k_qjl, ex);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uh[i].x = (_Float16)(uf[2 * i] * down);
+        uh[i].y = (_Float16)(uf[2 * i + 1] * down);
+      }
     }
     // HeadQ: this lane's 4 entries of w = U^T q (side codes 4j..4j+3) and the
     // offset lev * sum(w) that turns a 4-bit code into code - lev.
@@ -372,15 +406,22 @@ void decode_lut_kernel(DecodeParams p) {
 #define TQ_KSIGN(BB)                                                                           \
         {                                                                                      \
           const half8_t s = *reinterpret_cast<const half8_t*>(smem + byte_addr<BB>(cur.ks, lr_s)); \
-          _Pragma("unroll") for (int t = 0; t < 8; t += 2) {                                   \
-            pa = fmaf(u[8 * BB + t], (float)s[t], pa);                                         \
-            pb = fmaf(u[8 * BB + t + 1], (float)s[t + 1], pb);                                 \
+          if constexpr (kUDot) {                                                               \
+            pa = __builtin_amdgcn_fdot2(uh[4 * BB], s.s01, pa, false);                         \
+            pb = __builtin_amdgcn_fdot2(uh[4 * BB + 1], s.s23, pb, false);                     \
+            pa = __builtin_amdgcn_fdot2(uh[4 * BB + 2], s.s45, pa, false);                     \
+            pb = __builtin_amdgcn_fdot2(uh[4 * BB + 3], s.s67, pb, false);                     \
+          } else {                                                                             \
+            _Pragma("unroll") for (int t = 0; t < 8; t += 2) {                                 \
+              pa = fmaf(u[8 * BB + t], (float)s[t], pa);                                       \
+              pb = fmaf(u[8 * BB + t + 1], (float)s[t + 1], pb);                               \
+            }                                                                                  \
           }                                                                                    \
         }
         TQ_KSIGN(0) TQ_KSIGN(1) TQ_KSIGN(2) TQ_KSIGN(3)
 #undef TQ_KSIGN
         const float g_k = tok_bcast<L, 1>(cur.sc, lane);
-        part = fmaf(nu_k * p.k_qjl * g_k, pa + pb, part);
+        part = fmaf(nu_k * uscale * g_k, pa + pb, part);
       }
       float s = tok_sum<L>(part) * p.scale_log2;
       if (!valid) s = -INFINITY;
