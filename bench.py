@@ -256,9 +256,11 @@ def main():
         q_ms = [a.elapsed_time(b) for a, b, _ in ev]
         d_ms = [b.elapsed_time(c) for _, b, c in ev]
         assert torch.isfinite(out).all().item()
+        run_steps.decode_all = sorted(d_ms)
         return kp, vp, ws, sid, wall * 1000.0 / args.steps, sum(q_ms) / len(q_ms), sum(d_ms) / len(d_ms)
 
     kp, vp, ws, sid, step_ms, q_avg, d_avg = run_steps(args.scheme)
+    d_sorted = run_steps.decode_all
     packed = B * H * T * PACKED_BYTES[args.scheme]
     dec_gbs = packed / (d_avg * 1e-3) / 1e9
     tok_s = B * T / (q_avg * 1e-3)
@@ -324,6 +326,8 @@ def main():
                                % (B, H, T, d, args.scheme, n),
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "scheme": args.scheme, "n_bits": n},
         "decode_ms": round(d_avg, 4),
+        "decode_ms_median": round(d_sorted[len(d_sorted) // 2], 4),
+        "decode_ms_min": round(d_sorted[0], 4),
         "decode_pct_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
         "stream_read_GBps": round(stream_gbs, 1),
         "stream_read_bytes": int(packed_bytes_total(kp, vp)),
