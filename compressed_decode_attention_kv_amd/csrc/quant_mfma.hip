@@ -66,12 +66,13 @@ struct LutEntry {
 __device__ __forceinline__ int parity(uint32_t x) { return __builtin_popcount(x) & 1; }
 
 // Put the BITS-bit index of coordinate O (of the lane's 32) into its place
-// in the lane's LSB-first bitstream words.
+// in the lane's LSB-first bitstream words.  The fields are disjoint, so an
+// add is the same as an or and becomes one shift-and-add.
 template <int BITS, int O>
 __device__ __forceinline__ void put_index(uint32_t* words, uint32_t idx) {
   constexpr int bit = BITS * O, w = bit >> 5, sh = bit & 31;
-  words[w] |= idx << sh;
-  if constexpr (sh + BITS > 32) words[w + 1] |= idx >> (32 - sh);
+  words[w] += idx << sh;
+  if constexpr (sh + BITS > 32) words[w + 1] += idx >> (32 - sh);
 }
 
 // One tile's input for this lane: x[32 pp + 8 g + j] of token tau.  fp16:
@@ -231,7 +232,11 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
-    const float nu = sqrtf(ss);
+    // fp16 input: the hardware square root and reciprocal square root (about
+    // 1 ulp each; the norm is compared at 1e-6 and a decision moves only
+    // next to a boundary).  fp32 input: correctly rounded, its 2^14 / nu
+    // feeds the hi + lo split.
+    const float nu = kF32 ? sqrtf(ss) : __builtin_amdgcn_sqrtf(ss);
     if constexpr (kF32) {
       const float rn = nu > 0.f ? kSplitScale / nu : 0.f;
 #pragma unroll
@@ -291,7 +296,13 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
         }
       }
     }
-    // y[rb][2 i + b] <-> coordinate 32 g + 8 rb + 2 i + b: the 2-point stage.
+    // The scale to the unit vector (times kRes): fp32 input was already
+    // scaled by 2^14 / nu; fp16 input takes 1 / nu as rsq(||x||^2).
+    const float inv = nu > 0.f ? (kF32 ? (MODE == TQ_MODE_PLAIN ? 1.0f / kSplitScale : inv_sqrt_d * (kRes / kSplitScale))
+                                       : (MODE == TQ_MODE_PLAIN ? 1.0f : inv_sqrt_d * kRes) * __builtin_amdgcn_rsqf(ss))
+                               : 0.f;
+    // y[rb][2 i + b] <-> coordinate 32 g + 8 rb + 2 i + b, scaled: the
+    // 2-point stage (z0 +- z1) inv as z0 inv +- z1 inv, one product and two fmas.
     float y[4][8];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -299,19 +310,15 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       for (int i = 0; i < 4; ++i) {
         const float z0 = Z[0][rb][i], z1 = Z[1][rb][i];
         if (MODE == TQ_MODE_PLAIN) {
-          y[rb][2 * i] = z0;
-          y[rb][2 * i + 1] = z1;
+          y[rb][2 * i] = z0 * inv;
+          y[rb][2 * i + 1] = z1 * inv;
         } else {
-          y[rb][2 * i] = z0 + z1;
-          y[rb][2 * i + 1] = z0 - z1;
+          const float t1 = z1 * inv;
+          y[rb][2 * i] = fmaf(z0, inv, t1);
+          y[rb][2 * i + 1] = fmaf(z0, inv, -t1);
         }
       }
     }
-    // fp32 input was already scaled by 2^14 / nu.  Times kRes: exact, and
-    // (a 2^12) / nu rounds to exactly 2^12 (a / nu).
-    const float inv = nu > 0.f ? (kF32 ? (MODE == TQ_MODE_PLAIN ? 1.0f / kSplitScale : inv_sqrt_d * (kRes / kSplitScale))
-                                       : (MODE == TQ_MODE_PLAIN ? 1.0f / nu : (inv_sqrt_d * kRes) / nu))
-                               : 0.f;
 
     // ---- index and packing ----------------------------------------------------------
     uint32_t words[BITS];
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
     for (int k = 0; k < BITS; ++k) words[k] = 0;
 #define TQ_QIDX(I, A)                                                                          \
     {                                                                                          \
-      const float yy = y[I][A] * inv;                                                          \
+      const float yy = y[I][A];                                                                \
       const float f = fmaf(yy, gscale, bias);                                                  \
       const LutEntry e = *reinterpret_cast<const LutEntry*>(                                   \
           lut_bytes + ((__float_as_uint(f) << 3) - (0x4B400000u << 3)));                       \
