@@ -77,8 +77,9 @@ tq_status layout_of(int d, int mode, int bits, int side_rank, int side_bits, tq_
   if (tq_status s = check_d(d)) return s;
   if (mode < TQ_MODE_PLAIN || mode > TQ_MODE_HEADQ) return fail(TQ_EINVAL, "unknown mode %d", mode);
   if (bits < 1 || bits > kMaxIndexBits) return fail(TQ_EINVAL, "index bits %d outside [1, %d]", bits, kMaxIndexBits);
-  out->code_bytes = d * bits / 8;
-  out->qjl_bytes = mode == TQ_MODE_PROD ? d / 8 : 0;
+  // PROD: one (bits+1)-bit field per coordinate, code | QJL sign << bits.
+  out->code_bytes = d * (bits + (mode == TQ_MODE_PROD ? 1 : 0)) / 8;
+  out->qjl_bytes = 0;
   out->has_gamma = mode == TQ_MODE_PROD;
   out->side_bytes = 0;
   out->has_side_scale = 0;
@@ -287,8 +288,8 @@ tq_status check_packed(const tq_packed* p, const char* name) {
   if (tq_status s = layout_of(p->d, p->mode, p->bits, p->side_rank, p->side_bits, &lay)) return s;
   if (!p->codes || !p->norms) return fail(TQ_EINVAL, "%s codes/norms plane is NULL", name);
   if (!aligned(p->codes, 16) || !aligned(p->norms, 16)) return fail(TQ_EINVAL, "%s planes must be 16-byte aligned", name);
-  if (p->mode == TQ_MODE_PROD && (!p->qjl || !p->gamma || !aligned(p->qjl, 16) || !aligned(p->gamma, 16)))
-    return fail(TQ_EINVAL, "%s QJL planes missing or misaligned", name);
+  if (p->mode == TQ_MODE_PROD && (!p->gamma || !aligned(p->gamma, 16)))
+    return fail(TQ_EINVAL, "%s QJL gamma plane missing or misaligned", name);
   if (p->mode == TQ_MODE_HEADQ && (!p->side || !p->side_scale || !p->basis || !aligned(p->side, 16) || !aligned(p->side_scale, 16)))
     return fail(TQ_EINVAL, "%s HeadQ planes or basis missing or misaligned", name);
   return TQ_OK;
@@ -619,8 +620,8 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
   if (T_cap < x->T) return fail(TQ_EINVAL, "T_cap=%d < T=%d", T_cap, x->T);
   if (!out->codes || !out->norms || !aligned(out->codes, 16) || !aligned(out->norms, 16))
     return fail(TQ_EINVAL, "codes/norms planes missing or not 16-byte aligned");
-  if (mode == TQ_MODE_PROD && (!out->qjl || !out->gamma || !aligned(out->qjl, 16) || !aligned(out->gamma, 16)))
-    return fail(TQ_EINVAL, "QJL planes missing or not 16-byte aligned");
+  if (mode == TQ_MODE_PROD && (!out->gamma || !aligned(out->gamma, 16)))
+    return fail(TQ_EINVAL, "QJL gamma plane missing or not 16-byte aligned");
   if (mode == TQ_MODE_HEADQ && (!out->side || !out->side_scale || !aligned(out->side, 16) || !aligned(out->side_scale, 16)))
     return fail(TQ_EINVAL, "HeadQ side planes missing or not 16-byte aligned");
   if ((long)x->B * x->H * (long)T_cap > (1L << 40)) return fail(TQ_EINVAL, "cache too large");

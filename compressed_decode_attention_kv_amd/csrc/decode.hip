@@ -119,17 +119,19 @@ struct KScorer {
   // Returns this lane's share of s_j * sqrt(d) (natural units before scaling).
   __device__ float score(const DecodeParams& p, const float* kc, int64_t vec, int j, int L) const {
     const int d = p.d;
-    uint32_t w[KB];
-    const uint32_t* cw = reinterpret_cast<const uint32_t*>(p.k.codes + vec * (d * KB / 8)) + j * KB;
+    // PROD keys: (KB+1)-bit fields, code | sign << KB.
+    constexpr int KF = Field<KB, KQ>::kBits;
+    uint32_t w[KF];
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(p.k.codes + vec * (d * KF / 8)) + j * KF;
 #pragma unroll
-    for (int k = 0; k < KB; ++k) w[k] = ld_nt(cw + k);
+    for (int k = 0; k < KF; ++k) w[k] = ld_nt(cw + k);
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) acc = fmaf(qf[e], kc[code_at<KB>(w, e)], acc);
+    for (int e = 0; e < 32; ++e) acc = fmaf(qf[e], kc[code_at<KF>(w, e) & Field<KB, false>::kCodeMask], acc);
     const float nu = ld_nt(p.k.norms + vec);
     float part = nu * acc;
     if (KQ) {
-      const uint32_t sw = ld_nt(reinterpret_cast<const uint32_t*>(p.k.qjl + vec * (d / 8)) + j);
+      const uint32_t sw = sign_word<KB>(w);
       float pq = 0.f;
 #pragma unroll
       for (int e = 0; e < 32; ++e) pq += ((sw >> e) & 1u) ? uf[e] : -uf[e];
@@ -213,15 +215,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const float pt = valid ? exp2f(s - m) : 0.f;
     l += pt;
     const float wv = pt * ld_nt(p.v.norms + vec);
-    uint32_t w[VB];
-    const uint32_t* cw = reinterpret_cast<const uint32_t*>(p.v.codes + vec * (d * VB / 8)) + j * VB;
+    // PROD values: (VB+1)-bit fields, code | sign << VB.
+    constexpr int VF = Field<VB, VQ>::kBits;
+    uint32_t w[VF];
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(p.v.codes + vec * (d * VF / 8)) + j * VF;
 #pragma unroll
-    for (int k = 0; k < VB; ++k) w[k] = ld_nt(cw + k);
+    for (int k = 0; k < VF; ++k) w[k] = ld_nt(cw + k);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) acc[e] = fmaf(wv, s_vc[code_at<VB>(w, e)], acc[e]);
+    for (int e = 0; e < 32; ++e) acc[e] = fmaf(wv, s_vc[code_at<VF>(w, e) & Field<VB, false>::kCodeMask], acc[e]);
     if (VQ) {
       const float wq = wv * ld_nt(p.v.gamma + vec);
-      const uint32_t sw = ld_nt(reinterpret_cast<const uint32_t*>(p.v.qjl + vec * (d / 8)) + j);
+      const uint32_t sw = sign_word<VB>(w);
 #pragma unroll
       for (int e = 0; e < 32; ++e) ask[e] += ((sw >> e) & 1u) ? wq : -wq;
     }

@@ -12,20 +12,18 @@
 // Same arithmetic as decode_split_kernel (scores and value sums in the
 // rotated domain), organised so that each byte of packed cache costs about
 // one VALU instruction:
-//   * a packed byte (two 4-bit codes, or four 2-bit codes) is turned into an
-//     LDS address by one v_perm, a 6-bit field (two 3-bit codes) by a shift
-//     and one v_and_or_b32, and one LDS read returns the centroids;
+//   * a packed byte (two 4-bit codes, two (3-bit code, sign) fields of a
+//     sketched tensor, or four 2-bit codes) is turned into an LDS address by
+//     one v_perm, a 6-bit field (two 3-bit codes) by a shift and one
+//     v_and_or_b32, and one LDS read returns the centroids (and the signs);
 //   * the LDS tables are replicated across lanes so that every read of a
-//     wave hits distinct banks:
-//       V region  [0, 64K):     entry e at e*256, fp16 pair, one copy per lane (b32)
-//       K region  [64K, 128K):  entry e at 64K + e*256, fp32 pair, a copy per lane%16 (b64)
-//       S region  (same entries, +128): 8 fp16 signs (+-1) of byte e, a copy per lane%8 (b128)
+//     wave hits distinct banks (see the map below);
 //   * key centroids stay fp32 (scores are exact in fp32); value centroids and
 //     the +-1 sign patterns are fp16 and enter v_fma_mix_f32 with fp32
-//     weights and fp32 accumulators; with sketches on both sides (8 waves,
-//     registers to spare) the key sketch term <S q, sigma> runs on
-//     v_dot2_f32_f16 with S q in fp16 pairs (scaled by a power of two, its
-//     largest entry in [1/2, 1)) against the exact +-1 pairs;
+//     weights and fp32 accumulators; the key sketch term <S q, sigma> runs
+//     on v_dot2_f32_f16 with S q in fp16 pairs (scaled by a power of two, its
+//     largest entry in [1/2, 1)) against the exact +-1 pairs where registers
+//     allow (d = 128, or both sides sketched), else in fp32 fma;
 //   * d/32 lanes per token, lane j owns coordinates [32j, 32j+32); the
 //     per-token scalars (norms, residual norms) are loaded by lanes 0..3 of
 //     the token's group and broadcast (DPP within a quad at d = 128);
@@ -54,25 +52,28 @@ constexpr bool lut_two_buffers(int d, bool kq, bool vq) { return kq == vq || d <
 constexpr int kMaxLutWaves = 12;
 // LDS map.  A table indexed by a whole packed byte needs a 64 KB window
 // (entry e at window + e*256, the byte lands in address bits 8..15 straight
-// from v_perm); at most two such tables are live (4-bit keys, 4-bit values,
-// sign patterns).  Tables indexed by a 6-bit field (3-bit codes) hold 64
-// entries (16 KB) and sit above 128 KB, followed by the wave-merge buffer.
+// from v_perm); at most two such tables are live (one per tensor).  Tables
+// indexed by a 6-bit field (3-bit codes without a sketch) hold 64 entries
+// (16 KB) and sit above, followed by the wave-merge buffer.
 // Replication per table (chosen by measurement of read throughput):
-//   value pairs  fp16x2  b32   one copy per lane      (lane * 4)
-//   key pairs    fp32x2  b64   a copy per lane % 32   ((lane & 31) * 8)
-//   key quads    fp32x4  b128  a copy per lane % 16   ((lane & 15) * 16), 2-bit keys
-//   sign bytes   fp16x8  b128  a copy per lane % 16   ((lane & 15) * 16)
+//   value pairs        fp16x2            b32   one copy per lane      (lane * 4)
+//   sketched values    fp16x2 + 2 signs  b64   a copy per lane % 32   ((lane & 31) * 8)
+//   key pairs          fp32x2            b64   a copy per lane % 32   ((lane & 31) * 8)
+//   sketched keys      fp32x2 + 2 signs  b128  a copy per lane % 16   ((lane & 15) * 16)
+//   key quads          fp32x4            b128  a copy per lane % 16   ((lane & 15) * 16), 2-bit keys
+// A sketched tensor stores per coordinate a 4-bit field, 3-bit code | sign << 3
+// (the sign of the same-index sketch row), so a byte holds two of them.
 // KB == 2 is the HeadQ base (with its side code).
 template <int D, int KB, bool KQ, int VB, bool VQ>
 struct LutMap {
-  static constexpr bool kSigns = KQ || VQ;
-  static constexpr bool kKeyByte = KB == 4 || KB == 2;
-  static constexpr uint32_t nbyte_tables = kKeyByte + (VB == 4) + kSigns;
+  static constexpr bool kKeyByte = KB == 4 || KB == 2 || KQ;
+  static constexpr bool kValByte = VB == 4 || VQ;
+  static constexpr bool kKeySix = KB == 3 && !KQ, kValSix = VB == 3 && !VQ;
+  static constexpr uint32_t nbyte_tables = kKeyByte + kValByte;
   static constexpr uint32_t six_base = 0x10000u * nbyte_tables;
   static constexpr uint32_t k_base = kKeyByte ? 0u : six_base;
-  static constexpr uint32_t v_base = VB == 4 ? (kKeyByte ? 0x10000u : 0u) : six_base + (KB == 3 ? 0x4000u : 0u);
-  static constexpr uint32_t s_base = 0x10000u * (kKeyByte + (VB == 4));
-  static constexpr uint32_t merge = six_base + 0x4000u * ((KB == 3) + (VB == 3));
+  static constexpr uint32_t v_base = kValByte ? (kKeyByte ? 0x10000u : 0u) : six_base + (kKeySix ? 0x4000u : 0u);
+  static constexpr uint32_t merge = six_base + 0x4000u * (kKeySix + kValSix);
   // The wave-merge buffer exists at d = 128 only; wider heads write one
   // partial per wave and leave the merge to the combine step.
   static constexpr uint32_t bytes = merge + (D == 128 ? kMaxLutWaves * (2 + 2 * 128) * 4 + 256 : 0);
@@ -83,6 +84,7 @@ constexpr float kSlack = 8.0f;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -148,12 +150,15 @@ __device__ __forceinline__ float tok_sum(float v) {
   return v;
 }
 
+// Dwords per lane per token: b-bit codes, or 4-bit (code, sign) fields.
+template <int B, bool Q>
+constexpr int lane_dwords() { return Q ? B + 1 : B; }
+
 template <int KB, bool KQ, int VB, bool VQ>
 struct TokenData {
-  uint32_t k[KB];
-  uint32_t ks;   // key signs (KQ) or the HeadQ side-code dword (KB == 2)
-  uint32_t v[VB];
-  uint32_t vs;   // value signs (VQ)
+  uint32_t k[lane_dwords<KB, KQ>()];
+  uint32_t ks;   // the HeadQ side-code dword (KB == 2)
+  uint32_t v[lane_dwords<VB, VQ>()];
   float sc;      // this lane's per-token scalar (lane j: nu_k, gamma_k, nu_v, gamma_v)
 };
 
@@ -161,8 +166,7 @@ struct TokenData {
 struct HeadPlanes {
   const uint8_t* kc;
   const uint8_t* vc;
-  const uint8_t* ks;  // key signs, or the HeadQ side codes (KB == 2)
-  const uint8_t* vs;
+  const uint8_t* ks;  // the HeadQ side codes (KB == 2)
 };
 
 // A 32-bit lane offset the compiler keeps as is, so that loads take the
@@ -184,8 +188,9 @@ __device__ __forceinline__ uint32_t token_bytes(uint32_t tr) {
 template <int D, int KB, bool KQ, int VB, bool VQ>
 __device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int j, const float* sc_head,
                                            TokenData<KB, KQ, VB, VQ>& t) {
-  const uint32_t* kc = reinterpret_cast<const uint32_t*>(h.kc + lane_off(token_bytes<(uint32_t)D * KB / 8>(tr) + (uint32_t)j * (4u * KB)));
-  if constexpr (KB == 4) {
+  constexpr int KW = lane_dwords<KB, KQ>(), VW = lane_dwords<VB, VQ>();
+  const uint32_t* kc = reinterpret_cast<const uint32_t*>(h.kc + lane_off(token_bytes<(uint32_t)D * KW / 8>(tr) + (uint32_t)j * (4u * KW)));
+  if constexpr (KW == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc));
     t.k[0] = x.x; t.k[1] = x.y; t.k[2] = x.z; t.k[3] = x.w;
   } else if constexpr (KB == 2) {
@@ -195,18 +200,16 @@ __device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int
     t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.ks + lane_off(tr * 8u + (uint32_t)(j >> 1) * 4u)));
   } else {
 #pragma unroll
-    for (int i = 0; i < KB; ++i) t.k[i] = __builtin_nontemporal_load(kc + i);
+    for (int i = 0; i < KW; ++i) t.k[i] = __builtin_nontemporal_load(kc + i);
   }
-  const uint32_t* vc = reinterpret_cast<const uint32_t*>(h.vc + lane_off(token_bytes<(uint32_t)D * VB / 8>(tr) + (uint32_t)j * (4u * VB)));
-  if constexpr (VB == 4) {
+  const uint32_t* vc = reinterpret_cast<const uint32_t*>(h.vc + lane_off(token_bytes<(uint32_t)D * VW / 8>(tr) + (uint32_t)j * (4u * VW)));
+  if constexpr (VW == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc));
     t.v[0] = x.x; t.v[1] = x.y; t.v[2] = x.z; t.v[3] = x.w;
   } else {
 #pragma unroll
-    for (int i = 0; i < VB; ++i) t.v[i] = __builtin_nontemporal_load(vc + i);
+    for (int i = 0; i < VW; ++i) t.v[i] = __builtin_nontemporal_load(vc + i);
   }
-  if (KQ) t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.ks + lane_off(token_bytes<(uint32_t)D / 8>(tr) + (uint32_t)j * 4u)));
-  if (VQ) t.vs = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.vs + lane_off(token_bytes<(uint32_t)D / 8>(tr) + (uint32_t)j * 4u)));
   t.sc = __builtin_nontemporal_load(sc_head + tr);
 }
 
@@ -224,7 +227,19 @@ void decode_lut_kernel(DecodeParams p) {
 
   // ---- tables -------------------------------------------------------------------
   {
-    constexpr int NV = VB == 4 ? 256 : 64;
+    if constexpr (VQ) {
+      // Byte e = (code0 | s0 << 3) | (code1 | s1 << 3) << 4: both centroids and both signs.
+      for (int i = threadIdx.x; i < 256 * 32; i += kLutThreads) {
+        const int e = i >> 5, l = i & 31;
+        half4_t h;
+        h.x = (_Float16)p.vc[e & 7];
+        h.y = (_Float16)p.vc[(e >> 4) & 7];
+        h.z = (e & 8) ? (_Float16)1.0f : (_Float16)-1.0f;
+        h.w = (e & 128) ? (_Float16)1.0f : (_Float16)-1.0f;
+        *reinterpret_cast<half4_t*>(smem + Map::v_base + e * 256 + l * 8) = h;
+      }
+    }
+    constexpr int NV = VQ ? 0 : (VB == 4 ? 256 : 64);
     for (int i = threadIdx.x; i < NV * 64; i += kLutThreads) {
       const int e = i >> 6, l = i & 63;
       const int lo = VB == 4 ? (e & 15) : (e & 7), hi = VB == 4 ? (e >> 4) : (e >> 3);
@@ -244,7 +259,22 @@ void decode_lut_kernel(DecodeParams p) {
         *reinterpret_cast<float4_t*>(smem + Map::k_base + e * 256 + l * 16) = c;
       }
     }
-    constexpr int NK = KB == 4 ? 256 : (KB == 3 ? 64 : 0);
+    if constexpr (KQ) {
+      // Byte e as for sketched values: fp32 centroids, fp16 signs in z.
+      for (int i = threadIdx.x; i < 256 * 16; i += kLutThreads) {
+        const int e = i >> 4, l = i & 15;
+        half2_t sg;
+        sg.x = (e & 8) ? (_Float16)1.0f : (_Float16)-1.0f;
+        sg.y = (e & 128) ? (_Float16)1.0f : (_Float16)-1.0f;
+        float4_t c;
+        c.x = p.kc[e & 7];
+        c.y = p.kc[(e >> 4) & 7];
+        c.z = __builtin_bit_cast(float, sg);
+        c.w = 0.f;
+        *reinterpret_cast<float4_t*>(smem + Map::k_base + e * 256 + l * 16) = c;
+      }
+    }
+    constexpr int NK = KB == 4 ? 256 : (Map::kKeySix ? 64 : 0);
     for (int i = threadIdx.x; i < NK * 32; i += kLutThreads) {
       const int e = i >> 5, l = i & 31;
       const int lo = KB == 4 ? (e & 15) : (e & 7), hi = KB == 4 ? (e >> 4) : (e >> 3);
@@ -253,21 +283,11 @@ void decode_lut_kernel(DecodeParams p) {
       c.y = p.kc[hi];
       *reinterpret_cast<float2_t*>(smem + Map::k_base + e * 256 + l * 8) = c;
     }
-    if (KQ || VQ) {
-      for (int i = threadIdx.x; i < 256 * 16; i += kLutThreads) {
-        const int e = i >> 4, l = i & 15;
-        half8_t s;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) s[t] = ((e >> t) & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
-        *reinterpret_cast<half8_t*>(smem + Map::s_base + e * 256 + l * 16) = s;
-      }
-    }
   }
   __syncthreads();
 
-  const uint32_t lr_v = Map::v_base | ((uint32_t)lane * 4u);
-  const uint32_t lr_k = KB == 2 ? (Map::k_base | ((uint32_t)(lane & 15) << 4)) : (Map::k_base | ((uint32_t)(lane & 31) << 3));
-  const uint32_t lr_s = Map::s_base | ((uint32_t)(lane & 15) << 4);
+  const uint32_t lr_v = VQ ? (Map::v_base | ((uint32_t)(lane & 31) << 3)) : (Map::v_base | ((uint32_t)lane * 4u));
+  const uint32_t lr_k = (KB == 2 || KQ) ? (Map::k_base | ((uint32_t)(lane & 15) << 4)) : (Map::k_base | ((uint32_t)(lane & 31) << 3));
   // Lane j of a quad streams one per-token scalar: 0 nu_k, 1 gamma_k (or the
   // HeadQ side scale), 2 nu_v, 3 gamma_v.
   // (Lanes j >= 4 of wider groups load a norm they do not use.)
@@ -288,13 +308,12 @@ void decode_lut_kernel(DecodeParams p) {
     const int t0 = split * p.chunk, t1 = min(Tb, t0 + p.chunk);
     const size_t vbase = (size_t)bkv * p.T_cap;
     HeadPlanes hp;
-    hp.kc = p.k.codes + vbase * (D * KB / 8);
-    hp.vc = p.v.codes + vbase * (D * VB / 8);
-    hp.ks = KQ ? p.k.qjl + vbase * (D / 8) : (KB == 2 ? p.k.side + vbase * 8 : nullptr);
-    hp.vs = VQ ? p.v.qjl + vbase * (D / 8) : nullptr;
+    hp.kc = p.k.codes + vbase * (D * lane_dwords<KB, KQ>() / 8);
+    hp.vc = p.v.codes + vbase * (D * lane_dwords<VB, VQ>() / 8);
+    hp.ks = KB == 2 ? p.k.side + vbase * 8 : nullptr;
     const float* sc_head = sc_src + vbase;
 
-    constexpr bool kUDot = KQ && VQ;
+    constexpr bool kUDot = KQ && (VQ || D == 128);
     float q[32], u[KQ && !kUDot ? 32 : 1];
 #pragma unroll
     for (int e = 0; e < 32; ++e) q[e] = p.qrot[(size_t)qi * d + 32 * j + e];
@@ -352,8 +371,35 @@ void decode_lut_kernel(DecodeParams p) {
       const bool valid = t < t1;
 
       // ---- key score: this lane's 32 coordinates ---------------------------------
-      float sa = 0.f, sb = 0.f;
-      if constexpr (KB == 2) {
+      float sa = 0.f, sb = 0.f, pa = 0.f, pb = 0.f;
+      if constexpr (KQ) {
+        // Byte BB of dword w: coordinates (and sketch rows) 8 w + 2 BB, + 1.
+        // The entry is read as float4 and the sign pair taken out of it through
+        // an opaque copy: with bit casts of the elements of a 128-bit integer
+        // read (or of the sign element of a float4 read), this compiler
+        // (AMD clang 22, ROCm 7.2) fed element 0 to the later uses.
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#define TQ_KQBYTE(BB)                                                                          \
+          {                                                                                    \
+            const float4_t c = *reinterpret_cast<const float4_t*>(smem + byte_addr<BB>(cur.k[w], lr_k)); \
+            sa = fmaf(q[8 * w + 2 * BB], c.x, sa);                                             \
+            sb = fmaf(q[8 * w + 2 * BB + 1], c.y, sb);                                         \
+            uint32_t sgw = __float_as_uint(c.z);                                               \
+            asm volatile("" : "+v"(sgw));                                                      \
+            const half2_t sg = __builtin_bit_cast(half2_t, sgw);                               \
+            if constexpr (kUDot) {                                                             \
+              if ((BB) & 1) pb = __builtin_amdgcn_fdot2(uh[4 * w + BB], sg, pb, false);        \
+              else pa = __builtin_amdgcn_fdot2(uh[4 * w + BB], sg, pa, false);                 \
+            } else {                                                                           \
+              pa = fmaf(u[8 * w + 2 * BB], (float)sg.x, pa);                                   \
+              pb = fmaf(u[8 * w + 2 * BB + 1], (float)sg.y, pb);                               \
+            }                                                                                  \
+          }
+          TQ_KQBYTE(0) TQ_KQBYTE(1) TQ_KQBYTE(2) TQ_KQBYTE(3)
+#undef TQ_KQBYTE
+        }
+      } else if constexpr (KB == 2) {
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
 #define TQ_K2BYTE(BB)                                                                          \
@@ -402,24 +448,6 @@ void decode_lut_kernel(DecodeParams p) {
         part = fmaf(tok_bcast<L, 1>(cur.sc, lane), cs, part);
       }
       if (KQ) {
-        float pa = 0.f, pb = 0.f;
-#define TQ_KSIGN(BB)                                                                           \
-        {                                                                                      \
-          const half8_t s = *reinterpret_cast<const half8_t*>(smem + byte_addr<BB>(cur.ks, lr_s)); \
-          if constexpr (kUDot) {                                                               \
-            pa = __builtin_amdgcn_fdot2(uh[4 * BB], s.s01, pa, false);                         \
-            pb = __builtin_amdgcn_fdot2(uh[4 * BB + 1], s.s23, pb, false);                     \
-            pa = __builtin_amdgcn_fdot2(uh[4 * BB + 2], s.s45, pa, false);                     \
-            pb = __builtin_amdgcn_fdot2(uh[4 * BB + 3], s.s67, pb, false);                     \
-          } else {                                                                             \
-            _Pragma("unroll") for (int t = 0; t < 8; t += 2) {                                 \
-              pa = fmaf(u[8 * BB + t], (float)s[t], pa);                                       \
-              pb = fmaf(u[8 * BB + t + 1], (float)s[t + 1], pb);                               \
-            }                                                                                  \
-          }                                                                                    \
-        }
-        TQ_KSIGN(0) TQ_KSIGN(1) TQ_KSIGN(2) TQ_KSIGN(3)
-#undef TQ_KSIGN
         const float g_k = tok_bcast<L, 1>(cur.sc, lane);
         part = fmaf(nu_k * uscale * g_k, pa + pb, part);
       }
@@ -445,7 +473,23 @@ void decode_lut_kernel(DecodeParams p) {
       const float wv = pt * tok_bcast<L, 2>(cur.sc, lane);
 
       // ---- value accumulation -----------------------------------------------------
-      if (VB == 4) {
+      if constexpr (VQ) {
+        // Byte BB of dword w: coordinates (and sketch rows) 8 w + 2 BB, + 1.
+        const float wq = wv * tok_bcast<L, 3>(cur.sc, lane);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+#define TQ_VQBYTE(BB)                                                                          \
+          {                                                                                    \
+            const half4_t h = *reinterpret_cast<const half4_t*>(smem + byte_addr<BB>(cur.v[w], lr_v)); \
+            acc[8 * w + 2 * BB] = fmaf(wv, (float)h.x, acc[8 * w + 2 * BB]);                   \
+            acc[8 * w + 2 * BB + 1] = fmaf(wv, (float)h.y, acc[8 * w + 2 * BB + 1]);           \
+            ask[8 * w + 2 * BB] = fmaf(wq, (float)h.z, ask[8 * w + 2 * BB]);                   \
+            ask[8 * w + 2 * BB + 1] = fmaf(wq, (float)h.w, ask[8 * w + 2 * BB + 1]);           \
+          }
+          TQ_VQBYTE(0) TQ_VQBYTE(1) TQ_VQBYTE(2) TQ_VQBYTE(3)
+#undef TQ_VQBYTE
+        }
+      } else if (VB == 4) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
 #define TQ_VBYTE(BB)                                                                           \
@@ -468,17 +512,6 @@ void decode_lut_kernel(DecodeParams p) {
         TQ_VPAIR(0) TQ_VPAIR(1) TQ_VPAIR(2) TQ_VPAIR(3) TQ_VPAIR(4) TQ_VPAIR(5) TQ_VPAIR(6) TQ_VPAIR(7)
         TQ_VPAIR(8) TQ_VPAIR(9) TQ_VPAIR(10) TQ_VPAIR(11) TQ_VPAIR(12) TQ_VPAIR(13) TQ_VPAIR(14) TQ_VPAIR(15)
 #undef TQ_VPAIR
-      }
-      if (VQ) {
-        const float wq = wv * tok_bcast<L, 3>(cur.sc, lane);
-#define TQ_VSIGN(BB)                                                                           \
-        {                                                                                      \
-          const half8_t sg = *reinterpret_cast<const half8_t*>(smem + byte_addr<BB>(cur.vs, lr_s)); \
-          _Pragma("unroll") for (int t = 0; t < 8; ++t)                                        \
-            ask[8 * BB + t] = fmaf(wq, (float)sg[t], ask[8 * BB + t]);                         \
-        }
-        TQ_VSIGN(0) TQ_VSIGN(1) TQ_VSIGN(2) TQ_VSIGN(3)
-#undef TQ_VSIGN
       }
     };
 

@@ -40,6 +40,23 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int i) {
   return v & ((1u << BITS) - 1u);
 }
 
+// PROD stores index i as one (b+1)-bit field, code | sign << b, where the
+// sign is bit i of the QJL sketch; a 32-index group is b+1 dwords.
+template <int BITS, bool SKETCH>
+struct Field {
+  static constexpr int kBits = BITS + (SKETCH ? 1 : 0);   // field width
+  static constexpr uint32_t kCodeMask = (1u << BITS) - 1u;
+};
+
+// The 32 sign bits of a group of (BITS+1)-bit fields held in `w`.
+template <int BITS>
+__device__ __forceinline__ uint32_t sign_word(const uint32_t* w) {
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) s |= (code_at<BITS + 1>(w, i) >> BITS) << i;
+  return s;
+}
+
 // Load 32 consecutive input elements (fp16 or fp32) as float.
 template <typename T>
 __device__ __forceinline__ void load32(const T* src, float* v);

@@ -171,23 +171,25 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
       for (int k = 0; k < NB; ++k) c += (v[e] >= s_bnd[k]) ? 1u : 0u;
       idx[e] = nu > 0.f ? c : 0u;
     }
-    uint32_t w[BITS];
+    // PROD: (BITS+1)-bit fields whose sign bits sign_pack_kernel fills in.
+    constexpr int FB = Field<BITS, MODE == TQ_MODE_PROD>::kBits;
+    uint32_t w[FB];
 #pragma unroll
-    for (int k = 0; k < BITS; ++k) w[k] = 0;
+    for (int k = 0; k < FB; ++k) w[k] = 0;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      const int bit = BITS * e, wi = bit >> 5, sh = bit & 31;
+      const int bit = FB * e, wi = bit >> 5, sh = bit & 31;
       w[wi] |= idx[e] << sh;
-      if (sh + BITS > 32) w[wi + 1] |= idx[e] >> (32 - sh);
+      if (sh + FB > 32) w[wi + 1] |= idx[e] >> (32 - sh);
     }
     // Destination slot: t, or pos[b] + t when appending; never outside [0, T_cap).
     const int64_t tw = slot0 + t;
     const bool wr = valid && tw >= 0 && tw < p.T_cap;
     const int64_t vec = vbase + tw;
     if (wr) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vec * (d * BITS / 8)) + j * BITS;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vec * (d * FB / 8)) + j * FB;
 #pragma unroll
-      for (int k = 0; k < BITS; ++k) __builtin_nontemporal_store(w[k], dst + k);
+      for (int k = 0; k < FB; ++k) __builtin_nontemporal_store(w[k], dst + k);
       if (j == 0) __builtin_nontemporal_store(nu, p.norms + vec);
     }
 
@@ -258,20 +260,24 @@ __global__ __launch_bounds__(kThreads) void relerr_kernel(RelErrParams p) {
 #pragma unroll
       for (int e = 0; e < 32; ++e) a[e] *= p.inv_sqrt_d;
     }
-    uint32_t w[BITS];
-    const uint32_t* cw = reinterpret_cast<const uint32_t*>(p.planes.codes + vec * (d * BITS / 8)) + j * BITS;
+    constexpr int FB = Field<BITS, MODE == TQ_MODE_PROD>::kBits;
+    uint32_t w[FB];
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(p.planes.codes + vec * (d * FB / 8)) + j * FB;
 #pragma unroll
-    for (int k = 0; k < BITS; ++k) w[k] = cw[k];
+    for (int k = 0; k < FB; ++k) w[k] = cw[k];
     const float nu = p.planes.norms[vec];
     float ah[32];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) ah[e] = s_cent[code_at<BITS>(w, e)];
+    for (int e = 0; e < 32; ++e) ah[e] = s_cent[code_at<FB>(w, e) & Field<BITS, false>::kCodeMask];
     if (MODE == TQ_MODE_PROD) {
-      // y_hat += sqrt(pi/2)/m gamma S^T sigma
+      // y_hat += sqrt(pi/2)/m gamma S^T sigma, sigma from every group's fields
       const float g = p.planes.gamma[vec] * p.qjl_c;
-      const uint32_t* sb = reinterpret_cast<const uint32_t*>(p.planes.qjl + vec * (d / 8));
+      const uint32_t* vf = reinterpret_cast<const uint32_t*>(p.planes.codes + vec * (d * FB / 8));
       for (int iw = 0; iw < d / 32; ++iw) {
-        const uint32_t bits = sb[iw];
+        uint32_t gw[FB];
+#pragma unroll
+        for (int k = 0; k < FB; ++k) gw[k] = vf[iw * FB + k];
+        const uint32_t bits = sign_word<BITS>(gw);
         for (int ib = 0; ib < 32; ++ib) {
           const float sg = ((bits >> ib) & 1u) ? g : -g;
           const float* srow = p.S + (size_t)(32 * iw + ib) * d + 32 * j;
@@ -345,7 +351,9 @@ __global__ __launch_bounds__(kThreads) void rotate_basis_kernel(QuantParams p, f
   }
 }
 
-// Sign bits of P rows: one thread per (row, 32-bit word).
+// Sign bits of P rows, one thread per (row, 32-row group): bit k of the group
+// goes to bit (b+1) k + b of the group's (b+1)-bit fields, whose codes the
+// quantize kernel wrote (stream order makes them visible here).
 __global__ __launch_bounds__(256) void sign_pack_kernel(const float* __restrict__ P, QuantParams p) {
   const int d = p.d, words = d / 32;
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -359,11 +367,17 @@ __global__ __launch_bounds__(256) void sign_pack_kernel(const float* __restrict_
   if (tw < 0 || tw >= p.T_cap) return;
   const int64_t vec = (int64_t)bh * p.T_cap + tw;
   const float* pr = P + row * d + 32 * w;
-  uint32_t bits = 0;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) bits |= (pr[k] >= 0.f ? 1u : 0u) << k;
-  if (!(p.norms[vec] > 0.f)) bits = 0;
-  __builtin_nontemporal_store(bits, reinterpret_cast<uint32_t*>(p.qjl + vec * (d / 8)) + w);
+  const int fb = p.bits + 1;
+  uint32_t* grp = reinterpret_cast<uint32_t*>(p.codes + vec * (d * fb / 8)) + w * fb;
+  uint32_t f[8];
+  for (int k = 0; k < fb; ++k) f[k] = grp[k];
+  if (p.norms[vec] > 0.f) {
+    for (int k = 0; k < 32; ++k) {
+      const int bit = fb * k + p.bits;
+      f[bit >> 5] |= (pr[k] >= 0.f ? 1u : 0u) << (bit & 31);
+    }
+  }
+  for (int k = 0; k < fb; ++k) __builtin_nontemporal_store(f[k], grp + k);
 }
 
 template <int BITS, int MODE>

@@ -321,9 +321,11 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
     }
 
     // ---- index and packing ----------------------------------------------------------
-    uint32_t words[BITS];
+    // PROD: (BITS+1)-bit fields, the sign bits filled in after the sketch.
+    constexpr int FB = kProd ? BITS + 1 : BITS;
+    uint32_t words[FB];
 #pragma unroll
-    for (int k = 0; k < BITS; ++k) words[k] = 0;
+    for (int k = 0; k < FB; ++k) words[k] = 0;
 #define TQ_QIDX(I, A)                                                                          \
     {                                                                                          \
       const float yy = y[I][A];                                                                \
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       const LutEntry e = *reinterpret_cast<const LutEntry*>(                                   \
           lut_bytes + ((__float_as_uint(f) << 3) - (0x4B400000u << 3)));                       \
       const uint32_t idx = e.base + (yy >= e.t ? 1u : 0u);                                     \
-      put_index<BITS, 8 * (I) + (A)>(words, idx);                                              \
+      put_index<FB, 8 * (I) + (A)>(words, idx);                                                \
       y[I][A] = (kProd || kHeadq) ? yy - s_cent[idx] : yy;                                     \
     }
 #define TQ_QROW(I) TQ_QIDX(I, 0) TQ_QIDX(I, 1) TQ_QIDX(I, 2) TQ_QIDX(I, 3) \
@@ -342,27 +344,28 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
 
     // Per-head planes: scalar base + 32-bit lane offset.
     const size_t vbase = (size_t)bh * p.T_cap;
-    if (wr) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vbase * (16 * BITS) +
-                                                  (uint32_t)(tw * (16 * BITS) + g * (4 * BITS)));
+    auto store_codes = [&]() {
+      if (!wr) return;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vbase * (16 * FB) + (uint32_t)(tw * (16 * FB) + g * (4 * FB)));
       if (!(nu > 0.f)) {
 #pragma unroll
-        for (int k = 0; k < BITS; ++k) words[k] = 0;
+        for (int k = 0; k < FB; ++k) words[k] = 0;
       }
-      if (BITS == 4) {
+      if constexpr (FB == 4) {
         u32x4 w4 = {words[0], words[1], words[2], words[3]};
         __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(dst));
-      } else if (BITS == 3) {
+      } else if constexpr (FB == 3) {
         u32x3 w3 = {words[0], words[1], words[2]};
         __builtin_nontemporal_store(w3, reinterpret_cast<u32x3*>(dst));
-      } else if (BITS == 2) {
+      } else if constexpr (FB == 2) {
         u32x2 w2 = {words[0], words[1]};
         __builtin_nontemporal_store(w2, reinterpret_cast<u32x2*>(dst));
       } else {
         __builtin_nontemporal_store(words[0], dst);
       }
       if (g == 0) __builtin_nontemporal_store(nu, p.norms + vbase + tw);
-    }
+    };
+    if constexpr (!kProd) store_codes();
 
     if constexpr (kHeadq) {
       // ---- HeadQ side code ([P3] section 3) ----------------------------------------
@@ -458,30 +461,52 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
           Blo[pp][j] = lo.x; Blo[pp][j + 1] = lo.y;
         }
       }
-      // Row block mb gives lane (g, tau) sketch rows 32 g + 4 mb + i, i < 4:
-      // bits 4 mb + i of the lane's sign word.  Two blocks in flight at a time
-      // keep the S operands (LDS reads) from all being hoisted into registers.
-      // Rows are visited from 31 down, each shifting its product's sign bit in
-      // at the bottom; the bit is [p >= 0], the complement of the sign bit
-      // (they differ only at p = -0, where p is exactly zero).
-      uint32_t sneg = 0;
-#pragma unroll 2
-      for (int mb = 7; mb >= 0; --mb) {
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
+      // Row block mb gives lane (g, tau) sketch rows 32 g + 4 mb + i, i < 4,
+      // whose sign bit is bit [p >= 0], the complement of the product's sign
+      // bit (they differ only at p = -0, where p is exactly zero).  Two
+      // blocks in flight at a time keep the S operands (LDS reads) from all
+      // being hoisted into registers.  Rows are visited from 31 down.
+      //   4-bit fields: each row's sign bit is funnel-shifted in 4 bits at a
+      //   time (with 3 bits of exponent below it, masked off), so that rows
+      //   8 w .. 8 w + 7 end in nibbles 0 .. 7 of cur; the four dwords roll
+      //   through sx0..sx3.  Other widths: one bit per row, spread after.
+      uint32_t sx0 = 0, sx1 = 0, sx2 = 0, sx3 = 0, sneg = 0;
+#pragma unroll 1
+      for (int t = 3; t >= 0; --t) {
+        uint32_t cur = 0;
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const half8 A = s_S[(mb * 4 + pp) * 64 + lane];
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bhi[pp], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Blo[pp], acc, 0, 0, 0);
+        for (int h = 1; h >= 0; --h) {
+          const int mb = 2 * t + h;
+          float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const half8 A = s_S[(mb * 4 + pp) * 64 + lane];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bhi[pp], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Blo[pp], acc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 3; i >= 0; --i) {
+            if constexpr (FB == 4) cur = __builtin_amdgcn_alignbit(cur, __float_as_uint(acc[i]), 28);
+            else sneg = __builtin_amdgcn_alignbit(sneg, __float_as_uint(acc[i]), 31);
+          }
         }
+        sx3 = sx2; sx2 = sx1; sx1 = sx0; sx0 = cur;
+      }
+      if constexpr (FB == 4) {
+        words[0] |= ~sx0 & 0x88888888u;
+        words[1] |= ~sx1 & 0x88888888u;
+        words[2] |= ~sx2 & 0x88888888u;
+        words[3] |= ~sx3 & 0x88888888u;
+      } else {
+        const uint32_t sbits = ~sneg;
 #pragma unroll
-        for (int i = 3; i >= 0; --i) sneg = __builtin_amdgcn_alignbit(sneg, __float_as_uint(acc[i]), 31);
+        for (int o = 0; o < 32; ++o) {
+          const int bit = FB * o + BITS;
+          words[bit >> 5] |= ((sbits >> o) & 1u) << (bit & 31);
+        }
       }
-      if (wr) {
-        __builtin_nontemporal_store(nu > 0.f ? ~sneg : 0u,
-                                    reinterpret_cast<uint32_t*>(p.qjl + vbase * 16 + (uint32_t)(tw * 16 + g * 4)));
-        if (g == 0) __builtin_nontemporal_store(nu > 0.f ? sqrtf(g2) * (1.0f / 4096.0f) : 0.f, p.gamma + vbase + tw);
-      }
+      store_codes();
+      if (wr && g == 0) __builtin_nontemporal_store(nu > 0.f ? sqrtf(g2) * (1.0f / 4096.0f) : 0.f, p.gamma + vbase + tw);
     }
   }
 }

@@ -191,7 +191,7 @@ class PackedTensor:
 
         self.codes = plane(n * lay.code_bytes)
         self.norms = plane(n * 4)
-        self.qjl = plane(n * lay.qjl_bytes) if lay.qjl_bytes else None
+        self.qjl = None   # PROD keeps its sign bits in the code fields (qjl_bytes is 0)
         self.gamma = plane(n * 4) if lay.has_gamma else None
         self.side = plane(n * lay.side_bytes) if lay.side_bytes else None
         self.side_scale = plane(n * 4) if lay.has_side_scale else None
@@ -200,7 +200,7 @@ class PackedTensor:
         self.c.T_cap = T_cap
         self.c.codes = self.codes.data_ptr()
         self.c.norms = self.norms.data_ptr()
-        self.c.qjl = self.qjl.data_ptr() if self.qjl is not None else None
+        self.c.qjl = None
         self.c.gamma = self.gamma.data_ptr() if self.gamma is not None else None
         self.c.side = self.side.data_ptr() if self.side is not None else None
         self.c.side_scale = self.side_scale.data_ptr() if self.side_scale is not None else None
@@ -218,8 +218,7 @@ class PackedTensor:
         lay = self.layout
         v.c.codes = self.c.codes + off * lay.code_bytes
         v.c.norms = self.c.norms + off * 4
-        if self.c.qjl:
-            v.c.qjl = self.c.qjl + off * lay.qjl_bytes
+        if self.c.gamma:
             v.c.gamma = self.c.gamma + off * 4
         if self.c.side:
             v.c.side = self.c.side + off * lay.side_bytes
@@ -239,8 +238,7 @@ class PackedTensor:
         n = self.n
         out = {"codes": self.codes[: n * self.layout.code_bytes].cpu().numpy().reshape(n, -1),
                "norms": self.norms[: n * 4].cpu().numpy().view(np.float32).copy()}
-        if self.qjl is not None:
-            out["qjl"] = self.qjl[: n * self.layout.qjl_bytes].cpu().numpy().reshape(n, -1)
+        if self.gamma is not None:
             out["gamma"] = self.gamma[: n * 4].cpu().numpy().view(np.float32).copy()
         if self.side is not None:
             out["side"] = self.side[: n * self.layout.side_bytes].cpu().numpy().reshape(n, -1)

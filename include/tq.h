@@ -31,10 +31,14 @@
  *
  * Packed cache (one tq_packed per tensor, K or V)
  *   Vector index v = (b*H + h)*T_cap + t.  Structure-of-arrays planes:
- *     codes      uint8 [v][d*bits/8]   Lloyd-Max indices, LSB-first bitstream:
- *                                      coordinate i in bits [bits*i, bits*i+bits)
+ *     codes      uint8 [v][d*w/8]      LSB-first bitstream of d fields of w bits,
+ *                                      field i in bits [w*i, w*i+w):
+ *                                        PLAIN, MSE, HEADQ: w = bits, the
+ *                                          Lloyd-Max index of coordinate i;
+ *                                        PROD: w = bits+1, that index | s_i << bits
+ *                                          with s_i = [(S r)_i >= 0], the QJL
+ *                                          sign of sketch row i (m = d)
  *     norms      fp32  [v]             ||x||
- *     qjl        uint8 [v][d/8]        PROD: bit i = [(S r)_i >= 0]
  *     gamma      fp32  [v]             PROD: ||r||
  *     side       uint8 [v][rank*side_bits/8]  HEADQ side code, LSB-first
  *     side_scale fp32  [v]             HEADQ: s_z
@@ -50,7 +54,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 2
+#define TQ_ABI_VERSION 3
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -99,7 +103,7 @@ typedef struct tq_tensor_desc {
 /* Bytes per vector of each plane. */
 typedef struct tq_layout {
   int32_t code_bytes;
-  int32_t qjl_bytes;   /* 0 unless PROD  */
+  int32_t qjl_bytes;   /* 0: PROD keeps its sign bits in the code fields */
   int32_t side_bytes;  /* 0 unless HEADQ */
   int32_t has_gamma;
   int32_t has_side_scale;
@@ -124,7 +128,7 @@ typedef struct tq_packed {
   uint64_t seed;
   uint8_t* codes;
   float* norms;
-  uint8_t* qjl;
+  uint8_t* qjl;       /* unused (the sign bits live in the code fields) */
   float* gamma;
   uint8_t* side;
   float* side_scale;

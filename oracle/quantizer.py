@@ -21,9 +21,12 @@ The constant sqrt(pi/2)/m is the one that makes the sketch estimate of the
 residual unbiased ([P1] "Contribuciones Clave" 1: the QJL estimator is
 unbiased), because E[s sign(s.r)] = sqrt(2/pi) r/||r|| for s ~ N(0, I).
 
-Packing: per vector a little-endian LSB-first bitstream; coordinate i
-occupies bits [b i, b i + b) of the code block (d b / 8 bytes); sign bit i is
-bit i of the m/8-byte sign block.
+Packing: per vector a little-endian LSB-first bitstream of d fields.  MSE
+and PLAIN: field i is idx_i, b bits, at bits [b i, b i + b) of the d b / 8
+byte code block.  PROD (m = d): field i is idx_i | bit_i << b, b + 1 bits,
+at bits [(b+1) i, (b+1) i + b + 1) of the d (b+1) / 8 byte code block: the
+code of coordinate i and the sign of sketch row i side by side (the pages fix
+no layout; both are read at the same index i, see dequantize).
 """
 import math
 import numpy as np
@@ -152,9 +155,16 @@ def unpack_bits(packed, width, L):
 
 def pack(q, st):
     """Packed planes of one batch of vectors, as the cache stores them."""
-    planes = {"codes": pack_bits(q["idx"], st.base_bits),
-              "norms": q["nu"].astype(np.float32)}
     if st.mode == PROD:
-        planes["qjl"] = pack_bits(q["sign_bits"], 1)
-        planes["gamma"] = q["gamma"].astype(np.float32)
-    return planes
+        fields = np.asarray(q["idx"], dtype=np.int64) | (np.asarray(q["sign_bits"], dtype=np.int64) << st.base_bits)
+        return {"codes": pack_bits(fields, st.base_bits + 1), "norms": q["nu"].astype(np.float32),
+                "gamma": q["gamma"].astype(np.float32)}
+    return {"codes": pack_bits(q["idx"], st.base_bits), "norms": q["nu"].astype(np.float32)}
+
+
+def unpack_fields(codes, st, d):
+    """Inverse of pack's code block: (idx [N, d], sign bits [N, d] or None)."""
+    if st.mode == PROD:
+        f = unpack_bits(codes, st.base_bits + 1, d)
+        return f & ((1 << st.base_bits) - 1), f >> st.base_bits
+    return unpack_bits(codes, st.base_bits, d), None

@@ -58,7 +58,7 @@ def oracle_match(X, gpu, mode, n_bits_index, seed, U=None, side_bits=4, label=""
             (lambda **kw: oqz.quantize(X, st, **kw))
     q = quant()
     base = q["base"] if headq else q
-    g_idx = oqz.unpack_bits(gpu["codes"][:N], st.base_bits, d)
+    g_idx, g_bits = oqz.unpack_fields(gpu["codes"][:N], st, d)
     cmis = g_idx != base["idx"]
     bad = cmis & (base["bdist"] > BAND)
     assert not bad.any(), "%s: %d code mismatches outside the band (first at %s, y=%r)" % (
@@ -69,7 +69,6 @@ def oracle_match(X, gpu, mode, n_bits_index, seed, U=None, side_bits=4, label=""
         q = quant(**kw)
     ndec = N * d
     if mode == oqz.PROD:
-        g_bits = oqz.unpack_bits(gpu["qjl"][:N], 1, d)
         smis = g_bits != q["sign_bits"]
         sbad = smis & (q["sdist"] > BAND)
         assert not sbad.any(), "%s: %d sign mismatches outside the band" % (label, sbad.sum())
@@ -92,7 +91,7 @@ def oracle_match(X, gpu, mode, n_bits_index, seed, U=None, side_bits=4, label=""
         ss = gpu["side_scale"][:N].astype(np.float64)
         assert np.all(np.abs(ss - q["side_scale"]) <= 1e-5 * q["side_scale"] + 1e-9), "%s: side scale" % label
     base = q["base"] if headq else q
-    assert np.array_equal(oqz.unpack_bits(gpu["codes"][:N], st.base_bits, d), base["idx"])
+    assert np.array_equal(oqz.unpack_fields(gpu["codes"][:N], st, d)[0], base["idx"])
     nu = gpu["norms"][:N].astype(np.float64)
     assert np.all(np.abs(nu - base["nu"]) <= 1e-6 * base["nu"]), "%s: norms differ" % label
     xhat = q["khat"] if headq else oqz.dequantize(q, st)

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(tqlib):
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(tqlib.EXPORTS) == names
-    assert tqlib.lib().tq_abi_version() == 2
+    assert tqlib.lib().tq_abi_version() == 3
 
 
 @pytest.mark.parametrize("d,bits", [(32, 1), (128, 2), (128, 3), (128, 4), (1024, 2), (1024, 4)])
@@ -62,21 +62,24 @@ def test_scheme_modes_table(tqlib):
 
 
 def test_layouts(tqlib):
+    # PROD: 3-bit index + sign in 4-bit fields, no separate sign plane.
     lay = tqlib.packed_layout(128, tqlib.MODE_PROD, 3)
-    assert (lay.code_bytes, lay.qjl_bytes, lay.has_gamma) == (48, 16, 1)
+    assert (lay.code_bytes, lay.qjl_bytes, lay.has_gamma) == (64, 0, 1)
+    lay = tqlib.packed_layout(128, tqlib.MODE_PROD, 2)
+    assert (lay.code_bytes, lay.qjl_bytes, lay.has_gamma) == (48, 0, 1)
     lay = tqlib.packed_layout(128, tqlib.MODE_MSE, 4)
     assert (lay.code_bytes, lay.qjl_bytes, lay.has_gamma, lay.side_bytes) == (64, 0, 0, 0)
     lay = tqlib.packed_layout(128, tqlib.MODE_HEADQ, 2, 16, 4)
     assert (lay.code_bytes, lay.side_bytes, lay.has_side_scale) == (32, 8, 1)
     lay = tqlib.packed_layout(1024, tqlib.MODE_PROD, 3)
-    assert (lay.code_bytes, lay.qjl_bytes) == (384, 128)
+    assert (lay.code_bytes, lay.qjl_bytes) == (512, 0)
 
 
 @pytest.mark.parametrize("bad", [
     dict(d=48), dict(d=2048), dict(d=16), dict(n_bits=0), dict(n_bits=5),
     dict(scheme="kqv", which=1, n_bits=1), dict(scheme=99), dict(which=7),
     dict(dtype=9), dict(T=0), dict(B=0), dict(align=8), dict(stride_t=10),
-    dict(no_codes=True), dict(scheme="kqv", which=1, no_qjl=True),
+    dict(no_codes=True), dict(scheme="kqv", which=1, no_gamma=True),
     dict(scheme="headq", which=0, no_hq=True), dict(scheme="tq-kv", which=0, give_hq=True),
     dict(scheme="headq", which=0, hq_rank=12), dict(scheme="headq", which=0, hq_bits=1),
     dict(T_cap=3),
@@ -92,8 +95,8 @@ def test_quantize_rejects_before_any_gpu_call(tqlib, bad):
     out.T_cap = bad.get("T_cap", 0)
     out.codes = None if bad.get("no_codes") else fake
     out.norms = fake
-    out.qjl = None if bad.get("no_qjl") else fake
-    out.gamma = fake
+    out.qjl = None
+    out.gamma = None if bad.get("no_gamma") else fake
     out.side = fake
     out.side_scale = fake
     hq = None

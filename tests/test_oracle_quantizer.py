@@ -31,6 +31,28 @@ def test_pack_golden(case):
     assert np.array_equal(qz.unpack_bits(got, w, len(vals))[0], vals)
 
 
+def test_prod_fields_golden():
+    """PROD code block: field i = idx_i | sign_i << b, b + 1 bits, LSB first.
+    b = 3: (idx, sign) = (5, 1), (3, 0) -> fields 13, 3 -> byte 0x3d;
+    (7, 0), (0, 1) -> 7, 8 -> 0x87.  b = 2: (2, 1), (1, 0), (3, 1) ->
+    fields 6, 1, 7, LSB first 0 1 1 | 1 0 0 | 1 1 1 -> byte 0 =
+    2 + 4 + 8 + 64 + 128 = 0xce, byte 1 = 0x01."""
+    st = qz.QState(16, qz.PROD, 4, 0)            # n = 4: b = 3
+    assert st.base_bits == 3
+    q = {"idx": np.array([[5, 3, 7, 0] + [0] * 12]), "sign_bits": np.array([[1, 0, 0, 1] + [0] * 12]),
+         "nu": np.ones(1), "gamma": np.ones(1)}
+    pl = qz.pack(q, st)
+    assert set(pl) == {"codes", "norms", "gamma"} and pl["codes"].shape == (1, 8)
+    assert bytes(pl["codes"][0][:2]) == bytes([0x3D, 0x87])
+    idx, sb = qz.unpack_fields(pl["codes"], st, 16)
+    assert np.array_equal(idx, q["idx"]) and np.array_equal(sb, q["sign_bits"])
+    st2 = qz.QState(16, qz.PROD, 3, 0)           # n = 3: b = 2
+    q2 = {"idx": np.array([[2, 1, 3] + [0] * 13]), "sign_bits": np.array([[1, 0, 1] + [0] * 13]),
+          "nu": np.ones(1), "gamma": np.ones(1)}
+    c2 = qz.pack(q2, st2)["codes"]
+    assert c2.shape == (1, 6) and bytes(c2[0][:2]) == bytes([0xCE, 0x01])
+
+
 @pytest.mark.parametrize("w", [1, 2, 3, 4])
 def test_pack_roundtrip(w):
     v = np.random.default_rng(w).integers(0, 1 << w, size=(7, 128))

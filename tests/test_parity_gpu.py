@@ -83,7 +83,7 @@ def test_single_token_and_zero_vectors(tq, dtype):
     _, _, kp, vp, _ = _run_case(tq, K, V, Q, "qkqv", 4, label="zeros", dtype=dtype)
     pl = kp.planes()
     z = np.arange(0, 300, 7)
-    assert np.all(pl["codes"][z] == 0) and np.all(pl["qjl"][z] == 0) and np.all(pl["gamma"][z] == 0)
+    assert np.all(pl["codes"][z] == 0) and np.all(pl["gamma"][z] == 0)   # code fields hold the signs too
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
@@ -210,8 +210,9 @@ def test_fp32_input_path_matches_fp16_path(tq):
         a, b = tq.quantize(X16, which, scheme, 4, 2), tq.quantize(X32, which, scheme, 4, 2)
         torch.cuda.synchronize()
         pa, pb = a.planes(), b.planes()
-        ia = oqz.unpack_bits(pa["codes"], a.c.bits, 128)
-        ib = oqz.unpack_bits(pb["codes"], b.c.bits, 128)
+        fw = a.c.bits + (1 if a.c.mode == tq.MODE_PROD else 0)   # PROD fields carry the sign bit
+        ia = oqz.unpack_bits(pa["codes"], fw, 128)
+        ib = oqz.unpack_bits(pb["codes"], fw, 128)
         diff = ia != ib
         assert diff.mean() < pu.MAX_BAND_FRACTION, (scheme, diff.sum())
         na, nb = pa["norms"].astype(np.float64), pb["norms"].astype(np.float64)
