@@ -354,7 +354,9 @@ __global__ __launch_bounds__(kThreads) void rotate_basis_kernel(QuantParams p, f
 // Sign bits of P rows, one thread per (row, 32-row group): bit k of the group
 // goes to bit (b+1) k + b of the group's (b+1)-bit fields, whose codes the
 // quantize kernel wrote (stream order makes them visible here).
+template <int BITS>
 __global__ __launch_bounds__(256) void sign_pack_kernel(const float* __restrict__ P, QuantParams p) {
+  constexpr int FB = Field<BITS, true>::kBits;
   const int d = p.d, words = d / 32;
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long)p.nbh * p.tn * words) return;
@@ -366,18 +368,19 @@ __global__ __launch_bounds__(256) void sign_pack_kernel(const float* __restrict_
   const int64_t tw = (int64_t)t + (p.pos ? p.pos[bh / p.H] : 0);
   if (tw < 0 || tw >= p.T_cap) return;
   const int64_t vec = (int64_t)bh * p.T_cap + tw;
+  if (!(p.norms[vec] > 0.f)) return;  // a zero vector keeps all-zero fields
   const float* pr = P + row * d + 32 * w;
-  const int fb = p.bits + 1;
-  uint32_t* grp = reinterpret_cast<uint32_t*>(p.codes + vec * (d * fb / 8)) + w * fb;
-  uint32_t f[8];
-  for (int k = 0; k < fb; ++k) f[k] = grp[k];
-  if (p.norms[vec] > 0.f) {
-    for (int k = 0; k < 32; ++k) {
-      const int bit = fb * k + p.bits;
-      f[bit >> 5] |= (pr[k] >= 0.f ? 1u : 0u) << (bit & 31);
-    }
+  uint32_t* grp = reinterpret_cast<uint32_t*>(p.codes + vec * (d * FB / 8)) + w * FB;
+  uint32_t f[FB];
+#pragma unroll
+  for (int k = 0; k < FB; ++k) f[k] = grp[k];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int bit = FB * k + BITS;
+    f[bit >> 5] |= (pr[k] >= 0.f ? 1u : 0u) << (bit & 31);
   }
-  for (int k = 0; k < fb; ++k) __builtin_nontemporal_store(f[k], grp + k);
+#pragma unroll
+  for (int k = 0; k < FB; ++k) __builtin_nontemporal_store(f[k], grp + k);
 }
 
 template <int BITS, int MODE>
@@ -438,7 +441,13 @@ hipError_t launch_rotate_basis(const QuantParams& p, float* out, hipStream_t s) 
 
 hipError_t launch_sign_pack(const float* P, const QuantParams& p, hipStream_t s) {
   const long n = (long)p.nbh * p.tn * (p.d / 32);
-  hipLaunchKernelGGL(sign_pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, P, p);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  switch (p.bits) {
+    case 1: hipLaunchKernelGGL(sign_pack_kernel<1>, grid, dim3(256), 0, s, P, p); break;
+    case 2: hipLaunchKernelGGL(sign_pack_kernel<2>, grid, dim3(256), 0, s, P, p); break;
+    case 3: hipLaunchKernelGGL(sign_pack_kernel<3>, grid, dim3(256), 0, s, P, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
