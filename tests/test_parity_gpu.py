@@ -86,6 +86,21 @@ def test_single_token_and_zero_vectors(tq, dtype):
     assert np.all(pl["codes"][z] == 0) and np.all(pl["gamma"][z] == 0)   # code fields hold the signs too
 
 
+@pytest.mark.parametrize("scheme", ["kqv", "kv", "qkqv"])
+def test_value_norms_across_orders_of_magnitude(tq, scheme):
+    """Value vectors scaled by 10^u, u uniform in [-6, 6], with zero vectors
+    among them, and keys scaled up so that the softmax weights spread too.
+    The table-driven decode adds two tokens' values with fp16 weights kept in
+    range by a running exponent frame; the outputs must still match the
+    oracle's exact sums (T odd, so the last pair of a slot is a single token)."""
+    K, V, Q = synth.isotropic(1, 2, 2, 701, 128, seed=11, kv_std=1.0, dtype=np.float32)
+    rng = np.random.default_rng(12)
+    V = (V * 10.0 ** rng.uniform(-6.0, 6.0, size=V.shape[:3] + (1,))).astype(np.float32)
+    V[0, 0, ::9] = 0.0
+    K = (K * 3.0).astype(np.float32)
+    _run_case(tq, K, V, Q, scheme, 4, label="value norms " + scheme)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
 def test_strided_input_and_large_values(tq, dtype):
     base = np.random.default_rng(3).standard_normal((1, 2, 400, 256)).astype(np.float32) * 300.0
