@@ -386,7 +386,7 @@ void decode_lut_kernel(DecodeParams p) {
             sa = fmaf(q[8 * w + 2 * BB], c.x, sa);                                             \
             sb = fmaf(q[8 * w + 2 * BB + 1], c.y, sb);                                         \
             uint32_t sgw = __float_as_uint(c.z);                                               \
-            asm volatile("" : "+v"(sgw));                                                      \
+            asm("" : "+v"(sgw));                                                               \
             const half2_t sg = __builtin_bit_cast(half2_t, sgw);                               \
             if constexpr (kUDot) {                                                             \
               if ((BB) & 1) pb = __builtin_amdgcn_fdot2(uh[4 * w + BB], sg, pb, false);        \
