@@ -24,6 +24,10 @@
 //     on v_dot2_f32_f16 with S q in fp16 pairs (scaled by a power of two, its
 //     largest entry in [1/2, 1)) against the exact +-1 pairs where registers
 //     allow (d = 128, or both sides sketched), else in fp32 fma;
+//   * with sketches on both sides a lane adds two tokens' values at once:
+//     their 4-bit fields merged nibble by nibble index the same table, and
+//     v_dot2_f32_f16 takes both tokens' fp16 weights (kept in (0, 2^8] by a
+//     running exponent frame of their own);
 //   * d/32 lanes per token, lane j owns coordinates [32j, 32j+32); the
 //     per-token scalars (norms, residual norms) are loaded by lanes 0..3 of
 //     the token's group and broadcast (DPP within a quad at d = 128);
@@ -49,6 +53,15 @@ namespace {
 //     buffers) measured no faster.
 constexpr int lut_threads(bool both_sketched) { return both_sketched ? 512 : 768; }
 constexpr bool lut_two_buffers(int d, bool kq, bool vq) { return kq == vq || d <= 256; }
+// A value table indexed by a byte of two 4-bit fields (3-bit code | sketch
+// sign) also serves a lane's two tokens at once: a byte made of field i of
+// each token returns both tokens' centroids and signs, and one v_dot2_f32_f16
+// with the two tokens' fp16 weights adds both.  Taken where both sides carry
+// a sketch (8 waves, registers to spare); with 12 waves the loop it needs
+// measured no faster than the single-token one.
+constexpr bool lut_pair_values(bool kq, int vb, bool vq) {
+  return kq && vq && vb == 3;
+}
 constexpr int kMaxLutWaves = 12;
 // LDS map.  A table indexed by a whole packed byte needs a 64 KB window
 // (entry e at window + e*256, the byte lands in address bits 8..15 straight
@@ -95,6 +108,9 @@ template <int K>
 __device__ __forceinline__ uint32_t byte_addr(uint32_t w, uint32_t lanereg) {
   return __builtin_amdgcn_perm(w, lanereg, 0x0C020000u | ((4u + K) << 8));
 }
+
+// (x & m) | (y & ~m): one v_bfi_b32.
+__device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t x, uint32_t y) { return (x & m) | (y & ~m); }
 
 // LDS address of the 6-bit field at bit offset O of a 3-dword run:
 // (field << 8) | lanereg, as one shift (or funnel shift) that puts the field
@@ -185,10 +201,11 @@ __device__ __forceinline__ uint32_t token_bytes(uint32_t tr) {
 // Token tr (index within the head) for lane j.  The host sends only
 // T_cap <= 2^24 with T_cap * d / 2 < 2^32 here, so tr fits a 24-bit multiply
 // (full rate, unlike a 32-bit one) and every byte offset fits 32 bits.
+// Key words, side codes and the per-token scalar:
 template <int D, int KB, bool KQ, int VB, bool VQ>
-__device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int j, const float* sc_head,
-                                           TokenData<KB, KQ, VB, VQ>& t) {
-  constexpr int KW = lane_dwords<KB, KQ>(), VW = lane_dwords<VB, VQ>();
+__device__ __forceinline__ void load_keys(const HeadPlanes& h, uint32_t tr, int j, const float* sc_head,
+                                          TokenData<KB, KQ, VB, VQ>& t) {
+  constexpr int KW = lane_dwords<KB, KQ>();
   const uint32_t* kc = reinterpret_cast<const uint32_t*>(h.kc + lane_off(token_bytes<(uint32_t)D * KW / 8>(tr) + (uint32_t)j * (4u * KW)));
   if constexpr (KW == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc));
@@ -202,6 +219,13 @@ __device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int
 #pragma unroll
     for (int i = 0; i < KW; ++i) t.k[i] = __builtin_nontemporal_load(kc + i);
   }
+  t.sc = __builtin_nontemporal_load(sc_head + tr);
+}
+
+// Value words:
+template <int D, int KB, bool KQ, int VB, bool VQ>
+__device__ __forceinline__ void load_values(const HeadPlanes& h, uint32_t tr, int j, TokenData<KB, KQ, VB, VQ>& t) {
+  constexpr int VW = lane_dwords<VB, VQ>();
   const uint32_t* vc = reinterpret_cast<const uint32_t*>(h.vc + lane_off(token_bytes<(uint32_t)D * VW / 8>(tr) + (uint32_t)j * (4u * VW)));
   if constexpr (VW == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc));
@@ -210,7 +234,13 @@ __device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int
 #pragma unroll
     for (int i = 0; i < VW; ++i) t.v[i] = __builtin_nontemporal_load(vc + i);
   }
-  t.sc = __builtin_nontemporal_load(sc_head + tr);
+}
+
+template <int D, int KB, bool KQ, int VB, bool VQ>
+__device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int j, const float* sc_head,
+                                           TokenData<KB, KQ, VB, VQ>& t) {
+  load_keys<D>(h, tr, j, sc_head, t);
+  load_values<D>(h, tr, j, t);
 }
 
 template <int D, int KB, bool KQ, int VB, bool VQ>
@@ -362,14 +392,17 @@ void decode_lut_kernel(DecodeParams p) {
       for (int e = 0; e < 32; ++e) ask[e] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
+    // Paired values: acc and ask hold sums in units of 2^M, M a running
+    // maximum of s + log2(nu_v) (a finite sentinel until the first non-zero
+    // value vector), so that every fp16 weight 2^(s + log2 nu_v - M) lies in
+    // (0, 2^8] whatever the norms; the sums move to the 2^m frame of l at the end.
+    constexpr float kNoFrame = -1e30f;
+    float M = kNoFrame;
 
     const int stride = kLutWaves * vpw;
     int base = t0 + wave * vpw;
-    // One token step of this lane (slot, j): score, online softmax, value sums.
-    auto step = [&](const TokenData<KB, KQ, VB, VQ>& cur, int sbase) {
-      const int t = sbase + slot;
-      const bool valid = t < t1;
-
+    // Score of this lane's token (log2 units, -inf past the end).
+    auto score = [&](const TokenData<KB, KQ, VB, VQ>& cur, bool valid) -> float {
       // ---- key score: this lane's 32 coordinates ---------------------------------
       float sa = 0.f, sb = 0.f, pa = 0.f, pb = 0.f;
       if constexpr (KQ) {
@@ -386,7 +419,7 @@ void decode_lut_kernel(DecodeParams p) {
             sa = fmaf(q[8 * w + 2 * BB], c.x, sa);                                             \
             sb = fmaf(q[8 * w + 2 * BB + 1], c.y, sb);                                         \
             uint32_t sgw = __float_as_uint(c.z);                                               \
-            asm("" : "+v"(sgw));                                                               \
+            asm("" : "+v"(sgw));                                                                \
             const half2_t sg = __builtin_bit_cast(half2_t, sgw);                               \
             if constexpr (kUDot) {                                                             \
               if ((BB) & 1) pb = __builtin_amdgcn_fdot2(uh[4 * w + BB], sg, pb, false);        \
@@ -451,8 +484,14 @@ void decode_lut_kernel(DecodeParams p) {
         const float g_k = tok_bcast<L, 1>(cur.sc, lane);
         part = fmaf(nu_k * uscale * g_k, pa + pb, part);
       }
-      float s = tok_sum<L>(part) * p.scale_log2;
-      if (!valid) s = -INFINITY;
+      const float s = tok_sum<L>(part) * p.scale_log2;
+      return valid ? s : -INFINITY;
+    };
+
+    // One token step of this lane (slot, j): score, online softmax, value sums.
+    auto step = [&](const TokenData<KB, KQ, VB, VQ>& cur, int sbase) {
+      const bool valid = sbase + slot < t1;
+      const float s = score(cur, valid);
 
       // ---- online softmax (per token slot) ----------------------------------------
       if (s > m + kSlack) {
@@ -515,7 +554,102 @@ void decode_lut_kernel(DecodeParams p) {
       }
     };
 
-    if constexpr (lut_two_buffers(D, KQ, VQ)) {
+    if constexpr (lut_pair_values(KQ, VB, VQ)) {
+      // Tokens t and t + stride of this slot per step, two pairs of buffers
+      // used in turn: the next pair's value words are loaded as a step
+      // begins, its key words once this step's scores are in.  Past the end
+      // the token index is clamped (re-reads).
+      TokenData<KB, KQ, VB, VQ> xa, xb, ya, yb;
+      const int s2 = 2 * stride;
+      auto pair_step = [&](TokenData<KB, KQ, VB, VQ>& ta, TokenData<KB, KQ, VB, VQ>& tb,
+                           TokenData<KB, KQ, VB, VQ>& na, TokenData<KB, KQ, VB, VQ>& nb, int pb) {
+        load_values<D>(hp, (uint32_t)min(pb + s2 + slot, t1 - 1), j, na);
+        load_values<D>(hp, (uint32_t)min(pb + s2 + stride + slot, t1 - 1), j, nb);
+        const bool va = pb + slot < t1, vb = pb + stride + slot < t1;
+        const float sA = score(ta, va);
+        __builtin_amdgcn_sched_barrier(0);  // one key phase at a time (registers)
+        const float sB = score(tb, vb);
+        __builtin_amdgcn_sched_barrier(0);
+        const float nuA = tok_bcast<L, 2>(ta.sc, lane), nuB = tok_bcast<L, 2>(tb.sc, lane);
+        float gA = 0.f, gB = 0.f;
+        if constexpr (VQ) {
+          gA = tok_bcast<L, 3>(ta.sc, lane);
+          gB = tok_bcast<L, 3>(tb.sc, lane);
+        }
+        load_keys<D>(hp, (uint32_t)min(pb + s2 + slot, t1 - 1), j, sc_head, na);
+        load_keys<D>(hp, (uint32_t)min(pb + s2 + stride + slot, t1 - 1), j, sc_head, nb);
+        // ---- online softmax (per token slot): l in the 2^m frame -----------------------
+        const float smax = fmaxf(sA, sB);
+        if (smax > m + kSlack) {
+          l *= __builtin_amdgcn_exp2f(m - smax);  // 0 while m = -inf
+          m = smax;
+        }
+        l += (va ? __builtin_amdgcn_exp2f(sA - m) : 0.f) + (vb ? __builtin_amdgcn_exp2f(sB - m) : 0.f);
+        // Value weights in the 2^M frame (nu_v = 0 or past the end: weight 0).
+        const float lamA = sA + __builtin_amdgcn_logf(nuA), lamB = sB + __builtin_amdgcn_logf(nuB);
+        const float lmax = fmaxf(lamA, lamB);
+        if (lmax > M + kSlack) {
+          const float f = __builtin_amdgcn_exp2f(M - lmax);
+#pragma unroll
+          for (int e = 0; e < 32; ++e) acc[e] *= f;
+          if (VQ) {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) ask[e] *= f;
+          }
+          M = lmax;
+        }
+        const float wA = __builtin_amdgcn_exp2f(lamA - M), wB = __builtin_amdgcn_exp2f(lamB - M);
+        half2_t wv2, wq2;
+        wv2.x = (_Float16)wA;
+        wv2.y = (_Float16)wB;
+        if constexpr (VQ) {
+          wq2.x = (_Float16)(wA * gA);
+          wq2.y = (_Float16)(wB * gB);
+        }
+
+        // ---- value sums of the pair ----------------------------------------------------
+        // Byte BB of lo (hi) is field 2 BB (2 BB + 1) of dword w of each token:
+        // coordinate 8 w + 2 BB (+ 1), token A in the low nibble.
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // A scheduling fence per dword: left free, the scheduler hoists the
+          // table reads of all four and spills the query slice to make room.
+          __builtin_amdgcn_sched_barrier(0);
+          const uint32_t lo = bitsel(0x0F0F0F0Fu, ta.v[w], tb.v[w] << 4);
+          const uint32_t hi = bitsel(0x0F0F0F0Fu, ta.v[w] >> 4, tb.v[w]);
+#define TQ_VQPAIR(WORD, BB, E)                                                                 \
+          {                                                                                  \
+            const half4_t h = *reinterpret_cast<const half4_t*>(smem + byte_addr<BB>(WORD, lr_v)); \
+            acc[E] = __builtin_amdgcn_fdot2(__builtin_shufflevector(h, h, 0, 1), wv2, acc[E], false); \
+            ask[E] = __builtin_amdgcn_fdot2(__builtin_shufflevector(h, h, 2, 3), wq2, ask[E], false); \
+          }
+          TQ_VQPAIR(lo, 0, 8 * w) TQ_VQPAIR(hi, 0, 8 * w + 1) TQ_VQPAIR(lo, 1, 8 * w + 2) TQ_VQPAIR(hi, 1, 8 * w + 3)
+          TQ_VQPAIR(lo, 2, 8 * w + 4) TQ_VQPAIR(hi, 2, 8 * w + 5) TQ_VQPAIR(lo, 3, 8 * w + 6) TQ_VQPAIR(hi, 3, 8 * w + 7)
+#undef TQ_VQPAIR
+        }
+      };
+      if (base < t1) {
+        load_keys<D>(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, xa);
+        load_keys<D>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, xb);
+        load_values<D>(hp, (uint32_t)min(base + slot, t1 - 1), j, xa);
+        load_values<D>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, xb);
+      }
+      while (base < t1) {
+        pair_step(xa, xb, ya, yb, base);
+        base += s2;
+        if (base >= t1) break;
+        pair_step(ya, yb, xa, xb, base);
+        base += s2;
+      }
+      // Sums from the 2^M frame to the 2^m frame (no valid token: all zero).
+      const float f = m == -INFINITY ? 0.f : exp2f(M - m);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) acc[e] *= f;
+      if (VQ) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ask[e] *= f;
+      }
+    } else if constexpr (lut_two_buffers(D, KQ, VQ)) {
       // Two buffers used in turn, so that the next step's loads never
       // overwrite registers that the current step still reads (no copies).
       // The next step is loaded unconditionally (the token index is clamped,
