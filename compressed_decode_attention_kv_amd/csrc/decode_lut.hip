@@ -24,7 +24,7 @@
 //     on v_dot2_f32_f16 with S q in fp16 pairs (scaled by a power of two, its
 //     largest entry in [1/2, 1)) against the exact +-1 pairs where registers
 //     allow (d = 128, or both sides sketched), else in fp32 fma;
-//   * with sketches on both sides a lane adds two tokens' values at once:
+//   * with sketched values a lane adds two tokens' values at once:
 //     their 4-bit fields merged nibble by nibble index the same table, and
 //     v_dot2_f32_f16 takes both tokens' fp16 weights (kept in (0, 2^8] by a
 //     running exponent frame of their own);
@@ -44,23 +44,24 @@ namespace tq {
 namespace {
 
 // Block size and token loop, per variant (chosen by measurement):
-//   * sketches on both K and V: 8 waves (2 per SIMD, up to 256 VGPRs);
-//     every other variant 12 waves (3 per SIMD, 168 VGPRs);
+//   * sketched values: 8 waves (2 per SIMD, up to 256 VGPRs) and two tokens
+//     per lane step (below); every other variant 12 waves (3 per SIMD, 168
+//     VGPRs) and one token per lane step;
 //   * one token step is prefetched.  Two register buffers used in turn save
 //     the copies of a prefetch-then-copy loop, and win at d <= 256; with a
 //     sketch on one side only at d >= 512 they spill and serialise the table
 //     reads, and the copy loop is kept there.  Deeper prefetch (three or four
 //     buffers) measured no faster.
-constexpr int lut_threads(bool both_sketched) { return both_sketched ? 512 : 768; }
+constexpr int lut_threads(bool sketched_values) { return sketched_values ? 512 : 768; }
 constexpr bool lut_two_buffers(int d, bool kq, bool vq) { return kq == vq || d <= 256; }
 // A value table indexed by a byte of two 4-bit fields (3-bit code | sketch
 // sign) also serves a lane's two tokens at once: a byte made of field i of
 // each token returns both tokens' centroids and signs, and one v_dot2_f32_f16
-// with the two tokens' fp16 weights adds both.  Taken where both sides carry
-// a sketch (8 waves, registers to spare); with 12 waves the loop it needs
-// measured no faster than the single-token one.
+// with the two tokens' fp16 weights adds both.  Taken wherever the values
+// carry a sketch, at 8 waves (registers to spare; at 12 waves the loop it
+// needs measured no faster than the single-token one).
 constexpr bool lut_pair_values(bool kq, int vb, bool vq) {
-  return kq && vq && vb == 3;
+  return vq && vb == 3;
 }
 constexpr int kMaxLutWaves = 12;
 // LDS map.  A table indexed by a whole packed byte needs a 64 KB window
@@ -244,10 +245,10 @@ __device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int
 }
 
 template <int D, int KB, bool KQ, int VB, bool VQ>
-__global__ __launch_bounds__(lut_threads(KQ && VQ))
-__attribute__((amdgpu_waves_per_eu(lut_threads(KQ && VQ) / 256, lut_threads(KQ && VQ) / 256)))
+__global__ __launch_bounds__(lut_threads(VQ))
+__attribute__((amdgpu_waves_per_eu(lut_threads(VQ) / 256, lut_threads(VQ) / 256)))
 void decode_lut_kernel(DecodeParams p) {
-  constexpr int kLutThreads = lut_threads(KQ && VQ);
+  constexpr int kLutThreads = lut_threads(VQ);
   constexpr int kLutWaves = kLutThreads / 64;
   using Map = LutMap<D, KB, KQ, VB, VQ>;
   __shared__ __attribute__((aligned(16))) char smem[LutMap<D, KB, KQ, VB, VQ>::bytes];
@@ -746,7 +747,7 @@ void decode_lut_kernel(DecodeParams p) {
 
 template <int D, int KB, bool KQ, int VB, bool VQ>
 hipError_t launch_lut_d(const DecodeParams& p, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((decode_lut_kernel<D, KB, KQ, VB, VQ>), dim3(nblocks), dim3(lut_threads(KQ && VQ)), 0, s, p);
+  hipLaunchKernelGGL((decode_lut_kernel<D, KB, KQ, VB, VQ>), dim3(nblocks), dim3(lut_threads(VQ)), 0, s, p);
   return hipGetLastError();
 }
 
@@ -763,7 +764,7 @@ hipError_t launch_lut(const DecodeParams& p, int nblocks, hipStream_t s) {
 
 }  // namespace
 
-int lut_waves(int kqjl, int vqjl) { return lut_threads(kqjl && vqjl) / 64; }
+int lut_waves(int kqjl, int vqjl) { return lut_threads(vqjl) / 64; }
 
 bool lut_supported(int d, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl) {
   if (d != 128 && d != 256 && d != 512 && d != 1024) return false;
