@@ -149,7 +149,7 @@ struct RelErrParams {
 // ---- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 // Sign bits of the sketch P [rows][d] (row-major, rows as in QuantParams::rcat)
-// into the qjl plane; zero for zero vectors.
+// into the sign bits of the (bits+1)-bit code fields; zero vectors keep all-zero fields.
 hipError_t launch_sign_pack(const float* P, const QuantParams& p, hipStream_t s);
 // (Pi U_h)^T of every head into out [H][rank][d] (device).
 hipError_t launch_rotate_basis(const QuantParams& p, float* out, hipStream_t s);
