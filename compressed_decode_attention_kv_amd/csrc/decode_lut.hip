@@ -567,10 +567,14 @@ void decode_lut_kernel(DecodeParams p) {
         load_values<D>(hp, (uint32_t)min(pb + s2 + slot, t1 - 1), j, na);
         load_values<D>(hp, (uint32_t)min(pb + s2 + stride + slot, t1 - 1), j, nb);
         const bool va = pb + slot < t1, vb = pb + stride + slot < t1;
+        // Scheduling fences (measured): with sketched keys the scheduler
+        // otherwise interleaves the two key phases and the value dwords and
+        // runs out of registers (QKQV 0.50 -> 0.74 ms without them); with
+        // plain keys it is better left free (KQV 0.44 -> 0.41 ms).
         const float sA = score(ta, va);
-        __builtin_amdgcn_sched_barrier(0);  // one key phase at a time (registers)
+        if constexpr (KQ) __builtin_amdgcn_sched_barrier(0);
         const float sB = score(tb, vb);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KQ) __builtin_amdgcn_sched_barrier(0);
         const float nuA = tok_bcast<L, 2>(ta.sc, lane), nuB = tok_bcast<L, 2>(tb.sc, lane);
         float gA = 0.f, gB = 0.f;
         if constexpr (VQ) {
@@ -613,9 +617,7 @@ void decode_lut_kernel(DecodeParams p) {
         // coordinate 8 w + 2 BB (+ 1), token A in the low nibble.
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          // A scheduling fence per dword: left free, the scheduler hoists the
-          // table reads of all four and spills the query slice to make room.
-          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (KQ) __builtin_amdgcn_sched_barrier(0);
           const uint32_t lo = bitsel(0x0F0F0F0Fu, ta.v[w], tb.v[w] << 4);
           const uint32_t hi = bitsel(0x0F0F0F0Fu, ta.v[w] >> 4, tb.v[w]);
 #define TQ_VQPAIR(WORD, BB, E)                                                                 \
