@@ -346,7 +346,7 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   // The combine step merges at most 256 partials per query; the table-driven
   // kernel at d > 128 writes one per wave.
   const bool vq = v && v->mode == TQ_MODE_PROD;
-  const int per_split = (lut && d > 128) ? lut_waves(k->mode == TQ_MODE_PROD, vq) : 1;
+  const int per_split = (lut && d > 128) ? lut_waves(vq) : 1;
   const int max_split = 256 / per_split;
   if (nsplit > max_split) {
     chunk = (k->T + max_split - 1) / max_split;

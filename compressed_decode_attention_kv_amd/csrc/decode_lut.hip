@@ -60,7 +60,7 @@ constexpr bool lut_two_buffers(int d, bool kq, bool vq) { return kq == vq || d <
 // with the two tokens' fp16 weights adds both.  Taken wherever the values
 // carry a sketch, at 8 waves (registers to spare; at 12 waves the loop it
 // needs measured no faster than the single-token one).
-constexpr bool lut_pair_values(bool kq, int vb, bool vq) {
+constexpr bool lut_pair_values(int vb, bool vq) {
   return vq && vb == 3;
 }
 constexpr int kMaxLutWaves = 12;
@@ -555,7 +555,7 @@ void decode_lut_kernel(DecodeParams p) {
       }
     };
 
-    if constexpr (lut_pair_values(KQ, VB, VQ)) {
+    if constexpr (lut_pair_values(VB, VQ)) {
       // Tokens t and t + stride of this slot per step, two pairs of buffers
       // used in turn: the next pair's value words are loaded as a step
       // begins, its key words once this step's scores are in.  Past the end
@@ -766,7 +766,7 @@ hipError_t launch_lut(const DecodeParams& p, int nblocks, hipStream_t s) {
 
 }  // namespace
 
-int lut_waves(int kqjl, int vqjl) { return lut_threads(vqjl) / 64; }
+int lut_waves(int vqjl) { return lut_threads(vqjl) / 64; }
 
 bool lut_supported(int d, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl) {
   if (d != 128 && d != 256 && d != 512 && d != 1024) return false;
