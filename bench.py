@@ -231,8 +231,8 @@ def main():
         sid = tq.SCHEMES[scheme]
 
         def quant():
-            tq._check(lib.tq_quantize(ctypes.byref(kdesc), tq.KEYS, sid, n, 0, None, ctypes.byref(kp.c), stream()))
-            tq._check(lib.tq_quantize(ctypes.byref(vdesc), tq.VALUES, sid, n, 0, None, ctypes.byref(vp.c), stream()))
+            tq._check(lib.tq_quantize(ctypes.byref(kdesc), tq.KEYS, sid, n, 0, None, None, ctypes.byref(kp.c), stream()))
+            tq._check(lib.tq_quantize(ctypes.byref(vdesc), tq.VALUES, sid, n, 0, None, None, ctypes.byref(vp.c), stream()))
 
         def decode():
             tq._check(lib.tq_decode_attention(ctypes.byref(qdesc), ctypes.byref(kp.c), ctypes.byref(vp.c),
@@ -292,9 +292,9 @@ def main():
     vndesc, _ = tq.tensor_desc(vn)
 
     def gen_step():
-        tq._check(lib.tq_quantize_append(ctypes.byref(kndesc), tq.KEYS, sid, n, 0, None, pos.data_ptr(),
+        tq._check(lib.tq_quantize_append(ctypes.byref(kndesc), tq.KEYS, sid, n, 0, None, None, pos.data_ptr(),
                                          ctypes.byref(kp.c), stream()))
-        tq._check(lib.tq_quantize_append(ctypes.byref(vndesc), tq.VALUES, sid, n, 0, None, pos.data_ptr(),
+        tq._check(lib.tq_quantize_append(ctypes.byref(vndesc), tq.VALUES, sid, n, 0, None, None, pos.data_ptr(),
                                          ctypes.byref(vp.c), stream()))
         tq._check(lib.tq_decode_attention_lens(ctypes.byref(qdesc), ctypes.byref(kp.c), ctypes.byref(vp.c),
                                                lens.data_ptr(), out.data_ptr(), lse.data_ptr(), ws.data_ptr(),

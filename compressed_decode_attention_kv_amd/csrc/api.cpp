@@ -73,6 +73,32 @@ tq_status modes_of(int scheme, int n_bits, int which, int* mode, int* bits) {
   return TQ_OK;
 }
 
+// (mode, index bits) of one tensor: the scheme preset, or the caller's
+// per-tensor override (then scheme and n_bits are not used).
+tq_status resolve_mode(int scheme, int n_bits, int which, const tq_mode_override* ovr, int* mode, int* bits) {
+  if (!ovr) return modes_of(scheme, n_bits, which, mode, bits);
+  if (which != TQ_KEYS && which != TQ_VALUES) return fail(TQ_EINVAL, "which=%d is neither TQ_KEYS nor TQ_VALUES", which);
+  const int m = ovr->mode, b = ovr->bits;
+  switch (m) {
+    case TQ_MODE_PLAIN:
+    case TQ_MODE_MSE:
+      if (b < 1 || b > kMaxIndexBits) return fail(TQ_EINVAL, "override: index bits %d outside [1, %d]", b, kMaxIndexBits);
+      break;
+    case TQ_MODE_PROD:
+      if (b < 1 || b > kMaxIndexBits - 1)
+        return fail(TQ_EINVAL, "override: a QJL tensor takes 1..%d index bits (got %d)", kMaxIndexBits - 1, b);
+      break;
+    case TQ_MODE_HEADQ:
+      if (which != TQ_KEYS) return fail(TQ_EINVAL, "override: HeadQ is a key-side mode");
+      if (b != 2) return fail(TQ_EUNSUPPORTED, "override: the HeadQ base takes 2 index bits (got %d)", b);
+      break;
+    default: return fail(TQ_EINVAL, "override: unknown mode %d", m);
+  }
+  *mode = m;
+  *bits = b;
+  return TQ_OK;
+}
+
 tq_status layout_of(int d, int mode, int bits, int side_rank, int side_bits, tq_layout* out) {
   if (tq_status s = check_d(d)) return s;
   if (mode < TQ_MODE_PLAIN || mode > TQ_MODE_HEADQ) return fail(TQ_EINVAL, "unknown mode %d", mode);
@@ -317,8 +343,9 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   if (tq_status s = check_packed(k, "K")) return s;
   if (v) {
     if (tq_status s = check_packed(v, "V")) return s;
-    if (k->B != v->B || k->H != v->H || k->T != v->T || k->d != v->d)
-      return fail(TQ_EMISMATCH, "K and V packed headers disagree (B, H, T or d)");
+    // The kernels address both tensors' planes with one head stride, T_cap.
+    if (k->B != v->B || k->H != v->H || k->T != v->T || k->T_cap != v->T_cap || k->d != v->d)
+      return fail(TQ_EMISMATCH, "K and V packed headers disagree (B, H, T, T_cap or d)");
     if (v->mode == TQ_MODE_HEADQ) return fail(TQ_EINVAL, "HeadQ is a key-side mode");
   }
   if (Hq < 1 || Hq % k->H) return fail(TQ_EMISMATCH, "Hq=%d is not a multiple of the KV heads H=%d", Hq, k->H);
@@ -606,10 +633,10 @@ tq_status tq_rotation_state(uint64_t seed, int32_t d, float* signs, float* S) {
 }
 
 tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, int32_t n_bits, uint64_t seed,
-                      const tq_headq* hq, tq_packed* out, void* stream) {
+                      const tq_mode_override* ovr, const tq_headq* hq, tq_packed* out, void* stream) {
   if (tq_status s = check_tensor(x, "x")) return s;
   int mode, bits;
-  if (tq_status s = modes_of(scheme, n_bits, which, &mode, &bits)) return s;
+  if (tq_status s = resolve_mode(scheme, n_bits, which, ovr, &mode, &bits)) return s;
   if (!out) return fail(TQ_EINVAL, "output packed descriptor is NULL");
   if ((mode == TQ_MODE_HEADQ) != (hq != nullptr))
     return fail(TQ_EINVAL, mode == TQ_MODE_HEADQ ? "HeadQ keys need a tq_headq" : "tq_headq given for a non-HeadQ tensor");
@@ -634,17 +661,18 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
 }
 
 tq_status tq_quantize_append(const tq_tensor_desc* x, int32_t which, int32_t scheme, int32_t n_bits, uint64_t seed,
-                             const tq_headq* hq, const int32_t* pos, tq_packed* cache, void* stream) {
+                             const tq_mode_override* ovr, const tq_headq* hq, const int32_t* pos, tq_packed* cache,
+                             void* stream) {
   if (tq_status s = check_tensor(x, "x")) return s;
   int mode, bits;
-  if (tq_status s = modes_of(scheme, n_bits, which, &mode, &bits)) return s;
+  if (tq_status s = resolve_mode(scheme, n_bits, which, ovr, &mode, &bits)) return s;
   if (tq_status s = check_packed(cache, "cache")) return s;
   if (!pos || !aligned(pos, 4)) return fail(TQ_EINVAL, "positions NULL or not 4-byte aligned");
   if (cache->B != x->B || cache->H != x->H || cache->d != x->d)
     return fail(TQ_EMISMATCH, "new tokens (B=%d H=%d d=%d) do not match the cache (B=%d H=%d d=%d)", x->B, x->H, x->d,
                 cache->B, cache->H, cache->d);
   if (cache->mode != mode || cache->bits != bits || cache->seed != seed)
-    return fail(TQ_EMISMATCH, "scheme/bits/seed give mode %d with %d bits, seed %llu; the cache holds mode %d, %d bits, seed %llu",
+    return fail(TQ_EMISMATCH, "scheme/override/seed give mode %d with %d bits, seed %llu; the cache holds mode %d, %d bits, seed %llu",
                 mode, bits, (unsigned long long)seed, cache->mode, cache->bits, (unsigned long long)cache->seed);
   if ((mode == TQ_MODE_HEADQ) != (hq != nullptr))
     return fail(TQ_EINVAL, mode == TQ_MODE_HEADQ ? "HeadQ keys need a tq_headq" : "tq_headq given for a non-HeadQ tensor");

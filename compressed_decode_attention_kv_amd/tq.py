@@ -31,6 +31,10 @@ EXPORTS = ["tq_abi_version", "tq_status_str", "tq_last_error", "tq_codebook_buil
            "tq_stream_read", "tq_release_cache"]
 
 
+class ModeOverride(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("bits", ctypes.c_int32)]
+
+
 class TensorDesc(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("B", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("T", ctypes.c_int32), ("d", ctypes.c_int32),
@@ -75,10 +79,10 @@ _sigs = {
     "tq_scheme_modes": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P(ctypes.c_int32), _P(ctypes.c_int32)], ctypes.c_int),
     "tq_packed_layout": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P(Layout)], ctypes.c_int),
     "tq_rotation_state": ([ctypes.c_uint64, ctypes.c_int32, _P(ctypes.c_float), _P(ctypes.c_float)], ctypes.c_int),
-    "tq_quantize": ([_P(TensorDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64, _P(HeadQ),
-                     _P(Packed), ctypes.c_void_p], ctypes.c_int),
+    "tq_quantize": ([_P(TensorDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64,
+                     _P(ModeOverride), _P(HeadQ), _P(Packed), ctypes.c_void_p], ctypes.c_int),
     "tq_quantize_append": ([_P(TensorDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64,
-                            _P(HeadQ), ctypes.c_void_p, _P(Packed), ctypes.c_void_p], ctypes.c_int),
+                            _P(ModeOverride), _P(HeadQ), ctypes.c_void_p, _P(Packed), ctypes.c_void_p], ctypes.c_int),
     "tq_decode_workspace_size": ([_P(Packed), _P(Packed), ctypes.c_int32, _P(ctypes.c_size_t)], ctypes.c_int),
     "tq_decode_attention": ([_P(TensorDesc), _P(Packed), _P(Packed), ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
@@ -262,10 +266,23 @@ def _check_basis(basis, x, H, d):
         raise ValueError("HeadQ basis must be on the input's device (%s, got %s)" % (x.device, basis.device))
 
 
-def quantize(x, which, scheme, n_bits, seed=0, basis=None, rank=16, side_bits=4, T_cap=None):
-    """Quantise x [B, H, T, d] (device, fp16/fp32) into a new PackedTensor."""
+def _override(mode, bits):
+    """The per-tensor (mode, index bits) override, or None for the preset."""
+    if mode is None and bits is None:
+        return None
+    if mode is None or bits is None:
+        raise ValueError("a per-tensor override needs both mode and bits")
+    return ModeOverride(mode, bits)
+
+
+def quantize(x, which, scheme, n_bits, seed=0, basis=None, rank=16, side_bits=4, T_cap=None, mode=None, bits=None):
+    """Quantise x [B, H, T, d] (device, fp16/fp32) into a new PackedTensor.
+    The tensor's (mode, index bits) come from (scheme, n_bits, which), or
+    from `mode` and `bits` when both are given (per-tensor override)."""
     desc, x4 = tensor_desc(x)
-    mode, bits = scheme_modes(scheme, n_bits, which)
+    ovr = _override(mode, bits)
+    if ovr is None:
+        mode, bits = scheme_modes(scheme, n_bits, which)
     hq = None
     if mode == MODE_HEADQ:
         _check_basis(basis, x, desc.H, desc.d)
@@ -275,7 +292,8 @@ def quantize(x, which, scheme, n_bits, seed=0, basis=None, rank=16, side_bits=4,
                       rank if hq else 0, side_bits if hq else 0, device=x.device)
     pt.basis = basis
     _check(_lib.tq_quantize(ctypes.byref(desc), which, SCHEMES.get(scheme, scheme), n_bits, seed,
-                            ctypes.byref(hq) if hq else None, ctypes.byref(pt.c), _stream()))
+                            ctypes.byref(ovr) if ovr else None, ctypes.byref(hq) if hq else None,
+                            ctypes.byref(pt.c), _stream()))
     pt._keep = x4
     return pt
 
@@ -290,18 +308,19 @@ def _check_index_vector(v, B, like, what):
         raise ValueError("%s must be on %s (got %s)" % (what, like.device, v.device))
 
 
-def quantize_append(x, which, scheme, n_bits, pos, cache, seed=0):
+def quantize_append(x, which, scheme, n_bits, pos, cache, seed=0, mode=None, bits=None):
     """Quantise the new tokens x [B, H, Tn, d] and write token t of sequence b
-    at slot pos[b] + t of the PackedTensor `cache` (same scheme, bits and seed
-    as it was written with).  cache.c.T is left as is."""
+    at slot pos[b] + t of the PackedTensor `cache` (same scheme or override,
+    bits and seed as it was written with).  cache.c.T is left as is."""
     desc, x4 = tensor_desc(x)
+    ovr = _override(mode, bits)
     _check_index_vector(pos, desc.B, x, "pos")
     hq = None
     if cache.c.mode == MODE_HEADQ:
         hq = HeadQ(cache.c.basis, cache.c.side_rank, cache.c.side_bits)
     _check(_lib.tq_quantize_append(ctypes.byref(desc), which, SCHEMES.get(scheme, scheme), n_bits, seed,
-                                   ctypes.byref(hq) if hq else None, pos.data_ptr(), ctypes.byref(cache.c),
-                                   _stream()))
+                                   ctypes.byref(ovr) if ovr else None, ctypes.byref(hq) if hq else None,
+                                   pos.data_ptr(), ctypes.byref(cache.c), _stream()))
     cache._keep_append = (x4, pos)
 
 

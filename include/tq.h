@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 3
+#define TQ_ABI_VERSION 4
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -89,6 +89,20 @@ typedef enum tq_scheme {
   TQ_SCHEME_KV = 0, TQ_SCHEME_TQ_KV = 1, TQ_SCHEME_KQV = 2,
   TQ_SCHEME_QKQV = 3, TQ_SCHEME_TQ_QKV = 4, TQ_SCHEME_HEADQ = 5
 } tq_scheme;
+
+/* Per-tensor choice of quantiser mode and index width, overriding the
+ * scheme preset ([P1] "Esquemas de Cuantización" and [P2] "Contribuições
+ * Principais" 1 compare per-tensor choices of rotation, scalar code and QJL
+ * sketch; the presets above are the combinations the pages name).
+ *   mode:  tq_mode.  HEADQ only for keys (and with a tq_headq).
+ *   bits:  width of the Lloyd-Max index, in [1, 4] (PLAIN, MSE), [1, 3]
+ *          (PROD: each field is bits + 1 wide, the QJL sign beside the
+ *          index), 2 (HEADQ base).  A PROD tensor at bits = b spends b + 1
+ *          bits per coordinate, the budget of a preset at n = b + 1. */
+typedef struct tq_mode_override {
+  int32_t mode;
+  int32_t bits;
+} tq_mode_override;
 
 /* Dense device tensor [B][H][T][d]; the last dimension is contiguous and the
  * other strides are in elements.  Queries use T = 1 and H = number of query
@@ -201,14 +215,16 @@ tq_status tq_packed_layout(int32_t d, int32_t mode, int32_t bits, int32_t side_r
 tq_status tq_rotation_state(uint64_t seed, int32_t d, float* signs, float* S);
 
 /* Write side: quantise x [B][H][T][d] (fp16 or fp32, device) into `out`.
- * Mode and bits come from (scheme, n_bits, which).  n_bits in [1, 4]
- * (PROD needs n_bits >= 2).  hq must be non-NULL exactly when the mode is
- * HEADQ (keys of TQ_SCHEME_HEADQ).  out->T_cap >= x->T (0 means x->T); the
- * planes the mode needs must be set, 16-byte aligned and sized per
- * tq_packed_layout.  Writes tokens [0, x->T) and sets out->T = x->T.
- * Stream-ordered. */
+ * Mode and bits come from (scheme, n_bits, which), or from `ovr` when it is
+ * non-NULL (scheme and n_bits are then ignored; `which` still decides
+ * whether HEADQ is allowed).  n_bits in [1, 4] (PROD needs n_bits >= 2).
+ * hq must be non-NULL exactly when the mode is HEADQ.  out->T_cap >= x->T
+ * (0 means x->T); the planes the mode needs must be set, 16-byte aligned and
+ * sized per tq_packed_layout.  Writes tokens [0, x->T) and sets out->T =
+ * x->T.  Stream-ordered. */
 tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, int32_t n_bits,
-                      uint64_t seed, const tq_headq* hq, tq_packed* out, void* stream);
+                      uint64_t seed, const tq_mode_override* ovr, const tq_headq* hq, tq_packed* out,
+                      void* stream);
 
 /* Append to a packed cache (the generation loop around the read side:
  * [P2] "Resumo" and "Contribuições Principais" place the cost in long-context
@@ -218,12 +234,12 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
  * the kernels (no host synchronisation); a token whose slot falls outside
  * [0, cache->T_cap) is not written.  `cache` must carry a header written by
  * tq_quantize with the same mode, bits and seed as (scheme, n_bits, which,
- * seed), the same B, H and d as x, and for HEADQ the same basis, rank and
+ * seed) or `ovr`, the same B, H and d as x, and for HEADQ the same basis, rank and
  * side bits as hq; otherwise TQ_EMISMATCH.  cache->T is not changed: the
  * caller tracks lengths (tq_decode_attention_lens).  Stream-ordered. */
 tq_status tq_quantize_append(const tq_tensor_desc* x, int32_t which, int32_t scheme, int32_t n_bits,
-                             uint64_t seed, const tq_headq* hq, const int32_t* pos, tq_packed* cache,
-                             void* stream);
+                             uint64_t seed, const tq_mode_override* ovr, const tq_headq* hq,
+                             const int32_t* pos, tq_packed* cache, void* stream);
 
 /* Workspace bytes tq_decode_attention needs for Hq query heads. */
 tq_status tq_decode_workspace_size(const tq_packed* k, const tq_packed* v, int32_t Hq, size_t* bytes);
@@ -232,7 +248,8 @@ tq_status tq_decode_workspace_size(const tq_packed* k, const tq_packed* v, int32
  * for every query q [B][Hq][1][d] (device, fp16/fp32) attend over the packed
  * cache: s_j = (q^T k_hat_j + HeadQ correction q^T U z_hat_j) / sqrt(d),
  * p = softmax(s), out = sum_j p_j v_hat_j.  Query head g reads KV head
- * g / (Hq / H).  out: device fp32 [B][Hq][d]; lse: device fp32 [B][Hq]
+ * g / (Hq / H); k and v must agree on B, H, T, T_cap and d (else
+ * TQ_EMISMATCH).  out: device fp32 [B][Hq][d]; lse: device fp32 [B][Hq]
  * (log-sum-exp of s, may be NULL).  ws: device workspace of at least
  * tq_decode_workspace_size bytes, 256-byte aligned.  Stream-ordered. */
 tq_status tq_decode_attention(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v,

@@ -60,8 +60,8 @@ def sign_vector(seed, d):
     return np.where(top == 0, 1.0, -1.0)
 
 
-def gaussian_sketch(seed, d, m=None):
-    """S in R^{m x d}: the float16 values, returned as float64."""
+def gaussian_draws(seed, d, m=None):
+    """The Box-Muller doubles behind S, before the float16 rounding, [m, d]."""
     m = d if m is None else m
     n = m * d
     npairs = (n + 1) // 2
@@ -74,4 +74,9 @@ def gaussian_sketch(seed, d, m=None):
     z = np.empty(2 * npairs)
     z[0::2] = r * np.cos(TWO_PI * u2)
     z[1::2] = r * np.sin(TWO_PI * u2)
-    return z[:n].astype(np.float16).astype(np.float64).reshape(m, d)
+    return z[:n].reshape(m, d)
+
+
+def gaussian_sketch(seed, d, m=None):
+    """S in R^{m x d}: the float16 values, returned as float64."""
+    return gaussian_draws(seed, d, m).astype(np.float16).astype(np.float64)

@@ -13,11 +13,12 @@ def dev(a, dtype=None):
     return t.cuda()
 
 
-def run_case(tq, K, V, Q, scheme, n, seed=0, U=None, dtype=None, label=""):
+def run_case(tq, K, V, Q, scheme, n, seed=0, U=None, dtype=None, label="", modes=None):
     """K, V [B, H, T, d], Q [B, H*G, d] (numpy).  Quantise and decode on the
     GPU, run the oracle per (b, h), compare everything.  Returns the worst
     output error, the in-band mismatch count, the packed tensors, the device
-    inputs and the oracle's dense (K_hat, V_hat) per (b, h)."""
+    inputs and the oracle's dense (K_hat, V_hat) per (b, h).  modes:
+    ((k_mode, k_bits), (v_mode, v_bits)) per-tensor overrides of the preset."""
     B, H, T, d = K.shape
     Hq = Q.shape[1]
     G = Hq // H
@@ -28,8 +29,9 @@ def run_case(tq, K, V, Q, scheme, n, seed=0, U=None, dtype=None, label=""):
     Vh_in = Vd.double().cpu().numpy()
     Qh_in = Qd.double().cpu().numpy()
     basis = dev(U.astype(np.float32)) if U is not None else None
-    kp = tq.quantize(Kd, tq.KEYS, scheme, n, seed, basis=basis)
-    vp = tq.quantize(Vd, tq.VALUES, scheme, n, seed)
+    (km, kb), (vm, vb) = modes if modes is not None else ((None, None), (None, None))
+    kp = tq.quantize(Kd, tq.KEYS, scheme, n, seed, basis=basis, mode=km, bits=kb)
+    vp = tq.quantize(Vd, tq.VALUES, scheme, n, seed, mode=vm, bits=vb)
     out, lse = tq.decode_attention(Qd, kp, vp)
     torch.cuda.synchronize()
     out, lse = out.cpu().numpy(), lse.cpu().numpy()

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(tqlib):
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(tqlib.EXPORTS) == names
-    assert tqlib.lib().tq_abi_version() == 3
+    assert tqlib.lib().tq_abi_version() == 4
 
 
 @pytest.mark.parametrize("d,bits", [(32, 1), (128, 2), (128, 3), (128, 4), (1024, 2), (1024, 4)])
@@ -83,6 +83,10 @@ def test_layouts(tqlib):
     dict(scheme="headq", which=0, no_hq=True), dict(scheme="tq-kv", which=0, give_hq=True),
     dict(scheme="headq", which=0, hq_rank=12), dict(scheme="headq", which=0, hq_bits=1),
     dict(T_cap=3),
+    # per-tensor overrides (mode, index bits)
+    dict(ovr=(1, 0)), dict(ovr=(1, 5)), dict(ovr=(2, 4)), dict(ovr=(2, 0)), dict(ovr=(7, 2)),
+    dict(ovr=(3, 2), which=1, give_hq=True), dict(ovr=(3, 3), give_hq=True), dict(ovr=(3, 2), no_hq=True),
+    dict(ovr=(2, 2), no_gamma=True),
 ])
 def test_quantize_rejects_before_any_gpu_call(tqlib, bad):
     """Fake (never dereferenced) but aligned pointers: every case must be
@@ -104,8 +108,10 @@ def test_quantize_rejects_before_any_gpu_call(tqlib, bad):
     if (scheme == "headq" and not bad.get("no_hq")) or bad.get("give_hq"):
         hq = tqlib.HeadQ(fake, bad.get("hq_rank", 16), bad.get("hq_bits", 4))
     sid = tqlib.SCHEMES.get(scheme, scheme)
+    ovr = tqlib.ModeOverride(*bad["ovr"]) if "ovr" in bad else None
     st = tqlib.lib().tq_quantize(ctypes.byref(desc), bad.get("which", 0), sid, bad.get("n_bits", 4), 0,
-                                 ctypes.byref(hq) if hq else None, ctypes.byref(out), None)
+                                 ctypes.byref(ovr) if ovr else None, ctypes.byref(hq) if hq else None,
+                                 ctypes.byref(out), None)
     assert st in (tqlib.EINVAL, tqlib.EUNSUPPORTED), st
     assert tqlib.lib().tq_last_error().decode()
 
@@ -135,6 +141,12 @@ def test_decode_rejects_mismatches(tqlib):
                                    n.value - 256, None) == tqlib.ENOMEM
     assert lib.tq_decode_attention(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), out, None, fake + 16,
                                    n.value, None) == tqlib.EINVAL
+    # K and V with different capacities: the kernels address both with one head stride.
+    vcap = _packed(tqlib, tqlib.MODE_PROD, 3)
+    vcap.T_cap = 16
+    assert lib.tq_decode_workspace_size(ctypes.byref(k), ctypes.byref(vcap), 4, ctypes.byref(n)) == tqlib.EMISMATCH
+    assert lib.tq_decode_attention(ctypes.byref(q), ctypes.byref(k), ctypes.byref(vcap), out, None, fake,
+                                   1 << 30, None) == tqlib.EMISMATCH
     hv = _packed(tqlib, tqlib.MODE_HEADQ, 2)
     assert lib.tq_decode_workspace_size(ctypes.byref(k), ctypes.byref(hv), 4, ctypes.byref(n)) != tqlib.OK
     # A hand-made PROD header with 4 index bits has no kernel: rejected before launch.
@@ -199,12 +211,19 @@ def test_append_and_lengths_reject_before_any_gpu_call(tqlib):
         (desc(T=9), kqv, 4, 5, fake, tqlib.EINVAL),       # more new tokens than the capacity
     ]
     for d, scheme, n, seed, pos, want in cases:
-        st = lib.tq_quantize_append(ctypes.byref(d), tqlib.KEYS, scheme, n, seed, None, pos, ctypes.byref(cache), None)
+        st = lib.tq_quantize_append(ctypes.byref(d), tqlib.KEYS, scheme, n, seed, None, None, pos, ctypes.byref(cache),
+                                    None)
         assert st == want, (scheme, n, seed, pos, st)
         assert lib.tq_last_error().decode()
     hq = tqlib.HeadQ(fake, 16, 4)
-    assert lib.tq_quantize_append(ctypes.byref(desc()), tqlib.KEYS, kqv, 4, 5, ctypes.byref(hq), fake,
+    assert lib.tq_quantize_append(ctypes.byref(desc()), tqlib.KEYS, kqv, 4, 5, None, ctypes.byref(hq), fake,
                                   ctypes.byref(cache), None) == tqlib.EINVAL
+    # An override must name the cache's own mode and bits.
+    for mode, bits, want in ((tqlib.MODE_MSE, 3, tqlib.EMISMATCH), (tqlib.MODE_PROD, 3, tqlib.EMISMATCH),
+                             (tqlib.MODE_MSE, 9, tqlib.EINVAL)):
+        ovr = tqlib.ModeOverride(mode, bits)
+        assert lib.tq_quantize_append(ctypes.byref(desc()), tqlib.KEYS, kqv, 4, 5, ctypes.byref(ovr), None, fake,
+                                      ctypes.byref(cache), None) == want
     v = _packed(tqlib, tqlib.MODE_PROD, 3, B=1, H=2, T=8)
     q = tqlib.TensorDesc(fake, tqlib.F16, 1, 2, 1, 128, 2 * 128, 128, 128)
     for lens in (None, fake + 2):

@@ -146,6 +146,36 @@ def test_headq_side_code_rules():
     assert np.all(np.abs(out["z"] - out["zhat"]) <= 0.5 * s[:, None] * (1 + 1e-6) + 1e-7)
 
 
+def test_headq_side_code_score_error():
+    """[P3] section 3 reads the side code as a logit correction
+    q^T U z_hat / sqrt(d).  At the score level: for any q the error the side
+    code leaves, q^T U (z_hat - z) / sqrt(d), is at most
+    1/2 s_z ||U^T q||_1 / sqrt(d) (each coefficient within half a step); for
+    q in span(U) the corrected score error is that alone, far below the
+    base-only error q^T e / sqrt(d)."""
+    d, r, T = 128, 16, 2000
+    rng = np.random.default_rng(12)
+    U, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    K = rng.standard_normal((T, d))
+    st = qz.QState(d, qz.MSE, 2, seed=4)
+    out = hq.quantize(K, U, st, side_bits=4)
+    s_z = out["side_scale"]
+    for _ in range(20):
+        q = rng.standard_normal(d)
+        err = (out["zhat"] - out["z"]) @ (U.T @ q) / math.sqrt(d)
+        bound = 0.5 * s_z * np.sum(np.abs(U.T @ q)) / math.sqrt(d)
+        assert np.all(np.abs(err) <= bound * (1 + 1e-6) + 1e-7)
+    E = K - out["kbase"]
+    for _ in range(20):
+        q = U @ rng.standard_normal(r)
+        e_base = E @ q / math.sqrt(d)
+        e_corr = (E @ q - out["zhat"] @ (U.T @ q)) / math.sqrt(d)
+        assert np.mean(e_corr ** 2) < 0.05 * np.mean(e_base ** 2)
+        # The wrong sign ([P3] section 4 control) makes it worse than none.
+        e_wrong = (E @ q + out["zhat"] @ (U.T @ q)) / math.sqrt(d)
+        assert np.mean(e_wrong ** 2) > np.mean(e_base ** 2)
+
+
 def test_pca_basis_matches_dominant_subspace():
     d, r = 32, 4
     rng = np.random.default_rng(4)

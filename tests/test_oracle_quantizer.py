@@ -139,6 +139,38 @@ def test_qjl_unbiased_with_pinned_variance():
     assert abs(sq.mean() - exp_sq) < 4 * sq.std() / math.sqrt(n)
 
 
+def test_fp16_sketch_bias_within_rounding_bound():
+    """S is the fp16 rounding of Gaussian draws G (a reading: the pages fix
+    only the law).  Rounding moves each entry by a relative error rho_i with
+    |rho_i| <= eps = 2^-11, S = diag-scaled G, and for a fixed scaling
+    D = diag(1 + rho) the Gaussian identity gives E<q, r_hat> =
+    ||r|| <Dq, Dr> / ||Dr||, within (3 eps + eps^2) / (1 - eps) ||q|| ||r||
+    of <q, r>.  Checked on coupled draws: the same G with and without the
+    rounding, mean difference of the two estimates over 4000 sketches."""
+    from oracle.rng import gaussian_draws
+    d = 128
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal(d)
+    r = rng.standard_normal(d) * 0.2
+    gam = np.linalg.norm(r)
+    c = math.sqrt(math.pi / 2) / d * gam
+    diff = []
+    for seed in range(4000):
+        G = gaussian_draws(seed, d)
+        S = G.astype(np.float16).astype(np.float64)
+        assert np.all(np.abs(S - G) <= 2.0 ** -11 * np.abs(G) + 2.0 ** -25)
+        e16 = c * (S @ q) @ np.where(S @ r >= 0, 1.0, -1.0)
+        e64 = c * (G @ q) @ np.where(G @ r >= 0, 1.0, -1.0)
+        diff.append(e16 - e64)
+    diff = np.array(diff)
+    eps = 2.0 ** -11
+    bound = (3 * eps + eps * eps) / (1 - eps) * np.linalg.norm(q) * gam
+    se = diff.std() / math.sqrt(diff.size)
+    assert abs(diff.mean()) <= bound + 4 * se, (diff.mean(), bound, se)
+    # The bound is small against the spread of one sketch's estimate (m = d).
+    assert bound < 0.02 * math.sqrt(math.pi / 2 / d) * np.linalg.norm(q) * gam
+
+
 def test_prod_relmse_matches_closed_form():
     """relMSE of PROD(b+1) on isotropic data = d D(b) (pi/2 - 1/d) in
     expectation (the sketch adds the variance of the previous test)."""

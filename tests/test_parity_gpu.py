@@ -65,6 +65,22 @@ def test_schemes_ragged_gqa(tq, scheme, n):
     print(scheme, n, "worst rel L2 %.3g band %d" % (worst, n_band))
 
 
+@pytest.mark.parametrize("d,kmode,kbits,vmode,vbits", [
+    (128, 1, 3, 2, 2),    # K MSE(3), V PROD(2 + 1): 3 bits per coordinate on both sides
+    (128, 0, 4, 2, 1),    # K PLAIN(4), V PROD(1 + 1)
+    (256, 2, 2, 0, 3),    # K PROD(2 + 1), V PLAIN(3)
+    (64, 1, 4, 1, 2),     # K MSE(4), V MSE(2)
+])
+def test_per_tensor_override(tq, d, kmode, kbits, vmode, vbits):
+    """Per-tensor (mode, index bits) chosen outside the presets through the
+    ABI's override, fp16 inputs, ragged T, 2 queries per KV head."""
+    K, V, Q = synth.isotropic(1, 2, 2, 900, d, seed=20 + d, kv_std=1.0, dtype=np.float32)
+    worst, n_band, kp, vp, _ = _run_case(tq, K, V, Q, "kqv", 4, seed=3, dtype=torch.float16,
+                                         modes=((kmode, kbits), (vmode, vbits)), label="override")
+    assert (kp.c.mode, kp.c.bits, vp.c.mode, vp.c.bits) == (kmode, kbits, vmode, vbits)
+    print("override", d, kmode, kbits, vmode, vbits, "worst rel L2 %.3g band %d" % (worst, n_band))
+
+
 @pytest.mark.parametrize("d", [32, 64, 256, 512, 1024])
 @pytest.mark.parametrize("scheme", ["kqv", "qkqv", "kv"])
 def test_head_dims(tq, d, scheme):
