@@ -151,13 +151,19 @@ std::map<std::tuple<int, uint64_t, int>, _Float16*> g_sketch_cat;
 std::map<int, rocblas_handle> g_blas;
 std::mutex g_blas_mu;
 
-tq_status sketch_on_device(uint64_t seed, int d, const float** out) {
+// The device copy of S for (current device, seed, d), made on first use.
+// With may_alloc false nothing is allocated: a copy not yet resident is an
+// error (the allocation-free decode).
+tq_status sketch_on_device(uint64_t seed, int d, const float** out, bool may_alloc = true) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_EDEVICE, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_cache_mu);
   auto key = std::make_tuple(dev, seed, d);
   auto it = g_sketch.find(key);
   if (it != g_sketch.end()) { *out = it->second; return TQ_OK; }
+  if (!may_alloc)
+    return fail(TQ_EINVAL, "the QJL sketch for seed %llu, d=%d is not resident on device %d: quantize or decode "
+                "once with it through an allocating call first", (unsigned long long)seed, d, dev);
   std::vector<float> S((size_t)d * d);
   gaussian_sketch(seed, d, S.data());
   float* p = nullptr;
@@ -437,7 +443,7 @@ tq_status fill_codebook(int d, int bits, float* c16, float* b16) {
 tq_status quantize_core(const tq_tensor_desc* x, int mode, int bits, uint64_t seed, const tq_headq* hq,
                         const tq_packed* out, int T_cap, const int32_t* pos, void* stream);
 tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v, const int32_t* lens,
-                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream, bool may_alloc = true);
 
 void fill_scoring(const tq_tensor_desc* q, const tq_packed* k, const DecodePlan& pl, char* ws, DecodeParams* dp) {
   std::memset(dp, 0, sizeof(*dp));
@@ -765,12 +771,28 @@ tq_status tq_decode_attention_lens(const tq_tensor_desc* q, const tq_packed* k, 
   return decode_core(q, k, v, lens, out, lse, ws, ws_bytes, stream);
 }
 
+tq_status tq_decode_attention_static(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v,
+                                     const int32_t* lens, float* out, float* lse, void* stream) {
+  if (lens && !aligned(lens, 4)) return fail(TQ_EINVAL, "lengths not 4-byte aligned");
+  if (!k || !v) return fail(TQ_EINVAL, "packed descriptor is NULL");
+  if (!q) return fail(TQ_EINVAL, "query descriptor is NULL");
+  DecodePlan pl;
+  if (tq_status s = plan_decode(k, v, q->H, false, &pl)) return s;
+  if (pl.bytes > static_scratch_bytes())
+    return fail(TQ_ENOMEM, "this decode needs a %zu-byte workspace; the static one holds %zu bytes "
+                "(use tq_decode_attention with a workspace of its own)", pl.bytes, static_scratch_bytes());
+  if (tq_status s = check_query(q, k)) return s;
+  void* ws = nullptr;
+  if (tq_status s = hip_status(static_scratch(&ws), "static workspace address")) return s;
+  return decode_core(q, k, v, lens, out, lse, ws, static_scratch_bytes(), stream, false);
+}
+
 }  // extern "C"
 
 namespace {
 
 tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v, const int32_t* lens,
-                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream, bool may_alloc) {
   if (!k || !v) return fail(TQ_EINVAL, "packed descriptor is NULL");
   if (!q) return fail(TQ_EINVAL, "query descriptor is NULL");
   DecodePlan pl;
@@ -784,8 +806,8 @@ tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_pack
     return fail(TQ_EUNSUPPORTED, "no decode kernel for K (mode %d, %d bits) with V (mode %d, %d bits)", k->mode, k->bits, v->mode, v->bits);
   const float* Sk = nullptr;
   const float* Sv = nullptr;
-  if (kq) { if (tq_status s = sketch_on_device(k->seed, k->d, &Sk)) return s; }
-  if (vq) { if (tq_status s = sketch_on_device(v->seed, v->d, &Sv)) return s; }
+  if (kq) { if (tq_status s = sketch_on_device(k->seed, k->d, &Sk, may_alloc)) return s; }
+  if (vq) { if (tq_status s = sketch_on_device(v->seed, v->d, &Sv, may_alloc)) return s; }
   char* w = static_cast<char*>(ws);
   hipStream_t st = (hipStream_t)stream;
 

@@ -173,6 +173,10 @@ hipError_t launch_metric_scores(const MetricScoreParams& p, int kbits, int kqjl,
 hipError_t launch_metric_reduce(const MetricReduceParams& p, hipStream_t s);
 hipError_t launch_attn_ref(const AttnRefParams& p, hipStream_t s);
 hipError_t launch_relerr(const RelErrParams& p, int nblocks, hipStream_t s);
+// The static decode workspace (noalloc.hip): its size, and this device's
+// address of it (hipGetSymbolAddress, taken once per device).
+size_t static_scratch_bytes();
+hipError_t static_scratch(void** out);
 int stream_read_blocks();
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 

@@ -27,6 +27,7 @@ SCHEMES = {"kv": 0, "tq-kv": 1, "kqv": 2, "qkqv": 3, "tq-qkv": 4, "headq": 5}
 EXPORTS = ["tq_abi_version", "tq_status_str", "tq_last_error", "tq_codebook_build", "tq_scheme_modes",
            "tq_packed_layout", "tq_rotation_state", "tq_quantize", "tq_quantize_append",
            "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_attention_lens",
+           "tq_decode_attention_static",
            "tq_metrics_workspace_size", "tq_metrics", "tq_headq_fit",
            "tq_stream_read", "tq_release_cache"]
 
@@ -88,6 +89,8 @@ _sigs = {
                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "tq_decode_attention_lens": ([_P(TensorDesc), _P(Packed), _P(Packed), ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "tq_decode_attention_static": ([_P(TensorDesc), _P(Packed), _P(Packed), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "tq_metrics_workspace_size": ([_P(TensorDesc), _P(Packed), _P(Packed), _P(ctypes.c_size_t)], ctypes.c_int),
     "tq_metrics": ([_P(TensorDesc), _P(TensorDesc), _P(TensorDesc), _P(Packed), _P(Packed), _P(MetricsOut),
                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
@@ -352,6 +355,18 @@ def decode_attention(q, kp, vp, out=None, lse=None, ws=None, lens=None):
         _check(_lib.tq_decode_attention_lens(ctypes.byref(desc), ctypes.byref(kp.c), ctypes.byref(vp.c),
                                              lens.data_ptr(), out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
                                              ws.numel(), _stream()))
+    return out, lse
+
+
+def decode_attention_static(q, kp, vp, out, lse=None, lens=None):
+    """decode_attention into the caller's out [B, Hq, d] fp32 (and lse
+    [B, Hq]) with the library's static workspace: allocates nothing."""
+    desc, q4 = tensor_desc(q)
+    if lens is not None:
+        _check_index_vector(lens, desc.B, q, "lens")
+    _check(_lib.tq_decode_attention_static(ctypes.byref(desc), ctypes.byref(kp.c), ctypes.byref(vp.c),
+                                           lens.data_ptr() if lens is not None else None, out.data_ptr(),
+                                           lse.data_ptr() if lse is not None else None, _stream()))
     return out, lse
 
 

@@ -265,6 +265,23 @@ tq_status tq_decode_attention_lens(const tq_tensor_desc* q, const tq_packed* k, 
                                    const int32_t* lens, float* out, float* lse, void* ws, size_t ws_bytes,
                                    void* stream);
 
+/* tq_decode_attention (lens == NULL) or tq_decode_attention_lens (lens:
+ * device int32 [B], 4-byte aligned) without a caller workspace and without
+ * allocating: for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops, harnesses that forbid allocation).  The
+ * workspace is a static 64 MiB device array of the library, one per device,
+ * held until the process ends; its address is taken once per device, on the
+ * first call there.  A decode whose workspace (tq_decode_workspace_size)
+ * exceeds 64 MiB is refused with TQ_ENOMEM.  A cache with a QJL sketch needs
+ * that sketch (seed, d) already resident on the device -- any earlier
+ * tq_quantize or tq_decode_attention with it puts it there -- else
+ * TQ_EINVAL.  Every call on a device shares that device's array: calls that
+ * overlap in time on one device (other streams, other threads) race and
+ * must be ordered by the caller.  No part of the array needs clearing
+ * between calls.  Stream-ordered. */
+tq_status tq_decode_attention_static(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v,
+                                     const int32_t* lens, float* out, float* lse, void* stream);
+
 /* Workspace bytes tq_metrics needs. */
 tq_status tq_metrics_workspace_size(const tq_tensor_desc* q, const tq_packed* k, const tq_packed* v,
                                     size_t* bytes);
