@@ -15,7 +15,7 @@ SRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["api.cpp", "host_math.cpp", "quant.hip", "decode.hip", "decode_lut.hip", "quant_mfma.hip", "diag.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "quant_sketch.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # Keep the compiler from emitting packed-FP32 VALU instructions.
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -46,7 +46,7 @@ def build(verbose=False):
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + ["-lrocblas"]
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)

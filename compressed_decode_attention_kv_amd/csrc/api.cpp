@@ -12,8 +12,6 @@
 #include <tuple>
 #include <vector>
 
-#include <rocblas/rocblas.h>
-
 #include "internal.h"
 
 namespace tq {
@@ -144,16 +142,11 @@ void fill_signbits(uint64_t seed, int d, uint32_t* words) {
 // ---- per-device cache of the Gaussian sketch S ------------------------------------
 std::mutex g_cache_mu;
 std::map<std::tuple<int, uint64_t, int>, float*> g_sketch;
-// [S | S] in fp16, [d][2d] (S is exactly representable in fp16), per
-// (device, seed, d): the constant operand of the sketch GEMM at large d.
-std::map<std::tuple<int, uint64_t, int>, _Float16*> g_sketch_cat;
-// One rocBLAS handle per device; set_stream + gemm run under g_blas_mu.
-std::map<int, rocblas_handle> g_blas;
-std::mutex g_blas_mu;
+// S in fp16 (S is exactly representable in fp16), per (device, seed, d), in
+// the fragment order of the matrix-core sketch kernel at d >= 256.
+std::map<std::tuple<int, uint64_t, int>, _Float16*> g_sketch16;
 
 // The device copy of S for (current device, seed, d), made on first use.
-// With may_alloc false nothing is allocated: a copy not yet resident is an
-// error (the allocation-free decode).
 tq_status sketch_on_device(uint64_t seed, int d, const float** out, bool may_alloc = true) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_EDEVICE, "hipGetDevice failed");
@@ -177,104 +170,31 @@ tq_status sketch_on_device(uint64_t seed, int d, const float** out, bool may_all
   return TQ_OK;
 }
 
-tq_status sketch_cat_on_device(uint64_t seed, int d, const _Float16** out) {
+tq_status sketch16_on_device(uint64_t seed, int d, const _Float16** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_EDEVICE, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_cache_mu);
   auto key = std::make_tuple(dev, seed, d);
-  auto it = g_sketch_cat.find(key);
-  if (it != g_sketch_cat.end()) { *out = it->second; return TQ_OK; }
+  auto it = g_sketch16.find(key);
+  if (it != g_sketch16.end()) { *out = it->second; return TQ_OK; }
   std::vector<float> S((size_t)d * d);
   gaussian_sketch(seed, d, S.data());
-  std::vector<_Float16> cat((size_t)d * 2 * d);
-  for (int i = 0; i < d; ++i)
-    for (int k = 0; k < d; ++k) cat[(size_t)i * 2 * d + k] = cat[(size_t)i * 2 * d + d + k] = (_Float16)S[(size_t)i * d + k];
+  std::vector<_Float16> h(S.size());
+  for (int row = 0; row < d; ++row)
+    for (int col = 0; col < d; ++col)  // exact: S is defined in fp16
+      h[sketch_fragment_index(d, row, col)] = (_Float16)S[(size_t)row * d + col];
   _Float16* p = nullptr;
-  if (hipMalloc(&p, cat.size() * sizeof(_Float16)) != hipSuccess) return fail(TQ_ENOMEM, "hipMalloc of the sketch failed");
-  if (hipMemcpy(p, cat.data(), cat.size() * sizeof(_Float16), hipMemcpyHostToDevice) != hipSuccess) {
+  if (hipMalloc(&p, h.size() * sizeof(_Float16)) != hipSuccess) return fail(TQ_ENOMEM, "hipMalloc of the sketch failed");
+  if (hipMemcpy(p, h.data(), h.size() * sizeof(_Float16), hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(p);
     return fail(TQ_EDEVICE, "hipMemcpy of the sketch failed");
   }
-  g_sketch_cat[key] = p;
+  g_sketch16[key] = p;
   *out = p;
   return TQ_OK;
 }
 
-// PROD on the generic path (fp32 inputs, or d != 128): S r is a
-// [rows x d] x [d x d] GEMM, run by rocBLAS in chunks of vectors.  The quantiser writes 2^12 r as fp16
-// hi | lo rows; P = [r_hi | r_lo] [S | S]^T with fp16 products (exact) and
-// fp32 accumulation; a small kernel packs the signs.  Scratch for one chunk
-// (8 d bytes per row) is taken from and returned to the stream's pool.
-// Scratch per chunk: 8 d bytes per row (fp16 hi|lo residual + fp32 product),
-// 128 MiB in all, i.e. 16384 rows at d = 1024 and 131072 at d = 128.
-constexpr long kSketchChunkBytes = 128l << 20;
-
 tq_status hip_status(hipError_t e, const char* what);
-
-tq_status quantize_prod_gemm(const QuantParams& p0, hipStream_t st) {
-  const int d = p0.d;
-  const long BH = (long)p0.B * p0.H;
-  const long chunk_rows = kSketchChunkBytes / (8l * d);
-  int tn, nbh_per;
-  if (p0.T >= chunk_rows) {
-    tn = (int)chunk_rows;
-    nbh_per = 1;
-  } else {
-    tn = p0.T;
-    nbh_per = (int)std::max<long>(1, std::min<long>(BH, chunk_rows / p0.T));
-  }
-  const size_t rows = (size_t)tn * nbh_per;
-  const size_t rc_bytes = rows * 2 * d * sizeof(_Float16), p_bytes = rows * d * sizeof(float);
-  const _Float16* scat = nullptr;
-  if (tq_status s = sketch_cat_on_device(p0.seed_for_cat, d, &scat)) return s;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(TQ_EDEVICE, "hipGetDevice failed");
-  rocblas_handle hb = nullptr;
-  {
-    std::lock_guard<std::mutex> lk(g_blas_mu);
-    auto it = g_blas.find(dev);
-    if (it == g_blas.end()) {
-      if (rocblas_create_handle(&hb) != rocblas_status_success) return fail(TQ_EDEVICE, "rocblas_create_handle failed");
-      g_blas[dev] = hb;
-    } else {
-      hb = it->second;
-    }
-  }
-  void* ws = nullptr;
-  if (hipMallocAsync(&ws, rc_bytes + p_bytes, st) != hipSuccess) return fail(TQ_ENOMEM, "sketch scratch allocation failed");
-  _Float16* rcat = reinterpret_cast<_Float16*>(ws);
-  float* P = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + rc_bytes);
-  tq_status status = TQ_OK;
-  const float one = 1.0f, zero = 0.0f;
-  for (long bh0 = 0; bh0 < BH && status == TQ_OK; bh0 += nbh_per) {
-    for (int t0 = 0; t0 < p0.T && status == TQ_OK; t0 += tn) {
-      QuantParams c = p0;
-      c.bh0 = (int)bh0;
-      c.nbh = (int)std::min<long>(nbh_per, BH - bh0);
-      c.t0 = t0;
-      c.tn = tn;
-      c.rcat = rcat;
-      if ((status = hip_status(launch_quantize(c, st), "quantize launch"))) break;
-      rocblas_status rs;
-      {
-        std::lock_guard<std::mutex> lk(g_blas_mu);
-        rs = rocblas_set_stream(hb, st);
-        if (rs == rocblas_status_success)
-          rs = rocblas_gemm_ex(hb, rocblas_operation_transpose, rocblas_operation_none, d, c.nbh * tn, 2 * d, &one,
-                               scat, rocblas_datatype_f16_r, 2 * d, rcat, rocblas_datatype_f16_r, 2 * d, &zero,
-                               P, rocblas_datatype_f32_r, d, P, rocblas_datatype_f32_r, d, rocblas_datatype_f32_r,
-                               rocblas_gemm_algo_standard, 0, 0);
-      }
-      if (rs != rocblas_status_success) {
-        status = fail(TQ_EDEVICE, "rocblas_gemm_ex failed (%d)", (int)rs);
-        break;
-      }
-      status = hip_status(launch_sign_pack(P, c, st), "sign pack launch");
-    }
-  }
-  (void)hipFreeAsync(ws, st);
-  return status;
-}
 
 // Grid for the index search: a cell width of a third of the smallest gap
 // between boundaries puts at most one boundary in any three adjacent cells.
@@ -732,14 +652,14 @@ tq_status quantize_core(const tq_tensor_desc* x, int mode, int bits, uint64_t se
       const int nblocks = (int)std::max<long>(1, std::min<long>((tiles + 3) / 4, (long)cus * 8));
       status = hip_status(launch_quantize_mfma(p, grid, nblocks, st), "quantize launch");
     }
+  } else if (mode == TQ_MODE_PROD && quant_grid(x->d, bits, &grid) && quant_sketch_supported(p, grid)) {
+    // PROD at d >= 256: the sketch projection is a real GEMM over the token
+    // batch, on the matrix cores.
+    if (tq_status s = sketch16_on_device(seed, x->d, &p.S16)) status = s;
+    else status = hip_status(launch_quantize_sketch(p, grid, st), "quantize launch");
   } else {
-    p.bh0 = 0; p.nbh = x->B * x->H; p.t0 = 0; p.tn = x->T; p.rcat = nullptr;
-    if (mode == TQ_MODE_PROD) {
-      p.seed_for_cat = seed;
-      status = quantize_prod_gemm(p, st);
-    } else {
-      status = hip_status(launch_quantize(p, st), "quantize launch");
-    }
+    p.bh0 = 0; p.nbh = x->B * x->H; p.t0 = 0; p.tn = x->T;
+    status = hip_status(launch_quantize(p, st), "quantize launch");
   }
   if (rb) (void)hipFreeAsync(rb, st);
   if (status != TQ_OK) return status;
@@ -1023,19 +943,11 @@ tq_status tq_release_cache(void) {
     (void)hipFree(kv.second);
   }
   g_sketch.clear();
-  for (auto& kv : g_sketch_cat) {
+  for (auto& kv : g_sketch16) {
     (void)hipSetDevice(std::get<0>(kv.first));
     (void)hipFree(kv.second);
   }
-  g_sketch_cat.clear();
-  {
-    std::lock_guard<std::mutex> bl(g_blas_mu);
-    for (auto& kv : g_blas) {
-      (void)hipSetDevice(kv.first);
-      (void)rocblas_destroy_handle(kv.second);
-    }
-    g_blas.clear();
-  }
+  g_sketch16.clear();
   (void)hipSetDevice(cur);
   return ok();
 }

@@ -99,12 +99,14 @@ __device__ __forceinline__ void wht_group(float* v, int j, int L) {
       }
     }
   }
+  // Cross-lane stage: the upper lane of a pair keeps o - v, the lower v + o,
+  // both as one fma with a +-1 factor (o - v and v + o exactly).
   for (int m = 1; m < L; m <<= 1) {
-    const bool upper = (j & m) != 0;
+    const float sg = (j & m) ? -1.f : 1.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      float o = shfl_xor_f(v[e], m);
-      v[e] = upper ? (o - v[e]) : (v[e] + o);
+      const float o = shfl_xor_f(v[e], m);
+      v[e] = fmaf(v[e], sg, o);
     }
   }
 }

@@ -41,13 +41,10 @@ struct QuantParams {
   const float* basis;   // HEADQ: [H][d][rank] (device)
   int rank, side_bits;
   uint8_t* codes; float* norms; uint8_t* qjl; float* gamma; uint8_t* side; float* side_scale;
-  // Window of the launch: heads [bh0, bh0 + nbh), tokens [t0, t0 + tn).  With
-  // rcat set (PROD through a library GEMM), the kernel writes 2^12 r of each
-  // vector as fp16 hi | lo, row (bh - bh0) * tn + (t - t0) of [rows][2 d],
-  // instead of computing S r itself.
+  // Window of a generic-kernel launch: heads [bh0, bh0 + nbh), tokens
+  // [t0, t0 + tn).
   int bh0, nbh, t0, tn;
-  _Float16* rcat;
-  uint64_t seed_for_cat;  // host side only: the seed of S for the GEMM path
+  const _Float16* S16;    // PROD at d >= 256: S in fp16 (exact), fragment order (device)
   const float* rbasis;    // HEADQ: (Pi U_h)^T per head, [H][rank][d]
   // Append: token t of sequence b is written to slot pos[b] + t (device
   // int32 [B]); slots outside [0, T_cap) are skipped.  NULL: slot t.
@@ -148,9 +145,12 @@ struct RelErrParams {
 
 // ---- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
-// Sign bits of the sketch P [rows][d] (row-major, rows as in QuantParams::rcat)
-// into the sign bits of the (bits+1)-bit code fields; zero vectors keep all-zero fields.
-hipError_t launch_sign_pack(const float* P, const QuantParams& p, hipStream_t s);
+// PROD at d = 256..1024 with the sketch projection on the matrix cores (quant_sketch.hip).
+bool quant_sketch_supported(const QuantParams& p, const QuantGrid& grid);
+// Index of S[row][col] in the fragment-ordered fp16 copy of S that the
+// matrix-core sketch kernel reads (QuantParams::S16).
+size_t sketch_fragment_index(int d, int row, int col);
+hipError_t launch_quantize_sketch(const QuantParams& p, const QuantGrid& grid, hipStream_t s);
 // (Pi U_h)^T of every head into out [H][rank][d] (device).
 hipError_t launch_rotate_basis(const QuantParams& p, float* out, hipStream_t s);
 // Matrix-core write side (fp16 input, d = 128, PLAIN/MSE/PROD).

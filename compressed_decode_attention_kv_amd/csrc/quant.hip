@@ -115,7 +115,8 @@ __device__ __forceinline__ void headq_side(const QuantParams& p, const float* v,
 template <int BITS, int MODE, typename TIN>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   __shared__ float s_cent[16], s_bnd[16];
-  // HEADQ: (Pi U_h)^T, d * rank floats, in dynamic LDS (sized at launch).
+  // Dynamic LDS (sized at launch).  HEADQ: (Pi U_h)^T, d * rank floats.
+  // PROD: each wave's token residuals, 64 / L tokens x d floats per wave.
   extern __shared__ float s_side[];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
       for (int k = 0; k < NB; ++k) c += (v[e] >= s_bnd[k]) ? 1u : 0u;
       idx[e] = nu > 0.f ? c : 0u;
     }
-    // PROD: (BITS+1)-bit fields whose sign bits sign_pack_kernel fills in.
+    // PROD: (BITS+1)-bit fields; the sketch signs are added below.
     constexpr int FB = Field<BITS, MODE == TQ_MODE_PROD>::kBits;
     uint32_t w[FB];
 #pragma unroll
@@ -186,16 +187,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
     const int64_t tw = slot0 + t;
     const bool wr = valid && tw >= 0 && tw < p.T_cap;
     const int64_t vec = vbase + tw;
-    if (wr) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vec * (d * FB / 8)) + j * FB;
-#pragma unroll
-      for (int k = 0; k < FB; ++k) __builtin_nontemporal_store(w[k], dst + k);
-      if (j == 0) __builtin_nontemporal_store(nu, p.norms + vec);
-    }
 
     if (MODE == TQ_MODE_PROD) {
       // Residual of the rotated unit vector and its 1-bit Gaussian sketch
       // ([P1] "Esquemas de Cuantización" 2-3, "Contribuciones Clave" 1).
+      // This kernel takes PROD only at d <= 128 (and as a fallback for
+      // launches the matrix-core sketch kernel cannot index): the token's
+      // residual goes through LDS and lane j forms sketch rows 32 j .. 32 j
+      // + 31 as fp32 dot products against S (exact in fp32).
       float g2 = 0.f;
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
@@ -203,21 +202,39 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
         g2 = fmaf(v[e], v[e], g2);
       }
       g2 = group_sum(g2, L);
-      // Residual x 2^12 as fp16 hi (toward zero) + lo: r - hi is exact in
-      // fp32, so the sketch GEMM's fp16 products reproduce S r to ~2^-22.
-      if (valid) {
-        _Float16* row = p.rcat + ((size_t)blockIdx.y * p.tn + (t - p.t0)) * (2 * d);
+      float* rs = s_side + (wave * vpw + slot) * d;
+      __syncthreads();  // the previous step's readers are done with rs
 #pragma unroll
-        for (int e = 0; e < 32; e += 2) {
-          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-          const float r0 = v[e] * 4096.0f, r1 = v[e + 1] * 4096.0f;
-          const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-          const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(r0 - (float)hi[0], r1 - (float)hi[1]));
-          *reinterpret_cast<h2*>(row + 32 * j + e) = hi;
-          *reinterpret_cast<h2*>(row + d + 32 * j + e) = lo;
+      for (int e = 0; e < 32; ++e) rs[32 * j + e] = v[e];
+      __syncthreads();
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      uint32_t sw = 0;
+      for (int i = 0; i < 32; ++i) {
+        const f4* srow = reinterpret_cast<const f4*>(p.S + (size_t)(32 * j + i) * d);
+        const f4* rr = reinterpret_cast<const f4*>(rs);
+        float a0 = 0.f, a1 = 0.f;
+        for (int k = 0; k < d / 4; ++k) {
+          const f4 sv = srow[k], rv = rr[k];
+          a0 = fmaf(sv.x, rv.x, a0);
+          a1 = fmaf(sv.y, rv.y, a1);
+          a0 = fmaf(sv.z, rv.z, a0);
+          a1 = fmaf(sv.w, rv.w, a1);
         }
-        if (j == 0 && wr) __builtin_nontemporal_store(sqrtf(g2), p.gamma + vec);
+        sw |= (a0 + a1 >= 0.f ? 1u : 0u) << i;
       }
+      if (!(nu > 0.f)) sw = 0;  // a zero vector keeps all-zero fields
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int bit = FB * e + BITS;
+        w[bit >> 5] |= ((sw >> e) & 1u) << (bit & 31);
+      }
+      if (j == 0 && wr) __builtin_nontemporal_store(nu > 0.f ? sqrtf(g2) : 0.f, p.gamma + vec);
+    }
+    if (wr) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + vec * (d * FB / 8)) + j * FB;
+#pragma unroll
+      for (int k = 0; k < FB; ++k) __builtin_nontemporal_store(w[k], dst + k);
+      if (j == 0) __builtin_nontemporal_store(nu, p.norms + vec);
     }
 
     if (MODE == TQ_MODE_HEADQ) {
@@ -351,43 +368,12 @@ __global__ __launch_bounds__(kThreads) void rotate_basis_kernel(QuantParams p, f
   }
 }
 
-// Sign bits of P rows, one thread per (row, 32-row group): bit k of the group
-// goes to bit (b+1) k + b of the group's (b+1)-bit fields, whose codes the
-// quantize kernel wrote (stream order makes them visible here).
-template <int BITS>
-__global__ __launch_bounds__(256) void sign_pack_kernel(const float* __restrict__ P, QuantParams p) {
-  constexpr int FB = Field<BITS, true>::kBits;
-  const int d = p.d, words = d / 32;
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long)p.nbh * p.tn * words) return;
-  const long row = idx / words;
-  const int w = (int)(idx % words);
-  const int hh = (int)(row / p.tn), t = p.t0 + (int)(row % p.tn);
-  if (t >= p.T) return;
-  const int bh = p.bh0 + hh;
-  const int64_t tw = (int64_t)t + (p.pos ? p.pos[bh / p.H] : 0);
-  if (tw < 0 || tw >= p.T_cap) return;
-  const int64_t vec = (int64_t)bh * p.T_cap + tw;
-  if (!(p.norms[vec] > 0.f)) return;  // a zero vector keeps all-zero fields
-  const float* pr = P + row * d + 32 * w;
-  uint32_t* grp = reinterpret_cast<uint32_t*>(p.codes + vec * (d * FB / 8)) + w * FB;
-  uint32_t f[FB];
-#pragma unroll
-  for (int k = 0; k < FB; ++k) f[k] = grp[k];
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int bit = FB * k + BITS;
-    f[bit >> 5] |= (pr[k] >= 0.f ? 1u : 0u) << (bit & 31);
-  }
-#pragma unroll
-  for (int k = 0; k < FB; ++k) __builtin_nontemporal_store(f[k], grp + k);
-}
-
 template <int BITS, int MODE>
 hipError_t launch_q(const QuantParams& p, hipStream_t s) {
   const int vpw = 64 / p.L;
   dim3 grid((p.tn + 4 * vpw * kSteps - 1) / (4 * vpw * kSteps), p.nbh);
-  const size_t dyn = MODE == TQ_MODE_HEADQ ? (size_t)p.d * p.rank * sizeof(float) : 0;
+  const size_t dyn = MODE == TQ_MODE_HEADQ ? (size_t)p.d * p.rank * sizeof(float)
+                    : MODE == TQ_MODE_PROD ? (size_t)(kThreads / 64) * vpw * p.d * sizeof(float) : 0;
   if (p.dtype == TQ_F16)
     hipLaunchKernelGGL((quant_kernel<BITS, MODE, _Float16>), grid, dim3(kThreads), dyn, s, p);
   else
@@ -436,18 +422,6 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
 
 hipError_t launch_rotate_basis(const QuantParams& p, float* out, hipStream_t s) {
   hipLaunchKernelGGL(rotate_basis_kernel, dim3(p.H), dim3(kThreads), 0, s, p, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_sign_pack(const float* P, const QuantParams& p, hipStream_t s) {
-  const long n = (long)p.nbh * p.tn * (p.d / 32);
-  const dim3 grid((unsigned)((n + 255) / 256));
-  switch (p.bits) {
-    case 1: hipLaunchKernelGGL(sign_pack_kernel<1>, grid, dim3(256), 0, s, P, p); break;
-    case 2: hipLaunchKernelGGL(sign_pack_kernel<2>, grid, dim3(256), 0, s, P, p); break;
-    case 3: hipLaunchKernelGGL(sign_pack_kernel<3>, grid, dim3(256), 0, s, P, p); break;
-    default: return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 

@@ -12,13 +12,12 @@
  * Conventions for every entry point
  *   - Pointers documented as "device" are HIP device memory owned by the
  *     caller; "host" pointers are ordinary CPU memory.  The library owns only
- *     its cached per-(device, seed, d) constants and one rocBLAS handle per
- *     device (all freed by tq_release_cache).  A tq_quantize of a PROD
- *     tensor that is not fp16 at d = 128 also takes a stream-ordered scratch
- *     buffer (8 d bytes per row, at most 128 MiB), and one of a HEADQ tensor a
- *     buffer for the rotated basis (4 H d rank bytes), from the stream's
- *     memory pool and returns it before the call's work completes on that
- *     stream.
+ *     its cached per-(device, seed, d) constants (freed by
+ *     tq_release_cache) and the static workspace of
+ *     tq_decode_attention_static.  A tq_quantize of a HEADQ tensor also
+ *     takes a buffer for the rotated basis (4 H d rank bytes) from the
+ *     stream's memory pool and returns it before the call's work completes
+ *     on that stream.
  *   - Every call returns tq_status.  All argument and descriptor checks run
  *     on the host before any HIP call, so a rejected call touches no GPU
  *     state.  tq_last_error() returns a thread-local message for the last

@@ -5,12 +5,12 @@ length).
 
   * Appended planes equal those of quantising the whole sequence at once,
     slot by slot, at ragged per-sequence positions: bit-exact, since every
-    token is quantised on its own by the same kernel (the fp32 QJL sketch goes
-    through a library GEMM whose summation order may differ with its shape,
-    so there one sign bit of the code fields may flip where S r is within
-    rounding of zero).  Matrix-core path (fp16, d=128), generic path (fp32),
-    GEMM sketch (fp32 PROD), HeadQ.  Slots past T_cap are skipped and the
-    neighbouring head's slots keep their bytes.
+    token is quantised on its own by the same sequence of operations whatever
+    its slot in a tile.  Matrix-core path (fp16 and fp32, d=128), the
+    matrix-core sketch at d=256 (fp32 PROD keys), HeadQ.  Slots past T_cap are
+    skipped and the neighbouring head's slots keep their bytes.  The appended
+    sketched slots are also checked against the oracle (codes and signs exact
+    outside the decision band).
   * Decode over ragged lengths (full, partial, one token, zero) against the
     float64 oracle on each sequence's own prefix; a length-0 sequence gives
     out = 0 and lse = -inf.  Table-driven (d=128) and generic (d=64) kernels.
@@ -60,8 +60,9 @@ def _cmp_slots(a, b, slots, label, sign_tol=0, field_bits=0):
 @pytest.mark.parametrize("scheme,dtype,d", [
     ("kqv", torch.float16, 128),    # matrix-core quantiser, MSE keys, PROD values
     ("qkqv", torch.float16, 128),
-    ("kqv", torch.float32, 128),    # generic quantiser; PROD through the GEMM sketch
-    ("tq-qkv", torch.float32, 256),
+    ("kqv", torch.float32, 128),    # matrix-core quantiser on the fp32 hi + lo split
+    ("tq-qkv", torch.float32, 256), # PROD keys through the matrix-core sketch kernel
+    ("qkqv", torch.float16, 64),    # generic quantiser with the in-kernel sketch
     ("headq", torch.float16, 128),  # HeadQ side code (generic quantiser)
 ])
 def test_append_matches_whole_sequence(tq, scheme, dtype, d):
@@ -80,7 +81,7 @@ def test_append_matches_whole_sequence(tq, scheme, dtype, d):
         tq.quantize_append(xn, which, scheme, 4, torch.tensor(pos, dtype=torch.int32, device="cuda"), cache, seed=9)
         torch.cuda.synchronize()
         a, c = whole.planes(), cache.planes()
-        sign_tol = 1 if (dtype == torch.float32 and cache.c.mode == tq.MODE_PROD) else 0
+        sign_tol = 0
         fb = cache.c.bits + 1
         label = "%s %s d=%d which=%d" % (scheme, dtype, d, which)
         for b in range(B):
@@ -96,6 +97,12 @@ def test_append_matches_whole_sequence(tq, scheme, dtype, d):
                         got = {n: v[base + Tmax - 5 + k:base + Tmax - 4 + k] for n, v in c.items()}
                         ref = {n: v[base + src + k:base + src + k + 1] for n, v in a.items()}
                         _cmp_slots(ref, got, slice(0, 1), label + " clipped b=%d h=%d k=%d" % (b, h, k), sign_tol, fb)
+                if cache.c.mode == tq.MODE_PROD and b < 2:
+                    # The appended slots against the oracle on their source tokens.
+                    sl = slice(base + pos[b], base + pos[b] + Tn)
+                    src = xn[b, h].double().cpu().numpy()
+                    pu.oracle_match(src, {n: v[sl] for n, v in c.items()}, pu.MODE_NAMES[cache.c.mode],
+                                    cache.c.bits, 9, label=label + " appended vs oracle")
 
 
 def test_append_rejects_mismatched_cache(tq):

@@ -150,14 +150,18 @@ def test_headq_gqa_full_size_sampled(tq):
     assert abs(m["kl_mean"] - kl.mean()) <= pu.KL_ATOL and abs(m["kl_max"] - kl.max()) <= pu.KL_ATOL
 
 
-@pytest.mark.parametrize("scheme,d,H,T", [("kqv", 512, 1, 40000), ("qkqv", 256, 5, 16000)])
-def test_sketch_gemm_chunks(tq, scheme, d, H, T):
-    """fp32, B=1, n=4: the QJL sketch of the generic path runs as a library
-    GEMM over fp16 hi/lo residual rows, in chunks of 128 MiB of scratch
-    (8 d bytes per row).  d=512, T=40000 gives two chunks along the head, the
-    second ragged; d=256, 5 heads of 16000 gives chunks of four heads and
-    one.  Codes, signs, norms, gamma and outputs against the oracle."""
+@pytest.mark.parametrize("scheme,d,H,T,dtype", [("kqv", 512, 1, 40000, torch.float32),
+                                                ("qkqv", 256, 5, 16001, torch.float32),
+                                                ("qkqv", 1024, 3, 1000, torch.float16)])
+def test_sketch_tiles(tq, scheme, d, H, T, dtype):
+    """B=1, n=4: at d >= 256 the QJL sketch S r runs on the matrix cores over
+    tiles of 32768 / d tokens of one head (the residuals staged in LDS as
+    fp16 hi + lo).  Many tiles per head with a ragged last tile (T = 40000
+    at d=512: 625 tiles of 64; T = 16001 at d=256: the last tile holds one
+    token), several heads, fp32 and fp16 inputs.  Codes, signs, norms, gamma
+    and outputs against the oracle."""
     from tests import gpu_util
     K, V, Q = synth.isotropic(1, H, 2, T, d, seed=77, kv_std=1.0, dtype=np.float32)
-    worst, n_band, *_ = gpu_util.run_case(tq, K, V, Q, scheme, 4, seed=19, label="gemm %s d=%d" % (scheme, d))
-    print("sketch gemm", scheme, "worst rel L2 %.3g band %d" % (worst, n_band))
+    worst, n_band, *_ = gpu_util.run_case(tq, K, V, Q, scheme, 4, seed=19, dtype=dtype,
+                                          label="sketch %s d=%d" % (scheme, d))
+    print("sketch tiles", scheme, d, "worst rel L2 %.3g band %d" % (worst, n_band))
