@@ -6,10 +6,14 @@ workload: B=16, 32 heads, d=128, context 32768, fp16 K/V ~ N(0, 1/d), one
 fp16 query per head, scheme KQV at n=4 (KV and QKQV with --scheme).
 
 Prints one JSON line.  `value` = decode GB/s of packed cache read
-(algorithmic packed bytes / time of the decode entry point); quantize tok/s
-and the whole-step time ride along.  `roofline` covers the decode chain;
-`cpu_baseline` times the float64 oracle on a bounded sample of the same
-workload on the host cores.
+(algorithmic packed bytes / time of the decode entry point, HIP events on the
+stream the kernels run on); quantize tok/s and the whole-step time ride
+along.  `roofline` covers the decode chain, `quantize_roofline` the K + V
+quantize of the step; `quality` holds the measures of the packed cache at the
+workload's full size (computed outside the timed region); `cpu_baseline`
+times the float64 oracle on a bounded sample of the same workload on the
+host cores.  --workload heavy-tailed | low-rank | headq-gqa prints the line of
+another regime at its own full size instead (timings and quality).
 """
 import argparse
 import json
@@ -25,6 +29,12 @@ HBM_PEAK_GBS = 8000.0
 PACKED_BYTES = {  # per token-head (K + V) at d=128, n=4, fp32 norms / gamma
     "kv": 68 + 68, "kqv": 68 + 72, "qkqv": 72 + 72, "tq-kv": 68 + 68, "tq-qkv": 72 + 68,
 }
+# Arithmetic of the path: fp16 operands (value centroids, the fp16 sketch S,
+# S q and the softmax weights in the value sums; the write side's matrix-core
+# products) with fp32 accumulation; key scores against fp32 centroids.
+ARITH = "f16xf16+f32acc"
+QUALITY_KEYS = ("kl_mean", "kl_max", "top5_recall", "relmse_k", "relmse_v", "dir_err_k", "dir_err_v",
+                "fisher_mean", "spearman_fisher_kl", "spearman_keymse_kl", "a2_value_mean", "n_queries")
 
 
 def packed_bytes_total(kp, vp):
@@ -37,28 +47,64 @@ def packed_bytes_total(kp, vp):
     return n // 16 * 16
 
 
-def measured_traffic(scheme):
-    """HBM bytes per decode-chain launch from the committed rocprofv3 counter
-    summary, if it was taken on the current decode sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "decode_traffic_isotropic_%s.txt" % scheme)
+def _profile_fields(name):
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     fields = {}
     for line in open(path):
-        if "=" in line and not line.startswith("#"):
-            k, v = line.strip().split("=", 1)
+        line = line.strip().lstrip("#").strip()
+        if "=" in line:
+            k, v = line.split("=", 1)
             fields[k.strip()] = v.strip()
-    from compressed_decode_attention_kv_amd.profiling import decode_sources_sha
-    if fields.get("decode_sources_sha1") != decode_sources_sha():
+    return fields
+
+
+def measured_traffic(scheme, chain="decode"):
+    """HBM bytes per launch of the decode chain (or of the step's K + V
+    quantize, chain="quantize") from the committed rocprofv3 counter summary,
+    if it was taken on the current sources of that chain (else None)."""
+    from compressed_decode_attention_kv_amd import profiling as pf
+    f = _profile_fields("traffic_isotropic_%s.txt" % scheme)
+    if not f:
         return None
-    return float(fields["decode_chain_bytes"])
+    sha = pf.decode_sources_sha() if chain == "decode" else pf.quantize_sources_sha()
+    if f.get("%s_sources_sha1" % chain) != sha or "%s_chain_bytes" % chain not in f:
+        return None
+    return float(f["%s_chain_bytes" % chain])
+
+
+def measured_mfma_util(scheme):
+    """MfmaUtil (%) of the quantize kernels from the committed SQ counter
+    summary, if it was taken on the current quantize sources (else None)."""
+    from compressed_decode_attention_kv_amd import profiling as pf
+    path = os.path.join(ROOT, "profiles", "counters_isotropic_%s.txt" % scheme)
+    f = _profile_fields("counters_isotropic_%s.txt" % scheme)
+    if not f or f.get("quantize_sources_sha1") != pf.quantize_sources_sha():
+        return None
+    out = {}
+    cols = None
+    for line in open(path):
+        if line.startswith("kernel"):
+            cols = line.split()
+        elif cols and line.startswith(pf.QCHAIN):
+            name = line[:90].strip()
+            vals = line[90:].split()
+            try:  # columns counted from the right ("VALU insts" is two words in the header)
+                out[name] = float(vals[cols.index("MfmaUtil%") - len(cols)])
+            except (ValueError, IndexError):
+                pass
+    return out or None
 
 
 def cpu_baseline(scheme, budget_s=12.0):
     """Oracle (float64 numpy) on whole (b, h) slices of the same workload:
     quantise K and V of one head (32768 tokens) and decode its query; repeat
-    slices until the budget is spent.  Scaled to decode GB/s of packed bytes."""
+    slices until the budget is spent.  Scaled to decode GB/s of packed bytes.
+    Beside it, the oracle on the single-head workload (T=4096, d=128, 16
+    queries, fp32 N(0,1), KQV n=4) with one BLAS thread."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
     from compressed_decode_attention_kv_amd import synth
     from oracle import attention as oat
     from oracle import quantizer as oqz
@@ -89,10 +135,23 @@ def cpu_baseline(scheme, budget_s=12.0):
         cores = os.cpu_count()
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     gbs = done * PACKED_BYTES[scheme] / t_dec / 1e9
+    # Single head, T=4096, one thread.
+    K1, V1, Q1 = synth.isotropic_small(seed=0)
+    K1, V1, Q1 = K1[0, 0].astype(np.float64), V1[0, 0].astype(np.float64), Q1[0].astype(np.float64)
+    s1k, s1v = oqz.QState(128, oqz.MSE, 4, 0), oqz.QState(128, oqz.PROD, 4, 0)
+    with threadpool_limits(limits=1):
+        t0 = time.time()
+        q1k, q1v = oqz.quantize(K1, s1k), oqz.quantize(V1, s1v)
+        t1 = time.time()
+        oat.attend(Q1, oqz.dequantize(q1k, s1k), oqz.dequantize(q1v, s1v))
+        t2 = time.time()
     return {"value": gbs, "unit": "GB/s", "cores": min(cores, threads), "kind": "oracle",
             "sample": "%d whole (batch, head) slices x 32768 tokens, d=128, scheme %s n=4 "
                       "(decode = dense dequantise + attention); quantize %.3g tok/s"
-                      % (slices, scheme, done / t_quant)}
+                      % (slices, scheme, done / t_quant),
+            "single_head_1thread": {"workload": "T=4096 d=128, 16 queries, fp32 N(0,1), kqv n=4", "threads": 1,
+                                    "quantize_ms": round(1e3 * (t1 - t0), 2), "decode_ms": round(1e3 * (t2 - t1), 2),
+                                    "decode_GBps": round(4096 * 140 / (t2 - t1) / 1e9, 5)}}
 
 
 def _median_ms(torch, fn, steps, warmup):
@@ -109,9 +168,23 @@ def _median_ms(torch, fn, steps, warmup):
     return ms[len(ms) // 2]
 
 
+def _quality(tq, q, k, v, kp, vp):
+    """Quality measures of the packed cache against the raw tensors
+    (tq_metrics on the GPU), rounded."""
+    m = tq.metrics(q, k, v, kp, vp)
+    out = {}
+    for key in QUALITY_KEYS:
+        x = m[key]
+        if isinstance(x, float) and math.isnan(x):
+            continue
+        out[key] = int(x) if key == "n_queries" else float("%.6g" % x)
+    return out
+
+
 def other_workload(args):
     """The pages' other regimes at full size (not the headline): one JSON
-    line with the median quantize / decode time per scheme."""
+    line with the median quantize / decode time and the quality measures per
+    scheme."""
     import numpy as np
     import torch
     from compressed_decode_attention_kv_amd import synth, tq
@@ -136,10 +209,12 @@ def other_workload(args):
                 moved = in_bytes + sum(packed_bytes(p) for p in ps)
                 rows.append({"scheme": scheme, "n_bits": n, "quantize_ms": round(q_ms, 4),
                              "quantize_tok_per_s": round(B * T / (q_ms * 1e-3), 1),
-                             "quantize_hbm_GBps": round(moved / (q_ms * 1e-3) / 1e9, 1)})
+                             "quantize_hbm_GBps": round(moved / (q_ms * 1e-3) / 1e9, 1),
+                             "quality": _quality(tq, None, K, V, ps[0], ps[1])})
         cfg = "heavy-tailed: B=4 H=8 T=131072 d=128 fp32 Student-t(3) + 1% outlier tokens; quantize only"
     elif args.workload == "low-rank":
-        K, V, Q = synth.low_rank(4, 65536, 1024, 16, seed=40)
+        G = 64   # queries per head: half inside the key subspace, half isotropic
+        K, V, Q = synth.low_rank(4, 65536, 1024, G, seed=40)
         K, V, Q = (torch.from_numpy(x).cuda() for x in (K, V, Q))
         for scheme in ("kqv", "qkqv"):
             kp = tq.quantize(K, tq.KEYS, scheme, 4, 3)
@@ -151,8 +226,9 @@ def other_workload(args):
             d_ms = _median_ms(torch, lambda: tq.decode_attention(Q, kp, vp, out, lse, ws), args.steps, args.warmup)
             nb = packed_bytes(kp) + packed_bytes(vp)
             rows.append({"scheme": scheme, "n_bits": 4, "quantize_ms": round(q_ms, 4), "decode_ms": round(d_ms, 4),
-                         "decode_GBps": round(nb / (d_ms * 1e-3) / 1e9, 1), "queries": int(Q.shape[1])})
-        cfg = "low-rank: H=4 T=65536 d=1024 fp32, K rank 16 (0.7^i) + 0.01 noise, 16 queries per head"
+                         "decode_GBps": round(nb / (d_ms * 1e-3) / 1e9, 1), "queries": int(Q.shape[1]),
+                         "quality": _quality(tq, Q, K, V, kp, vp)})
+        cfg = "low-rank: H=4 T=65536 d=1024 fp32, K rank 16 (0.7^i) + 0.01 noise, 64 queries per head"
     else:  # headq-gqa
         B, Hkv, G, T, d, r = 8, 8, 4, 131072, 128, 16
         K, V, Q, C = synth.device_rope_gqa(B, Hkv, G, T, d, seed=55)
@@ -170,11 +246,12 @@ def other_workload(args):
             nb = packed_bytes(kp) + packed_bytes(vp)
             rows.append({"scheme": scheme, "n_bits": 4, "quantize_ms": round(q_ms, 4), "decode_ms": round(d_ms, 4),
                          "decode_GBps": round(nb / (d_ms * 1e-3) / 1e9, 1),
-                         "decode_pct_hbm_peak": round(100.0 * nb / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+                         "decode_pct_hbm_peak": round(100.0 * nb / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                         "quality": _quality(tq, Q, K, V, kp, vp)})
         cfg = "headq-gqa: B=8, 8 KV heads x 4 query heads, T=131072, d=128, fp16 post-RoPE keys; rank-16 basis " \
               "fitted from 4096 calibration queries per KV head"
     print(json.dumps({"workload": args.workload, "config": cfg, "data": "synthetic", "n_gpus": 1,
-                      "steps": args.steps, "warmup": args.warmup, "results": rows}))
+                      "steps": args.steps, "warmup": args.warmup, "dtype": ARITH, "results": rows}))
 
 
 def main():
@@ -189,11 +266,15 @@ def main():
                          "(default: the other two of kv, kqv, qkqv; '' for none)")
     ap.add_argument("--no-gen-step", action="store_true",
                     help="skip the append + decode generation-step timing (profiling runs)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="no quality pass and no MALL-flushed leg after the step loop (profiling runs: the step "
+                         "loop's decode launches are then the last full-size ones before the streaming-read "
+                         "reference)")
     ap.add_argument("--B", type=int, default=16)
     ap.add_argument("--H", type=int, default=32)
     ap.add_argument("--T", type=int, default=32768)
     ap.add_argument("--workload", default="isotropic", choices=["isotropic", "heavy-tailed", "low-rank", "headq-gqa"],
-                    help="isotropic: the headline line; the others print their own timing line")
+                    help="isotropic: the headline line; the others print their own line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
@@ -224,7 +305,8 @@ def main():
 
     def run_steps(scheme):
         """Quantize K and V, then decode, `warmup` untimed and `steps` timed
-        times; returns the packed tensors, workspace and the timings."""
+        times; returns the packed tensors, workspace, decode callable and
+        the timings."""
         kp = tq.quantize(K, tq.KEYS, scheme, n, 0)
         vp = tq.quantize(V, tq.VALUES, scheme, n, 0)
         ws = torch.empty(tq.decode_workspace_size(kp, vp, H), dtype=torch.uint8, device="cuda")
@@ -232,7 +314,8 @@ def main():
 
         def quant():
             tq._check(lib.tq_quantize(ctypes.byref(kdesc), tq.KEYS, sid, n, 0, None, None, ctypes.byref(kp.c), stream()))
-            tq._check(lib.tq_quantize(ctypes.byref(vdesc), tq.VALUES, sid, n, 0, None, None, ctypes.byref(vp.c), stream()))
+            tq._check(lib.tq_quantize(ctypes.byref(vdesc), tq.VALUES, sid, n, 0, None, None, ctypes.byref(vp.c),
+                                      stream()))
 
         def decode():
             tq._check(lib.tq_decode_attention(ctypes.byref(qdesc), ctypes.byref(kp.c), ctypes.byref(vp.c),
@@ -256,17 +339,51 @@ def main():
         q_ms = [a.elapsed_time(b) for a, b, _ in ev]
         d_ms = [b.elapsed_time(c) for _, b, c in ev]
         assert torch.isfinite(out).all().item()
-        run_steps.decode_all = sorted(d_ms)
-        return kp, vp, ws, sid, wall * 1000.0 / args.steps, sum(q_ms) / len(q_ms), sum(d_ms) / len(d_ms)
+        return {"kp": kp, "vp": vp, "ws": ws, "sid": sid, "decode": decode, "step_ms": wall * 1000.0 / args.steps,
+                "q_avg": sum(q_ms) / len(q_ms), "d_avg": sum(d_ms) / len(d_ms), "d_sorted": sorted(d_ms)}
 
-    kp, vp, ws, sid, step_ms, q_avg, d_avg = run_steps(args.scheme)
-    d_sorted = run_steps.decode_all
+    r = run_steps(args.scheme)
+    kp, vp, ws, sid = r["kp"], r["vp"], r["ws"], r["sid"]
     packed = B * H * T * PACKED_BYTES[args.scheme]
-    dec_gbs = packed / (d_avg * 1e-3) / 1e9
-    tok_s = B * T / (q_avg * 1e-3)
+    dec_gbs = packed / (r["d_avg"] * 1e-3) / 1e9
+    tok_s = B * T / (r["q_avg"] * 1e-3)
+    # Quantize: both fp16 inputs read, every packed plane written, per step.
+    q_bytes = 2 * K.numel() * K.element_size() + packed
+    q_gbs = q_bytes / (r["q_avg"] * 1e-3) / 1e9
+    d_sorted = r["d_sorted"]
+
+    res = {
+        "metric": "packed-KV decode attention GB/s (% HBM peak) + quantize tok/s, d=128 n=4",
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["step_ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": ARITH, "data": "synthetic",
+        "config": {"workload": "isotropic decode: B=%d H=%d T=%d d=%d fp16 K/V~N(0,1/d), 1 query/head, %s n=%d"
+                               % (B, H, T, d, args.scheme, n),
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "scheme": args.scheme, "n_bits": n},
+        "decode_ms": round(r["d_avg"], 4),
+        "decode_ms_median": round(d_sorted[len(d_sorted) // 2], 4),
+        "decode_ms_min": round(d_sorted[0], 4),
+        "decode_pct_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
+        "quantize_ms": round(r["q_avg"], 4),
+        "quantize_tok_per_s": round(tok_s, 1),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.scheme),
+                     "kernel": "decode chain (query prep + split decode + combine)",
+                     "algorithmic_bytes_per_launch": packed},
+        "quantize_roofline": {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+                              "traffic": measured_traffic(args.scheme, "quantize"),
+                              "kernel": "K + V quantize of one step",
+                              "algorithmic_bytes_per_launch": q_bytes,
+                              "mfma_util_pct": measured_mfma_util(args.scheme)},
+    }
 
     # Streaming-read reference: the same non-temporal 128-bit loads over a
-    # plain buffer of the packed cache's size.
+    # plain buffer of the packed cache's size (also the known-size reference
+    # of the HBM byte counters).
     sbuf = torch.empty(packed_bytes_total(kp, vp), dtype=torch.uint8, device="cuda")
     sink = torch.empty(2048, dtype=torch.int32, device="cuda")
     tq.stream_read(sbuf, sink)
@@ -279,7 +396,26 @@ def main():
     torch.cuda.synchronize()
     s_ms = sum(a.elapsed_time(b) for a, b in sev) / len(sev)
     stream_gbs = sbuf.numel() / (s_ms * 1e-3) / 1e9
+    res["stream_read_GBps"] = round(stream_gbs, 1)
+    res["stream_read_bytes"] = int(packed_bytes_total(kp, vp))
+    res["decode_pct_of_stream_read"] = round(100.0 * dec_gbs / stream_gbs, 2)
     del sbuf
+    if not args.no_extras:
+        # The decode alone, each repetition after a 1 GiB write that evicts
+        # the 256 MB MALL (the step's quantize leaves the planes in no cache:
+        # its stores are non-temporal).
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for i, (a, b) in enumerate(fev):
+            flush.fill_(i & 0xFF)
+            a.record()
+            r["decode"]()
+            b.record()
+        torch.cuda.synchronize()
+        f_ms = sorted(a.elapsed_time(b) for a, b in fev)
+        res["decode_ms_mall_flushed_median"] = round(f_ms[len(f_ms) // 2], 4)
+        del flush
+        res["quality"] = {args.scheme: _quality(tq, Q, K, V, kp, vp)}
 
     # One generation step on the same cache: append one new token per
     # (batch, head) to K and V, then decode over per-sequence lengths.  The
@@ -300,7 +436,6 @@ def main():
                                                lens.data_ptr(), out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
                                                ws.numel(), stream()))
 
-    gen_ms = None
     if not args.no_gen_step:
         for _ in range(3):
             gen_step()
@@ -311,49 +446,31 @@ def main():
             gen_step()
             b.record()
         torch.cuda.synchronize()
-        gen_ms = round(sorted(a.elapsed_time(b) for a, b in gev)[len(gev) // 2], 4)
+        res["append_decode_step_ms"] = round(sorted(a.elapsed_time(b) for a, b in gev)[len(gev) // 2], 4)
         assert torch.isfinite(out).all().item()
 
-    res = {
-        "metric": "packed-KV decode attention GB/s (% HBM peak) + quantize tok/s, d=128 n=4",
-        "value": round(dec_gbs, 1),
-        "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "isotropic decode: B=%d H=%d T=%d d=%d fp16 K/V~N(0,1/d), 1 query/head, %s n=%d"
-                               % (B, H, T, d, args.scheme, n),
-                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": d, "scheme": args.scheme, "n_bits": n},
-        "decode_ms": round(d_avg, 4),
-        "decode_ms_median": round(d_sorted[len(d_sorted) // 2], 4),
-        "decode_ms_min": round(d_sorted[0], 4),
-        "decode_pct_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
-        "stream_read_GBps": round(stream_gbs, 1),
-        "stream_read_bytes": int(packed_bytes_total(kp, vp)),
-        "decode_pct_of_stream_read": round(100.0 * dec_gbs / stream_gbs, 2),
-        "quantize_ms": round(q_avg, 4),
-        "quantize_tok_per_s": round(tok_s, 1),
-        "append_decode_step_ms": gen_ms,
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.scheme),
-                     "kernel": "decode chain (query prep + split decode + combine)",
-                     "algorithmic_bytes_per_launch": packed},
-    }
     # The other schemes of the workload, timed the same way (not the headline).
     beside = [x for x in ("kv", "kqv", "qkqv") if x != args.scheme] if args.beside is None else \
         [x for x in args.beside.split(",") if x]
-    del kp, vp, ws
+    del kp, vp, ws, r
     torch.cuda.empty_cache()
     res["beside"] = {}
     for scheme in beside:
-        bkp, bvp, bws, _, _, bq, bd = run_steps(scheme)
+        br = run_steps(scheme)
         nbytes = B * H * T * PACKED_BYTES[scheme]
-        res["beside"][scheme] = {"decode_ms": round(bd, 4), "decode_GBps": round(nbytes / (bd * 1e-3) / 1e9, 1),
-                                 "decode_pct_hbm_peak": round(100.0 * nbytes / (bd * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                                 "quantize_ms": round(bq, 4)}
-        del bkp, bvp, bws
+        res["beside"][scheme] = {"decode_ms": round(br["d_avg"], 4),
+                                 "decode_GBps": round(nbytes / (br["d_avg"] * 1e-3) / 1e9, 1),
+                                 "decode_pct_hbm_peak": round(100.0 * nbytes / (br["d_avg"] * 1e-3) / 1e9
+                                                              / HBM_PEAK_GBS, 2),
+                                 "quantize_ms": round(br["q_avg"], 4)}
+        if not args.no_extras:
+            res["quality"][scheme] = _quality(tq, Q, K, V, br["kp"], br["vp"])
+        del br
         torch.cuda.empty_cache()
+    if "quality" in res and "kqv" in res["quality"] and "qkqv" in res["quality"]:
+        # [P1] "Contribuciones Clave" 2 compares the KL of QKQV and KQV at n=4.
+        res["quality"]["kl_ratio_qkqv_over_kqv"] = round(res["quality"]["qkqv"]["kl_mean"]
+                                                         / res["quality"]["kqv"]["kl_mean"], 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.scheme)
     print(json.dumps(res))

@@ -1,21 +1,26 @@
 """Summaries of rocprofv3 output for the library's kernels.
 
-  python -m compressed_decode_attention_kv_amd.profiling stats <kernel_stats.csv>
+  python -m compressed_decode_attention_kv_amd.profiling stats <kernel_stats.csv> [--last N]
   python -m compressed_decode_attention_kv_amd.profiling traffic <fetch counter_collection.csv> \
         <write counter_collection.csv> --calib-bytes N
-  python -m compressed_decode_attention_kv_amd.profiling decode-traffic <fetch csv> <write csv> \
-        --calib-bytes N --algorithmic-bytes A --title "..." --command "..." [--command ...]
+  python -m compressed_decode_attention_kv_amd.profiling traffic-summary <fetch csv> <write csv> \
+        --calib-bytes N --decode-bytes A --quantize-bytes Q --title "..." --command "..." [--command ...]
   python -m compressed_decode_attention_kv_amd.profiling counters <counter_collection.csv> [...]
 
-Every summary keeps, per kernel, only the dispatches at its largest grid
-size: the workload's full-size launch (a benchmark run also makes small
-launches of the same kernels, e.g. one-token appends, which would otherwise
-dominate the per-kernel averages and medians).  `stats` prints the average
-duration per kernel over those dispatches, from the kernel trace beside the
-stats file.  `decode-traffic` writes the
+Every summary lists every kernel of the run (the library's and any other,
+e.g. the input generator's), keeping per kernel only the dispatches at its
+largest grid size: the workload's full-size launch (a benchmark run also
+makes small launches of the same kernels, e.g. one-token appends, which
+would otherwise dominate the per-kernel averages and medians).  `stats`
+prints, from the kernel trace beside the stats file, the average duration
+per kernel over those dispatches and, with --last N, over the last N of
+them as well: the timed steps of a benchmark run that makes no full-size
+dispatch after them, i.e. the figure its HIP-event timing measures (the
+first dispatches run while the clocks settle).  `traffic-summary` writes the
 committed per-scheme summary: the traffic table, the decode chain's bytes
-(query prep + split decode + combine) and the hash of the decode sources it
-was measured on (a summary taken on other sources is not used).  `traffic` prints HBM bytes
+(query prep + split decode + combine), the quantize chain's bytes (the K and
+V quantize launches of one step) and the hash of the sources of each chain
+(a summary taken on other sources is not used).  `traffic` prints HBM bytes
 per dispatch from the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch),
 the fetch side scaled by what the same counter reads for the library's
 streaming-read kernel over a buffer of N bytes (non-temporal loads count at
@@ -40,18 +45,29 @@ import re
 import sys
 
 DECODE_SOURCES = ("decode_lut.hip", "decode.hip", "device_common.h", "internal.h")
+QUANTIZE_SOURCES = ("quant_mfma.hip", "quant.hip", "quant_sketch.hip", "device_common.h", "internal.h")
 CHAIN = ("qprep_kernel", "decode_lut_kernel", "decode_split_kernel", "combine_kernel")
+QCHAIN = ("quant_mfma_kernel", "quant_kernel", "quant_sketch_kernel")
+
+
+def _sources_sha(files):
+    h = hashlib.sha1()
+    pkg = os.path.dirname(os.path.abspath(__file__))
+    for f in files:
+        h.update(open(os.path.join(pkg, "csrc", f), "rb").read())
+    h.update(open(os.path.join(pkg, "build.py"), "rb").read())
+    return h.hexdigest()
 
 
 def decode_sources_sha():
     """sha1 over the sources of the decode chain's kernels and the build
     script (its per-source compiler flags shape the kernels too)."""
-    h = hashlib.sha1()
-    pkg = os.path.dirname(os.path.abspath(__file__))
-    for f in DECODE_SOURCES:
-        h.update(open(os.path.join(pkg, "csrc", f), "rb").read())
-    h.update(open(os.path.join(pkg, "build.py"), "rb").read())
-    return h.hexdigest()
+    return _sources_sha(DECODE_SOURCES)
+
+
+def quantize_sources_sha():
+    """sha1 over the sources of the quantize kernels and the build script."""
+    return _sources_sha(QUANTIZE_SOURCES)
 
 
 def short(name):
@@ -79,18 +95,26 @@ def _trace_grid(r):
     return int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
 
 
-def stats(path):
-    """Calls and average duration per library kernel, over the dispatches at
-    its largest grid size, from run_kernel_trace.csv beside `path`."""
+def stats(path, last=None):
+    """Calls and average duration per kernel (every kernel of the run), over
+    the dispatches at its largest grid size, from run_kernel_trace.csv beside
+    `path`; with `last`, also the average over the last `last` of them."""
     trace = os.path.join(os.path.dirname(path), "run_kernel_trace.csv")
-    rows = [r for r in csv.DictReader(open(trace)) if "tq" in r["Kernel_Name"] or "stream_read" in r["Kernel_Name"]]
+    rows = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"]))
     calls = collections.Counter(r["Kernel_Name"] for r in rows)
     dur = collections.defaultdict(list)
     for r in _largest_grid(rows, _trace_grid):
         dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
-    out = ["%-90s %6s %10s %14s" % ("kernel", "calls", "full-size", "avg_us")]
+    head = "%-90s %6s %10s %14s" % ("kernel", "calls", "full-size", "avg_us")
+    if last:
+        head += " %18s" % ("avg_last%d_us" % last)
+    out = [head]
     for k in sorted(dur, key=lambda k: -sum(dur[k])):
-        out.append("%-90s %6d %10d %14.2f" % (short(k), calls[k], len(dur[k]), sum(dur[k]) / len(dur[k])))
+        line = "%-90s %6d %10d %14.2f" % (short(k), calls[k], len(dur[k]), sum(dur[k]) / len(dur[k]))
+        if last:
+            tail = dur[k][-last:]
+            line += " %18.2f" % (sum(tail) / len(tail))
+        out.append(line)
     return "\n".join(out)
 
 
@@ -112,8 +136,6 @@ def _traffic_table(fetch_path, write_path, calib_bytes, write_factor):
     fetch_factor = calib_bytes / (sum(fetch[cal[0]]) / len(fetch[cal[0]]) * 1024.0)
     rows = []
     for k in sorted(fetch):
-        if "tq" not in k and "stream_read" not in k:
-            continue
         f = sum(fetch[k]) / len(fetch[k]) * 1024.0 * fetch_factor
         w = sum(write.get(k, [0])) / max(1, len(write.get(k, [0]))) * 1024.0 * write_factor
         rows.append((short(k), f, w))
@@ -129,11 +151,15 @@ def traffic(fetch_path, write_path, calib_bytes, write_factor=1.0):
     return "\n".join(out)
 
 
-def decode_traffic(fetch_path, write_path, calib_bytes, algorithmic, title, commands, write_factor=1.0):
+def traffic_summary(fetch_path, write_path, calib_bytes, algorithmic, qalgorithmic, title, commands,
+                    write_factor=1.0):
     fetch_factor, rows = _traffic_table(fetch_path, write_path, calib_bytes, write_factor)
     chain = [r for r in rows if r[0].startswith(CHAIN)]
     cf = sum(r[1] for r in chain)
     cw = sum(r[2] for r in chain)
+    qchain = [r for r in rows if r[0].startswith(QCHAIN)]
+    qf = sum(r[1] for r in qchain)
+    qw = sum(r[2] for r in qchain)
     out = ["# " + title]
     out += ["#   " + c for c in commands]
     out += ["# The fetch counter is scaled by the streaming-read kernel over %d bytes" % calib_bytes,
@@ -150,7 +176,15 @@ def decode_traffic(fetch_path, write_path, calib_bytes, algorithmic, title, comm
             "decode_chain_fetch_bytes = %.6g" % cf,
             "decode_chain_write_bytes = %.6g" % cw,
             "decode_chain_bytes = %.6g" % (cf + cw),
-            "ratio_to_algorithmic = %.4f" % ((cf + cw) / algorithmic)]
+            "ratio_to_algorithmic = %.4f" % ((cf + cw) / algorithmic),
+            "#",
+            "# quantize chain = %s (one K and one V launch); algorithmic bytes (inputs read + planes written) = %d"
+            % (" + ".join(r[0].split("(")[0] for r in qchain), qalgorithmic),
+            "quantize_sources_sha1 = %s" % quantize_sources_sha(),
+            "quantize_chain_fetch_bytes = %.6g" % qf,
+            "quantize_chain_write_bytes = %.6g" % qw,
+            "quantize_chain_bytes = %.6g" % (qf + qw),
+            "quantize_ratio_to_algorithmic = %.4f" % ((qf + qw) / qalgorithmic)]
     return "\n".join(out)
 
 
@@ -181,7 +215,7 @@ def counters(paths):
         cu, simd, xcc = _agent(path)
         disp = collections.defaultdict(dict)
         names = {}
-        rows = [r for r in csv.DictReader(open(path)) if "tq" in r["Kernel_Name"]]
+        rows = list(csv.DictReader(open(path)))
         for r in _largest_grid(rows, lambda r: int(r["Grid_Size"])):
             disp[r["Dispatch_Id"]][r["Counter_Name"]] = float(r["Counter_Value"])
             names[r["Dispatch_Id"]] = r["Kernel_Name"]
@@ -201,7 +235,9 @@ def counters(paths):
         return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
 
     cols = ["VALU insts"] + [d[0] for d in _DERIVED]
-    out = ["%-90s %5s " % ("kernel", "disp") + " ".join("%16s" % c for c in cols)]
+    out = ["# decode_sources_sha1 = %s" % decode_sources_sha(),
+           "# quantize_sources_sha1 = %s" % quantize_sources_sha(),
+           "%-90s %5s " % ("kernel", "disp") + " ".join("%16s" % c for c in cols)]
     for k in sorted(per):
         n = max(len(v) for v in per[k].values())
         out.append("%-90s %5d " % (short(k), n) +
@@ -214,16 +250,18 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
+    s.add_argument("--last", type=int, default=None)
     t = sub.add_parser("traffic")
     t.add_argument("fetch_csv")
     t.add_argument("write_csv")
     t.add_argument("--calib-bytes", type=int, required=True)
     t.add_argument("--write-factor", type=float, default=1.0)
-    dt = sub.add_parser("decode-traffic")
+    dt = sub.add_parser("traffic-summary")
     dt.add_argument("fetch_csv")
     dt.add_argument("write_csv")
     dt.add_argument("--calib-bytes", type=int, required=True)
-    dt.add_argument("--algorithmic-bytes", type=int, required=True)
+    dt.add_argument("--decode-bytes", type=int, required=True)
+    dt.add_argument("--quantize-bytes", type=int, required=True)
     dt.add_argument("--title", required=True)
     dt.add_argument("--command", action="append", default=[])
     dt.add_argument("--write-factor", type=float, default=1.0)
@@ -231,14 +269,14 @@ def main(argv=None):
     c.add_argument("csv", nargs="+")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
-        print(stats(a.csv))
+        print(stats(a.csv, a.last))
     elif a.cmd == "counters":
         print(counters(a.csv))
     elif a.cmd == "traffic":
         print(traffic(a.fetch_csv, a.write_csv, a.calib_bytes, a.write_factor))
     else:
-        print(decode_traffic(a.fetch_csv, a.write_csv, a.calib_bytes, a.algorithmic_bytes, a.title, a.command,
-                             a.write_factor))
+        print(traffic_summary(a.fetch_csv, a.write_csv, a.calib_bytes, a.decode_bytes, a.quantize_bytes, a.title,
+                              a.command, a.write_factor))
 
 
 if __name__ == "__main__":

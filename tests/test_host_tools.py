@@ -34,12 +34,36 @@ def test_bench_traffic_needs_matching_sources(tmp_path, monkeypatch):
     prof.mkdir()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.measured_traffic("kqv") is None                        # no summary
-    (prof / "decode_traffic_isotropic_kqv.txt").write_text(
-        "# header\ndecode_sources_sha1 = %s\ndecode_chain_bytes = 2.5e+09\n" % pf.decode_sources_sha())
+    (prof / "traffic_isotropic_kqv.txt").write_text(
+        "# header\ndecode_sources_sha1 = %s\ndecode_chain_bytes = 2.5e+09\n"
+        "quantize_sources_sha1 = %s\nquantize_chain_bytes = 1.1e+10\n"
+        % (pf.decode_sources_sha(), pf.quantize_sources_sha()))
     assert bench.measured_traffic("kqv") == 2.5e9
-    (prof / "decode_traffic_isotropic_kqv.txt").write_text(
-        "decode_sources_sha1 = 0000\ndecode_chain_bytes = 2.5e+09\n")
+    assert bench.measured_traffic("kqv", "quantize") == 1.1e10
+    (prof / "traffic_isotropic_kqv.txt").write_text(
+        "decode_sources_sha1 = 0000\ndecode_chain_bytes = 2.5e+09\n"
+        "quantize_sources_sha1 = %s\nquantize_chain_bytes = 1.1e+10\n" % pf.quantize_sources_sha())
     assert bench.measured_traffic("kqv") is None                        # taken on other sources
+    assert bench.measured_traffic("kqv", "quantize") == 1.1e10
+
+
+def test_bench_reads_quantize_mfma_util(tmp_path, monkeypatch):
+    import bench
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    head = "%-90s %5s " % ("kernel", "disp") + " ".join("%16s" % c for c in
+                                                       ("VALU insts", "VALUBusy%", "LdsUtil%", "LDSBankConflict%",
+                                                        "MfmaUtil%"))
+    row = "%-90s %5d " % ("quant_mfma_kernel<3, 2, _Float16>(tq::QuantParamsENS_9QuantGrid)", 4) + \
+        " ".join("%16.4g" % v for v in (6.4e8, 74.7, 37.1, 0.5, 38.47))
+    body = "\n".join([head, row]) + "\n"
+    (prof / "counters_isotropic_kqv.txt").write_text("# quantize_sources_sha1 = %s\n" % pf.quantize_sources_sha()
+                                                     + body)
+    assert bench.measured_mfma_util("kqv") == {"quant_mfma_kernel<3, 2, _Float16>(tq::QuantParamsENS_9QuantGrid)":
+                                               38.47}
+    (prof / "counters_isotropic_kqv.txt").write_text("# quantize_sources_sha1 = 00\n" + body)
+    assert bench.measured_mfma_util("kqv") is None
 
 
 def _trace_row(name, grid, t0, dur_ns):
@@ -53,6 +77,7 @@ def test_stats_keeps_full_size_dispatches(tmp_path):
     rows = [_trace_row(k, 524288, 0, 2_000_000), _trace_row(k, 524288, 10**7, 2_200_000),
             _trace_row(k, 512, 2 * 10**7, 9_000)] + \
            [_trace_row("tq::(anonymous namespace)::combine_kernel(tq::CombineParams)", 8192, 3 * 10**7, 9_000)]
+    rows.append(_trace_row("void at::native::distribution_kernel<float>(int)", 1024, 4 * 10**7, 5_000))
     _write_csv(tmp_path / "run_kernel_trace.csv", rows)
     (tmp_path / "run_kernel_stats.csv").write_text("")
     lines = pf.stats(str(tmp_path / "run_kernel_stats.csv")).split("\n")
@@ -61,6 +86,12 @@ def test_stats_keeps_full_size_dispatches(tmp_path):
     calls, full, avg = quant[0].split()[-3:]
     assert (int(calls), int(full), float(avg)) == (3, 2, 2100.0)
     assert any(l.startswith("combine_kernel") for l in lines)
+    # Kernels that are not the library's are listed too.
+    assert any(l.startswith("at::native::distribution_kernel") for l in lines)
+    # --last N: the average over the last N full-size dispatches (in time order).
+    lines = pf.stats(str(tmp_path / "run_kernel_stats.csv"), last=1).split("\n")
+    quant = [l for l in lines if l.startswith("quant_mfma_kernel<3, 2, _Float16>")][0].split()
+    assert (float(quant[-2]), float(quant[-1])) == (2100.0, 2200.0)
 
 
 def test_counters_derived_utilisations(tmp_path):
