@@ -75,8 +75,11 @@ def other_side(Y, idx, boundaries, mask, band):
 
 def quantize(X, st, flip_codes=None, flip_signs=None, band=1e-6):
     """X: [N, d] float64.  Returns a dict of unpacked fields plus the
-    parity-band diagnostics (distance of y to its nearest boundary, and
-    |(S r)_i| / ||r|| for the sign bits).
+    parity-band diagnostics, both distances to a decision boundary in the
+    domain of the rotated unit vector: for a code, the distance of y_i to its
+    nearest boundary; for a sign bit, the distance of the residual r (which
+    lives in that same domain) to the hyperplane S_i . r = 0 that decides it,
+    |(S r)_i| / ||S_i||.
 
     flip_codes / flip_signs ([N, d] / [N, m] boolean, optional) select
     decisions taken within `band` of their boundary; those take the other
@@ -101,8 +104,8 @@ def quantize(X, st, flip_codes=None, flip_signs=None, band=1e-6):
         bits = (P >= 0).astype(np.int64)
         gamma[zero] = 0.0
         bits[zero] = 0
-        g = np.where(gamma > 0, gamma, 1.0)
-        sdist = np.where(zero[:, None], np.inf, np.abs(P) / g[:, None])
+        row_norm = np.sqrt(np.sum(st.S * st.S, axis=1))
+        sdist = np.where(zero[:, None], np.inf, np.abs(P) / row_norm[None, :])
         if flip_signs is not None and np.any(flip_signs):
             assert np.all(sdist[flip_signs] <= band), "sign flip requested outside the band"
             bits[flip_signs] = 1 - bits[flip_signs]

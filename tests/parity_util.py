@@ -3,8 +3,9 @@ compare with what the library wrote.
 
 Decision band.  A code, a sign bit or a side code may differ from the
 oracle's only when the oracle puts that decision within BAND of its
-boundary (1e-6 of the unit-sphere coordinate for codes, 1e-6 of ||r|| for
-signs, 1e-5 of a step for HeadQ side codes).  Such a decision has two valid
+boundary: 1e-6 in the domain of the rotated unit vector for codes (y_i to
+its nearest boundary) and for sketch signs (the residual r to the hyperplane
+S_i . r = 0, |(S r)_i| / ||S_i||), 1e-5 of a step for HeadQ side codes.  Such a decision has two valid
 outcomes; the oracle then recomputes everything downstream (residual,
 sketch, dense vectors, attention) with that decision taken the other way,
 and the GPU must match that branch exactly as it would the first.  In-band

@@ -196,6 +196,26 @@ def test_jensen_amplification():
         assert abs(e.mean() / math.exp(sig * sig / 2) - 1) < 4 * e.std() / math.sqrt(e.size)
 
 
+def test_sign_band_is_distance_to_the_deciding_hyperplane():
+    """The band of a sketch sign is the Euclidean distance, in the rotated
+    unit-vector domain the residual lives in, from r to the hyperplane
+    S_i . r = 0 that decides the sign (the same units as the code band):
+    moving r by exactly that distance along S_i lands on the hyperplane."""
+    d = 64
+    st = qz.QState(d, qz.PROD, 3, seed=7)
+    x = np.random.default_rng(4).standard_normal((5, d))
+    q = qz.quantize(x, st)
+    Y = x / np.linalg.norm(x, axis=1, keepdims=True) @ st.Pi.T
+    R = Y - st.centroids[q["idx"]]
+    for n in range(5):
+        for i in (0, 17, 63):
+            s = st.S[i]
+            dist = q["sdist"][n, i]
+            r_on = R[n] - np.sign(s @ R[n]) * dist * s / np.linalg.norm(s)
+            assert abs(s @ r_on) <= 1e-12 * np.linalg.norm(s)
+            assert abs(dist - abs(s @ R[n]) / np.linalg.norm(s)) <= 1e-15
+
+
 def test_in_band_flip_takes_the_other_cell():
     """A coordinate placed exactly on a boundary has two valid codes; the
     flip selects the neighbour across that boundary and the sketch of the

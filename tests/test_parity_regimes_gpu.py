@@ -7,11 +7,12 @@
   * low-rank keys at d = 1024 (rank 16, eigenvalues 0.7^i, 0.01 noise) with
     queries half inside the key subspace, KQV and QKQV at n = 4, with KL and
     top-5 recall;
-  * the full-size heavy-tailed cache (B=4, 8 heads, T=131072) and the
-    full-size HeadQ cache under GQA (B=8, 8 KV heads x 4 query heads,
-    T=131072, fp16, rank-16 basis fitted from 4096 calibration queries), with
-    a sampled (batch, head) slice checked element by element against the
-    oracle.
+  * the full-size heavy-tailed cache (B=4, 8 heads, T=131072; every scheme
+    and budget), the full-size low-rank cache (H=4, T=65536, d=1024, 64
+    queries per head; KQV and QKQV) and the full-size HeadQ cache under GQA
+    (B=8, 8 KV heads x 4 query heads, T=131072, fp16, rank-16 basis fitted
+    from 4096 calibration queries), with a sampled (batch, head) slice
+    checked element by element against the oracle.
 Same bar as the other parity tests: codes, sign bits and side codes
 bit-exact outside the decision band; outputs within 1e-3 relative L2;
 metrics against the oracle's."""
@@ -87,32 +88,81 @@ def test_low_rank_d1024(tq, scheme):
     assert abs(m["top5_recall"] - recs.mean()) <= amb / (5.0 * len(recs)) + 1e-12
 
 
-def test_heavy_tailed_full_size_sampled(tq):
-    """B=4, 8 heads, T=131072, d=128, fp32, TQ-QKV at n=3 (the regime's
-    largest sketch case): full quantisation on the GPU, finiteness of every
-    norm, and one sampled (batch, head) slice against the oracle (codes, sign
-    bits, norms; relMSE and direction error of that slice)."""
+@pytest.fixture(scope="module")
+def heavy_full(tq):
+    """The heavy-tailed cache at full size, drawn once on the device."""
     B, H, T, d = 4, 8, 131072, 128
     K, V = synth.device_heavy_tailed(B, H, T, d, seed=33)
-    kp = tq.quantize(K, tq.KEYS, "tq-qkv", 3, 21)
-    vp = tq.quantize(V, tq.VALUES, "tq-qkv", 3, 21)
+    return K, V
+
+
+@pytest.mark.parametrize("scheme,n", [("tq-qkv", 3), ("tq-qkv", 2), ("kv", 2), ("kv", 3), ("tq-kv", 2),
+                                      ("tq-kv", 3)])
+def test_heavy_tailed_full_size_sampled(tq, heavy_full, scheme, n):
+    """B=4, 8 heads, T=131072, d=128, fp32, every scheme and budget of the
+    regime: full quantisation on the GPU, finiteness of every norm, and one
+    sampled (batch, head) slice against the oracle (codes, sign bits, norms;
+    relMSE and direction error of that slice)."""
+    B, H, T, d = 4, 8, 131072, 128
+    K, V = heavy_full
+    kp = tq.quantize(K, tq.KEYS, scheme, n, 21)
+    vp = tq.quantize(V, tq.VALUES, scheme, n, 21)
     torch.cuda.synchronize()
     kpl, vpl = kp.planes(), vp.planes()
-    assert np.isfinite(kpl["norms"]).all() and np.isfinite(vpl["norms"]).all() and np.isfinite(kpl["gamma"]).all()
-    b, h = 2, 5
+    assert np.isfinite(kpl["norms"]).all() and np.isfinite(vpl["norms"]).all()
+    if "gamma" in kpl:
+        assert np.isfinite(kpl["gamma"]).all()
+    b, h = (2, 5) if n == 3 else (3, 1)
     sl = slice((b * H + h) * T, (b * H + h + 1) * T)
     Kn = K[b, h].double().cpu().numpy()
     Vn = V[b, h].double().cpu().numpy()
     _, Khat, _, nb1, nd1 = pu.oracle_match(Kn, {k: v[sl] for k, v in kpl.items()}, pu.MODE_NAMES[kp.c.mode],
-                                           kp.c.bits, 21, label="heavy full K")
+                                           kp.c.bits, 21, label="heavy full %s %d K" % (scheme, n))
     _, Vhat, _, nb2, nd2 = pu.oracle_match(Vn, {k: v[sl] for k, v in vpl.items()}, pu.MODE_NAMES[vp.c.mode],
-                                           vp.c.bits, 21, label="heavy full V")
+                                           vp.c.bits, 21, label="heavy full %s %d V" % (scheme, n))
     assert nb1 + nb2 <= max(1, pu.MAX_BAND_FRACTION * (nd1 + nd2))
     m = tq.metrics(None, K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], kp.head_view(b, h), vp.head_view(b, h))
     for key, ref, hat in (("k", Kn, Khat), ("v", Vn, Vhat)):
         rel = ome.rel_mse(ref, hat)
         assert abs(m["relmse_" + key] - rel) <= 1e-5 * rel, (key, m["relmse_" + key], rel)
         assert abs(m["dir_err_" + key] - ome.direction_error(ref, hat)) <= 1e-5, key
+
+
+@pytest.mark.parametrize("scheme", ["kqv", "qkqv"])
+def test_low_rank_full_size_sampled(tq, scheme):
+    """The low-rank workload at its own size: H=4, T=65536, d=1024, fp32,
+    64 queries per head (half inside the key subspace), n=4, in the launch
+    configuration the benchmark times.  Full quantisation and decode on the
+    GPU; every output finite; one sampled head with its 64 queries against the
+    oracle (codes and signs, norms, gamma, outputs, LSE, KL and top-5)."""
+    H, T, d, G = 4, 65536, 1024, 64
+    K, V, Q = synth.low_rank(H, T, d, G, seed=40)
+    Kd, Vd, Qd = (torch.from_numpy(x).cuda() for x in (K, V, Q))
+    kp = tq.quantize(Kd, tq.KEYS, scheme, 4, 3)
+    vp = tq.quantize(Vd, tq.VALUES, scheme, 4, 3)
+    out, lse = tq.decode_attention(Qd, kp, vp)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item()
+    h = 2 if scheme == "kqv" else 1
+    sl = slice(h * T, (h + 1) * T)
+    Kn, Vn = K[0, h].astype(np.float64), V[0, h].astype(np.float64)
+    qn = Q[0, G * h:G * h + G].astype(np.float64)
+    kpl, vpl = kp.planes(), vp.planes()
+    _, Khat, _, nb1, nd1 = pu.oracle_match(Kn, {k: v[sl] for k, v in kpl.items()}, pu.MODE_NAMES[kp.c.mode],
+                                           kp.c.bits, 3, label="low-rank full K")
+    _, Vhat, _, nb2, nd2 = pu.oracle_match(Vn, {k: v[sl] for k, v in vpl.items()}, pu.MODE_NAMES[vp.c.mode],
+                                           vp.c.bits, 3, label="low-rank full V")
+    assert nb1 + nb2 <= max(1, pu.MAX_BAND_FRACTION * (nd1 + nd2))
+    o_ref, lse_ref, _ = pu.oracle_decode(qn, Khat, Vhat)
+    err = pu.rel_l2(out[0, G * h:G * h + G].cpu().numpy(), o_ref)
+    print("low-rank full %s: worst rel L2 %.3g, in-band %d" % (scheme, err.max(), nb1 + nb2))
+    assert err.max() <= pu.OUT_RTOL, err
+    assert np.allclose(lse[0, G * h:G * h + G].cpu().numpy(), lse_ref, atol=2e-4, rtol=1e-5)
+    m = tq.metrics(Qd[:, G * h:G * h + G].contiguous(), Kd[:, h:h + 1], None, kp.head_view(0, h), None)
+    kl, rec, s, sh = pu.kl_and_recall(qn, Kn, Khat)
+    assert abs(m["kl_mean"] - kl.mean()) <= pu.KL_ATOL and abs(m["kl_max"] - kl.max()) <= pu.KL_ATOL
+    amb = int(pu.top5_ambiguous(s).sum() + pu.top5_ambiguous(sh).sum())
+    assert abs(m["top5_recall"] - rec.mean()) <= amb / (5.0 * len(rec)) + 1e-12
 
 
 def test_headq_gqa_full_size_sampled(tq):
