@@ -22,9 +22,12 @@ is applied.
 
 Parity status of each part (what pins it is listed in the tests):
   codebook, rotation, quantiser, QJL estimator, attention, metrics: pinned.
+  SpectralQuant with uniform allocation (spectral.py): pinned (Gaussian
+      codebook against Max's table, calibration, hand-worked case,
+      equivariance, distortion, the pages' orderings).
   HeadQ side quantiser Q_q: parity unpinned (the pages give no form; the
       per-token symmetric absmax 4-bit reading is our own).
   RNG streams for the sign vector and the Gaussian sketch: a reading (the
       pages fix only the distributions, which are pinned statistically).
 """
-from . import codebook, rng, rotation, quantizer, attention, metrics, headq, schemes  # noqa: F401
+from . import codebook, rng, rotation, quantizer, attention, metrics, headq, schemes, spectral  # noqa: F401

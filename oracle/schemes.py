@@ -6,11 +6,14 @@
   QKQV          : K PROD(n),   V PROD(n)    [P1] "Esquemas" 3
   TQ-QKV        : K PROD(n),   V MSE(n)     [P2] "Contribuições" 1 (QJL on the key path)
   HEADQ         : K HEADQ(base MSE 2 + side code), V MSE(n)   [P3] section 3
+  SQU-KV        : K SPECTRAL(n), V SPECTRAL(n)   [P2] "Recomendações Práticas" 2 (see spectral.py)
 PROD(n) spends n-1 bits on the Lloyd-Max index and 1 bit per coordinate on
 the QJL sketch (m = d), so every preset keeps n bits per coordinate
 (HEADQ aside, whose key budget is 2 bits plus the side code).
 """
 from .quantizer import PLAIN, MSE, PROD, HEADQ
+
+SPECTRAL = "spectral"
 
 TABLE = {
     "kv": (PLAIN, PLAIN),
@@ -19,6 +22,7 @@ TABLE = {
     "qkqv": (PROD, PROD),
     "tq-qkv": (PROD, MSE),
     "headq": (HEADQ, MSE),
+    "squ-kv": (SPECTRAL, SPECTRAL),
 }
 
 
