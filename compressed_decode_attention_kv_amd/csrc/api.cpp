@@ -36,6 +36,10 @@ tq_status fail(tq_status s, const char* fmt, ...) {
 
 tq_status ok() { return TQ_OK; }
 
+// Modes coded in the seeded rotated domain (the SPECTRAL basis is the
+// caller's, and PLAIN is not rotated).
+bool rotated(int mode) { return mode == TQ_MODE_MSE || mode == TQ_MODE_PROD || mode == TQ_MODE_HEADQ; }
+
 bool pow2_in(int d, int lo, int hi) { return d >= lo && d <= hi && (d & (d - 1)) == 0; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -57,6 +61,7 @@ tq_status modes_of(int scheme, int n_bits, int which, int* mode, int* bits) {
     case TQ_SCHEME_QKQV: km = TQ_MODE_PROD; vm = TQ_MODE_PROD; break;
     case TQ_SCHEME_TQ_QKV: km = TQ_MODE_PROD; vm = TQ_MODE_MSE; break;
     case TQ_SCHEME_HEADQ: km = TQ_MODE_HEADQ; vm = TQ_MODE_MSE; break;
+    case TQ_SCHEME_SQU_KV: km = TQ_MODE_SPECTRAL; vm = TQ_MODE_SPECTRAL; break;
     default: return fail(TQ_EINVAL, "unknown scheme %d", scheme);
   }
   const int m = which == TQ_KEYS ? km : vm;
@@ -80,6 +85,7 @@ tq_status resolve_mode(int scheme, int n_bits, int which, const tq_mode_override
   switch (m) {
     case TQ_MODE_PLAIN:
     case TQ_MODE_MSE:
+    case TQ_MODE_SPECTRAL:
       if (b < 1 || b > kMaxIndexBits) return fail(TQ_EINVAL, "override: index bits %d outside [1, %d]", b, kMaxIndexBits);
       break;
     case TQ_MODE_PROD:
@@ -99,8 +105,10 @@ tq_status resolve_mode(int scheme, int n_bits, int which, const tq_mode_override
 
 tq_status layout_of(int d, int mode, int bits, int side_rank, int side_bits, tq_layout* out) {
   if (tq_status s = check_d(d)) return s;
-  if (mode < TQ_MODE_PLAIN || mode > TQ_MODE_HEADQ) return fail(TQ_EINVAL, "unknown mode %d", mode);
+  if (mode < TQ_MODE_PLAIN || mode > TQ_MODE_SPECTRAL) return fail(TQ_EINVAL, "unknown mode %d", mode);
   if (bits < 1 || bits > kMaxIndexBits) return fail(TQ_EINVAL, "index bits %d outside [1, %d]", bits, kMaxIndexBits);
+  if (mode == TQ_MODE_SPECTRAL && d > spectral_max_d())
+    return fail(TQ_EUNSUPPORTED, "SPECTRAL supports d <= %d (got %d): the head's basis is held on chip", spectral_max_d(), d);
   // PROD: one (bits+1)-bit field per coordinate, code | QJL sign << bits.
   out->code_bytes = d * (bits + (mode == TQ_MODE_PROD ? 1 : 0)) / 8;
   out->qjl_bytes = 0;
@@ -232,6 +240,10 @@ tq_status hip_status(hipError_t e, const char* what) {
   return TQ_OK;
 }
 
+bool spectral_ok(const float* basis, const float* mean, const float* scale) {
+  return basis && mean && scale && aligned(basis, 4) && aligned(mean, 4) && aligned(scale, 4);
+}
+
 tq_status check_packed(const tq_packed* p, const char* name) {
   if (!p) return fail(TQ_EINVAL, "%s packed descriptor is NULL", name);
   if (p->B < 1 || p->H < 1 || p->T < 1 || p->T_cap < p->T)
@@ -244,6 +256,8 @@ tq_status check_packed(const tq_packed* p, const char* name) {
     return fail(TQ_EINVAL, "%s QJL gamma plane missing or misaligned", name);
   if (p->mode == TQ_MODE_HEADQ && (!p->side || !p->side_scale || !p->basis || !aligned(p->side, 16) || !aligned(p->side_scale, 16)))
     return fail(TQ_EINVAL, "%s HeadQ planes or basis missing or misaligned", name);
+  if (p->mode == TQ_MODE_SPECTRAL && !spectral_ok(p->basis, p->mean, p->scale))
+    return fail(TQ_EINVAL, "%s SPECTRAL basis, mean or scale missing or not 4-byte aligned", name);
   return TQ_OK;
 }
 
@@ -262,7 +276,7 @@ struct DecodePlan {
   int nsplit, chunk, part_stride, units, G;
   int nparts;  // partials per query: nsplit, times the waves per block at d > 128 (table-driven)
   bool lut;
-  size_t off_qrot, off_qsk, off_qw, off_part, off_qraw, bytes;
+  size_t off_qrot, off_qsk, off_qw, off_part, off_qraw, off_qoff, bytes;
 };
 
 tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_qraw, DecodePlan* pl) {
@@ -319,6 +333,7 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   pl->off_qsk = off;  off = round_up(off + (k->mode == TQ_MODE_PROD ? (size_t)nq * d * 4 : 0), 256);
   pl->off_qw = off;   off = round_up(off + (k->mode == TQ_MODE_HEADQ ? (size_t)nq * k->side_rank * 4 : 0), 256);
   pl->off_qraw = off; off = round_up(off + (with_qraw ? (size_t)nq * d * 4 : 0), 256);
+  pl->off_qoff = off; off = round_up(off + (k->mode == TQ_MODE_SPECTRAL ? (size_t)nq * 4 : 0), 256);
   pl->off_part = off; off = round_up(off + (v ? (size_t)nq * pl->nparts * pl->part_stride * 4 : 0), 256);
   pl->bytes = off;
   return TQ_OK;
@@ -337,10 +352,15 @@ void fill_qprep(const tq_tensor_desc* q, const tq_packed* k, const float* S, cha
   std::memset(qp, 0, sizeof(*qp));
   qp->q = q->data; qp->dtype = q->dtype; qp->B = q->B; qp->Hq = q->H; qp->d = q->d; qp->Hkv = k->H;
   qp->sb = q->stride_b; qp->sh = q->stride_h;
-  qp->rotate = k->mode != TQ_MODE_PLAIN;
+  qp->rotate = rotated(k->mode);
   qp->kqjl = k->mode == TQ_MODE_PROD;
   qp->kside = k->mode == TQ_MODE_HEADQ;
   qp->rank = k->side_rank;
+  if (k->mode == TQ_MODE_SPECTRAL) {
+    qp->kspectral = 1;
+    qp->sbasis = k->basis; qp->smean = k->mean; qp->sscale = k->scale;
+    qp->qoff = reinterpret_cast<float*>(ws + pl.off_qoff);
+  }
   fill_signbits(k->seed, k->d, qp->signbits);
   qp->inv_sqrt_d = 1.0f / std::sqrt((float)k->d);
   qp->S = S; qp->basis = k->basis;
@@ -350,9 +370,12 @@ void fill_qprep(const tq_tensor_desc* q, const tq_packed* k, const float* S, cha
   qp->qraw = qraw ? reinterpret_cast<float*>(ws + pl.off_qraw) : nullptr;
 }
 
-tq_status fill_codebook(int d, int bits, float* c16, float* b16) {
+// Centroids and boundaries of a tensor's scalar code: the Beta sphere
+// marginal of the rotated modes, the standard normal for SPECTRAL.
+tq_status fill_codebook(int mode, int d, int bits, float* c16, float* b16) {
   std::vector<double> c, t;
-  if (!codebook(d, bits, &c, &t)) return fail(TQ_EINVAL, "codebook(d=%d, bits=%d) failed", d, bits);
+  const bool okc = mode == TQ_MODE_SPECTRAL ? gaussian_codebook(bits, &c, &t) : codebook(d, bits, &c, &t);
+  if (!okc) return fail(TQ_EINVAL, "codebook(mode=%d, d=%d, bits=%d) failed", mode, d, bits);
   for (int i = 0; i < 16; ++i) {
     c16[i] = i < (int)c.size() ? (float)c[i] : 0.f;
     b16[i] = i < (int)t.size() ? (float)t[i] : INFINITY;
@@ -373,12 +396,13 @@ void fill_scoring(const tq_tensor_desc* q, const tq_packed* k, const DecodePlan&
   dp->k = {k->codes, k->norms, k->qjl, k->gamma, k->side, k->side_scale};
   dp->rank = k->side_rank; dp->side_bits = k->side_bits;
   float bnd[16];
-  fill_codebook(k->d, k->bits, dp->kc, bnd);
+  fill_codebook(k->mode, k->d, k->bits, dp->kc, bnd);
   dp->k_qjl = (float)(std::sqrt(M_PI / 2.0) / k->d);
   dp->scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)k->d));
   dp->qrot = reinterpret_cast<const float*>(ws + pl.off_qrot);
   dp->qsk = reinterpret_cast<const float*>(ws + pl.off_qsk);
   dp->qw = reinterpret_cast<const float*>(ws + pl.off_qw);
+  dp->qoff = k->mode == TQ_MODE_SPECTRAL ? reinterpret_cast<const float*>(ws + pl.off_qoff) : nullptr;
   dp->part = reinterpret_cast<float*>(ws + pl.off_part);
 }
 
@@ -473,11 +497,11 @@ tq_status relerr(const tq_tensor_desc* x, const tq_packed* pk, double* blk, floa
   std::memset(&p, 0, sizeof(p));
   p.x = x->data; p.dtype = x->dtype; p.B = x->B; p.H = x->H; p.T = x->T; p.T_cap = pk->T_cap; p.d = x->d; p.L = x->d / 32;
   p.sb = x->stride_b; p.sh = x->stride_h; p.st = x->stride_t;
-  p.mode = pk->mode; p.bits = pk->bits; p.rotate = pk->mode != TQ_MODE_PLAIN;
+  p.mode = pk->mode; p.bits = pk->bits; p.rotate = rotated(pk->mode);
   p.kqjl = pk->mode == TQ_MODE_PROD; p.kside = pk->mode == TQ_MODE_HEADQ;
   p.rank = pk->side_rank; p.side_bits = pk->side_bits;
   float bnd[16];
-  if (tq_status s = fill_codebook(pk->d, pk->bits, p.centroids, bnd)) return s;
+  if (tq_status s = fill_codebook(pk->mode, pk->d, pk->bits, p.centroids, bnd)) return s;
   fill_signbits(pk->seed, pk->d, p.signbits);
   p.inv_sqrt_d = 1.0f / std::sqrt((float)pk->d);
   p.qjl_c = (float)(std::sqrt(M_PI / 2.0) / pk->d);
@@ -488,7 +512,13 @@ tq_status relerr(const tq_tensor_desc* x, const tq_packed* pk, double* blk, floa
   p.per_vec = per_vec;
   const int BH = pk->B * pk->H;
   const int nb = relerr_blocks(pk->T, pk->d / 32, BH);
-  if (tq_status s = hip_status(launch_relerr(p, nb, st), "relerr launch")) return s;
+  if (pk->mode == TQ_MODE_SPECTRAL) {
+    // Same block count and (b, h)-major block order as relerr_kernel.
+    p.smean = pk->mean; p.sscale = pk->scale;
+    if (tq_status s = hip_status(launch_relerr_spectral(p, st), "relerr launch")) return s;
+  } else {
+    if (tq_status s = hip_status(launch_relerr(p, nb, st), "relerr launch")) return s;
+  }
   std::vector<double> host((size_t)nb * 5);
   if (tq_status s = hip_status(hipMemcpyAsync(host.data(), blk, host.size() * 8, hipMemcpyDeviceToHost, st), "copy")) return s;
   if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
@@ -566,6 +596,8 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
   if (!out) return fail(TQ_EINVAL, "output packed descriptor is NULL");
   if ((mode == TQ_MODE_HEADQ) != (hq != nullptr))
     return fail(TQ_EINVAL, mode == TQ_MODE_HEADQ ? "HeadQ keys need a tq_headq" : "tq_headq given for a non-HeadQ tensor");
+  if (mode == TQ_MODE_SPECTRAL && !spectral_ok(out->basis, out->mean, out->scale))
+    return fail(TQ_EINVAL, "SPECTRAL needs out->basis, out->mean and out->scale (device, 4-byte aligned)");
   tq_layout lay;
   if (tq_status s = layout_of(x->d, mode, bits, hq ? hq->rank : 0, hq ? hq->side_bits : 0, &lay)) return s;
   if (hq && (!hq->basis || !aligned(hq->basis, 4))) return fail(TQ_EINVAL, "HeadQ basis is NULL or misaligned");
@@ -582,7 +614,11 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
   out->B = x->B; out->H = x->H; out->T = x->T; out->T_cap = T_cap; out->d = x->d;
   out->mode = mode; out->bits = bits; out->seed = seed;
   out->side_rank = hq ? hq->rank : 0; out->side_bits = hq ? hq->side_bits : 0;
-  out->basis = hq ? hq->basis : nullptr;
+  if (mode != TQ_MODE_SPECTRAL) {
+    out->basis = hq ? hq->basis : nullptr;
+    out->mean = nullptr;
+    out->scale = nullptr;
+  }
   return ok();
 }
 
@@ -619,8 +655,8 @@ tq_status quantize_core(const tq_tensor_desc* x, int mode, int bits, uint64_t se
   std::memset(&p, 0, sizeof(p));
   p.x = x->data; p.dtype = x->dtype; p.B = x->B; p.H = x->H; p.T = x->T; p.T_cap = T_cap; p.d = x->d; p.L = x->d / 32;
   p.sb = x->stride_b; p.sh = x->stride_h; p.st = x->stride_t;
-  p.mode = mode; p.bits = bits; p.rotate = mode != TQ_MODE_PLAIN;
-  if (tq_status s = fill_codebook(x->d, bits, p.centroids, p.bounds)) return s;
+  p.mode = mode; p.bits = bits; p.rotate = rotated(mode);
+  if (tq_status s = fill_codebook(mode, x->d, bits, p.centroids, p.bounds)) return s;
   fill_signbits(seed, x->d, p.signbits);
   p.inv_sqrt_d = 1.0f / std::sqrt((float)x->d);
   if (mode == TQ_MODE_PROD) {
@@ -644,7 +680,15 @@ tq_status quantize_core(const tq_tensor_desc* x, int mode, int bits, uint64_t se
   }
   tq_status status = TQ_OK;
   QuantGrid grid;
-  if (quant_mfma_supported(p) && quant_grid(x->d, bits, &grid)) {
+  if (mode == TQ_MODE_SPECTRAL) {
+    // The caller's per-head basis, mean and spreads; decisions in double
+    // against the N(0, 1) boundaries.
+    std::vector<double> c, t;
+    if (!gaussian_codebook(bits, &c, &t)) return fail(TQ_EINVAL, "Gaussian codebook (%d bits) failed", bits);
+    for (int k = 0; k < 16; ++k) p.gbounds[k] = k < (int)t.size() ? t[k] : INFINITY;
+    p.basis = out->basis; p.smean = out->mean; p.sscale = out->scale;
+    status = hip_status(launch_quantize_spectral(p, st), "quantize launch");
+  } else if (quant_mfma_supported(p) && quant_grid(x->d, bits, &grid)) {
     int cus = 0;
     status = hip_status(cu_count(&cus), "device query");
     if (status == TQ_OK) {
@@ -736,7 +780,7 @@ tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_pack
   dp.v = {v->codes, v->norms, v->qjl, v->gamma, v->side, v->side_scale};
   dp.lens = lens;
   float vb[16];
-  if (tq_status s = fill_codebook(v->d, v->bits, dp.vc, vb)) return s;
+  if (tq_status s = fill_codebook(v->mode, v->d, v->bits, dp.vc, vb)) return s;
   dp.v_qjl = (float)(std::sqrt(M_PI / 2.0) / v->d);
 
   QPrepParams qp;
@@ -744,10 +788,16 @@ tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_pack
   CombineParams cp;
   std::memset(&cp, 0, sizeof(cp));
   cp.nq = q->B * q->H; cp.d = k->d; cp.nsplit = pl.nparts; cp.part_stride = pl.part_stride;
-  cp.vqjl = vq; cp.vrotate = v->mode != TQ_MODE_PLAIN; cp.v_qjl = dp.v_qjl;
+  cp.vqjl = vq; cp.vrotate = rotated(v->mode); cp.v_qjl = dp.v_qjl;
   fill_signbits(v->seed, v->d, cp.signbits);
   cp.inv_sqrt_d = 1.0f / std::sqrt((float)k->d);
   cp.S = Sv; cp.part = dp.part; cp.out = out; cp.lse = lse;
+  cp.Hq = q->H; cp.G = pl.G;
+  if (v->mode == TQ_MODE_SPECTRAL) {
+    cp.vspectral = 1;
+    cp.vbasis = v->basis; cp.vmean = v->mean; cp.vscale = v->scale;
+  }
+  cp.qoff = dp.qoff;
 
   bool supported = true;
   if (tq_status s = hip_status(launch_qprep(qp, st), "query prep launch")) return s;
@@ -916,6 +966,19 @@ tq_status tq_metrics(const tq_tensor_desc* q, const tq_tensor_desc* k_ref, const
     out->n_queries = (int64_t)nq;
   }
   if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
+  return ok();
+}
+
+tq_status tq_spectral_fit(const float* calib, int32_t N, int32_t d, float* basis, float* mean, float* scale) {
+  if (!calib || !basis || !mean || !scale) return fail(TQ_EINVAL, "NULL pointer");
+  if (tq_status s = check_d(d)) return s;
+  if (d > spectral_max_d()) return fail(TQ_EUNSUPPORTED, "SPECTRAL supports d <= %d (got %d)", spectral_max_d(), d);
+  if (N < 2) return fail(TQ_EINVAL, "N=%d: at least two calibration vectors", N);
+  std::vector<float> lam(d);
+  if (!pca_basis(calib, N, d, d, basis, lam.data(), mean)) return fail(TQ_EINVAL, "eigendecomposition failed");
+  double total = 0.0;
+  for (int i = 0; i < d; ++i) total += lam[i];
+  for (int i = 0; i < d; ++i) scale[i] = total > 0 ? (float)std::sqrt((double)lam[i] / total) : 0.f;
   return ok();
 }
 

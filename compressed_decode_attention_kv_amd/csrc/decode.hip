@@ -60,6 +60,30 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(QPrepParams p) {
     for (int i = threadIdx.x; i < d; i += blockDim.x) s_r[i] *= p.inv_sqrt_d;
     __syncthreads();
   }
+  if (p.kspectral) {
+    // q . k_hat = q . mu + nu sum_i (s_i (V^T q)_i) c[idx_i]: the score runs
+    // on s * V^T q like a rotated query; the mean adds q . mu / sqrt(d) to
+    // every score of the query (softmax-invariant; only the LSE moves).
+    __shared__ float s_red[kThreads / 64];
+    const float* V = p.sbasis + (size_t)kvh * d * d;
+    const float* sc = p.sscale + (size_t)kvh * d;
+    const float* mu = p.smean + (size_t)kvh * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+      float acc = 0.f;
+      for (int k = 0; k < d; ++k) acc = fmaf(V[(size_t)k * d + i], s_q[k], acc);
+      s_r[i] = sc[i] * acc;
+    }
+    float part = 0.f;
+    for (int k = threadIdx.x; k < d; k += blockDim.x) part = fmaf(s_q[k], mu[k], part);
+    for (int m = 32; m > 0; m >>= 1) part += __shfl_xor(part, m, 64);
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float t = 0.f;
+      for (int w = 0; w < (int)blockDim.x / 64; ++w) t += s_red[w];
+      p.qoff[qi] = t * p.inv_sqrt_d;
+    }
+  }
   for (int i = threadIdx.x; i < d; i += blockDim.x) p.qrot[(size_t)qi * d + i] = s_r[i];
   if (p.qraw)
     for (int i = threadIdx.x; i < d; i += blockDim.x) p.qraw[(size_t)qi * d + i] = s_q[i];
@@ -272,8 +296,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 }
 
 // ---- combine + finalize --------------------------------------------------------
-// LSE-merge of the splits, then out = Pi^T (acc/l + a S^T ask / l) (rotated V)
-// or acc / l (plain V).  One block per query.
+// LSE-merge of the splits, then out = Pi^T (acc/l + a S^T ask / l) (rotated V),
+// mu + V (s * acc / l) (SPECTRAL V) or acc / l (plain V).  One block per query.
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   __shared__ float s_o[kMaxD], s_k[kMaxD];
   __shared__ float s_w[256];
@@ -325,6 +349,27 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     }
     __syncthreads();
   }
+  if (p.vspectral) {
+    // out = mu + V (s * acc / l), V row-major [k][i]: one wave per output
+    // coordinate k, lanes over i (coalesced), d <= 128.
+    const int kvh = (qi % p.Hq) / p.G;
+    const float* V = p.vbasis + (size_t)kvh * d * d;
+    const float* sc = p.vscale + (size_t)kvh * d;
+    const float* mu = p.vmean + (size_t)kvh * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) s_k[i] = sc[i] * s_o[i];
+    __syncthreads();
+    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    for (int k = threadIdx.x >> 6; k < d; k += nw) {
+      float acc = 0.f;
+      for (int i = lane; i < d; i += 64) acc = fmaf(V[(size_t)k * d + i], s_k[i], acc);
+      for (int m = 32; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
+      if (lane == 0) s_w[k] = mu[k] + acc;
+    }
+    __syncthreads();
+    // A sequence with no tokens keeps its zero output.
+    for (int i = threadIdx.x; i < d; i += blockDim.x) s_o[i] = s_L > 0.f ? s_w[i] : 0.f;
+    __syncthreads();
+  }
   if (p.vrotate) {
     for (int h = 1; h < d; h <<= 1) {
       for (int i = threadIdx.x; i < d / 2; i += blockDim.x) {
@@ -342,7 +387,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     __syncthreads();
   }
   for (int i = threadIdx.x; i < d; i += blockDim.x) p.out[(size_t)qi * d + i] = s_o[i];
-  if (threadIdx.x == 0 && p.lse) p.lse[qi] = s_L > 0.f ? (s_M + log2f(s_L)) * 0.69314718055994530942f : -INFINITY;
+  if (threadIdx.x == 0 && p.lse)
+    p.lse[qi] = s_L > 0.f ? (s_M + log2f(s_L)) * 0.69314718055994530942f + (p.qoff ? p.qoff[qi] : 0.f) : -INFINITY;
 }
 
 // ---- metric scores ---------------------------------------------------------------
@@ -375,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void metric_scores_kernel(MetricScorePara
     const bool valid = t < t1;
     const int tc = valid ? t : t1 - 1;
     const int64_t vec = vbase + tc;
-    const float sh = group_sum(ks.score(p, s_kc, vec, j, L), L) * inv_sqrt_d;
+    const float sh = group_sum(ks.score(p, s_kc, vec, j, L), L) * inv_sqrt_d + (p.qoff ? p.qoff[qi] : 0.f);
     float kv[32];
     load32<TIN>(kbase + (int64_t)tc * mp.kst + 32 * j, kv);
     float sr = 0.f;

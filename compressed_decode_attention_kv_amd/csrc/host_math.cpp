@@ -1,5 +1,6 @@
-// Host-side math of libtq: the Beta Lloyd-Max codebook, the SplitMix64
-// streams of the rotation and the sketch, and the PCA of HeadQ calibration.
+// Host-side math of libtq: the Beta and Gaussian Lloyd-Max codebooks, the
+// SplitMix64 streams of the rotation and the sketch, and the eigenbases of
+// HeadQ and SpectralQuant calibration.
 //
 // [P1] = "Resumen Técnico: Inferencia Estadística y Medidas de Calidad de
 //        Cuantizaciones de Cache KV Inspiradas en TurboQuant"
@@ -170,7 +171,7 @@ void gaussian_sketch(uint64_t seed, int d, float* S) {
 // Centred covariance in double, cyclic Jacobi rotations to diagonal form,
 // eigenvectors of the r largest eigenvalues, each flipped so that its
 // largest-magnitude entry is positive.
-bool pca_basis(const float* X, int N, int d, int rank, float* U) {
+bool pca_basis(const float* X, int N, int d, int rank, float* U, float* eigenvalues, float* mean_out) {
   if (N < 2 || d < 1 || rank < 1 || rank > d) return false;
   std::vector<double> mean(d, 0.0), A((size_t)d * d, 0.0), V((size_t)d * d, 0.0);
   for (int n = 0; n < N; ++n)
@@ -232,7 +233,54 @@ bool pca_basis(const float* X, int N, int d, int rank, float* U) {
       if (std::fabs(V[(size_t)i * d + col]) > std::fabs(V[(size_t)arg * d + col])) arg = i;
     double sgn = V[(size_t)arg * d + col] < 0 ? -1.0 : 1.0;
     for (int i = 0; i < d; ++i) U[(size_t)i * rank + j] = (float)(sgn * V[(size_t)i * d + col]);
+    if (eigenvalues) eigenvalues[j] = (float)std::max(0.0, A[(size_t)col * d + col]);
   }
+  if (mean_out)
+    for (int i = 0; i < d; ++i) mean_out[i] = (float)mean[i];
+  return true;
+}
+
+// Lloyd-Max codebook of N(0, 1) at `bits` bits: boundaries at midpoints,
+// centroids at the conditional means (phi(a) - phi(b)) / (Phi(b) - Phi(a)) of
+// their cells, from the quantile midpoints to a fixed point; made exactly
+// symmetric (the middle boundary 0).  Cached per bits.
+bool gaussian_codebook(int bits, std::vector<double>* centroids, std::vector<double>* boundaries) {
+  if (bits < 1 || bits > 8) return false;
+  static std::mutex mu;
+  static std::map<int, std::pair<std::vector<double>, std::vector<double>>> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(bits);
+  if (it == cache.end()) {
+    const int K = 1 << bits;
+    const double inv_sqrt2 = 0.70710678118654752440, inv_sqrt2pi = 0.39894228040143267794;
+    auto pdf = [&](double x) { return std::isinf(x) ? 0.0 : inv_sqrt2pi * std::exp(-0.5 * x * x); };
+    auto sf = [&](double x) { return 0.5 * std::erfc(x * inv_sqrt2); };   // upper tail, exact far out
+    // Start: levels spread over +-2 standard deviations.
+    std::vector<double> c(K), t(K - 1);
+    for (int k = 0; k < K; ++k) c[k] = -2.0 + 4.0 * (k + 0.5) / K;
+    for (int iter = 0; iter < 200000; ++iter) {
+      double delta = 0.0;
+      std::vector<double> e(K + 1);
+      e[0] = -INFINITY;
+      e[K] = INFINITY;
+      for (int k = 1; k < K; ++k) e[k] = 0.5 * (c[k - 1] + c[k]);
+      for (int k = 0; k < K; ++k) {
+        const double m0 = sf(e[k]) - sf(e[k + 1]);
+        const double m1 = pdf(e[k]) - pdf(e[k + 1]);
+        const double nc = m1 / m0;
+        delta = std::max(delta, std::fabs(nc - c[k]));
+        c[k] = nc;
+      }
+      if (delta < 1e-15) break;
+    }
+    std::vector<double> cs(K);
+    for (int k = 0; k < K; ++k) cs[k] = 0.5 * (c[k] - c[K - 1 - k]);
+    for (int k = 0; k + 1 < K; ++k) t[k] = 0.5 * (cs[k] + cs[k + 1]);
+    t[K / 2 - 1] = 0.0;
+    it = cache.emplace(bits, std::make_pair(cs, t)).first;
+  }
+  *centroids = it->second.first;
+  *boundaries = it->second.second;
   return true;
 }
 

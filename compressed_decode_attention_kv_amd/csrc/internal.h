@@ -22,8 +22,13 @@ bool codebook(int d, int bits, std::vector<double>* centroids, std::vector<doubl
 // SplitMix64 streams for the sign vector and the Gaussian sketch.
 void sign_vector(uint64_t seed, int d, float* signs);
 void gaussian_sketch(uint64_t seed, int d, float* S);  // m = d rows, row-major
-// Rank-r PCA of centred rows, Jacobi eigensolver.
-bool pca_basis(const float* X, int N, int d, int rank, float* U);
+// Rank-r PCA of centred rows, Jacobi eigensolver: the top-r eigenvectors as
+// the columns of U [d][rank] (largest-|.| entry positive); optionally their
+// eigenvalues [rank] and the mean [d].
+bool pca_basis(const float* X, int N, int d, int rank, float* U, float* eigenvalues = nullptr,
+               float* mean = nullptr);
+// Lloyd-Max codebook of N(0, 1) in double, cached per bits.
+bool gaussian_codebook(int bits, std::vector<double>* centroids, std::vector<double>* boundaries);
 
 // ---- kernel parameter blocks ----------------------------------------------
 struct QuantParams {
@@ -46,6 +51,11 @@ struct QuantParams {
   int bh0, nbh, t0, tn;
   const _Float16* S16;    // PROD at d >= 256: S in fp16 (exact), fragment order (device)
   const float* rbasis;    // HEADQ: (Pi U_h)^T per head, [H][rank][d]
+  // SPECTRAL: basis (V, [H][d][d]) in `basis`, the mean and spreads [H][d],
+  // and the N(0, 1) Lloyd-Max boundaries in double.
+  const float* smean;
+  const float* sscale;
+  double gbounds[16];
   // Append: token t of sequence b is written to slot pos[b] + t (device
   // int32 [B]); slots outside [0, T_cap) are skipped.  NULL: slot t.
   const int* pos;
@@ -74,6 +84,7 @@ struct DecodeParams {
   float k_qjl, v_qjl;   // sqrt(pi/2)/m
   float scale_log2;     // log2(e)/sqrt(d)
   const float* qrot; const float* qsk; const float* qw;
+  const float* qoff;    // SPECTRAL keys: per-query score offset q . mu / sqrt(d), else NULL
   float* part;
   // Per-sequence lengths (device int32 [B]), each clamped to [0, T); NULL:
   // every sequence has T tokens.
@@ -84,6 +95,11 @@ struct QPrepParams {
   const void* q; int dtype; int B, Hq, d, Hkv;
   int64_t sb, sh;
   int rotate, kqjl, kside, rank;
+  // SPECTRAL keys: q_rot = s * (V^T q) with the query's KV head's basis,
+  // spreads and mean; qoff = q . mu / sqrt(d) (the score offset the mean adds).
+  int kspectral;
+  const float* sbasis; const float* smean; const float* sscale;
+  float* qoff;
   uint32_t signbits[kMaxD / 32];
   float inv_sqrt_d;
   const float* S; const float* basis;
@@ -99,6 +115,12 @@ struct CombineParams {
   const float* S;
   const float* part;
   float* out; float* lse;
+  // SPECTRAL values: out = mu + V (s * acc / l) with the query's KV head's
+  // basis, mean and spreads (query qi reads KV head (qi % Hq) / G).
+  int vspectral, Hq, G;
+  const float* vbasis; const float* vmean; const float* vscale;
+  // SPECTRAL keys: the per-query score offset added to the log-sum-exp.
+  const float* qoff;
 };
 
 struct MetricScoreParams {
@@ -138,6 +160,7 @@ struct RelErrParams {
   uint32_t signbits[kMaxD / 32];
   float inv_sqrt_d, qjl_c;
   const float* S; const float* basis;
+  const float* smean; const float* sscale;  // SPECTRAL: mean and spreads [H][d]
   TensorPlanes planes;
   double* block_sums;  // [gridDim][5] = err2, ref2, (1-cos) sum, count, angle sum
   float* per_vec;      // [B*H][T_cap] ||x_hat - x||^2 per vector, or NULL
@@ -145,6 +168,10 @@ struct RelErrParams {
 
 // ---- launchers (defined in the .hip files) --------------------------------
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+// SPECTRAL at d = 32, 64, 128 (quant_spectral.hip) and its reconstruction error.
+int spectral_max_d();
+hipError_t launch_quantize_spectral(const QuantParams& p, hipStream_t s);
+hipError_t launch_relerr_spectral(const RelErrParams& p, hipStream_t s);
 // PROD at d = 256..1024 with the sketch projection on the matrix cores (quant_sketch.hip).
 bool quant_sketch_supported(const QuantParams& p, const QuantGrid& grid);
 // Index of S[row][col] in the fragment-ordered fp16 copy of S that the

@@ -12,6 +12,11 @@ Regimes (the pages name them; the exact laws below are readings):
   low_rank      -- K = Z diag(sqrt(lambda)) W^T + 0.01 E, lambda_i = 0.7^i,
                    W an orthonormal d x 16 basis; queries half inside span(W)
                    (norm matched), half isotropic.
+  structured    -- K and V each a per-head mean plus a rank-16 part with
+                   lambda_i = 0.7^i on an orthonormal basis of its own, plus
+                   0.01 E; mean entries N(0, 1/d); queries half inside the key
+                   span (norm matched), half isotropic; separate calibration
+                   draws of K and V from the same law.
   rope          -- post-RoPE-like keys: N(0,1) pairs rotated by position *
                    theta_i, theta_i = 10000^(-2i/d); queries whose pair i has
                    variance proportional to 0.7^i (E||q||^2 = d), rotated by
@@ -32,6 +37,7 @@ WORKLOADS = {
     "heavy_tailed": dict(B=4, H=8, G=0, T=131072, d=128, dtype="f32"),
     "low_rank": dict(B=1, H=4, G=64, T=65536, d=1024, dtype="f32"),
     "rope_gqa": dict(B=8, H=8, G=4, T=131072, d=128, dtype="f16"),
+    "structured_decode": dict(B=16, H=32, G=1, T=32768, d=128, dtype="f16"),
 }
 
 
@@ -102,6 +108,45 @@ def low_rank(H, T, d, nq, seed=4, rank=16, decay=0.7, noise=0.01, dtype=np.float
         Q[0, h * nq + ni:(h + 1) * nq] = rng.standard_normal((nq - ni, d))
     V = _np_rng(seed, 1).standard_normal((1, H, T, d))
     return K.astype(dtype), V.astype(dtype), Q.astype(dtype)
+
+
+def _structured_law(rng, H, d, rank, decay):
+    lam = decay ** np.arange(rank)
+    laws = []
+    for _ in range(H):
+        W, _ = np.linalg.qr(rng.standard_normal((d, rank)))
+        laws.append((rng.standard_normal(d) / math.sqrt(d), W))
+    return lam, laws
+
+
+def _structured_draw(rng, lam, law, n, noise):
+    mu, W = law
+    d, rank = W.shape
+    return mu + (rng.standard_normal((n, rank)) * np.sqrt(lam)) @ W.T + noise * rng.standard_normal((n, d))
+
+
+def structured(B, H, G, T, d, seed=6, rank=16, decay=0.7, noise=0.01, n_calib=4096, dtype=np.float32):
+    """K, V [B,H,T,d] (structured regime), Q [B,H*G,d], and the calibration
+    draws CK, CV [H, n_calib, d] (float32)."""
+    rng = _np_rng(seed, 0)
+    lam, klaws = _structured_law(rng, H, d, rank, decay)
+    _, vlaws = _structured_law(rng, H, d, rank, decay)
+    K = np.empty((B, H, T, d))
+    V = np.empty((B, H, T, d))
+    Q = np.empty((B, H * G, d))
+    drng = _np_rng(seed, 1)
+    for b in range(B):
+        for h in range(H):
+            K[b, h] = _structured_draw(drng, lam, klaws[h], T, noise)
+            V[b, h] = _structured_draw(drng, lam, vlaws[h], T, noise)
+            ni = G // 2
+            g = drng.standard_normal((ni, rank)) * math.sqrt(d / rank)
+            Q[b, h * G:h * G + ni] = g @ klaws[h][1].T
+            Q[b, h * G + ni:(h + 1) * G] = drng.standard_normal((G - ni, d))
+    crng = _np_rng(seed, 2)
+    CK = np.stack([_structured_draw(crng, lam, klaws[h], n_calib, noise) for h in range(H)])
+    CV = np.stack([_structured_draw(crng, lam, vlaws[h], n_calib, noise) for h in range(H)])
+    return K.astype(dtype), V.astype(dtype), Q.astype(dtype), CK.astype(np.float32), CV.astype(np.float32)
 
 
 def _rope(X, pos, d):
@@ -213,3 +258,39 @@ def device_rope_gqa(B, Hkv, G, T, d, seed=5, n_calib=4096, decay=0.7, device="cu
     cpos = crng.integers(0, T, size=(Hkv, n_calib))
     C = _rope(crng.standard_normal((Hkv, n_calib, d)) * np.repeat(np.sqrt(lam_np), 2), cpos, d)
     return K, V, Q, C.astype(np.float32)
+
+
+def device_structured(B, H, G, T, d, seed=6, rank=16, decay=0.7, noise=0.01, n_calib=4096, device="cuda"):
+    """Full-size structured regime drawn on the device: K, V [B,H,T,d]
+    float16, Q [B,H*G,d] float16, and the calibration draws CK, CV
+    [H, n_calib, d] (host float32); the law of `structured`."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    f32 = torch.float32
+    sl = torch.sqrt(torch.tensor([decay ** i for i in range(rank)], dtype=f32, device=device))
+
+    def law():
+        W = torch.linalg.qr(torch.randn((H, d, rank), generator=g, device=device, dtype=f32))[0]
+        mu = torch.randn((H, 1, d), generator=g, device=device, dtype=f32) / math.sqrt(d)
+        return mu, W.transpose(1, 2).contiguous()          # [H, rank, d]
+
+    def draw(mu, Wt, n):
+        Z = torch.randn((H, n, rank), generator=g, device=device, dtype=f32) * sl
+        return mu + torch.matmul(Z, Wt) + noise * torch.randn((H, n, d), generator=g, device=device, dtype=f32)
+
+    (mk, Wk), (mv, Wv) = law(), law()
+    K = torch.empty((B, H, T, d), dtype=torch.float16, device=device)
+    V = torch.empty((B, H, T, d), dtype=torch.float16, device=device)
+    for b in range(B):
+        K[b] = draw(mk, Wk, T).half()
+        V[b] = draw(mv, Wv, T).half()
+    ni = G // 2
+    Q = torch.randn((B, H, G, d), generator=g, device=device, dtype=f32)
+    if ni:
+        c = torch.randn((B, H, ni, rank), generator=g, device=device, dtype=f32) * math.sqrt(d / rank)
+        Q[:, :, :ni] = torch.matmul(c, Wk.unsqueeze(0))
+    Q = Q.reshape(B, H * G, d).half()
+    CK = draw(mk, Wk, n_calib).cpu().numpy().astype(np.float32)
+    CV = draw(mv, Wv, n_calib).cpu().numpy().astype(np.float32)
+    return K, V, Q, CK, CV

@@ -21,14 +21,14 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, EINVAL, EUNSUPPORTED, EMISMATCH, ENOMEM, EDEVICE = range(6)
 F32, F16 = 0, 1
 KEYS, VALUES = 0, 1
-MODE_PLAIN, MODE_MSE, MODE_PROD, MODE_HEADQ = range(4)
-SCHEMES = {"kv": 0, "tq-kv": 1, "kqv": 2, "qkqv": 3, "tq-qkv": 4, "headq": 5}
+MODE_PLAIN, MODE_MSE, MODE_PROD, MODE_HEADQ, MODE_SPECTRAL = range(5)
+SCHEMES = {"kv": 0, "tq-kv": 1, "kqv": 2, "qkqv": 3, "tq-qkv": 4, "headq": 5, "squ-kv": 6}
 
 EXPORTS = ["tq_abi_version", "tq_status_str", "tq_last_error", "tq_codebook_build", "tq_scheme_modes",
            "tq_packed_layout", "tq_rotation_state", "tq_quantize", "tq_quantize_append",
            "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_attention_lens",
            "tq_decode_attention_static",
-           "tq_metrics_workspace_size", "tq_metrics", "tq_headq_fit",
+           "tq_metrics_workspace_size", "tq_metrics", "tq_spectral_fit", "tq_headq_fit",
            "tq_stream_read", "tq_release_cache"]
 
 
@@ -57,7 +57,7 @@ class Packed(ctypes.Structure):
                 ("side_rank", ctypes.c_int32), ("side_bits", ctypes.c_int32), ("seed", ctypes.c_uint64),
                 ("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("qjl", ctypes.c_void_p),
                 ("gamma", ctypes.c_void_p), ("side", ctypes.c_void_p), ("side_scale", ctypes.c_void_p),
-                ("basis", ctypes.c_void_p)]
+                ("basis", ctypes.c_void_p), ("mean", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
 
 
 class MetricsOut(ctypes.Structure):
@@ -146,6 +146,20 @@ def rotation_state(seed, d):
     return s, S
 
 
+def spectral_fit(calib):
+    """(basis [d, d] with the eigenvectors as columns, mean [d], scale [d]),
+    float32, of one head's calibration vectors calib [N, d]."""
+    calib = np.ascontiguousarray(calib, dtype=np.float32)
+    N, d = calib.shape
+    V = np.zeros((d, d), dtype=np.float32)
+    mu = np.zeros(d, dtype=np.float32)
+    sc = np.zeros(d, dtype=np.float32)
+    f = _P(ctypes.c_float)
+    _check(_lib.tq_spectral_fit(calib.ctypes.data_as(f), N, d, V.ctypes.data_as(f), mu.ctypes.data_as(f),
+                                sc.ctypes.data_as(f)))
+    return V, mu, sc
+
+
 def headq_fit(calib, rank):
     calib = np.ascontiguousarray(calib, dtype=np.float32)
     N, d = calib.shape
@@ -203,6 +217,7 @@ class PackedTensor:
         self.side = plane(n * lay.side_bytes) if lay.side_bytes else None
         self.side_scale = plane(n * 4) if lay.has_side_scale else None
         self.basis = None
+        self.spectral = None
         self.c = Packed()
         self.c.T_cap = T_cap
         self.c.codes = self.codes.data_ptr()
@@ -218,6 +233,7 @@ class PackedTensor:
         v = PackedTensor.__new__(PackedTensor)
         v.layout = self.layout
         v.basis = self.basis
+        v.spectral = self.spectral
         v.c = Packed()
         ctypes.pointer(v.c)[0] = self.c
         v.c.B, v.c.H = 1, 1
@@ -230,7 +246,12 @@ class PackedTensor:
         if self.c.side:
             v.c.side = self.c.side + off * lay.side_bytes
             v.c.side_scale = self.c.side_scale + off * 4
-        if self.c.basis:
+        if self.c.basis and self.c.mode == MODE_SPECTRAL:
+            d = self.c.d
+            v.c.basis = self.c.basis + h * d * d * 4
+            v.c.mean = self.c.mean + h * d * 4
+            v.c.scale = self.c.scale + h * d * 4
+        elif self.c.basis:
             d, r = self.c.d, self.c.side_rank
             v.c.basis = self.c.basis + h * d * r * 4
         v._parent = self
@@ -269,6 +290,21 @@ def _check_basis(basis, x, H, d):
         raise ValueError("HeadQ basis must be on the input's device (%s, got %s)" % (x.device, basis.device))
 
 
+def _check_spectral(spectral, x, H, d):
+    """The ABI reads the SPECTRAL state as dense float32 arrays on the input's
+    device: basis [H][d][d] (V[h][k][i], eigenvector i in column i), mean and
+    scale [H][d]."""
+    torch = _torch()
+    if spectral is None or len(spectral) != 3:
+        raise ValueError("SPECTRAL needs spectral=(basis [H, d, d], mean [H, d], scale [H, d])")
+    for t, shape, name in zip(spectral, [(H, d, d), (H, d), (H, d)], ["basis", "mean", "scale"]):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError("SPECTRAL %s must be contiguous float32 %s, got %s %s"
+                             % (name, shape, t.dtype, tuple(t.shape)))
+        if t.device != x.device:
+            raise ValueError("SPECTRAL %s must be on the input's device (%s, got %s)" % (name, x.device, t.device))
+
+
 def _override(mode, bits):
     """The per-tensor (mode, index bits) override, or None for the preset."""
     if mode is None and bits is None:
@@ -278,10 +314,13 @@ def _override(mode, bits):
     return ModeOverride(mode, bits)
 
 
-def quantize(x, which, scheme, n_bits, seed=0, basis=None, rank=16, side_bits=4, T_cap=None, mode=None, bits=None):
+def quantize(x, which, scheme, n_bits, seed=0, basis=None, rank=16, side_bits=4, T_cap=None, mode=None, bits=None,
+             spectral=None):
     """Quantise x [B, H, T, d] (device, fp16/fp32) into a new PackedTensor.
     The tensor's (mode, index bits) come from (scheme, n_bits, which), or
-    from `mode` and `bits` when both are given (per-tensor override)."""
+    from `mode` and `bits` when both are given (per-tensor override).
+    HEADQ takes `basis` [H, d, rank]; SPECTRAL takes `spectral` = (basis
+    [H, d, d], mean [H, d], scale [H, d]), device float32."""
     desc, x4 = tensor_desc(x)
     ovr = _override(mode, bits)
     if ovr is None:
@@ -294,6 +333,10 @@ def quantize(x, which, scheme, n_bits, seed=0, basis=None, rank=16, side_bits=4,
     pt = PackedTensor(desc.B, desc.H, T_cap or desc.T, desc.d, mode, bits,
                       rank if hq else 0, side_bits if hq else 0, device=x.device)
     pt.basis = basis
+    if mode == MODE_SPECTRAL:
+        _check_spectral(spectral, x, desc.H, desc.d)
+        pt.spectral = tuple(spectral)
+        pt.c.basis, pt.c.mean, pt.c.scale = (t.data_ptr() for t in spectral)
     _check(_lib.tq_quantize(ctypes.byref(desc), which, SCHEMES.get(scheme, scheme), n_bits, seed,
                             ctypes.byref(ovr) if ovr else None, ctypes.byref(hq) if hq else None,
                             ctypes.byref(pt.c), _stream()))

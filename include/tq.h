@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 4
+#define TQ_ABI_VERSION 5
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -76,17 +76,29 @@ typedef enum tq_tensor { TQ_KEYS = 0, TQ_VALUES = 1 } tq_tensor;
  *   PROD:  [P1] "Esquemas de Cuantización" 2-3: MSE at n-1 bits plus a 1-bit
  *          QJL sketch sign(S r) and ||r|| of the rotated residual.
  *   HEADQ: [P3] section 3 "Metodologia: HeadQ": MSE base at 2 bits plus a
- *          rank-r side code of the residual in a query-PCA basis (keys only). */
-typedef enum tq_mode { TQ_MODE_PLAIN = 0, TQ_MODE_MSE = 1, TQ_MODE_PROD = 2, TQ_MODE_HEADQ = 3 } tq_mode;
+ *          rank-r side code of the residual in a query-PCA basis (keys only).
+ *   SPECTRAL: [P2] "Configuração Experimental" (SpectralQuant) with the
+ *          uniform allocation of "Recomendações Práticas" 2-3 (SQU-KV): the
+ *          norm split about a calibrated mean mu, x - mu = nu u; the direction
+ *          in a calibrated per-head eigenbasis V, z = V^T u; every coordinate
+ *          coded at the same width against the Lloyd-Max codebook of N(0, 1)
+ *          after scaling by its calibrated spread s_i: idx_i = #{k : z_i >=
+ *          s_i t_k}; x_hat = mu + nu V (s * c[idx]).  No sketch.  The decision
+ *          is taken in double precision (the small spreads of a low-rank head
+ *          would turn float rounding into code changes).  d <= 128. */
+typedef enum tq_mode {
+  TQ_MODE_PLAIN = 0, TQ_MODE_MSE = 1, TQ_MODE_PROD = 2, TQ_MODE_HEADQ = 3, TQ_MODE_SPECTRAL = 4
+} tq_mode;
 
 /* Scheme presets at a budget of n bits per coordinate ([P1] "Esquemas de
  * Cuantización", [P2] "Contribuições Principais" 1, [P3] section 3):
  *   KV     K PLAIN(n)  V PLAIN(n)      TQ_KV  K MSE(n)   V MSE(n)
  *   KQV    K MSE(n)    V PROD(n)       QKQV   K PROD(n)  V PROD(n)
- *   TQ_QKV K PROD(n)   V MSE(n)        HEADQ  K HEADQ(2) V MSE(n)          */
+ *   TQ_QKV K PROD(n)   V MSE(n)        HEADQ  K HEADQ(2) V MSE(n)
+ *   SQU_KV K SPECTRAL(n) V SPECTRAL(n)  ([P2] "Recomendações Práticas" 2)   */
 typedef enum tq_scheme {
   TQ_SCHEME_KV = 0, TQ_SCHEME_TQ_KV = 1, TQ_SCHEME_KQV = 2,
-  TQ_SCHEME_QKQV = 3, TQ_SCHEME_TQ_QKV = 4, TQ_SCHEME_HEADQ = 5
+  TQ_SCHEME_QKQV = 3, TQ_SCHEME_TQ_QKV = 4, TQ_SCHEME_HEADQ = 5, TQ_SCHEME_SQU_KV = 6
 } tq_scheme;
 
 /* Per-tensor choice of quantiser mode and index width, overriding the
@@ -94,7 +106,7 @@ typedef enum tq_scheme {
  * Principais" 1 compare per-tensor choices of rotation, scalar code and QJL
  * sketch; the presets above are the combinations the pages name).
  *   mode:  tq_mode.  HEADQ only for keys (and with a tq_headq).
- *   bits:  width of the Lloyd-Max index, in [1, 4] (PLAIN, MSE), [1, 3]
+ *   bits:  width of the Lloyd-Max index, in [1, 4] (PLAIN, MSE, SPECTRAL), [1, 3]
  *          (PROD: each field is bits + 1 wide, the QJL sign beside the
  *          index), 2 (HEADQ base).  A PROD tensor at bits = b spends b + 1
  *          bits per coordinate, the budget of a preset at n = b + 1. */
@@ -131,8 +143,9 @@ typedef struct tq_headq {
   int32_t side_bits; /* q_s in [2, 8]                              */
 } tq_headq;
 
-/* One packed tensor.  The caller sets T_cap and the plane pointers; the
- * header fields are written by tq_quantize. */
+/* One packed tensor.  The caller sets T_cap and the plane pointers (and,
+ * for SPECTRAL, basis, mean and scale); the other header fields are written
+ * by tq_quantize. */
 typedef struct tq_packed {
   int32_t B, H, T, T_cap, d;
   int32_t mode;      /* tq_mode                                           */
@@ -145,7 +158,11 @@ typedef struct tq_packed {
   float* gamma;
   uint8_t* side;
   float* side_scale;
-  const float* basis; /* HEADQ: U, device [H][d][side_rank] */
+  const float* basis; /* HEADQ: U, device [H][d][side_rank];
+                         SPECTRAL: V, device [H][d][d], V[h][k][i] = entry k of
+                         eigenvector i (caller-owned, set before tq_quantize) */
+  const float* mean;  /* SPECTRAL: mu, device [H][d]                       */
+  const float* scale; /* SPECTRAL: s, device [H][d] (s_i >= 0)             */
 } tq_packed;
 
 /* Quality measures ([P1] "Métricas de Evaluación" and "Significado y
@@ -217,7 +234,8 @@ tq_status tq_rotation_state(uint64_t seed, int32_t d, float* signs, float* S);
  * Mode and bits come from (scheme, n_bits, which), or from `ovr` when it is
  * non-NULL (scheme and n_bits are then ignored; `which` still decides
  * whether HEADQ is allowed).  n_bits in [1, 4] (PROD needs n_bits >= 2).
- * hq must be non-NULL exactly when the mode is HEADQ.  out->T_cap >= x->T
+ * hq must be non-NULL exactly when the mode is HEADQ; for SPECTRAL the caller
+ * sets out->basis, out->mean and out->scale (d <= 128).  out->T_cap >= x->T
  * (0 means x->T); the planes the mode needs must be set, 16-byte aligned and
  * sized per tq_packed_layout.  Writes tokens [0, x->T) and sets out->T =
  * x->T.  Stream-ordered. */
@@ -292,6 +310,15 @@ tq_status tq_metrics_workspace_size(const tq_tensor_desc* q, const tq_packed* k,
 tq_status tq_metrics(const tq_tensor_desc* q, const tq_tensor_desc* k_ref, const tq_tensor_desc* v_ref,
                      const tq_packed* k, const tq_packed* v, tq_metrics_out* out, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* SpectralQuant calibration ([P2] "Configuração Experimental": a per-head
+ * eigenvector basis from representative tokens; K and V calibrated on
+ * separate sets): from calib [N][d] (host fp32, one head's vectors), the
+ * mean (host fp32 [d]), the eigenvectors of the centred covariance as the
+ * columns of basis (host fp32 [d][d], descending eigenvalues, each column's
+ * largest-magnitude entry positive) and the spreads scale_i =
+ * sqrt(lambda_i / sum lambda) (host fp32 [d]).  Host only, synchronous. */
+tq_status tq_spectral_fit(const float* calib, int32_t N, int32_t d, float* basis, float* mean, float* scale);
 
 /* HeadQ calibration ([P3] section 3, "Calibração"): rank-r PCA of the
  * centred calibration queries calib [N][d] (host fp32).  U: host fp32

@@ -3,7 +3,10 @@ compare it with the float64 oracle head by head."""
 import numpy as np
 import torch
 
+from oracle import spectral as osq
 from tests import parity_util as pu
+
+MODE_SPECTRAL = 4
 
 
 def dev(a, dtype=None):
@@ -13,12 +16,25 @@ def dev(a, dtype=None):
     return t.cuda()
 
 
-def run_case(tq, K, V, Q, scheme, n, seed=0, U=None, dtype=None, label="", modes=None):
+def spectral_states(CK, CV):
+    """Per-head SpectralQuant state (basis, mean, spreads) of the keys and
+    values, fitted by the oracle on the calibration draws CK, CV [H, N, d]
+    and rounded to float32 (the values both sides then read)."""
+    out = {}
+    for name, C in (("K", CK), ("V", CV)):
+        fits = [osq.fit(C[h].astype(np.float64)) for h in range(C.shape[0])]
+        out[name] = tuple(np.stack([f[i] for f in fits]).astype(np.float32) for i in range(3))
+    return out
+
+
+def run_case(tq, K, V, Q, scheme, n, seed=0, U=None, dtype=None, label="", modes=None, spectral=None):
     """K, V [B, H, T, d], Q [B, H*G, d] (numpy).  Quantise and decode on the
     GPU, run the oracle per (b, h), compare everything.  Returns the worst
     output error, the in-band mismatch count, the packed tensors, the device
     inputs and the oracle's dense (K_hat, V_hat) per (b, h).  modes:
-    ((k_mode, k_bits), (v_mode, v_bits)) per-tensor overrides of the preset."""
+    ((k_mode, k_bits), (v_mode, v_bits)) per-tensor overrides of the preset.
+    spectral: {"K": (basis [H,d,d], mean [H,d], scale [H,d]), "V": ...}
+    float32 numpy, for SPECTRAL tensors."""
     B, H, T, d = K.shape
     Hq = Q.shape[1]
     G = Hq // H
@@ -30,13 +46,22 @@ def run_case(tq, K, V, Q, scheme, n, seed=0, U=None, dtype=None, label="", modes
     Qh_in = Qd.double().cpu().numpy()
     basis = dev(U.astype(np.float32)) if U is not None else None
     (km, kb), (vm, vb) = modes if modes is not None else ((None, None), (None, None))
-    kp = tq.quantize(Kd, tq.KEYS, scheme, n, seed, basis=basis, mode=km, bits=kb)
-    vp = tq.quantize(Vd, tq.VALUES, scheme, n, seed, mode=vm, bits=vb)
+    spec = {k: tuple(dev(a) for a in v) for k, v in spectral.items()} if spectral else {}
+    kp = tq.quantize(Kd, tq.KEYS, scheme, n, seed, basis=basis, mode=km, bits=kb, spectral=spec.get("K"))
+    vp = tq.quantize(Vd, tq.VALUES, scheme, n, seed, mode=vm, bits=vb, spectral=spec.get("V"))
     out, lse = tq.decode_attention(Qd, kp, vp)
     torch.cuda.synchronize()
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     kplanes, vplanes = kp.planes(), vp.planes()
-    kmode, vmode = pu.MODE_NAMES[kp.c.mode], pu.MODE_NAMES[vp.c.mode]
+    kmode, vmode = pu.MODE_NAMES.get(kp.c.mode), pu.MODE_NAMES.get(vp.c.mode)
+
+    def match(X, planes, pk, mode, name, h, Uh=None):
+        if pk.c.mode == MODE_SPECTRAL:
+            Vb, mu, sc = spectral[name]
+            st = osq.SQState(Vb[h], mu[h], sc[h], pk.c.bits)
+            return pu.spectral_match(X, planes, st, label=label + " " + name)
+        return pu.oracle_match(X, planes, mode, pk.c.bits, seed, U=Uh, label=label + " " + name)
+
     n_band, n_dec = 0, 0
     worst = 0.0
     heads = []
@@ -44,10 +69,8 @@ def run_case(tq, K, V, Q, scheme, n, seed=0, U=None, dtype=None, label="", modes
         for h in range(H):
             sl = slice((b * H + h) * T, (b * H + h + 1) * T)
             Uh = U[h] if U is not None else None
-            _, Khat, _, nb1, nd1 = pu.oracle_match(Kh_in[b, h], {k: v[sl] for k, v in kplanes.items()}, kmode,
-                                                   kp.c.bits, seed, U=Uh, label=label + " K")
-            _, Vhat, _, nb2, nd2 = pu.oracle_match(Vh_in[b, h], {k: v[sl] for k, v in vplanes.items()}, vmode,
-                                                   vp.c.bits, seed, label=label + " V")
+            _, Khat, _, nb1, nd1 = match(Kh_in[b, h], {k: v[sl] for k, v in kplanes.items()}, kp, kmode, "K", h, Uh)
+            _, Vhat, _, nb2, nd2 = match(Vh_in[b, h], {k: v[sl] for k, v in vplanes.items()}, vp, vmode, "V", h)
             heads.append((Khat, Vhat))
             n_band += nb1 + nb2
             n_dec += nd1 + nd2

@@ -18,6 +18,7 @@ from oracle import attention as oat
 from oracle import headq as ohq
 from oracle import metrics as ome
 from oracle import quantizer as oqz
+from oracle import spectral as osq
 
 BAND = 1e-6
 SIDE_BAND = 1e-5
@@ -97,6 +98,27 @@ def oracle_match(X, gpu, mode, n_bits_index, seed, U=None, side_bits=4, label=""
     assert np.all(np.abs(nu - base["nu"]) <= 1e-6 * base["nu"]), "%s: norms differ" % label
     xhat = q["khat"] if headq else oqz.dequantize(q, st)
     return q, xhat, st, n_band, ndec
+
+
+def spectral_match(X, gpu, st, label=""):
+    """SpectralQuant counterpart of oracle_match: X [N, d] float64, st an
+    oracle SQState built from the same float32 basis, mean and spreads the
+    GPU read.  Codes exact outside the band (distance of z_i to its nearest
+    boundary s_i t_k), norms to float32 rounding.  Returns (q, x_hat, st,
+    n_in_band, n_decisions)."""
+    N, d = X.shape
+    q = osq.quantize(X, st)
+    g_idx = oqz.unpack_bits(gpu["codes"][:N], st.bits, d)
+    cmis = g_idx != q["idx"]
+    bad = cmis & (q["bdist"] > BAND)
+    assert not bad.any(), "%s: %d code mismatches outside the band (first at %s)" % (
+        label, bad.sum(), np.argwhere(bad)[0])
+    if cmis.any():
+        q = osq.quantize(X, st, flip_codes=cmis)
+    assert np.array_equal(g_idx, q["idx"])
+    nu = gpu["norms"][:N].astype(np.float64)
+    assert np.all(np.abs(nu - q["nu"]) <= 1e-6 * q["nu"]), "%s: norms differ" % label
+    return q, osq.dequantize(q, st), st, int(cmis.sum()), N * d
 
 
 def rel_l2(a, b):

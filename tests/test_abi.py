@@ -11,6 +11,7 @@ import pytest
 from oracle import codebook as ocb
 from oracle import headq as ohq
 from oracle import rng as orng
+from oracle import spectral as osq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -27,7 +28,7 @@ def test_exports_every_declared_symbol(tqlib):
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(tqlib.EXPORTS) == names
-    assert tqlib.lib().tq_abi_version() == 4
+    assert tqlib.lib().tq_abi_version() == 5
 
 
 @pytest.mark.parametrize("d,bits", [(32, 1), (128, 2), (128, 3), (128, 4), (1024, 2), (1024, 4)])
@@ -59,6 +60,8 @@ def test_scheme_modes_table(tqlib):
     assert tqlib.scheme_modes("qkqv", 4, K) == (Q, 3) and tqlib.scheme_modes("qkqv", 2, V) == (Q, 1)
     assert tqlib.scheme_modes("tq-qkv", 3, K) == (Q, 2) and tqlib.scheme_modes("tq-qkv", 3, V) == (M, 3)
     assert tqlib.scheme_modes("headq", 4, K) == (H, 2) and tqlib.scheme_modes("headq", 4, V) == (M, 4)
+    S = tqlib.MODE_SPECTRAL
+    assert tqlib.scheme_modes("squ-kv", 2, K) == (S, 2) and tqlib.scheme_modes("squ-kv", 3, V) == (S, 3)
 
 
 def test_layouts(tqlib):
@@ -73,6 +76,13 @@ def test_layouts(tqlib):
     assert (lay.code_bytes, lay.side_bytes, lay.has_side_scale) == (32, 8, 1)
     lay = tqlib.packed_layout(1024, tqlib.MODE_PROD, 3)
     assert (lay.code_bytes, lay.qjl_bytes) == (512, 0)
+    lay = tqlib.packed_layout(128, tqlib.MODE_SPECTRAL, 3)
+    assert (lay.code_bytes, lay.qjl_bytes, lay.has_gamma, lay.side_bytes) == (48, 0, 0, 0)
+    lay = tqlib.packed_layout(32, tqlib.MODE_SPECTRAL, 1)
+    assert lay.code_bytes == 4
+    # The head's basis is held on chip: d <= 128.
+    with pytest.raises(tqlib.TQError):
+        tqlib.packed_layout(256, tqlib.MODE_SPECTRAL, 2)
 
 
 @pytest.mark.parametrize("bad", [
@@ -87,6 +97,10 @@ def test_layouts(tqlib):
     dict(ovr=(1, 0)), dict(ovr=(1, 5)), dict(ovr=(2, 4)), dict(ovr=(2, 0)), dict(ovr=(7, 2)),
     dict(ovr=(3, 2), which=1, give_hq=True), dict(ovr=(3, 3), give_hq=True), dict(ovr=(3, 2), no_hq=True),
     dict(ovr=(2, 2), no_gamma=True),
+    # SPECTRAL: state missing, misaligned, too wide, with a HeadQ basis, bad bits
+    dict(scheme="squ-kv"), dict(scheme="squ-kv", spec_align=2), dict(scheme="squ-kv", d=256, give_spec=True),
+    dict(scheme="squ-kv", give_spec=True, give_hq=True), dict(ovr=(4, 5), give_spec=True),
+    dict(ovr=(4, 0), give_spec=True), dict(ovr=(4, 2), which=1),
 ])
 def test_quantize_rejects_before_any_gpu_call(tqlib, bad):
     """Fake (never dereferenced) but aligned pointers: every case must be
@@ -103,6 +117,10 @@ def test_quantize_rejects_before_any_gpu_call(tqlib, bad):
     out.gamma = None if bad.get("no_gamma") else fake
     out.side = fake
     out.side_scale = fake
+    if bad.get("give_spec") or "spec_align" in bad:
+        out.basis = fake
+        out.mean = fake + bad.get("spec_align", 0)
+        out.scale = fake
     hq = None
     scheme = bad.get("scheme", "tq-kv")
     if (scheme == "headq" and not bad.get("no_hq")) or bad.get("give_hq"):
@@ -154,6 +172,58 @@ def test_decode_rejects_mismatches(tqlib):
     assert lib.tq_decode_workspace_size(ctypes.byref(k4), ctypes.byref(v), 4, ctypes.byref(n)) == tqlib.OK
     assert lib.tq_decode_attention(ctypes.byref(q), ctypes.byref(k4), ctypes.byref(v), out, None, fake,
                                    1 << 30, None) == tqlib.EUNSUPPORTED
+
+
+def test_decode_rejects_spectral_without_state(tqlib):
+    """A SPECTRAL header without its basis, mean or spreads is refused on the
+    host, by the workspace query and the decode."""
+    lib = tqlib.lib()
+    fake = 1 << 20
+    k = _packed(tqlib, tqlib.MODE_SPECTRAL, 3)
+    v = _packed(tqlib, tqlib.MODE_SPECTRAL, 3)
+    n = ctypes.c_size_t()
+    for missing in ("basis", "mean", "scale"):
+        k.basis, k.mean, k.scale = fake, fake, fake
+        setattr(k, missing, None)
+        assert lib.tq_decode_workspace_size(ctypes.byref(k), ctypes.byref(v), 2, ctypes.byref(n)) == tqlib.EINVAL
+    k.basis, k.mean, k.scale = fake, fake, fake
+    v.basis, v.mean, v.scale = fake, fake, fake
+    assert lib.tq_decode_workspace_size(ctypes.byref(k), ctypes.byref(v), 2, ctypes.byref(n)) == tqlib.OK
+    # The workspace grows by the per-query score offsets of SPECTRAL keys.
+    m = _packed(tqlib, tqlib.MODE_MSE, 3)
+    n2 = ctypes.c_size_t()
+    assert lib.tq_decode_workspace_size(ctypes.byref(m), ctypes.byref(v), 2, ctypes.byref(n2)) == tqlib.OK
+    assert n.value >= n2.value
+
+
+def test_spectral_fit_matches_oracle(tqlib):
+    """tq_spectral_fit (Jacobi in double on the host) against the oracle's
+    fit (LAPACK eigh): the same mean, spreads, eigenvectors with the same
+    sign convention (well separated spectrum), orthonormal columns."""
+    rng = np.random.default_rng(11)
+    d = 64
+    W, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    lam = 0.8 ** np.arange(d)
+    X = ((rng.standard_normal((5000, d)) * np.sqrt(lam)) @ W.T + 0.3).astype(np.float32)
+    V, mu, s = tqlib.spectral_fit(X)
+    Vo, muo, so = osq.fit(X.astype(np.float64))
+    assert np.max(np.abs(V.T.astype(np.float64) @ V - np.eye(d))) < 1e-5
+    assert np.max(np.abs(mu - muo)) < 1e-6
+    assert np.max(np.abs(s - so)) < 1e-6
+    assert abs(float(np.sum(s.astype(np.float64) ** 2)) - 1.0) < 1e-5
+    assert np.max(np.abs(V - Vo)) < 1e-3
+    with pytest.raises(tqlib.TQError):
+        tqlib.spectral_fit(np.zeros((10, 256), dtype=np.float32))
+
+
+def test_binding_refuses_bad_spectral_state(tqlib):
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 2, 8, 64), dtype=torch.float32)
+    good = (torch.zeros((2, 64, 64)), torch.zeros((2, 64)), torch.zeros((2, 64)))
+    for bad in (None, good[:2], (good[0].transpose(1, 2), good[1], good[2]),
+                (good[0], good[1].double(), good[2]), (good[0], good[1], torch.zeros((2, 32)))):
+        with pytest.raises(ValueError):
+            tqlib.quantize(x, tqlib.KEYS, "squ-kv", 2, spectral=bad)
 
 
 def test_headq_fit_matches_oracle_projector(tqlib):
