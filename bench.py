@@ -12,8 +12,9 @@ along.  `roofline` covers the decode chain, `quantize_roofline` the K + V
 quantize of the step; `quality` holds the measures of the packed cache at the
 workload's full size (computed outside the timed region); `cpu_baseline`
 times the float64 oracle on a bounded sample of the same workload on the
-host cores.  --workload heavy-tailed | low-rank | headq-gqa prints the line of
-another regime at its own full size instead (timings and quality).
+host cores.  --workload heavy-tailed | low-rank | headq-gqa | structured prints
+the line of another regime at its own full size instead (timings and quality;
+structured compares SQU-KV with TQ-KV).
 """
 import argparse
 import json
@@ -229,6 +230,49 @@ def other_workload(args):
                          "decode_GBps": round(nb / (d_ms * 1e-3) / 1e9, 1), "queries": int(Q.shape[1]),
                          "quality": _quality(tq, Q, K, V, kp, vp)})
         cfg = "low-rank: H=4 T=65536 d=1024 fp32, K rank 16 (0.7^i) + 0.01 noise, 64 queries per head"
+    elif args.workload == "structured":
+        # SQU-KV against TQ-KV at 2 and 3 bits ([P2] Recomendações Práticas 2:
+        # structured data, low bit widths) at the headline decode shape.
+        B, H, G, T, d = 16, 32, 1, 32768, 128
+        K, V, Q, CK, CV = synth.device_structured(B, H, G, T, d, seed=66)
+        fit_t0 = time.time()
+        spec = {}
+        for name, C in (("K", CK), ("V", CV)):
+            fits = [tq.spectral_fit(C[h]) for h in range(H)]
+            spec[name] = tuple(torch.from_numpy(np.ascontiguousarray(np.stack([f[i] for f in fits]))).cuda()
+                               for i in range(3))
+        fit_s = time.time() - fit_t0
+        in_bytes = 2 * K.numel() * 2
+        for scheme in ("squ-kv", "tq-kv"):
+            for n in (2, 3):
+                ks, vs = (spec["K"], spec["V"]) if scheme == "squ-kv" else (None, None)
+                ps = []
+
+                def quant():
+                    ps[:] = [tq.quantize(K, tq.KEYS, scheme, n, 0, spectral=ks),
+                             tq.quantize(V, tq.VALUES, scheme, n, 0, spectral=vs)]
+                q_ms = _median_ms(torch, quant, args.steps, args.warmup)
+                kp, vp = ps
+                out, lse = tq.decode_attention(Q, kp, vp)
+                ws = torch.empty(tq.decode_workspace_size(kp, vp, Q.shape[1]), dtype=torch.uint8, device="cuda")
+                d_ms = _median_ms(torch, lambda: tq.decode_attention(Q, kp, vp, out, lse, ws), args.steps,
+                                  args.warmup)
+                nb = packed_bytes(kp) + packed_bytes(vp)
+                row = {"scheme": scheme, "n_bits": n, "quantize_ms": round(q_ms, 4),
+                       "quantize_tok_per_s": round(B * H * T / (q_ms * 1e-3), 1),
+                       "quantize_hbm_GBps": round((in_bytes + nb) / (q_ms * 1e-3) / 1e9, 1),
+                       "decode_ms": round(d_ms, 4), "decode_GBps": round(nb / (d_ms * 1e-3) / 1e9, 1),
+                       "decode_pct_hbm_peak": round(100.0 * nb / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                       "quality": _quality(tq, Q, K, V, kp, vp)}
+                if scheme == "squ-kv":
+                    # The SQU-KV write side is fp64-bound: 2 d^2 flops per token-head per tensor.
+                    fl = 2.0 * 2 * d * d * B * H * T
+                    row["quantize_fp64_TFLOPs"] = round(fl / (q_ms * 1e-3) / 1e12, 2)
+                    row["quantize_pct_fp64_peak"] = round(100.0 * fl / (q_ms * 1e-3) / 1e12 / 78.6, 2)
+                rows.append(row)
+        cfg = "structured: B=16 H=32 T=32768 d=128 fp16, K and V each a per-head mean + rank-16 (0.7^i) + 0.01 " \
+              "noise, 1 query per head (those of the even heads in the key span); SQU-KV fitted by " \
+              "tq_spectral_fit on 4096 separate calibration draws per head and tensor (%.1f s on the host)" % fit_s
     else:  # headq-gqa
         B, Hkv, G, T, d, r = 8, 8, 4, 131072, 128, 16
         K, V, Q, C = synth.device_rope_gqa(B, Hkv, G, T, d, seed=55)
@@ -273,7 +317,7 @@ def main():
     ap.add_argument("--B", type=int, default=16)
     ap.add_argument("--H", type=int, default=32)
     ap.add_argument("--T", type=int, default=32768)
-    ap.add_argument("--workload", default="isotropic", choices=["isotropic", "heavy-tailed", "low-rank", "headq-gqa"],
+    ap.add_argument("--workload", default="isotropic", choices=["isotropic", "heavy-tailed", "low-rank", "headq-gqa", "structured"],
                     help="isotropic: the headline line; the others print their own line")
     args = ap.parse_args()
     if args.gpus != 1:

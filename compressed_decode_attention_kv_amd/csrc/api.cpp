@@ -240,8 +240,10 @@ tq_status hip_status(hipError_t e, const char* what) {
   return TQ_OK;
 }
 
+// The SPECTRAL state: basis 16-byte aligned (read with 16-byte loads),
+// mean and spreads 4-byte aligned.
 bool spectral_ok(const float* basis, const float* mean, const float* scale) {
-  return basis && mean && scale && aligned(basis, 4) && aligned(mean, 4) && aligned(scale, 4);
+  return basis && mean && scale && aligned(basis, 16) && aligned(mean, 4) && aligned(scale, 4);
 }
 
 tq_status check_packed(const tq_packed* p, const char* name) {
@@ -257,7 +259,7 @@ tq_status check_packed(const tq_packed* p, const char* name) {
   if (p->mode == TQ_MODE_HEADQ && (!p->side || !p->side_scale || !p->basis || !aligned(p->side, 16) || !aligned(p->side_scale, 16)))
     return fail(TQ_EINVAL, "%s HeadQ planes or basis missing or misaligned", name);
   if (p->mode == TQ_MODE_SPECTRAL && !spectral_ok(p->basis, p->mean, p->scale))
-    return fail(TQ_EINVAL, "%s SPECTRAL basis, mean or scale missing or not 4-byte aligned", name);
+    return fail(TQ_EINVAL, "%s SPECTRAL basis (16-byte aligned), mean or scale (4-byte aligned) missing or misaligned", name);
   return TQ_OK;
 }
 
@@ -597,7 +599,7 @@ tq_status tq_quantize(const tq_tensor_desc* x, int32_t which, int32_t scheme, in
   if ((mode == TQ_MODE_HEADQ) != (hq != nullptr))
     return fail(TQ_EINVAL, mode == TQ_MODE_HEADQ ? "HeadQ keys need a tq_headq" : "tq_headq given for a non-HeadQ tensor");
   if (mode == TQ_MODE_SPECTRAL && !spectral_ok(out->basis, out->mean, out->scale))
-    return fail(TQ_EINVAL, "SPECTRAL needs out->basis, out->mean and out->scale (device, 4-byte aligned)");
+    return fail(TQ_EINVAL, "SPECTRAL needs out->basis (16-byte aligned), out->mean and out->scale (4-byte aligned) on the device");
   tq_layout lay;
   if (tq_status s = layout_of(x->d, mode, bits, hq ? hq->rank : 0, hq ? hq->side_bits : 0, &lay)) return s;
   if (hq && (!hq->basis || !aligned(hq->basis, 4))) return fail(TQ_EINVAL, "HeadQ basis is NULL or misaligned");

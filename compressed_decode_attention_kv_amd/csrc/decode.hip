@@ -64,13 +64,20 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(QPrepParams p) {
     // q . k_hat = q . mu + nu sum_i (s_i (V^T q)_i) c[idx_i]: the score runs
     // on s * V^T q like a rotated query; the mean adds q . mu / sqrt(d) to
     // every score of the query (softmax-invariant; only the LSE moves).
+    // The head's basis is staged in (dynamic) LDS with 16-byte loads, all
+    // in flight at once: read straight from L2, the d-long dependent loop
+    // waited one load latency per term.
     __shared__ float s_red[kThreads / 64];
-    const float* V = p.sbasis + (size_t)kvh * d * d;
+    extern __shared__ float4 s_dyn[];
+    float* sV = reinterpret_cast<float*>(s_dyn);
+    const float4* V4 = reinterpret_cast<const float4*>(p.sbasis + (size_t)kvh * d * d);
     const float* sc = p.sscale + (size_t)kvh * d;
     const float* mu = p.smean + (size_t)kvh * d;
+    for (int e = threadIdx.x; e < d * d / 4; e += blockDim.x) s_dyn[e] = V4[e];
+    __syncthreads();
     for (int i = threadIdx.x; i < d; i += blockDim.x) {
       float acc = 0.f;
-      for (int k = 0; k < d; ++k) acc = fmaf(V[(size_t)k * d + i], s_q[k], acc);
+      for (int k = 0; k < d; ++k) acc = fmaf(sV[k * d + i], s_q[k], acc);
       s_r[i] = sc[i] * acc;
     }
     float part = 0.f;
@@ -352,18 +359,25 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   if (p.vspectral) {
     // out = mu + V (s * acc / l), V row-major [k][i]: one wave per output
     // coordinate k, lanes over i (coalesced), d <= 128.
+    // The basis is staged in (dynamic) LDS as for the query prep; thread k
+    // then forms row k (row-major [k][i], reads spread over the banks by the
+    // per-row offset k).
     const int kvh = (qi % p.Hq) / p.G;
-    const float* V = p.vbasis + (size_t)kvh * d * d;
+    extern __shared__ float4 s_dyn[];
+    float* sV = reinterpret_cast<float*>(s_dyn);
+    const float4* V4 = reinterpret_cast<const float4*>(p.vbasis + (size_t)kvh * d * d);
     const float* sc = p.vscale + (size_t)kvh * d;
     const float* mu = p.vmean + (size_t)kvh * d;
+    for (int e = threadIdx.x; e < d * d / 4; e += blockDim.x) s_dyn[e] = V4[e];
     for (int i = threadIdx.x; i < d; i += blockDim.x) s_k[i] = sc[i] * s_o[i];
     __syncthreads();
-    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-    for (int k = threadIdx.x >> 6; k < d; k += nw) {
+    for (int k = threadIdx.x; k < d; k += blockDim.x) {
       float acc = 0.f;
-      for (int i = lane; i < d; i += 64) acc = fmaf(V[(size_t)k * d + i], s_k[i], acc);
-      for (int m = 32; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
-      if (lane == 0) s_w[k] = mu[k] + acc;
+      for (int u = 0; u < d; ++u) {
+        const int i = (u + k) & (d - 1);
+        acc = fmaf(sV[k * d + i], s_k[i], acc);
+      }
+      s_w[k] = mu[k] + acc;
     }
     __syncthreads();
     // A sequence with no tokens keeps its zero output.
@@ -594,12 +608,14 @@ hipError_t launch_ms(const MetricScoreParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_qprep(const QPrepParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(qprep_kernel, dim3(p.B * p.Hq), dim3(kThreads), 0, s, p);
+  const size_t dyn = p.kspectral ? (size_t)p.d * p.d * sizeof(float) : 0;  // the SPECTRAL basis (d <= 128)
+  hipLaunchKernelGGL(qprep_kernel, dim3(p.B * p.Hq), dim3(kThreads), dyn, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(p.nq), dim3(kThreads), 0, s, p);
+  const size_t dyn = p.vspectral ? (size_t)p.d * p.d * sizeof(float) : 0;  // the SPECTRAL basis (d <= 128)
+  hipLaunchKernelGGL(combine_kernel, dim3(p.nq), dim3(kThreads), dyn, s, p);
   return hipGetLastError();
 }
 

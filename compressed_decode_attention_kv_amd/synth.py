@@ -285,12 +285,17 @@ def device_structured(B, H, G, T, d, seed=6, rank=16, decay=0.7, noise=0.01, n_c
     for b in range(B):
         K[b] = draw(mk, Wk, T).half()
         V[b] = draw(mv, Wv, T).half()
-    ni = G // 2
+    # Half the queries in the key span (norm matched): the first G/2 of each
+    # head, or with one query per head those of the even heads.
     Q = torch.randn((B, H, G, d), generator=g, device=device, dtype=f32)
-    if ni:
-        c = torch.randn((B, H, ni, rank), generator=g, device=device, dtype=f32) * math.sqrt(d / rank)
-        Q[:, :, :ni] = torch.matmul(c, Wk.unsqueeze(0))
-    Q = Q.reshape(B, H * G, d).half()
+    c = torch.randn((B, H, G, rank), generator=g, device=device, dtype=f32) * math.sqrt(d / rank)
+    inspan = torch.matmul(c, Wk.unsqueeze(0))
+    sel = torch.zeros((H, G), dtype=torch.bool, device=device)
+    if G >= 2:
+        sel[:, :G // 2] = True
+    else:
+        sel[0::2, 0] = True
+    Q = torch.where(sel[None, :, :, None], inspan, Q).reshape(B, H * G, d).half()
     CK = draw(mk, Wk, n_calib).cpu().numpy().astype(np.float32)
     CV = draw(mv, Wv, n_calib).cpu().numpy().astype(np.float32)
     return K, V, Q, CK, CV

@@ -160,9 +160,10 @@ typedef struct tq_packed {
   float* side_scale;
   const float* basis; /* HEADQ: U, device [H][d][side_rank];
                          SPECTRAL: V, device [H][d][d], V[h][k][i] = entry k of
-                         eigenvector i (caller-owned, set before tq_quantize) */
-  const float* mean;  /* SPECTRAL: mu, device [H][d]                       */
-  const float* scale; /* SPECTRAL: s, device [H][d] (s_i >= 0)             */
+                         eigenvector i, 16-byte aligned (caller-owned, set
+                         before tq_quantize) */
+  const float* mean;  /* SPECTRAL: mu, device [H][d], 4-byte aligned       */
+  const float* scale; /* SPECTRAL: s, device [H][d] (s_i >= 0), 4-byte aligned */
 } tq_packed;
 
 /* Quality measures ([P1] "Métricas de Evaluación" and "Significado y

@@ -98,7 +98,7 @@ def test_layouts(tqlib):
     dict(ovr=(3, 2), which=1, give_hq=True), dict(ovr=(3, 3), give_hq=True), dict(ovr=(3, 2), no_hq=True),
     dict(ovr=(2, 2), no_gamma=True),
     # SPECTRAL: state missing, misaligned, too wide, with a HeadQ basis, bad bits
-    dict(scheme="squ-kv"), dict(scheme="squ-kv", spec_align=2), dict(scheme="squ-kv", d=256, give_spec=True),
+    dict(scheme="squ-kv"), dict(scheme="squ-kv", spec_align=2), dict(scheme="squ-kv", basis_align=4), dict(scheme="squ-kv", d=256, give_spec=True),
     dict(scheme="squ-kv", give_spec=True, give_hq=True), dict(ovr=(4, 5), give_spec=True),
     dict(ovr=(4, 0), give_spec=True), dict(ovr=(4, 2), which=1),
 ])
@@ -117,8 +117,8 @@ def test_quantize_rejects_before_any_gpu_call(tqlib, bad):
     out.gamma = None if bad.get("no_gamma") else fake
     out.side = fake
     out.side_scale = fake
-    if bad.get("give_spec") or "spec_align" in bad:
-        out.basis = fake
+    if bad.get("give_spec") or "spec_align" in bad or "basis_align" in bad:
+        out.basis = fake + bad.get("basis_align", 0)
         out.mean = fake + bad.get("spec_align", 0)
         out.scale = fake
     hq = None
