@@ -25,9 +25,14 @@ Parity status of each part (what pins it is listed in the tests):
   SpectralQuant with uniform allocation (spectral.py): pinned (Gaussian
       codebook against Max's table, calibration, hand-worked case,
       equivariance, distortion, the pages' orderings).
+  A^2-weighted value policy (value_policy.py): pinned (weights in closed
+      form for equal and dominant keys and their bounds, the selection by
+      brute force, uniform chosen for equal weights by the convexity of the
+      distortion in the bit width, the expected surrogate by Monte Carlo,
+      the pages' ordering against uniform values at 2 bits).
   HeadQ side quantiser Q_q: parity unpinned (the pages give no form; the
       per-token symmetric absmax 4-bit reading is our own).
   RNG streams for the sign vector and the Gaussian sketch: a reading (the
       pages fix only the distributions, which are pinned statistically).
 """
-from . import codebook, rng, rotation, quantizer, attention, metrics, headq, schemes, spectral  # noqa: F401
+from . import codebook, rng, rotation, quantizer, attention, metrics, headq, schemes, spectral, value_policy  # noqa: F401
