@@ -182,6 +182,74 @@ def _quality(tq, q, k, v, kp, vp):
     return out
 
 
+def _exact_attention(torch, Q, K, V, G):
+    """Reference attention over the raw tensors in float32 (a quality
+    reference outside the timed region): out [B, Hq, d]."""
+    B, Hkv, T, d = K.shape
+    out = torch.empty((B, Hkv * G, d), dtype=torch.float32, device=K.device)
+    for b in range(B):
+        q = Q[b].float().reshape(Hkv, G, d)
+        kt = K[b].float().transpose(1, 2).contiguous()
+        p = torch.softmax(torch.matmul(q, kt) / math.sqrt(d), dim=-1)
+        out[b] = torch.matmul(p, V[b].float().contiguous()).reshape(Hkv * G, d)
+    return out
+
+
+def _a2_policy_rows(torch, tq, args, K, V, Q, C, basis, B, Hkv, G, T, d, packed_bytes):
+    """HeadQ keys with 2-bit values: uniform widths against the A^2-weighted
+    two-tier policy at the same 2-bit mean ([P3] section 5).  Output error
+    against exact float32 attention; the plan's surrogate for both."""
+    import numpy as np
+    Np = 8
+    probes = torch.from_numpy(np.ascontiguousarray(
+        np.broadcast_to(C[:, :G * Np].reshape(1, Hkv * G, Np, d), (B, Hkv * G, Np, d)))).cuda().half()
+    o_ref = _exact_attention(torch, Q, K, V, G)
+
+    def out_err(o):
+        e2 = float(torch.sum((o - o_ref) ** 2))
+        s2 = float(torch.sum(o_ref ** 2))
+        cos = torch.sum(o * o_ref, dim=-1) / (torch.linalg.norm(o, dim=-1) * torch.linalg.norm(o_ref, dim=-1))
+        return {"snr_out_db": round(10 * math.log10(s2 / e2), 4),
+                "phi_out": float("%.6g" % float(torch.mean(torch.arccos(torch.clamp(cos, -1, 1)))))}
+
+    kp = tq.quantize(K, tq.KEYS, "headq", 2, 13, basis=basis)
+    vp = tq.quantize(V, tq.VALUES, "headq", 2, 13)
+    u_q_ms = _median_ms(torch, lambda: (tq.quantize(K, tq.KEYS, "headq", 2, 13, basis=basis),
+                                        tq.quantize(V, tq.VALUES, "headq", 2, 13)), args.steps, args.warmup)
+    out, lse = tq.decode_attention(Q, kp, vp)
+    ws = torch.empty(tq.decode_workspace_size(kp, vp, Q.shape[1]), dtype=torch.uint8, device="cuda")
+    u_d_ms = _median_ms(torch, lambda: tq.decode_attention(Q, kp, vp, out, lse, ws), args.steps, args.warmup)
+    uniform = {"values": "uniform 2-bit TQ-MSE", "quantize_ms": round(u_q_ms, 4), "decode_ms": round(u_d_ms, 4),
+               "packed_bytes": packed_bytes(kp) + packed_bytes(vp),
+               "quality": dict(_quality(tq, Q, K, V, kp, vp), **out_err(out))}
+    del kp, vp
+
+    def policy_row(pr, label):
+        cache = [None]
+
+        def build():
+            cache[0] = tq.TwoTierCache(pr, K, V, "headq", 2, seed=13, basis=basis)
+        p_q_ms = _median_ms(torch, build, max(2, args.steps // 4), 1)
+        c = cache[0]
+        p_d_ms = _median_ms(torch, lambda: c.decode(Q), args.steps, args.warmup)
+        o_pol, _ = c.decode(Q)
+        plan = c.plan
+        return {"probes": label,
+                "values": "A^2 two-tier: %d tokens/head at %d bits, %d at %d bits" % (
+                    plan["n_high"], plan["b_hi"], T - plan["n_high"], plan["b_lo"]),
+                "quantize_ms": round(p_q_ms, 4), "decode_ms": round(p_d_ms, 4),
+                "packed_bytes": sum(packed_bytes(kp) + packed_bytes(vp) for kp, vp in c.tiers),
+                "quality": out_err(o_pol),
+                "surrogate": {"%d/%d bits, %d high" % cand: float("%.6g" % sv)
+                              for cand, sv in zip(plan["candidates"], plan["surrogate"])}}
+    # Probes that do not know the step's queries (calibration queries at
+    # random positions), and probes that do (the step's own queries, as when
+    # the queries of the last window are known at write time).
+    pol = [policy_row(probes, "8 calibration queries per query head"),
+           policy_row(Q.reshape(B, Hkv * G, 1, d).contiguous(), "the step's own queries")]
+    return {"scheme": "headq + A^2 value policy", "n_bits": 2, "uniform": uniform, "policy": pol}
+
+
 def other_workload(args):
     """The pages' other regimes at full size (not the headline): one JSON
     line with the median quantize / decode time and the quality measures per
@@ -292,8 +360,10 @@ def other_workload(args):
                          "decode_GBps": round(nb / (d_ms * 1e-3) / 1e9, 1),
                          "decode_pct_hbm_peak": round(100.0 * nb / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                          "quality": _quality(tq, Q, K, V, kp, vp)})
+        rows.append(_a2_policy_rows(torch, tq, args, K, V, Q, C, basis, B, Hkv, G, T, d, packed_bytes))
         cfg = "headq-gqa: B=8, 8 KV heads x 4 query heads, T=131072, d=128, fp16 post-RoPE keys; rank-16 basis " \
-              "fitted from 4096 calibration queries per KV head"
+              "fitted from 4096 calibration queries per KV head; the A^2 value policy at a 2-bit value budget " \
+              "takes 8 of those calibration queries per query head as its probes"
     print(json.dumps({"workload": args.workload, "config": cfg, "data": "synthetic", "n_gpus": 1,
                       "steps": args.steps, "warmup": args.warmup, "dtype": ARITH, "results": rows}))
 

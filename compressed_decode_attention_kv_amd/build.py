@@ -15,7 +15,7 @@ SRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["api.cpp", "host_math.cpp", "quant.hip", "decode.hip", "decode_lut.hip", "quant_mfma.hip", "diag.hip",
-           "noalloc.hip", "quant_sketch.hip", "quant_spectral.hip"]
+           "noalloc.hip", "quant_sketch.hip", "quant_spectral.hip", "policy.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # Keep the compiler from emitting packed-FP32 VALU instructions.
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -992,6 +992,166 @@ tq_status tq_headq_fit(const float* calib, int32_t N, int32_t d, int32_t rank, f
   return ok();
 }
 
+// ---- A^2-weighted value policy --------------------------------------------------
+namespace {
+
+tq_status check_a2(const tq_tensor_desc* q, const tq_tensor_desc* k, int* P) {
+  if (tq_status s = check_tensor(q, "q_probe")) return s;
+  if (tq_status s = check_tensor(k, "k_ref")) return s;
+  if (q->B != k->B || q->d != k->d) return fail(TQ_EMISMATCH, "probe B/d (%d, %d) differ from the keys (%d, %d)", q->B, q->d, k->B, k->d);
+  if (q->H % k->H) return fail(TQ_EMISMATCH, "probe heads %d not a multiple of KV heads %d", q->H, k->H);
+  *P = (q->H / k->H) * q->T;
+  if ((long)*P * q->d > 16384) return fail(TQ_EUNSUPPORTED, "%d probes per KV head at d=%d exceed 16384 / d", *P, q->d);
+  return TQ_OK;
+}
+
+size_t a2_bytes(const tq_tensor_desc* q, const tq_tensor_desc* k) {
+  return a2_workspace_bytes(q->B * q->H * q->T, k->T);
+}
+
+// Workspace of the policy: gains [BH][T], selections [BH][3], totals [BH].
+struct PolicyLayout { size_t off_gain, off_sel, off_total, bytes; };
+PolicyLayout policy_layout(const tq_tensor_desc* v) {
+  PolicyLayout l;
+  const size_t BH = (size_t)v->B * v->H;
+  size_t off = 0;
+  l.off_gain = off;  off = round_up(off + BH * v->T * 4, 256);
+  l.off_sel = off;   off = round_up(off + BH * 3 * sizeof(PolicySel), 256);
+  l.off_total = off; off = round_up(off + BH * 8, 256);
+  l.bytes = off;
+  return l;
+}
+
+}  // namespace
+
+tq_status tq_a2_workspace_size(const tq_tensor_desc* q_probe, const tq_tensor_desc* k_ref, size_t* bytes) {
+  if (!bytes) return fail(TQ_EINVAL, "output pointer is NULL");
+  int P;
+  if (tq_status s = check_a2(q_probe, k_ref, &P)) return s;
+  *bytes = a2_bytes(q_probe, k_ref);
+  return ok();
+}
+
+tq_status tq_a2_weights(const tq_tensor_desc* q_probe, const tq_tensor_desc* k_ref, float* weights, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int P;
+  if (tq_status s = check_a2(q_probe, k_ref, &P)) return s;
+  if (!weights || !aligned(weights, 4)) return fail(TQ_EINVAL, "weights NULL or not 4-byte aligned");
+  const size_t need = a2_bytes(q_probe, k_ref);
+  if (!ws || !aligned(ws, 256)) return fail(TQ_EINVAL, "workspace NULL or not 256-byte aligned");
+  if (ws_bytes < need) return fail(TQ_ENOMEM, "workspace %zu bytes < required %zu", ws_bytes, need);
+  A2Params p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q_probe->data; p.qdtype = q_probe->dtype;
+  p.qsb = q_probe->stride_b; p.qsh = q_probe->stride_h; p.qst = q_probe->stride_t;
+  p.k = k_ref->data; p.kdtype = k_ref->dtype;
+  p.ksb = k_ref->stride_b; p.ksh = k_ref->stride_h; p.kst = k_ref->stride_t;
+  p.B = k_ref->B; p.Hq = q_probe->H; p.Hkv = k_ref->H; p.G = q_probe->H / k_ref->H; p.Np = q_probe->T;
+  p.P = P; p.T = k_ref->T; p.d = k_ref->d;
+  p.chunk = 8 * 4 * (64 / (k_ref->d / 32));   // 8 steps of the block's 4 waves
+  p.inv_sqrt_d = 1.0f / std::sqrt((float)k_ref->d);
+  char* w = static_cast<char*>(ws);
+  const size_t rows = (size_t)p.B * p.Hq * p.Np;
+  p.scores = reinterpret_cast<float*>(w);
+  p.lse = reinterpret_cast<double*>(w + round_up(rows * p.T * 4, 256));
+  p.weights = weights;
+  return hip_status(launch_a2_weights(p, (hipStream_t)stream), "A^2 weight launch");
+}
+
+tq_status tq_value_policy_workspace_size(const tq_tensor_desc* v_ref, size_t* bytes) {
+  if (!bytes) return fail(TQ_EINVAL, "output pointer is NULL");
+  if (tq_status s = check_tensor(v_ref, "v_ref")) return s;
+  *bytes = policy_layout(v_ref).bytes;
+  return ok();
+}
+
+tq_status tq_value_policy(const float* weights, const tq_tensor_desc* v_ref, int32_t budget_bits, int32_t* perm,
+                          tq_value_plan* plan, void* ws, size_t ws_bytes, void* stream) {
+  if (tq_status s = check_tensor(v_ref, "v_ref")) return s;
+  if (!weights || !aligned(weights, 4) || !perm || !aligned(perm, 4) || !plan)
+    return fail(TQ_EINVAL, "weights, perm or plan NULL or misaligned");
+  if (budget_bits < 1 || budget_bits > kMaxIndexBits) return fail(TQ_EINVAL, "budget_bits=%d outside [1, %d]", budget_bits, kMaxIndexBits);
+  const PolicyLayout lay = policy_layout(v_ref);
+  if (!ws || !aligned(ws, 256)) return fail(TQ_EINVAL, "workspace NULL or not 256-byte aligned");
+  if (ws_bytes < lay.bytes) return fail(TQ_ENOMEM, "workspace %zu bytes < required %zu", ws_bytes, lay.bytes);
+  // Candidates: uniform, (b-1, b+1) with half high, (b-1, b+2) with a third high.
+  tq_value_plan pl;
+  std::memset(&pl, 0, sizeof(pl));
+  const int T = v_ref->T;
+  auto add = [&](int lo, int hi, int num, int den) {
+    if (lo < 1 || hi > kMaxIndexBits) return;
+    const int c = pl.n_candidates++;
+    pl.cand_lo[c] = lo; pl.cand_hi[c] = hi; pl.cand_high[c] = (int)(((long)T * num) / den);
+  };
+  add(budget_bits, budget_bits, 0, 1);
+  add(budget_bits - 1, budget_bits + 1, 1, 2);
+  add(budget_bits - 1, budget_bits + 2, 1, 3);
+  char* w = static_cast<char*>(ws);
+  hipStream_t st = (hipStream_t)stream;
+  PolicyParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.v = v_ref->data; p.vdtype = v_ref->dtype;
+  p.vsb = v_ref->stride_b; p.vsh = v_ref->stride_h; p.vst = v_ref->stride_t;
+  p.B = v_ref->B; p.H = v_ref->H; p.T = T; p.d = v_ref->d;
+  p.weights = weights;
+  p.gain = reinterpret_cast<float*>(w + lay.off_gain);
+  p.sel = reinterpret_cast<PolicySel*>(w + lay.off_sel);
+  p.total = reinterpret_cast<double*>(w + lay.off_total);
+  p.perm = perm;
+  p.ncand = pl.n_candidates;
+  for (int c = 0; c < pl.n_candidates; ++c) p.cand_R[c] = pl.cand_high[c];
+  if (tq_status s = hip_status(launch_policy_select(p, st), "policy selection launch")) return s;
+  const size_t BH = (size_t)p.B * p.H;
+  std::vector<PolicySel> sel(BH * p.ncand);
+  std::vector<double> total(BH);
+  if (tq_status s = hip_status(hipMemcpyAsync(sel.data(), p.sel, sel.size() * sizeof(PolicySel), hipMemcpyDeviceToHost, st), "copy")) return s;
+  if (tq_status s = hip_status(hipMemcpyAsync(total.data(), p.total, BH * 8, hipMemcpyDeviceToHost, st), "copy")) return s;
+  if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
+  int best = 0;
+  for (int c = 0; c < pl.n_candidates; ++c) {
+    const double Dl = codebook_distortion(v_ref->d, pl.cand_lo[c]), Dh = codebook_distortion(v_ref->d, pl.cand_hi[c]);
+    double sur = 0.0;
+    for (size_t bh = 0; bh < BH; ++bh) {
+      const double top = sel[bh * p.ncand + c].top;
+      sur += Dl * (total[bh] - top) + Dh * top;
+    }
+    pl.surrogate[c] = sur;
+    if (sur < pl.surrogate[best]) best = c;
+  }
+  pl.b_lo = pl.cand_lo[best]; pl.b_hi = pl.cand_hi[best]; pl.n_high = pl.cand_high[best];
+  p.chosen = best;
+  if (tq_status s = hip_status(launch_policy_permute(p, st), "permutation launch")) return s;
+  if (tq_status s = hip_status(hipStreamSynchronize(st), "sync")) return s;
+  *plan = pl;
+  return ok();
+}
+
+tq_status tq_gather_tokens(const tq_tensor_desc* x, const int32_t* perm, int32_t t0, const tq_tensor_desc* out,
+                           void* stream) {
+  if (tq_status s = check_tensor(x, "x")) return s;
+  if (tq_status s = check_tensor(out, "out")) return s;
+  if (!perm || !aligned(perm, 4)) return fail(TQ_EINVAL, "perm NULL or not 4-byte aligned");
+  if (x->B != out->B || x->H != out->H || x->d != out->d || x->dtype != out->dtype)
+    return fail(TQ_EMISMATCH, "out differs from x in B, H, d or dtype");
+  if (t0 < 0 || (long)t0 + out->T > x->T) return fail(TQ_EINVAL, "tokens [%d, %d) outside [0, %d)", t0, t0 + out->T, x->T);
+  GatherParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = x->data; p.out = const_cast<void*>(out->data); p.es = elem_size(x->dtype);
+  p.xsb = x->stride_b; p.xsh = x->stride_h; p.xst = x->stride_t;
+  p.osb = out->stride_b; p.osh = out->stride_h; p.ost = out->stride_t;
+  p.B = x->B; p.H = x->H; p.T = x->T; p.t0 = t0; p.tn = out->T; p.row_bytes = x->d * p.es;
+  p.perm = perm;
+  return hip_status(launch_gather(p, (hipStream_t)stream), "gather launch");
+}
+
+tq_status tq_attention_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b,
+                             int32_t n, int32_t d, float* out, float* lse, void* stream) {
+  if (!out_a || !lse_a || !out_b || !lse_b || !out) return fail(TQ_EINVAL, "NULL pointer");
+  if (n < 1 || d < 1) return fail(TQ_EINVAL, "n=%d d=%d", n, d);
+  MergeParams p{out_a, lse_a, out_b, lse_b, n, d, out, lse};
+  return hip_status(launch_merge(p, (hipStream_t)stream), "merge launch");
+}
+
 tq_status tq_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
   if (!src || !sink) return fail(TQ_EINVAL, "NULL pointer");
   if (!aligned(src, 16) || !aligned(sink, 4)) return fail(TQ_EINVAL, "src must be 16-byte aligned, sink 4-byte aligned");

@@ -136,6 +136,23 @@ bool codebook(int d, int bits, std::vector<double>* centroids, std::vector<doubl
   return true;
 }
 
+// Relative MSE d * E[(T - c[idx(T)])^2] of the b-bit Beta Lloyd-Max code of
+// one coordinate T of a uniform unit vector in R^d: at the fixed point every
+// centroid is its cell's conditional mean, so the per-coordinate distortion is
+// E[T^2] - sum_k P_k c_k^2 with E[T^2] = 1/d.
+double codebook_distortion(int d, int bits) {
+  std::vector<double> c, t;
+  if (!codebook(d, bits, &c, &t)) return NAN;
+  const double a = 0.5 * (d - 1);
+  const int K = (int)c.size();
+  double s = 0.0;
+  for (int k = 0; k < K; ++k) {
+    const double lo = k == 0 ? -1.0 : t[k - 1], hi = k == K - 1 ? 1.0 : t[k];
+    s += cell_mass(lo, hi, a) * c[k] * c[k];
+  }
+  return d * (1.0 / d - s);
+}
+
 // Sign vector of the randomised Walsh-Hadamard rotation ([P2]
 // "Configuração Experimental"): D_i = -1 iff bit 63 of the i-th output of
 // the SplitMix64 stream started at seed ^ kTagSign is set.

@@ -29,6 +29,8 @@ bool pca_basis(const float* X, int N, int d, int rank, float* U, float* eigenval
                float* mean = nullptr);
 // Lloyd-Max codebook of N(0, 1) in double, cached per bits.
 bool gaussian_codebook(int bits, std::vector<double>* centroids, std::vector<double>* boundaries);
+// Relative MSE of the b-bit Beta Lloyd-Max code (TQ-MSE) at head dim d.
+double codebook_distortion(int d, int bits);
 
 // ---- kernel parameter blocks ----------------------------------------------
 struct QuantParams {
@@ -202,6 +204,49 @@ hipError_t launch_attn_ref(const AttnRefParams& p, hipStream_t s);
 hipError_t launch_relerr(const RelErrParams& p, int nblocks, hipStream_t s);
 // The static decode workspace (noalloc.hip): its size, and this device's
 // address of it (hipGetSymbolAddress, taken once per device).
+// ---- A^2-weighted value policy (policy.hip) -----------------------------------
+struct A2Params {
+  const void* q; int qdtype; int64_t qsb, qsh, qst;   // probes [B][Hq][Np][d]
+  const void* k; int kdtype; int64_t ksb, ksh, kst;   // raw keys [B][Hkv][T][d]
+  int B, Hq, Hkv, G, Np, P, T, d, chunk;              // P = G * Np probes per KV head
+  float inv_sqrt_d;
+  float* scores;        // [B*Hq*Np][T]
+  double* lse;          // [B*Hq*Np]
+  float* weights;       // [B*Hkv][T]
+};
+struct PolicySel {
+  uint32_t thr;         // bit pattern of the R-th largest gain
+  int need_eq;          // how many tokens equal to it are taken (lowest indices)
+  double top;           // sum of the R largest gains
+};
+struct PolicyParams {
+  const void* v; int vdtype; int64_t vsb, vsh, vst;   // raw values [B][H][T][d]
+  int B, H, T, d;
+  const float* weights; float* gain;                  // [B*H][T]
+  int ncand, chosen;
+  int cand_R[4];
+  PolicySel* sel;       // [B*H][ncand]
+  double* total;        // [B*H]
+  int32_t* perm;        // [B*H][T]
+};
+struct GatherParams {
+  const void* x; void* out; int es;
+  int64_t xsb, xsh, xst, osb, osh, ost;
+  int B, H, T, t0, tn, row_bytes;
+  const int32_t* perm;
+};
+struct MergeParams {
+  const float* out_a; const float* lse_a; const float* out_b; const float* lse_b;
+  int n, d;
+  float* out; float* lse;
+};
+size_t a2_workspace_bytes(int rows, int T);
+hipError_t launch_a2_weights(const A2Params& p, hipStream_t s);
+hipError_t launch_policy_select(const PolicyParams& p, hipStream_t s);
+hipError_t launch_policy_permute(const PolicyParams& p, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+
 size_t static_scratch_bytes();
 hipError_t static_scratch(void** out);
 int stream_read_blocks();

@@ -29,6 +29,8 @@ EXPORTS = ["tq_abi_version", "tq_status_str", "tq_last_error", "tq_codebook_buil
            "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_attention_lens",
            "tq_decode_attention_static",
            "tq_metrics_workspace_size", "tq_metrics", "tq_spectral_fit", "tq_headq_fit",
+           "tq_a2_workspace_size", "tq_a2_weights", "tq_value_policy_workspace_size", "tq_value_policy",
+           "tq_gather_tokens", "tq_attention_merge",
            "tq_stream_read", "tq_release_cache"]
 
 
@@ -71,6 +73,12 @@ class MetricsOut(ctypes.Structure):
                 ("a2_value_mean", ctypes.c_double)]
 
 
+class ValuePlan(ctypes.Structure):
+    _fields_ = [("b_lo", ctypes.c_int32), ("b_hi", ctypes.c_int32), ("n_high", ctypes.c_int32),
+                ("n_candidates", ctypes.c_int32), ("cand_lo", ctypes.c_int32 * 3), ("cand_hi", ctypes.c_int32 * 3),
+                ("cand_high", ctypes.c_int32 * 3), ("surrogate", ctypes.c_double * 3)]
+
+
 _P = ctypes.POINTER
 _sigs = {
     "tq_abi_version": ([], ctypes.c_int32),
@@ -95,6 +103,18 @@ _sigs = {
     "tq_metrics": ([_P(TensorDesc), _P(TensorDesc), _P(TensorDesc), _P(Packed), _P(Packed), _P(MetricsOut),
                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "tq_headq_fit": ([_P(ctypes.c_float), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P(ctypes.c_float)], ctypes.c_int),
+    "tq_spectral_fit": ([_P(ctypes.c_float), ctypes.c_int32, ctypes.c_int32, _P(ctypes.c_float), _P(ctypes.c_float),
+                         _P(ctypes.c_float)], ctypes.c_int),
+    "tq_a2_workspace_size": ([_P(TensorDesc), _P(TensorDesc), _P(ctypes.c_size_t)], ctypes.c_int),
+    "tq_a2_weights": ([_P(TensorDesc), _P(TensorDesc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                       ctypes.c_void_p], ctypes.c_int),
+    "tq_value_policy_workspace_size": ([_P(TensorDesc), _P(ctypes.c_size_t)], ctypes.c_int),
+    "tq_value_policy": ([ctypes.c_void_p, _P(TensorDesc), ctypes.c_int32, ctypes.c_void_p, _P(ValuePlan),
+                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "tq_gather_tokens": ([_P(TensorDesc), ctypes.c_void_p, ctypes.c_int32, _P(TensorDesc), ctypes.c_void_p],
+                         ctypes.c_int),
+    "tq_attention_merge": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "tq_stream_read": ([ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "tq_release_cache": ([], ctypes.c_int),
 }
@@ -439,3 +459,93 @@ def stream_read(buf, sink):
 
 def release_cache():
     _check(_lib.tq_release_cache())
+
+
+# ---- A^2-weighted value policy ------------------------------------------------------
+def a2_weights(q_probe, k):
+    """A [B, H, T] fp32: per token, the mean over the probe queries of its KV
+    head of the squared attention probability.  q_probe [B, Hq, Np, d], k
+    [B, H, T, d] (device)."""
+    torch = _torch()
+    dq, q4 = tensor_desc(q_probe)
+    dk, k4 = tensor_desc(k)
+    n = ctypes.c_size_t()
+    _check(_lib.tq_a2_workspace_size(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=k.device)
+    w = torch.empty((dk.B, dk.H, dk.T), dtype=torch.float32, device=k.device)
+    _check(_lib.tq_a2_weights(ctypes.byref(dq), ctypes.byref(dk), w.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    return w
+
+
+def value_policy(weights, v, budget_bits):
+    """(perm [B, H, T] int32, plan dict) of the two-tier value policy."""
+    torch = _torch()
+    dv, v4 = tensor_desc(v)
+    if weights.dtype != torch.float32 or tuple(weights.shape) != (dv.B, dv.H, dv.T) or not weights.is_contiguous():
+        raise ValueError("weights must be contiguous float32 [B, H, T]")
+    n = ctypes.c_size_t()
+    _check(_lib.tq_value_policy_workspace_size(ctypes.byref(dv), ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=v.device)
+    perm = torch.empty((dv.B, dv.H, dv.T), dtype=torch.int32, device=v.device)
+    plan = ValuePlan()
+    _check(_lib.tq_value_policy(weights.data_ptr(), ctypes.byref(dv), budget_bits, perm.data_ptr(),
+                                ctypes.byref(plan), ws.data_ptr(), ws.numel(), _stream()))
+    k = plan.n_candidates
+    return perm, {"b_lo": plan.b_lo, "b_hi": plan.b_hi, "n_high": plan.n_high,
+                  "candidates": [(plan.cand_lo[i], plan.cand_hi[i], plan.cand_high[i]) for i in range(k)],
+                  "surrogate": [plan.surrogate[i] for i in range(k)]}
+
+
+def gather_tokens(x, perm, t0, tn):
+    """x[b, h, perm[b, h, t0 + t]] for t < tn, as a new [B, H, tn, d] tensor."""
+    torch = _torch()
+    dx, x4 = tensor_desc(x)
+    if perm.dtype != torch.int32 or tuple(perm.shape) != (dx.B, dx.H, dx.T) or not perm.is_contiguous():
+        raise ValueError("perm must be contiguous int32 [B, H, T]")
+    out = torch.empty((dx.B, dx.H, tn, dx.d), dtype=x.dtype, device=x.device)
+    do, _ = tensor_desc(out)
+    _check(_lib.tq_gather_tokens(ctypes.byref(dx), perm.data_ptr(), t0, ctypes.byref(do), _stream()))
+    return out
+
+
+def attention_merge(out_a, lse_a, out_b, lse_b):
+    """Attention over the union of two disjoint token sets."""
+    torch = _torch()
+    for t in (out_a, lse_a, out_b, lse_b):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("merge operands must be contiguous float32")
+    d = out_a.shape[-1]
+    n = out_a.numel() // d
+    out = torch.empty_like(out_a)
+    lse = torch.empty_like(lse_a)
+    _check(_lib.tq_attention_merge(out_a.data_ptr(), lse_a.data_ptr(), out_b.data_ptr(), lse_b.data_ptr(), n, d,
+                                   out.data_ptr(), lse.data_ptr(), _stream()))
+    return out, lse
+
+
+class TwoTierCache:
+    """A packed cache under the A^2-weighted value policy: the tokens of each
+    (batch, head) permuted (high tier first), keys quantised with their own
+    scheme over both tiers, values at the plan's two widths (TQ-MSE)."""
+
+    def __init__(self, q_probe, K, V, key_scheme, budget_bits, seed=0, key_bits=None, basis=None, side_bits=4):
+        self.weights = a2_weights(q_probe, K)
+        self.perm, self.plan = value_policy(self.weights, V, budget_bits)
+        T = K.shape[2]
+        R = self.plan["n_high"]
+        kb = budget_bits if key_bits is None else key_bits
+        self.tiers = []
+        for t0, tn, vbits in ((0, R, self.plan["b_hi"]), (R, T - R, self.plan["b_lo"])):
+            if tn == 0:
+                continue
+            Kt = gather_tokens(K, self.perm, t0, tn)
+            Vt = gather_tokens(V, self.perm, t0, tn)
+            kp = quantize(Kt, KEYS, key_scheme, kb, seed, basis=basis, side_bits=side_bits)
+            vp = quantize(Vt, VALUES, key_scheme, kb, seed, mode=MODE_MSE, bits=vbits)
+            self.tiers.append((kp, vp))
+
+    def decode(self, q):
+        outs = [decode_attention(q, kp, vp) for kp, vp in self.tiers]
+        if len(outs) == 1:
+            return outs[0]
+        return attention_merge(outs[0][0], outs[0][1], outs[1][0], outs[1][1])

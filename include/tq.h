@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 5
+#define TQ_ABI_VERSION 6
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -326,6 +326,69 @@ tq_status tq_spectral_fit(const float* calib, int32_t N, int32_t d, float* basis
  * [d][rank], columns = eigenvectors of the largest eigenvalues, each with
  * its largest-magnitude entry positive.  Host only, synchronous. */
 tq_status tq_headq_fit(const float* calib, int32_t N, int32_t d, int32_t rank, float* U);
+
+/* ---- A^2-weighted value policy ([P3] section 2.2: values are read by
+ * o = sum_j p_j v_j, and sum_j p_j^2 ||dv_j||^2 is the value error that
+ * matters; section 5: HeadQ keys with a value policy weighted by it at 2
+ * bits).  The policy splits each (batch, head)'s tokens into a high and a
+ * low value tier at a fixed mean number of index bits; attention does not
+ * depend on the order of the (key, value) pairs, so each tier is an
+ * ordinary packed cache over a permutation of the tokens, and the two
+ * tiers' attention outputs combine with tq_attention_merge. */
+
+/* Workspace bytes of tq_a2_weights. */
+tq_status tq_a2_workspace_size(const tq_tensor_desc* q_probe, const tq_tensor_desc* k_ref, size_t* bytes);
+
+/* A_j = mean over the probe queries of KV head h of p_j(q)^2, p(q) the
+ * softmax of q^T k_j / sqrt(d) over the T raw keys of the sequence.
+ * q_probe: device [B][Hq][Np][d] (Np probes per query head, the tensor's T
+ * dimension), Hq a multiple of k_ref->H; the probes of KV head h are those of
+ * its Hq / H query heads, at most 16384 / d of them.  k_ref: device
+ * [B][H][T][d].  weights: device fp32 [B][H][T].  ws: 256-byte aligned,
+ * tq_a2_workspace_size bytes.  Stream-ordered. */
+tq_status tq_a2_weights(const tq_tensor_desc* q_probe, const tq_tensor_desc* k_ref, float* weights, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Candidates and choice of tq_value_policy. */
+typedef struct tq_value_plan {
+  int32_t b_lo, b_hi;      /* index bits of the low and high value tiers (equal: uniform) */
+  int32_t n_high;          /* tokens per (batch, head) in the high tier                   */
+  int32_t n_candidates;
+  int32_t cand_lo[3], cand_hi[3], cand_high[3];
+  double surrogate[3];     /* sum_j A_j ||v_j||^2 D_{b_j} of each candidate                */
+} tq_value_plan;
+
+/* Workspace bytes of tq_value_policy. */
+tq_status tq_value_policy_workspace_size(const tq_tensor_desc* v_ref, size_t* bytes);
+
+/* The two-tier value plan at a mean of budget_bits index bits per value
+ * coordinate (budget_bits in [1, 4]).  Candidates, in this order: uniform
+ * budget_bits; (budget_bits - 1, budget_bits + 1) with floor(T/2) tokens high;
+ * (budget_bits - 1, budget_bits + 2) with floor(T/3) high (widths in [1, 4]).
+ * In each, the high tokens of a (batch, head) are those with the largest
+ * w_j = A_j ||v_j||^2 (ties to the lower index).  The candidate with the
+ * smallest surrogate sum_j w_j D_{b_j} over the whole tensor is chosen (ties
+ * to the earlier one), D_b = the relative MSE of the b-bit TQ-MSE code.
+ * weights: device fp32 [B][H][T] (tq_a2_weights); v_ref: device [B][H][T][d]
+ * raw values.  perm: device int32 [B][H][T], the chosen high tier first,
+ * each tier in increasing token order.  *plan (host) receives the choice
+ * and the candidates.  Synchronises `stream`. */
+tq_status tq_value_policy(const float* weights, const tq_tensor_desc* v_ref, int32_t budget_bits, int32_t* perm,
+                          tq_value_plan* plan, void* ws, size_t ws_bytes, void* stream);
+
+/* out[b][h][t] = x[b][h][perm[b][h][t0 + t]] for t in [0, out->T): the
+ * tokens of one tier, in order.  x: device [B][H][T][d]; perm: device
+ * int32 [B][H][x->T] (a permutation of [0, x->T) per (b, h)); out: device,
+ * same B, H, d and dtype, out->T <= x->T - t0.  Stream-ordered. */
+tq_status tq_gather_tokens(const tq_tensor_desc* x, const int32_t* perm, int32_t t0, const tq_tensor_desc* out,
+                           void* stream);
+
+/* Attention over the union of two disjoint token sets from the outputs and
+ * log-sum-exps of each (device fp32 out_* [n][d], lse_* [n]): out =
+ * sum_s exp(lse_s - lse) out_s, lse = log(exp(lse_a) + exp(lse_b)); a side
+ * with lse = -inf contributes nothing.  lse may be NULL.  Stream-ordered. */
+tq_status tq_attention_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b,
+                             int32_t n, int32_t d, float* out, float* lse, void* stream);
 
 /* Diagnostic: reads `bytes` (a positive multiple of 16) of device memory at
  * `src` (16-byte aligned) with the non-temporal 128-bit loads the decode

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(tqlib):
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(tqlib.EXPORTS) == names
-    assert tqlib.lib().tq_abi_version() == 5
+    assert tqlib.lib().tq_abi_version() == 6
 
 
 @pytest.mark.parametrize("d,bits", [(32, 1), (128, 2), (128, 3), (128, 4), (1024, 2), (1024, 4)])
@@ -299,3 +299,38 @@ def test_append_and_lengths_reject_before_any_gpu_call(tqlib):
     for lens in (None, fake + 2):
         assert lib.tq_decode_attention_lens(ctypes.byref(q), ctypes.byref(cache), ctypes.byref(v), lens, fake, None,
                                             fake, 1 << 30, None) == tqlib.EINVAL
+
+
+def test_value_policy_rejects_before_any_gpu_call(tqlib):
+    """Host validation of the value-policy entry points (fake pointers)."""
+    lib = tqlib.lib()
+    fake = 1 << 20
+    n = ctypes.c_size_t()
+
+    def desc(B=1, H=2, T=8, d=64, dtype=None):
+        return tqlib.TensorDesc(fake, tqlib.F16 if dtype is None else dtype, B, H, T, d, H * T * d, T * d, d)
+    k = desc()
+    assert lib.tq_a2_workspace_size(ctypes.byref(desc(H=3)), ctypes.byref(k), ctypes.byref(n)) == tqlib.EMISMATCH
+    assert lib.tq_a2_workspace_size(ctypes.byref(desc(B=2, H=4)), ctypes.byref(k), ctypes.byref(n)) == tqlib.EMISMATCH
+    # 2 query heads per KV head x 200 probes x d=64 > 16384
+    assert lib.tq_a2_workspace_size(ctypes.byref(desc(H=4, T=200)), ctypes.byref(k), ctypes.byref(n)) == tqlib.EUNSUPPORTED
+    assert lib.tq_a2_workspace_size(ctypes.byref(desc(H=4, T=3)), ctypes.byref(k), ctypes.byref(n)) == tqlib.OK
+    assert lib.tq_a2_weights(ctypes.byref(desc(H=4, T=3)), ctypes.byref(k), fake, fake, n.value - 1, None) == tqlib.ENOMEM
+    assert lib.tq_a2_weights(ctypes.byref(desc(H=4, T=3)), ctypes.byref(k), None, fake, n.value, None) == tqlib.EINVAL
+    v = desc()
+    assert lib.tq_value_policy_workspace_size(ctypes.byref(v), ctypes.byref(n)) == tqlib.OK
+    plan = tqlib.ValuePlan()
+    for budget in (0, 5):
+        assert lib.tq_value_policy(fake, ctypes.byref(v), budget, fake, ctypes.byref(plan), fake, n.value,
+                                   None) == tqlib.EINVAL
+    assert lib.tq_value_policy(fake, ctypes.byref(v), 2, fake, None, fake, n.value, None) == tqlib.EINVAL
+    assert lib.tq_value_policy(fake, ctypes.byref(v), 2, fake, ctypes.byref(plan), fake, n.value - 256,
+                               None) == tqlib.ENOMEM
+    out = desc(T=4)
+    assert lib.tq_gather_tokens(ctypes.byref(v), fake, 5, ctypes.byref(out), None) == tqlib.EINVAL
+    assert lib.tq_gather_tokens(ctypes.byref(v), fake, -1, ctypes.byref(out), None) == tqlib.EINVAL
+    assert lib.tq_gather_tokens(ctypes.byref(v), fake, 0, ctypes.byref(desc(T=4, d=32)), None) == tqlib.EMISMATCH
+    assert lib.tq_gather_tokens(ctypes.byref(v), fake, 0, ctypes.byref(desc(T=4, dtype=tqlib.F32)), None) == tqlib.EMISMATCH
+    assert lib.tq_attention_merge(fake, fake, None, fake, 4, 64, fake, None, None) == tqlib.EINVAL
+    assert lib.tq_attention_merge(fake, fake, fake, fake, 0, 64, fake, None, None) == tqlib.EINVAL
+
