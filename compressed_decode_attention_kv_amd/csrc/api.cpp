@@ -807,7 +807,7 @@ tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_pack
     int cus = 0;
     if (tq_status s = hip_status(cu_count(&cus), "device query")) return s;
     const int nblocks = std::min(pl.units, std::max(1, cus));
-    if (tq_status s = hip_status(launch_decode_lut(dp, k->bits, kq, v->bits, vq, nblocks, st), "decode launch")) return s;
+    if (tq_status s = hip_status(launch_decode_lut(dp, k->bits, kq, ksd, v->bits, vq, nblocks, st), "decode launch")) return s;
   } else {
     if (tq_status s = hip_status(launch_decode_split(dp, k->bits, kq, ksd, v->bits, vq, st, &supported), "decode launch")) return s;
   }

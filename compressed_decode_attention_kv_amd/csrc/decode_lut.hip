@@ -1,8 +1,8 @@
-// Table-driven split decode for 3- and 4-bit caches at d = 128..1024, the
-// read side of [P1] "Esquemas de Cuantización" (KV, KQV, QKQV at n = 4) and
-// [P2] "Contribuições Principais" 1 (TQ-KV, TQ-QKV), plus HeadQ keys (2-bit
-// base with a rank-16 4-bit side code, [P3] section 3 "Metodologia: HeadQ")
-// over 4-bit values.
+// Table-driven split decode for 2- to 4-bit keys and 1- to 4-bit values at
+// d = 128..1024, the read side of [P1] "Esquemas de Cuantización" (KV, KQV,
+// QKQV at n = 4) and [P2] "Contribuições Principais" 1 (TQ-KV, TQ-QKV at
+// n = 2..4), plus HeadQ keys (2-bit base with a rank-16 4-bit side code, [P3]
+// section 3 "Metodologia: HeadQ") over 1- to 4-bit values.
 //
 // [P1] = "Resumen Técnico: Inferencia Estadística y Medidas de Calidad de
 //        Cuantizaciones de Cache KV Inspiradas en TurboQuant"
@@ -75,13 +75,16 @@ constexpr int kMaxLutWaves = 12;
 //   key pairs          fp32x2            b64   a copy per lane % 32   ((lane & 31) * 8)
 //   sketched keys      fp32x2 + 2 signs  b128  a copy per lane % 16   ((lane & 15) * 16)
 //   key quads          fp32x4            b128  a copy per lane % 16   ((lane & 15) * 16), 2-bit keys
+//   value quads        fp16x4            b64   a copy per lane % 32   ((lane & 31) * 8), 2-bit values
+//   value octets       fp16x8            b128  a copy per lane % 16   ((lane & 15) * 16), 1-bit values
 // A sketched tensor stores per coordinate a 4-bit field, 3-bit code | sign << 3
 // (the sign of the same-index sketch row), so a byte holds two of them.
-// KB == 2 is the HeadQ base (with its side code).
+// KB == 2 is a 2-bit key code: the HeadQ base when the kernel's KS is set
+// (with its side code), plain TQ-MSE otherwise.
 template <int D, int KB, bool KQ, int VB, bool VQ>
 struct LutMap {
   static constexpr bool kKeyByte = KB == 4 || KB == 2 || KQ;
-  static constexpr bool kValByte = VB == 4 || VQ;
+  static constexpr bool kValByte = VB == 4 || VB <= 2 || VQ;
   static constexpr bool kKeySix = KB == 3 && !KQ, kValSix = VB == 3 && !VQ;
   static constexpr uint32_t nbyte_tables = kKeyByte + kValByte;
   static constexpr uint32_t six_base = 0x10000u * nbyte_tables;
@@ -174,7 +177,7 @@ constexpr int lane_dwords() { return Q ? B + 1 : B; }
 template <int KB, bool KQ, int VB, bool VQ>
 struct TokenData {
   uint32_t k[lane_dwords<KB, KQ>()];
-  uint32_t ks;   // the HeadQ side-code dword (KB == 2)
+  uint32_t ks;   // the HeadQ side-code dword (KS)
   uint32_t v[lane_dwords<VB, VQ>()];
   float sc;      // this lane's per-token scalar (lane j: nu_k, gamma_k, nu_v, gamma_v)
 };
@@ -183,7 +186,7 @@ struct TokenData {
 struct HeadPlanes {
   const uint8_t* kc;
   const uint8_t* vc;
-  const uint8_t* ks;  // the HeadQ side codes (KB == 2)
+  const uint8_t* ks;  // the HeadQ side codes (KS)
 };
 
 // A 32-bit lane offset the compiler keeps as is, so that loads take the
@@ -203,7 +206,7 @@ __device__ __forceinline__ uint32_t token_bytes(uint32_t tr) {
 // T_cap <= 2^24 with T_cap * d / 2 < 2^32 here, so tr fits a 24-bit multiply
 // (full rate, unlike a 32-bit one) and every byte offset fits 32 bits.
 // Key words, side codes and the per-token scalar:
-template <int D, int KB, bool KQ, int VB, bool VQ>
+template <int D, bool KS, int KB, bool KQ, int VB, bool VQ>
 __device__ __forceinline__ void load_keys(const HeadPlanes& h, uint32_t tr, int j, const float* sc_head,
                                           TokenData<KB, KQ, VB, VQ>& t) {
   constexpr int KW = lane_dwords<KB, KQ>();
@@ -215,7 +218,8 @@ __device__ __forceinline__ void load_keys(const HeadPlanes& h, uint32_t tr, int 
     u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kc));
     t.k[0] = x.x; t.k[1] = x.y;
     // Side codes: 16 x 4 bits = 8 bytes per token; lane j uses codes 4j..4j+3.
-    t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.ks + lane_off(tr * 8u + (uint32_t)(j >> 1) * 4u)));
+    if constexpr (KS)
+      t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(h.ks + lane_off(tr * 8u + (uint32_t)(j >> 1) * 4u)));
   } else {
 #pragma unroll
     for (int i = 0; i < KW; ++i) t.k[i] = __builtin_nontemporal_load(kc + i);
@@ -231,20 +235,23 @@ __device__ __forceinline__ void load_values(const HeadPlanes& h, uint32_t tr, in
   if constexpr (VW == 4) {
     u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc));
     t.v[0] = x.x; t.v[1] = x.y; t.v[2] = x.z; t.v[3] = x.w;
+  } else if constexpr (VW == 2) {
+    u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vc));
+    t.v[0] = x.x; t.v[1] = x.y;
   } else {
 #pragma unroll
     for (int i = 0; i < VW; ++i) t.v[i] = __builtin_nontemporal_load(vc + i);
   }
 }
 
-template <int D, int KB, bool KQ, int VB, bool VQ>
+template <int D, bool KS, int KB, bool KQ, int VB, bool VQ>
 __device__ __forceinline__ void load_token(const HeadPlanes& h, uint32_t tr, int j, const float* sc_head,
                                            TokenData<KB, KQ, VB, VQ>& t) {
-  load_keys<D>(h, tr, j, sc_head, t);
+  load_keys<D, KS>(h, tr, j, sc_head, t);
   load_values<D>(h, tr, j, t);
 }
 
-template <int D, int KB, bool KQ, int VB, bool VQ>
+template <int D, int KB, bool KQ, bool KS, int VB, bool VQ>
 __global__ __launch_bounds__(lut_threads(VQ))
 __attribute__((amdgpu_waves_per_eu(lut_threads(VQ) / 256, lut_threads(VQ) / 256)))
 void decode_lut_kernel(DecodeParams p) {
@@ -270,7 +277,29 @@ void decode_lut_kernel(DecodeParams p) {
         *reinterpret_cast<half4_t*>(smem + Map::v_base + e * 256 + l * 8) = h;
       }
     }
-    constexpr int NV = VQ ? 0 : (VB == 4 ? 256 : 64);
+    if constexpr (VB == 2 && !VQ) {
+      // Byte e: four 2-bit codes, coordinate i of the byte in bits 2i..2i+1.
+      for (int i = threadIdx.x; i < 256 * 32; i += kLutThreads) {
+        const int e = i >> 5, l = i & 31;
+        half4_t h;
+        h.x = (_Float16)p.vc[e & 3];
+        h.y = (_Float16)p.vc[(e >> 2) & 3];
+        h.z = (_Float16)p.vc[(e >> 4) & 3];
+        h.w = (_Float16)p.vc[e >> 6];
+        *reinterpret_cast<half4_t*>(smem + Map::v_base + e * 256 + l * 8) = h;
+      }
+    }
+    if constexpr (VB == 1 && !VQ) {
+      // Byte e: eight 1-bit codes, coordinate i of the byte in bit i.
+      for (int i = threadIdx.x; i < 256 * 16; i += kLutThreads) {
+        const int e = i >> 4, l = i & 15;
+        half8_t h;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) h[b] = (_Float16)p.vc[(e >> b) & 1];
+        *reinterpret_cast<half8_t*>(smem + Map::v_base + e * 256 + l * 16) = h;
+      }
+    }
+    constexpr int NV = (VQ || VB <= 2) ? 0 : (VB == 4 ? 256 : 64);
     for (int i = threadIdx.x; i < NV * 64; i += kLutThreads) {
       const int e = i >> 6, l = i & 63;
       const int lo = VB == 4 ? (e & 15) : (e & 7), hi = VB == 4 ? (e >> 4) : (e >> 3);
@@ -317,12 +346,13 @@ void decode_lut_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  const uint32_t lr_v = VQ ? (Map::v_base | ((uint32_t)(lane & 31) << 3)) : (Map::v_base | ((uint32_t)lane * 4u));
+  const uint32_t lr_v = (VQ || VB == 2) ? (Map::v_base | ((uint32_t)(lane & 31) << 3))
+                       : (VB == 1 ? (Map::v_base | ((uint32_t)(lane & 15) << 4)) : (Map::v_base | ((uint32_t)lane * 4u)));
   const uint32_t lr_k = (KB == 2 || KQ) ? (Map::k_base | ((uint32_t)(lane & 15) << 4)) : (Map::k_base | ((uint32_t)(lane & 31) << 3));
   // Lane j of a quad streams one per-token scalar: 0 nu_k, 1 gamma_k (or the
   // HeadQ side scale), 2 nu_v, 3 gamma_v.
   // (Lanes j >= 4 of wider groups load a norm they do not use.)
-  const float* sc_src = j == 0 ? p.k.norms : (j == 1 ? (KQ ? p.k.gamma : (KB == 2 ? p.k.side_scale : p.k.norms))
+  const float* sc_src = j == 0 ? p.k.norms : (j == 1 ? (KQ ? p.k.gamma : (KS ? p.k.side_scale : p.k.norms))
                                           : (j == 2 ? p.v.norms : (j == 3 ? (VQ ? p.v.gamma : p.v.norms) : p.k.norms)));
   float* merge = reinterpret_cast<float*>(smem + Map::merge);
   const int R = p.B * p.Hkv * p.nsplit;
@@ -341,7 +371,7 @@ void decode_lut_kernel(DecodeParams p) {
     HeadPlanes hp;
     hp.kc = p.k.codes + vbase * (D * lane_dwords<KB, KQ>() / 8);
     hp.vc = p.v.codes + vbase * (D * lane_dwords<VB, VQ>() / 8);
-    hp.ks = KB == 2 ? p.k.side + vbase * 8 : nullptr;
+    hp.ks = KS ? p.k.side + vbase * 8 : nullptr;
     const float* sc_head = sc_src + vbase;
 
     constexpr bool kUDot = KQ && (VQ || D == 128);
@@ -376,8 +406,8 @@ void decode_lut_kernel(DecodeParams p) {
     }
     // HeadQ: this lane's 4 entries of w = U^T q (side codes 4j..4j+3) and the
     // offset lev * sum(w) that turns a 4-bit code into code - lev.
-    float sw4[KB == 2 ? 4 : 1], swoff = 0.f;
-    if constexpr (KB == 2) {
+    float sw4[KS ? 4 : 1], swoff = 0.f;
+    if constexpr (KS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sw4[i] = p.qw[(size_t)qi * 16 + 4 * j + i];
@@ -473,7 +503,7 @@ void decode_lut_kernel(DecodeParams p) {
       }
       const float nu_k = tok_bcast<L, 0>(cur.sc, lane);
       float part = nu_k * (sa + sb);
-      if constexpr (KB == 2) {
+      if constexpr (KS) {
         // Side-code correction s_z (w . (code - lev)) of this lane's 4 codes.
         const uint32_t sd = cur.ks >> (16 * (j & 1));
         float cs = -swoff;
@@ -529,6 +559,28 @@ void decode_lut_kernel(DecodeParams p) {
           TQ_VQBYTE(0) TQ_VQBYTE(1) TQ_VQBYTE(2) TQ_VQBYTE(3)
 #undef TQ_VQBYTE
         }
+      } else if constexpr (VB == 2) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+#define TQ_V2BYTE(BB)                                                                          \
+          {                                                                                    \
+            const half4_t h = *reinterpret_cast<const half4_t*>(smem + byte_addr<BB>(cur.v[w], lr_v)); \
+            acc[16 * w + 4 * BB] = fmaf(wv, (float)h.x, acc[16 * w + 4 * BB]);                 \
+            acc[16 * w + 4 * BB + 1] = fmaf(wv, (float)h.y, acc[16 * w + 4 * BB + 1]);         \
+            acc[16 * w + 4 * BB + 2] = fmaf(wv, (float)h.z, acc[16 * w + 4 * BB + 2]);         \
+            acc[16 * w + 4 * BB + 3] = fmaf(wv, (float)h.w, acc[16 * w + 4 * BB + 3]);         \
+          }
+          TQ_V2BYTE(0) TQ_V2BYTE(1) TQ_V2BYTE(2) TQ_V2BYTE(3)
+#undef TQ_V2BYTE
+        }
+      } else if constexpr (VB == 1) {
+#define TQ_V1BYTE(BB)                                                                          \
+        {                                                                                      \
+          const half8_t h = *reinterpret_cast<const half8_t*>(smem + byte_addr<BB>(cur.v[0], lr_v)); \
+          _Pragma("unroll") for (int i = 0; i < 8; ++i) acc[8 * BB + i] = fmaf(wv, (float)h[i], acc[8 * BB + i]); \
+        }
+        TQ_V1BYTE(0) TQ_V1BYTE(1) TQ_V1BYTE(2) TQ_V1BYTE(3)
+#undef TQ_V1BYTE
       } else if (VB == 4) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -581,8 +633,8 @@ void decode_lut_kernel(DecodeParams p) {
           gA = tok_bcast<L, 3>(ta.sc, lane);
           gB = tok_bcast<L, 3>(tb.sc, lane);
         }
-        load_keys<D>(hp, (uint32_t)min(pb + s2 + slot, t1 - 1), j, sc_head, na);
-        load_keys<D>(hp, (uint32_t)min(pb + s2 + stride + slot, t1 - 1), j, sc_head, nb);
+        load_keys<D, KS>(hp, (uint32_t)min(pb + s2 + slot, t1 - 1), j, sc_head, na);
+        load_keys<D, KS>(hp, (uint32_t)min(pb + s2 + stride + slot, t1 - 1), j, sc_head, nb);
         // ---- online softmax (per token slot): l in the 2^m frame -----------------------
         const float smax = fmaxf(sA, sB);
         if (smax > m + kSlack) {
@@ -632,8 +684,8 @@ void decode_lut_kernel(DecodeParams p) {
         }
       };
       if (base < t1) {
-        load_keys<D>(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, xa);
-        load_keys<D>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, xb);
+        load_keys<D, KS>(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, xa);
+        load_keys<D, KS>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, xb);
         load_values<D>(hp, (uint32_t)min(base + slot, t1 - 1), j, xa);
         load_values<D>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, xb);
       }
@@ -660,22 +712,22 @@ void decode_lut_kernel(DecodeParams p) {
       // loads in flight the wait before each step leaves the other buffer's
       // loads outstanding.
       TokenData<KB, KQ, VB, VQ> ta, tb;
-      if (base < t1) load_token<D>(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, ta);
+      if (base < t1) load_token<D, KS>(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, ta);
       while (base < t1) {
-        load_token<D>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, tb);
+        load_token<D, KS>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, tb);
         step(ta, base);
         base += stride;
         if (base >= t1) break;
-        load_token<D>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, ta);
+        load_token<D, KS>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, ta);
         step(tb, base);
         base += stride;
       }
     } else {
       TokenData<KB, KQ, VB, VQ> nxt;
-      if (base < t1) load_token<D>(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, nxt);
+      if (base < t1) load_token<D, KS>(hp, (uint32_t)min(base + slot, t1 - 1), j, sc_head, nxt);
       for (; base < t1; base += stride) {
         const TokenData<KB, KQ, VB, VQ> cur = nxt;
-        if (base + stride < t1) load_token<D>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, nxt);
+        if (base + stride < t1) load_token<D, KS>(hp, (uint32_t)min(base + stride + slot, t1 - 1), j, sc_head, nxt);
         step(cur, base);
       }
     }
@@ -747,19 +799,32 @@ void decode_lut_kernel(DecodeParams p) {
   }
 }
 
-template <int D, int KB, bool KQ, int VB, bool VQ>
+template <int D, int KB, bool KQ, bool KS, int VB, bool VQ>
 hipError_t launch_lut_d(const DecodeParams& p, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((decode_lut_kernel<D, KB, KQ, VB, VQ>), dim3(nblocks), dim3(lut_threads(VQ)), 0, s, p);
+  hipLaunchKernelGGL((decode_lut_kernel<D, KB, KQ, KS, VB, VQ>), dim3(nblocks), dim3(lut_threads(VQ)), 0, s, p);
   return hipGetLastError();
 }
 
 template <int KB, bool KQ, int VB, bool VQ>
 hipError_t launch_lut(const DecodeParams& p, int nblocks, hipStream_t s) {
   switch (p.d) {
-    case 128: return launch_lut_d<128, KB, KQ, VB, VQ>(p, nblocks, s);
-    case 256: return launch_lut_d<256, KB, KQ, VB, VQ>(p, nblocks, s);
-    case 512: return launch_lut_d<512, KB, KQ, VB, VQ>(p, nblocks, s);
-    case 1024: return launch_lut_d<1024, KB, KQ, VB, VQ>(p, nblocks, s);
+    case 128: return launch_lut_d<128, KB, KQ, false, VB, VQ>(p, nblocks, s);
+    case 256: return launch_lut_d<256, KB, KQ, false, VB, VQ>(p, nblocks, s);
+    case 512: return launch_lut_d<512, KB, KQ, false, VB, VQ>(p, nblocks, s);
+    case 1024: return launch_lut_d<1024, KB, KQ, false, VB, VQ>(p, nblocks, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Value widths for one key variant: 4, 3 (with or without a sketch), 2, 1.
+template <int KB, bool KQ>
+hipError_t launch_lut_v(const DecodeParams& p, int vbits, int vqjl, int nblocks, hipStream_t s) {
+  if (vqjl) return launch_lut<KB, KQ, 3, true>(p, nblocks, s);
+  switch (vbits) {
+    case 4: return launch_lut<KB, KQ, 4, false>(p, nblocks, s);
+    case 3: return launch_lut<KB, KQ, 3, false>(p, nblocks, s);
+    case 2: return launch_lut<KB, KQ, 2, false>(p, nblocks, s);
+    case 1: return launch_lut<KB, KQ, 1, false>(p, nblocks, s);
   }
   return hipErrorInvalidValue;
 }
@@ -770,25 +835,28 @@ int lut_waves(int vqjl) { return lut_threads(vqjl) / 64; }
 
 bool lut_supported(int d, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl) {
   if (d != 128 && d != 256 && d != 512 && d != 1024) return false;
-  if (kside) return d == 128 && kbits == 2 && side_rank == 16 && side_bits == 4 && vbits == 4 && !vqjl;
-  return (kbits == 3 || kbits == 4) && (vbits == 3 || vbits == 4) && (!kqjl || kbits == 3) && (!vqjl || vbits == 3);
+  const bool vok = vbits >= 1 && vbits <= 4 && (!vqjl || vbits == 3);
+  if (kside) return d == 128 && kbits == 2 && side_rank == 16 && side_bits == 4 && vok && !vqjl;
+  return kbits >= 2 && kbits <= 4 && (!kqjl || kbits == 3) && vok;
 }
 
 
-hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int vbits, int vqjl, int nblocks,
-                             hipStream_t s) {
-  if (kbits == 2) return launch_lut_d<128, 2, false, 4, false>(p, nblocks, s);  // HeadQ keys, 4-bit values
-  const int key = (kbits == 4 ? 0 : 2 + kqjl) * 4 + (vbits == 4 ? 0 : 2 + vqjl);
-  switch (key) {
-    case 0 * 4 + 0: return launch_lut<4, false, 4, false>(p, nblocks, s);
-    case 0 * 4 + 2: return launch_lut<4, false, 3, false>(p, nblocks, s);
-    case 0 * 4 + 3: return launch_lut<4, false, 3, true>(p, nblocks, s);
-    case 2 * 4 + 0: return launch_lut<3, false, 4, false>(p, nblocks, s);
-    case 2 * 4 + 2: return launch_lut<3, false, 3, false>(p, nblocks, s);
-    case 2 * 4 + 3: return launch_lut<3, false, 3, true>(p, nblocks, s);
-    case 3 * 4 + 0: return launch_lut<3, true, 4, false>(p, nblocks, s);
-    case 3 * 4 + 2: return launch_lut<3, true, 3, false>(p, nblocks, s);
-    case 3 * 4 + 3: return launch_lut<3, true, 3, true>(p, nblocks, s);
+hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl,
+                             int nblocks, hipStream_t s) {
+  if (kside) {  // HeadQ keys (2-bit base + side code) at d = 128, 1- to 4-bit values
+    switch (vbits) {
+      case 4: return launch_lut_d<128, 2, false, true, 4, false>(p, nblocks, s);
+      case 3: return launch_lut_d<128, 2, false, true, 3, false>(p, nblocks, s);
+      case 2: return launch_lut_d<128, 2, false, true, 2, false>(p, nblocks, s);
+      case 1: return launch_lut_d<128, 2, false, true, 1, false>(p, nblocks, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (kqjl) return launch_lut_v<3, true>(p, vbits, vqjl, nblocks, s);
+  switch (kbits) {
+    case 4: return launch_lut_v<4, false>(p, vbits, vqjl, nblocks, s);
+    case 3: return launch_lut_v<3, false>(p, vbits, vqjl, nblocks, s);
+    case 2: return launch_lut_v<2, false>(p, vbits, vqjl, nblocks, s);
   }
   return hipErrorInvalidValue;
 }

@@ -195,7 +195,7 @@ bool lut_supported(int d, int kbits, int kqjl, int kside, int side_rank, int sid
 // Waves per block of the table-driven kernel (at d > 128 each wave writes its
 // own partial).
 int lut_waves(int vqjl);
-hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int vbits, int vqjl, int nblocks,
+hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl, int nblocks,
                              hipStream_t s);
 hipError_t launch_metric_scores(const MetricScoreParams& p, int kbits, int kqjl, int kside, hipStream_t s,
                                 bool* supported);

@@ -157,6 +157,41 @@ def test_headq_gqa(tq):
     assert abs(m["kl_mean"] - kls.mean()) <= pu.KL_ATOL and abs(m["kl_max"] - kls.max()) <= pu.KL_ATOL
 
 
+@pytest.mark.parametrize("d,kmode,kbits,vmode,vbits", [
+    (128, 1, 2, 1, 2),    # TQ-KV at n = 2
+    (128, 1, 2, 1, 1),
+    (128, 1, 4, 1, 1),
+    (128, 2, 2, 1, 2),    # K PROD(2 + 1), V MSE(2)
+    (128, 1, 2, 2, 2),    # K MSE(2), V PROD(2 + 1)
+    (256, 1, 2, 1, 2),
+    (512, 1, 3, 1, 1),
+    (1024, 1, 2, 1, 2),
+    (128, 0, 2, 0, 2),    # Plain-KV at n = 2
+])
+def test_table_decode_low_bits(tq, d, kmode, kbits, vmode, vbits):
+    """The table-driven decode at 2-bit keys (fp32 centroid quads per byte)
+    and 1- and 2-bit values (fp16 centroid octets and quads per byte), every
+    head dim it serves; B=1, H=2, 3 queries per KV head, ragged T, fp16."""
+    K, V, Q = synth.isotropic(1, 2, 3, 1100, d, seed=30 + d + kbits + vbits, kv_std=1.0, dtype=np.float32)
+    worst, n_band, kp, vp, _ = _run_case(tq, K, V, Q, "kqv", 4, seed=6, dtype=torch.float16,
+                                         modes=((kmode, kbits), (vmode, vbits)), label="lowbits")
+    assert (kp.c.mode, kp.c.bits, vp.c.mode, vp.c.bits) == (kmode, kbits, vmode, vbits)
+    print("low bits d=%d K(%d,%d) V(%d,%d) worst %.3g" % (d, kmode, kbits, vmode, vbits, worst))
+
+
+@pytest.mark.parametrize("vbits", [1, 2, 3])
+def test_headq_keys_low_bit_values(tq, vbits):
+    """HeadQ keys over 1-, 2- and 3-bit values (the value tiers of the A^2
+    policy), 4 query heads per KV head."""
+    d, r = 128, 16
+    K, V, Q, C = synth.rope_gqa(1, 2, 4, 900, d, seed=7, n_calib=2048, dtype=np.float32)
+    from oracle import headq as ohq
+    U = np.stack([ohq.fit_basis(C[h].astype(np.float64), r)[0] for h in range(2)])
+    worst, n_band, kp, vp, _ = _run_case(tq, K, V, Q, "headq", 4, seed=4, U=U, modes=((3, 2), (1, vbits)),
+                                         label="headq v%d" % vbits)
+    assert (kp.c.mode, vp.c.bits) == (3, vbits)
+
+
 @pytest.mark.parametrize("scheme", ["kqv", "kv", "qkqv"])
 def test_isotropic_decode_full_size_sampled(tq, scheme):
     """The benchmark workload at full size (B=16, 32 heads, T=32768, d=128,
