@@ -689,7 +689,18 @@ tq_status quantize_core(const tq_tensor_desc* x, int mode, int bits, uint64_t se
     if (!gaussian_codebook(bits, &c, &t)) return fail(TQ_EINVAL, "Gaussian codebook (%d bits) failed", bits);
     for (int k = 0; k < 16; ++k) p.gbounds[k] = k < (int)t.size() ? t[k] : INFINITY;
     p.basis = out->basis; p.smean = out->mean; p.sscale = out->scale;
-    status = hip_status(launch_quantize_spectral(p, st), "quantize launch");
+    // Lookup grid over u = z / s_i: cells a third of the smallest boundary gap
+    // wide, covering the boundaries plus two cells.
+    double gap = 2.0, tmax = 0.0;
+    for (size_t k = 0; k < t.size(); ++k) {
+      tmax = std::max(tmax, std::fabs(t[k]));
+      if (k) gap = std::min(gap, t[k] - t[k - 1]);
+    }
+    QuantGrid g;
+    g.scale = (float)(3.2 / gap);
+    g.center = (int)std::ceil((tmax + 2.0 / g.scale) * g.scale) + 2;
+    g.cells = 2 * g.center + 1;
+    status = hip_status(launch_quantize_spectral(p, &g, st), "quantize launch");
   } else if (quant_mfma_supported(p) && quant_grid(x->d, bits, &grid)) {
     int cus = 0;
     status = hip_status(cu_count(&cus), "device query");

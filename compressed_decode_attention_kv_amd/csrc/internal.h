@@ -172,7 +172,9 @@ struct RelErrParams {
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 // SPECTRAL at d = 32, 64, 128 (quant_spectral.hip) and its reconstruction error.
 int spectral_max_d();
-hipError_t launch_quantize_spectral(const QuantParams& p, hipStream_t s);
+// d = 128 takes the matrix-core kernel with certified decisions when `grid`
+// (the N(0, 1) boundaries' lookup grid) fits; otherwise the fp64 kernel.
+hipError_t launch_quantize_spectral(const QuantParams& p, const QuantGrid* grid, hipStream_t s);
 hipError_t launch_relerr_spectral(const RelErrParams& p, hipStream_t s);
 // PROD at d = 256..1024 with the sketch projection on the matrix cores (quant_sketch.hip).
 bool quant_sketch_supported(const QuantParams& p, const QuantGrid& grid);

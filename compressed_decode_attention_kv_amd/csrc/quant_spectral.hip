@@ -144,6 +144,297 @@ __global__ __launch_bounds__(kSqThreads) void quant_spectral_kernel(QuantParams 
   }
 }
 
+// ---- d = 128 on the matrix cores, decisions certified --------------------------------
+// The projection z' = V^T (x - mu) of a tile of 64 tokens is a [64 x 128] x
+// [128 x 128] product: v_mfma_f32_32x32x16_f16 on fp16 hi + lo splits of the
+// centred inputs (scaled by sigma = 2^(13 - e), nu in [2^(e-1), 2^e), so
+// sigma nu in [2^12, 2^13)) and of V (scaled by 2^12), the hi x hi products
+// in four accumulators of 32 terms each and the hi x lo + lo x hi terms in a
+// fifth.  In the unit domain (z = z' / nu) the computed value is within
+// kSmEps of the exact one: 2 * 2^-24 per addition over 32 terms against
+// sum |terms| <= 1 (Cauchy-Schwarz, the columns of V are unit vectors), plus
+// the dropped lo x lo term (2^-22), the split and centring roundings and
+// fp16 denormals (each < 4e-7).  A decision is certified when no boundary
+// s_i t_k lies within kSmEps of z; the others (a few per thousand) are
+// queued and recomputed exactly in double, as the fp64 kernel above does
+// for every decision.
+constexpr int kSmThreads = 256;
+constexpr int kSmD = 128;
+constexpr int kSmTT = 64;                 // tokens per tile
+constexpr int kSmRow = kSmD + 8;          // fp16 per A row: rows 4 banks apart
+constexpr int kSmXRow = kSmD + 4;         // floats per raw-input row: rows 4 banks apart
+constexpr int kSmIRow = kSmD + 16;        // bytes per index row: rows 4 banks apart
+constexpr int kSmVRow = kSmD + 1;         // floats per V^T row: columns of V spread over the banks
+constexpr int kSmQueue = 4096;
+constexpr int kSmLutMax = 256;
+constexpr int kSmTilesPerBlock = 16;
+constexpr float kSmEps = 8e-6f;
+constexpr float kSmVScale = 4096.0f;      // V x 2^12 before the split
+
+typedef _Float16 sm_half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 sm_half2 __attribute__((ext_vector_type(2)));
+typedef float sm_float16 __attribute__((ext_vector_type(16)));
+typedef float sm_float4 __attribute__((ext_vector_type(4)));
+
+struct SmLut {
+  float t;
+  uint32_t base;
+};
+
+struct SmShared {
+  float vt[kSmD * kSmVRow];         // V transposed: vt[i][k] = V[k][i]
+  float xr[kSmTT * kSmXRow];        // the tile's raw inputs as fp32
+  _Float16 ah[kSmTT * kSmRow];      // sigma (x - mu), fp16 hi
+  _Float16 al[kSmTT * kSmRow];      // and lo
+  uint8_t idx[kSmTT * kSmIRow];
+  uint16_t queue[kSmQueue];         // (token << 7) | coordinate of uncertain decisions
+  float mean[kSmD], scale[kSmD];
+  double nu[kSmTT];
+  float zinv[kSmTT];                // 1 / (sigma 2^12 nu), 0 for a zero (or padding) token
+  SmLut lut[kSmLutMax];
+  int qcount;
+};
+
+template <int BITS, typename TIN>
+__global__ __launch_bounds__(kSmThreads) void quant_spectral_mfma_kernel(QuantParams p, QuantGrid grid) {
+  constexpr int NB = (1 << BITS) - 1;
+  __shared__ __attribute__((aligned(16))) SmShared sh;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 3, slot = lane >> 2;        // phase 1: 4 lanes per token, 32 coordinates each
+  const int hh = lane >> 5, mm = lane & 31;        // phases 2-3: operand / result lane
+  const int tph = (p.T + kSmTT - 1) / kSmTT;        // tiles per head
+  const int cph = (tph + kSmTilesPerBlock - 1) / kSmTilesPerBlock;
+  const int bh = blockIdx.x / cph;
+  const int tile0 = (blockIdx.x - bh * cph) * kSmTilesPerBlock;
+  const int tile1 = min(tph, tile0 + kSmTilesPerBlock);
+  const int b = bh / p.H, h = bh - b * p.H;
+
+  // ---- per head: V^T, mean, spreads, the grid table; B operands in registers --------
+  {
+    const float* V = p.basis + (size_t)h * kSmD * kSmD;
+    for (int e = threadIdx.x; e < kSmD * kSmD; e += kSmThreads) {
+      const int k = e >> 7, i = e & 127;          // coalesced over i
+      sh.vt[i * kSmVRow + k] = V[e];
+    }
+    if (threadIdx.x < kSmD) {
+      sh.mean[threadIdx.x] = p.smean[(size_t)h * kSmD + threadIdx.x];
+      sh.scale[threadIdx.x] = p.sscale[(size_t)h * kSmD + threadIdx.x];
+    }
+    for (int n = threadIdx.x; n < grid.cells; n += kSmThreads) {
+      const float lo = ((float)(n - 1) - 0.5f - (float)grid.center) / grid.scale;
+      const float hi = ((float)(n + 1) + 0.5f - (float)grid.center) / grid.scale;
+      uint32_t base = 0;
+      float t = INFINITY;
+      for (int k = 0; k < NB; ++k) {
+        const float bk = p.bounds[k];
+        if (bk < lo) base++;
+        else if (bk < hi && t == INFINITY) t = bk;
+      }
+      sh.lut[n].t = t;
+      sh.lut[n].base = base;
+    }
+  }
+  __syncthreads();
+  // Wave w owns eigen-coordinates 32 w .. 32 w + 31; lane (hh, mm) holds V[k][32 w + mm]
+  // for k = 16 ks + 8 hh + e, e < 8, as fp16 hi + lo of V x 2^12.
+  const int col = 32 * wave + mm;
+  sm_half8 Bh[8], Bl[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const float* src = sh.vt + col * kSmVRow + 16 * ks + 8 * hh;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = src[e] * kSmVScale;
+      const _Float16 hi = (_Float16)v;
+      Bh[ks][e] = hi;
+      Bl[ks][e] = (_Float16)(v - (float)hi);
+    }
+  }
+  const float s_col = sh.scale[col];
+  const float inv_s = s_col > 0.f ? 1.0f / s_col : 0.f;
+  float tmax = 0.f;
+  for (int k = 0; k < NB; ++k) tmax = fmaxf(tmax, fabsf(p.bounds[k]));
+  const float umax = tmax + 2.0f / grid.scale;
+  const bool lut_ok = s_col * grid.scale > 2.0f * kSmEps;  // margin within one grid cell in u
+  const float gbias = 12582912.0f + (float)grid.center;
+
+  const TIN* xbase = reinterpret_cast<const TIN*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const int64_t slot0 = p.pos ? p.pos[b] : 0;
+  const size_t vbase = (size_t)bh * p.T_cap;
+  const int m1 = wave * 16 + slot;                  // phase-1 token of this lane
+  float xin[32];
+  auto load_tile = [&](int tile) {
+    const int t = tile * kSmTT + m1;
+    load32<TIN>(xbase + (int64_t)min(t, p.T - 1) * p.st + 32 * j, xin);
+    if (t >= p.T) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) xin[e] = 0.f;
+    }
+  };
+  if (tile0 < tile1) load_tile(tile0);
+
+  for (int tile = tile0; tile < tile1; ++tile) {
+    const int tt0 = tile * kSmTT;
+    // ---- 1. centre, norm (double), scale, split into the A tile -----------------------
+    {
+      float mu[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const sm_float4 v4 = *reinterpret_cast<const sm_float4*>(sh.mean + 32 * j + 4 * q);
+        mu[4 * q] = v4.x; mu[4 * q + 1] = v4.y; mu[4 * q + 2] = v4.z; mu[4 * q + 3] = v4.w;
+      }
+      double ss = 0.0;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const double xc = (double)xin[e] - (double)mu[e];
+        ss = fma(xc, xc, ss);
+      }
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      const double nu = sqrt(ss);
+      int ex = 0;
+      (void)frexp(nu, &ex);
+      // x - mu in fp32 (one rounding, within the margin), times a power of two.
+      const float sigma = nu > 0.0 ? ldexpf(1.0f, 13 - ex) : 0.f;
+      float* xr = sh.xr + m1 * kSmXRow + 32 * j;
+      _Float16* dh = sh.ah + m1 * kSmRow + 32 * j;
+      _Float16* dl = sh.al + m1 * kSmRow + 32 * j;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        *reinterpret_cast<sm_float4*>(xr + 4 * q) = sm_float4{xin[4 * q], xin[4 * q + 1], xin[4 * q + 2], xin[4 * q + 3]};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sm_half8 h8, l8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = (xin[8 * q + e] - mu[8 * q + e]) * sigma;
+          const _Float16 hi = (_Float16)v;
+          h8[e] = hi;
+          l8[e] = (_Float16)(v - (float)hi);
+        }
+        *reinterpret_cast<sm_half8*>(dh + 8 * q) = h8;
+        *reinterpret_cast<sm_half8*>(dl + 8 * q) = l8;
+      }
+      if (j == 0) {
+        sh.nu[m1] = nu;
+        sh.zinv[m1] = nu > 0.0 ? (float)(1.0 / ((double)sigma * (double)kSmVScale * nu)) : 0.f;
+        const int t = tt0 + m1;
+        const int64_t tw = slot0 + t;
+        if (t < p.T && tw >= 0 && tw < p.T_cap) __builtin_nontemporal_store((float)nu, p.norms + vbase + tw);
+      }
+      if (threadIdx.x == 0) sh.qcount = 0;
+    }
+    __syncthreads();
+    if (tile + 1 < tile1) load_tile(tile + 1);     // in flight during phases 2-5
+
+    // ---- 2./3. projection on the matrix cores, certified decisions ---------------------
+#pragma unroll 1
+    for (int tb = 0; tb < 2; ++tb) {
+      sm_float16 acc[4], accc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc[0][i] = 0.f; acc[1][i] = 0.f; acc[2][i] = 0.f; acc[3][i] = 0.f; accc[i] = 0.f;
+      }
+      const _Float16* arow_h = sh.ah + (tb * 32 + mm) * kSmRow + 8 * hh;
+      const _Float16* arow_l = sh.al + (tb * 32 + mm) * kSmRow + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const sm_half8 xh = *reinterpret_cast<const sm_half8*>(arow_h + 16 * ks);
+        const sm_half8 xl = *reinterpret_cast<const sm_half8*>(arow_l + 16 * ks);
+        acc[ks >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, Bh[ks], acc[ks >> 1], 0, 0, 0);
+        accc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, Bl[ks], accc, 0, 0, 0);
+        accc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl, Bh[ks], accc, 0, 0, 0);
+      }
+      // Register i: token tb*32 + 8 (i/4) + 4 hh + i % 4, coordinate col.
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = tb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const float zs = ((acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i])) + accc[i];
+        const float zi = sh.zinv[m];
+        const float z = zs * zi;                    // unit domain
+        // Grid lookup of u = z / s_i (clamped: no boundary lies beyond umax).
+        const float u = fminf(fmaxf(z * inv_s, -umax), umax);
+        const float f = fmaf(u, grid.scale, gbias);
+        const SmLut ent = sh.lut[__float_as_uint(f) - 0x4B400000u];
+        uint32_t c = ent.base + (u >= ent.t ? 1u : 0u);
+        bool sure = !(fabsf(z - s_col * ent.t) <= kSmEps);    // t = inf: sure
+        // Spreads too small for the grid: sure only beyond every boundary.
+        const bool far = fabsf(z) > s_col * tmax + kSmEps;
+        c = lut_ok ? c : (z > 0.f ? (uint32_t)NB : 0u);
+        sure = lut_ok ? sure : far;
+        // Zero (or padding) token: every field 0.
+        c = zi == 0.f ? 0u : c;
+        sure = sure || zi == 0.f;
+        sh.idx[m * kSmIRow + col] = (uint8_t)c;
+        if (!sure) {
+          const int q = atomicAdd(&sh.qcount, 1);
+          if (q < kSmQueue) sh.queue[q] = (uint16_t)((m << 7) | col);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- 4. exact decisions for the queue: 16 lanes per decision, in double ------------
+    {
+      const int qn = sh.qcount;
+      const bool all = qn > kSmQueue;              // overflow: recompute every decision
+      const int n_items = all ? kSmTT * kSmD : qn;
+      const int grp = threadIdx.x >> 4, gl = threadIdx.x & 15;
+      for (int it = grp; it < n_items; it += kSmThreads / 16) {
+        const uint32_t item = all ? (uint32_t)it : sh.queue[it];
+        const int m = (int)(item >> 7), i = (int)(item & 127);
+        const float* xr = sh.xr + m * kSmXRow + 8 * gl;
+        const float* vr = sh.vt + i * kSmVRow + 8 * gl;
+        const float* mu = sh.mean + 8 * gl;
+        double a = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fma((double)xr[e] - (double)mu[e], (double)vr[e], a);
+        a += __shfl_xor(a, 1, 64);
+        a += __shfl_xor(a, 2, 64);
+        a += __shfl_xor(a, 4, 64);
+        a += __shfl_xor(a, 8, 64);
+        if (gl == 0) {
+          const double nu = sh.nu[m];
+          const double si = (double)sh.scale[i];
+          uint32_t c = 0;
+          for (int k = 0; k < NB; ++k) c += (a >= nu * (si * p.gbounds[k])) ? 1u : 0u;
+          sh.idx[m * kSmIRow + i] = (uint8_t)(nu > 0.0 ? c : 0u);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- 5. pack and store ------------------------------------------------------------
+    {
+      const int t = tt0 + m1;
+      const int64_t tw = slot0 + t;
+      if (t < p.T && tw >= 0 && tw < p.T_cap) {
+        uint32_t w[BITS];
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) w[k] = 0;
+        uint32_t cb[8];
+        {
+          const uint4 a = *reinterpret_cast<const uint4*>(sh.idx + m1 * kSmIRow + 32 * j);
+          const uint4 b2 = *reinterpret_cast<const uint4*>(sh.idx + m1 * kSmIRow + 32 * j + 16);
+          cb[0] = a.x; cb[1] = a.y; cb[2] = a.z; cb[3] = a.w; cb[4] = b2.x; cb[5] = b2.y; cb[6] = b2.z; cb[7] = b2.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const uint32_t c = (cb[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+          const int bit = BITS * e, wi = bit >> 5, shf = bit & 31;
+          w[wi] |= c << shf;
+          if (shf + BITS > 32) w[wi + 1] |= c >> (32 - shf);
+        }
+        uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + (vbase + tw) * (size_t)(kSmD * BITS / 8)) + j * BITS;
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) __builtin_nontemporal_store(w[k], dst + k);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Reconstruction error of a SPECTRAL tensor against its raw input, with the
 // block layout of relerr_kernel (4 waves, 4 steps of 64/L tokens per wave):
 // x_hat = mu + nu V (s * c[idx]) densely in the original domain, lane j its
@@ -279,11 +570,35 @@ hipError_t launch_rsq_d(const RelErrParams& p, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int BITS>
+hipError_t launch_sm(const QuantParams& p, const QuantGrid& grid, hipStream_t s) {
+  const long tph = (p.T + kSmTT - 1) / kSmTT;
+  const long blocks = (long)p.B * p.H * ((tph + kSmTilesPerBlock - 1) / kSmTilesPerBlock);
+  if (p.dtype == TQ_F16)
+    hipLaunchKernelGGL((quant_spectral_mfma_kernel<BITS, _Float16>), dim3((unsigned)blocks), dim3(kSmThreads), 0, s, p, grid);
+  else
+    hipLaunchKernelGGL((quant_spectral_mfma_kernel<BITS, float>), dim3((unsigned)blocks), dim3(kSmThreads), 0, s, p, grid);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int spectral_max_d() { return kSqMaxD; }
 
-hipError_t launch_quantize_spectral(const QuantParams& p, hipStream_t s) {
+bool spectral_mfma_supported(const QuantParams& p, const QuantGrid& grid) {
+  return p.d == kSmD && p.bits >= 1 && p.bits <= 4 && grid.cells >= 1 && grid.cells <= kSmLutMax;
+}
+
+hipError_t launch_quantize_spectral(const QuantParams& p, const QuantGrid* grid, hipStream_t s) {
+  if (grid && spectral_mfma_supported(p, *grid)) {
+    switch (p.bits) {
+      case 1: return launch_sm<1>(p, *grid, s);
+      case 2: return launch_sm<2>(p, *grid, s);
+      case 3: return launch_sm<3>(p, *grid, s);
+      case 4: return launch_sm<4>(p, *grid, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (p.d) {
     case 32: return launch_sq_d<32>(p, s);
     case 64: return launch_sq_d<64>(p, s);

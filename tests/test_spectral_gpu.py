@@ -12,6 +12,7 @@ import pytest
 
 from compressed_decode_attention_kv_amd import synth
 from oracle import metrics as ome
+from oracle import spectral as osq
 from tests import gpu_util
 from tests import parity_util as pu
 
@@ -78,10 +79,39 @@ def test_squ_kv_metrics(tq):
     assert abs(m["top5_recall"] - np.concatenate(recs).mean()) <= amb / (5.0 * len(kl)) + 1e-12
 
 
-def test_squ_kv_append_matches_full_quantize(tq):
+@pytest.mark.parametrize("n,dt", [(3, "f16"), (4, "f32"), (1, "f16")])
+def test_squ_kv_many_tiles(tq, n, dt):
+    """d = 128 over many 64-token tiles and several blocks per head (T=2500,
+    a ragged last tile), the matrix-core projection with certified
+    decisions against the oracle."""
+    K, V, Q, spec = _case(1, 2, 2, 2500, 128, seed=60 + n)
+    dtype = torch.float16 if dt == "f16" else torch.float32
+    gpu_util.run_case(tq, K, V, Q, "squ-kv", n, seed=0, dtype=dtype, spectral=spec, label="tiles n=%d" % n)
+
+
+def test_squ_kv_degenerate_calibration(tq):
+    """A calibration without noise: 112 of 128 spreads are (numerically)
+    zero, so most decisions cannot be certified and every tile takes the
+    exact path for all its decisions; keys with and without a component
+    outside the calibrated span."""
+    rng = np.random.default_rng(70)
+    d, T, r = 128, 700, 16
+    W, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    lam = 0.7 ** np.arange(r)
+    C = (rng.standard_normal((2048, r)) * np.sqrt(lam)) @ W.T
+    X = (rng.standard_normal((1, 1, T, r)) * np.sqrt(lam)) @ W.T
+    X[0, 0, T // 2:] += 0.05 * rng.standard_normal((T - T // 2, d))   # half the tokens leave the span
+    V0, mu, sc = (a.astype(np.float32) for a in osq.fit(C.astype(np.float64)))
+    spec = {"K": (V0[None], mu[None], sc[None]), "V": (V0[None], mu[None], sc[None])}
+    Q = rng.standard_normal((1, 2, d))
+    gpu_util.run_case(tq, X, X, Q, "squ-kv", 3, spectral=spec, label="degenerate")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_squ_kv_append_matches_full_quantize(tq, d):
     """Appending a SPECTRAL cache in pieces at per-sequence positions writes
     the same bytes as quantising it whole."""
-    K, V, Q, spec = _case(2, 2, 1, 400, 64, seed=52)
+    K, V, Q, spec = _case(2, 2, 1, 400, d, seed=52)
     Kd = gpu_util.dev(K)
     sd = tuple(gpu_util.dev(a) for a in spec["K"])
     full = tq.quantize(Kd, tq.KEYS, "squ-kv", 3, spectral=sd)
