@@ -15,18 +15,19 @@ SRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["api.cpp", "host_math.cpp", "quant.hip", "decode.hip", "decode_lut.hip", "quant_mfma.hip", "diag.hip",
-           "noalloc.hip", "quant_sketch.hip", "quant_spectral.hip", "policy.hip"]
+           "noalloc.hip", "quant_sketch.hip", "quant_spectral.hip", "policy.hip", "decode_mq.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # Keep the compiler from emitting packed-FP32 VALU instructions.
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(PKG, "..", "include")]
-# Per-source extras.  The quantiser's matrix-core results are read by vector
-# code right away: keep them in ordinary VGPRs (no accumulator-register copies).
-# The table-driven decode is scheduled for instruction-level parallelism
-# (max ILP): at its register budget the default occupancy-first scheduler
-# waits for each LDS table read before issuing the next; the iterative-ILP
-# strategy measured equal or up to 1.5 % slower.
+# Per-source extras.  The matrix-core results of the quantisers are read by
+# vector code right away: keep them in ordinary VGPRs (no accumulator-register
+# copies).  The table-driven decode is scheduled for instruction-level
+# parallelism (max ILP): at its register budget the default occupancy-first
+# scheduler waits for each LDS table read before issuing the next; the
+# iterative-ILP strategy measured equal or up to 1.5 % slower.
 EXTRA = {"quant_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "quant_spectral.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "decode_lut.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 

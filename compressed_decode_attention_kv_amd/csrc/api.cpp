@@ -278,6 +278,7 @@ struct DecodePlan {
   int nsplit, chunk, part_stride, units, G;
   int nparts;  // partials per query: nsplit, times the waves per block at d > 128 (table-driven)
   bool lut;
+  bool mq;     // grouped-query matrix-core decode (units: KV head x block of 16 queries x chunk)
   size_t off_qrot, off_qsk, off_qw, off_part, off_qraw, off_qoff, bytes;
 };
 
@@ -300,14 +301,17 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   const bool lut = v && k->T_cap <= (1 << 24) && (long)k->T_cap * (d / 2) < (1L << 32) &&
                    lut_supported(d, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, k->side_rank,
                                  k->side_bits, v->bits, v->mode == TQ_MODE_PROD);
+  const bool mq = v && mq_supported(d, G, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, k->side_rank,
+                                    k->side_bits, v->bits, v->mode == TQ_MODE_PROD);
   // The table-driven kernel walks 8-12 waves x (64/L) tokens per block step
-  // and runs one persistent block per CU; the generic one 4 waves per block.
-  const int step = (lut ? 8 : 4) * vpw;
-  const long groups = (long)k->B * k->H * G;
+  // and runs one persistent block per CU; the generic one 4 waves per block;
+  // the grouped-query one steps 16 tokens per wave.
+  const int step = mq ? 16 : (lut ? 8 : 4) * vpw;
+  const long groups = mq ? (long)k->B * k->H * ((G + 15) / 16) : (long)k->B * k->H * G;
   // Work units (query, context chunk): the generic kernel wants ~2048 blocks
   // in flight; the persistent table-driven kernel wants few, long units
   // (about two per CU) because each unit ends with a merge of its token slots.
-  const long target = lut ? 512 : 2048;
+  const long target = mq ? 4096 : (lut ? 512 : 2048);
   int nsplit = (int)std::max<long>(1, (target + groups - 1) / groups);
   int chunk = (k->T + nsplit - 1) / nsplit;
   chunk = std::max(step, (chunk + step - 1) / step * step);
@@ -325,7 +329,8 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   pl->nsplit = nsplit;
   pl->nparts = nsplit * per_split;
   pl->chunk = chunk;
-  pl->lut = lut;
+  pl->lut = lut && !mq;
+  pl->mq = mq;
   pl->G = G;
   pl->part_stride = (int)round_up(2 + d + (vq ? d : 0), 4);
   const long R = (long)k->B * k->H * nsplit;
@@ -814,7 +819,13 @@ tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_pack
 
   bool supported = true;
   if (tq_status s = hip_status(launch_qprep(qp, st), "query prep launch")) return s;
-  if (pl.lut) {
+  if (pl.mq) {
+    int cus = 0;
+    if (tq_status s = hip_status(cu_count(&cus), "device query")) return s;
+    const long wunits = (long)k->B * k->H * ((pl.G + 15) / 16) * pl.nsplit;   // one wave per unit
+    const int nblocks = (int)std::max<long>(1, std::min<long>((wunits + 3) / 4, (long)cus * 8));
+    if (tq_status s = hip_status(launch_decode_mq(dp, k->bits, ksd, v->bits, nblocks, st), "decode launch")) return s;
+  } else if (pl.lut) {
     int cus = 0;
     if (tq_status s = hip_status(cu_count(&cus), "device query")) return s;
     const int nblocks = std::min(pl.units, std::max(1, cus));

@@ -199,6 +199,11 @@ bool lut_supported(int d, int kbits, int kqjl, int kside, int side_rank, int sid
 int lut_waves(int vqjl);
 hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl, int nblocks,
                              hipStream_t s);
+// Grouped-query decode on the matrix cores (decode_mq.hip): d = 128, G >= 2
+// query heads per KV head, MSE/PLAIN/SPECTRAL or HeadQ keys, 2- to 4-bit
+// unsketched values.
+bool mq_supported(int d, int G, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl);
+hipError_t launch_decode_mq(const DecodeParams& p, int kbits, int kside, int vbits, int nblocks, hipStream_t s);
 hipError_t launch_metric_scores(const MetricScoreParams& p, int kbits, int kqjl, int kside, hipStream_t s,
                                 bool* supported);
 hipError_t launch_metric_reduce(const MetricReduceParams& p, hipStream_t s);

@@ -179,6 +179,48 @@ def test_table_decode_low_bits(tq, d, kmode, kbits, vmode, vbits):
     print("low bits d=%d K(%d,%d) V(%d,%d) worst %.3g" % (d, kmode, kbits, vmode, vbits, worst))
 
 
+@pytest.mark.parametrize("G,kbits,vbits,T", [
+    (2, 4, 4, 700), (4, 3, 4, 1000), (16, 2, 2, 333), (17, 4, 3, 900), (64, 4, 4, 257), (5, 2, 3, 1),
+])
+def test_grouped_query_decode(tq, G, kbits, vbits, T):
+    """The grouped-query matrix-core decode (G >= 2 query heads per KV head at
+    d = 128, unsketched tensors): one block of 16 queries per pass, ragged
+    query blocks (G = 17: 16 + 1), T not a multiple of the 16-token step,
+    T = 1; fp16 inputs, B=2, H=2."""
+    K, V, Q = synth.isotropic(2, 2, G, T, 128, seed=80 + G + T, kv_std=1.0, dtype=np.float32)
+    _run_case(tq, K, V, Q, "kqv", 4, seed=2, dtype=torch.float16, modes=((1, kbits), (1, vbits)),
+              label="gqa G=%d" % G)
+
+
+def test_grouped_query_decode_lengths_and_static(tq):
+    """Per-sequence lengths (0, ragged, full) and the allocation-free decode
+    through the grouped-query path agree with the oracle on each prefix."""
+    from oracle import attention as oat
+    B, H, G, T, d = 3, 2, 4, 600, 128
+    K, V, Q = synth.isotropic(B, H, G, T, d, seed=91, kv_std=1.0, dtype=np.float32)
+    Kd, Vd, Qd = _dev(K, torch.float16), _dev(V, torch.float16), _dev(Q, torch.float16)
+    kp = tq.quantize(Kd, tq.KEYS, "tq-kv", 4, 3)
+    vp = tq.quantize(Vd, tq.VALUES, "tq-kv", 3, 3)
+    lens = torch.tensor([0, 301, 600], dtype=torch.int32, device="cuda")
+    out, lse = tq.decode_attention(Qd, kp, vp, lens=lens)
+    o2 = torch.empty_like(out)
+    l2 = torch.empty_like(lse)
+    tq.decode_attention_static(Qd, kp, vp, o2, l2, lens=lens)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    Kh, Vh, Qh = Kd.double().cpu().numpy(), Vd.double().cpu().numpy(), Qd.double().cpu().numpy()
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    for b, n in ((1, 301), (2, 600)):
+        for h in range(H):
+            sl = slice((b * H + h) * T, (b * H + h) * T + n)
+            _, Khat, _, _, _ = pu.oracle_match(Kh[b, h, :n], {k: v[sl] for k, v in kp.planes().items()}, oqz.MSE, 4, 3)
+            _, Vhat, _, _, _ = pu.oracle_match(Vh[b, h, :n], {k: v[sl] for k, v in vp.planes().items()}, oqz.MSE, 3, 3)
+            o_ref, _, _, l_ref = oat.attend(Qh[b, h * G:(h + 1) * G], Khat, Vhat)
+            assert np.all(pu.rel_l2(out[b, h * G:(h + 1) * G], o_ref) <= pu.OUT_RTOL)
+            assert np.allclose(lse[b, h * G:(h + 1) * G], l_ref, atol=2e-4)
+
+
 @pytest.mark.parametrize("vbits", [1, 2, 3])
 def test_headq_keys_low_bit_values(tq, vbits):
     """HeadQ keys over 1-, 2- and 3-bit values (the value tiers of the A^2
