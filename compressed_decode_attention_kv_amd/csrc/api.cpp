@@ -298,11 +298,13 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   // The table-driven kernel addresses a head's planes with 24-bit token
   // indices and 32-bit byte offsets (at most d/2 code bytes per token),
   // hence the T_cap bounds.
-  const bool lut = v && k->T_cap <= (1 << 24) && (long)k->T_cap * (d / 2) < (1L << 32) &&
-                   lut_supported(d, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, k->side_rank,
-                                 k->side_bits, v->bits, v->mode == TQ_MODE_PROD);
+  // Several query heads per KV head: the grouped-query kernel reads each
+  // token once per block of 16 of them.
   const bool mq = v && mq_supported(d, G, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, k->side_rank,
                                     k->side_bits, v->bits, v->mode == TQ_MODE_PROD);
+  const bool lut = !mq && v && k->T_cap <= (1 << 24) && (long)k->T_cap * (d / 2) < (1L << 32) &&
+                   lut_supported(d, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, k->side_rank,
+                                 k->side_bits, v->bits, v->mode == TQ_MODE_PROD);
   // The table-driven kernel walks 8-12 waves x (64/L) tokens per block step
   // and runs one persistent block per CU; the generic one 4 waves per block;
   // the grouped-query one steps 16 tokens per wave.
@@ -329,7 +331,7 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   pl->nsplit = nsplit;
   pl->nparts = nsplit * per_split;
   pl->chunk = chunk;
-  pl->lut = lut && !mq;
+  pl->lut = lut;
   pl->mq = mq;
   pl->G = G;
   pl->part_stride = (int)round_up(2 + d + (vq ? d : 0), 4);
@@ -822,9 +824,11 @@ tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_pack
   if (pl.mq) {
     int cus = 0;
     if (tq_status s = hip_status(cu_count(&cus), "device query")) return s;
-    const long wunits = (long)k->B * k->H * ((pl.G + 15) / 16) * pl.nsplit;   // one wave per unit
-    const int nblocks = (int)std::max<long>(1, std::min<long>((wunits + 3) / 4, (long)cus * 8));
-    if (tq_status s = hip_status(launch_decode_mq(dp, k->bits, ksd, v->bits, nblocks, st), "decode launch")) return s;
+    const long units = (long)k->B * k->H * ((pl.G + 15) / 16) * pl.nsplit;
+    const int upb = mq_units_per_block(k->d);
+    const long cap = (long)cus * (8 / mq_waves_per_unit(k->d) > 0 ? 8 / mq_waves_per_unit(k->d) : 1) * (k->d == 128 ? 1 : 2);
+    const int nblocks = (int)std::max<long>(1, std::min<long>((units + upb - 1) / upb, cap));
+    if (tq_status s = hip_status(launch_decode_mq(dp, k->bits, kq, ksd, v->bits, vq, nblocks, st), "decode launch")) return s;
   } else if (pl.lut) {
     int cus = 0;
     if (tq_status s = hip_status(cu_count(&cus), "device query")) return s;

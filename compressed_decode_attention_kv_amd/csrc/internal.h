@@ -199,11 +199,16 @@ bool lut_supported(int d, int kbits, int kqjl, int kside, int side_rank, int sid
 int lut_waves(int vqjl);
 hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl, int nblocks,
                              hipStream_t s);
-// Grouped-query decode on the matrix cores (decode_mq.hip): d = 128, G >= 2
-// query heads per KV head, MSE/PLAIN/SPECTRAL or HeadQ keys, 2- to 4-bit
-// unsketched values.
+// Grouped-query decode on the matrix cores (decode_mq.hip): d = 128..1024,
+// G >= 2 query heads per KV head, 2- to 4-bit keys (3-bit with a sketch) or
+// HeadQ at d = 128, 2- to 4-bit values (3-bit with a sketch).  A unit (KV
+// head, 16 queries, chunk) takes mq_waves_per_unit(d) waves; a block holds
+// mq_units_per_block(d) units.
 bool mq_supported(int d, int G, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl);
-hipError_t launch_decode_mq(const DecodeParams& p, int kbits, int kside, int vbits, int nblocks, hipStream_t s);
+int mq_waves_per_unit(int d);
+int mq_units_per_block(int d);
+hipError_t launch_decode_mq(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl, int nblocks,
+                            hipStream_t s);
 hipError_t launch_metric_scores(const MetricScoreParams& p, int kbits, int kqjl, int kside, hipStream_t s,
                                 bool* supported);
 hipError_t launch_metric_reduce(const MetricReduceParams& p, hipStream_t s);

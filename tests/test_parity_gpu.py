@@ -192,6 +192,18 @@ def test_grouped_query_decode(tq, G, kbits, vbits, T):
               label="gqa G=%d" % G)
 
 
+@pytest.mark.parametrize("d,G,scheme", [
+    (128, 4, "kqv"), (128, 3, "qkqv"), (256, 2, "tq-kv"), (256, 16, "qkqv"), (512, 5, "kqv"),
+    (1024, 2, "qkqv"), (1024, 17, "kqv"), (1024, 8, "tq-kv"),
+])
+def test_grouped_query_decode_wide_and_sketched(tq, d, G, scheme):
+    """The grouped-query decode over wider heads (d / 128 waves per unit adding
+    partial scores through LDS) and over sketched keys and values (QJL sign
+    products on the matrix cores), n = 4, fp16, ragged T."""
+    K, V, Q = synth.isotropic(1, 2, G, 530, d, seed=100 + d + G, kv_std=1.0, dtype=np.float32)
+    _run_case(tq, K, V, Q, scheme, 4, seed=4, dtype=torch.float16, label="gqa %s d=%d G=%d" % (scheme, d, G))
+
+
 def test_grouped_query_decode_lengths_and_static(tq):
     """Per-sequence lengths (0, ragged, full) and the allocation-free decode
     through the grouped-query path agree with the oracle on each prefix."""
