@@ -9,7 +9,8 @@ Prints one JSON line.  `value` = decode GB/s of packed cache read
 (algorithmic packed bytes / time of the decode entry point, HIP events on the
 stream the kernels run on); quantize tok/s and the whole-step time ride
 along.  `roofline` covers the decode chain, `quantize_roofline` the K + V
-quantize of the step; `quality` holds the measures of the packed cache at the
+quantize of the step, beside `copy_floor_ms`: the same bytes moved in the
+same access pattern with no arithmetic (tq_stream_rw); `quality` holds the measures of the packed cache at the
 workload's full size (computed outside the timed region); `cpu_baseline`
 times the float64 oracle on a bounded sample of the same workload on the
 host cores.  --workload heavy-tailed | low-rank | headq-gqa | structured prints
@@ -514,6 +515,31 @@ def main():
     res["stream_read_bytes"] = int(packed_bytes_total(kp, vp))
     res["decode_pct_of_stream_read"] = round(100.0 * dec_gbs / stream_gbs, 2)
     del sbuf
+    # Write-side floor: the step's quantize traffic (fp16 rows in; packed code
+    # rows and per-token float planes out, in the quantiser's access pattern)
+    # with no arithmetic, timed the same way.
+    rows = B * H * T
+    code_rows = [p.codes.numel() // rows for p in (kp, vp)]
+    if all(c % 64 == 0 for c in code_rows):
+        dst = torch.empty(rows * max(code_rows), dtype=torch.uint8, device="cuda")
+        pl = torch.empty((2, rows), dtype=torch.float32, device="cuda")
+        nplanes = [sum(1 for t in (p.norms, p.gamma, p.side_scale) if t is not None) for p in (kp, vp)]
+
+        def floor_step():
+            for c, npl in zip(code_rows, nplanes):
+                tq.stream_rw(K, rows, d * K.element_size(), dst, c, pl, npl)
+        floor_step()
+        torch.cuda.synchronize()
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in fev:
+            a.record()
+            floor_step()
+            b.record()
+        torch.cuda.synchronize()
+        fl_ms = sum(a.elapsed_time(b) for a, b in fev) / len(fev)
+        res["quantize_roofline"]["copy_floor_ms"] = round(fl_ms, 4)
+        res["quantize_roofline"]["pct_of_copy_floor"] = round(100.0 * fl_ms / r["q_avg"], 2)
+        del dst, pl
     if not args.no_extras:
         # The decode alone, each repetition after a 1 GiB write that evicts
         # the 256 MB MALL (the step's quantize leaves the planes in no cache:

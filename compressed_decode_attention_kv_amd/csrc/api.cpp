@@ -204,14 +204,17 @@ tq_status sketch16_on_device(uint64_t seed, int d, const _Float16** out) {
 
 tq_status hip_status(hipError_t e, const char* what);
 
-// Grid for the index search: a cell width of a third of the smallest gap
-// between boundaries puts at most one boundary in any three adjacent cells.
+// Grid for the index search: a cell width of gap / 1.25 (gap = the smallest
+// distance between boundaries) keeps the window of 1 + 2 kGridMargin cells
+// around any cell narrower than the gap, so it holds at most one boundary.
+// Coarse cells keep the table small: the coordinates of a token fall into a
+// few dozen adjacent entries, which spread over distinct LDS banks.
 bool quant_grid(int d, int bits, QuantGrid* g) {
   std::vector<double> c, t;
   if (!codebook(d, bits, &c, &t)) return false;
   double gap = 2.0;
   for (size_t k = 1; k < t.size(); ++k) gap = std::min(gap, t[k] - t[k - 1]);
-  g->scale = (float)(3.2 / gap);
+  g->scale = (float)(1.25 / gap);
   g->center = (int)std::ceil(g->scale) + 2;
   g->cells = 2 * g->center + 1;
   return g->cells <= quant_mfma_lut_max();
@@ -1183,6 +1186,23 @@ tq_status tq_stream_read(const void* src, size_t bytes, void* sink, void* stream
   if (!aligned(src, 16) || !aligned(sink, 4)) return fail(TQ_EINVAL, "src must be 16-byte aligned, sink 4-byte aligned");
   if (bytes == 0 || bytes % 16) return fail(TQ_EINVAL, "bytes must be a positive multiple of 16");
   return hip_status(launch_stream_read(src, bytes, sink, (hipStream_t)stream), "stream read launch");
+}
+
+tq_status tq_stream_rw(const void* src, int64_t rows, int32_t in_row_bytes, void* dst, int32_t out_row_bytes,
+                       float* planes, int32_t nplanes, void* stream) {
+  if (!src || !dst || (nplanes > 0 && !planes)) return fail(TQ_EINVAL, "NULL pointer");
+  if (!aligned(src, 16) || !aligned(dst, 16) || (planes && !aligned(planes, 4)))
+    return fail(TQ_EINVAL, "src and dst must be 16-byte aligned, planes 4-byte aligned");
+  if (in_row_bytes < 64 || in_row_bytes > 4096 || in_row_bytes % 64 || out_row_bytes < 64 || out_row_bytes > 4096 ||
+      out_row_bytes % 64)
+    return fail(TQ_EINVAL, "row sizes must be multiples of 64 in [64, 4096]");
+  if (nplanes < 0 || nplanes > 4) return fail(TQ_EINVAL, "nplanes must be in [0, 4]");
+  if (rows < 1 || rows > (int64_t(1) << 35)) return fail(TQ_EINVAL, "rows must be in [1, 2^35]");
+  int cus = 0;
+  if (tq_status st = hip_status(cu_count(&cus), "device query")) return st;
+  return hip_status(launch_stream_rw(src, (long)rows, in_row_bytes, dst, out_row_bytes, planes, nplanes, cus,
+                                     (hipStream_t)stream),
+                    "stream read-write launch");
 }
 
 tq_status tq_release_cache(void) {

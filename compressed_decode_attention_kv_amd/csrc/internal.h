@@ -65,6 +65,11 @@ struct QuantParams {
 
 // Uniform grid over the unit-sphere coordinate y in [-1, 1] used to find the
 // Lloyd-Max index: cell n = round(y * scale) + center, cells = 2 center + 1.
+// A coordinate in cell n lies within half a cell of its centre; the window
+// of half-width 0.5 + kGridMargin cells around it holds at most one boundary
+// (the cell width is below the smallest gap / (1 + 2 kGridMargin)), so a
+// cell's entry is that boundary and the count of boundaries below the window.
+constexpr float kGridMargin = 0.0625f;
 struct QuantGrid {
   float scale;
   int center, cells;
@@ -263,5 +268,7 @@ size_t static_scratch_bytes();
 hipError_t static_scratch(void** out);
 int stream_read_blocks();
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
+hipError_t launch_stream_rw(const void* src, long rows, int in_row_bytes, void* dst, int out_row_bytes, float* planes,
+                            int nplanes, int cus, hipStream_t s);
 
 }  // namespace tq

@@ -59,8 +59,8 @@ typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct LutEntry {
-  float t;        // the boundary inside cells n-1..n+1 (+inf if none)
-  uint32_t base;  // number of boundaries below cell n-1
+  float t;        // the boundary inside cell n's window (+inf if none)
+  uint32_t base;  // number of boundaries below the window
 };
 
 __device__ __forceinline__ int parity(uint32_t x) { return __builtin_popcount(x) & 1; }
@@ -100,8 +100,8 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
 
   // ---- per-block tables -------------------------------------------------------------
   for (int n = threadIdx.x; n < grid.cells; n += kThreadsM) {
-    const float lo = ((float)(n - 1) - 0.5f - (float)grid.center) / grid.scale;
-    const float hi = ((float)(n + 1) + 0.5f - (float)grid.center) / grid.scale;
+    const float lo = ((float)n - (0.5f + kGridMargin) - (float)grid.center) / grid.scale;
+    const float hi = ((float)n + (0.5f + kGridMargin) - (float)grid.center) / grid.scale;
     uint32_t base = 0;
     float t = INFINITY;
     for (int k = 0; k < NB; ++k) {

@@ -79,8 +79,8 @@ size_t sketch_fragment_index(int d, int row, int col) {
 namespace {
 
 // Grid lookup of the Lloyd-Max index: cell n = round(y * scale) + center
-// holds the boundary inside cells n-1..n+1 (+inf if none) and the number of
-// boundaries below them, so the index is base + [y >= t].
+// holds the boundary inside the cell's window (+inf if none) and the number of
+// boundaries below it, so the index is base + [y >= t].
 struct SkLut {
   float t;
   uint32_t base;
@@ -106,8 +106,8 @@ void quant_sketch_kernel(QuantParams p, QuantGrid grid) {
   const int j = lane & (G::L - 1), slot = lane / G::L;
   if (threadIdx.x < 16) s_cent[threadIdx.x] = p.centroids[threadIdx.x];
   for (int n = threadIdx.x; n < grid.cells; n += kSkThreads) {
-    const float lo = ((float)(n - 1) - 0.5f - (float)grid.center) / grid.scale;
-    const float hi = ((float)(n + 1) + 0.5f - (float)grid.center) / grid.scale;
+    const float lo = ((float)n - (0.5f + kGridMargin) - (float)grid.center) / grid.scale;
+    const float hi = ((float)n + (0.5f + kGridMargin) - (float)grid.center) / grid.scale;
     uint32_t base = 0;
     float t = INFINITY;
     for (int k = 0; k < NB; ++k) {

@@ -31,7 +31,7 @@ EXPORTS = ["tq_abi_version", "tq_status_str", "tq_last_error", "tq_codebook_buil
            "tq_metrics_workspace_size", "tq_metrics", "tq_spectral_fit", "tq_headq_fit",
            "tq_a2_workspace_size", "tq_a2_weights", "tq_value_policy_workspace_size", "tq_value_policy",
            "tq_gather_tokens", "tq_attention_merge",
-           "tq_stream_read", "tq_release_cache"]
+           "tq_stream_read", "tq_stream_rw", "tq_release_cache"]
 
 
 class ModeOverride(ctypes.Structure):
@@ -116,6 +116,8 @@ _sigs = {
     "tq_attention_merge": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "tq_stream_read": ([ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "tq_stream_rw": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                      ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
     "tq_release_cache": ([], ctypes.c_int),
 }
 for _name, (_args, _res) in _sigs.items():
@@ -455,6 +457,14 @@ def metrics(q=None, k_ref=None, v_ref=None, kp=None, vp=None):
 def stream_read(buf, sink):
     """Stream-read the device tensor `buf` (non-temporal 128-bit loads)."""
     _check(_lib.tq_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), _stream()))
+
+
+def stream_rw(src, rows, in_row_bytes, dst, out_row_bytes, planes=None, nplanes=0):
+    """The write side's traffic with no arithmetic: per row, read in_row_bytes
+    of the device tensor `src`, write out_row_bytes of `dst` and one float to
+    each of `nplanes` planes of `planes` ([nplanes][rows] float32)."""
+    _check(_lib.tq_stream_rw(src.data_ptr(), rows, in_row_bytes, dst.data_ptr(), out_row_bytes,
+                             planes.data_ptr() if planes is not None else None, nplanes, _stream()))
 
 
 def release_cache():

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 6
+#define TQ_ABI_VERSION 7
 
 typedef enum tq_status {
   TQ_OK = 0,
@@ -397,6 +397,19 @@ tq_status tq_attention_merge(const float* out_a, const float* lse_a, const float
  * streaming-read bandwidth and serves as the known-size reference for the
  * HBM byte counters.  Stream-ordered. */
 tq_status tq_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
+/* Diagnostic: the memory traffic of the write side with no arithmetic.  For
+ * each of `rows` rows, reads `in_row_bytes` at src + row * in_row_bytes and
+ * writes `out_row_bytes` (their XOR fold) at dst + row * out_row_bytes, plus
+ * one float per row to each of `nplanes` planes (planes + p * rows + row), in
+ * the access pattern of the d = 128 quantiser (16 rows per wave, 16-byte
+ * non-temporal loads and stores).  in_row_bytes and out_row_bytes are
+ * multiples of 64 in [64, 4096]; nplanes in [0, 4] (planes may be NULL when
+ * 0); src and dst 16-byte aligned, planes 4-byte aligned; rows in
+ * [1, 2^35].  Its time is the floor for a quantise that moves the same
+ * bytes (input rows, packed codes, per-token norms).  Stream-ordered. */
+tq_status tq_stream_rw(const void* src, int64_t rows, int32_t in_row_bytes, void* dst, int32_t out_row_bytes,
+                       float* planes, int32_t nplanes, void* stream);
 
 /* Frees the cached device constants of every device. */
 tq_status tq_release_cache(void);

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(tqlib):
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(tqlib.EXPORTS) == names
-    assert tqlib.lib().tq_abi_version() == 6
+    assert tqlib.lib().tq_abi_version() == 7
 
 
 @pytest.mark.parametrize("d,bits", [(32, 1), (128, 2), (128, 3), (128, 4), (1024, 2), (1024, 4)])
@@ -334,3 +334,23 @@ def test_value_policy_rejects_before_any_gpu_call(tqlib):
     assert lib.tq_attention_merge(fake, fake, None, fake, 4, 64, fake, None, None) == tqlib.EINVAL
     assert lib.tq_attention_merge(fake, fake, fake, fake, 0, 64, fake, None, None) == tqlib.EINVAL
 
+
+
+def test_stream_rw_rejects_before_any_gpu_call(tqlib):
+    """Host validation of the write-side traffic diagnostic (fake pointers)."""
+    lib = tqlib.lib()
+    fake = 1 << 20
+
+    def call(src=fake, rows=1024, ib=256, dst=fake, ob=64, planes=fake, np_=2):
+        return lib.tq_stream_rw(src, rows, ib, dst, ob, planes, np_, None)
+    assert call(src=None) == tqlib.EINVAL
+    assert call(dst=None) == tqlib.EINVAL
+    assert call(planes=None) == tqlib.EINVAL
+    assert call(src=fake + 8) == tqlib.EINVAL
+    assert call(planes=fake + 2) == tqlib.EINVAL
+    for ib, ob in ((0, 64), (96, 64), (8192, 64), (256, 0), (256, 80), (256, 8192)):
+        assert call(ib=ib, ob=ob) == tqlib.EINVAL, (ib, ob)
+    for np_ in (-1, 5):
+        assert call(np_=np_) == tqlib.EINVAL
+    for rows in (0, -3, (1 << 35) + 1):
+        assert call(rows=rows) == tqlib.EINVAL
