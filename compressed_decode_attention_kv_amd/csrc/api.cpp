@@ -315,8 +315,11 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   const long groups = mq ? (long)k->B * k->H * ((G + 15) / 16) : (long)k->B * k->H * G;
   // Work units (query, context chunk): the generic kernel wants ~2048 blocks
   // in flight; the persistent table-driven kernel wants few, long units
-  // (about two per CU) because each unit ends with a merge of its token slots.
-  const long target = mq ? 4096 : (lut ? 512 : 2048);
+  // (about two per CU) because each unit ends with a merge of its token slots;
+  // the grouped-query kernel about as many units as fit on the device at once
+  // (d/128 waves each): every unit writes 16 partials of 2 + 2d floats, which
+  // the combine step reads back.
+  const long target = mq ? 4096 / mq_waves_per_unit(d) : (lut ? 512 : 2048);
   int nsplit = (int)std::max<long>(1, (target + groups - 1) / groups);
   int chunk = (k->T + nsplit - 1) / nsplit;
   chunk = std::max(step, (chunk + step - 1) / step * step);
