@@ -162,9 +162,7 @@ constexpr int kSmThreads = 256;
 constexpr int kSmD = 128;
 constexpr int kSmTT = 64;                 // tokens per tile
 constexpr int kSmRow = kSmD + 8;          // fp16 per A row: rows 4 banks apart
-constexpr int kSmXRow = kSmD + 4;         // floats per raw-input row: rows 4 banks apart
 constexpr int kSmIRow = kSmD + 16;        // bytes per index row: rows 4 banks apart
-constexpr int kSmVRow = kSmD + 1;         // floats per V^T row: columns of V spread over the banks
 constexpr int kSmQueue = 4096;
 constexpr int kSmLutMax = 256;
 constexpr int kSmTilesPerBlock = 16;
@@ -181,9 +179,9 @@ struct SmLut {
   uint32_t base;
 };
 
+// The exact recomputations read V and the raw inputs from global memory (L2):
+// they are rare, and without copies of them here a block fits twice per CU.
 struct SmShared {
-  float vt[kSmD * kSmVRow];         // V transposed: vt[i][k] = V[k][i]
-  float xr[kSmTT * kSmXRow];        // the tile's raw inputs as fp32
   _Float16 ah[kSmTT * kSmRow];      // sigma (x - mu), fp16 hi
   _Float16 al[kSmTT * kSmRow];      // and lo
   uint8_t idx[kSmTT * kSmIRow];
@@ -210,13 +208,9 @@ __global__ __launch_bounds__(kSmThreads) void quant_spectral_mfma_kernel(QuantPa
   const int tile1 = min(tph, tile0 + kSmTilesPerBlock);
   const int b = bh / p.H, h = bh - b * p.H;
 
-  // ---- per head: V^T, mean, spreads, the grid table; B operands in registers --------
+  // ---- per head: mean, spreads, the grid table; B operands in registers ------------
+  const float* V = p.basis + (size_t)h * kSmD * kSmD;
   {
-    const float* V = p.basis + (size_t)h * kSmD * kSmD;
-    for (int e = threadIdx.x; e < kSmD * kSmD; e += kSmThreads) {
-      const int k = e >> 7, i = e & 127;          // coalesced over i
-      sh.vt[i * kSmVRow + k] = V[e];
-    }
     if (threadIdx.x < kSmD) {
       sh.mean[threadIdx.x] = p.smean[(size_t)h * kSmD + threadIdx.x];
       sh.scale[threadIdx.x] = p.sscale[(size_t)h * kSmD + threadIdx.x];
@@ -242,10 +236,10 @@ __global__ __launch_bounds__(kSmThreads) void quant_spectral_mfma_kernel(QuantPa
   sm_half8 Bh[8], Bl[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    const float* src = sh.vt + col * kSmVRow + 16 * ks + 8 * hh;
+    const float* src = V + (size_t)(16 * ks + 8 * hh) * kSmD + col;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = src[e] * kSmVScale;
+      const float v = src[(size_t)e * kSmD] * kSmVScale;
       const _Float16 hi = (_Float16)v;
       Bh[ks][e] = hi;
       Bl[ks][e] = (_Float16)(v - (float)hi);
@@ -297,12 +291,8 @@ __global__ __launch_bounds__(kSmThreads) void quant_spectral_mfma_kernel(QuantPa
       (void)frexp(nu, &ex);
       // x - mu in fp32 (one rounding, within the margin), times a power of two.
       const float sigma = nu > 0.0 ? ldexpf(1.0f, 13 - ex) : 0.f;
-      float* xr = sh.xr + m1 * kSmXRow + 32 * j;
       _Float16* dh = sh.ah + m1 * kSmRow + 32 * j;
       _Float16* dl = sh.al + m1 * kSmRow + 32 * j;
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        *reinterpret_cast<sm_float4*>(xr + 4 * q) = sm_float4{xin[4 * q], xin[4 * q + 1], xin[4 * q + 2], xin[4 * q + 3]};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         sm_half8 h8, l8;
@@ -384,12 +374,15 @@ __global__ __launch_bounds__(kSmThreads) void quant_spectral_mfma_kernel(QuantPa
       for (int it = grp; it < n_items; it += kSmThreads / 16) {
         const uint32_t item = all ? (uint32_t)it : sh.queue[it];
         const int m = (int)(item >> 7), i = (int)(item & 127);
-        const float* xr = sh.xr + m * kSmXRow + 8 * gl;
-        const float* vr = sh.vt + i * kSmVRow + 8 * gl;
+        // Token tt0 + m's raw input (a padding token past T reads the last
+        // token; its nu is 0, so its fields are 0 whatever the sum) and
+        // column i of V, coordinates 8 gl .. 8 gl + 7.
+        const TIN* xr = xbase + (int64_t)min(tt0 + m, p.T - 1) * p.st + 8 * gl;
+        const float* vr = V + (size_t)(8 * gl) * kSmD + i;
         const float* mu = sh.mean + 8 * gl;
         double a = 0.0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a = fma((double)xr[e] - (double)mu[e], (double)vr[e], a);
+        for (int e = 0; e < 8; ++e) a = fma((double)(float)xr[e] - (double)mu[e], (double)vr[(size_t)e * kSmD], a);
         a += __shfl_xor(a, 1, 64);
         a += __shfl_xor(a, 2, 64);
         a += __shfl_xor(a, 4, 64);
