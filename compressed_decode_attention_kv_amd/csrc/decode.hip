@@ -51,13 +51,6 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
-// From this head dimension on, S q_rot of sketched keys runs in its own
-// kernel (below) that shares each load of S among kQskQueries queries: S is
-// d^2 floats (4 MB at d = 1024), and reading it once per query dominated the
-// query preparation of many queries.
-constexpr int kQskMinD = 512;
-constexpr int kQskQueries = 16;
-
 // ---- query preparation -------------------------------------------------------
 // q_rot = Pi q (rotated keys) or q; q_sk = S q_rot (QJL keys); q_w = U_h^T q
 // (HeadQ keys).  One block per query.
@@ -123,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(QPrepParams p) {
   for (int i = threadIdx.x; i < d; i += blockDim.x) p.qrot[(size_t)qi * d + i] = s_r[i];
   if (p.qraw)
     for (int i = threadIdx.x; i < d; i += blockDim.x) p.qraw[(size_t)qi * d + i] = s_q[i];
-  if (p.kqjl && d < kQskMinD) {
+  if (p.kqjl) {
     for (int i = threadIdx.x; i < d; i += blockDim.x) {
       const float* srow = p.S + (size_t)i * d;
       float acc = 0.f;
@@ -331,173 +324,105 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   if (threadIdx.x == 0) { out[0] = M; out[1] = lt; }
 }
 
-// ---- S q_rot for many queries (d >= kQskMinD) ------------------------------------
-// Block (query group of QB, 64 rows of S): the group's rotated queries in
-// LDS, S in 64 x 64 tiles through LDS (row pitch 65: lane i reads row i,
-// distinct banks); thread (row i, query quarter) accumulates QB / 4 queries
-// in k order, the same fma sequence as the per-query loop.
-template <int QB>
-__global__ __launch_bounds__(kThreads) void qsk_kernel(QPrepParams p) {
-  __shared__ float s_r[QB][kMaxD];
-  __shared__ float s_S[64][65];
-  const int d = p.d, nq = p.B * p.Hq;
-  const int q0 = blockIdx.x * QB, i0 = blockIdx.y * 64;
-  for (int e = threadIdx.x; e < QB * d; e += blockDim.x) {
-    const int q = e / d, k = e - q * d;
-    s_r[q][k] = q0 + q < nq ? p.qrot[(size_t)(q0 + q) * d + k] : 0.f;
-  }
-  const int i = threadIdx.x & 63, qg = threadIdx.x >> 6;
-  constexpr int QT = QB / (kThreads / 64);
-  float acc[QT];
-#pragma unroll
-  for (int u = 0; u < QT; ++u) acc[u] = 0.f;
-  for (int k0 = 0; k0 < d; k0 += 64) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
-      const int r = e >> 6, c = e & 63;
-      s_S[r][c] = p.S[(size_t)(i0 + r) * d + k0 + c];
-    }
-    __syncthreads();
-    for (int c = 0; c < 64; ++c) {
-      const float sv = s_S[i][c];
-#pragma unroll
-      for (int u = 0; u < QT; ++u) acc[u] = fmaf(sv, s_r[qg * QT + u][k0 + c], acc[u]);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < QT; ++u) {
-    const int q = q0 + qg * QT + u;
-    if (q < nq) p.qsk[(size_t)q * d + i0 + i] = acc[u];
-  }
-}
-
 // ---- combine + finalize --------------------------------------------------------
 // LSE-merge of the splits, then out = Pi^T (acc/l + a S^T ask / l) (rotated V),
-// mu + V (s * acc / l) (SPECTRAL V) or acc / l (plain V).  QB queries per
-// block: at large d with sketched values the S^T ask product reads S (d^2
-// floats) once for the block's QB queries.  SPECTRAL values take QB = 1.
-template <int QB>
+// mu + V (s * acc / l) (SPECTRAL V) or acc / l (plain V).  One block per query;
+// the split weights are reduced block-wide (thread s takes split s).
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
-  __shared__ float s_o[QB][kMaxD], s_k[QB][kMaxD];
-  __shared__ float s_w[QB][256];
-  __shared__ float s_M[QB], s_L[QB];
+  __shared__ float s_o[kMaxD], s_k[kMaxD];
+  __shared__ float s_w[256];
+  __shared__ float s_M, s_L;
   __shared__ float s_red[kThreads / 64];
-  const int d = p.d, q0 = blockIdx.x * QB;
-  // A padding query of the last block repeats the last query and is not written.
-  auto part_of = [&](int q) { return p.part + (size_t)min(q0 + q, p.nq - 1) * p.nsplit * p.part_stride; };
-  // Merge weights of the splits (thread s takes split s; nsplit <= 256).
-  for (int q = 0; q < QB; ++q) {
-    const float* part = part_of(q);
-    const int sp = threadIdx.x;
+  const int qi = blockIdx.x, d = p.d;
+  const float* part = p.part + (size_t)qi * p.nsplit * p.part_stride;
+  {
+    const int sp = threadIdx.x;  // nsplit <= 256 = kThreads
     const float ms = sp < p.nsplit ? part[(size_t)sp * p.part_stride] : -INFINITY;
     const float M = block_max(ms, s_red);
     const float w = sp < p.nsplit ? safe_exp2_diff(ms, M) : 0.f;
-    if (sp < p.nsplit) s_w[q][sp] = w;
+    if (sp < p.nsplit) s_w[sp] = w;
     const float L = block_sum(sp < p.nsplit ? part[(size_t)sp * p.part_stride + 1] * w : 0.f, s_red);
-    if (threadIdx.x == 0) { s_M[q] = M; s_L[q] = L; }
+    if (threadIdx.x == 0) { s_M = M; s_L = L; }
   }
   __syncthreads();
   // A sequence with no tokens (length 0) has l = 0: its output is 0 and its
   // log-sum-exp -inf.
-  for (int e = threadIdx.x; e < QB * d; e += blockDim.x) {
-    const int q = e / d, i = e - q * d;
-    const float* part = part_of(q);
+  const float invl = s_L > 0.f ? 1.0f / s_L : 0.f;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
     float a = 0.f, k = 0.f;
     for (int sp = 0; sp < p.nsplit; ++sp) {
-      a = fmaf(part[(size_t)sp * p.part_stride + 2 + i], s_w[q][sp], a);
-      if (p.vqjl) k = fmaf(part[(size_t)sp * p.part_stride + 2 + d + i], s_w[q][sp], k);
+      a = fmaf(part[(size_t)sp * p.part_stride + 2 + i], s_w[sp], a);
+      if (p.vqjl) k = fmaf(part[(size_t)sp * p.part_stride + 2 + d + i], s_w[sp], k);
     }
-    const float invl = s_L[q] > 0.f ? 1.0f / s_L[q] : 0.f;
-    s_o[q][i] = a * invl;
-    s_k[q][i] = k * invl;
+    s_o[i] = a * invl;
+    s_k[i] = k * invl;
   }
   __syncthreads();
   if (p.vqjl) {
-    float add[QB][kMaxD / kThreads];
+    float add[kMaxD / kThreads];
     for (int c = 0; c < d / (int)blockDim.x + 1; ++c) {
       const int kk = threadIdx.x + c * blockDim.x;
       if (kk < d && c < kMaxD / kThreads) {
         // S^T acc_sk: coalesced across kk; unrolled so that several L2
-        // loads are in flight per thread; each S entry serves QB queries.
-        float acc[QB];
-#pragma unroll
-        for (int q = 0; q < QB; ++q) acc[q] = 0.f;
+        // loads are in flight per thread.
+        float acc = 0.f;
 #pragma unroll 16
-        for (int i = 0; i < d; ++i) {
-          const float sv = p.S[(size_t)i * d + kk];
-#pragma unroll
-          for (int q = 0; q < QB; ++q) acc[q] = fmaf(sv, s_k[q][i], acc[q]);
-        }
-#pragma unroll
-        for (int q = 0; q < QB; ++q) add[q][c] = acc[q];
+        for (int i = 0; i < d; ++i) acc = fmaf(p.S[(size_t)i * d + kk], s_k[i], acc);
+        add[c] = acc;
       }
     }
     __syncthreads();
     for (int c = 0; c < d / (int)blockDim.x + 1; ++c) {
       const int kk = threadIdx.x + c * blockDim.x;
-      if (kk < d && c < kMaxD / kThreads) {
-#pragma unroll
-        for (int q = 0; q < QB; ++q) s_o[q][kk] = fmaf(p.v_qjl, add[q][c], s_o[q][kk]);
-      }
+      if (kk < d && c < kMaxD / kThreads) s_o[kk] = fmaf(p.v_qjl, add[c], s_o[kk]);
     }
     __syncthreads();
   }
-  if constexpr (QB == 1) {
-    if (p.vspectral) {
-      // out = mu + V (s * acc / l), V row-major [k][i], d <= 128.  The basis
-      // is staged in (dynamic) LDS as for the query prep; thread k then forms
-      // row k (reads spread over the banks by the per-row offset k).
-      const int qi = q0;
-      const int kvh = (qi % p.Hq) / p.G;
-      extern __shared__ float4 s_dyn[];
-      float* sV = reinterpret_cast<float*>(s_dyn);
-      const float4* V4 = reinterpret_cast<const float4*>(p.vbasis + (size_t)kvh * d * d);
-      const float* sc = p.vscale + (size_t)kvh * d;
-      const float* mu = p.vmean + (size_t)kvh * d;
-      for (int e = threadIdx.x; e < d * d / 4; e += blockDim.x) s_dyn[e] = V4[e];
-      for (int i = threadIdx.x; i < d; i += blockDim.x) s_k[0][i] = sc[i] * s_o[0][i];
-      __syncthreads();
-      for (int k = threadIdx.x; k < d; k += blockDim.x) {
-        float acc = 0.f;
-        for (int u = 0; u < d; ++u) {
-          const int i = (u + k) & (d - 1);
-          acc = fmaf(sV[k * d + i], s_k[0][i], acc);
-        }
-        s_w[0][k] = mu[k] + acc;
+  if (p.vspectral) {
+    // out = mu + V (s * acc / l), V row-major [k][i], d <= 128.  The basis is
+    // staged in (dynamic) LDS as for the query prep; thread k then forms row
+    // k (reads spread over the banks by the per-row offset k).
+    const int kvh = (qi % p.Hq) / p.G;
+    extern __shared__ float4 s_dyn[];
+    float* sV = reinterpret_cast<float*>(s_dyn);
+    const float4* V4 = reinterpret_cast<const float4*>(p.vbasis + (size_t)kvh * d * d);
+    const float* sc = p.vscale + (size_t)kvh * d;
+    const float* mu = p.vmean + (size_t)kvh * d;
+    for (int e = threadIdx.x; e < d * d / 4; e += blockDim.x) s_dyn[e] = V4[e];
+    for (int i = threadIdx.x; i < d; i += blockDim.x) s_k[i] = sc[i] * s_o[i];
+    __syncthreads();
+    for (int k = threadIdx.x; k < d; k += blockDim.x) {
+      float acc = 0.f;
+      for (int u = 0; u < d; ++u) {
+        const int i = (u + k) & (d - 1);
+        acc = fmaf(sV[k * d + i], s_k[i], acc);
       }
-      __syncthreads();
-      // A sequence with no tokens keeps its zero output.
-      for (int i = threadIdx.x; i < d; i += blockDim.x) s_o[0][i] = s_L[0] > 0.f ? s_w[0][i] : 0.f;
-      __syncthreads();
+      s_w[k] = mu[k] + acc;
     }
+    __syncthreads();
+    // A sequence with no tokens keeps its zero output.
+    for (int i = threadIdx.x; i < d; i += blockDim.x) s_o[i] = s_L > 0.f ? s_w[i] : 0.f;
+    __syncthreads();
   }
   if (p.vrotate) {
     for (int h = 1; h < d; h <<= 1) {
-      for (int e = threadIdx.x; e < QB * (d / 2); e += blockDim.x) {
-        const int q = e / (d / 2), i = e - q * (d / 2);
+      for (int i = threadIdx.x; i < d / 2; i += blockDim.x) {
         const int lo = (i / h) * 2 * h + (i % h), hi = lo + h;
-        float a = s_o[q][lo], c = s_o[q][hi];
-        s_o[q][lo] = a + c;
-        s_o[q][hi] = a - c;
+        float a = s_o[lo], c = s_o[hi];
+        s_o[lo] = a + c;
+        s_o[hi] = a - c;
       }
       __syncthreads();
     }
-    for (int e = threadIdx.x; e < QB * d; e += blockDim.x) {
-      const int q = e / d, i = e - q * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
       const float sg = ((p.signbits[i >> 5] >> (i & 31)) & 1u) ? -1.f : 1.f;
-      s_o[q][i] *= sg * p.inv_sqrt_d;
+      s_o[i] *= sg * p.inv_sqrt_d;
     }
     __syncthreads();
   }
-  for (int e = threadIdx.x; e < QB * d; e += blockDim.x) {
-    const int q = e / d, i = e - q * d;
-    if (q0 + q < p.nq) p.out[(size_t)(q0 + q) * d + i] = s_o[q][i];
-  }
-  if (threadIdx.x < QB && q0 + (int)threadIdx.x < p.nq && p.lse) {
-    const int q = threadIdx.x, qi = q0 + q;
-    p.lse[qi] = s_L[q] > 0.f ? (s_M[q] + log2f(s_L[q])) * 0.69314718055994530942f + (p.qoff ? p.qoff[qi] : 0.f)
-                             : -INFINITY;
-  }
+  for (int i = threadIdx.x; i < d; i += blockDim.x) p.out[(size_t)qi * d + i] = s_o[i];
+  if (threadIdx.x == 0 && p.lse)
+    p.lse[qi] = s_L > 0.f ? (s_M + log2f(s_L)) * 0.69314718055994530942f + (p.qoff ? p.qoff[qi] : 0.f) : -INFINITY;
 }
 
 // ---- metric scores ---------------------------------------------------------------
@@ -704,24 +629,13 @@ hipError_t launch_ms(const MetricScoreParams& p, hipStream_t s) {
 
 hipError_t launch_qprep(const QPrepParams& p, hipStream_t s) {
   const size_t dyn = p.kspectral ? (size_t)p.d * p.d * sizeof(float) : 0;  // the SPECTRAL basis (d <= 128)
-  const int nq = p.B * p.Hq;
-  hipLaunchKernelGGL(qprep_kernel, dim3(nq), dim3(kThreads), dyn, s, p);
-  if (p.kqjl && p.d >= kQskMinD) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((qsk_kernel<kQskQueries>), dim3((nq + kQskQueries - 1) / kQskQueries, p.d / 64), dim3(kThreads),
-                       0, s, p);
-  }
+  hipLaunchKernelGGL(qprep_kernel, dim3(p.B * p.Hq), dim3(kThreads), dyn, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   const size_t dyn = p.vspectral ? (size_t)p.d * p.d * sizeof(float) : 0;  // the SPECTRAL basis (d <= 128)
-  // Sketched values at large d: 4 queries share each read of S.
-  if (p.vqjl && !p.vspectral && p.d >= kQskMinD)
-    hipLaunchKernelGGL((combine_kernel<4>), dim3((p.nq + 3) / 4), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL((combine_kernel<1>), dim3(p.nq), dim3(kThreads), dyn, s, p);
+  hipLaunchKernelGGL(combine_kernel, dim3(p.nq), dim3(kThreads), dyn, s, p);
   return hipGetLastError();
 }
 
