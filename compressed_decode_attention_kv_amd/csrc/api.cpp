@@ -282,7 +282,8 @@ struct DecodePlan {
   int nparts;  // partials per query: nsplit, times the waves per block at d > 128 (table-driven)
   bool lut;
   bool mq;     // grouped-query matrix-core decode (units: KV head x block of 16 queries x chunk)
-  size_t off_qrot, off_qsk, off_qw, off_part, off_qraw, off_qoff, bytes;
+  size_t off_qrot, off_qsk, off_qw, off_part, off_qraw, off_qoff, off_comb, bytes;
+  bool comb;   // split combine (large d, sketched values): three [nq][d] float arrays at off_comb
 };
 
 tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_qraw, DecodePlan* pl) {
@@ -350,6 +351,8 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   pl->off_qraw = off; off = round_up(off + (with_qraw ? (size_t)nq * d * 4 : 0), 256);
   pl->off_qoff = off; off = round_up(off + (k->mode == TQ_MODE_SPECTRAL ? (size_t)nq * 4 : 0), 256);
   pl->off_part = off; off = round_up(off + (v ? (size_t)nq * pl->nparts * pl->part_stride * 4 : 0), 256);
+  pl->comb = vq && combine_splits(d, true, v->mode == TQ_MODE_SPECTRAL);
+  pl->off_comb = off; off = round_up(off + (pl->comb ? 3 * (size_t)nq * d * 4 : 0), 256);
   pl->bytes = off;
   return TQ_OK;
 }
@@ -824,6 +827,11 @@ tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_pack
     cp.vbasis = v->basis; cp.vmean = v->mean; cp.vscale = v->scale;
   }
   cp.qoff = dp.qoff;
+  if (pl.comb) {
+    float* cw = reinterpret_cast<float*>(w + pl.off_comb);
+    const size_t n = (size_t)cp.nq * k->d;
+    cp.ow = cw; cp.kw = cw + n; cp.add = cw + 2 * n;
+  }
 
   bool supported = true;
   if (tq_status s = hip_status(launch_qprep(qp, st), "query prep launch")) return s;

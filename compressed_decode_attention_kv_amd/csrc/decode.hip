@@ -51,6 +51,11 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
+// From this head dimension on, S q of sketched keys and S^T acc_sk of
+// sketched values run as one tiled product over all queries (sproj_kernel)
+// instead of once per query block: S is d^2 floats (4 MB at d = 1024).
+constexpr int kBigD = 512;
+
 // ---- query preparation -------------------------------------------------------
 // q_rot = Pi q (rotated keys) or q; q_sk = S q_rot (QJL keys); q_w = U_h^T q
 // (HeadQ keys).  One block per query.
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(QPrepParams p) {
   for (int i = threadIdx.x; i < d; i += blockDim.x) p.qrot[(size_t)qi * d + i] = s_r[i];
   if (p.qraw)
     for (int i = threadIdx.x; i < d; i += blockDim.x) p.qraw[(size_t)qi * d + i] = s_q[i];
-  if (p.kqjl) {
+  if (p.kqjl && d < kBigD) {
     for (int i = threadIdx.x; i < d; i += blockDim.x) {
       const float* srow = p.S + (size_t)i * d;
       float acc = 0.f;
@@ -324,6 +329,61 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   if (threadIdx.x == 0) { out[0] = M; out[1] = lt; }
 }
 
+// ---- S x and S^T x for many queries (d >= kBigD) ---------------------------------
+// Y[q][i] = sum_k M(i, k) X[q][k], M = S (trans = 0) or S^T (trans = 1), k
+// ascending: the fma sequence of the per-query loops, so the result is the
+// same bit for bit.  Block: 16 queries x 64 outputs, thread (query tq, outputs
+// 4 ti .. 4 ti + 3); K in steps of 32 through LDS, the next step's tiles
+// loaded into registers while the current ones are used.
+__global__ __launch_bounds__(kThreads) void sproj_kernel(SProjParams p) {
+  __shared__ float Xs[16][33];
+  __shared__ __attribute__((aligned(16))) float Ms[32][68];
+  const int d = p.d, q0 = blockIdx.x * 16, i0 = blockIdx.y * 64;
+  const int tq = threadIdx.x >> 4, ti = threadIdx.x & 15;
+  float xr[2], mr[8];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int e = threadIdx.x + kThreads * n, q = e >> 5, k = e & 31;
+      xr[n] = q0 + q < p.nq ? p.X[(size_t)(q0 + q) * d + k0 + k] : 0.f;
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int e = threadIdx.x + kThreads * n;
+      mr[n] = p.trans ? p.S[(size_t)(k0 + (e >> 6)) * d + i0 + (e & 63)] : p.S[(size_t)(i0 + (e >> 5)) * d + k0 + (e & 31)];
+    }
+  };
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  load(0);
+  for (int k0 = 0; k0 < d; k0 += 32) {
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int e = threadIdx.x + kThreads * n;
+      Xs[e >> 5][e & 31] = xr[n];
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int e = threadIdx.x + kThreads * n;
+      if (p.trans) Ms[e >> 6][e & 63] = mr[n];
+      else Ms[e & 31][e >> 5] = mr[n];
+    }
+    __syncthreads();
+    if (k0 + 32 < d) load(k0 + 32);
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const float x = Xs[tq][k];
+      const float4 m = *reinterpret_cast<const float4*>(&Ms[k][4 * ti]);
+      acc[0] = fmaf(m.x, x, acc[0]);
+      acc[1] = fmaf(m.y, x, acc[1]);
+      acc[2] = fmaf(m.z, x, acc[2]);
+      acc[3] = fmaf(m.w, x, acc[3]);
+    }
+  }
+  if (q0 + tq < p.nq)
+    *reinterpret_cast<float4*>(p.Y + (size_t)(q0 + tq) * d + i0 + 4 * ti) = float4{acc[0], acc[1], acc[2], acc[3]};
+}
+
 // ---- combine + finalize --------------------------------------------------------
 // LSE-merge of the splits, then out = Pi^T (acc/l + a S^T ask / l) (rotated V),
 // mu + V (s * acc / l) (SPECTRAL V) or acc / l (plain V).  One block per query;
@@ -335,6 +395,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   __shared__ float s_red[kThreads / 64];
   const int qi = blockIdx.x, d = p.d;
   const float* part = p.part + (size_t)qi * p.nsplit * p.part_stride;
+  // Stage 2 of a split combine: o + a S^T k from the workspace, then Pi^T.
+  if (p.stage == 2) {
+    for (int i = threadIdx.x; i < d; i += blockDim.x)
+      s_o[i] = fmaf(p.v_qjl, p.add[(size_t)qi * d + i], p.ow[(size_t)qi * d + i]);
+    __syncthreads();
+  } else {
   {
     const int sp = threadIdx.x;  // nsplit <= 256 = kThreads
     const float ms = sp < p.nsplit ? part[(size_t)sp * p.part_stride] : -INFINITY;
@@ -358,6 +424,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     s_k[i] = k * invl;
   }
   __syncthreads();
+  if (p.stage == 1) {
+    // Stage 1 of a split combine: o = acc / l and k = acc_sk / l to the
+    // workspace (S^T k follows for all queries at once), and the LSE.
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+      p.ow[(size_t)qi * d + i] = s_o[i];
+      p.kw[(size_t)qi * d + i] = s_k[i];
+    }
+    if (threadIdx.x == 0 && p.lse)
+      p.lse[qi] = s_L > 0.f ? (s_M + log2f(s_L)) * 0.69314718055994530942f + (p.qoff ? p.qoff[qi] : 0.f) : -INFINITY;
+    return;
+  }
   if (p.vqjl) {
     float add[kMaxD / kThreads];
     for (int c = 0; c < d / (int)blockDim.x + 1; ++c) {
@@ -404,6 +481,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     for (int i = threadIdx.x; i < d; i += blockDim.x) s_o[i] = s_L > 0.f ? s_w[i] : 0.f;
     __syncthreads();
   }
+  }  // stage 0 / 1
   if (p.vrotate) {
     for (int h = 1; h < d; h <<= 1) {
       for (int i = threadIdx.x; i < d / 2; i += blockDim.x) {
@@ -421,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     __syncthreads();
   }
   for (int i = threadIdx.x; i < d; i += blockDim.x) p.out[(size_t)qi * d + i] = s_o[i];
-  if (threadIdx.x == 0 && p.lse)
+  if (p.stage == 0 && threadIdx.x == 0 && p.lse)
     p.lse[qi] = s_L > 0.f ? (s_M + log2f(s_L)) * 0.69314718055994530942f + (p.qoff ? p.qoff[qi] : 0.f) : -INFINITY;
 }
 
@@ -627,15 +705,41 @@ hipError_t launch_ms(const MetricScoreParams& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_qprep(const QPrepParams& p, hipStream_t s) {
-  const size_t dyn = p.kspectral ? (size_t)p.d * p.d * sizeof(float) : 0;  // the SPECTRAL basis (d <= 128)
-  hipLaunchKernelGGL(qprep_kernel, dim3(p.B * p.Hq), dim3(kThreads), dyn, s, p);
+hipError_t launch_sproj(const SProjParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(sproj_kernel, dim3((p.nq + 15) / 16, p.d / 64), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
+hipError_t launch_qprep(const QPrepParams& p, hipStream_t s) {
+  const size_t dyn = p.kspectral ? (size_t)p.d * p.d * sizeof(float) : 0;  // the SPECTRAL basis (d <= 128)
+  hipLaunchKernelGGL(qprep_kernel, dim3(p.B * p.Hq), dim3(kThreads), dyn, s, p);
+  if (p.kqjl && p.d >= kBigD) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_sproj(SProjParams{p.S, p.qrot, p.qsk, p.B * p.Hq, p.d, 0}, s);
+  }
+  return hipGetLastError();
+}
+
+bool combine_splits(int d, bool vqjl, bool vspectral) { return vqjl && !vspectral && d >= kBigD; }
+
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   const size_t dyn = p.vspectral ? (size_t)p.d * p.d * sizeof(float) : 0;  // the SPECTRAL basis (d <= 128)
-  hipLaunchKernelGGL(combine_kernel, dim3(p.nq), dim3(kThreads), dyn, s, p);
+  if (combine_splits(p.d, p.vqjl, p.vspectral) && p.ow && p.kw && p.add) {
+    CombineParams c = p;
+    c.stage = 1;
+    hipLaunchKernelGGL(combine_kernel, dim3(p.nq), dim3(kThreads), 0, s, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_sproj(SProjParams{p.S, p.kw, p.add, p.nq, p.d, 1}, s);
+    if (e != hipSuccess) return e;
+    c.stage = 2;
+    hipLaunchKernelGGL(combine_kernel, dim3(p.nq), dim3(kThreads), 0, s, c);
+    return hipGetLastError();
+  }
+  CombineParams c = p;
+  c.stage = 0;
+  hipLaunchKernelGGL(combine_kernel, dim3(p.nq), dim3(kThreads), dyn, s, c);
   return hipGetLastError();
 }
 

@@ -128,6 +128,18 @@ struct CombineParams {
   const float* vbasis; const float* vmean; const float* vscale;
   // SPECTRAL keys: the per-query score offset added to the log-sum-exp.
   const float* qoff;
+  // Large d with sketched values (combine_splits): workspace for o = acc / l,
+  // k = acc_sk / l and S^T k, [nq][d] floats each; the combine then runs as
+  // merge (stage 1), one S^T product over all queries, finalize (stage 2).
+  // NULL: one pass (stage 0).  `stage` is set by launch_combine.
+  float* ow; float* kw; float* add;
+  int stage;
+};
+
+// Y[q][i] = sum_k M(i, k) X[q][k] for nq queries, M = S (trans = 0) or S^T.
+struct SProjParams {
+  const float* S; const float* X; float* Y;
+  int nq, d, trans;
 };
 
 struct MetricScoreParams {
@@ -197,6 +209,9 @@ hipError_t launch_qprep(const QPrepParams& p, hipStream_t s);
 hipError_t launch_decode_split(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl,
                                hipStream_t s, bool* supported);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+// Whether the combine of a decode with these values takes the split form
+// (its workspace then holds three [nq][d] float arrays).
+bool combine_splits(int d, bool vqjl, bool vspectral);
 // Table-driven decode (3/4-bit codes at d = 128), persistent blocks.
 bool lut_supported(int d, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl);
 // Waves per block of the table-driven kernel (at d > 128 each wave writes its
