@@ -732,7 +732,8 @@ tq_status quantize_core(const tq_tensor_desc* x, int mode, int bits, uint64_t se
     else status = hip_status(launch_quantize_sketch(p, grid, st), "quantize launch");
   } else {
     p.bh0 = 0; p.nbh = x->B * x->H; p.t0 = 0; p.tn = x->T;
-    status = hip_status(launch_quantize(p, st), "quantize launch");
+    const bool have_grid = quant_grid(x->d, bits, &grid);
+    status = hip_status(launch_quantize(p, have_grid ? &grid : nullptr, st), "quantize launch");
   }
   if (rb) (void)hipFreeAsync(rb, st);
   if (status != TQ_OK) return status;

@@ -186,7 +186,9 @@ struct RelErrParams {
 };
 
 // ---- launchers (defined in the .hip files) --------------------------------
-hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+// grid: the index-search table's grid (NULL or too many cells: every
+// boundary is compared instead).
+hipError_t launch_quantize(const QuantParams& p, const QuantGrid* grid, hipStream_t s);
 // SPECTRAL at d = 32, 64, 128 (quant_spectral.hip) and its reconstruction error.
 int spectral_max_d();
 // d = 128 takes the matrix-core kernel with certified decisions when `grid`

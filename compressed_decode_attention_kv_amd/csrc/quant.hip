@@ -112,9 +112,20 @@ __device__ __forceinline__ void headq_side(const QuantParams& p, const float* v,
   }
 }
 
+// Grid lookup of the Lloyd-Max index (as in the matrix-core quantisers):
+// cell n = round(y * scale) + center holds the boundary inside the cell's
+// window (+inf if none) and the number of boundaries below it, so the index
+// is base + [y >= t], the same count as comparing y with every boundary.
+struct QLut {
+  float t;
+  uint32_t base;
+};
+constexpr int kQLutMax = 1024;
+
 template <int BITS, int MODE, typename TIN>
-__global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
+__global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p, QuantGrid grid) {
   __shared__ float s_cent[16], s_bnd[16];
+  __shared__ __attribute__((aligned(8))) QLut s_lut[kQLutMax];
   // Dynamic LDS (sized at launch).  HEADQ: (Pi U_h)^T, d * rank floats.
   // PROD: each wave's token residuals, 64 / L tokens x d floats per wave.
   extern __shared__ float s_side[];
@@ -129,6 +140,24 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
     s_cent[threadIdx.x] = p.centroids[threadIdx.x];
     s_bnd[threadIdx.x] = p.bounds[threadIdx.x];
   }
+  constexpr int NB = (1 << BITS) - 1;
+  // grid.cells == 0: no table (every boundary compared instead).
+  for (int n = threadIdx.x; n < grid.cells; n += blockDim.x) {
+    const float lo = ((float)n - (0.5f + kGridMargin) - (float)grid.center) / grid.scale;
+    const float hi = ((float)n + (0.5f + kGridMargin) - (float)grid.center) / grid.scale;
+    uint32_t base = 0;
+    float t = INFINITY;
+    for (int k = 0; k < NB; ++k) {
+      const float bk = p.bounds[k];
+      if (bk < lo) base++;
+      else if (bk < hi && t == INFINITY) t = bk;
+    }
+    s_lut[n].t = t;
+    s_lut[n].base = base;
+  }
+  // 1.5 * 2^23 + center: fma(y, scale, bias) holds round(y * scale) + center
+  // in its low mantissa bits.
+  const float gbias = 12582912.0f + (float)grid.center;
   if (MODE == TQ_MODE_HEADQ) {
     // (Pi U_h)^T, [rank][d], computed once per head by rotate_basis_kernel.
     const float* src = p.rbasis + (size_t)h * d * p.rank;
@@ -136,7 +165,6 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   }
   __syncthreads();
 
-  constexpr int NB = (1 << BITS) - 1;
   const uint32_t myword = p.signbits[j];
   const TIN* xbase = reinterpret_cast<const TIN*>(p.x) + (int64_t)b * p.sb + (int64_t)h * p.sh;
   const int64_t vbase = (int64_t)bh * p.T_cap;
@@ -164,13 +192,28 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
       inv = nu > 0.f ? p.inv_sqrt_d / nu : 0.f;
     }
     uint32_t idx[32];
+    if (grid.cells > 0) {
+      // All table reads of the lane issued before any is used.
+      QLut ent[32];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      v[e] *= inv;  // y: the rotated unit vector
-      uint32_t c = 0;
+      for (int e = 0; e < 32; ++e) {
+        v[e] *= inv;  // y: the rotated unit vector
+        ent[e] = s_lut[__float_as_uint(fmaf(v[e], grid.scale, gbias)) - 0x4B400000u];
+      }
 #pragma unroll
-      for (int k = 0; k < NB; ++k) c += (v[e] >= s_bnd[k]) ? 1u : 0u;
-      idx[e] = nu > 0.f ? c : 0u;
+      for (int e = 0; e < 32; ++e) {
+        const uint32_t c = ent[e].base + (v[e] >= ent[e].t ? 1u : 0u);
+        idx[e] = nu > 0.f ? c : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        v[e] *= inv;
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) c += (v[e] >= s_bnd[k]) ? 1u : 0u;
+        idx[e] = nu > 0.f ? c : 0u;
+      }
     }
     // PROD: (BITS+1)-bit fields; the sketch signs are added below.
     constexpr int FB = Field<BITS, MODE == TQ_MODE_PROD>::kBits;
@@ -369,15 +412,15 @@ __global__ __launch_bounds__(kThreads) void rotate_basis_kernel(QuantParams p, f
 }
 
 template <int BITS, int MODE>
-hipError_t launch_q(const QuantParams& p, hipStream_t s) {
+hipError_t launch_q(const QuantParams& p, const QuantGrid& g, hipStream_t s) {
   const int vpw = 64 / p.L;
   dim3 grid((p.tn + 4 * vpw * kSteps - 1) / (4 * vpw * kSteps), p.nbh);
   const size_t dyn = MODE == TQ_MODE_HEADQ ? (size_t)p.d * p.rank * sizeof(float)
                     : MODE == TQ_MODE_PROD ? (size_t)(kThreads / 64) * vpw * p.d * sizeof(float) : 0;
   if (p.dtype == TQ_F16)
-    hipLaunchKernelGGL((quant_kernel<BITS, MODE, _Float16>), grid, dim3(kThreads), dyn, s, p);
+    hipLaunchKernelGGL((quant_kernel<BITS, MODE, _Float16>), grid, dim3(kThreads), dyn, s, p, g);
   else
-    hipLaunchKernelGGL((quant_kernel<BITS, MODE, float>), grid, dim3(kThreads), dyn, s, p);
+    hipLaunchKernelGGL((quant_kernel<BITS, MODE, float>), grid, dim3(kThreads), dyn, s, p, g);
   return hipGetLastError();
 }
 
@@ -399,22 +442,24 @@ int relerr_blocks(int T, int L, int BH) {
   return ((T + 4 * vpw * kSteps - 1) / (4 * vpw * kSteps)) * BH;
 }
 
-hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
+hipError_t launch_quantize(const QuantParams& p, const QuantGrid* grid, hipStream_t s) {
+  QuantGrid g{0.f, 0, 0};
+  if (grid && grid->cells <= kQLutMax) g = *grid;
   switch (p.mode) {
     case TQ_MODE_PLAIN:
-      switch (p.bits) { case 1: return launch_q<1, TQ_MODE_PLAIN>(p, s); case 2: return launch_q<2, TQ_MODE_PLAIN>(p, s);
-                        case 3: return launch_q<3, TQ_MODE_PLAIN>(p, s); case 4: return launch_q<4, TQ_MODE_PLAIN>(p, s); }
+      switch (p.bits) { case 1: return launch_q<1, TQ_MODE_PLAIN>(p, g, s); case 2: return launch_q<2, TQ_MODE_PLAIN>(p, g, s);
+                        case 3: return launch_q<3, TQ_MODE_PLAIN>(p, g, s); case 4: return launch_q<4, TQ_MODE_PLAIN>(p, g, s); }
       break;
     case TQ_MODE_MSE:
-      switch (p.bits) { case 1: return launch_q<1, TQ_MODE_MSE>(p, s); case 2: return launch_q<2, TQ_MODE_MSE>(p, s);
-                        case 3: return launch_q<3, TQ_MODE_MSE>(p, s); case 4: return launch_q<4, TQ_MODE_MSE>(p, s); }
+      switch (p.bits) { case 1: return launch_q<1, TQ_MODE_MSE>(p, g, s); case 2: return launch_q<2, TQ_MODE_MSE>(p, g, s);
+                        case 3: return launch_q<3, TQ_MODE_MSE>(p, g, s); case 4: return launch_q<4, TQ_MODE_MSE>(p, g, s); }
       break;
     case TQ_MODE_PROD:
-      switch (p.bits) { case 1: return launch_q<1, TQ_MODE_PROD>(p, s); case 2: return launch_q<2, TQ_MODE_PROD>(p, s);
-                        case 3: return launch_q<3, TQ_MODE_PROD>(p, s); }
+      switch (p.bits) { case 1: return launch_q<1, TQ_MODE_PROD>(p, g, s); case 2: return launch_q<2, TQ_MODE_PROD>(p, g, s);
+                        case 3: return launch_q<3, TQ_MODE_PROD>(p, g, s); }
       break;
     case TQ_MODE_HEADQ:
-      if (p.bits == 2) return launch_q<2, TQ_MODE_HEADQ>(p, s);
+      if (p.bits == 2) return launch_q<2, TQ_MODE_HEADQ>(p, g, s);
       break;
   }
   return hipErrorInvalidValue;
