@@ -333,45 +333,49 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 // Y[q][i] = sum_k M(i, k) X[q][k], M = S (trans = 0) or S^T (trans = 1), k
 // ascending: the fma sequence of the per-query loops, so the result is the
 // same bit for bit.  Block: 16 queries x 64 outputs, thread (query tq, outputs
-// 4 ti .. 4 ti + 3); K in steps of 32 through LDS, the next step's tiles
-// loaded into registers while the current ones are used.
+// 4 ti .. 4 ti + 3); K in steps of 128 through LDS, the next step's tiles
+// loaded into registers while the current ones are used (a step's work
+// covers the L2 latency of the next one's loads).
+constexpr int kSpK = 128;
 __global__ __launch_bounds__(kThreads) void sproj_kernel(SProjParams p) {
-  __shared__ float Xs[16][33];
-  __shared__ __attribute__((aligned(16))) float Ms[32][68];
+  __shared__ float Xs[16][kSpK + 4];
+  __shared__ __attribute__((aligned(16))) float Ms[kSpK][68];
   const int d = p.d, q0 = blockIdx.x * 16, i0 = blockIdx.y * 64;
   const int tq = threadIdx.x >> 4, ti = threadIdx.x & 15;
-  float xr[2], mr[8];
+  constexpr int NX = 16 * kSpK / kThreads, NM = 64 * kSpK / kThreads;
+  float xr[NX], mr[NM];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int e = threadIdx.x + kThreads * n, q = e >> 5, k = e & 31;
+    for (int n = 0; n < NX; ++n) {
+      const int e = threadIdx.x + kThreads * n, q = e / kSpK, k = e % kSpK;
       xr[n] = q0 + q < p.nq ? p.X[(size_t)(q0 + q) * d + k0 + k] : 0.f;
     }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int n = 0; n < NM; ++n) {
       const int e = threadIdx.x + kThreads * n;
-      mr[n] = p.trans ? p.S[(size_t)(k0 + (e >> 6)) * d + i0 + (e & 63)] : p.S[(size_t)(i0 + (e >> 5)) * d + k0 + (e & 31)];
+      mr[n] = p.trans ? p.S[(size_t)(k0 + (e >> 6)) * d + i0 + (e & 63)]
+                      : p.S[(size_t)(i0 + e / kSpK) * d + k0 + e % kSpK];
     }
   };
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   load(0);
-  for (int k0 = 0; k0 < d; k0 += 32) {
+  for (int k0 = 0; k0 < d; k0 += kSpK) {
     __syncthreads();
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int n = 0; n < NX; ++n) {
       const int e = threadIdx.x + kThreads * n;
-      Xs[e >> 5][e & 31] = xr[n];
+      Xs[e / kSpK][e % kSpK] = xr[n];
     }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int n = 0; n < NM; ++n) {
       const int e = threadIdx.x + kThreads * n;
       if (p.trans) Ms[e >> 6][e & 63] = mr[n];
-      else Ms[e & 31][e >> 5] = mr[n];
+      else Ms[e % kSpK][e / kSpK] = mr[n];
     }
     __syncthreads();
-    if (k0 + 32 < d) load(k0 + 32);
+    if (k0 + kSpK < d) load(k0 + kSpK);
 #pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
+    for (int k = 0; k < kSpK; ++k) {
       const float x = Xs[tq][k];
       const float4 m = *reinterpret_cast<const float4*>(&Ms[k][4 * ti]);
       acc[0] = fmaf(m.x, x, acc[0]);
