@@ -21,13 +21,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(PKG, "..", "include")]
 # Per-source extras.  The matrix-core results of the quantisers are read by
-# vector code right away: keep them in ordinary VGPRs (no accumulator-register
-# copies).  The table-driven decode is scheduled for instruction-level
+# vector code right away, and the grouped-query decode rescales its value sums
+# on a rare branch: keep them in ordinary VGPRs (in accumulator registers the
+# grouped-query loop copied all 32 value sums out and back every step).  The table-driven decode is scheduled for instruction-level
 # parallelism (max ILP): at its register budget the default occupancy-first
 # scheduler waits for each LDS table read before issuing the next; the
 # iterative-ILP strategy measured equal or up to 1.5 % slower.
 EXTRA = {"quant_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "quant_spectral.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_mq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "decode_lut.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 

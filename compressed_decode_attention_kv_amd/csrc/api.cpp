@@ -303,9 +303,11 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   // indices and 32-bit byte offsets (at most d/2 code bytes per token),
   // hence the T_cap bounds.
   // Several query heads per KV head: the grouped-query kernel reads each
-  // token once per block of 16 of them.
-  const bool mq = v && mq_supported(d, G, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, k->side_rank,
-                                    k->side_bits, v->bits, v->mode == TQ_MODE_PROD);
+  // token once per block of 16 of them, through buffer descriptors of at most
+  // 2^32 bytes per head plane (at most d/2 code bytes per token).
+  const bool mq = v && (long)k->T_cap * (d / 2) < (1L << 32) &&
+                  mq_supported(d, G, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, k->side_rank,
+                               k->side_bits, v->bits, v->mode == TQ_MODE_PROD);
   const bool lut = !mq && v && k->T_cap <= (1 << 24) && (long)k->T_cap * (d / 2) < (1L << 32) &&
                    lut_supported(d, k->bits, k->mode == TQ_MODE_PROD, k->mode == TQ_MODE_HEADQ, k->side_rank,
                                  k->side_bits, v->bits, v->mode == TQ_MODE_PROD);

@@ -28,11 +28,17 @@
 //     product's second operand), value weights 2^(s + log2 nu_v - M) in fp16
 //     against a running frame M of their own (lazy rescale, weights in
 //     (0, 2^8]) so no norm can overflow them;
-//   * values: the token's centroids go to an LDS tile row by row and come
-//     back transposed as the first operand of eight v_mfma_f32_16x16x16_f16
-//     (16 coordinates x 16 tokens each) against the weights; sketched values
-//     also send their signs through a second tile against the weights times
-//     gamma_v (the sums the combine step turns into S^T acc_sk).
+//   * values: eight v_mfma_f32_16x16x16_f16 against the weights, product j
+//     taking coordinate 8 m + j of the wave's 128 in row m: lane (h, m) reads
+//     the fields of coordinates 8 m .. 8 m + 7 of tokens 4 h .. 4 h + 3 (one
+//     load per token) and looks their centroids up by pairs (or quads) of
+//     tokens, so the operand arrives already in the token-major slots the
+//     product needs; sketched values also look up their signs, against the
+//     weights times gamma_v (the sums the combine step turns into S^T acc_sk).
+// Each lookup is one LDS read per table part at entry * stride + copy offset;
+// the step's planes are read through buffer descriptors that end at the
+// chunk's last token, so the tail of a chunk needs no clamps (reads past it
+// return 0: finite centroids, zero norms, zero weights).
 // Key centroids, queries and the HeadQ side weights enter the scores as fp16
 // hi + lo pairs (hi x hi + hi x lo + lo x hi, about 22 bits: in fp16 alone
 // the score error reached ~7e-4 at unit-variance keys); value centroids and
@@ -46,9 +52,10 @@
 namespace tq {
 namespace {
 
-constexpr int kMqRow = 136;               // fp16 per row of a wave's centroid tile (16 B pad)
 constexpr int kMqCopies = 8;              // table copies (lane % 8) against bank conflicts
 constexpr float kMqSlack = 8.0f;          // log2 units
+constexpr int kMqRsrcWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data
+constexpr int kMqNT = 2;                  // buffer load cache policy: non-temporal
 
 // Waves per block: at d = 128 four independent workers; above, one unit's
 // d / 128 waves, each on 128 coordinates.
@@ -61,135 +68,157 @@ typedef float mq_float4 __attribute__((ext_vector_type(4)));
 typedef uint32_t mq_u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t mq_u32x2 __attribute__((ext_vector_type(2)));
 
-// Table of one tensor's centroids indexed by a packed unit: a byte of two
-// 4-bit fields (half2; with a sketch the fields are 3-bit code | sign << 3
-// and the sign bit is masked off), a byte of four 2-bit codes (half4) or a
-// 6-bit field of two 3-bit codes (half2).  With SPLIT (keys) each entry holds
-// the fp16 hi parts followed by the lo parts (c - hi).
-// W is the field width in the packed words (B, or 4 for a sketched 3-bit code).
-template <int W, bool SPLIT>
+// Table of one tensor's centroids indexed by a unit of W-bit fields, the first
+// field in the lowest bits and the first slot: two 4-bit fields (half2; with a
+// sketch a field is 3-bit code | sign << 3 and the code is taken), two 3-bit
+// fields (a 6-bit index, half2) or four 2-bit fields (half4).  Each entry sits
+// in kMqCopies copies, copy = lane % kMqCopies, against bank conflicts.  Up to
+// three parts share one indexing: keys hold the fp16 hi parts of the
+// centroids, the lo parts (c - hi) and, with a sketch, the signs (bit 3 of
+// each field) as fp16 +-1 (+1 for a set bit); values the centroids and, with
+// a sketch, the signs.
+template <int W, int PARTS>
 struct MqTab {
   static constexpr int entries = W == 3 ? 64 : 256;
-  static constexpr int bytes_per = (W == 2 ? 8 : 4) * (SPLIT ? 2 : 1);
-  static constexpr int bytes = entries * kMqCopies * bytes_per;
+  static constexpr int bytes_per = W == 2 ? 8 : 4;        // one copy of one part of an entry
+  static constexpr int stride = kMqCopies * bytes_per;    // bytes between entries
+  // Parts lie 16 B further apart than their size: no multiple of 256 B and
+  // more than 2 KB, so reads of two parts at one index never merge into one
+  // wider LDS read (whose halves would then be moved apart into two operands).
+  static constexpr int part = entries * stride + 16;
+  static constexpr int bytes = PARTS * part;
 };
 
-template <int W, bool SPLIT>
+template <int W, int PARTS, bool LO, bool SIGNS, bool MASK>
 __device__ __forceinline__ void build_tab(char* tab, const float* c, int tid, int nthreads) {
-  constexpr int N = W == 2 ? 4 : 2;               // centroids per entry
-  for (int i = tid; i < MqTab<W, SPLIT>::entries * kMqCopies; i += nthreads) {
+  using Tab = MqTab<W, PARTS>;
+  constexpr int N = W == 2 ? 4 : 2;               // fields per entry
+  for (int i = tid; i < Tab::entries * kMqCopies; i += nthreads) {
     const int e = i / kMqCopies;
-    _Float16 h[2 * N];
+    _Float16* d0 = reinterpret_cast<_Float16*>(tab + i * Tab::bytes_per);
 #pragma unroll
     for (int q = 0; q < N; ++q) {
-      // 4-bit fields: the low 3 bits are the code when a sketch sign sits in bit 3
-      // (codes of a 4-bit index never exceed 15, so masking with 15 is the identity).
-      const int code = W == 2 ? (e >> (2 * q)) & 3 : (W == 4 ? (e >> (4 * q)) & 15 : (e >> (3 * q)) & 7);
-      const float v = c[code];
-      h[q] = (_Float16)v;
-      h[N + q] = (_Float16)(v - (float)h[q]);
+      const int f = (e >> (W * q)) & ((1 << W) - 1);
+      const float v = c[MASK ? (f & 7) : f];
+      const _Float16 h = (_Float16)v;
+      d0[q] = h;
+      if constexpr (LO) d0[Tab::part / 2 + q] = (_Float16)(v - (float)h);
+      if constexpr (SIGNS) d0[(LO ? 2 : 1) * Tab::part / 2 + q] = ((f >> 3) & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
     }
-    _Float16* dst = reinterpret_cast<_Float16*>(tab + i * MqTab<W, SPLIT>::bytes_per);
+  }
+}
+
+__device__ __forceinline__ uint32_t mq_bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+// Part P of the entry at byte offset a (entry * stride + the lane's copy offset).
+template <int W, int PARTS, int P>
+__device__ __forceinline__ auto mq_ent(const char* tab, uint32_t a) {
+  if constexpr (W == 2) return *reinterpret_cast<const mq_half4*>(tab + P * MqTab<W, PARTS>::part + a);
+  else return *reinterpret_cast<const mq_half2*>(tab + P * MqTab<W, PARTS>::part + a);
+}
+
+// Key operands of coordinates 8 ks .. 8 ks + 7 of the lane's 32 (its words w,
+// LSB-first W-bit fields): hi parts, lo parts and, with a sketch, the signs.
+template <int W, int PARTS, bool SIGNS>
+__device__ __forceinline__ void key8(const char* tab, const uint32_t* w, int ks, uint32_t cofs, mq_half8& ah,
+                                     mq_half8& al, mq_half8& as) {
+  constexpr uint32_t S = MqTab<W, PARTS>::stride;
+  if constexpr (W == 2) {
+    const uint32_t x = w[ks >> 1] >> (16 * (ks & 1));
 #pragma unroll
-    for (int q = 0; q < (SPLIT ? 2 * N : N); ++q) dst[q] = h[q];
-  }
-}
-
-// A sketched tensor's 4-bit fields carry the code in bits 0..2: its table
-// entries use c[field & 7].  Built like build_tab<4> over masked codes.
-template <bool SPLIT>
-__device__ __forceinline__ void build_tab_sketched(char* tab, const float* c, int tid, int nthreads) {
-  for (int i = tid; i < 256 * kMqCopies; i += nthreads) {
-    const int e = i / kMqCopies;
-    const float v0 = c[e & 7], v1 = c[(e >> 4) & 7];
-    const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-    _Float16* dst = reinterpret_cast<_Float16*>(tab + i * MqTab<4, SPLIT>::bytes_per);
-    dst[0] = h0;
-    dst[1] = h1;
-    if constexpr (SPLIT) {
-      dst[2] = (_Float16)(v0 - (float)h0);
-      dst[3] = (_Float16)(v1 - (float)h1);
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t a = ((x >> (8 * q)) & 255u) * S + cofs;
+      const mq_half4 h = mq_ent<W, PARTS, 0>(tab, a), l = mq_ent<W, PARTS, 1>(tab, a);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { ah[4 * q + e] = h[e]; al[4 * q + e] = l[e]; }
     }
-  }
-}
-
-// Eight consecutive coordinates 8 k .. 8 k + 7 of a lane's 32, decoded from
-// its words (LSB-first W-bit fields): hi parts in r, lo parts in rl (SPLIT).
-template <int W, bool SPLIT>
-__device__ __forceinline__ void decode8(const char* tab, const uint32_t* w, int k, int copy, mq_half8& r,
-                                        mq_half8& rl) {
-  constexpr int BP = MqTab<W, SPLIT>::bytes_per;
-  if constexpr (W == 4 || W == 3) {
+  } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t f;
       if constexpr (W == 4) {
-        f = (w[k] >> (8 * q)) & 255u;
+        f = (w[ks] >> (8 * q)) & 255u;
       } else {
-        const int bit = 24 * k + 6 * q, wi = bit >> 5, sh = bit & 31;
+        const int bit = 24 * ks + 6 * q, wi = bit >> 5, sh = bit & 31;
         f = w[wi] >> sh;
         if (sh > 26) f |= w[wi + 1] << (32 - sh);
         f &= 63u;
       }
-      const char* ent = tab + (f * kMqCopies + copy) * BP;
-      if constexpr (SPLIT) {
-        const mq_half4 h = *reinterpret_cast<const mq_half4*>(ent);
-        r[2 * q] = h.x; r[2 * q + 1] = h.y;
-        rl[2 * q] = h.z; rl[2 * q + 1] = h.w;
-      } else {
-        const mq_half2 h = *reinterpret_cast<const mq_half2*>(ent);
-        r[2 * q] = h.x; r[2 * q + 1] = h.y;
-      }
-    }
-  } else {
-    const uint32_t x = w[k >> 1] >> (16 * (k & 1));
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const char* ent = tab + (((x >> (8 * q)) & 255u) * kMqCopies + copy) * BP;
-      if constexpr (SPLIT) {
-        const mq_half8 h = *reinterpret_cast<const mq_half8*>(ent);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { r[4 * q + e] = h[e]; rl[4 * q + e] = h[4 + e]; }
-      } else {
-        const mq_half4 h = *reinterpret_cast<const mq_half4*>(ent);
-        r[4 * q] = h.x; r[4 * q + 1] = h.y; r[4 * q + 2] = h.z; r[4 * q + 3] = h.w;
+      const uint32_t a = f * S + cofs;
+      const mq_half2 h = mq_ent<W, PARTS, 0>(tab, a), l = mq_ent<W, PARTS, 1>(tab, a);
+      ah[2 * q] = h.x; ah[2 * q + 1] = h.y;
+      al[2 * q] = l.x; al[2 * q + 1] = l.y;
+      if constexpr (SIGNS) {
+        const mq_half2 s = mq_ent<W, PARTS, 2>(tab, a);
+        as[2 * q] = s.x; as[2 * q + 1] = s.y;
       }
     }
   }
 }
 
-// The sketch signs (bit 3 of each 4-bit field) of coordinates 8 k .. 8 k + 7
-// as fp16 +-1 (+1 for a set bit).
-__device__ __forceinline__ mq_half8 signs8(const uint32_t* w, int k) {
-  mq_half8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = ((w[k] >> (4 * e + 3)) & 1u) ? (_Float16)1.0f : (_Float16)-1.0f;
-  return r;
-}
-
-// W dwords of slice s of a vector with (D * W / 8)-byte code rows.
-template <int D, int W>
-__device__ __forceinline__ void load_words(const uint8_t* plane, size_t vec, int s, uint32_t* w) {
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(plane + vec * (size_t)(D * W / 8)) + W * s;
+// Value fields: vr holds, for each token 4 hq + e of the step, the fields of
+// coordinates 8 mm .. 8 mm + 7 of the wave's 128 (W = 4: a word; W = 2: 16
+// bits; W = 3: the two words that hold its 24 bits, vsh bits into the first).
+// value_index turns them once per step into the table indices of the value
+// products: the pair (tokens 0, 1 | 2, 3) or quad entries of each coordinate.
+template <int W>
+__device__ __forceinline__ void value_index(const uint32_t* vr, uint32_t vsh, uint32_t* ix) {
   if constexpr (W == 4) {
-    const mq_u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const mq_u32x4*>(src));
-    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-  } else if constexpr (W == 2) {
-    const mq_u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const mq_u32x2*>(src));
-    w[0] = x.x; w[1] = x.y;
-  } else {
+    // byte k: field 2 k (ix[0], ix[2]) or 2 k + 1 (ix[1], ix[3]) of the two tokens
+    ix[0] = mq_bfi(0x0F0F0F0Fu, vr[0], vr[1] << 4);
+    ix[1] = mq_bfi(0x0F0F0F0Fu, vr[0] >> 4, vr[1]);
+    ix[2] = mq_bfi(0x0F0F0F0Fu, vr[2], vr[3] << 4);
+    ix[3] = mq_bfi(0x0F0F0F0Fu, vr[2] >> 4, vr[3]);
+  } else if constexpr (W == 3) {
 #pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = __builtin_nontemporal_load(src + i);
+    for (int e = 0; e < 4; ++e) ix[e] = __builtin_amdgcn_alignbit(vr[2 * e + 1], vr[2 * e], vsh);
+  } else {
+    // Nibbles of R: fields 2 i of tokens 0 | 1 (low half) and 2 | 3 (high
+    // half); of S: fields 2 i + 1.  Bytes 0 and 1 of ix[] then pair them up:
+    // ix[0]: fields 0, 4; ix[1]: 2, 6; ix[2]: 1, 5; ix[3]: 3, 7.
+    const uint32_t P = vr[0] | (vr[2] << 16), Q = vr[1] | (vr[3] << 16);
+    const uint32_t R = mq_bfi(0x33333333u, P, Q << 2), S = mq_bfi(0x33333333u, P >> 2, Q);
+    ix[0] = mq_bfi(0x0F0Fu, R, R >> 12);
+    ix[1] = mq_bfi(0x0F0Fu, R >> 4, R >> 16);
+    ix[2] = mq_bfi(0x0F0Fu, S, S >> 12);
+    ix[3] = mq_bfi(0x0F0Fu, S >> 4, S >> 16);
   }
 }
 
-// Four per-token scalars of tokens t .. t + 3 of a head (clamped past the
-// end).  (A branch that skips the clamps away from the end measured slower.)
-__device__ __forceinline__ mq_float4 load_f4(const float* base, int t, int t1) {
-  mq_float4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = base[min(t + i, t1 - 1)];
-  return r;
+// First operand of value product j: coordinate 8 mm + j of tokens 4 hq .. 4 hq
+// + 3 (and, with a sketch, their signs).
+template <int W, int PARTS, bool SIGNS>
+__device__ __forceinline__ void value_ops(const char* tab, const uint32_t* ix, int j, uint32_t cofs, mq_half4& A,
+                                          mq_half4& As) {
+  constexpr uint32_t S = MqTab<W, PARTS>::stride;
+  if constexpr (W == 2) {
+    const uint32_t f = (ix[(j & 1) * 2 + ((j >> 1) & 1)] >> (8 * (j >> 2))) & 255u;
+    A = mq_ent<W, PARTS, 0>(tab, f * S + cofs);
+  } else {
+    uint32_t f01, f23;
+    if constexpr (W == 4) {
+      f01 = (ix[j & 1] >> (8 * (j >> 1))) & 255u;
+      f23 = (ix[2 + (j & 1)] >> (8 * (j >> 1))) & 255u;
+    } else {
+      f01 = ((ix[0] >> (3 * j)) & 7u) | (((ix[1] >> (3 * j)) & 7u) << 3);
+      f23 = ((ix[2] >> (3 * j)) & 7u) | (((ix[3] >> (3 * j)) & 7u) << 3);
+    }
+    const uint32_t a01 = f01 * S + cofs, a23 = f23 * S + cofs;
+    const mq_half2 h01 = mq_ent<W, PARTS, 0>(tab, a01), h23 = mq_ent<W, PARTS, 0>(tab, a23);
+    A = mq_half4{h01.x, h01.y, h23.x, h23.y};
+    if constexpr (SIGNS) {
+      const mq_half2 s01 = mq_ent<W, PARTS, 1>(tab, a01), s23 = mq_ent<W, PARTS, 1>(tab, a23);
+      As = mq_half4{s01.x, s01.y, s23.x, s23.y};
+    }
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mq_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kMqRsrcWord3);
+}
+
+__device__ __forceinline__ float mq_ldf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
 // KB, VB: index bits; KQ, VQ: sketched (4-bit fields, KB = VB = 3); KS: HeadQ
@@ -201,25 +230,31 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
   constexpr int NWU = D / 128;                     // waves per unit
   constexpr int UPB = NW / NWU;                    // units per block (4 at d = 128, else 1)
   constexpr int KW = KQ ? 4 : KB, VW = VQ ? 4 : VB;  // field widths
-  __shared__ __attribute__((aligned(16))) char s_ktab[MqTab<KW, true>::bytes];
-  __shared__ __attribute__((aligned(16))) char s_vtab[MqTab<VW, false>::bytes];
-  __shared__ __attribute__((aligned(16))) _Float16 s_tile[NW][16 * kMqRow];
-  __shared__ __attribute__((aligned(16))) _Float16 s_stile[VQ ? NW : 1][VQ ? 16 * kMqRow : 8];
+  constexpr int KPARTS = KQ ? 3 : 2, VPARTS = VQ ? 2 : 1;
+  constexpr uint32_t RBK = D * KW / 8, RBV = D * VW / 8;  // code bytes per token
+  __shared__ __attribute__((aligned(16))) char s_ktab[MqTab<KW, KPARTS>::bytes];
+  __shared__ __attribute__((aligned(16))) char s_vtab[MqTab<VW, VPARTS>::bytes];
   // Partial scores of the waves of a unit (d > 128), double-buffered by step parity.
   __shared__ __attribute__((aligned(16))) mq_float4 s_red[NWU > 1 ? 2 : 1][NWU > 1 ? NWU : 1][NWU > 1 ? (KQ ? 128 : 64) : 1];
-  if constexpr (KQ) build_tab_sketched<true>(s_ktab, p.kc, threadIdx.x, NT);
-  else build_tab<KW, true>(s_ktab, p.kc, threadIdx.x, NT);
-  if constexpr (VQ) build_tab_sketched<false>(s_vtab, p.vc, threadIdx.x, NT);
-  else build_tab<VW, false>(s_vtab, p.vc, threadIdx.x, NT);
+  build_tab<KW, KPARTS, true, KQ, KQ>(s_ktab, p.kc, threadIdx.x, NT);
+  build_tab<VW, VPARTS, false, VQ, VQ>(s_vtab, p.vc, threadIdx.x, NT);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wu = NWU > 1 ? wave : 0;               // wave within the unit: coordinates 128 wu ..
-  const int slice = 4 * wu;                         // first 32-coordinate slice of the wave
   const int hq = lane >> 4, mm = lane & 15;        // operand / result lane (h, m)
   const int copy = lane & (kMqCopies - 1);
-  _Float16* tile = s_tile[wave];
-  _Float16* stile = s_stile[VQ ? wave : 0];
+  const uint32_t kcofs = copy * MqTab<KW, KPARTS>::bytes_per, vcofs = copy * MqTab<VW, VPARTS>::bytes_per;
+  // Lane offsets within a step: key words of token mm, slice 4 wu + hq (32
+  // coordinates); value fields of coordinates 8 mm .. of the wave's 128, token
+  // 4 hq (+ e rows); per-token scalars of tokens 4 hq .. 4 hq + 3.
+  const uint32_t vk = mm * RBK + 4 * KW * (4 * wu + hq);
+  const uint32_t vj0 = VW == 3 ? (3 * mm) >> 2 : 0;
+  const uint32_t vv = 4 * hq * RBV + 16 * VW * wu + (VW == 4 ? 4 * mm : (VW == 2 ? 2 * mm : 4 * vj0));
+  const uint32_t vv2 = vv + (VW == 3 && vj0 < 11 ? 4 : 0);
+  const uint32_t vsh = VW == 3 ? 8 * ((3 * mm) & 3) : 0;
+  const uint32_t vn = 16 * hq, vsd = 8 * mm + 2 * hq;
   const int nqb = (p.G + 15) >> 4;
   const int R = p.B * p.Hkv * nqb * p.nsplit;
   const int u0 = NWU > 1 ? blockIdx.x : blockIdx.x * UPB + wave;
@@ -236,6 +271,20 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
     const int Tb = p.lens ? min(max(p.lens[b], 0), p.T) : p.T;
     const int t0 = split * p.chunk, t1 = min(Tb, t0 + p.chunk);
     const size_t vbase = (size_t)bkv * p.T_cap;
+    // The head's planes up to token t1: reads of tokens t1 and beyond return 0
+    // (finite centroids, zero norms; their weights are 0).
+    const uint32_t n1 = t1 > 0 ? (uint32_t)t1 : 0u;
+    const __amdgpu_buffer_rsrc_t rk = mq_rsrc(p.k.codes + vbase * RBK, n1 * RBK);
+    const __amdgpu_buffer_rsrc_t rv = mq_rsrc(p.v.codes + vbase * RBV, n1 * RBV);
+    const __amdgpu_buffer_rsrc_t rnk = mq_rsrc(p.k.norms + vbase, 4 * n1);
+    const __amdgpu_buffer_rsrc_t rnv = mq_rsrc(p.v.norms + vbase, 4 * n1);
+    __amdgpu_buffer_rsrc_t rsd = rnk, rsz = rnk, rgk = rnk, rgv = rnk;
+    if constexpr (KS) {
+      rsd = mq_rsrc(p.k.side + vbase * 8, 8 * n1);
+      rsz = mq_rsrc(p.k.side_scale + vbase, 4 * n1);
+    }
+    if constexpr (KQ) rgk = mq_rsrc(p.k.gamma + vbase, 4 * n1);
+    if constexpr (VQ) rgv = mq_rsrc(p.v.gamma + vbase, 4 * n1);
 
     // Queries (second operand of the scores): slots 128 wu + 32 h + 8 ks + e of
     // query g, and the same slots of S q for sketched keys.
@@ -263,40 +312,57 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
         Wl[e] = (_Float16)(v - (float)Wh[e]);
       }
     }
+    // acc[j], ask[j]: rows = coordinate groups m (coordinate 8 m + j), columns = queries.
     mq_float4 acc[8], ask[VQ ? 8 : 1];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) acc[cb] = mq_float4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) acc[j] = mq_float4{0.f, 0.f, 0.f, 0.f};
     if constexpr (VQ) {
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb) ask[cb] = mq_float4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 8; ++j) ask[j] = mq_float4{0.f, 0.f, 0.f, 0.f};
     }
     float m = -INFINITY, l = 0.f;
     constexpr float kNoFrame = -1e30f;
     float M = kNoFrame;
 
-    // One step's loads: this lane's token base + mm (code words of slice
-    // slice + hq, side code) and the per-token scalars of the result rows,
-    // tokens base + 4 hq + i; past the end the token index is clamped (re-reads).
+    // One step's loads (buffer offsets: the step's first token in the scalar
+    // offset, the lane's part in the vector offset).
     struct Step {
-      uint32_t kw[KW], vw[VW], side;
+      uint32_t kw[KW], vr[VW == 3 ? 8 : 4], side;
       mq_float4 nuk, nuv, sz, gk, gv;
     };
     auto load_step = [&](int base, Step& st) {
-      const int tk = min(base + mm, t1 - 1);
-      load_words<D, KW>(p.k.codes, vbase + tk, slice + hq, st.kw);
-      load_words<D, VW>(p.v.codes, vbase + tk, slice + hq, st.vw);
+      const uint32_t sk = (uint32_t)base * RBK, sv = (uint32_t)base * RBV, sn = 4u * (uint32_t)base;
+      if constexpr (KW == 4) {
+        const mq_u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, vk, sk, kMqNT);
+        st.kw[0] = x.x; st.kw[1] = x.y; st.kw[2] = x.z; st.kw[3] = x.w;
+      } else if constexpr (KW == 2) {
+        const mq_u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rk, vk, sk, kMqNT);
+        st.kw[0] = x.x; st.kw[1] = x.y;
+      } else {
+#pragma unroll
+        for (int i = 0; i < KW; ++i) st.kw[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, vk + 4 * i, sk, kMqNT);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (VW == 4) {
+          st.vr[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, vv + e * RBV, sv, kMqNT);
+        } else if constexpr (VW == 2) {
+          st.vr[e] = __builtin_amdgcn_raw_buffer_load_b16(rv, vv + e * RBV, sv, kMqNT);
+        } else {
+          st.vr[2 * e] = __builtin_amdgcn_raw_buffer_load_b32(rv, vv + e * RBV, sv, kMqNT);
+          st.vr[2 * e + 1] = __builtin_amdgcn_raw_buffer_load_b32(rv, vv2 + e * RBV, sv, kMqNT);
+        }
+      }
       st.side = 0;
-      if constexpr (KS)
-        st.side = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p.k.side + (vbase + tk) * 8 + 2 * hq));
-      const int tr = base + 4 * hq;
-      st.nuk = load_f4(p.k.norms + vbase, tr, t1);
-      st.nuv = load_f4(p.v.norms + vbase, tr, t1);
-      st.sz = mq_float4{0.f, 0.f, 0.f, 0.f};
-      st.gk = st.sz;
-      st.gv = st.sz;
-      if constexpr (KS) st.sz = load_f4(p.k.side_scale + vbase, tr, t1);
-      if constexpr (KQ) st.gk = load_f4(p.k.gamma + vbase, tr, t1);
-      if constexpr (VQ) st.gv = load_f4(p.v.gamma + vbase, tr, t1);
+      if constexpr (KS) st.side = __builtin_amdgcn_raw_buffer_load_b16(rsd, vsd, 8u * (uint32_t)base, kMqNT);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st.nuk[i] = mq_ldf(rnk, vn + 4 * i, sn);
+        st.nuv[i] = mq_ldf(rnv, vn + 4 * i, sn);
+        st.sz[i] = KS ? mq_ldf(rsz, vn + 4 * i, sn) : 0.f;
+        st.gk[i] = KQ ? mq_ldf(rgk, vn + 4 * i, sn) : 0.f;
+        st.gv[i] = VQ ? mq_ldf(rgv, vn + 4 * i, sn) : 0.f;
+      }
     };
     Step nxt;
     if (t0 < t1) load_step(t0, nxt);
@@ -311,13 +377,12 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
       mq_float4 S = {0.f, 0.f, 0.f, 0.f}, Sk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        mq_half8 Ah, Al;
-        decode8<KW, true>(s_ktab, cur.kw, ks, copy, Ah, Al);
+        mq_half8 Ah, Al, As;
+        key8<KW, KPARTS, KQ>(s_ktab, cur.kw, ks, kcofs, Ah, Al, As);
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Qh[ks], S, 0, 0, 0);
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Ql[ks], S, 0, 0, 0);
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Qh[ks], S, 0, 0, 0);
         if constexpr (KQ) {
-          const mq_half8 As = signs8(cur.kw, ks);
           Sk = __builtin_amdgcn_mfma_f32_16x16x32_f16(As, Uh[ks], Sk, 0, 0, 0);
           Sk = __builtin_amdgcn_mfma_f32_16x16x32_f16(As, Ul[ks], Sk, 0, 0, 0);
         }
@@ -378,10 +443,10 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
         const bool up = lmax > M + kMqSlack;
         const float f = up ? __builtin_amdgcn_exp2f(M - lmax) : 1.0f;
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) acc[cb] *= f;
+        for (int j = 0; j < 8; ++j) acc[j] *= f;
         if constexpr (VQ) {
 #pragma unroll
-          for (int cb = 0; cb < 8; ++cb) ask[cb] *= f;
+          for (int j = 0; j < 8; ++j) ask[j] *= f;
         }
         M = up ? lmax : M;
       }
@@ -393,34 +458,16 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
         if constexpr (VQ) Wq[i] = (_Float16)(wgt * cur.gv[i]);
       }
 
-      // ---- values: centroids (and signs) to the tiles, rows = tokens --------------------
+      // ---- values: coordinate 8 mm + j of tokens 4 hq .. 4 hq + 3 per product ----------
+      uint32_t ix[4];
+      value_index<VW>(cur.vr, vsh, ix);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        mq_half8 vh, unused;
-        decode8<VW, false>(s_vtab, cur.vw, k, copy, vh, unused);
-        *reinterpret_cast<mq_half8*>(tile + mm * kMqRow + 32 * hq + 8 * k) = vh;
-        if constexpr (VQ) *reinterpret_cast<mq_half8*>(stile + mm * kMqRow + 32 * hq + 8 * k) = signs8(cur.vw, k);
+      for (int j = 0; j < 8; ++j) {
+        mq_half4 A, As;
+        value_ops<VW, VPARTS, VQ>(s_vtab, ix, j, vcofs, A, As);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Wv, acc[j], 0, 0, 0);
+        if constexpr (VQ) ask[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(As, Wq, ask[j], 0, 0, 0);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
-        // First operand: coordinate 16 cb + mm of tokens 4 hq .. 4 hq + 3.
-        mq_half4 A;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) A[e] = tile[(4 * hq + e) * kMqRow + 16 * cb + mm];
-        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Wv, acc[cb], 0, 0, 0);
-        if constexpr (VQ) {
-          mq_half4 As;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) As[e] = stile[(4 * hq + e) * kMqRow + 16 * cb + mm];
-          ask[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(As, Wq, ask[cb], 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     // ---- partial record: [m, l, acc[d] (, ask[d])] in the 2^m frame, query g ----------
@@ -429,13 +476,14 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
     const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - m);
     if (gvalid) {
       float* out = p.part + ((size_t)qi * p.nsplit + split) * p.part_stride;
+      // Result rows 4 hq + i of product j: coordinate 8 (4 hq + i) + j.
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 128 * wu + 16 * cb + 4 * hq + i;
-          out[2 + c] = acc[cb][i] * f;
-          if constexpr (VQ) out[2 + D + c] = ask[cb][i] * f;
+        for (int j = 0; j < 8; ++j) {
+          const int c = 128 * wu + 32 * hq + 8 * i + j;
+          out[2 + c] = acc[j][i] * f;
+          if constexpr (VQ) out[2 + D + c] = ask[j][i] * f;
         }
       if (hq == 0 && wu == 0) { out[0] = m; out[1] = l; }
     }
