@@ -320,9 +320,10 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
 #pragma unroll
       for (int j = 0; j < 8; ++j) ask[j] = mq_float4{0.f, 0.f, 0.f, 0.f};
     }
-    float m = -INFINITY, l = 0.f;
+    // Running score maximum m and value frame M start below every score, so
+    // that 2^(s - m) of a masked token (s = -inf) is 0; c = 2^(m - M).
     constexpr float kNoFrame = -1e30f;
-    float M = kNoFrame;
+    float m = kNoFrame, l = 0.f, M = kNoFrame, c = 1.f;
 
     // One step's loads (buffer offsets: the step's first token in the scalar
     // offset, the lane's part in the vector offset).
@@ -364,13 +365,8 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
         st.gv[i] = VQ ? mq_ldf(rgv, vn + 4 * i, sn) : 0.f;
       }
     };
-    Step nxt;
-    if (t0 < t1) load_step(t0, nxt);
     int parity = 0;
-    for (int base = t0; base < t1; base += 16) {
-      // The next step's loads are in flight while this step computes.
-      const Step cur = nxt;
-      if (base + 16 < t1) load_step(base + 16, nxt);
+    auto step = [&](int base, const Step& cur) __attribute__((always_inline)) {
       const int tr = base + 4 * hq;
 
       // ---- scores (this wave's 128 coordinates) ------------------------------------------
@@ -410,36 +406,49 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
         Ss = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Wl, Ss, 0, 0, 0);
       }
       float s[4];
-      float smax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = S[i];
         if constexpr (KQ) v = fmaf(cur.gk[i] * p.k_qjl, Sk[i], v);
         v *= cur.nuk[i];
         if constexpr (KS) v = fmaf(cur.sz[i], Ss[i], v);
-        v *= p.scale_log2;
-        s[i] = (tr + i < t1) ? v : -INFINITY;
-        smax = fmaxf(smax, s[i]);
+        s[i] = v * p.scale_log2;
       }
+      if (base + 16 > t1) {
+        // The chunk's last step: tokens past its end score -inf.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = tr + i < t1 ? s[i] : -INFINITY;
+      }
+      float smax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
       smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
       if (smax > m + kMqSlack) {
-        l *= __builtin_amdgcn_exp2f(m - smax);      // 0 while m = -inf
+        l *= __builtin_amdgcn_exp2f(m - smax);
         m = smax;
+        c = __builtin_amdgcn_exp2f(m - M);
       }
-      // Weights in the 2^M frame of the value sums (nu_v = 0 or past the end: 0).
-      float lam[4], lmax = -INFINITY;
+      // Value weights 2^(s + log2 nu_v - M) = 2^(s - m) nu_v c, at most 2^8;
+      // past the end or at nu_v = 0 they are 0.
+      float w[4];
+      bool big = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        l += s[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[i] - m);
-        lam[i] = s[i] + __builtin_amdgcn_logf(cur.nuv[i]);
-        lmax = fmaxf(lmax, lam[i]);
+        const float e = __builtin_amdgcn_exp2f(s[i] - m);
+        l += e;
+        w[i] = e * (cur.nuv[i] * c);
+        big |= !(w[i] <= 256.f);
       }
-      lmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
-      lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
-      // Rare (the frame moves only when a weight would exceed 2^8): one
+      // Rare (the first weights, or a weight beyond 2^8 moves the frame): one
       // wave-uniform branch.
-      if (__builtin_amdgcn_ballot_w64(lmax > M + kMqSlack) != 0) {
+      if (__builtin_amdgcn_ballot_w64(big) != 0) {
+        float lam[4], lmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lam[i] = s[i] + __builtin_amdgcn_logf(cur.nuv[i]);
+          lmax = fmaxf(lmax, lam[i]);
+        }
+        lmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+        lmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
         const bool up = lmax > M + kMqSlack;
         const float f = up ? __builtin_amdgcn_exp2f(M - lmax) : 1.0f;
 #pragma unroll
@@ -449,13 +458,15 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
           for (int j = 0; j < 8; ++j) ask[j] *= f;
         }
         M = up ? lmax : M;
+        c = __builtin_amdgcn_exp2f(m - M);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_exp2f(lam[i] - M);
       }
       mq_half4 Wv, Wq;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float wgt = __builtin_amdgcn_exp2f(lam[i] - M);
-        Wv[i] = (_Float16)wgt;
-        if constexpr (VQ) Wq[i] = (_Float16)(wgt * cur.gv[i]);
+        Wv[i] = (_Float16)w[i];
+        if constexpr (VQ) Wq[i] = (_Float16)(w[i] * cur.gv[i]);
       }
 
       // ---- values: coordinate 8 mm + j of tokens 4 hq .. 4 hq + 3 per product ----------
@@ -468,11 +479,21 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Wv, acc[j], 0, 0, 0);
         if constexpr (VQ) ask[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(As, Wq, ask[j], 0, 0, 0);
       }
+    };
+    // The next step's loads are in flight while a step computes (loads two
+    // steps ahead, or two buffers in turn instead of the copy, measured slower).
+    Step nxt;
+    if (t0 < t1) load_step(t0, nxt);
+    for (int base = t0; base < t1; base += 16) {
+      const Step cur = nxt;
+      if (base + 16 < t1) load_step(base + 16, nxt);
+      step(base, cur);
     }
 
     // ---- partial record: [m, l, acc[d] (, ask[d])] in the 2^m frame, query g ----------
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
+    if (m == kNoFrame) m = -INFINITY;             // no token scored
     const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - m);
     if (gvalid) {
       float* out = p.part + ((size_t)qi * p.nsplit + split) * p.part_stride;
