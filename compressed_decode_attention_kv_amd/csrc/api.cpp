@@ -320,9 +320,13 @@ tq_status plan_decode(const tq_packed* k, const tq_packed* v, int Hq, bool with_
   // in flight; the persistent table-driven kernel wants few, long units
   // (about two per CU) because each unit ends with a merge of its token slots;
   // the grouped-query kernel about as many units as fit on the device at once
-  // (d/128 waves each): every unit writes 16 partials of 2 + 2d floats, which
-  // the combine step reads back.
-  const long target = mq ? 4096 / mq_waves_per_unit(d) : (lut ? 512 : 2048);
+  // (d/128 waves each; at d = 128 exactly one round): every unit writes 16
+  // partials of 2 + 2d floats, which the combine step reads back.
+  // (Without a device, e.g. a size query on a host without one: 256 CUs.)
+  int cus = 256;
+  if (mq && (cu_count(&cus) != hipSuccess || cus < 1)) cus = 256;
+  const long target = mq ? mq_target_units(d, k->mode == TQ_MODE_PROD, v->mode == TQ_MODE_PROD, cus)
+                         : (lut ? 512 : 2048);
   int nsplit = (int)std::max<long>(1, (target + groups - 1) / groups);
   int chunk = (k->T + nsplit - 1) / nsplit;
   chunk = std::max(step, (chunk + step - 1) / step * step);
@@ -842,7 +846,7 @@ tq_status decode_core(const tq_tensor_desc* q, const tq_packed* k, const tq_pack
     int cus = 0;
     if (tq_status s = hip_status(cu_count(&cus), "device query")) return s;
     const long units = (long)k->B * k->H * ((pl.G + 15) / 16) * pl.nsplit;
-    const int upb = mq_units_per_block(k->d);
+    const int upb = mq_units_per_block(k->d, kq, vq);
     const long cap = (long)cus * (8 / mq_waves_per_unit(k->d) > 0 ? 8 / mq_waves_per_unit(k->d) : 1) * (k->d == 128 ? 1 : 2);
     const int nblocks = (int)std::max<long>(1, std::min<long>((units + upb - 1) / upb, cap));
     if (tq_status s = hip_status(launch_decode_mq(dp, k->bits, kq, ksd, v->bits, vq, nblocks, st), "decode launch")) return s;

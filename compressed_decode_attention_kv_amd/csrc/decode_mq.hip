@@ -52,14 +52,24 @@
 namespace tq {
 namespace {
 
-constexpr int kMqCopies = 8;              // table copies (lane % 8) against bank conflicts
+// Units (waves) per block at d = 128: one block per CU shares one set of
+// tables, whose copies then fill most of the LDS; 12 waves (3 per SIMD, the
+// register budget of 168), or 8 with a sketch (whose registers exceed it).
+constexpr int mq_upb(int D, bool KQ, bool VQ) { return D == 128 ? (KQ || VQ ? 8 : 12) : 1; }
 constexpr float kMqSlack = 8.0f;          // log2 units
 constexpr int kMqRsrcWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data
 constexpr int kMqNT = 2;                  // buffer load cache policy: non-temporal
 
 // Waves per block: at d = 128 four independent workers; above, one unit's
 // d / 128 waves, each on 128 coordinates.
-constexpr int mq_threads(int D) { return D == 128 ? 256 : 64 * (D / 128); }
+constexpr int mq_threads(int D, bool KQ, bool VQ) { return 64 * (D == 128 ? mq_upb(D, KQ, VQ) : D / 128); }
+
+// LDS budgets of the key and value tables: at d = 128 most of the LDS (one
+// block per CU); at d = 256 and 512 small enough for several blocks per CU; at
+// d = 1024 (one block of 8 waves per CU, by registers) beside the partial
+// scores' 32 KB.
+constexpr int mq_kbudget(int D) { return D == 128 ? 65536 : D == 256 ? 16384 : D == 512 ? 32768 : 65536; }
+constexpr int mq_vbudget(int D) { return D == 128 ? 65536 : D == 256 ? 8192 : D == 512 ? 16384 : 32768; }
 
 typedef _Float16 mq_half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 mq_half4 __attribute__((ext_vector_type(4)));
@@ -72,16 +82,16 @@ typedef uint32_t mq_u32x2 __attribute__((ext_vector_type(2)));
 // field in the lowest bits and the first slot: two 4-bit fields (half2; with a
 // sketch a field is 3-bit code | sign << 3 and the code is taken), two 3-bit
 // fields (a 6-bit index, half2) or four 2-bit fields (half4).  Each entry sits
-// in kMqCopies copies, copy = lane % kMqCopies, against bank conflicts.  Up to
+// in C copies, copy = lane % C, against bank conflicts.  Up to
 // three parts share one indexing: keys hold the fp16 hi parts of the
 // centroids, the lo parts (c - hi) and, with a sketch, the signs (bit 3 of
 // each field) as fp16 +-1 (+1 for a set bit); values the centroids and, with
 // a sketch, the signs.
-template <int W, int PARTS>
+template <int W, int PARTS, int C>
 struct MqTab {
   static constexpr int entries = W == 3 ? 64 : 256;
   static constexpr int bytes_per = W == 2 ? 8 : 4;        // one copy of one part of an entry
-  static constexpr int stride = kMqCopies * bytes_per;    // bytes between entries
+  static constexpr int stride = C * bytes_per;            // bytes between entries
   // Parts lie 16 B further apart than their size: no multiple of 256 B and
   // more than 2 KB, so reads of two parts at one index never merge into one
   // wider LDS read (whose halves would then be moved apart into two operands).
@@ -89,12 +99,22 @@ struct MqTab {
   static constexpr int bytes = PARTS * part;
 };
 
-template <int W, int PARTS, bool LO, bool SIGNS, bool MASK>
+// Copies of a table, copy = lane % copies: the most (a power of two, at most
+// 64) within budget bytes.  At 64 copies every lane of a wave reads its
+// own bank; at 32 two lanes share a bank (a conflict when their entries differ
+// but fall into the same bank), at 8, eight.
+constexpr int mq_copies(int W, int PARTS, int budget) {
+  int c = 64;
+  while (c > 1 && PARTS * (W == 3 ? 64 : 256) * (W == 2 ? 8 : 4) * c > budget) c /= 2;
+  return c;
+}
+
+template <int W, int PARTS, int C, bool LO, bool SIGNS, bool MASK>
 __device__ __forceinline__ void build_tab(char* tab, const float* c, int tid, int nthreads) {
-  using Tab = MqTab<W, PARTS>;
+  using Tab = MqTab<W, PARTS, C>;
   constexpr int N = W == 2 ? 4 : 2;               // fields per entry
-  for (int i = tid; i < Tab::entries * kMqCopies; i += nthreads) {
-    const int e = i / kMqCopies;
+  for (int i = tid; i < Tab::entries * C; i += nthreads) {
+    const int e = i / C;
     _Float16* d0 = reinterpret_cast<_Float16*>(tab + i * Tab::bytes_per);
 #pragma unroll
     for (int q = 0; q < N; ++q) {
@@ -111,24 +131,24 @@ __device__ __forceinline__ void build_tab(char* tab, const float* c, int tid, in
 __device__ __forceinline__ uint32_t mq_bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
 
 // Part P of the entry at byte offset a (entry * stride + the lane's copy offset).
-template <int W, int PARTS, int P>
+template <int W, int PARTS, int C, int P>
 __device__ __forceinline__ auto mq_ent(const char* tab, uint32_t a) {
-  if constexpr (W == 2) return *reinterpret_cast<const mq_half4*>(tab + P * MqTab<W, PARTS>::part + a);
-  else return *reinterpret_cast<const mq_half2*>(tab + P * MqTab<W, PARTS>::part + a);
+  if constexpr (W == 2) return *reinterpret_cast<const mq_half4*>(tab + P * MqTab<W, PARTS, C>::part + a);
+  else return *reinterpret_cast<const mq_half2*>(tab + P * MqTab<W, PARTS, C>::part + a);
 }
 
 // Key operands of coordinates 8 ks .. 8 ks + 7 of the lane's 32 (its words w,
 // LSB-first W-bit fields): hi parts, lo parts and, with a sketch, the signs.
-template <int W, int PARTS, bool SIGNS>
+template <int W, int PARTS, int C, bool SIGNS>
 __device__ __forceinline__ void key8(const char* tab, const uint32_t* w, int ks, uint32_t cofs, mq_half8& ah,
                                      mq_half8& al, mq_half8& as) {
-  constexpr uint32_t S = MqTab<W, PARTS>::stride;
+  constexpr uint32_t S = MqTab<W, PARTS, C>::stride;
   if constexpr (W == 2) {
     const uint32_t x = w[ks >> 1] >> (16 * (ks & 1));
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const uint32_t a = ((x >> (8 * q)) & 255u) * S + cofs;
-      const mq_half4 h = mq_ent<W, PARTS, 0>(tab, a), l = mq_ent<W, PARTS, 1>(tab, a);
+      const mq_half4 h = mq_ent<W, PARTS, C, 0>(tab, a), l = mq_ent<W, PARTS, C, 1>(tab, a);
 #pragma unroll
       for (int e = 0; e < 4; ++e) { ah[4 * q + e] = h[e]; al[4 * q + e] = l[e]; }
     }
@@ -145,11 +165,11 @@ __device__ __forceinline__ void key8(const char* tab, const uint32_t* w, int ks,
         f &= 63u;
       }
       const uint32_t a = f * S + cofs;
-      const mq_half2 h = mq_ent<W, PARTS, 0>(tab, a), l = mq_ent<W, PARTS, 1>(tab, a);
+      const mq_half2 h = mq_ent<W, PARTS, C, 0>(tab, a), l = mq_ent<W, PARTS, C, 1>(tab, a);
       ah[2 * q] = h.x; ah[2 * q + 1] = h.y;
       al[2 * q] = l.x; al[2 * q + 1] = l.y;
       if constexpr (SIGNS) {
-        const mq_half2 s = mq_ent<W, PARTS, 2>(tab, a);
+        const mq_half2 s = mq_ent<W, PARTS, C, 2>(tab, a);
         as[2 * q] = s.x; as[2 * q + 1] = s.y;
       }
     }
@@ -187,13 +207,13 @@ __device__ __forceinline__ void value_index(const uint32_t* vr, uint32_t vsh, ui
 
 // First operand of value product j: coordinate 8 mm + j of tokens 4 hq .. 4 hq
 // + 3 (and, with a sketch, their signs).
-template <int W, int PARTS, bool SIGNS>
+template <int W, int PARTS, int C, bool SIGNS>
 __device__ __forceinline__ void value_ops(const char* tab, const uint32_t* ix, int j, uint32_t cofs, mq_half4& A,
                                           mq_half4& As) {
-  constexpr uint32_t S = MqTab<W, PARTS>::stride;
+  constexpr uint32_t S = MqTab<W, PARTS, C>::stride;
   if constexpr (W == 2) {
     const uint32_t f = (ix[(j & 1) * 2 + ((j >> 1) & 1)] >> (8 * (j >> 2))) & 255u;
-    A = mq_ent<W, PARTS, 0>(tab, f * S + cofs);
+    A = mq_ent<W, PARTS, C, 0>(tab, f * S + cofs);
   } else {
     uint32_t f01, f23;
     if constexpr (W == 4) {
@@ -204,10 +224,10 @@ __device__ __forceinline__ void value_ops(const char* tab, const uint32_t* ix, i
       f23 = ((ix[2] >> (3 * j)) & 7u) | (((ix[3] >> (3 * j)) & 7u) << 3);
     }
     const uint32_t a01 = f01 * S + cofs, a23 = f23 * S + cofs;
-    const mq_half2 h01 = mq_ent<W, PARTS, 0>(tab, a01), h23 = mq_ent<W, PARTS, 0>(tab, a23);
+    const mq_half2 h01 = mq_ent<W, PARTS, C, 0>(tab, a01), h23 = mq_ent<W, PARTS, C, 0>(tab, a23);
     A = mq_half4{h01.x, h01.y, h23.x, h23.y};
     if constexpr (SIGNS) {
-      const mq_half2 s01 = mq_ent<W, PARTS, 1>(tab, a01), s23 = mq_ent<W, PARTS, 1>(tab, a23);
+      const mq_half2 s01 = mq_ent<W, PARTS, C, 1>(tab, a01), s23 = mq_ent<W, PARTS, C, 1>(tab, a23);
       As = mq_half4{s01.x, s01.y, s23.x, s23.y};
     }
   }
@@ -224,28 +244,29 @@ __device__ __forceinline__ float mq_ldf(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 // KB, VB: index bits; KQ, VQ: sketched (4-bit fields, KB = VB = 3); KS: HeadQ
 // side code (d = 128).
 template <int D, int KB, bool KQ, bool KS, int VB, bool VQ>
-__global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p) {
-  constexpr int NT = mq_threads(D);
+__global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(DecodeParams p) {
+  constexpr int NT = mq_threads(D, KQ, VQ);
   constexpr int NW = NT / 64;                      // waves per block
   constexpr int NWU = D / 128;                     // waves per unit
-  constexpr int UPB = NW / NWU;                    // units per block (4 at d = 128, else 1)
+  constexpr int UPB = NW / NWU;                    // units per block (mq_upb at d = 128, else 1)
   constexpr int KW = KQ ? 4 : KB, VW = VQ ? 4 : VB;  // field widths
   constexpr int KPARTS = KQ ? 3 : 2, VPARTS = VQ ? 2 : 1;
+  constexpr int CK = mq_copies(KW, KPARTS, mq_kbudget(D)), CV = mq_copies(VW, VPARTS, mq_vbudget(D));
   constexpr uint32_t RBK = D * KW / 8, RBV = D * VW / 8;  // code bytes per token
-  __shared__ __attribute__((aligned(16))) char s_ktab[MqTab<KW, KPARTS>::bytes];
-  __shared__ __attribute__((aligned(16))) char s_vtab[MqTab<VW, VPARTS>::bytes];
+  __shared__ __attribute__((aligned(16))) char s_ktab[MqTab<KW, KPARTS, CK>::bytes];
+  __shared__ __attribute__((aligned(16))) char s_vtab[MqTab<VW, VPARTS, CV>::bytes];
   // Partial scores of the waves of a unit (d > 128), double-buffered by step parity.
   __shared__ __attribute__((aligned(16))) mq_float4 s_red[NWU > 1 ? 2 : 1][NWU > 1 ? NWU : 1][NWU > 1 ? (KQ ? 128 : 64) : 1];
-  build_tab<KW, KPARTS, true, KQ, KQ>(s_ktab, p.kc, threadIdx.x, NT);
-  build_tab<VW, VPARTS, false, VQ, VQ>(s_vtab, p.vc, threadIdx.x, NT);
+  build_tab<KW, KPARTS, CK, true, KQ, KQ>(s_ktab, p.kc, threadIdx.x, NT);
+  build_tab<VW, VPARTS, CV, false, VQ, VQ>(s_vtab, p.vc, threadIdx.x, NT);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wu = NWU > 1 ? wave : 0;               // wave within the unit: coordinates 128 wu ..
   const int hq = lane >> 4, mm = lane & 15;        // operand / result lane (h, m)
-  const int copy = lane & (kMqCopies - 1);
-  const uint32_t kcofs = copy * MqTab<KW, KPARTS>::bytes_per, vcofs = copy * MqTab<VW, VPARTS>::bytes_per;
+  const uint32_t kcofs = (lane & (CK - 1)) * MqTab<KW, KPARTS, CK>::bytes_per;
+  const uint32_t vcofs = (lane & (CV - 1)) * MqTab<VW, VPARTS, CV>::bytes_per;
   // Lane offsets within a step: key words of token mm, slice 4 wu + hq (32
   // coordinates); value fields of coordinates 8 mm .. of the wave's 128, token
   // 4 hq (+ e rows); per-token scalars of tokens 4 hq .. 4 hq + 3.
@@ -374,7 +395,7 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         mq_half8 Ah, Al, As;
-        key8<KW, KPARTS, KQ>(s_ktab, cur.kw, ks, kcofs, Ah, Al, As);
+        key8<KW, KPARTS, CK, KQ>(s_ktab, cur.kw, ks, kcofs, Ah, Al, As);
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Qh[ks], S, 0, 0, 0);
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Ql[ks], S, 0, 0, 0);
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Qh[ks], S, 0, 0, 0);
@@ -475,7 +496,7 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         mq_half4 A, As;
-        value_ops<VW, VPARTS, VQ>(s_vtab, ix, j, vcofs, A, As);
+        value_ops<VW, VPARTS, CV, VQ>(s_vtab, ix, j, vcofs, A, As);
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Wv, acc[j], 0, 0, 0);
         if constexpr (VQ) ask[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(As, Wq, ask[j], 0, 0, 0);
       }
@@ -513,11 +534,12 @@ __global__ __launch_bounds__(mq_threads(D)) void decode_mq_kernel(DecodeParams p
 
 template <int D, int KB, bool KQ, bool KS>
 hipError_t launch_mq_v(const DecodeParams& p, int vbits, int vqjl, int nblocks, hipStream_t s) {
-  constexpr int NT = mq_threads(D);
   if (vqjl) {
-    hipLaunchKernelGGL((decode_mq_kernel<D, KB, KQ, KS, 3, true>), dim3(nblocks), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((decode_mq_kernel<D, KB, KQ, KS, 3, true>), dim3(nblocks), dim3(mq_threads(D, KQ, true)), 0, s,
+                       p);
     return hipGetLastError();
   }
+  constexpr int NT = mq_threads(D, KQ, false);
   switch (vbits) {
     case 4: hipLaunchKernelGGL((decode_mq_kernel<D, KB, KQ, KS, 4, false>), dim3(nblocks), dim3(NT), 0, s, p); break;
     case 3: hipLaunchKernelGGL((decode_mq_kernel<D, KB, KQ, KS, 3, false>), dim3(nblocks), dim3(NT), 0, s, p); break;
@@ -552,7 +574,13 @@ bool mq_supported(int d, int G, int kbits, int kqjl, int kside, int side_rank, i
 }
 
 int mq_waves_per_unit(int d) { return d == 128 ? 1 : d / 128; }
-int mq_units_per_block(int d) { return d == 128 ? 4 : 1; }
+int mq_units_per_block(int d, int kqjl, int vqjl) { return mq_upb(d, kqjl != 0, vqjl != 0); }
+
+// Units of work the planner aims at: at d = 128 one per resident wave (one
+// block per CU, a single round); above, 16 waves' worth per CU.
+int mq_target_units(int d, int kqjl, int vqjl, int cus) {
+  return d == 128 ? cus * mq_upb(d, kqjl != 0, vqjl != 0) : cus * 16 / (d / 128);
+}
 
 hipError_t launch_decode_mq(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl, int nblocks,
                             hipStream_t s) {

@@ -225,10 +225,11 @@ hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int ksi
 // G >= 2 query heads per KV head, 2- to 4-bit keys (3-bit with a sketch) or
 // HeadQ at d = 128, 2- to 4-bit values (3-bit with a sketch).  A unit (KV
 // head, 16 queries, chunk) takes mq_waves_per_unit(d) waves; a block holds
-// mq_units_per_block(d) units.
+// mq_units_per_block(d, kqjl, vqjl) units.
 bool mq_supported(int d, int G, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl);
 int mq_waves_per_unit(int d);
-int mq_units_per_block(int d);
+int mq_units_per_block(int d, int kqjl, int vqjl);
+int mq_target_units(int d, int kqjl, int vqjl, int cus);
 hipError_t launch_decode_mq(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl, int nblocks,
                             hipStream_t s);
 hipError_t launch_metric_scores(const MetricScoreParams& p, int kbits, int kqjl, int kside, hipStream_t s,
