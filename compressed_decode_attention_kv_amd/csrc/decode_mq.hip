@@ -211,19 +211,27 @@ template <int W, int PARTS, int C, bool SIGNS>
 __device__ __forceinline__ void value_ops(const char* tab, const uint32_t* ix, int j, uint32_t cofs, mq_half4& A,
                                           mq_half4& As) {
   constexpr uint32_t S = MqTab<W, PARTS, C>::stride;
+  // With 256-byte entries an index byte k of a word becomes the offset
+  // byte k * 256 + copy offset in one byte permute (result bytes: the copy
+  // offset, byte k, zero, zero).
+  constexpr bool PERM = S == 256 && W != 3;
+  auto at = [&](uint32_t word, int k) -> uint32_t {
+    if constexpr (PERM) return __builtin_amdgcn_perm(word, cofs, 0x0C0C0000u | ((4u + k) << 8));
+    else return ((word >> (8 * k)) & 255u) * S + cofs;
+  };
   if constexpr (W == 2) {
-    const uint32_t f = (ix[(j & 1) * 2 + ((j >> 1) & 1)] >> (8 * (j >> 2))) & 255u;
-    A = mq_ent<W, PARTS, C, 0>(tab, f * S + cofs);
+    A = mq_ent<W, PARTS, C, 0>(tab, at(ix[(j & 1) * 2 + ((j >> 1) & 1)], j >> 2));
   } else {
-    uint32_t f01, f23;
+    uint32_t a01, a23;
     if constexpr (W == 4) {
-      f01 = (ix[j & 1] >> (8 * (j >> 1))) & 255u;
-      f23 = (ix[2 + (j & 1)] >> (8 * (j >> 1))) & 255u;
+      a01 = at(ix[j & 1], j >> 1);
+      a23 = at(ix[2 + (j & 1)], j >> 1);
     } else {
-      f01 = ((ix[0] >> (3 * j)) & 7u) | (((ix[1] >> (3 * j)) & 7u) << 3);
-      f23 = ((ix[2] >> (3 * j)) & 7u) | (((ix[3] >> (3 * j)) & 7u) << 3);
+      const uint32_t f01 = ((ix[0] >> (3 * j)) & 7u) | (((ix[1] >> (3 * j)) & 7u) << 3);
+      const uint32_t f23 = ((ix[2] >> (3 * j)) & 7u) | (((ix[3] >> (3 * j)) & 7u) << 3);
+      a01 = f01 * S + cofs;
+      a23 = f23 * S + cofs;
     }
-    const uint32_t a01 = f01 * S + cofs, a23 = f23 * S + cofs;
     const mq_half2 h01 = mq_ent<W, PARTS, C, 0>(tab, a01), h23 = mq_ent<W, PARTS, C, 0>(tab, a23);
     A = mq_half4{h01.x, h01.y, h23.x, h23.y};
     if constexpr (SIGNS) {
@@ -253,10 +261,17 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
   constexpr int KPARTS = KQ ? 3 : 2, VPARTS = VQ ? 2 : 1;
   constexpr int CK = mq_copies(KW, KPARTS, mq_kbudget(D)), CV = mq_copies(VW, VPARTS, mq_vbudget(D));
   constexpr uint32_t RBK = D * KW / 8, RBV = D * VW / 8;  // code bytes per token
-  __shared__ __attribute__((aligned(16))) char s_ktab[MqTab<KW, KPARTS, CK>::bytes];
-  __shared__ __attribute__((aligned(16))) char s_vtab[MqTab<VW, VPARTS, CV>::bytes];
-  // Partial scores of the waves of a unit (d > 128), double-buffered by step parity.
-  __shared__ __attribute__((aligned(16))) mq_float4 s_red[NWU > 1 ? 2 : 1][NWU > 1 ? NWU : 1][NWU > 1 ? (KQ ? 128 : 64) : 1];
+  // One LDS block: the value table first (at address 0, so that its lookup
+  // offsets need no base), the key table, and for d > 128 the partial scores
+  // of the unit's waves, double-buffered by step parity.
+  constexpr int VBYTES = (MqTab<VW, VPARTS, CV>::bytes + 15) / 16 * 16;
+  constexpr int KBYTES = (MqTab<KW, KPARTS, CK>::bytes + 15) / 16 * 16;
+  constexpr int RED = NWU > 1 ? 2 * NWU * (KQ ? 128 : 64) : 0;   // float4 entries
+  __shared__ __attribute__((aligned(16))) char s_lds[VBYTES + KBYTES + 16 * RED + 16];
+  char* const s_vtab = s_lds;
+  char* const s_ktab = s_lds + VBYTES;
+  typedef mq_float4 RedRow[NWU > 1 ? NWU : 1][NWU > 1 ? (KQ ? 128 : 64) : 1];
+  RedRow* const s_red = reinterpret_cast<RedRow*>(s_lds + VBYTES + KBYTES);
   build_tab<KW, KPARTS, CK, true, KQ, KQ>(s_ktab, p.kc, threadIdx.x, NT);
   build_tab<VW, VPARTS, CV, false, VQ, VQ>(s_vtab, p.vc, threadIdx.x, NT);
   __syncthreads();
@@ -265,7 +280,10 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wu = NWU > 1 ? wave : 0;               // wave within the unit: coordinates 128 wu ..
   const int hq = lane >> 4, mm = lane & 15;        // operand / result lane (h, m)
-  const uint32_t kcofs = (lane & (CK - 1)) * MqTab<KW, KPARTS, CK>::bytes_per;
+  // Key lookups: the key table's base rides in the lane's copy offset (kept
+  // opaque, so it is not split off into an LDS offset field too narrow for it).
+  uint32_t kcofs = VBYTES + (lane & (CK - 1)) * MqTab<KW, KPARTS, CK>::bytes_per;
+  asm volatile("" : "+v"(kcofs));
   const uint32_t vcofs = (lane & (CV - 1)) * MqTab<VW, VPARTS, CV>::bytes_per;
   // Lane offsets within a step: key words of token mm, slice 4 wu + hq (32
   // coordinates); value fields of coordinates 8 mm .. of the wave's 128, token
@@ -395,7 +413,7 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         mq_half8 Ah, Al, As;
-        key8<KW, KPARTS, CK, KQ>(s_ktab, cur.kw, ks, kcofs, Ah, Al, As);
+        key8<KW, KPARTS, CK, KQ>(s_lds, cur.kw, ks, kcofs, Ah, Al, As);
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Qh[ks], S, 0, 0, 0);
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Ql[ks], S, 0, 0, 0);
         S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Qh[ks], S, 0, 0, 0);
