@@ -245,8 +245,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mq_rsrc(const void* base, uint
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kMqRsrcWord3);
 }
 
-__device__ __forceinline__ float mq_ldf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+__device__ __forceinline__ mq_float4 mq_ldf4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(mq_float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
 // KB, VB: index bits; KQ, VQ: sketched (4-bit fields, KB = VB = 3); KS: HeadQ
@@ -395,14 +395,13 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
       }
       st.side = 0;
       if constexpr (KS) st.side = __builtin_amdgcn_raw_buffer_load_b16(rsd, vsd, 8u * (uint32_t)base, kMqNT);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        st.nuk[i] = mq_ldf(rnk, vn + 4 * i, sn);
-        st.nuv[i] = mq_ldf(rnv, vn + 4 * i, sn);
-        st.sz[i] = KS ? mq_ldf(rsz, vn + 4 * i, sn) : 0.f;
-        st.gk[i] = KQ ? mq_ldf(rgk, vn + 4 * i, sn) : 0.f;
-        st.gv[i] = VQ ? mq_ldf(rgv, vn + 4 * i, sn) : 0.f;
-      }
+      // 16-byte loads of four tokens' scalars (the range check is per dword).
+      st.nuk = mq_ldf4(rnk, vn, sn);
+      st.nuv = mq_ldf4(rnv, vn, sn);
+      st.sz = st.gk = st.gv = mq_float4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KS) st.sz = mq_ldf4(rsz, vn, sn);
+      if constexpr (KQ) st.gk = mq_ldf4(rgk, vn, sn);
+      if constexpr (VQ) st.gv = mq_ldf4(rgv, vn, sn);
     };
     int parity = 0;
     auto step = [&](int base, const Step& cur) __attribute__((always_inline)) {
