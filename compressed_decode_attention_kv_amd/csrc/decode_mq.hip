@@ -81,7 +81,8 @@ typedef uint32_t mq_u32x2 __attribute__((ext_vector_type(2)));
 // Table of one tensor's centroids indexed by a unit of W-bit fields, the first
 // field in the lowest bits and the first slot: two 4-bit fields (half2; with a
 // sketch a field is 3-bit code | sign << 3 and the code is taken), two 3-bit
-// fields (a 6-bit index, half2) or four 2-bit fields (half4).  Each entry sits
+// fields (a 6-bit index, half2), four 2-bit fields (half4) or four 1-bit
+// fields (a 4-bit index, half4).  Each entry sits
 // in C copies, copy = lane % C, against bank conflicts.  Up to
 // three parts share one indexing: keys hold the fp16 hi parts of the
 // centroids, the lo parts (c - hi) and, with a sketch, the signs (bit 3 of
@@ -89,8 +90,8 @@ typedef uint32_t mq_u32x2 __attribute__((ext_vector_type(2)));
 // a sketch, the signs.
 template <int W, int PARTS, int C>
 struct MqTab {
-  static constexpr int entries = W == 3 ? 64 : 256;
-  static constexpr int bytes_per = W == 2 ? 8 : 4;        // one copy of one part of an entry
+  static constexpr int entries = W == 3 ? 64 : W == 1 ? 16 : 256;
+  static constexpr int bytes_per = W <= 2 ? 8 : 4;        // one copy of one part of an entry
   static constexpr int stride = C * bytes_per;            // bytes between entries
   // Parts lie 16 B further apart than their size: no multiple of 256 B and
   // more than 2 KB, so reads of two parts at one index never merge into one
@@ -105,14 +106,14 @@ struct MqTab {
 // but fall into the same bank), at 8, eight.
 constexpr int mq_copies(int W, int PARTS, int budget) {
   int c = 64;
-  while (c > 1 && PARTS * (W == 3 ? 64 : 256) * (W == 2 ? 8 : 4) * c > budget) c /= 2;
+  while (c > 1 && PARTS * (W == 3 ? 64 : W == 1 ? 16 : 256) * (W <= 2 ? 8 : 4) * c > budget) c /= 2;
   return c;
 }
 
 template <int W, int PARTS, int C, bool LO, bool SIGNS, bool MASK>
 __device__ __forceinline__ void build_tab(char* tab, const float* c, int tid, int nthreads) {
   using Tab = MqTab<W, PARTS, C>;
-  constexpr int N = W == 2 ? 4 : 2;               // fields per entry
+  constexpr int N = W <= 2 ? 4 : 2;               // fields per entry
   for (int i = tid; i < Tab::entries * C; i += nthreads) {
     const int e = i / C;
     _Float16* d0 = reinterpret_cast<_Float16*>(tab + i * Tab::bytes_per);
@@ -133,7 +134,7 @@ __device__ __forceinline__ uint32_t mq_bfi(uint32_t m, uint32_t a, uint32_t b) {
 // Part P of the entry at byte offset a (entry * stride + the lane's copy offset).
 template <int W, int PARTS, int C, int P>
 __device__ __forceinline__ auto mq_ent(const char* tab, uint32_t a) {
-  if constexpr (W == 2) return *reinterpret_cast<const mq_half4*>(tab + P * MqTab<W, PARTS, C>::part + a);
+  if constexpr (W <= 2) return *reinterpret_cast<const mq_half4*>(tab + P * MqTab<W, PARTS, C>::part + a);
   else return *reinterpret_cast<const mq_half2*>(tab + P * MqTab<W, PARTS, C>::part + a);
 }
 
@@ -178,7 +179,8 @@ __device__ __forceinline__ void key8(const char* tab, const uint32_t* w, int ks,
 
 // Value fields: vr holds, for each token 4 hq + e of the step, the fields of
 // coordinates 8 mm .. 8 mm + 7 of the wave's 128 (W = 4: a word; W = 2: 16
-// bits; W = 3: the two words that hold its 24 bits, vsh bits into the first).
+// bits; W = 1: a byte; W = 3: the two words that hold its 24 bits, vsh bits
+// into the first).
 // value_index turns them once per step into the table indices of the value
 // products: the pair (tokens 0, 1 | 2, 3) or quad entries of each coordinate.
 template <int W>
@@ -192,6 +194,16 @@ __device__ __forceinline__ void value_index(const uint32_t* vr, uint32_t vsh, ui
   } else if constexpr (W == 3) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) ix[e] = __builtin_amdgcn_alignbit(vr[2 * e + 1], vr[2 * e], vsh);
+  } else if constexpr (W == 1) {
+    // The 4 x 8 bit matrix (byte e = token e, bit j = coordinate j) transposed
+    // by two delta swaps: byte k then holds coordinate k's four bits in its
+    // low nibble and coordinate k + 4's in its high nibble (token e at bit e).
+    uint32_t x = vr[0] | (vr[1] << 8) | (vr[2] << 16) | (vr[3] << 24);
+    uint32_t t = (x ^ (x >> 7)) & 0x00AA00AAu;
+    x ^= t ^ (t << 7);
+    t = (x ^ (x >> 14)) & 0x0000CCCCu;
+    x ^= t ^ (t << 14);
+    ix[0] = x;
   } else {
     // Nibbles of R: fields 2 i of tokens 0 | 1 (low half) and 2 | 3 (high
     // half); of S: fields 2 i + 1.  Bytes 0 and 1 of ix[] then pair them up:
@@ -214,13 +226,16 @@ __device__ __forceinline__ void value_ops(const char* tab, const uint32_t* ix, i
   // With 256-byte entries an index byte k of a word becomes the offset
   // byte k * 256 + copy offset in one byte permute (result bytes: the copy
   // offset, byte k, zero, zero).
-  constexpr bool PERM = S == 256 && W != 3;
+  constexpr bool PERM = S == 256 && (W == 4 || W == 2);
   auto at = [&](uint32_t word, int k) -> uint32_t {
     if constexpr (PERM) return __builtin_amdgcn_perm(word, cofs, 0x0C0C0000u | ((4u + k) << 8));
     else return ((word >> (8 * k)) & 255u) * S + cofs;
   };
   if constexpr (W == 2) {
     A = mq_ent<W, PARTS, C, 0>(tab, at(ix[(j & 1) * 2 + ((j >> 1) & 1)], j >> 2));
+  } else if constexpr (W == 1) {
+    const uint32_t f = (ix[0] >> (8 * (j & 3) + 4 * (j >> 2))) & 15u;
+    A = mq_ent<W, PARTS, C, 0>(tab, f * S + cofs);
   } else {
     uint32_t a01, a23;
     if constexpr (W == 4) {
@@ -290,7 +305,7 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
   // 4 hq (+ e rows); per-token scalars of tokens 4 hq .. 4 hq + 3.
   const uint32_t vk = mm * RBK + 4 * KW * (4 * wu + hq);
   const uint32_t vj0 = VW == 3 ? (3 * mm) >> 2 : 0;
-  const uint32_t vv = 4 * hq * RBV + 16 * VW * wu + (VW == 4 ? 4 * mm : (VW == 2 ? 2 * mm : 4 * vj0));
+  const uint32_t vv = 4 * hq * RBV + 16 * VW * wu + (VW == 4 ? 4 * mm : VW == 2 ? 2 * mm : VW == 1 ? mm : 4 * vj0);
   const uint32_t vv2 = vv + (VW == 3 && vj0 < 11 ? 4 : 0);
   const uint32_t vsh = VW == 3 ? 8 * ((3 * mm) & 3) : 0;
   const uint32_t vn = 16 * hq, vsd = 8 * mm + 2 * hq;
@@ -388,6 +403,8 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
           st.vr[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, vv + e * RBV, sv, kMqNT);
         } else if constexpr (VW == 2) {
           st.vr[e] = __builtin_amdgcn_raw_buffer_load_b16(rv, vv + e * RBV, sv, kMqNT);
+        } else if constexpr (VW == 1) {
+          st.vr[e] = __builtin_amdgcn_raw_buffer_load_b8(rv, vv + e * RBV, sv, kMqNT);
         } else {
           st.vr[2 * e] = __builtin_amdgcn_raw_buffer_load_b32(rv, vv + e * RBV, sv, kMqNT);
           st.vr[2 * e + 1] = __builtin_amdgcn_raw_buffer_load_b32(rv, vv2 + e * RBV, sv, kMqNT);
@@ -561,6 +578,7 @@ hipError_t launch_mq_v(const DecodeParams& p, int vbits, int vqjl, int nblocks, 
     case 4: hipLaunchKernelGGL((decode_mq_kernel<D, KB, KQ, KS, 4, false>), dim3(nblocks), dim3(NT), 0, s, p); break;
     case 3: hipLaunchKernelGGL((decode_mq_kernel<D, KB, KQ, KS, 3, false>), dim3(nblocks), dim3(NT), 0, s, p); break;
     case 2: hipLaunchKernelGGL((decode_mq_kernel<D, KB, KQ, KS, 2, false>), dim3(nblocks), dim3(NT), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_mq_kernel<D, KB, KQ, KS, 1, false>), dim3(nblocks), dim3(NT), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -585,7 +603,7 @@ hipError_t launch_mq_d(const DecodeParams& p, int kbits, int kqjl, int kside, in
 
 bool mq_supported(int d, int G, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl) {
   if ((d != 128 && d != 256 && d != 512 && d != 1024) || G < 2) return false;
-  if (vqjl ? vbits != 3 : (vbits < 2 || vbits > 4)) return false;
+  if (vqjl ? vbits != 3 : (vbits < 1 || vbits > 4)) return false;
   if (kside) return d == 128 && !kqjl && kbits == 2 && side_rank == 16 && side_bits == 4;
   return kqjl ? kbits == 3 : (kbits >= 2 && kbits <= 4);
 }

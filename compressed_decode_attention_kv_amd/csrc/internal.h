@@ -223,7 +223,7 @@ hipError_t launch_decode_lut(const DecodeParams& p, int kbits, int kqjl, int ksi
                              hipStream_t s);
 // Grouped-query decode on the matrix cores (decode_mq.hip): d = 128..1024,
 // G >= 2 query heads per KV head, 2- to 4-bit keys (3-bit with a sketch) or
-// HeadQ at d = 128, 2- to 4-bit values (3-bit with a sketch).  A unit (KV
+// HeadQ at d = 128, 1- to 4-bit values (3-bit with a sketch).  A unit (KV
 // head, 16 queries, chunk) takes mq_waves_per_unit(d) waves; a block holds
 // mq_units_per_block(d, kqjl, vqjl) units.
 bool mq_supported(int d, int G, int kbits, int kqjl, int kside, int side_rank, int side_bits, int vbits, int vqjl);

@@ -181,12 +181,14 @@ def test_table_decode_low_bits(tq, d, kmode, kbits, vmode, vbits):
 
 @pytest.mark.parametrize("G,kbits,vbits,T", [
     (2, 4, 4, 700), (4, 3, 4, 1000), (16, 2, 2, 333), (17, 4, 3, 900), (64, 4, 4, 257), (5, 2, 3, 1),
+    (4, 4, 1, 513), (16, 3, 1, 70),
 ])
 def test_grouped_query_decode(tq, G, kbits, vbits, T):
     """The grouped-query matrix-core decode (G >= 2 query heads per KV head at
     d = 128, unsketched tensors): one block of 16 queries per pass, ragged
     query blocks (G = 17: 16 + 1), T not a multiple of the 16-token step,
-    T = 1; fp16 inputs, B=2, H=2."""
+    T = 1, 1-bit values (four tokens' bits per table entry); fp16 inputs, B=2,
+    H=2."""
     K, V, Q = synth.isotropic(2, 2, G, T, 128, seed=80 + G + T, kv_std=1.0, dtype=np.float32)
     _run_case(tq, K, V, Q, "kqv", 4, seed=2, dtype=torch.float16, modes=((1, kbits), (1, vbits)),
               label="gqa G=%d" % G)
