@@ -691,16 +691,21 @@ tq_status quantize_core(const tq_tensor_desc* x, int mode, int bits, uint64_t se
   p.side = out->side; p.side_scale = out->side_scale;
   p.pos = pos;
   hipStream_t st = (hipStream_t)stream;
-  // HeadQ: Pi U_h once per head, [H][rank][d], in stream-ordered scratch.
+  // HeadQ: Pi U_h once per head, [H][rank][d], in stream-ordered scratch,
+  // followed by its fp16 hi and lo parts (times 2^10) for the matrix cores.
   void* rb = nullptr;
   if (mode == TQ_MODE_HEADQ) {
-    if (hipMallocAsync(&rb, (size_t)x->H * x->d * hq->rank * sizeof(float), st) != hipSuccess)
+    const size_t n = (size_t)x->H * x->d * hq->rank;
+    if (hipMallocAsync(&rb, n * (sizeof(float) + 2 * sizeof(_Float16)), st) != hipSuccess)
       return fail(TQ_ENOMEM, "rotated-basis scratch allocation failed");
-    if (tq_status s = hip_status(launch_rotate_basis(p, reinterpret_cast<float*>(rb), st), "basis rotation launch")) {
+    _Float16* rb16 = reinterpret_cast<_Float16*>(reinterpret_cast<float*>(rb) + n);
+    if (tq_status s = hip_status(launch_rotate_basis(p, reinterpret_cast<float*>(rb), rb16, st),
+                                 "basis rotation launch")) {
       (void)hipFreeAsync(rb, st);
       return s;
     }
     p.rbasis = reinterpret_cast<const float*>(rb);
+    p.rbasis16 = rb16;
   }
   tq_status status = TQ_OK;
   QuantGrid grid;

@@ -53,6 +53,9 @@ struct QuantParams {
   int bh0, nbh, t0, tn;
   const _Float16* S16;    // PROD at d >= 256: S in fp16 (exact), fragment order (device)
   const float* rbasis;    // HEADQ: (Pi U_h)^T per head, [H][rank][d]
+  // HEADQ at d = 128, rank 16: rbasis times 2^10 split into fp16 hi (first
+  // [H][rank][d] block) and lo = rest (second block); NULL elsewhere.
+  const _Float16* rbasis16;
   // SPECTRAL: basis (V, [H][d][d]) in `basis`, the mean and spreads [H][d],
   // and the N(0, 1) Lloyd-Max boundaries in double.
   const float* smean;
@@ -202,7 +205,7 @@ bool quant_sketch_supported(const QuantParams& p, const QuantGrid& grid);
 size_t sketch_fragment_index(int d, int row, int col);
 hipError_t launch_quantize_sketch(const QuantParams& p, const QuantGrid& grid, hipStream_t s);
 // (Pi U_h)^T of every head into out [H][rank][d] (device).
-hipError_t launch_rotate_basis(const QuantParams& p, float* out, hipStream_t s);
+hipError_t launch_rotate_basis(const QuantParams& p, float* out, _Float16* out16, hipStream_t s);
 // Matrix-core write side (fp16 input, d = 128, PLAIN/MSE/PROD).
 bool quant_mfma_supported(const QuantParams& p);
 int quant_mfma_lut_max();

@@ -400,14 +400,24 @@ __global__ __launch_bounds__(kThreads) void relerr_kernel(RelErrParams p) {
   }
 }
 
-// (Pi U_h)^T for every head h (one block per head) into out [H][rank][d].
-__global__ __launch_bounds__(kThreads) void rotate_basis_kernel(QuantParams p, float* out) {
+// (Pi U_h)^T for every head h (one block per head) into out [H][rank][d];
+// with out16, also 2^10 times it as fp16 hi (out16) and lo (out16 + H rank d),
+// the matrix-core quantiser's operands.
+__global__ __launch_bounds__(kThreads) void rotate_basis_kernel(QuantParams p, float* out, _Float16* out16) {
   __shared__ float s_side[kMaxSideLds];
   const int h = blockIdx.x, n = p.d * p.rank;
   rotated_basis(p.basis + (size_t)h * n, p.d, p.rank, p.signbits, p.inv_sqrt_d, s_side);
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int r = i / p.d, k = i % p.d;
-    out[(size_t)h * n + i] = s_side[k * p.rank + r];
+    const float u = s_side[k * p.rank + r];
+    out[(size_t)h * n + i] = u;
+    if (out16) {
+      float uv = u * 1024.0f;
+      asm volatile("" : "+v"(uv));
+      const _Float16 hi = (_Float16)uv;
+      out16[(size_t)h * n + i] = hi;
+      out16[(size_t)(p.H + h) * n + i] = (_Float16)(uv - (float)hi);
+    }
   }
 }
 
@@ -465,8 +475,8 @@ hipError_t launch_quantize(const QuantParams& p, const QuantGrid* grid, hipStrea
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_rotate_basis(const QuantParams& p, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(rotate_basis_kernel, dim3(p.H), dim3(kThreads), 0, s, p, out);
+hipError_t launch_rotate_basis(const QuantParams& p, float* out, _Float16* out16, hipStream_t s) {
+  hipLaunchKernelGGL(rotate_basis_kernel, dim3(p.H), dim3(kThreads), 0, s, p, out, out16);
   return hipGetLastError();
 }
 

@@ -376,15 +376,18 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
       // U'[32 g + 8 kb + j][tau] at lane (g, tau) and the result gives lane
       // (g, tau) ranks 4 g .. 4 g + 3 of token tau.  Both factors are split
       // into fp16 hi + lo (residual x 2^12, basis x 2^10; each value pinned as
-      // its rounded fp32 before the split) and hi hi + hi lo + lo hi summed.
+      // its rounded fp32 before the split) and hi hi + hi lo + lo hi summed;
+      // the basis parts come split already (rotate_basis_kernel).
       // y holds the residual times 2^12 already; for nu = 0 the scale zs below is 0.
-      const float* ub = p.rbasis + (size_t)(bh % p.H) * (16 * 128) + tau * 128 + 32 * g;
+      const size_t uo = (size_t)(bh % p.H) * (16 * 128) + tau * 128 + 32 * g;
+      const _Float16* ubh = p.rbasis16 + uo;
+      const _Float16* ubl = p.rbasis16 + (size_t)p.H * (16 * 128) + uo;
       float4v zacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        half8 eh, el, uh, ul;
-        const float4v u0 = *reinterpret_cast<const float4v*>(ub + 8 * kb);
-        const float4v u1 = *reinterpret_cast<const float4v*>(ub + 8 * kb + 4);
+        half8 eh, el;
+        const half8 uh = *reinterpret_cast<const half8*>(ubh + 8 * kb);
+        const half8 ul = *reinterpret_cast<const half8*>(ubl + 8 * kb);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           float ev = y[kb][j];
@@ -392,11 +395,6 @@ __global__ __launch_bounds__(kThreadsM) void quant_mfma_kernel(QuantParams p, Qu
           const _Float16 ehj = (_Float16)ev;
           eh[j] = ehj;
           el[j] = (_Float16)(ev - (float)ehj);
-          float uv = (j < 4 ? u0[j] : u1[j - 4]) * 1024.0f;
-          asm volatile("" : "+v"(uv));
-          const _Float16 uhj = (_Float16)uv;
-          uh[j] = uhj;
-          ul[j] = (_Float16)(uv - (float)uhj);
         }
         zacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(uh, eh, zacc, 0, 0, 0);
         zacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(uh, el, zacc, 0, 0, 0);
@@ -526,8 +524,8 @@ bool quant_mfma_supported(const QuantParams& p) {
   // 32-bit tile indices and per-head byte offsets (at most 64 bytes per token).
   const long tiles = (long)p.B * p.H * ((p.T + 15) / 16);
   // HeadQ: the 2-bit base with a rank-16, 4-bit side code, once the rotated
-  // basis (Pi U_h)^T [H][16][128] is in p.rbasis.
-  const bool headq_ok = p.mode == TQ_MODE_HEADQ && p.bits == 2 && p.rank == 16 && p.side_bits == 4 && p.rbasis;
+  // basis (Pi U_h)^T [H][16][128] is in p.rbasis and its fp16 split in p.rbasis16.
+  const bool headq_ok = p.mode == TQ_MODE_HEADQ && p.bits == 2 && p.rank == 16 && p.side_bits == 4 && p.rbasis16;
   return p.d == 128 && (p.dtype == TQ_F16 || p.dtype == TQ_F32) && (p.mode != TQ_MODE_HEADQ || headq_ok) &&
          p.bits >= 1 && p.bits <= 4 &&
          tiles < (1L << 31) && p.T_cap <= (1 << 24);
