@@ -206,6 +206,16 @@ def test_grouped_query_decode_wide_and_sketched(tq, d, G, scheme):
     _run_case(tq, K, V, Q, scheme, 4, seed=4, dtype=torch.float16, label="gqa %s d=%d G=%d" % (scheme, d, G))
 
 
+@pytest.mark.parametrize("d,G,kbits,vbits", [(256, 4, 2, 1), (512, 3, 3, 2), (1024, 5, 4, 1)])
+def test_grouped_query_decode_wide_narrow_values(tq, d, G, kbits, vbits):
+    """The grouped-query decode over wider heads with 1- and 2-bit values
+    (quad table entries, the 1-bit ones from a bit transpose of four tokens)
+    and 2- to 4-bit keys, fp16, ragged T."""
+    K, V, Q = synth.isotropic(1, 2, G, 301, d, seed=120 + d + G, kv_std=1.0, dtype=np.float32)
+    _run_case(tq, K, V, Q, "kqv", 4, seed=5, dtype=torch.float16, modes=((1, kbits), (1, vbits)),
+              label="gqa d=%d G=%d K%d V%d" % (d, G, kbits, vbits))
+
+
 def test_grouped_query_decode_lengths_and_static(tq):
     """Per-sequence lengths (0, ragged, full) and the allocation-free decode
     through the grouped-query path agree with the oracle on each prefix."""
