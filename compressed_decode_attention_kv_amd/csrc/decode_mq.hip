@@ -454,9 +454,13 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
       }
       mq_float4 Ss = {0.f, 0.f, 0.f, 0.f};
       if constexpr (KS) {
-        mq_half4 A;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) A[e] = (_Float16)((float)((cur.side >> (4 * e)) & 15u) - 7.0f);
+        // code - 7 as fp16: 0x6400 | code is 1024 + code exactly, less 1031 (exact).
+        const uint32_t sd = cur.side;
+        const uint32_t p01 = (sd & 0xFu) | ((sd & 0xF0u) << 12) | 0x64006400u;
+        const uint32_t p23 = ((sd >> 8) & 0xFu) | ((sd & 0xF000u) << 4) | 0x64006400u;
+        const mq_half2 lev = {(_Float16)1031.0f, (_Float16)1031.0f};
+        const mq_half2 a01 = __builtin_bit_cast(mq_half2, p01) - lev, a23 = __builtin_bit_cast(mq_half2, p23) - lev;
+        const mq_half4 A = {a01.x, a01.y, a23.x, a23.y};
         Ss = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Wh, Ss, 0, 0, 0);
         Ss = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Wl, Ss, 0, 0, 0);
       }
