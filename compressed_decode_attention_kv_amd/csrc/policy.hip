@@ -277,6 +277,88 @@ __global__ __launch_bounds__(kPThreads) void merge_kernel(MergeParams p) {
 
 }  // namespace
 
+// The same scores on the matrix cores: per wave 16 tokens x 16 probes per
+// v_mfma_f32_16x16x32_f16 product, the contraction over d in steps of 32.
+// Keys enter exact (fp16) or as fp16 hi + lo (fp32); the probes as fp16 hi +
+// lo parts (about 22 bits), held in LDS in operand order: (probe block pb,
+// step ks, lane (h, n)) holds coordinates 32 ks + 8 h .. + 7 of probe
+// 16 pb + n (zero past the last probe).  Lane (h, t) takes token t's
+// coordinates 32 ks + 8 h .. + 7; the result hands lane (h, n) tokens
+// 4 h .. 4 h + 3 of probe 16 pb + n.
+typedef _Float16 a2_half8 __attribute__((ext_vector_type(8)));
+typedef float a2_float4 __attribute__((ext_vector_type(4)));
+
+template <typename TIN, int NPB>
+__global__ __launch_bounds__(kPThreads) void a2_scores_mfma_kernel(A2Params p) {
+  extern __shared__ __attribute__((aligned(16))) char s_raw[];
+  const int d = p.d, KS = d / 32, P = p.P;
+  a2_half8* s_qh = reinterpret_cast<a2_half8*>(s_raw);
+  a2_half8* s_ql = s_qh + NPB * KS * 64;
+  const int bkv = blockIdx.y, b = bkv / p.Hkv, kvh = bkv % p.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hq = lane >> 4, mm = lane & 15;
+  const int row0 = (b * p.Hq + kvh * p.G) * p.Np;
+  for (int i = threadIdx.x; i < NPB * KS * 64; i += kPThreads) {
+    const int l = i & 63, pk = i >> 6, ks = pk % KS, pb = pk / KS;
+    const int r = 16 * pb + (l & 15), c = 32 * ks + 8 * (l >> 4);
+    a2_half8 h, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = 0.f;
+      if (r < P) {
+        const int hq2 = kvh * p.G + r / p.Np, n = r % p.Np;
+        const int64_t off = (int64_t)b * p.qsb + (int64_t)hq2 * p.qsh + (int64_t)n * p.qst + c + e;
+        v = p.qdtype == TQ_F16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off]
+                               : reinterpret_cast<const float*>(p.q)[off];
+      }
+      h[e] = (_Float16)v;
+      lo[e] = (_Float16)(v - (float)h[e]);
+    }
+    s_qh[i] = h;
+    s_ql[i] = lo;
+  }
+  __syncthreads();
+  const TIN* kb = reinterpret_cast<const TIN*>(p.k) + (int64_t)b * p.ksb + (int64_t)kvh * p.ksh;
+  const int t0 = blockIdx.x * p.chunk, t1 = min(p.T, t0 + p.chunk);
+  for (int base = t0 + 16 * wave; base < t1; base += 16 * (kPThreads / 64)) {
+    const TIN* krow = kb + (int64_t)min(base + mm, t1 - 1) * p.kst + 8 * hq;
+    a2_float4 S[NPB];
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) S[pb] = a2_float4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks) {
+      a2_half8 kh, kl;
+      if constexpr (sizeof(TIN) == 2) {
+        kh = *reinterpret_cast<const a2_half8*>(krow + 32 * ks);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = krow[32 * ks + e];
+          kh[e] = (_Float16)v;
+          kl[e] = (_Float16)(v - (float)kh[e]);
+        }
+      }
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        const a2_half8 qh = s_qh[(pb * KS + ks) * 64 + lane], ql = s_ql[(pb * KS + ks) * 64 + lane];
+        S[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qh, S[pb], 0, 0, 0);
+        S[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, ql, S[pb], 0, 0, 0);
+        if constexpr (sizeof(TIN) == 4) S[pb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kl, qh, S[pb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+      const int r = 16 * pb + mm;
+      if (r >= P) continue;
+      float* dst = p.scores + (size_t)(row0 + r) * p.T;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = base + 4 * hq + i;
+        if (t < t1) dst[t] = S[pb][i] * p.inv_sqrt_d;
+      }
+    }
+  }
+}
+
 size_t a2_workspace_bytes(int rows, int T) {
   return ((size_t)rows * T * 4 + 255) / 256 * 256 + (size_t)rows * 8;
 }
@@ -286,10 +368,25 @@ hipError_t launch_a2_weights(const A2Params& p, hipStream_t s) {
   const dim3 g1((p.T + p.chunk - 1) / p.chunk, p.B * p.Hkv);
   const size_t dyn = (size_t)p.P * p.d * sizeof(float);
   (void)L;
-  if (p.kdtype == TQ_F16)
+  // Up to 64 probes per KV head on the matrix cores (chunks of whole 64-token
+  // block steps); more on the vector units.
+  const int npb = (p.P + 15) / 16;
+  if (npb <= 4 && p.d % 32 == 0 && p.chunk % 64 == 0) {
+    const int nb = npb <= 1 ? 1 : (npb <= 2 ? 2 : 4);
+    const size_t dq = (size_t)2 * nb * 16 * p.d * sizeof(_Float16);
+    const bool f16 = p.kdtype == TQ_F16;
+#define TQ_A2M(NB)                                                                                   \
+    if (nb == NB) {                                                                                  \
+      if (f16) hipLaunchKernelGGL((a2_scores_mfma_kernel<_Float16, NB>), g1, dim3(kPThreads), dq, s, p); \
+      else hipLaunchKernelGGL((a2_scores_mfma_kernel<float, NB>), g1, dim3(kPThreads), dq, s, p);       \
+    }
+    TQ_A2M(1) TQ_A2M(2) TQ_A2M(4)
+#undef TQ_A2M
+  } else if (p.kdtype == TQ_F16) {
     hipLaunchKernelGGL(a2_scores_kernel<_Float16>, g1, dim3(kPThreads), dyn, s, p);
-  else
+  } else {
     hipLaunchKernelGGL(a2_scores_kernel<float>, g1, dim3(kPThreads), dyn, s, p);
+  }
   hipLaunchKernelGGL(a2_lse_kernel, dim3(p.B * p.Hq * p.Np), dim3(kPThreads), 0, s, p);
   hipLaunchKernelGGL(a2_weight_kernel, dim3((p.T + kPThreads - 1) / kPThreads, p.B * p.Hkv), dim3(kPThreads), 0, s, p);
   return hipGetLastError();
