@@ -74,7 +74,27 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(QPrepParams p) {
     s_r[i] = (p.rotate && ((p.signbits[i >> 5] >> (i & 31)) & 1u)) ? -v : v;
   }
   __syncthreads();
-  if (p.rotate) {
+  if (p.rotate && d == 128) {
+    // The same butterflies in the registers of one wave: lane l holds
+    // elements 2l and 2l + 1; the stage of span h > 1 pairs lane l with lane
+    // l ^ (h / 2), whose value comes first in the sum or the difference
+    // when this lane is the pair's upper half (same operations, same result).
+    if (threadIdx.x < 64) {
+      const int l = threadIdx.x;
+      const float a = s_r[2 * l], c = s_r[2 * l + 1];
+      float x0 = a + c, x1 = a - c;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const float y0 = __shfl_xor(x0, m, 64), y1 = __shfl_xor(x1, m, 64);
+        const bool upper = (l & m) != 0;
+        x0 = upper ? y0 - x0 : x0 + y0;
+        x1 = upper ? y1 - x1 : x1 + y1;
+      }
+      s_r[2 * l] = x0 * p.inv_sqrt_d;
+      s_r[2 * l + 1] = x1 * p.inv_sqrt_d;
+    }
+    __syncthreads();
+  } else if (p.rotate) {
     for (int h = 1; h < d; h <<= 1) {
       for (int i = threadIdx.x; i < d / 2; i += blockDim.x) {
         const int lo = (i / h) * 2 * h + (i % h), hi = lo + h;
@@ -439,7 +459,28 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
       p.lse[qi] = s_L > 0.f ? (s_M + log2f(s_L)) * 0.69314718055994530942f + (p.qoff ? p.qoff[qi] : 0.f) : -INFINITY;
     return;
   }
-  if (p.vqjl) {
+  if (p.vqjl && d < (int)blockDim.x) {
+    // S^T acc_sk with blockDim / d threads per column, each over its own
+    // slice of rows with all of the slice's loads in flight (one L2 round
+    // trip instead of one per 16 rows), the slices summed in LDS.
+    const int nsl = (int)blockDim.x / d, rows = d / nsl;
+    const int kk = threadIdx.x % d, sl = threadIdx.x / d;
+    float acc = 0.f;
+    if (sl < nsl) {
+      const float* Sc = p.S + (size_t)sl * rows * d + kk;
+      const float* kc = s_k + sl * rows;
+#pragma unroll 64
+      for (int i = 0; i < rows; ++i) acc = fmaf(Sc[(size_t)i * d], kc[i], acc);
+    }
+    s_w[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x < d) {
+      float t = 0.f;
+      for (int u = 0; u < nsl; ++u) t += s_w[u * d + threadIdx.x];
+      s_o[threadIdx.x] = fmaf(p.v_qjl, t, s_o[threadIdx.x]);
+    }
+    __syncthreads();
+  } else if (p.vqjl) {
     float add[kMaxD / kThreads];
     for (int c = 0; c < d / (int)blockDim.x + 1; ++c) {
       const int kk = threadIdx.x + c * blockDim.x;
