@@ -66,10 +66,12 @@ constexpr int mq_threads(int D, bool KQ, bool VQ) { return 64 * (D == 128 ? mq_u
 
 // LDS budgets of the key and value tables: at d = 128 most of the LDS (one
 // block per CU); at d = 256 and 512 small enough for several blocks per CU; at
-// d = 1024 (one block of 8 waves per CU, by registers) beside the partial
-// scores' 32 KB.
+// d = 1024 (one block of 8 waves per CU, by registers) 64 KB each beside the
+// partial scores' 16 or 32 KB (at most 147.5 KB in all): a sketched value
+// table then holds 32 copies (16 before: KQV at d = 1024 3-6 % faster), a
+// sketched key table 16 (its three parts at 32 copies would not fit).
 constexpr int mq_kbudget(int D) { return D == 128 ? 65536 : D == 256 ? 16384 : D == 512 ? 32768 : 65536; }
-constexpr int mq_vbudget(int D) { return D == 128 ? 65536 : D == 256 ? 8192 : D == 512 ? 16384 : 32768; }
+constexpr int mq_vbudget(int D) { return D == 128 ? 65536 : D == 256 ? 8192 : D == 512 ? 16384 : 65536; }
 
 typedef _Float16 mq_half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 mq_half4 __attribute__((ext_vector_type(4)));
