@@ -66,12 +66,17 @@ constexpr int mq_threads(int D, bool KQ, bool VQ) { return 64 * (D == 128 ? mq_u
 
 // LDS budgets of the key and value tables: at d = 128 most of the LDS (one
 // block per CU); at d = 256 and 512 small enough for several blocks per CU; at
-// d = 1024 (one block of 8 waves per CU, by registers) 64 KB each beside the
-// partial scores' 16 or 32 KB (at most 147.5 KB in all): a sketched value
-// table then holds 32 copies (16 before: KQV at d = 1024 3-6 % faster), a
-// sketched key table 16 (its three parts at 32 copies would not fit).
-constexpr int mq_kbudget(int D) { return D == 128 ? 65536 : D == 256 ? 16384 : D == 512 ? 32768 : 65536; }
-constexpr int mq_vbudget(int D) { return D == 128 ? 65536 : D == 256 ? 8192 : D == 512 ? 16384 : 65536; }
+// d = 1024 (one block of 8 waves per CU, by registers) about 128 KB beside the
+// partial scores' 16 KB (at most 147.5 KB in all): 64 KB each (a sketched
+// value table at 32 copies, not 16: KQV at d = 1024 3-6 % faster), or with
+// sketched keys 96 KB for their three parts at 32 copies and 32 KB for the
+// values.
+constexpr int mq_kbudget(int D, bool KQ) {
+  return D == 128 ? 65536 : D == 256 ? 16384 : D == 512 ? 32768 : (KQ ? 98304 : 65536);
+}
+constexpr int mq_vbudget(int D, bool KQ) {
+  return D == 128 ? 65536 : D == 256 ? 8192 : D == 512 ? 16384 : (KQ ? 32768 : 65536);
+}
 
 typedef _Float16 mq_half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 mq_half4 __attribute__((ext_vector_type(4)));
@@ -276,18 +281,18 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
   constexpr int UPB = NW / NWU;                    // units per block (mq_upb at d = 128, else 1)
   constexpr int KW = KQ ? 4 : KB, VW = VQ ? 4 : VB;  // field widths
   constexpr int KPARTS = KQ ? 3 : 2, VPARTS = VQ ? 2 : 1;
-  constexpr int CK = mq_copies(KW, KPARTS, mq_kbudget(D)), CV = mq_copies(VW, VPARTS, mq_vbudget(D));
+  constexpr int CK = mq_copies(KW, KPARTS, mq_kbudget(D, KQ)), CV = mq_copies(VW, VPARTS, mq_vbudget(D, KQ));
   constexpr uint32_t RBK = D * KW / 8, RBV = D * VW / 8;  // code bytes per token
   // One LDS block: the value table first (at address 0, so that its lookup
   // offsets need no base), the key table, and for d > 128 the partial scores
   // of the unit's waves, double-buffered by step parity.
   constexpr int VBYTES = (MqTab<VW, VPARTS, CV>::bytes + 15) / 16 * 16;
   constexpr int KBYTES = (MqTab<KW, KPARTS, CK>::bytes + 15) / 16 * 16;
-  constexpr int RED = NWU > 1 ? 2 * NWU * (KQ ? 128 : 64) : 0;   // float4 entries
+  constexpr int RED = NWU > 1 ? 2 * NWU * 64 : 0;   // float4 entries
   __shared__ __attribute__((aligned(16))) char s_lds[VBYTES + KBYTES + 16 * RED + 16];
   char* const s_vtab = s_lds;
   char* const s_ktab = s_lds + VBYTES;
-  typedef mq_float4 RedRow[NWU > 1 ? NWU : 1][NWU > 1 ? (KQ ? 128 : 64) : 1];
+  typedef mq_float4 RedRow[NWU > 1 ? NWU : 1][NWU > 1 ? 64 : 1];
   RedRow* const s_red = reinterpret_cast<RedRow*>(s_lds + VBYTES + KBYTES);
   build_tab<KW, KPARTS, CK, true, KQ, KQ>(s_ktab, p.kc, threadIdx.x, NT);
   build_tab<VW, VPARTS, CV, false, VQ, VQ>(s_vtab, p.vc, threadIdx.x, NT);
@@ -441,17 +446,17 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
         }
       }
       if constexpr (NWU > 1) {
-        // Sum the partial scores of the unit's waves.
+        // Sum the partial scores of the unit's waves, each with its share of
+        // the sketch term already added (one exchange instead of two).
+        if constexpr (KQ) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[i] = fmaf(cur.gk[i] * p.k_qjl, Sk[i], S[i]);
+        }
         s_red[parity][wu][lane] = S;
-        if constexpr (KQ) s_red[parity][wu][64 + lane] = Sk;
         __syncthreads();
         S = s_red[parity][0][lane];
-        if constexpr (KQ) Sk = s_red[parity][0][64 + lane];
 #pragma unroll
-        for (int w = 1; w < NWU; ++w) {
-          S += s_red[parity][w][lane];
-          if constexpr (KQ) Sk += s_red[parity][w][64 + lane];
-        }
+        for (int w = 1; w < NWU; ++w) S += s_red[parity][w][lane];
         parity ^= 1;
       }
       mq_float4 Ss = {0.f, 0.f, 0.f, 0.f};
@@ -470,7 +475,7 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = S[i];
-        if constexpr (KQ) v = fmaf(cur.gk[i] * p.k_qjl, Sk[i], v);
+        if constexpr (KQ && NWU == 1) v = fmaf(cur.gk[i] * p.k_qjl, Sk[i], v);
         v *= cur.nuk[i];
         if constexpr (KS) v = fmaf(cur.sz[i], Ss[i], v);
         s[i] = v * p.scale_log2;
