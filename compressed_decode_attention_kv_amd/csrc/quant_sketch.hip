@@ -59,10 +59,12 @@ struct SkGeom {
   static constexpr int WPT = kSkWaves / TB;                // waves per token block
   static constexpr int RBW = (D / 32) / WPT;               // 32-row blocks per wave
   static constexpr int KSTEPS = D / 64;                    // contraction steps of 64
-  static constexpr size_t kLds = 2 * (size_t)MT * ROW * 2 + (size_t)MT * (D / 32) * 4;
+  // Residual rows (hi, lo), sign words, and the code words of phase 1 (at
+  // most 4 bits per coordinate), which wait there for their sign bits
+  // instead of in registers across the product.
+  static constexpr size_t kLds = 2 * (size_t)MT * ROW * 2 + (size_t)MT * (D / 32) * 4 + (size_t)MT * D / 2;
   static_assert(STEPS * kSkWaves * VPW == MT, "tile split");
   static_assert(RBW == 2 && KSTEPS % 2 == 0, "product split");
-  static_assert(kLds + 16 * 4 + 1024 * 8 <= 163840, "LDS budget");
 };
 
 }  // namespace
@@ -85,7 +87,7 @@ struct SkLut {
   float t;
   uint32_t base;
 };
-constexpr int kSkLutMax = 1024;
+constexpr int kSkLutMax = 512;  // cells of a 3-bit grid at d = 1024: 165
 
 template <int D, int BITS, typename TIN>
 __global__ __launch_bounds__(kSkThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
@@ -97,9 +99,11 @@ void quant_sketch_kernel(QuantParams p, QuantGrid grid) {
   __shared__ __attribute__((aligned(16))) char smem[G::kLds];
   __shared__ float s_cent[16];
   __shared__ __attribute__((aligned(8))) SkLut s_lut[kSkLutMax];
+  static_assert(G::kLds + sizeof(float) * 16 + sizeof(SkLut) * kSkLutMax <= 163840, "LDS budget");
   _Float16* a_hi = reinterpret_cast<_Float16*>(smem);
   _Float16* a_lo = a_hi + G::MT * G::ROW;
   uint32_t* sgn = reinterpret_cast<uint32_t*>(a_lo + G::MT * G::ROW);
+  uint32_t* cwords = sgn + G::MT * NW;  // [token m][lane j][FB]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -135,6 +139,7 @@ void quant_sketch_kernel(QuantParams p, QuantGrid grid) {
   // ---- 1. quantise the tile's tokens ------------------------------------------------
   uint32_t words[G::STEPS][FB];
   bool nonzero[G::STEPS];
+  static_assert(FB <= 4, "code words per lane");
 #pragma unroll
   for (int s = 0; s < G::STEPS; ++s) {
     const int m = s * (kSkWaves * G::VPW) + wave * G::VPW + slot;  // token within the tile
@@ -174,6 +179,11 @@ void quant_sketch_kernel(QuantParams p, QuantGrid grid) {
     if (valid && j == 0 && tw >= 0 && tw < p.T_cap) {
       __builtin_nontemporal_store(nu, p.norms + vbase + tw);
       __builtin_nontemporal_store(nz ? sqrtf(g2) : 0.f, p.gamma + vbase + tw);
+    }
+    {
+      uint32_t* cw = cwords + ((size_t)m * G::L + j) * FB;
+#pragma unroll
+      for (int k = 0; k < FB; ++k) cw[k] = words[s][k];
     }
     // Residual x 2^12 as fp16 hi (toward zero) + lo into row m of the tile.
     _Float16* dh = a_hi + m * G::ROW + 32 * j;
@@ -271,6 +281,11 @@ void quant_sketch_kernel(QuantParams p, QuantGrid grid) {
     const int64_t tw = slot0 + t;
     if (!(t < p.T && tw >= 0 && tw < p.T_cap)) continue;
     const uint32_t sw = nonzero[s] ? sgn[m * NW + j] : 0u;  // a zero vector keeps all-zero fields
+    {
+      const uint32_t* cw = cwords + ((size_t)m * G::L + j) * FB;
+#pragma unroll
+      for (int k = 0; k < FB; ++k) words[s][k] = cw[k];
+    }
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const int bit = FB * e + BITS;
