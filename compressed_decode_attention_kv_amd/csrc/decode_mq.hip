@@ -66,17 +66,11 @@ constexpr int mq_threads(int D, bool KQ, bool VQ) { return 64 * (D == 128 ? mq_u
 
 // LDS budgets of the key and value tables: at d = 128 most of the LDS (one
 // block per CU); at d = 256 and 512 small enough for several blocks per CU; at
-// d = 1024 (one block of 8 waves per CU, by registers) about 128 KB beside the
-// partial scores' 16 KB (at most 147.5 KB in all): 64 KB each (a sketched
-// value table at 32 copies, not 16: KQV at d = 1024 3-6 % faster), or with
-// sketched keys 96 KB for their three parts at 32 copies and 32 KB for the
-// values.
-constexpr int mq_kbudget(int D, bool KQ) {
-  return D == 128 ? 65536 : D == 256 ? 16384 : D == 512 ? 32768 : (KQ ? 98304 : 65536);
-}
-constexpr int mq_vbudget(int D, bool KQ) {
-  return D == 128 ? 65536 : D == 256 ? 8192 : D == 512 ? 16384 : (KQ ? 32768 : 65536);
-}
+// d = 1024 (one block of 8 waves per CU, by registers) 64 KB each beside the
+// partial scores' 16 KB (at most 144 KB in all): two-part tables (keys' hi
+// and lo; sketched values' centroids and signs) at 32 copies.
+constexpr int mq_kbudget(int D, bool) { return D == 128 ? 65536 : D == 256 ? 16384 : D == 512 ? 32768 : 65536; }
+constexpr int mq_vbudget(int D, bool) { return D == 128 ? 65536 : D == 256 ? 8192 : D == 512 ? 16384 : 65536; }
 
 typedef _Float16 mq_half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 mq_half4 __attribute__((ext_vector_type(4)));
@@ -90,11 +84,11 @@ typedef uint32_t mq_u32x2 __attribute__((ext_vector_type(2)));
 // sketch a field is 3-bit code | sign << 3 and the code is taken), two 3-bit
 // fields (a 6-bit index, half2), four 2-bit fields (half4) or four 1-bit
 // fields (a 4-bit index, half4).  Each entry sits
-// in C copies, copy = lane % C, against bank conflicts.  Up to
-// three parts share one indexing: keys hold the fp16 hi parts of the
-// centroids, the lo parts (c - hi) and, with a sketch, the signs (bit 3 of
-// each field) as fp16 +-1 (+1 for a set bit); values the centroids and, with
-// a sketch, the signs.
+// in C copies, copy = lane % C, against bank conflicts.  Two parts
+// share one indexing: keys hold the fp16 hi parts of the centroids and the lo
+// parts (c - hi) (a sketched key's signs are formed from its code words);
+// values the centroids and, with a sketch, the signs (bit 3 of each field) as
+// fp16 +-1 (+1 for a set bit).
 template <int W, int PARTS, int C>
 struct MqTab {
   static constexpr int entries = W == 3 ? 64 : W == 1 ? 16 : 256;
@@ -177,7 +171,14 @@ __device__ __forceinline__ void key8(const char* tab, const uint32_t* w, int ks,
       ah[2 * q] = h.x; ah[2 * q + 1] = h.y;
       al[2 * q] = l.x; al[2 * q + 1] = l.y;
       if constexpr (SIGNS) {
-        const mq_half2 s = mq_ent<W, PARTS, C, 2>(tab, a);
+        // The sign bit (bit 3) of fields 2q and 2q + 1 as fp16 +1 / -1
+        // (0x3C00 / 0xBC00) straight from the word: each byte of lsg / hsg is
+        // 0xBC with bit 7 flipped by the sign of the byte's low / high field,
+        // and byte q of each goes to the high byte of its half.
+        const uint32_t x = w[ks];
+        const uint32_t lsg = ((x & 0x08080808u) << 4) ^ 0xBCBCBCBCu, hsg = (x & 0x80808080u) ^ 0xBCBCBCBCu;
+        const uint32_t sel = 0x000C000Cu | ((uint32_t)q << 8) | ((uint32_t)(4 + q) << 24);
+        const mq_half2 s = __builtin_bit_cast(mq_half2, __builtin_amdgcn_perm(hsg, lsg, sel));
         as[2 * q] = s.x; as[2 * q + 1] = s.y;
       }
     }
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
   constexpr int NWU = D / 128;                     // waves per unit
   constexpr int UPB = NW / NWU;                    // units per block (mq_upb at d = 128, else 1)
   constexpr int KW = KQ ? 4 : KB, VW = VQ ? 4 : VB;  // field widths
-  constexpr int KPARTS = KQ ? 3 : 2, VPARTS = VQ ? 2 : 1;
+  constexpr int KPARTS = 2, VPARTS = VQ ? 2 : 1;  // key signs come from the code words
   constexpr int CK = mq_copies(KW, KPARTS, mq_kbudget(D, KQ)), CV = mq_copies(VW, VPARTS, mq_vbudget(D, KQ));
   constexpr uint32_t RBK = D * KW / 8, RBV = D * VW / 8;  // code bytes per token
   // One LDS block: the value table first (at address 0, so that its lookup
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(mq_threads(D, KQ, VQ)) void decode_mq_kernel(Decode
   char* const s_ktab = s_lds + VBYTES;
   typedef mq_float4 RedRow[NWU > 1 ? NWU : 1][NWU > 1 ? 64 : 1];
   RedRow* const s_red = reinterpret_cast<RedRow*>(s_lds + VBYTES + KBYTES);
-  build_tab<KW, KPARTS, CK, true, KQ, KQ>(s_ktab, p.kc, threadIdx.x, NT);
+  build_tab<KW, KPARTS, CK, true, false, KQ>(s_ktab, p.kc, threadIdx.x, NT);
   build_tab<VW, VPARTS, CV, false, VQ, VQ>(s_vtab, p.vc, threadIdx.x, NT);
   __syncthreads();
 
