@@ -15,7 +15,8 @@ SRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["api.cpp", "host_math.cpp", "quant.hip", "decode.hip", "decode_lut.hip", "quant_mfma.hip", "diag.hip",
-           "noalloc.hip", "quant_sketch.hip", "quant_spectral.hip", "policy.hip", "decode_mq.hip"]
+           "noalloc.hip", "quant_sketch.hip", "quant_spectral.hip", "policy.hip", "decode_mq.hip",
+           "decode_mq_wide.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # Keep the compiler from emitting packed-FP32 VALU instructions.
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -26,10 +27,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # grouped-query loop copied all 32 value sums out and back every step).  The table-driven decode is scheduled for instruction-level
 # parallelism (max ILP): at its register budget the default occupancy-first
 # scheduler waits for each LDS table read before issuing the next; the
-# iterative-ILP strategy measured equal or up to 1.5 % slower.
+# iterative-ILP strategy measured equal or up to 1.5 % slower; the grouped-query
+# decode at d = 256..1024 runs 2-7 % faster under it (at d = 128 not).
 EXTRA = {"quant_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "quant_spectral.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "decode_mq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_mq_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
          "decode_lut.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 

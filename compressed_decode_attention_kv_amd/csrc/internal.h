@@ -235,6 +235,9 @@ int mq_units_per_block(int d, int kqjl, int vqjl);
 int mq_target_units(int d, int kqjl, int vqjl, int cus);
 hipError_t launch_decode_mq(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl, int nblocks,
                             hipStream_t s);
+// The same for d = 256..1024 (decode_mq_wide.hip).
+hipError_t launch_decode_mq_wide(const DecodeParams& p, int kbits, int kqjl, int kside, int vbits, int vqjl,
+                                 int nblocks, hipStream_t s);
 hipError_t launch_metric_scores(const MetricScoreParams& p, int kbits, int kqjl, int kside, hipStream_t s,
                                 bool* supported);
 hipError_t launch_metric_reduce(const MetricReduceParams& p, hipStream_t s);

@@ -44,7 +44,8 @@ import os
 import re
 import sys
 
-DECODE_SOURCES = ("decode_lut.hip", "decode.hip", "decode_mq.hip", "device_common.h", "internal.h")
+DECODE_SOURCES = ("decode_lut.hip", "decode.hip", "decode_mq.hip", "decode_mq_kernel.h", "decode_mq_wide.hip",
+                  "device_common.h", "internal.h")
 QUANTIZE_SOURCES = ("quant_mfma.hip", "quant.hip", "quant_sketch.hip", "device_common.h", "internal.h")
 CHAIN = ("qprep_kernel", "decode_lut_kernel", "decode_mq_kernel", "decode_split_kernel", "sproj_kernel", "combine_kernel")
 QCHAIN = ("quant_mfma_kernel", "quant_kernel", "quant_sketch_kernel")
